@@ -1,0 +1,218 @@
+"""Benchmark of the fused-path FNO spectral-convolution layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config c1] [--dtype f32]
+
+A step is one whole layer (every launch of the path) over one batch of
+synthetic input already resident in HBM. Buffer sets are rotated so that the
+whole working set exceeds 1 GiB and the 256 MB Infinity Cache cannot serve
+it. Prints one JSON line:
+
+* value: layers/s on the main workload (default: the 128x128 fp32 layer,
+  B=16, Cin=Cout=32, modes 16x16), plus GB/s and the fraction of the 8 TB/s
+  HBM peak from the minimal bytes (read x + read w + write y once);
+* roofline: the dominant kernel's algorithmic bytes per launch over its
+  average launch time (HIP events on the stream it runs on);
+* cpu_baseline: the float64 oracle timed on this host's cores on the same
+  workload;
+* configs: the same layers/s and GB/s figures for the 128^2 fp16, 256^2
+  fp16 / bf16 and 64^3 fp32 layers.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused spectral-conv layers/sec + GB/s (% HBM peak) at 128², 256², 64³"
+HBM_PEAK_GBPS = 8000.0
+ROTATE_BYTES = 1 << 30
+
+
+def _bytes_per_launch(cfg, dtype):
+    """Algorithmic bytes of each launch: its compulsory input and output."""
+    s = 4 if dtype == "f32" else 2
+    pts = int(np.prod(cfg.grid))
+    x = cfg.batch * cfg.c_in * pts * s
+    y = cfg.batch * cfg.c_out * pts * s
+    w = cfg.n_modes * cfg.c_in * cfg.c_out * 2 * s
+    xh = cfg.batch * cfg.c_in * cfg.n_modes * 8
+    yh = cfg.batch * cfg.c_out * cfg.n_modes * 8
+    if cfg.ndim == 2:
+        return {"fno_fwd_plane": x + xh, "fno_contract": xh + w + yh, "fno_inv_plane": yh + y}
+    C = 2 * cfg.modes[1] * cfg.modes[2]
+    ti = cfg.batch * cfg.c_in * cfg.grid[0] * C * 8
+    to = cfg.batch * cfg.c_out * cfg.grid[0] * C * 8
+    return {"fno_fwd_plane": x + ti, "fno_fwd_axis": ti + xh, "fno_contract": xh + w + yh,
+            "fno_inv_axis": yh + to, "fno_inv_plane": to + y}
+
+
+def to_device(arr, dtype, device="cuda:0"):
+    import torch
+    a = np.ascontiguousarray(arr)
+    t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if dtype == "bf16" \
+        else torch.from_numpy(a)
+    return t.to(device)
+
+
+class Layer:
+    """Plan plus rotating device buffer sets for one workload."""
+
+    def __init__(self, cfg, dtype):
+        import torch
+        import spectral_convolution_amd as fno
+        import workloads as wl
+        self.fno, self.cfg, self.dtype = fno, cfg, dtype
+        inp = wl.layer_inputs(cfg, dtype)
+        self.plan = fno.fno_plan_create(cfg.ndim, cfg.batch, cfg.c_in, cfg.c_out, cfg.grid,
+                                        cfg.modes, dtype, 0)
+        x0, w0 = to_device(inp["x"], dtype), to_device(inp["w"], dtype)
+        per_set = cfg.minimal_bytes(dtype)
+        self.nsets = max(1, math.ceil(ROTATE_BYTES / per_set))
+        self.sets = []
+        for i in range(self.nsets):
+            x = x0 if i == 0 else x0.clone()
+            w = w0 if i == 0 else w0.clone()
+            y = torch.empty(self.plan.y_shape(), dtype=x0.dtype, device=x0.device)
+            self.sets.append((x, w, y))
+        self.call = fno.fno_spectral_conv2d if cfg.ndim == 2 else fno.fno_spectral_conv3d
+        self.stream = torch.cuda.current_stream()
+        self.names = [fno.fno_plan_launch_name(self.plan, i)
+                      for i in range(fno.fno_plan_num_launches(self.plan))]
+
+    def step(self, i):
+        x, w, y = self.sets[i % self.nsets]
+        self.call(self.plan, x, w, y, self.stream)
+
+    def launch(self, idx, i):
+        x, w, y = self.sets[i % self.nsets]
+        self.fno.fno_plan_run_launch(self.plan, idx, x, w, y, self.stream)
+
+    def close(self):
+        self.fno.fno_plan_destroy(self.plan)
+        self.sets = []
+
+
+def _time_loop(fn, steps, warmup, stream):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per call
+
+
+def measure(cfg, dtype, steps, warmup, per_kernel=True):
+    lay = Layer(cfg, dtype)
+    try:
+        ms = _time_loop(lay.step, steps, warmup, lay.stream)
+        res = {"workload": cfg.name, "dtype": dtype, "ms_per_layer": ms,
+               "layers_per_s": 1000.0 / ms,
+               "gbps": cfg.minimal_bytes(dtype) / (ms * 1e-3) / 1e9}
+        res["hbm_frac"] = res["gbps"] / HBM_PEAK_GBPS
+        if per_kernel:
+            bpl = _bytes_per_launch(cfg, dtype)
+            kern = []
+            for idx, name in enumerate(lay.names):
+                kms = _time_loop(lambda i, idx=idx: lay.launch(idx, i), steps, max(2, warmup // 4),
+                                 lay.stream)
+                kern.append({"kernel": name, "ms": kms, "bytes": bpl[name],
+                             "gbps": bpl[name] / (kms * 1e-3) / 1e9})
+            res["kernels"] = kern
+        return res
+    finally:
+        lay.close()
+
+
+def cpu_baseline(cfg, dtype, min_seconds=10.0):
+    """The float64 oracle on this host's cores, repeated for ~min_seconds."""
+    import oracle
+    import workloads as wl
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = len(os.sched_getaffinity(0))
+    inp = wl.layer_inputs(cfg, dtype)
+    f = oracle.spectral_conv2d if cfg.ndim == 2 else oracle.spectral_conv3d
+    with threadpool_limits(limits=cores):
+        used = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        f(inp["x64"], inp["w64"], *cfg.modes)  # warm-up
+        n, t0 = 0, time.perf_counter()
+        while True:
+            f(inp["x64"], inp["w64"], *cfg.modes)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds:
+                break
+    return {"value": n / el, "unit": "layers/s", "cores": int(used), "kind": "oracle",
+            "sample": f"whole {cfg.name} {dtype} layer (B={cfg.batch}), {n} runs in {el:.1f} s "
+                      f"after one warm-up, float64 numpy, host affinity {cores} cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c1")
+    ap.add_argument("--dtype", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer shards over the batch with no communication; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU available", file=sys.stderr)
+        sys.exit(1)
+    cfg = wl.CONFIGS[args.config]
+    dtype = args.dtype or cfg.dtypes[0]
+    main_res = measure(cfg, dtype, args.steps, args.warmup)
+    dom = max(main_res["kernels"], key=lambda k: k["ms"])
+    out = {
+        "metric": METRIC, "value": main_res["layers_per_s"], "unit": "layers/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_layer"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if dtype == "f32" else f"{dtype} storage, f32 compute",
+        "data": "synthetic (seeded Gaussian random fields; random weights)",
+        "config": {"workload": cfg.description, "name": cfg.name, "batch": cfg.batch,
+                   "c_in": cfg.c_in, "c_out": cfg.c_out, "grid": list(cfg.grid),
+                   "modes": list(cfg.modes), "storage": dtype,
+                   "minimal_bytes": cfg.minimal_bytes(dtype)},
+        "gbps": main_res["gbps"], "hbm_frac": main_res["hbm_frac"],
+        "roofline": {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["gbps"],
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dom["gbps"] / HBM_PEAK_GBPS,
+                     "traffic": None, "bytes_per_launch": dom["bytes"], "ms_per_launch": dom["ms"]},
+        "kernels": main_res["kernels"],
+    }
+    if not args.no_extra:
+        extra = []
+        for name, dt in (("c1", "f16"), ("c2", "f16"), ("c2", "bf16"), ("c3", "f32"), ("c0", "f32")):
+            if name == cfg.name and dt == dtype:
+                continue
+            r = measure(wl.CONFIGS[name], dt, max(20, args.steps // 2), max(5, args.warmup // 2))
+            extra.append(r)
+            print(f"[bench] {name} {dt}: {r['layers_per_s']:.1f} layers/s, {r['gbps']:.0f} GB/s",
+                  file=sys.stderr, flush=True)
+        out["configs"] = extra
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, dtype)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,132 @@
+/*
+ * fno.h - C ABI of the MI355X (gfx950) FNO spectral-convolution library.
+ *
+ * The operation is the Fourier Neural Operator spectral-convolution layer as
+ * the TurboFNO write-up ("TurboFNO: FFT-GEMM-iFFT fusion kernels") describes
+ * it: section 1 and sections 2.1-2.3 (real FFT of a [B, C, H, W] field, the
+ * per-mode complex contraction einsum("xyij,xyik->xyjk") over the input
+ * channel with a learnable weight of shape (modes_x, modes_y, in_ch, out_ch),
+ * inverse real FFT), and section 4.3 (a C function on raw device pointers
+ * called from a PyTorch autograd Function). Sizes are fixed when a plan is
+ * made (section 2.3: the output size is a build-time constant of the fused
+ * kernel), and grids are powers of two (section 2.1).
+ *
+ * For every plane the layer computes
+ *   Xh[kx, ky] = (1 / prod(grid)) * sum_n x[n] exp(-2 pi i k.n / grid)
+ * on the retained modes only, then Yh[b, o, k] = sum_i Xh[b, i, k] w[k, i, o]
+ * (no conjugation), then the inverse real transform from the retained modes
+ * (every other mode zero), which keeps the real part of the kz = 0 (2D:
+ * ky = 0) term and doubles the others. This equals torch.fft.rfft2 ->
+ * per-mode einsum -> torch.fft.irfft2 with the default normalisation.
+ *
+ * Retained modes. 2D: kx in [0, m1) and [H - m1, H) (two corners), ky in
+ * [0, m2) (half spectrum). 3D: kx in [0, m1) and [X - m1, X), ky in [0, m2)
+ * and [Y - m2, Y), kz in [0, m3).
+ *
+ * Layouts (all arrays contiguous, on the plan's device, in the plan's dtype):
+ *   x  2D [B][Ci][H][W]          3D [B][Ci][X][Y][Z]   (last axis contiguous)
+ *   y  2D [B][Co][H][W]          3D [B][Co][X][Y][Z]
+ *   w  2D [2*m1][m2][Ci][Co][2]  3D [2*m1][2*m2][m3][Ci][Co][2]
+ *      (re, im interleaved; along a corner axis index a < m selects k = a,
+ *       index a >= m selects k = N - 2*m + a, i.e. the low corner first.)
+ *
+ * Ownership. The caller owns x, w and y and keeps them alive until the work
+ * queued on `stream` has finished. The plan owns its twiddle tables and its
+ * spectra workspace (allocated by fno_plan_create, freed by
+ * fno_plan_destroy). Execution calls allocate nothing.
+ *
+ * Execution calls are asynchronous on `stream` (a hipStream_t; NULL is the
+ * null stream) and return as soon as the kernels are queued. One plan runs
+ * one call at a time: concurrent calls on different streams need different
+ * plans, because they share the plan's workspace. Results are deterministic
+ * run to run (no atomics on the data path).
+ *
+ * Errors. No function throws. Argument errors are detected on the host
+ * before any HIP call. A failed fno_plan_create sets *plan to NULL.
+ */
+#ifndef FNO_H
+#define FNO_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fno_plan_s *fno_plan_t;
+
+/* Storage dtype of x, w and y. Arithmetic is fp32 throughout (fp32
+ * accumulation in the contraction); fp16 / bf16 are storage formats. */
+typedef enum { FNO_F32 = 0, FNO_F16 = 1, FNO_BF16 = 2 } fno_dtype_t;
+
+typedef enum {
+  FNO_OK = 0,
+  FNO_ERR_INVALID_ARG = 1, /* NULL / misaligned / overlapping pointer, bad
+                              size, mode out of range, wrong ndim */
+  FNO_ERR_UNSUPPORTED = 2, /* valid but outside the built kernels' range */
+  FNO_ERR_OUT_OF_MEMORY = 3, /* workspace allocation failed */
+  FNO_ERR_DEVICE = 4       /* any HIP runtime error (launch included) */
+} fno_status_t;
+
+/* Make a plan for one layer shape.
+ *   plan   out: the new plan (NULL on failure)
+ *   ndim   2 or 3
+ *   batch, c_in, c_out  >= 1
+ *   grid   ndim entries (H, W or X, Y, Z): powers of two in [8, 256]
+ *   modes  ndim entries (m1, m2 or m1, m2, m3): 1 <= m_d <= grid_d / 2
+ *   dtype  storage dtype of x, w, y
+ *   device HIP device ordinal
+ * UNSUPPORTED when max(next_pow2(m_d)) over the axes of a transformed plane
+ * exceeds 32 or half the smallest axis of that plane. Allocates the
+ * workspace and twiddle tables on `device`; synchronous. */
+fno_status_t fno_plan_create(fno_plan_t *plan, int ndim, int batch, int c_in,
+                             int c_out, const int *grid, const int *modes,
+                             fno_dtype_t dtype, int device);
+
+/* One 2D layer: y = SpectralConv2d(x; w). x, w, y are device pointers laid
+ * out as above, 16-byte aligned; x and y must not overlap. INVALID_ARG on a
+ * 3D plan. */
+fno_status_t fno_spectral_conv2d(fno_plan_t plan, const void *x, const void *w,
+                                 void *y, void *stream);
+
+/* One 3D layer (3D plan only); as fno_spectral_conv2d. */
+fno_status_t fno_spectral_conv3d(fno_plan_t plan, const void *x, const void *w,
+                                 void *y, void *stream);
+
+/* Free the plan's device memory after synchronising its device.
+ * fno_plan_destroy(NULL) returns FNO_OK. Destroying a plan twice is
+ * undefined. */
+fno_status_t fno_plan_destroy(fno_plan_t plan);
+
+/* Static string naming a status code. */
+const char *fno_status_string(fno_status_t s);
+
+/* ---- inspection and measurement ---------------------------------------- */
+
+/* Bytes of device workspace the plan holds (spectra and staging). */
+fno_status_t fno_plan_workspace_bytes(fno_plan_t plan, size_t *bytes);
+
+/* Number of kernel launches one execution call queues, and the name of
+ * launch `index` (0-based, in queue order; a static string). */
+fno_status_t fno_plan_num_launches(fno_plan_t plan, int *n);
+fno_status_t fno_plan_launch_name(fno_plan_t plan, int index,
+                                  const char **name);
+
+/* Queue only launch `index` of an execution call, with the same arguments
+ * and preconditions as the full call (the launches before it must have
+ * produced the workspace contents it reads). Used to time one kernel and to
+ * check intermediate spectra. */
+fno_status_t fno_plan_run_launch(fno_plan_t plan, int index, const void *x,
+                                 const void *w, void *y, void *stream);
+
+/* Device pointer to the plan's forward spectra (which = 0, complex fp32
+ * [B][Ci][K], already scaled by 1/prod(grid)) or to the contracted spectra
+ * (which = 1, complex fp32 [B][Co][K]); K = 2*m1*m2 (2D) or 4*m1*m2*m3 (3D),
+ * modes ordered as in w. Valid after an execution call has finished. */
+fno_status_t fno_plan_spectra(fno_plan_t plan, int which, void **ptr);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FNO_H */

@@ -1,0 +1,117 @@
+// common.hpp - shared device helpers and kernel argument blocks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fft_reg.hpp"
+
+namespace fno {
+
+// storage dtype tags (values equal fno_dtype_t)
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (quiet NaN preserved)
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Load two adjacent storage elements p[0], p[1] as fp32 (p 2-element aligned).
+template <int DT>
+__device__ __forceinline__ float2 load_pair(const void *base, size_t idx) {
+  if constexpr (DT == DT_F32) {
+    return *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(base) + idx);
+  } else if constexpr (DT == DT_F16) {
+    half2_t h = *reinterpret_cast<const half2_t *>(reinterpret_cast<const _Float16 *>(base) + idx);
+    return make_float2((float)h.x, (float)h.y);
+  } else {
+    uint32_t v = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(base) + idx);
+    return make_float2(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
+  }
+}
+
+// Store two adjacent elements (RNE conversion to the storage dtype).
+template <int DT>
+__device__ __forceinline__ void store_pair(void *base, size_t idx, float a, float b) {
+  if constexpr (DT == DT_F32) {
+    *reinterpret_cast<float2 *>(reinterpret_cast<float *>(base) + idx) = make_float2(a, b);
+  } else if constexpr (DT == DT_F16) {
+    half2_t h;
+    h.x = (_Float16)a;
+    h.y = (_Float16)b;
+    *reinterpret_cast<half2_t *>(reinterpret_cast<_Float16 *>(base) + idx) = h;
+  } else {
+    uint32_t v = f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+    *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(base) + idx) = v;
+  }
+}
+
+// ---------------------------------------------------------------- arguments
+
+// Forward transform of real planes: a pruned r2c DFT along the contiguous axis
+// (length W, modes ky < m2) then a pruned c2c DFT along the other axis
+// (length H, kx in the two corners of m1), output [plane][2*m1][m2] complex,
+// multiplied by `scale`.
+struct PlaneFwdArgs {
+  const void *x;        // nplanes * H * W storage elements
+  float2 *out;          // nplanes * 2*m1*m2
+  const float2 *tw_h;   // exp(-2 pi i k / H), k < H
+  const float2 *tw_w;   // exp(-2 pi i k / W), k < W
+  int nplanes, H, W, m1, m2, PH, PW;
+  int CH;  // rows per chunk of the row stage (plane_fwd_chunk_rows)
+  float scale;
+};
+
+// Inverse of the above without scaling: [plane][2*m1][m2] complex -> real.
+struct PlaneInvArgs {
+  const float2 *in;
+  void *y;
+  const float2 *tw_h;
+  const float2 *tw_w;
+  int nplanes, H, W, m1, m2, PH, PW;
+};
+
+// Pruned c2c DFT along a strided axis: in [vol][N][C] -> out [vol][2*m][C]
+// (forward, times `scale`), or the inverse out [vol][N][C] from [vol][2*m][C].
+struct AxisArgs {
+  const float2 *in;
+  float2 *out;
+  const float2 *tw;  // exp(-2 pi i k / N), k < N
+  int nvol, N, m, P, C;
+  float scale;
+};
+
+// Per-mode contraction: yh[b][o][k] = sum_i xh[b][i][k] w[k][i][o].
+struct ContractArgs {
+  const float2 *xh;  // [B][Ci][K]
+  const void *w;     // [K][Ci][Co][2] storage dtype
+  float2 *yh;        // [B][Co][K]
+  int B, Ci, Co, K;
+};
+
+// host launchers (defined next to their kernels)
+int plane_fwd_chunk_rows(int H, int W, int m1, int m2, int MP);
+size_t plane_fwd_lds_bytes(int H, int W, int m1, int m2, int MP);
+size_t plane_inv_lds_bytes(int H, int W, int m1, int m2, int MP);
+size_t axis_fwd_lds_bytes(int N, int m, int MP);
+hipError_t plane_fwd_prepare(int MP, int dtype, size_t lds);
+hipError_t plane_inv_prepare(int MP, int dtype, size_t lds);
+hipError_t launch_plane_fwd(const PlaneFwdArgs &a, int MP, int dtype, size_t lds, hipStream_t s);
+hipError_t launch_plane_inv(const PlaneInvArgs &a, int MP, int dtype, size_t lds, hipStream_t s);
+hipError_t axis_fwd_prepare(int MP, size_t lds);
+hipError_t launch_axis_fwd(const AxisArgs &a, int MP, size_t lds, hipStream_t s);
+hipError_t launch_axis_inv(const AxisArgs &a, int MP, hipStream_t s);
+int contract_pick_bb(int B, int Co, int K);
+hipError_t launch_contract(const ContractArgs &a, int bb, int dtype, hipStream_t s);
+
+}  // namespace fno

@@ -1,0 +1,443 @@
+// fno_api.cpp - the C ABI: plan validation, tables, workspace and launches.
+//
+// A 2D layer is three stream-ordered launches:
+//   fno_fwd_plane  (pruned r2c along W + pruned c2c along H, scaled)
+//   fno_contract   (per-mode complex contraction on MFMA)
+//   fno_inv_plane  (pruned c2c along H + pruned c2r along W)
+// A 3D layer applies the plane transforms to every x-slab (axes Y, Z) and
+// adds the outermost axis as a separate pruned c2c pass:
+//   fno_fwd_plane(slabs) -> fno_fwd_axis(X) -> fno_contract ->
+//   fno_inv_axis(X) -> fno_inv_plane(slabs)
+// Spectra between launches live in the plan's workspace (complex fp32).
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/fno.h"
+#include "common.hpp"
+
+using namespace fno;
+
+namespace {
+
+constexpr int kMaxAxis = 256;
+constexpr int kMinAxis = 8;
+constexpr int kMaxRegFFT = 32;
+constexpr size_t kMaxLds = 160 * 1024;
+
+enum LaunchKind { L_FWD_PLANE, L_FWD_AXIS, L_CONTRACT, L_INV_AXIS, L_INV_PLANE };
+
+bool is_pow2(long v) { return v > 0 && (v & (v - 1)) == 0; }
+int next_pow2(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+// exp(-2 pi i k / n) for k < n from the definition in double precision: the
+// angle is reduced in integers to a quarter turn plus an angle in [0, pi/2),
+// whose cos / sin are taken and rotated back by the quarter turns
+std::vector<float2> twiddles(int n) {
+  std::vector<float2> t(n);
+  for (int k = 0; k < n; ++k) {
+    const long q = (4L * k) / n;            // quarter turns
+    const long rem = 4L * k - q * n;        // remaining angle = (pi/2) * rem / n
+    const double a = (M_PI / 2.0) * (double)rem / (double)n;
+    const double ca = std::cos(a), sa = std::sin(a);
+    double c, s;
+    switch (q) {
+      case 0: c = ca; s = sa; break;
+      case 1: c = -sa; s = ca; break;
+      case 2: c = -ca; s = -sa; break;
+      default: c = sa; s = -ca; break;
+    }
+    t[k] = make_float2((float)c, (float)(-s));
+  }
+  return t;
+}
+
+}  // namespace
+
+struct fno_plan_s {
+  int ndim = 0, B = 0, Ci = 0, Co = 0;
+  int grid[3] = {0, 0, 0};
+  int modes[3] = {0, 0, 0};
+  int dtype = 0, device = 0;
+  int K = 0;            // retained modes per plane
+  // plane transform (2D: axes H, W; 3D: axes Y, Z of every x-slab)
+  int pH = 0, pW = 0, pm1 = 0, pm2 = 0, pMP = 0;
+  size_t lds_fwd = 0, lds_inv = 0;
+  // 3D outer axis
+  int xN = 0, xm = 0, xMP = 0;
+  size_t lds_axis = 0;
+  int bb = 1;
+  float2 *tw_h = nullptr, *tw_w = nullptr, *tw_x = nullptr;
+  float2 *xh = nullptr, *yh = nullptr, *tbuf = nullptr;
+  void *mem = nullptr;
+  size_t ws_bytes = 0;
+  std::vector<int> launches;
+};
+
+static fno_status_t map_err(hipError_t e) {
+  if (e == hipSuccess) return FNO_OK;
+  if (e == hipErrorOutOfMemory) return FNO_ERR_OUT_OF_MEMORY;
+  return FNO_ERR_DEVICE;
+}
+
+// Validate sizes; fills the shape fields. No HIP calls.
+static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c_out, const int *grid,
+                             const int *modes, fno_dtype_t dtype) {
+  if (ndim != 2 && ndim != 3) return FNO_ERR_INVALID_ARG;
+  if (!grid || !modes) return FNO_ERR_INVALID_ARG;
+  if (batch < 1 || c_in < 1 || c_out < 1) return FNO_ERR_INVALID_ARG;
+  if (batch > 65535 || c_in > 65535 || c_out > 65535) return FNO_ERR_UNSUPPORTED;
+  if (dtype != FNO_F32 && dtype != FNO_F16 && dtype != FNO_BF16) return FNO_ERR_INVALID_ARG;
+  for (int d = 0; d < ndim; ++d) {
+    if (grid[d] < 2) return FNO_ERR_INVALID_ARG;
+    if (modes[d] < 1 || modes[d] > grid[d] / 2) return FNO_ERR_INVALID_ARG;
+  }
+  for (int d = 0; d < ndim; ++d) {
+    if (!is_pow2(grid[d]) || grid[d] < kMinAxis || grid[d] > kMaxAxis) return FNO_ERR_UNSUPPORTED;
+  }
+  p.ndim = ndim;
+  p.B = batch;
+  p.Ci = c_in;
+  p.Co = c_out;
+  p.dtype = (int)dtype;
+  for (int d = 0; d < ndim; ++d) {
+    p.grid[d] = grid[d];
+    p.modes[d] = modes[d];
+  }
+  const int o = ndim - 2;  // plane axes are the last two
+  p.pH = grid[o];
+  p.pW = grid[o + 1];
+  p.pm1 = modes[o];
+  p.pm2 = modes[o + 1];
+  p.pMP = next_pow2(p.pm1 > p.pm2 ? p.pm1 : p.pm2);
+  if (p.pMP < 2) p.pMP = 2;
+  const int pmin = p.pH < p.pW ? p.pH : p.pW;
+  if (p.pMP > kMaxRegFFT || p.pMP > pmin / 2) return FNO_ERR_UNSUPPORTED;
+  if (ndim == 3) {
+    p.xN = grid[0];
+    p.xm = modes[0];
+    p.xMP = next_pow2(p.xm);
+    if (p.xMP < 2) p.xMP = 2;
+    if (p.xMP > kMaxRegFFT || p.xMP > p.xN / 2) return FNO_ERR_UNSUPPORTED;
+    p.K = 4 * modes[0] * modes[1] * modes[2];
+  } else {
+    p.K = 2 * modes[0] * modes[1];
+  }
+  p.lds_fwd = plane_fwd_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP);
+  p.lds_inv = plane_inv_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP);
+  if (p.lds_fwd > kMaxLds || p.lds_inv > kMaxLds) return FNO_ERR_UNSUPPORTED;
+  if (ndim == 3) {
+    p.lds_axis = axis_fwd_lds_bytes(p.xN, p.xm, p.xMP);
+    if (p.lds_axis > kMaxLds) return FNO_ERR_UNSUPPORTED;
+    if ((long)batch * (c_in > c_out ? c_in : c_out) > 65535) return FNO_ERR_UNSUPPORTED;
+  }
+  // element counts must stay well inside 64-bit / 32-bit grid limits
+  long pts = 1;
+  for (int d = 0; d < ndim; ++d) pts *= grid[d];
+  const long planes = (long)batch * (c_in > c_out ? c_in : c_out) * (ndim == 3 ? grid[0] : 1);
+  if (planes > 0x7fffffffL || (double)batch * (c_in > c_out ? c_in : c_out) * pts > 1e12)
+    return FNO_ERR_UNSUPPORTED;
+  p.bb = contract_pick_bb(batch, c_out, p.K);
+  if (ndim == 2) {
+    p.launches = {L_FWD_PLANE, L_CONTRACT, L_INV_PLANE};
+  } else {
+    p.launches = {L_FWD_PLANE, L_FWD_AXIS, L_CONTRACT, L_INV_AXIS, L_INV_PLANE};
+  }
+  return FNO_OK;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  hipError_t err = hipSuccess;
+  explicit DeviceGuard(int dev) {
+    err = hipGetDevice(&prev);
+    if (err == hipSuccess && prev != dev) err = hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+extern "C" {
+
+const char *fno_status_string(fno_status_t s) {
+  switch (s) {
+    case FNO_OK: return "FNO_OK";
+    case FNO_ERR_INVALID_ARG: return "FNO_ERR_INVALID_ARG";
+    case FNO_ERR_UNSUPPORTED: return "FNO_ERR_UNSUPPORTED";
+    case FNO_ERR_OUT_OF_MEMORY: return "FNO_ERR_OUT_OF_MEMORY";
+    case FNO_ERR_DEVICE: return "FNO_ERR_DEVICE";
+  }
+  return "FNO_ERR_UNKNOWN";
+}
+
+fno_status_t fno_plan_destroy(fno_plan_t plan) {
+  if (!plan) return FNO_OK;
+  fno_status_t st = FNO_OK;
+  if (plan->mem) {
+    DeviceGuard g(plan->device);
+    if (g.err != hipSuccess) st = FNO_ERR_DEVICE;
+    if (hipDeviceSynchronize() != hipSuccess) st = FNO_ERR_DEVICE;
+    if (hipFree(plan->mem) != hipSuccess) st = FNO_ERR_DEVICE;
+  }
+  delete plan;
+  return st;
+}
+
+fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int c_out, const int *grid,
+                             const int *modes, fno_dtype_t dtype, int device) {
+  if (!out) return FNO_ERR_INVALID_ARG;
+  *out = nullptr;
+  fno_plan_s *p = new (std::nothrow) fno_plan_s();
+  if (!p) return FNO_ERR_OUT_OF_MEMORY;
+  fno_status_t st = validate(*p, ndim, batch, c_in, c_out, grid, modes, dtype);
+  if (st != FNO_OK) {
+    delete p;
+    return st;
+  }
+  if (device < 0) {
+    delete p;
+    return FNO_ERR_INVALID_ARG;
+  }
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess) {
+    delete p;
+    return FNO_ERR_DEVICE;
+  }
+  if (device >= ndev) {
+    delete p;
+    return FNO_ERR_INVALID_ARG;
+  }
+  p->device = device;
+  DeviceGuard g(device);
+  if (g.err != hipSuccess) {
+    delete p;
+    return FNO_ERR_DEVICE;
+  }
+
+  // workspace layout (each piece 256-byte aligned)
+  auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  const size_t n_xh = (size_t)p->B * p->Ci * p->K, n_yh = (size_t)p->B * p->Co * p->K;
+  size_t n_t = 0;
+  if (ndim == 3) {
+    const size_t C = (size_t)2 * p->modes[1] * p->modes[2];
+    n_t = (size_t)p->B * (p->Ci > p->Co ? p->Ci : p->Co) * p->xN * C;
+  }
+  const int nth = p->pH, ntw = p->pW, ntx = ndim == 3 ? p->xN : 0;
+  size_t off = 0;
+  const size_t o_th = off; off += al(nth * sizeof(float2));
+  const size_t o_tw = off; off += al(ntw * sizeof(float2));
+  const size_t o_tx = off; off += al(ntx * sizeof(float2));
+  const size_t o_xh = off; off += al(n_xh * sizeof(float2));
+  const size_t o_yh = off; off += al(n_yh * sizeof(float2));
+  const size_t o_t = off; off += al(n_t * sizeof(float2));
+  p->ws_bytes = off;
+  hipError_t e = hipMalloc(&p->mem, off);
+  if (e != hipSuccess) {
+    p->mem = nullptr;
+    delete p;
+    (void)hipGetLastError();
+    return e == hipErrorOutOfMemory ? FNO_ERR_OUT_OF_MEMORY : FNO_ERR_DEVICE;
+  }
+  char *base = (char *)p->mem;
+  p->tw_h = (float2 *)(base + o_th);
+  p->tw_w = (float2 *)(base + o_tw);
+  p->tw_x = ntx ? (float2 *)(base + o_tx) : nullptr;
+  p->xh = (float2 *)(base + o_xh);
+  p->yh = (float2 *)(base + o_yh);
+  p->tbuf = n_t ? (float2 *)(base + o_t) : nullptr;
+
+  std::vector<float2> th = twiddles(nth), tw = twiddles(ntw);
+  e = hipMemcpy(p->tw_h, th.data(), nth * sizeof(float2), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(p->tw_w, tw.data(), ntw * sizeof(float2), hipMemcpyHostToDevice);
+  if (e == hipSuccess && ntx) {
+    std::vector<float2> tx = twiddles(ntx);
+    e = hipMemcpy(p->tw_x, tx.data(), ntx * sizeof(float2), hipMemcpyHostToDevice);
+  }
+  if (e == hipSuccess) e = plane_fwd_prepare(p->pMP, p->dtype, p->lds_fwd);
+  if (e == hipSuccess) e = plane_inv_prepare(p->pMP, p->dtype, p->lds_inv);
+  if (e == hipSuccess && ndim == 3) e = axis_fwd_prepare(p->xMP, p->lds_axis);
+  if (e != hipSuccess) {
+    (void)hipFree(p->mem);
+    delete p;
+    return map_err(e);
+  }
+  *out = p;
+  return FNO_OK;
+}
+
+}  // extern "C"
+
+static size_t elem_bytes(int dtype) { return dtype == FNO_F32 ? 4 : 2; }
+
+static bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+static fno_status_t check_exec(fno_plan_t p, int ndim, const void *x, const void *w, void *y) {
+  if (!p || p->ndim != ndim) return FNO_ERR_INVALID_ARG;
+  if (!x || !w || !y) return FNO_ERR_INVALID_ARG;
+  if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y) & 15) return FNO_ERR_INVALID_ARG;
+  size_t pts = 1;
+  for (int d = 0; d < p->ndim; ++d) pts *= (size_t)p->grid[d];
+  const size_t es = elem_bytes(p->dtype);
+  const size_t nx = (size_t)p->B * p->Ci * pts * es, ny = (size_t)p->B * p->Co * pts * es;
+  const size_t nw = (size_t)p->K * p->Ci * p->Co * 2 * es;
+  if (overlap(x, nx, y, ny) || overlap(w, nw, y, ny)) return FNO_ERR_INVALID_ARG;
+  return FNO_OK;
+}
+
+static hipError_t run_one(fno_plan_t p, int kind, const void *x, const void *w, void *y, hipStream_t s) {
+  const int nd = p->ndim;
+  switch (kind) {
+    case L_FWD_PLANE: {
+      PlaneFwdArgs a;
+      a.x = x;
+      a.out = nd == 2 ? p->xh : p->tbuf;
+      a.tw_h = p->tw_h;
+      a.tw_w = p->tw_w;
+      a.nplanes = p->B * p->Ci * (nd == 3 ? p->xN : 1);
+      a.H = p->pH;
+      a.W = p->pW;
+      a.m1 = p->pm1;
+      a.m2 = p->pm2;
+      a.PH = p->pH / p->pMP;
+      a.PW = p->pW / p->pMP;
+      a.CH = plane_fwd_chunk_rows(p->pH, p->pW, p->pm1, p->pm2, p->pMP);
+      a.scale = nd == 2 ? 1.0f / ((float)p->pH * (float)p->pW) : 1.0f;
+      return launch_plane_fwd(a, p->pMP, p->dtype, p->lds_fwd, s);
+    }
+    case L_FWD_AXIS: {
+      AxisArgs a;
+      a.in = p->tbuf;
+      a.out = p->xh;
+      a.tw = p->tw_x;
+      a.nvol = p->B * p->Ci;
+      a.N = p->xN;
+      a.m = p->xm;
+      a.P = p->xN / p->xMP;
+      a.C = 2 * p->modes[1] * p->modes[2];
+      a.scale = 1.0f / ((float)p->grid[0] * (float)p->grid[1] * (float)p->grid[2]);
+      return launch_axis_fwd(a, p->xMP, p->lds_axis, s);
+    }
+    case L_CONTRACT: {
+      ContractArgs a;
+      a.xh = p->xh;
+      a.w = w;
+      a.yh = p->yh;
+      a.B = p->B;
+      a.Ci = p->Ci;
+      a.Co = p->Co;
+      a.K = p->K;
+      return launch_contract(a, p->bb, p->dtype, s);
+    }
+    case L_INV_AXIS: {
+      AxisArgs a;
+      a.in = p->yh;
+      a.out = p->tbuf;
+      a.tw = p->tw_x;
+      a.nvol = p->B * p->Co;
+      a.N = p->xN;
+      a.m = p->xm;
+      a.P = p->xN / p->xMP;
+      a.C = 2 * p->modes[1] * p->modes[2];
+      a.scale = 1.0f;
+      return launch_axis_inv(a, p->xMP, s);
+    }
+    case L_INV_PLANE: {
+      PlaneInvArgs a;
+      a.in = nd == 2 ? p->yh : p->tbuf;
+      a.y = y;
+      a.tw_h = p->tw_h;
+      a.tw_w = p->tw_w;
+      a.nplanes = p->B * p->Co * (nd == 3 ? p->xN : 1);
+      a.H = p->pH;
+      a.W = p->pW;
+      a.m1 = p->pm1;
+      a.m2 = p->pm2;
+      a.PH = p->pH / p->pMP;
+      a.PW = p->pW / p->pMP;
+      return launch_plane_inv(a, p->pMP, p->dtype, p->lds_inv, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+static const char *launch_name(int kind) {
+  switch (kind) {
+    case L_FWD_PLANE: return "fno_fwd_plane";
+    case L_FWD_AXIS: return "fno_fwd_axis";
+    case L_CONTRACT: return "fno_contract";
+    case L_INV_AXIS: return "fno_inv_axis";
+    case L_INV_PLANE: return "fno_inv_plane";
+  }
+  return "?";
+}
+
+static fno_status_t exec(fno_plan_t p, int ndim, const void *x, const void *w, void *y, void *stream, int only) {
+  fno_status_t st = check_exec(p, ndim, x, w, y);
+  if (st != FNO_OK) return st;
+  DeviceGuard g(p->device);
+  if (g.err != hipSuccess) return FNO_ERR_DEVICE;
+  hipStream_t s = (hipStream_t)stream;
+  for (size_t i = 0; i < p->launches.size(); ++i) {
+    if (only >= 0 && (int)i != only) continue;
+    hipError_t e = run_one(p, p->launches[i], x, w, y, s);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return map_err(e);
+  }
+  return FNO_OK;
+}
+
+extern "C" {
+
+fno_status_t fno_spectral_conv2d(fno_plan_t plan, const void *x, const void *w, void *y, void *stream) {
+  return exec(plan, 2, x, w, y, stream, -1);
+}
+
+fno_status_t fno_spectral_conv3d(fno_plan_t plan, const void *x, const void *w, void *y, void *stream) {
+  return exec(plan, 3, x, w, y, stream, -1);
+}
+
+fno_status_t fno_plan_workspace_bytes(fno_plan_t plan, size_t *bytes) {
+  if (!plan || !bytes) return FNO_ERR_INVALID_ARG;
+  *bytes = plan->ws_bytes;
+  return FNO_OK;
+}
+
+fno_status_t fno_plan_num_launches(fno_plan_t plan, int *n) {
+  if (!plan || !n) return FNO_ERR_INVALID_ARG;
+  *n = (int)plan->launches.size();
+  return FNO_OK;
+}
+
+fno_status_t fno_plan_launch_name(fno_plan_t plan, int index, const char **name) {
+  if (!plan || !name || index < 0 || index >= (int)plan->launches.size()) return FNO_ERR_INVALID_ARG;
+  *name = launch_name(plan->launches[index]);
+  return FNO_OK;
+}
+
+fno_status_t fno_plan_run_launch(fno_plan_t plan, int index, const void *x, const void *w, void *y,
+                                 void *stream) {
+  if (!plan || index < 0 || index >= (int)plan->launches.size()) return FNO_ERR_INVALID_ARG;
+  return exec(plan, plan->ndim, x, w, y, stream, index);
+}
+
+fno_status_t fno_plan_spectra(fno_plan_t plan, int which, void **ptr) {
+  if (!plan || !ptr || (which != 0 && which != 1)) return FNO_ERR_INVALID_ARG;
+  *ptr = which == 0 ? (void *)plan->xh : (void *)plan->yh;
+  return FNO_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,182 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle on the
+same seeded inputs. Bar: relative L2 over the compared output <= 1e-5 for
+fp32 storage, <= 3e-3 for fp16 / bf16 storage.
+
+* small and ragged shapes, compared element by element in full;
+* the five workload shapes at full size in the launch configuration the
+  benchmark times, compared on sampled batch elements (the oracle runs on
+  those samples only; batch elements are independent);
+* the intermediate spectra, determinism, launch structure and error paths.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import spectral_convolution_amd as fno
+import workloads as wl
+from gpu_util import TOL, read_spectra, rel_l2, run_layer, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg(name, ndim, B, Ci, Co, grid, modes, kind="grf", seed=11):
+    return wl.LayerConfig(name, ndim, B, Ci, Co, tuple(grid), tuple(modes), ("f32",), seed, kind)
+
+
+def _oracle(cfg, x64, w64):
+    if cfg.ndim == 2:
+        return oracle.spectral_conv2d(x64, w64, *cfg.modes)
+    return oracle.spectral_conv3d(x64, w64, *cfg.modes)
+
+
+SMALL = [
+    ("c0", wl.CONFIGS["c0"], "f32"),
+    ("c1-b2-f32", _cfg("c1s", 2, 2, 32, 32, (128, 128), (16, 16), seed=1), "f32"),
+    ("c1-b2-f16", _cfg("c1s", 2, 2, 32, 32, (128, 128), (16, 16), seed=1), "f16"),
+    ("c2-b1-f16", _cfg("c2s", 2, 1, 64, 64, (256, 256), (32, 32), seed=2), "f16"),
+    ("c2-b1-bf16", _cfg("c2s", 2, 1, 64, 64, (256, 256), (32, 32), seed=2), "bf16"),
+    ("c3-b1-f32", _cfg("c3s", 3, 1, 32, 32, (64, 64, 64), (16, 16, 16), seed=3), "f32"),
+    # ragged: odd channel counts and batch, non-square grids, modes that are
+    # not powers of two, the smallest and the largest register FFT
+    ("rag2d-a", _cfg("r", 2, 3, 5, 3, (32, 64), (5, 3), "uniform"), "f32"),
+    ("rag2d-b", _cfg("r", 2, 5, 1, 7, (64, 32), (16, 9), "uniform"), "f16"),
+    ("rag2d-m1", _cfg("r", 2, 2, 2, 2, (8, 8), (1, 1), "uniform"), "f32"),
+    ("rag2d-max", _cfg("r", 2, 2, 3, 2, (16, 16), (8, 8), "uniform"), "f32"),
+    ("rag2d-tall", _cfg("r", 2, 2, 4, 6, (256, 64), (3, 32), "uniform"), "bf16"),
+    ("rag2d-wide", _cfg("r", 2, 17, 3, 19, (64, 256), (7, 24), "uniform"), "f32"),
+    ("rag3d-a", _cfg("r", 3, 2, 3, 5, (16, 32, 16), (3, 5, 2), "uniform"), "f32"),
+    ("rag3d-b", _cfg("r", 3, 1, 4, 4, (8, 8, 8), (4, 4, 4), "uniform"), "f16"),
+    ("rag3d-c", _cfg("r", 3, 3, 2, 1, (32, 16, 64), (16, 8, 5), "uniform"), "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_parity_small(case):
+    name, cfg, dtype = case
+    print(f"[parity] {name} dtype={dtype} grid={cfg.grid} modes={cfg.modes}", flush=True)
+    inp = wl.layer_inputs(cfg, dtype)
+    got, _ = run_layer(cfg.ndim, cfg.batch, cfg.c_in, cfg.c_out, cfg.grid, cfg.modes, dtype,
+                       inp["x"], inp["w"])
+    ref = _oracle(cfg, inp["x64"], inp["w64"])
+    err = rel_l2(got, ref)
+    print(f"[parity] {name} rel_l2={err:.3e}", flush=True)
+    assert err <= TOL[dtype], f"{name}: rel L2 {err:.3e} > {TOL[dtype]}"
+
+
+FULL = [("c1", "f32", (0, 15)), ("c1", "f16", (0, 15)), ("c2", "f16", (0, 31)),
+        ("c2", "bf16", (0, 31)), ("c3", "f32", (0, 3))]
+
+
+@pytest.mark.parametrize("case", FULL, ids=[f"{c[0]}-{c[1]}" for c in FULL])
+def test_parity_full_size_sampled(case):
+    name, dtype, samples = case
+    cfg = wl.CONFIGS[name]
+    print(f"[parity-full] {name} {dtype} B={cfg.batch} samples={samples}", flush=True)
+    inp = wl.layer_inputs(cfg, dtype)
+    got, _ = run_layer(cfg.ndim, cfg.batch, cfg.c_in, cfg.c_out, cfg.grid, cfg.modes, dtype,
+                       inp["x"], inp["w"])
+    idx = list(samples)
+    ref = _oracle(cfg, inp["x64"][idx], inp["w64"])
+    err = rel_l2(got[idx], ref)
+    print(f"[parity-full] {name} {dtype} rel_l2={err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+    assert np.isfinite(got).all()
+
+
+def test_intermediate_spectra():
+    cfg = _cfg("s", 2, 2, 3, 4, (64, 128), (6, 11), "uniform")
+    inp = wl.layer_inputs(cfg, "f32")
+    _, plan = run_layer(2, 2, 3, 4, cfg.grid, cfg.modes, "f32", inp["x"], inp["w"],
+                        plan=fno.fno_plan_create(2, 2, 3, 4, cfg.grid, cfg.modes, "f32", 0))
+    try:
+        xh = read_spectra(plan, 0).reshape(2, 3, 12, 11)
+        ref = oracle.forward2d(inp["x64"], *cfg.modes) / (64 * 128)
+        assert rel_l2(xh, ref) <= 1e-6
+        yh = read_spectra(plan, 1).reshape(2, 4, 12, 11)
+        ref_y = oracle.contract(ref, inp["w64"])
+        assert rel_l2(yh, ref_y) <= 1e-6
+    finally:
+        fno.fno_plan_destroy(plan)
+
+
+def test_intermediate_spectra_3d():
+    cfg = _cfg("s", 3, 1, 2, 3, (16, 32, 16), (4, 6, 3), "uniform")
+    inp = wl.layer_inputs(cfg, "f32")
+    plan = fno.fno_plan_create(3, 1, 2, 3, cfg.grid, cfg.modes, "f32", 0)
+    try:
+        run_layer(3, 1, 2, 3, cfg.grid, cfg.modes, "f32", inp["x"], inp["w"], plan=plan)
+        xh = read_spectra(plan, 0).reshape(1, 2, 8, 12, 3)
+        ref = oracle.forward3d(inp["x64"], *cfg.modes) / (16 * 32 * 16)
+        assert rel_l2(xh, ref) <= 1e-6
+    finally:
+        fno.fno_plan_destroy(plan)
+
+
+def test_deterministic_bitwise():
+    cfg = wl.CONFIGS["c0"]
+    inp = wl.layer_inputs(cfg, "f32")
+    a, _ = run_layer(2, 2, 4, 4, cfg.grid, cfg.modes, "f32", inp["x"], inp["w"])
+    b, _ = run_layer(2, 2, 4, 4, cfg.grid, cfg.modes, "f32", inp["x"], inp["w"])
+    assert np.array_equal(a, b)
+
+
+def test_launch_structure():
+    p2 = fno.fno_plan_create(2, 2, 4, 4, (16, 16), (4, 4), "f32", 0)
+    p3 = fno.fno_plan_create(3, 1, 2, 2, (8, 8, 8), (2, 2, 2), "f32", 0)
+    try:
+        assert [fno.fno_plan_launch_name(p2, i) for i in range(fno.fno_plan_num_launches(p2))] == \
+            ["fno_fwd_plane", "fno_contract", "fno_inv_plane"]
+        assert fno.fno_plan_num_launches(p3) == 5
+        assert fno.fno_plan_workspace_bytes(p2) > 0
+    finally:
+        fno.fno_plan_destroy(p2)
+        fno.fno_plan_destroy(p3)
+
+
+def test_execution_argument_errors():
+    import torch
+    plan = fno.fno_plan_create(2, 2, 4, 4, (16, 16), (4, 4), "f32", 0)
+    L = fno.lib()
+    try:
+        x = torch.zeros((2 * 4 * 16 * 16 + 64,), device="cuda:0")
+        y = torch.zeros((2 * 4 * 16 * 16 + 64,), device="cuda:0")
+        w = torch.zeros((8 * 4 * 4 * 4 * 2,), device="cuda:0")
+        xp, yp, wp = x.data_ptr(), y.data_ptr(), w.data_ptr()
+        s = torch.cuda.current_stream().cuda_stream
+        assert L.fno_spectral_conv2d(plan.handle, xp + 4, wp, yp, s) == 1   # misaligned
+        assert L.fno_spectral_conv2d(plan.handle, xp, wp, xp + 64, s) == 1  # x / y overlap
+        assert L.fno_spectral_conv2d(plan.handle, xp, None, yp, s) == 1     # NULL
+        assert L.fno_spectral_conv3d(plan.handle, xp, wp, yp, s) == 1       # wrong ndim
+        assert L.fno_plan_run_launch(plan.handle, 7, xp, wp, yp, s) == 1    # bad index
+        assert L.fno_spectral_conv2d(plan.handle, xp, wp, yp, s) == 0
+        torch.cuda.synchronize()
+    finally:
+        fno.fno_plan_destroy(plan)
+
+
+def test_plan_device_out_of_range():
+    h = ctypes.c_void_p()
+    g = (ctypes.c_int * 2)(16, 16)
+    m = (ctypes.c_int * 2)(4, 4)
+    assert fno.lib().fno_plan_create(ctypes.byref(h), 2, 1, 1, 1, g, m, 0, 1000) == 1
+
+
+def test_binding_rejects_wrong_tensors():
+    import torch
+    plan = fno.fno_plan_create(2, 2, 4, 4, (16, 16), (4, 4), "f16", 0)
+    try:
+        x = torch.zeros(plan.x_shape(), dtype=torch.float32, device="cuda:0")
+        w = torch.zeros(plan.w_shape(), dtype=torch.float16, device="cuda:0")
+        y = torch.zeros(plan.y_shape(), dtype=torch.float16, device="cuda:0")
+        with pytest.raises(ValueError):
+            fno.fno_spectral_conv2d(plan, x, w, y)
+        with pytest.raises(ValueError):
+            fno.fno_spectral_conv2d(plan, x.half()[:1], w, y)
+        fno.fno_spectral_conv2d(plan, to_device(np.zeros(plan.x_shape(), np.float16), "f16"), w, y)
+        torch.cuda.synchronize()
+        assert float(y.float().abs().max()) == 0.0
+    finally:
+        fno.fno_plan_destroy(plan)
