@@ -136,6 +136,17 @@ def measure(cfg, dtype, steps, warmup, per_kernel=True):
         lay.close()
 
 
+def copy_bandwidth(nbytes, steps=20, warmup=3):
+    """Device-to-device copy of nbytes (read + write counted): the achievable
+    HBM rate on this machine, and a plain copy kernel of known size for scaling
+    hardware byte counters."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    ms = _time_loop(lambda i: dst.copy_(src), steps, warmup, torch.cuda.current_stream())
+    return {"bytes_copied": nbytes, "ms": ms, "gbps": 2 * nbytes / (ms * 1e-3) / 1e9}
+
+
 def cpu_baseline(cfg, dtype, min_seconds=10.0):
     """The float64 oracle on this host's cores, repeated for ~min_seconds."""
     import oracle
@@ -168,6 +179,8 @@ def main():
     ap.add_argument("--dtype", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--copy-only", type=int, default=0, metavar="BYTES",
+                    help="only time a device-to-device copy of BYTES (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -179,6 +192,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU available", file=sys.stderr)
         sys.exit(1)
+    if args.copy_only:
+        print(json.dumps({"copy": copy_bandwidth(args.copy_only, args.steps, args.warmup)}))
+        return
     cfg = wl.CONFIGS[args.config]
     dtype = args.dtype or cfg.dtypes[0]
     main_res = measure(cfg, dtype, args.steps, args.warmup)
@@ -209,6 +225,7 @@ def main():
             print(f"[bench] {name} {dt}: {r['layers_per_s']:.1f} layers/s, {r['gbps']:.0f} GB/s",
                   file=sys.stderr, flush=True)
         out["configs"] = extra
+    out["copy_1gib"] = copy_bandwidth(1 << 30)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, dtype)
     print(json.dumps(out), flush=True)

@@ -125,6 +125,59 @@ fno_status_t fno_plan_run_launch(fno_plan_t plan, int index, const void *x,
  * modes ordered as in w. Valid after an execution call has finished. */
 fno_status_t fno_plan_spectra(fno_plan_t plan, int which, void **ptr);
 
+/* ---- the full FNO2d network ---------------------------------------------
+ * The layer inside its model (TurboFNO write-up, sections 1 and 4.3: the
+ * fused layer drops into an FNO module): lift Linear, n_layers blocks of
+ * GELU(spectral conv + 1x1 conv + bias), projection Linear -> GELU -> Linear.
+ * Activations are stored in the storage dtype; arithmetic is fp32. GELU is
+ * the exact erf form 0.5 v (1 + erf(v / sqrt 2)). */
+
+/* Per-pixel channel mix:
+ *   y[b][o][p] = act(sum_i A[o][i] x[b][i][p] + bias[o] + add[b][o][p])
+ * x [batch][c_in][pixels], A [c_out][c_in], bias [c_out] (NULL: none),
+ * add [batch][c_out][pixels] (NULL: none), y [batch][c_out][pixels]; all in
+ * `dtype` on the current device; act: 0 none, 1 GELU. y must not overlap x
+ * or add. c_in <= 128. Asynchronous on `stream`. */
+fno_status_t fno_channel_mix(const void *x, const void *A, const void *bias,
+                             const void *add, void *y, int batch, int c_in,
+                             int c_out, long pixels, int act,
+                             fno_dtype_t dtype, void *stream);
+
+/* Per-pixel projection:
+ *   y[b][c][p] = sum_j Q2[c][j] GELU(sum_i Q1[j][i] x[b][i][p] + q1[j]) + q2[c]
+ * Q1 [hidden][c_in], q1 [hidden], Q2 [c_out][hidden], q2 [c_out].
+ * c_in <= 64, hidden <= 128, c_out <= 4. */
+fno_status_t fno_projection(const void *x, const void *Q1, const void *q1,
+                            const void *Q2, const void *q2, void *y, int batch,
+                            int c_in, int hidden, int c_out, long pixels,
+                            fno_dtype_t dtype, void *stream);
+
+typedef struct fno_model2d_s *fno_model2d_t;
+
+/* Plan of the network on [batch][in_channels][height][width] inputs with
+ * `channels` hidden channels, spectral modes (m1, m2) in every block,
+ * `proj_channels` hidden units in the projection, `out_channels` outputs.
+ * Owns a spectral-conv plan and three activation buffers of
+ * batch*channels*height*width elements. */
+fno_status_t fno_model2d_create(fno_model2d_t *model, int batch, int height,
+                                int width, int in_channels, int channels,
+                                int n_layers, int m1, int m2,
+                                int proj_channels, int out_channels,
+                                fno_dtype_t dtype, int device);
+
+/* Forward pass. features [batch][in_channels][height][width]; out
+ * [batch][out_channels][height][width]; params: 2 + 3*n_layers + 4 device
+ * pointers in this order: P [channels][in_channels], p [channels], then per
+ * block (spectral weights as fno_spectral_conv2d's w, W [channels][channels],
+ * b [channels]), then Q1 [proj][channels], q1 [proj], Q2 [out][proj],
+ * q2 [out]. params itself is a host array. One call in flight per model. */
+fno_status_t fno_model2d_forward(fno_model2d_t model, const void *features,
+                                 const void *const *params, void *out,
+                                 void *stream);
+
+/* Free the model (synchronises its device). NULL is a no-op. */
+fno_status_t fno_model2d_destroy(fno_model2d_t model);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,6 +15,8 @@ __all__ = [
     "fno_plan_destroy", "fno_status_string", "fno_plan_workspace_bytes",
     "fno_plan_num_launches", "fno_plan_launch_name", "fno_plan_run_launch",
     "fno_plan_spectra", "SpectralConv", "FnoError", "DTYPES",
+    "fno_channel_mix", "fno_projection", "fno_model2d_create", "fno_model2d_forward",
+    "fno_model2d_destroy", "Model2d",
 ]
 
 
@@ -173,3 +175,72 @@ class SpectralConv:
             self.close()
         except Exception:
             pass
+
+
+# ------------------------------------------------------------ FNO2d network
+
+def _dtype_of(t):
+    import torch
+    return {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[t.dtype]
+
+
+def fno_channel_mix(x, A, bias, add, y, act=0, stream=None):
+    """y[b][o][p] = act(sum_i A[o][i] x[b][i][p] + bias[o] + add[b][o][p]);
+    x [B][Ci][...], y [B][Co][...] (trailing dims flattened to pixels)."""
+    B, Ci = x.shape[0], x.shape[1]
+    Co = y.shape[1]
+    P = x[0, 0].numel()
+    dt = _dtype_of(x)
+    check(lib().fno_channel_mix(_ptr(x), _ptr(A), _ptr(bias), _ptr(add), _ptr(y), B, Ci, Co, P, act,
+                                DTYPES[dt], _stream(stream, x.device.index or 0)), "fno_channel_mix")
+
+
+def fno_projection(x, Q1, q1, Q2, q2, y, stream=None):
+    """y[b][c][p] = sum_j Q2[c][j] GELU(sum_i Q1[j][i] x[b][i][p] + q1[j]) + q2[c]."""
+    B, Ci = x.shape[0], x.shape[1]
+    J, C = Q1.shape[0], Q2.shape[0]
+    P = x[0, 0].numel()
+    dt = _dtype_of(x)
+    check(lib().fno_projection(_ptr(x), _ptr(Q1), _ptr(q1), _ptr(Q2), _ptr(q2), _ptr(y), B, Ci, J, C, P,
+                               DTYPES[dt], _stream(stream, x.device.index or 0)), "fno_projection")
+
+
+class Model2d:
+    """Handle of a C FNO2d model plan plus its shape."""
+
+    def __init__(self, handle, batch, grid, in_channels, channels, n_layers, modes, proj_channels,
+                 out_channels, dtype, device):
+        self.handle = handle
+        self.batch, self.grid, self.in_channels, self.channels = batch, tuple(grid), in_channels, channels
+        self.n_layers, self.modes, self.proj_channels = n_layers, tuple(modes), proj_channels
+        self.out_channels, self.dtype, self.device = out_channels, dtype, device
+
+    def n_params(self):
+        return 2 + 3 * self.n_layers + 4
+
+
+def fno_model2d_create(batch, grid, in_channels, channels, n_layers, modes, proj_channels, out_channels,
+                       dtype="f16", device=0):
+    h = ctypes.c_void_p()
+    check(lib().fno_model2d_create(ctypes.byref(h), batch, grid[0], grid[1], in_channels, channels, n_layers,
+                                   modes[0], modes[1], proj_channels, out_channels, DTYPES[dtype], device),
+          "fno_model2d_create")
+    return Model2d(h, batch, grid, in_channels, channels, n_layers, modes, proj_channels, out_channels,
+                   dtype, device)
+
+
+def fno_model2d_forward(model, features, params, out, stream=None):
+    """params: list of device tensors in the documented order
+    [P, p, (spectral w, W, b) * n_layers, Q1, q1, Q2, q2]."""
+    if len(params) != model.n_params():
+        raise ValueError(f"expected {model.n_params()} parameter tensors, got {len(params)}")
+    arr = (ctypes.c_void_p * len(params))(*[_ptr(t) for t in params])
+    check(lib().fno_model2d_forward(model.handle, _ptr(features), arr, _ptr(out),
+                                    _stream(stream, model.device)), "fno_model2d_forward")
+
+
+def fno_model2d_destroy(model):
+    if model is None or model.handle is None:
+        return
+    check(lib().fno_model2d_destroy(model.handle), "fno_model2d_destroy")
+    model.handle = None

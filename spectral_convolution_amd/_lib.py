@@ -26,6 +26,15 @@ SIGNATURES = {
     "fno_plan_launch_name": (_c_int, [_c_void_p, _c_int, ctypes.POINTER(ctypes.c_char_p)]),
     "fno_plan_run_launch": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "fno_plan_spectra": (_c_int, [_c_void_p, _c_int, ctypes.POINTER(_c_void_p)]),
+    "fno_channel_mix": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
+                                 _c_int, ctypes.c_long, _c_int, _c_int, _c_void_p]),
+    "fno_projection": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
+                                _c_int, _c_int, _c_int, ctypes.c_long, _c_int, _c_void_p]),
+    "fno_model2d_create": (_c_int, [ctypes.POINTER(_c_void_p), _c_int, _c_int, _c_int, _c_int, _c_int,
+                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "fno_model2d_forward": (_c_int, [_c_void_p, _c_void_p, ctypes.POINTER(_c_void_p), _c_void_p,
+                                     _c_void_p]),
+    "fno_model2d_destroy": (_c_int, [_c_void_p]),
 }
 
 _lib = None

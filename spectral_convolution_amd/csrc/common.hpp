@@ -112,6 +112,18 @@ hipError_t axis_fwd_prepare(int MP, size_t lds);
 hipError_t launch_axis_fwd(const AxisArgs &a, int MP, size_t lds, hipStream_t s);
 hipError_t launch_axis_inv(const AxisArgs &a, int MP, hipStream_t s);
 int contract_pick_bb(int B, int Co, int K);
-hipError_t launch_contract(const ContractArgs &a, int bb, int dtype, hipStream_t s);
+int contract_pick_split(int B, int Ci, int Co, int K, int bb);
+size_t contract_lds_bytes(int bb, int S);
+hipError_t contract_prepare(int bb, int dtype, size_t lds);
+hipError_t launch_contract(const ContractArgs &a, int bb, int S, int dtype, hipStream_t s);
+
+hipError_t launch_channel_mix(const void *x, const void *A, const void *bias, const void *add, void *y, int B,
+                              int I, int O, long P, int act, int dtype, hipStream_t s);
+hipError_t launch_projection(const void *x, const void *Q1, const void *q1, const void *Q2, const void *q2, void *y,
+                             int B, int I, int J, int C, long P, int dtype, hipStream_t s);
+constexpr int kMixMaxIn = 128;   // channel mix: input channels
+constexpr int kProjMaxIn = 64;   // projection: input channels
+constexpr int kProjMaxHidden = 128;
+constexpr int kProjMaxOut = 4;
 
 }  // namespace fno

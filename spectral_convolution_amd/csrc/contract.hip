@@ -58,18 +58,61 @@ __device__ __forceinline__ void load_w4(const void *w, size_t idx, int nvalid, f
   }
 }
 
+template <int BB>
+struct Frag {
+  float ar[BB], ai[BB], an[BB];
+  float wr[4], wi[4];
+};
+
 template <int BB, int DT>
-__global__ __launch_bounds__(64) void fno_contract(ContractArgs a) {
-  const int lane = threadIdx.x;
+__device__ __forceinline__ void load_frag(const ContractArgs &a, int i, int mode, bool mode_ok, int b0, int nn,
+                                          int ol, int nw, bool vec, Frag<BB> &f) {
+  const int K = a.K, Ci = a.Ci, Co = a.Co, B = a.B;
+#pragma unroll
+  for (int bb = 0; bb < BB; ++bb) {
+    const int b = b0 + 4 * bb + nn;
+    float2 xv = make_float2(0.f, 0.f);
+    if (mode_ok && b < B) xv = a.xh[((size_t)b * Ci + i) * K + mode];
+    f.ar[bb] = xv.x;
+    f.ai[bb] = xv.y;
+  }
+  const size_t widx = ((size_t)(mode_ok ? mode : 0) * Ci + i) * Co + ol;
+  if (vec) {
+    load_w4<DT>(a.w, widx, nw, f.wr, f.wi);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < nw) {
+        const float2 v = load_pair<DT>(a.w, 2 * (widx + t));
+        f.wr[t] = v.x;
+        f.wi[t] = v.y;
+      } else {
+        f.wr[t] = 0.f;
+        f.wi[t] = 0.f;
+      }
+    }
+  }
+}
+
+// The input-channel sum is split over the S waves of a workgroup (wave s
+// takes channels [s*Ci/S, (s+1)*Ci/S)); each wave prefetches the operands of
+// its next channel while the MFMAs of the current one run. Partial sums meet
+// in LDS and wave 0 adds them in wave order, so results do not depend on
+// timing.
+template <int BB, int DT>
+__global__ __launch_bounds__(512) void fno_contract(ContractArgs a) {
+  extern __shared__ float red[];
+  const int lane = threadIdx.x & 63, s = threadIdx.x >> 6, S = blockDim.x >> 6;
   const int blk = lane >> 2, nn = lane & 3;
   const int K = a.K, Ci = a.Ci, Co = a.Co, B = a.B;
   const int mode = blockIdx.x * 16 + blk;
   const int b0 = blockIdx.y * 4 * BB;
   const int o0 = blockIdx.z * 16;
   const bool mode_ok = mode < K;
-  const int ol = o0 + 4 * nn;                   // first of this lane's 4 output channels
+  const int ol = o0 + 4 * nn;  // first of this lane's 4 output channels
   const int nw = mode_ok ? min(4, max(0, Co - ol)) : 0;
   const bool vec = (Co & 3) == 0;
+  const int i0 = (Ci * s) / S, i1 = (Ci * (s + 1)) / S;
 
   v4f accr[BB][4], acci[BB][4];
 #pragma unroll
@@ -80,43 +123,53 @@ __global__ __launch_bounds__(64) void fno_contract(ContractArgs a) {
       acci[bb][ob] = v4f{0.f, 0.f, 0.f, 0.f};
     }
 
-  for (int i = 0; i < Ci; ++i) {
-    float ar[BB], ai[BB], an[BB];
+  Frag<BB> cur, nxt;
+  if (i0 < i1) load_frag<BB, DT>(a, i0, mode, mode_ok, b0, nn, ol, nw, vec, cur);
+  for (int i = i0; i < i1; ++i) {
+    if (i + 1 < i1) load_frag<BB, DT>(a, i + 1, mode, mode_ok, b0, nn, ol, nw, vec, nxt);
 #pragma unroll
-    for (int bb = 0; bb < BB; ++bb) {
-      const int b = b0 + 4 * bb + nn;
-      float2 xv = make_float2(0.f, 0.f);
-      if (mode_ok && b < B) xv = a.xh[((size_t)b * Ci + i) * K + mode];
-      ar[bb] = xv.x;
-      ai[bb] = xv.y;
-      an[bb] = -xv.y;
-    }
-    float wr[4], wi[4];
-    const size_t widx = ((size_t)mode * Ci + i) * Co + ol;
-    if (vec) {
-      load_w4<DT>(a.w, widx, nw, wr, wi);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (t < nw) {
-          const float2 v = load_pair<DT>(a.w, 2 * (widx + t));
-          wr[t] = v.x;
-          wi[t] = v.y;
-        } else {
-          wr[t] = 0.f;
-          wi[t] = 0.f;
-        }
-      }
-    }
+    for (int bb = 0; bb < BB; ++bb) cur.an[bb] = -cur.ai[bb];
 #pragma unroll
     for (int bb = 0; bb < BB; ++bb)
 #pragma unroll
       for (int ob = 0; ob < 4; ++ob) {
-        accr[bb][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(ar[bb], wr[ob], accr[bb][ob], 0, 0, 0);
-        accr[bb][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(an[bb], wi[ob], accr[bb][ob], 0, 0, 0);
-        acci[bb][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(ar[bb], wi[ob], acci[bb][ob], 0, 0, 0);
-        acci[bb][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(ai[bb], wr[ob], acci[bb][ob], 0, 0, 0);
+        accr[bb][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(cur.ar[bb], cur.wr[ob], accr[bb][ob], 0, 0, 0);
+        accr[bb][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(cur.an[bb], cur.wi[ob], accr[bb][ob], 0, 0, 0);
+        acci[bb][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(cur.ar[bb], cur.wi[ob], acci[bb][ob], 0, 0, 0);
+        acci[bb][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(cur.ai[bb], cur.wr[ob], acci[bb][ob], 0, 0, 0);
       }
+    cur = nxt;
+  }
+
+  if (S > 1) {
+    // partial sums of waves 1..S-1 -> LDS [wave-1][reg][lane]
+    constexpr int NR = BB * 4 * 8;
+    if (s > 0) {
+      float *dst = red + (size_t)(s - 1) * NR * 64 + lane;
+#pragma unroll
+      for (int bb = 0; bb < BB; ++bb)
+#pragma unroll
+        for (int ob = 0; ob < 4; ++ob)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            dst[((bb * 4 + ob) * 8 + j) * 64] = accr[bb][ob][j];
+            dst[((bb * 4 + ob) * 8 + 4 + j) * 64] = acci[bb][ob][j];
+          }
+    }
+    __syncthreads();
+    if (s > 0) return;
+    for (int w = 1; w < S; ++w) {
+      const float *src = red + (size_t)(w - 1) * NR * 64 + lane;
+#pragma unroll
+      for (int bb = 0; bb < BB; ++bb)
+#pragma unroll
+        for (int ob = 0; ob < 4; ++ob)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            accr[bb][ob][j] += src[((bb * 4 + ob) * 8 + j) * 64];
+            acci[bb][ob][j] += src[((bb * 4 + ob) * 8 + 4 + j) * 64];
+          }
+    }
   }
 
   // accumulator register j of lane l holds block l/4, row j, column l%4
@@ -156,12 +209,29 @@ static const void *contract_kernel(int dtype) {
   return nullptr;
 }
 
-hipError_t launch_contract(const ContractArgs &a, int bb, int dtype, hipStream_t s) {
+int contract_pick_split(int B, int Ci, int Co, int K, int bb) {
+  // waves per workgroup sharing one output tile: enough waves in flight to
+  // fill the chip, at least two input channels per wave
+  const long waves = (long)((K + 15) / 16) * ((Co + 15) / 16) * ((B + 4 * bb - 1) / (4 * bb));
+  int S = 1;
+  while (waves * S < 2048 && S < 8 && Ci >= 4 * S) S *= 2;
+  return S;
+}
+
+size_t contract_lds_bytes(int bb, int S) { return (size_t)(S - 1) * bb * 32 * 64 * sizeof(float); }
+
+hipError_t contract_prepare(int bb, int dtype, size_t lds) {
+  const void *k = bb == 4 ? contract_kernel<4>(dtype) : bb == 2 ? contract_kernel<2>(dtype) : contract_kernel<1>(dtype);
+  if (!k) return hipErrorInvalidValue;
+  return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+hipError_t launch_contract(const ContractArgs &a, int bb, int S, int dtype, hipStream_t s) {
   const void *k = bb == 4 ? contract_kernel<4>(dtype) : bb == 2 ? contract_kernel<2>(dtype) : contract_kernel<1>(dtype);
   if (!k) return hipErrorInvalidValue;
   dim3 grid((a.K + 15) / 16, (a.B + 4 * bb - 1) / (4 * bb), (a.Co + 15) / 16);
   void *args[] = {(void *)&a};
-  return hipLaunchKernel(k, grid, dim3(64), args, 0, s);
+  return hipLaunchKernel(k, grid, dim3(64 * S), args, contract_lds_bytes(bb, S), s);
 }
 
 }  // namespace fno

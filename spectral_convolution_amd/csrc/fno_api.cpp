@@ -75,7 +75,7 @@ struct fno_plan_s {
   // 3D outer axis
   int xN = 0, xm = 0, xMP = 0;
   size_t lds_axis = 0;
-  int bb = 1;
+  int bb = 1, split = 1;
   float2 *tw_h = nullptr, *tw_w = nullptr, *tw_x = nullptr;
   float2 *xh = nullptr, *yh = nullptr, *tbuf = nullptr;
   void *mem = nullptr;
@@ -147,6 +147,7 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
   if (planes > 0x7fffffffL || (double)batch * (c_in > c_out ? c_in : c_out) * pts > 1e12)
     return FNO_ERR_UNSUPPORTED;
   p.bb = contract_pick_bb(batch, c_out, p.K);
+  p.split = contract_pick_split(batch, c_in, c_out, p.K, p.bb);
   if (ndim == 2) {
     p.launches = {L_FWD_PLANE, L_CONTRACT, L_INV_PLANE};
   } else {
@@ -267,6 +268,7 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   if (e == hipSuccess) e = plane_fwd_prepare(p->pMP, p->dtype, p->lds_fwd);
   if (e == hipSuccess) e = plane_inv_prepare(p->pMP, p->dtype, p->lds_inv);
   if (e == hipSuccess && ndim == 3) e = axis_fwd_prepare(p->xMP, p->lds_axis);
+  if (e == hipSuccess) e = contract_prepare(p->bb, p->dtype, contract_lds_bytes(p->bb, p->split));
   if (e != hipSuccess) {
     (void)hipFree(p->mem);
     delete p;
@@ -340,7 +342,7 @@ static hipError_t run_one(fno_plan_t p, int kind, const void *x, const void *w, 
       a.Ci = p->Ci;
       a.Co = p->Co;
       a.K = p->K;
-      return launch_contract(a, p->bb, p->dtype, s);
+      return launch_contract(a, p->bb, p->split, p->dtype, s);
     }
     case L_INV_AXIS: {
       AxisArgs a;

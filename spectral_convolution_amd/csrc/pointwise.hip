@@ -1,0 +1,281 @@
+// pointwise.hip - per-pixel channel mixing for the full FNO2d network.
+//
+// The network around the spectral layer (TurboFNO write-up, sections 1 and
+// 4.3: the fused layer replaces the spectral convolution inside an FNO
+// model): a lifting Linear, per block a 1x1 convolution added to the
+// spectral branch followed by GELU, and a two-Linear projection with GELU
+// between them.
+//
+// Both kernels are per-pixel GEMMs on v_mfma_f32_16x16x4f32 in the natural
+// [B][C][pixels] layout: the B operand of the MFMA holds one channel x 16
+// pixels per 16-lane group, so every activation load and store is a
+// contiguous run of pixels of one channel. A lane owns 4 consecutive pixels
+// (one per MFMA "t"), 16 lanes span 64 pixels. Weights are converted to fp32
+// once per workgroup into LDS. Accumulation is fp32; outputs are rounded
+// (RNE) to the storage dtype.
+
+#include "common.hpp"
+
+namespace fno {
+
+// y[b][o][p] = act(sum_i A[o][i] x[b][i][p] + bias[o] + add[b][o][p])
+struct MixArgs {
+  const void *x, *A, *bias, *add;
+  void *y;
+  int B, I, O;
+  long P;
+  int act;  // 0: none, 1: GELU
+};
+
+// y[b][c][p] = sum_j Q2[c][j] GELU(sum_i Q1[j][i] x[b][i][p] + q1[j]) + q2[c]
+struct ProjArgs {
+  const void *x, *Q1, *q1, *Q2, *q2;
+  void *y;
+  int B, I, J, C;
+  long P;
+};
+
+template <int DT>
+__device__ __forceinline__ float load1(const void *p, size_t i) {
+  if constexpr (DT == DT_F32) return reinterpret_cast<const float *>(p)[i];
+  else if constexpr (DT == DT_F16) return (float)reinterpret_cast<const _Float16 *>(p)[i];
+  else return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(p)[i] << 16);
+}
+
+// four consecutive elements p[i..i+3]: one vector access when all four are in
+// range and the run is 4-element aligned (al), else element by element
+template <int DT>
+__device__ __forceinline__ void load4(const void *p, size_t i, int n, bool al, float (&v)[4]) {
+  if (n >= 4 && al) {
+    if constexpr (DT == DT_F32) {
+      const float4 u = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(p) + i);
+      v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+    } else {
+      const uint2 u = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(p) + i);
+      if constexpr (DT == DT_F16) {
+        const half2_t h0 = __builtin_bit_cast(half2_t, u.x), h1 = __builtin_bit_cast(half2_t, u.y);
+        v[0] = (float)h0.x; v[1] = (float)h0.y; v[2] = (float)h1.x; v[3] = (float)h1.y;
+      } else {
+        v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+        v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[t] = t < n ? load1<DT>(p, i + t) : 0.f;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store4(void *p, size_t i, int n, bool al, const float (&v)[4]) {
+  if (n >= 4 && al) {
+    store_pair<DT>(p, i, v[0], v[1]);
+    store_pair<DT>(p, i + 2, v[2], v[3]);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < n) {
+        if constexpr (DT == DT_F32) reinterpret_cast<float *>(p)[i + t] = v[t];
+        else if constexpr (DT == DT_F16) reinterpret_cast<_Float16 *>(p)[i + t] = (_Float16)v[t];
+        else reinterpret_cast<uint16_t *>(p)[i + t] = (uint16_t)f32_to_bf16(v[t]);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ float gelu(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+
+static constexpr int kPwThreads = 256;
+static constexpr int kMaxI = 128;   // input channels held per workgroup
+static constexpr int kOB = 64;      // output channels per workgroup (4 MFMA row tiles)
+
+// Rows of A (o0 .. o0+63) x all I input channels, fp32, padded to a multiple
+// of 4 channels with zeros: [kOB][Ipad].
+template <int DT>
+__device__ void stage_weights(const void *A, int O, int I, int o0, int Ipad, float *w) {
+  for (int v = threadIdx.x; v < kOB * Ipad; v += kPwThreads) {
+    const int o = v / Ipad, i = v - o * Ipad;
+    w[v] = (o0 + o < O && i < I) ? load1<DT>(A, (size_t)(o0 + o) * I + i) : 0.f;
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kPwThreads) void fno_channel_mix(MixArgs a) {
+  __shared__ float w[kOB * kMaxI];
+  __shared__ float bias[kOB];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int o0 = blockIdx.y * kOB, b = blockIdx.z;
+  const int I = a.I, O = a.O;
+  const long P = a.P;
+  const int Ipad = (I + 3) & ~3;
+  stage_weights<DT>(a.A, O, I, o0, Ipad, w);
+  for (int v = threadIdx.x; v < kOB; v += kPwThreads)
+    bias[v] = (a.bias && o0 + v < O) ? load1<DT>(a.bias, o0 + v) : 0.f;
+  __syncthreads();
+
+  const int kr = lane >> 4, n = lane & 15;
+  const bool al = (P & 3) == 0;
+  const size_t xb = (size_t)b * I * P, yb = (size_t)b * O * P;
+  const long ntiles = (P + 63) / 64;
+  for (long tile = (long)blockIdx.x * 4 + wv; tile < ntiles; tile += (long)gridDim.x * 4) {
+    const long p0 = tile * 64 + 4 * n;
+    const int np = (int)min((long)4, max(0L, P - p0));
+    v4f acc[4][4];
+#pragma unroll
+    for (int mo = 0; mo < 4; ++mo)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[mo][t] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < Ipad; k0 += 4) {
+      const int i = k0 + kr;
+      float xv[4];
+      load4<DT>(a.x, xb + (size_t)(i < I ? i : 0) * P + p0, i < I ? np : 0, al, xv);
+#pragma unroll
+      for (int mo = 0; mo < 4; ++mo) {
+        const float av = w[(16 * mo + n) * Ipad + i];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc[mo][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, xv[t], acc[mo][t], 0, 0, 0);
+      }
+    }
+    // accumulator register j of lane l: row 4*(l/16) + j, column l%16
+#pragma unroll
+    for (int mo = 0; mo < 4; ++mo)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ol = 16 * mo + 4 * kr + j, o = o0 + ol;
+        if (o >= O || np <= 0) continue;
+        float v[4] = {acc[mo][0][j] + bias[ol], acc[mo][1][j] + bias[ol], acc[mo][2][j] + bias[ol],
+                      acc[mo][3][j] + bias[ol]};
+        if (a.add) {
+          float ad[4];
+          load4<DT>(a.add, yb + (size_t)o * P + p0, np, al, ad);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] += ad[t];
+        }
+        if (a.act == 1) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = gelu(v[t]);
+        }
+        store4<DT>(a.y, yb + (size_t)o * P + p0, np, al, v);
+      }
+  }
+}
+
+static constexpr int kMaxJ = 128;
+static constexpr int kMaxC = 4;
+
+template <int DT>
+__global__ __launch_bounds__(kPwThreads) void fno_projection(ProjArgs a) {
+  __shared__ float q1w[kMaxJ * 64];  // [J][Ipad], Ipad <= 64
+  __shared__ float q1b[kMaxJ];
+  __shared__ float q2w[kMaxC * kMaxJ];
+  __shared__ float q2b[kMaxC];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int b = blockIdx.z;
+  const int I = a.I, J = a.J, C = a.C;
+  const long P = a.P;
+  const int Ipad = (I + 3) & ~3;
+  for (int v = threadIdx.x; v < kMaxJ * Ipad; v += kPwThreads) {
+    const int j = v / Ipad, i = v - j * Ipad;
+    q1w[v] = (j < J && i < I) ? load1<DT>(a.Q1, (size_t)j * I + i) : 0.f;
+  }
+  for (int v = threadIdx.x; v < kMaxJ; v += kPwThreads) q1b[v] = v < J ? load1<DT>(a.q1, v) : 0.f;
+  for (int v = threadIdx.x; v < kMaxC * kMaxJ; v += kPwThreads) {
+    const int c = v / kMaxJ, j = v - c * kMaxJ;
+    q2w[v] = (c < C && j < J) ? load1<DT>(a.Q2, (size_t)c * J + j) : 0.f;
+  }
+  for (int v = threadIdx.x; v < kMaxC; v += kPwThreads) q2b[v] = v < C ? load1<DT>(a.q2, v) : 0.f;
+  __syncthreads();
+
+  const int kr = lane >> 4, n = lane & 15;
+  const bool al = (P & 3) == 0;
+  const size_t xb = (size_t)b * I * P, yb = (size_t)b * C * P;
+  const long ntiles = (P + 63) / 64;
+  for (long tile = (long)blockIdx.x * 4 + wv; tile < ntiles; tile += (long)gridDim.x * 4) {
+    const long p0 = tile * 64 + 4 * n;
+    const int np = (int)min((long)4, max(0L, P - p0));
+    float part[kMaxC][4];
+#pragma unroll
+    for (int c = 0; c < kMaxC; ++c)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) part[c][t] = 0.f;
+    for (int jc = 0; jc < kMaxJ; jc += 64) {  // hidden units in chunks of 64
+      v4f acc[4][4];
+#pragma unroll
+      for (int mo = 0; mo < 4; ++mo)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[mo][t] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < Ipad; k0 += 4) {
+        const int i = k0 + kr;
+        float xv[4];
+        load4<DT>(a.x, xb + (size_t)(i < I ? i : 0) * P + p0, i < I ? np : 0, al, xv);
+#pragma unroll
+        for (int mo = 0; mo < 4; ++mo) {
+          const float av = q1w[(jc + 16 * mo + n) * Ipad + i];
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            acc[mo][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, xv[t], acc[mo][t], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int mo = 0; mo < 4; ++mo)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = jc + 16 * mo + 4 * kr + jj;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float h = gelu(acc[mo][t][jj] + q1b[j]);
+#pragma unroll
+            for (int c = 0; c < kMaxC; ++c) part[c][t] = fmaf(q2w[c * kMaxJ + j], h, part[c][t]);
+          }
+        }
+    }
+    // sum the four row groups (lanes n, n+16, n+32, n+48) in a fixed order
+#pragma unroll
+    for (int c = 0; c < kMaxC; ++c)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float v0 = __shfl(part[c][t], n, 64), v1 = __shfl(part[c][t], n + 16, 64);
+        const float v2 = __shfl(part[c][t], n + 32, 64), v3 = __shfl(part[c][t], n + 48, 64);
+        part[c][t] = ((v0 + v1) + (v2 + v3)) + q2b[c];
+      }
+    if (kr == 0 && np > 0) {
+      for (int c = 0; c < C; ++c) {
+        float v[4] = {part[c][0], part[c][1], part[c][2], part[c][3]};
+        store4<DT>(a.y, yb + (size_t)c * P + p0, np, al, v);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+static int pw_blocks(long P) {
+  const long tiles = (P + 63) / 64;
+  long blocks = (tiles + 3) / 4;
+  return (int)(blocks < 4096 ? blocks : 4096);
+}
+
+hipError_t launch_channel_mix(const void *x, const void *A, const void *bias, const void *add, void *y, int B,
+                              int I, int O, long P, int act, int dtype, hipStream_t s) {
+  MixArgs a{x, A, bias, add, y, B, I, O, P, act};
+  dim3 grid(pw_blocks(P), (O + kOB - 1) / kOB, B);
+  void *args[] = {(void *)&a};
+  const void *k = dtype == DT_F32 ? (const void *)fno_channel_mix<DT_F32>
+                  : dtype == DT_F16 ? (const void *)fno_channel_mix<DT_F16>
+                                    : (const void *)fno_channel_mix<DT_BF16>;
+  return hipLaunchKernel(k, grid, dim3(kPwThreads), args, 0, s);
+}
+
+hipError_t launch_projection(const void *x, const void *Q1, const void *q1, const void *Q2, const void *q2, void *y,
+                             int B, int I, int J, int C, long P, int dtype, hipStream_t s) {
+  ProjArgs a{x, Q1, q1, Q2, q2, y, B, I, J, C, P};
+  dim3 grid(pw_blocks(P), 1, B);
+  void *args[] = {(void *)&a};
+  const void *k = dtype == DT_F32 ? (const void *)fno_projection<DT_F32>
+                  : dtype == DT_F16 ? (const void *)fno_projection<DT_F16>
+                                    : (const void *)fno_projection<DT_BF16>;
+  return hipLaunchKernel(k, grid, dim3(kPwThreads), args, 0, s);
+}
+
+}  // namespace fno

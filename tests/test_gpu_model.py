@@ -1,0 +1,105 @@
+"""GPU parity of the full FNO2d network and its per-pixel kernels against the
+float64 oracle (relative L2 <= 3e-3 for fp16 storage, 1e-5 for fp32)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import spectral_convolution_amd as fno
+import workloads as wl
+from gpu_util import rel_l2, to_device, to_float64
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand(rng, shape, dtype, scale=1.0):
+    v = rng.standard_normal(shape) * scale
+    s = wl.round_to_storage(v, dtype)
+    return s, wl.storage_to_float64(s, dtype)
+
+
+@pytest.mark.parametrize("dtype,B,I,O,P,act,add", [
+    ("f32", 2, 3, 64, 4096, 0, False),     # lift shape
+    ("f16", 3, 64, 64, 1000, 1, True),     # block epilogue, ragged pixel count
+    ("bf16", 1, 17, 70, 259, 1, True),     # ragged channels (two output blocks)
+    ("f32", 2, 128, 5, 64, 0, False),
+])
+def test_channel_mix(dtype, B, I, O, P, act, add):
+    import torch
+    rng = np.random.default_rng(5)
+    xs, x64 = _rand(rng, (B, I, P), dtype)
+    As, A64 = _rand(rng, (O, I), dtype, 1 / np.sqrt(I))
+    bs, b64 = _rand(rng, (O,), dtype)
+    ads, ad64 = _rand(rng, (B, O, P), dtype)
+    x, A, b = to_device(xs, dtype), to_device(As, dtype), to_device(bs, dtype)
+    ad = to_device(ads, dtype) if add else None
+    y = torch.empty((B, O, P), dtype=x.dtype, device=x.device)
+    fno.fno_channel_mix(x, A, b, ad, y, act)
+    torch.cuda.synchronize()
+    ref = np.einsum("oi,bip->bop", A64, x64) + b64[None, :, None] + (ad64 if add else 0)
+    if act:
+        ref = oracle.gelu(ref)
+    tol = 1e-5 if dtype == "f32" else 3e-3
+    assert rel_l2(to_float64(y), ref) <= tol
+
+
+@pytest.mark.parametrize("dtype,B,I,J,C,P", [("f16", 2, 64, 128, 1, 4096), ("f32", 1, 20, 33, 3, 333)])
+def test_projection(dtype, B, I, J, C, P):
+    import torch
+    rng = np.random.default_rng(6)
+    xs, x64 = _rand(rng, (B, I, P), dtype)
+    Q1s, Q164 = _rand(rng, (J, I), dtype, 1 / np.sqrt(I))
+    q1s, q164 = _rand(rng, (J,), dtype)
+    Q2s, Q264 = _rand(rng, (C, J), dtype, 1 / np.sqrt(J))
+    q2s, q264 = _rand(rng, (C,), dtype)
+    t = [to_device(v, dtype) for v in (xs, Q1s, q1s, Q2s, q2s)]
+    y = torch.empty((B, C, P), dtype=t[0].dtype, device=t[0].device)
+    fno.fno_projection(*t, y)
+    torch.cuda.synchronize()
+    h = oracle.gelu(np.einsum("ji,bip->bjp", Q164, x64) + q164[None, :, None])
+    ref = np.einsum("cj,bjp->bcp", Q264, h) + q264[None, :, None]
+    tol = 1e-5 if dtype == "f32" else 3e-3
+    assert rel_l2(to_float64(y), ref) <= tol
+
+
+def _run_model(cfg, batch=None, grid=None, samples=None):
+    import torch
+    inp = wl.model_inputs(cfg, batch=batch, grid=grid)
+    dt = inp["dtype"]
+    B = inp["batch"]
+    H, W = inp["grid"]
+    model = fno.fno_model2d_create(B, (H, W), cfg.in_channels, cfg.width, cfg.n_layers, cfg.modes,
+                                   cfg.proj_hidden, cfg.out_channels, dt, 0)
+    try:
+        params = [to_device(inp["P"], dt), to_device(inp["p"], dt)]
+        for L in inp["layers"]:
+            params += [to_device(L["spectral"], dt), to_device(L["W"], dt), to_device(L["b"], dt)]
+        params += [to_device(inp[k], dt) for k in ("Q1", "q1", "Q2", "q2")]
+        f = to_device(inp["features"], dt)
+        out = torch.empty((B, cfg.out_channels, H, W), dtype=f.dtype, device=f.device)
+        fno.fno_model2d_forward(model, f, params, out)
+        torch.cuda.synchronize()
+        got = to_float64(out)
+    finally:
+        fno.fno_model2d_destroy(model)
+    idx = list(range(B)) if samples is None else list(samples)
+    ref = oracle.fno2d_forward(inp["features64"][idx], inp["P64"], inp["p64"], inp["layers64"],
+                               inp["Q164"], inp["q164"], inp["Q264"], inp["q264"], *cfg.modes)
+    return got[idx], ref
+
+
+def test_model_small():
+    cfg = wl.CONFIGS["c4"]
+    got, ref = _run_model(cfg, batch=2, grid=(64, 64))
+    err = rel_l2(got, ref)
+    print(f"[model] 64x64 B=2 rel_l2={err:.3e}", flush=True)
+    assert err <= 3e-3
+
+
+def test_model_full_size_sampled():
+    cfg = wl.CONFIGS["c4"]
+    print("[model-full] B=20 256x256 samples (0, 19)", flush=True)
+    got, ref = _run_model(cfg, samples=(0, 19))
+    err = rel_l2(got, ref)
+    print(f"[model-full] rel_l2={err:.3e}", flush=True)
+    assert err <= 3e-3
