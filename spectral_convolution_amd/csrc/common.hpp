@@ -68,7 +68,8 @@ struct PlaneFwdArgs {
   const float2 *tw_h;   // exp(-2 pi i k / H), k < H
   const float2 *tw_w;   // exp(-2 pi i k / W), k < W
   int nplanes, H, W, m1, m2, PH, PW;
-  int CH;  // rows per chunk of the row stage (plane_fwd_chunk_rows)
+  int ppw;  // planes per workgroup
+  int rc;   // residues per thread in the column stage
   float scale;
 };
 
@@ -79,6 +80,7 @@ struct PlaneInvArgs {
   const float2 *tw_h;
   const float2 *tw_w;
   int nplanes, H, W, m1, m2, PH, PW;
+  int ppw;  // planes per workgroup
 };
 
 // Pruned c2c DFT along a strided axis: in [vol][N][C] -> out [vol][2*m][C]
@@ -100,14 +102,15 @@ struct ContractArgs {
 };
 
 // host launchers (defined next to their kernels)
-int plane_fwd_chunk_rows(int H, int W, int m1, int m2, int MP);
-size_t plane_fwd_lds_bytes(int H, int W, int m1, int m2, int MP);
-size_t plane_inv_lds_bytes(int H, int W, int m1, int m2, int MP);
+int plane_rpt(int MP, int PW);
+int plane_rc(int H, int MP);
+int plane_ppw(bool fwd, int H, int W, int m1, int m2, int MP, int nplanes);
+size_t plane_fwd_lds_bytes(int H, int W, int m1, int m2, int MP, int ppw);
+size_t plane_inv_lds_bytes(int H, int W, int m1, int m2, int MP, int ppw);
 size_t axis_fwd_lds_bytes(int N, int m, int MP);
-hipError_t plane_fwd_prepare(int MP, int dtype, size_t lds);
-hipError_t plane_inv_prepare(int MP, int dtype, size_t lds);
-hipError_t launch_plane_fwd(const PlaneFwdArgs &a, int MP, int dtype, size_t lds, hipStream_t s);
-hipError_t launch_plane_inv(const PlaneInvArgs &a, int MP, int dtype, size_t lds, hipStream_t s);
+hipError_t plane_prepare(bool fwd, int MP, int rpt, int dtype, size_t lds);
+hipError_t launch_plane_fwd(const PlaneFwdArgs &a, int MP, int rpt, int dtype, size_t lds, hipStream_t s);
+hipError_t launch_plane_inv(const PlaneInvArgs &a, int MP, int rpt, int dtype, size_t lds, hipStream_t s);
 hipError_t axis_fwd_prepare(int MP, size_t lds);
 hipError_t launch_axis_fwd(const AxisArgs &a, int MP, size_t lds, hipStream_t s);
 hipError_t launch_axis_inv(const AxisArgs &a, int MP, hipStream_t s);

@@ -70,7 +70,7 @@ struct fno_plan_s {
   int dtype = 0, device = 0;
   int K = 0;            // retained modes per plane
   // plane transform (2D: axes H, W; 3D: axes Y, Z of every x-slab)
-  int pH = 0, pW = 0, pm1 = 0, pm2 = 0, pMP = 0;
+  int pH = 0, pW = 0, pm1 = 0, pm2 = 0, pMP = 0, rpt = 2, rc = 1, ppw_f = 1, ppw_i = 1;
   size_t lds_fwd = 0, lds_inv = 0;
   // 3D outer axis
   int xN = 0, xm = 0, xMP = 0;
@@ -132,8 +132,14 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
   } else {
     p.K = 2 * modes[0] * modes[1];
   }
-  p.lds_fwd = plane_fwd_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP);
-  p.lds_inv = plane_inv_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP);
+  const int np_f = batch * c_in * (ndim == 3 ? grid[0] : 1);
+  const int np_i = batch * c_out * (ndim == 3 ? grid[0] : 1);
+  p.rpt = plane_rpt(p.pMP, p.pW / p.pMP);
+  p.rc = plane_rc(p.pH, p.pMP);
+  p.ppw_f = plane_ppw(true, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_f);
+  p.ppw_i = plane_ppw(false, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_i);
+  p.lds_fwd = plane_fwd_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP, p.ppw_f);
+  p.lds_inv = plane_inv_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP, p.ppw_i);
   if (p.lds_fwd > kMaxLds || p.lds_inv > kMaxLds) return FNO_ERR_UNSUPPORTED;
   if (ndim == 3) {
     p.lds_axis = axis_fwd_lds_bytes(p.xN, p.xm, p.xMP);
@@ -265,8 +271,8 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
     std::vector<float2> tx = twiddles(ntx);
     e = hipMemcpy(p->tw_x, tx.data(), ntx * sizeof(float2), hipMemcpyHostToDevice);
   }
-  if (e == hipSuccess) e = plane_fwd_prepare(p->pMP, p->dtype, p->lds_fwd);
-  if (e == hipSuccess) e = plane_inv_prepare(p->pMP, p->dtype, p->lds_inv);
+  if (e == hipSuccess) e = plane_prepare(true, p->pMP, p->rpt, p->dtype, p->lds_fwd);
+  if (e == hipSuccess) e = plane_prepare(false, p->pMP, p->rpt, p->dtype, p->lds_inv);
   if (e == hipSuccess && ndim == 3) e = axis_fwd_prepare(p->xMP, p->lds_axis);
   if (e == hipSuccess) e = contract_prepare(p->bb, p->dtype, contract_lds_bytes(p->bb, p->split));
   if (e != hipSuccess) {
@@ -316,9 +322,10 @@ static hipError_t run_one(fno_plan_t p, int kind, const void *x, const void *w, 
       a.m2 = p->pm2;
       a.PH = p->pH / p->pMP;
       a.PW = p->pW / p->pMP;
-      a.CH = plane_fwd_chunk_rows(p->pH, p->pW, p->pm1, p->pm2, p->pMP);
+      a.ppw = p->ppw_f;
+      a.rc = p->rc;
       a.scale = nd == 2 ? 1.0f / ((float)p->pH * (float)p->pW) : 1.0f;
-      return launch_plane_fwd(a, p->pMP, p->dtype, p->lds_fwd, s);
+      return launch_plane_fwd(a, p->pMP, p->rpt, p->dtype, p->lds_fwd, s);
     }
     case L_FWD_AXIS: {
       AxisArgs a;
@@ -370,7 +377,8 @@ static hipError_t run_one(fno_plan_t p, int kind, const void *x, const void *w, 
       a.m2 = p->pm2;
       a.PH = p->pH / p->pMP;
       a.PW = p->pW / p->pMP;
-      return launch_plane_inv(a, p->pMP, p->dtype, p->lds_inv, s);
+      a.ppw = p->ppw_i;
+      return launch_plane_inv(a, p->pMP, p->rpt, p->dtype, p->lds_inv, s);
     }
   }
   return hipErrorInvalidValue;

@@ -1,24 +1,27 @@
 // plane_kernels.hip - pruned forward / inverse 2D transforms of real planes.
 //
-// One workgroup (256 threads) per plane. The transforms keep only the
-// retained low-frequency modes of the FNO layer (TurboFNO write-up, section
-// 2.2 and 2.3: corners in kx, half spectrum in ky) and never form the full
-// spectrum.
+// A 256-thread workgroup handles `ppw` whole planes (more than one when the
+// planes are small). The transforms keep only the retained low-frequency
+// modes of the FNO layer (TurboFNO write-up, sections 2.2 and 2.3: corners
+// in kx, half spectrum in ky) and never form the full spectrum.
 //
-// Pruning by decimation: with MP = next_pow2(m) and P = N / MP, sample n of
-// a length-N axis is split as n = r + P q (r < P, q < MP). Forward, for
-// every residue r an MP-point DFT over q gives D_r[j]; a retained output k
-// is then sum_r w^r D_r[k mod MP] with w = exp(-2 pi i k / N), summed by
-// Horner's rule. Inverse (input pruned), the retained inputs are
-// pre-multiplied per residue and one MP-point inverse DFT per residue gives
-// the P-strided outputs n = r + P q directly.
+// Pruning by decimation: with MP = next_pow2(max mode count) and P = N / MP,
+// sample n of a length-N axis is split as n = r + P q (residue r < P,
+// q < MP). Forward, an MP-point DFT over q of every residue gives D_r[j];
+// a retained output k is sum_r w^(r k) D_r[k mod MP], w = exp(-2 pi i / N).
+// Inverse (input pruned), the retained inputs are pre-multiplied per residue
+// and one MP-point inverse DFT per residue yields the strided outputs
+// n = r + P q directly.
 //
-// The MP-point DFTs run in registers (fft_reg.hpp). Along the contiguous
-// (real) axis two residues are packed as the real and imaginary parts of one
-// complex sequence, so one complex FFT serves two real ones. Rows are read
-// straight from global memory in adjacent pairs; the partial spectra of a
-// chunk of rows meet in LDS for the Horner combine; the row spectra of the
-// whole plane (H x m2 complex) stay in LDS for the column stage.
+// Row (contiguous, real) axis: chunks of rows are copied between global
+// memory and LDS with coalesced 16-byte accesses (one wave instruction moves
+// 1 KiB of consecutive bytes); in LDS a thread takes two adjacent residues of
+// one row and packs them as the real and imaginary parts of one complex
+// sequence (one complex FFT for two real ones). Forward, the residues'
+// weighted sums are added over the T = P/2 threads of a row by a butterfly
+// across lanes (DPP quad permutes and row mirrors). Column axis: one thread
+// per (column, residue), partial sums reduced the same way. LDS holds the
+// row spectra (H x m2 per plane), one staging chunk and the twiddle tables.
 
 #include "common.hpp"
 
@@ -26,113 +29,309 @@ namespace fno {
 
 static constexpr int kThreads = 256;
 
-static size_t fwd_lds_for(int H, int W, int m2, int MP, int CH) {
-  const int PW = W / MP;
-  const size_t rowd = (size_t)(MP / 2 + 1) * CH * (PW + 1);
-  const size_t cold = (size_t)H * m2;
-  const size_t dreg = rowd > cold ? rowd : cold;
-  return (dreg + (size_t)H * (m2 + 1)) * sizeof(float2);
+// the value held by another lane of the same 16-lane row (DPP control CTRL)
+template <int CTRL>
+__device__ __forceinline__ float dpp_get(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-// Rows per chunk of the row stage: enough units for all threads, halved
-// while the LDS footprint exceeds the 160 KiB a workgroup may hold.
-int plane_fwd_chunk_rows(int H, int W, int m1, int m2, int MP) {
-  (void)m1;
-  const int Q = (W / MP) >> 1;
-  int ch = kThreads / Q;
-  if (ch > H) ch = H;
-  while (ch > 1 && fwd_lds_for(H, W, m2, MP, ch) > 160 * 1024) ch >>= 1;
-  return ch;
+// Sum over each group of T consecutive lanes (T a power of two <= 64, groups
+// aligned to multiples of T); every lane of a group receives the group sum.
+// Butterfly order: lane ^ 1, ^ 2 (quad permutes), ^ 4 (half-row mirror, valid
+// once quads agree), ^ 8 (row mirror), then ^ 16, ^ 32 through LDS permutes.
+__device__ __forceinline__ float lane_group_sum(float v, int T) {
+  if (T >= 2) v += dpp_get<0xB1>(v);    // quad_perm [1,0,3,2]
+  if (T >= 4) v += dpp_get<0x4E>(v);    // quad_perm [2,3,0,1]
+  if (T >= 8) v += dpp_get<0x141>(v);   // row_half_mirror
+  if (T >= 16) v += dpp_get<0x140>(v);  // row_mirror
+  if (T >= 32) v += __shfl_xor(v, 16, 64);
+  if (T >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
 }
 
-size_t plane_fwd_lds_bytes(int H, int W, int m1, int m2, int MP) {
-  return fwd_lds_for(H, W, m2, MP, plane_fwd_chunk_rows(H, W, m1, m2, MP));
+__device__ __forceinline__ float2 lane_group_sum(float2 v, int T) {
+  return make_float2(lane_group_sum(v.x, T), lane_group_sum(v.y, T));
 }
 
-size_t plane_inv_lds_bytes(int H, int W, int m1, int m2, int MP) {
+template <int CTRL, int N>
+__device__ __forceinline__ void dpp_add_all(float2 (&S)[N]) {
+  static_for<0, N>([&](auto kk) {
+    constexpr int k = decltype(kk)::value;
+    S[k].x += dpp_get<CTRL>(S[k].x);
+    S[k].y += dpp_get<CTRL>(S[k].y);
+  });
+}
+
+template <int N>
+__device__ __forceinline__ void shfl_add_all(float2 (&S)[N], int s) {
+  static_for<0, N>([&](auto kk) {
+    constexpr int k = decltype(kk)::value;
+    S[k].x += __shfl_xor(S[k].x, s, 64);
+    S[k].y += __shfl_xor(S[k].y, s, 64);
+  });
+}
+
+// lane_group_sum applied to a whole array: one uniform branch per level
+template <int N>
+__device__ __forceinline__ void group_sum_all(float2 (&S)[N], int T) {
+  if (T >= 2) dpp_add_all<0xB1>(S);
+  if (T >= 4) dpp_add_all<0x4E>(S);
+  if (T >= 8) dpp_add_all<0x141>(S);
+  if (T >= 16) dpp_add_all<0x140>(S);
+  if (T >= 32) shfl_add_all(S, 16);
+  if (T >= 64) shfl_add_all(S, 32);
+}
+
+// residues per thread along the row axis (two per complex FFT)
+int plane_rpt(int MP, int PW) {
   (void)MP;
-  return ((size_t)2 * m1 * m2 + (size_t)H * (m2 + 1) + W + H) * sizeof(float2);
+  (void)PW;
+  return 2;
+}
+
+// residues per thread in the column stage: lane groups of at most 64
+int plane_rc(int H, int MP) {
+  const int PH = H / MP;
+  return PH > 64 ? PH / 64 : 1;
+}
+
+// Row-stage chunk: CH = 256 / T rows (T = PW / RPT threads per row) staged in
+// LDS as fp32 with a row pitch of W + 2T floats, which spreads the 16 rows x
+// T lanes of one 8-byte LDS access over all 32 banks.
+__host__ __device__ inline int chunk_rows(int W, int MP) { return kThreads / ((W / MP) / 2); }
+__host__ __device__ inline int stage_pitch(int W, int MP) {
+  const int T = (W / MP) / 2;
+  return W + (T < 16 ? 2 * T : 0);
+}
+
+size_t plane_fwd_lds_bytes(int H, int W, int m1, int m2, int MP, int ppw) {
+  (void)m1;
+  const size_t stage = (size_t)chunk_rows(W, MP) * stage_pitch(W, MP) * sizeof(float);
+  return ((size_t)W + H + (size_t)ppw * H * (m2 + 1)) * sizeof(float2) + stage;
+}
+
+size_t plane_inv_lds_bytes(int H, int W, int m1, int m2, int MP, int ppw) {
+  const size_t stage = (size_t)chunk_rows(W, MP) * stage_pitch(W, MP) * sizeof(float);
+  return ((size_t)W + H + (size_t)ppw * (2 * m1 * m2 + (size_t)H * (m2 + 1))) * sizeof(float2) + stage;
+}
+
+// planes per workgroup: at least one chunk of rows, within 64 KiB of LDS
+int plane_ppw(bool fwd, int H, int W, int m1, int m2, int MP, int nplanes) {
+  int ppw = chunk_rows(W, MP) / H;
+  if (ppw < 1) ppw = 1;
+  if (ppw > nplanes) ppw = nplanes;
+  while (ppw > 1 && (fwd ? plane_fwd_lds_bytes(H, W, m1, m2, MP, ppw) : plane_inv_lds_bytes(H, W, m1, m2, MP, ppw)) >
+                        64 * 1024)
+    ppw >>= 1;
+  return ppw;
+}
+
+// elements per 16-byte (or smaller) vector of the coalesced chunk copies
+template <int MP, int DT>
+struct ChunkVec {
+  static constexpr int kMax = DT == DT_F32 ? 4 : 8;
+  static constexpr int V = kMax < 2 * MP ? kMax : 2 * MP;  // divides the 2*MP elements per thread
+  static constexpr int N = 2 * MP / V;                      // vectors per thread per chunk
+};
+
+template <int DT, int V>
+__device__ __forceinline__ void gload_vec(const void *base, size_t idx, float (&v)[V]) {
+  if constexpr (DT == DT_F32) {
+    if constexpr (V == 4) {
+      const float4 u = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + idx);
+      v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+    } else {
+      static_for<0, V / 2>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        const float2 u = *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(base) + idx + 2 * c);
+        v[2 * c] = u.x; v[2 * c + 1] = u.y;
+      });
+    }
+  } else {
+    static_for<0, V / 2>([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      const float2 u = load_pair<DT>(base, idx + 2 * c);
+      v[2 * c] = u.x; v[2 * c + 1] = u.y;
+    });
+  }
+}
+
+template <int DT, int V>
+__device__ __forceinline__ void gstore_vec(void *base, size_t idx, const float (&v)[V]) {
+  if constexpr (DT == DT_F32 && V == 4) {
+    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(base) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    static_for<0, V / 2>([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      store_pair<DT>(base, idx + 2 * c, v[2 * c], v[2 * c + 1]);
+    });
+  }
 }
 
 template <int MP, int DT>
 __global__ __launch_bounds__(kThreads) void fno_fwd_plane(PlaneFwdArgs a) {
   extern __shared__ float2 smem[];
   constexpr int LG = ilog2(MP);
-  constexpr int KH = MP / 2 + 1;
   const int tid = threadIdx.x;
-  const int H = a.H, W = a.W, m1 = a.m1, m2 = a.m2, PH = a.PH, PW = a.PW;
-  const int Q = PW >> 1;
-  const int CH = a.CH;
-  const int PWp = PW + 1, m2p = m2 + 1;
-  const size_t rowd = (size_t)KH * CH * PWp, cold = (size_t)H * m2;
-  float2 *D = smem;
-  float2 *R = smem + (rowd > cold ? rowd : cold);
+  const int H = a.H, W = a.W, m1 = a.m1, m2 = a.m2, PH = a.PH, PW = a.PW, ppw = a.ppw;
+  const int m2p = m2 + 1;
+  float2 *tww = smem;
+  float2 *twh = tww + W;
+  float2 *R = twh + H;                                        // [ppw][H][m2 + 1]
+  float *stage = reinterpret_cast<float *>(R + (size_t)ppw * H * m2p);  // [CH][pitch]
+  for (int v = tid; v < W; v += kThreads) tww[v] = a.tw_w[v];
+  for (int v = tid; v < H; v += kThreads) twh[v] = a.tw_h[v];
+  const int plane0 = blockIdx.x * ppw;
+  const int nlive = min(ppw, a.nplanes - plane0);
 
-  const int plane = blockIdx.x;
-  const size_t xoff = (size_t)plane * H * W;
-
-  // ---- row stage: r2c along W, outputs ky < m2, into R[h][ky]
-  for (int row0 = 0; row0 < H; row0 += CH) {
-    if (tid < CH * Q) {
-      const int rl = tid / Q, p = tid - rl * Q;
-      const size_t rbase = xoff + (size_t)(row0 + rl) * W + 2 * p;
-      float2 z[MP];
-      static_for<0, MP>([&](auto q) { z[q] = load_pair<DT>(a.x, rbase + (size_t)decltype(q)::value * PW); });
-      fft_reg<MP, false>(z);
-      // split the packed pair: D_{2p}[k] = Z[k] + conj Z[-k], D_{2p+1}[k] =
-      // -i (Z[k] - conj Z[-k]) (both doubled; the 1/2 is folded into scale)
-      float2 *d = D + (size_t)rl * PWp + 2 * p;
-      static_for<0, KH>([&](auto kk) {
+  // ---- row stage: r2c along W, outputs ky < m2, into R. Rows are copied
+  // chunk by chunk into LDS with coalesced 16-byte accesses (the next chunk's
+  // loads are in flight while the current one is transformed); a thread then
+  // takes two adjacent residues of one row. Each output is reduced over the
+  // T threads of its row and stored as soon as it is formed.
+  using CV = ChunkVec<MP, DT>;
+  const int T = PW / 2;
+  const int CH = kThreads / T, pitch = stage_pitch(W, MP);
+  const int nrows = nlive * H;
+  const int nchunks = (nrows + CH - 1) / CH;
+  const size_t gbase = (size_t)plane0 * H * W;
+  float pre[CV::N][CV::V];
+  auto fetch = [&](int c) {
+    static_for<0, CV::N>([&](auto vv) {
+      constexpr int v = decltype(vv)::value;
+      const int e = (v * kThreads + tid) * CV::V;  // element within the chunk
+      const int row = c * CH + e / W;
+      if (row < nrows) gload_vec<DT, CV::V>(a.x, gbase + (size_t)c * CH * W + e, pre[v]);
+    });
+  };
+  fetch(0);
+  for (int c = 0; c < nchunks; ++c) {
+    static_for<0, CV::N>([&](auto vv) {
+      constexpr int v = decltype(vv)::value;
+      const int e = (v * kThreads + tid) * CV::V;
+      const int rl = e / W, col = e - rl * W;
+      float2 *dst = reinterpret_cast<float2 *>(stage + rl * pitch + col);
+      static_for<0, CV::V / 2>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        dst[i] = make_float2(pre[v][2 * i], pre[v][2 * i + 1]);
+      });
+    });
+    __syncthreads();
+    if (c + 1 < nchunks) fetch(c + 1);
+    const int rl = tid / T, t = tid - rl * T;
+    const int grow = c * CH + rl;
+    const bool live = grow < nrows;
+    const int pl = grow / H, row = grow - pl * H;
+    const int r0 = 2 * t;
+    float2 za[MP];
+    const float *src = stage + rl * pitch + r0;
+    static_for<0, MP>([&](auto qq) {
+      constexpr int q = decltype(qq)::value;
+      za[q] = *reinterpret_cast<const float2 *>(src + q * PW);
+    });
+    fft_reg<MP, false>(za);
+    float2 S[MP];
+    static_for<0, MP>([&](auto kk) {
+      constexpr int k = decltype(kk)::value;
+      constexpr int ik = bitrev(k, LG), im = bitrev((MP - k) & (MP - 1), LG);
+      // two real spectra from one complex one (both doubled; 1/2 folded into scale)
+      const float2 A = za[ik], Am = za[im];
+      const float2 d0 = make_float2(A.x + Am.x, A.y - Am.y);
+      const float2 d1 = make_float2(A.y + Am.y, Am.x - A.x);
+      const float2 acc = cfma(d1, tww[k], d0);
+      S[k] = k < m2 ? cmul(acc, tww[(r0 * k) & (W - 1)]) : make_float2(0.f, 0.f);
+    });
+    group_sum_all(S, T);
+    if (live && t == 0) {
+      float2 *rr = R + ((size_t)pl * H + row) * m2p;
+      static_for<0, MP>([&](auto kk) {
         constexpr int k = decltype(kk)::value;
-        const float2 zk = z[bitrev(k, LG)];
-        const float2 zm = z[bitrev((MP - k) & (MP - 1), LG)];
-        float2 *dk = d + (size_t)k * CH * PWp;
-        dk[0] = make_float2(zk.x + zm.x, zk.y - zm.y);
-        dk[1] = make_float2(zk.y + zm.y, zm.x - zk.x);
+        if (k < m2) rr[k] = S[k];
       });
     }
     __syncthreads();
-    for (int v = tid; v < CH * m2; v += kThreads) {
-      const int k = v / CH, rl = v - k * CH;
-      const bool cj = k > MP / 2;
-      const int kk = cj ? MP - k : k;
-      const float2 w = a.tw_w[k];
-      const float2 *dp = D + ((size_t)kk * CH + rl) * PWp;
-      float2 acc = dp[PW - 1];
-      if (cj) acc.y = -acc.y;
-      for (int r = PW - 2; r >= 0; --r) {
-        float2 dv = dp[r];
-        if (cj) dv.y = -dv.y;
-        acc = cfma(acc, w, dv);
-      }
-      R[(size_t)(row0 + rl) * m2p + k] = acc;
-    }
-    __syncthreads();
   }
 
-  // ---- column stage: c2c along H on the m2 retained columns, kx corners
-  for (int u = tid; u < m2 * PH; u += kThreads) {
-    const int r = u / m2, ky = u - r * m2;
-    float2 z[MP];
-    static_for<0, MP>([&](auto q) { z[q] = R[(size_t)(r + decltype(q)::value * PH) * m2p + ky]; });
-    fft_reg<MP, false>(z);
-    static_for<0, MP>([&](auto jj) {
-      constexpr int j = decltype(jj)::value;
-      D[((size_t)j * PH + r) * m2 + ky] = z[bitrev(j, LG)];
-    });
-  }
-  __syncthreads();
+  // ---- column stage: c2c along H on the m2 retained columns, kx corners.
+  // One residue per thread (PH <= 64 lanes per column); for MP <= 2, where
+  // PH can exceed 64, RC residues per thread accumulate before the reduction.
+  const int RC = a.rc, Tc = PH / RC;
+  const int K = 2 * m1 * m2;
   const float sc = a.scale * 0.5f;
-  float2 *op = a.out + (size_t)plane * 2 * m1 * m2;
-  for (int v = tid; v < 2 * m1 * m2; v += kThreads) {
-    const int ai = v / m2, ky = v - ai * m2;
-    const int kx = ai < m1 ? ai : H - 2 * m1 + ai;
-    const int j = kx & (MP - 1);
-    const float2 w = a.tw_h[kx];
-    const float2 *dp = D + (size_t)j * PH * m2 + ky;
-    float2 acc = dp[(size_t)(PH - 1) * m2];
-    for (int r = PH - 2; r >= 0; --r) acc = cfma(acc, w, dp[(size_t)r * m2]);
-    op[v] = make_float2(acc.x * sc, acc.y * sc);
+  for (int u = tid; u < nlive * m2 * Tc; u += kThreads) {
+    const int g = u / Tc, t = u - g * Tc;
+    const int pl = g / m2, ky = g - pl * m2;
+    const bool live = true;
+    const float2 *col = R + (size_t)pl * H * m2p + ky;
+    float2 *op = a.out + (size_t)(live ? plane0 + pl : 0) * K + ky;
+    // corner 0: kx = j (j < m1) -> row j; corner 1: kx = H - MP + j
+    // (j >= MP - m1) -> row 2*m1 - MP + j
+    if constexpr (MP > 2) {
+      // one residue per thread; the two corners are formed and reduced in turn
+      const int r = t;
+      float2 z[MP];
+      static_for<0, MP>([&](auto qq) {
+        constexpr int q = decltype(qq)::value;
+        z[q] = col[(size_t)(r + q * PH) * m2p];
+      });
+      fft_reg<MP, false>(z);
+      float2 O[MP];
+      static_for<0, MP>([&](auto jj) {
+        constexpr int j = decltype(jj)::value;
+        O[j] = j < m1 ? cmul(z[bitrev(j, LG)], twh[(j * r) & (H - 1)]) : make_float2(0.f, 0.f);
+      });
+      group_sum_all(O, Tc);
+      if (live && t == 0)
+        static_for<0, MP>([&](auto jj) {
+          constexpr int j = decltype(jj)::value;
+          if (j < m1) op[(size_t)j * m2] = make_float2(O[j].x * sc, O[j].y * sc);
+        });
+      static_for<0, MP>([&](auto jj) {
+        constexpr int j = decltype(jj)::value;
+        O[j] = j >= MP - m1 ? cmul(z[bitrev(j, LG)], twh[((H - MP + j) * r) & (H - 1)]) : make_float2(0.f, 0.f);
+      });
+      group_sum_all(O, Tc);
+      if (live && t == 0)
+        static_for<0, MP>([&](auto jj) {
+          constexpr int j = decltype(jj)::value;
+          if (j >= MP - m1) op[(size_t)(2 * m1 - MP + j) * m2] = make_float2(O[j].x * sc, O[j].y * sc);
+        });
+    } else {
+      // MP <= 2: RC residues per thread accumulate first
+      float2 Olo[MP], Ohi[MP];
+      static_for<0, MP>([&](auto jj) {
+        Olo[decltype(jj)::value] = make_float2(0.f, 0.f);
+        Ohi[decltype(jj)::value] = make_float2(0.f, 0.f);
+      });
+      for (int rr = 0; rr < RC; ++rr) {
+        const int r = t * RC + rr;
+        float2 z[MP];
+        static_for<0, MP>([&](auto qq) {
+          constexpr int q = decltype(qq)::value;
+          z[q] = col[(size_t)(r + q * PH) * m2p];
+        });
+        fft_reg<MP, false>(z);
+        static_for<0, MP>([&](auto jj) {
+          constexpr int j = decltype(jj)::value;
+          const float2 d = z[bitrev(j, LG)];
+          if (j < m1) Olo[j] = cfma(d, twh[(j * r) & (H - 1)], Olo[j]);
+          if (j >= MP - m1) Ohi[j] = cfma(d, twh[((H - MP + j) * r) & (H - 1)], Ohi[j]);
+        });
+      }
+      static_for<0, MP>([&](auto jj) {
+        constexpr int j = decltype(jj)::value;
+        if (j < m1) {
+          float2 v = Olo[j];
+          v = lane_group_sum(v, Tc);
+          if (live && t == 0) op[(size_t)j * m2] = make_float2(v.x * sc, v.y * sc);
+        }
+        if (j >= MP - m1) {
+          float2 v = Ohi[j];
+          v = lane_group_sum(v, Tc);
+          if (live && t == 0) op[(size_t)(2 * m1 - MP + j) * m2] = make_float2(v.x * sc, v.y * sc);
+        }
+      });
+    }
   }
 }
 
@@ -141,140 +340,151 @@ __global__ __launch_bounds__(kThreads) void fno_inv_plane(PlaneInvArgs a) {
   extern __shared__ float2 smem[];
   constexpr int LG = ilog2(MP);
   const int tid = threadIdx.x;
-  const int H = a.H, W = a.W, m1 = a.m1, m2 = a.m2, PH = a.PH, PW = a.PW;
+  const int H = a.H, W = a.W, m1 = a.m1, m2 = a.m2, PH = a.PH, PW = a.PW, ppw = a.ppw;
   const int m2p = m2 + 1;
   const int K = 2 * m1 * m2;
-  float2 *Yh = smem;                       // [2*m1][m2]
-  float2 *Zb = Yh + K;                     // [H][m2 + 1]
-  float2 *tww = Zb + (size_t)H * m2p;      // [W]
+  float2 *tww = smem;                      // [W]
   float2 *twh = tww + W;                   // [H]
-
-  const int plane = blockIdx.x;
-  const float2 *ip = a.in + (size_t)plane * K;
-  for (int v = tid; v < K; v += kThreads) Yh[v] = ip[v];
+  float2 *Yh = twh + H;                    // [ppw][K]
+  float2 *Zb = Yh + (size_t)ppw * K;       // [ppw][H][m2 + 1]
+  float *stage = reinterpret_cast<float *>(Zb + (size_t)ppw * H * m2p);  // [CH][pitch]
+  const int plane0 = blockIdx.x * ppw;
+  const int nlive = min(ppw, a.nplanes - plane0);
   for (int v = tid; v < W; v += kThreads) tww[v] = a.tw_w[v];
   for (int v = tid; v < H; v += kThreads) twh[v] = a.tw_h[v];
+  for (int v = tid; v < nlive * K; v += kThreads) Yh[v] = a.in[(size_t)plane0 * K + v];
   __syncthreads();
 
   // ---- column stage (input pruned): Z[r + PH q][ky] from the 2*m1 rows
-  for (int u = tid; u < m2 * PH; u += kThreads) {
-    const int r = u / m2, ky = u - r * m2;
+  for (int u = tid; u < nlive * PH * m2; u += kThreads) {
+    const int g = u / m2, ky = u - g * m2;
+    const int pl = g / PH, r = g - pl * PH;
+    const float2 *yp = Yh + (size_t)pl * K + ky;
     const float2 wc = twh[(MP * r) & (H - 1)];  // exp(-2 pi i r / PH)
     float2 e[MP];
     static_for<0, MP>([&](auto jj) {
       constexpr int j = decltype(jj)::value;
       float2 s = make_float2(0.f, 0.f);
-      if (j < m1) s = Yh[j * m2 + ky];
-      if (j >= MP - m1) s = cfma(Yh[(2 * m1 - MP + j) * m2 + ky], wc, s);
+      if (j < m1) s = yp[j * m2];
+      if (j >= MP - m1) s = cfma(yp[(2 * m1 - MP + j) * m2], wc, s);
       e[j] = cmulc(s, twh[(j * r) & (H - 1)]);
     });
     fft_reg<MP, true>(e);
+    float2 *zp = Zb + (size_t)pl * H * m2p + ky;
     static_for<0, MP>([&](auto qq) {
       constexpr int q = decltype(qq)::value;
-      Zb[(size_t)(r + q * PH) * m2p + ky] = e[bitrev(q, LG)];
+      zp[(size_t)(r + q * PH) * m2p] = e[bitrev(q, LG)];
     });
   }
   __syncthreads();
 
-  // ---- row stage (c2r): two residues per unit, one complex inverse FFT
-  const int Q = PW >> 1;
-  const size_t yoff = (size_t)plane * H * W;
-  for (int u = tid; u < H * Q; u += kThreads) {
-    const int row = u / Q, p = u - row * Q;
-    const int r0 = 2 * p, r1 = r0 + 1;
-    const float2 *zr = Zb + (size_t)row * m2p;
-    // F_t[j] = g_j Z[j] exp(+2 pi i j r_t / W), g_0 = 1/2, g_j = 1, zero for j >= m2
-    float2 f0[MP], f1[MP];
-    static_for<0, MP>([&](auto jj) {
-      constexpr int j = decltype(jj)::value;
-      if (j < m2) {
-        float2 zv = zr[j];
-        if (j == 0) zv = make_float2(0.5f * zv.x, 0.5f * zv.y);
-        f0[j] = cmulc(zv, tww[(j * r0) & (W - 1)]);
-        f1[j] = cmulc(zv, tww[(j * r1) & (W - 1)]);
-      } else {
-        f0[j] = make_float2(0.f, 0.f);
-        f1[j] = make_float2(0.f, 0.f);
+  // ---- row stage (c2r): two adjacent residues per thread in one complex
+  // inverse FFT (Hermitian parts as real and imaginary parts). Results go to
+  // an LDS chunk of rows, which is then written out with coalesced stores.
+  using CV = ChunkVec<MP, DT>;
+  const int T = PW / 2;
+  const int CH = kThreads / T, pitch = stage_pitch(W, MP);
+  const int nrows = nlive * H;
+  const int nchunks = (nrows + CH - 1) / CH;
+  const size_t gbase = (size_t)plane0 * H * W;
+  for (int c = 0; c < nchunks; ++c) {
+    const int rl = tid / T, t = tid - rl * T;
+    const int grow = c * CH + rl;
+    if (grow < nrows) {
+      const int pl = grow / H, row = grow - pl * H;
+      const float2 *zr = Zb + ((size_t)pl * H + row) * m2p;
+      const int ra = 2 * t, rb = ra + 1;
+      // F_t[j] = g_j Z[j] exp(+2 pi i j r_t / W), g_0 = 1/2, g_j = 1; zero for j >= m2
+      float2 fa[MP], fb[MP], g[MP];
+      static_for<0, MP>([&](auto jj) {
+        constexpr int j = decltype(jj)::value;
+        if (j < m2) {
+          float2 zv = zr[j];
+          if (j == 0) zv = make_float2(0.5f * zv.x, 0.5f * zv.y);
+          fa[j] = cmulc(zv, tww[(j * ra) & (W - 1)]);
+          fb[j] = cmulc(zv, tww[(j * rb) & (W - 1)]);
+        } else {
+          fa[j] = make_float2(0.f, 0.f);
+          fb[j] = make_float2(0.f, 0.f);
+        }
+      });
+      static_for<0, MP>([&](auto jj) {
+        constexpr int j = decltype(jj)::value;
+        constexpr int mj = (MP - j) & (MP - 1);
+        const float2 u0 = make_float2(fa[j].x + fa[mj].x, fa[j].y - fa[mj].y);
+        const float2 u1 = make_float2(fb[j].x + fb[mj].x, fb[j].y - fb[mj].y);
+        g[j] = make_float2(u0.x - u1.y, u0.y + u1.x);
+      });
+      fft_reg<MP, true>(g);
+      float *dst = stage + rl * pitch + ra;
+      static_for<0, MP>([&](auto qq) {
+        constexpr int q = decltype(qq)::value;
+        *reinterpret_cast<float2 *>(dst + q * PW) = g[bitrev(q, LG)];
+      });
+    }
+    __syncthreads();
+    static_for<0, CV::N>([&](auto vv) {
+      constexpr int v = decltype(vv)::value;
+      const int e = (v * kThreads + tid) * CV::V;
+      const int rl2 = e / W, col = e - rl2 * W;
+      if (c * CH + rl2 < nrows) {
+        float o[CV::V];
+        const float2 *sp = reinterpret_cast<const float2 *>(stage + rl2 * pitch + col);
+        static_for<0, CV::V / 2>([&](auto ii) {
+          constexpr int i = decltype(ii)::value;
+          const float2 w2 = sp[i];
+          o[2 * i] = w2.x;
+          o[2 * i + 1] = w2.y;
+        });
+        gstore_vec<DT, CV::V>(a.y, gbase + (size_t)c * CH * W + e, o);
       }
     });
-    // G[j] = (F0[j] + conj F0[-j]) + i (F1[j] + conj F1[-j]); IDFT(G) = y_r0 + i y_r1
-    float2 g[MP];
-    static_for<0, MP>([&](auto jj) {
-      constexpr int j = decltype(jj)::value;
-      constexpr int mj = (MP - j) & (MP - 1);
-      const float2 u0 = make_float2(f0[j].x + f0[mj].x, f0[j].y - f0[mj].y);
-      const float2 u1 = make_float2(f1[j].x + f1[mj].x, f1[j].y - f1[mj].y);
-      g[j] = make_float2(u0.x - u1.y, u0.y + u1.x);
-    });
-    fft_reg<MP, true>(g);
-    const size_t rbase = yoff + (size_t)row * W + r0;
-    static_for<0, MP>([&](auto qq) {
-      constexpr int q = decltype(qq)::value;
-      const float2 v = g[bitrev(q, LG)];
-      store_pair<DT>(a.y, rbase + (size_t)q * PW, v.x, v.y);
-    });
+    __syncthreads();
   }
 }
 
 // --------------------------------------------------------------- launchers
 
-template <int DT>
-static const void *fwd_kernel_ptr(int MP) {
+template <int DT, bool FWD>
+static const void *kernel_for(int MP, int rpt) {
+  if (rpt != 2) return nullptr;
   switch (MP) {
-    case 2: return (const void *)fno_fwd_plane<2, DT>;
-    case 4: return (const void *)fno_fwd_plane<4, DT>;
-    case 8: return (const void *)fno_fwd_plane<8, DT>;
-    case 16: return (const void *)fno_fwd_plane<16, DT>;
-    case 32: return (const void *)fno_fwd_plane<32, DT>;
+    case 2: return FWD ? (const void *)fno_fwd_plane<2, DT> : (const void *)fno_inv_plane<2, DT>;
+    case 4: return FWD ? (const void *)fno_fwd_plane<4, DT> : (const void *)fno_inv_plane<4, DT>;
+    case 8: return FWD ? (const void *)fno_fwd_plane<8, DT> : (const void *)fno_inv_plane<8, DT>;
+    case 16: return FWD ? (const void *)fno_fwd_plane<16, DT> : (const void *)fno_inv_plane<16, DT>;
+    case 32: return FWD ? (const void *)fno_fwd_plane<32, DT> : (const void *)fno_inv_plane<32, DT>;
   }
   return nullptr;
 }
 
-template <int DT>
-static const void *inv_kernel_ptr(int MP) {
-  switch (MP) {
-    case 2: return (const void *)fno_inv_plane<2, DT>;
-    case 4: return (const void *)fno_inv_plane<4, DT>;
-    case 8: return (const void *)fno_inv_plane<8, DT>;
-    case 16: return (const void *)fno_inv_plane<16, DT>;
-    case 32: return (const void *)fno_inv_plane<32, DT>;
-  }
-  return nullptr;
-}
-
-static const void *plane_kernel(bool fwd, int MP, int dtype) {
+static const void *plane_kernel(bool fwd, int MP, int rpt, int dtype) {
   switch (dtype) {
-    case DT_F32: return fwd ? fwd_kernel_ptr<DT_F32>(MP) : inv_kernel_ptr<DT_F32>(MP);
-    case DT_F16: return fwd ? fwd_kernel_ptr<DT_F16>(MP) : inv_kernel_ptr<DT_F16>(MP);
-    case DT_BF16: return fwd ? fwd_kernel_ptr<DT_BF16>(MP) : inv_kernel_ptr<DT_BF16>(MP);
+    case DT_F32: return fwd ? kernel_for<DT_F32, true>(MP, rpt) : kernel_for<DT_F32, false>(MP, rpt);
+    case DT_F16: return fwd ? kernel_for<DT_F16, true>(MP, rpt) : kernel_for<DT_F16, false>(MP, rpt);
+    case DT_BF16: return fwd ? kernel_for<DT_BF16, true>(MP, rpt) : kernel_for<DT_BF16, false>(MP, rpt);
   }
   return nullptr;
 }
 
-hipError_t plane_fwd_prepare(int MP, int dtype, size_t lds) {
-  const void *k = plane_kernel(true, MP, dtype);
+hipError_t plane_prepare(bool fwd, int MP, int rpt, int dtype, size_t lds) {
+  const void *k = plane_kernel(fwd, MP, rpt, dtype);
   if (!k) return hipErrorInvalidValue;
   return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
-hipError_t plane_inv_prepare(int MP, int dtype, size_t lds) {
-  const void *k = plane_kernel(false, MP, dtype);
-  if (!k) return hipErrorInvalidValue;
-  return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-}
-
-hipError_t launch_plane_fwd(const PlaneFwdArgs &a, int MP, int dtype, size_t lds, hipStream_t s) {
-  const void *k = plane_kernel(true, MP, dtype);
+hipError_t launch_plane_fwd(const PlaneFwdArgs &a, int MP, int rpt, int dtype, size_t lds, hipStream_t s) {
+  const void *k = plane_kernel(true, MP, rpt, dtype);
   if (!k) return hipErrorInvalidValue;
   void *args[] = {(void *)&a};
-  return hipLaunchKernel(k, dim3(a.nplanes), dim3(kThreads), args, lds, s);
+  return hipLaunchKernel(k, dim3((a.nplanes + a.ppw - 1) / a.ppw), dim3(kThreads), args, lds, s);
 }
 
-hipError_t launch_plane_inv(const PlaneInvArgs &a, int MP, int dtype, size_t lds, hipStream_t s) {
-  const void *k = plane_kernel(false, MP, dtype);
+hipError_t launch_plane_inv(const PlaneInvArgs &a, int MP, int rpt, int dtype, size_t lds, hipStream_t s) {
+  const void *k = plane_kernel(false, MP, rpt, dtype);
   if (!k) return hipErrorInvalidValue;
   void *args[] = {(void *)&a};
-  return hipLaunchKernel(k, dim3(a.nplanes), dim3(kThreads), args, lds, s);
+  return hipLaunchKernel(k, dim3((a.nplanes + a.ppw - 1) / a.ppw), dim3(kThreads), args, lds, s);
 }
 
 }  // namespace fno

@@ -47,6 +47,7 @@ SMALL = [
     ("rag2d-max", _cfg("r", 2, 2, 3, 2, (16, 16), (8, 8), "uniform"), "f32"),
     ("rag2d-tall", _cfg("r", 2, 2, 4, 6, (256, 64), (3, 32), "uniform"), "bf16"),
     ("rag2d-wide", _cfg("r", 2, 17, 3, 19, (64, 256), (7, 24), "uniform"), "f32"),
+    ("rag2d-mp2", _cfg("r", 2, 1, 2, 3, (256, 256), (1, 2), "uniform"), "f32"),
     ("rag3d-a", _cfg("r", 3, 2, 3, 5, (16, 32, 16), (3, 5, 2), "uniform"), "f32"),
     ("rag3d-b", _cfg("r", 3, 1, 4, 4, (8, 8, 8), (4, 4, 4), "uniform"), "f16"),
     ("rag3d-c", _cfg("r", 3, 3, 2, 1, (32, 16, 64), (16, 8, 5), "uniform"), "bf16"),
