@@ -45,12 +45,14 @@ def _bytes_per_launch(cfg, dtype):
     xh = cfg.batch * cfg.c_in * cfg.n_modes * 8
     yh = cfg.batch * cfg.c_out * cfg.n_modes * 8
     if cfg.ndim == 2:
-        return {"fno_fwd_plane": x + xh, "fno_contract": xh + w + yh, "fno_inv_plane": yh + y}
+        return {"fno_fwd_plane": x + xh, "fno_fwd_plane_mx": x + xh, "fno_contract": xh + w + yh,
+                "fno_inv_plane": yh + y, "fno_inv_plane_mx": yh + y}
     C = 2 * cfg.modes[1] * cfg.modes[2]
     ti = cfg.batch * cfg.c_in * cfg.grid[0] * C * 8
     to = cfg.batch * cfg.c_out * cfg.grid[0] * C * 8
-    return {"fno_fwd_plane": x + ti, "fno_fwd_axis": ti + xh, "fno_contract": xh + w + yh,
-            "fno_inv_axis": yh + to, "fno_inv_plane": to + y}
+    return {"fno_fwd_plane": x + ti, "fno_fwd_plane_mx": x + ti, "fno_fwd_axis": ti + xh,
+            "fno_contract": xh + w + yh, "fno_inv_axis": yh + to, "fno_inv_plane": to + y,
+            "fno_inv_plane_mx": to + y}
 
 
 def to_device(arr, dtype, device="cuda:0"):

@@ -18,9 +18,9 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfno.so")
 
-SOURCES = ["plane_kernels.hip", "axis_kernels.hip", "contract.hip", "pointwise.hip", "fno_api.cpp",
+SOURCES = ["plane_kernels.hip", "plane_mfma.hip", "axis_kernels.hip", "contract.hip", "pointwise.hip", "fno_api.cpp",
            "fno_model.cpp"]
-HEADERS = ["common.hpp", "fft_reg.hpp"]
+HEADERS = ["common.hpp", "fft_reg.hpp", "plane_common.hpp"]
 
 ARCH = "gfx950"
 CFLAGS = [

@@ -79,9 +79,12 @@ __global__ __launch_bounds__(kAxThreads) void fno_inv_axis(AxisArgs a) {
   float2 e[MP];
   static_for<0, MP>([&](auto jj) {
     constexpr int j = decltype(jj)::value;
-    float2 s = make_float2(0.f, 0.f);
-    if (j < m) s = ip[(size_t)j * C + c];
-    if (j >= MP - m) s = cfma(ip[(size_t)(2 * m - MP + j) * C + c], wc, s);
+    // branch-free: out-of-corner rows read row 0 and are selected away
+    const bool lo = j < m, hi = j >= MP - m;
+    const float2 vl = ip[(size_t)(lo ? j : 0) * C + c];
+    const float2 vh = ip[(size_t)(hi ? 2 * m - MP + j : 0) * C + c];
+    const float2 th = cmul(vh, wc);
+    const float2 s = make_float2((lo ? vl.x : 0.f) + (hi ? th.x : 0.f), (lo ? vl.y : 0.f) + (hi ? th.y : 0.f));
     e[j] = cmulc(s, a.tw[(j * r) & (N - 1)]);
   });
   fft_reg<MP, true>(e);

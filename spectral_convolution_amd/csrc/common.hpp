@@ -83,6 +83,25 @@ struct PlaneInvArgs {
   int ppw;  // planes per workgroup
 };
 
+// Plane transforms whose row stage runs on MFMA (fp16 / bf16 storage).
+struct PlaneMxFwdArgs {
+  const void *x;
+  float2 *out;
+  const float2 *tw_h;
+  const uint4 *tf;     // row DFT fragments [NT][W/32][64 lanes] (8 halves each)
+  const uint4 *tf_lo;  // bf16 only: low parts of the same fragments
+  int nplanes, H, W, m1, m2, PH, rc;
+  float scale;
+};
+
+struct PlaneMxInvArgs {
+  const float2 *in;
+  void *y;
+  const float2 *tw_h;
+  const uint4 *tb;  // inverse row fragments [W/16][KBT][64 lanes] (fp16)
+  int nplanes, H, W, m1, m2, PH;
+};
+
 // Pruned c2c DFT along a strided axis: in [vol][N][C] -> out [vol][2*m][C]
 // (forward, times `scale`), or the inverse out [vol][N][C] from [vol][2*m][C].
 struct AxisArgs {
@@ -111,6 +130,13 @@ size_t axis_fwd_lds_bytes(int N, int m, int MP);
 hipError_t plane_prepare(bool fwd, int MP, int rpt, int dtype, size_t lds);
 hipError_t launch_plane_fwd(const PlaneFwdArgs &a, int MP, int rpt, int dtype, size_t lds, hipStream_t s);
 hipError_t launch_plane_inv(const PlaneInvArgs &a, int MP, int rpt, int dtype, size_t lds, hipStream_t s);
+int mx_ntiles(int m2);
+bool mx_supported(int H, int W, int m2, int dtype);
+size_t mx_fwd_lds_bytes(int H, int W, int m2);
+size_t mx_inv_lds_bytes(int H, int W, int m1, int m2);
+hipError_t mx_prepare(bool fwd, int MP, int m2, int W, int dtype, size_t lds);
+hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int MP, int dtype, size_t lds, hipStream_t s);
+hipError_t launch_plane_mx_inv(const PlaneMxInvArgs &a, int MP, int dtype, size_t lds, hipStream_t s);
 hipError_t axis_fwd_prepare(int MP, size_t lds);
 hipError_t launch_axis_fwd(const AxisArgs &a, int MP, size_t lds, hipStream_t s);
 hipError_t launch_axis_inv(const AxisArgs &a, int MP, hipStream_t s);

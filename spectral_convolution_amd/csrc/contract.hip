@@ -20,50 +20,39 @@
 
 namespace fno {
 
-template <int DT>
-__device__ __forceinline__ void load_w4(const void *w, size_t idx, int nvalid, float (&re)[4], float (&im)[4]) {
-  if (nvalid >= 4) {
-    if constexpr (DT == DT_F32) {
-      const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(w) + 2 * idx);
-      const float4 u = p[0], v = p[1];
-      re[0] = u.x; im[0] = u.y; re[1] = u.z; im[1] = u.w;
-      re[2] = v.x; im[2] = v.y; re[3] = v.z; im[3] = v.w;
-    } else {
-      const uint4 u = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(w) + 2 * idx);
-      const uint32_t q[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if constexpr (DT == DT_F16) {
-          half2_t h = __builtin_bit_cast(half2_t, q[t]);
-          re[t] = (float)h.x;
-          im[t] = (float)h.y;
-        } else {
-          re[t] = __uint_as_float(q[t] << 16);
-          im[t] = __uint_as_float(q[t] & 0xffff0000u);
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (t < nvalid) {
-        const float2 v = load_pair<DT>(w, 2 * (idx + t));
-        re[t] = v.x;
-        im[t] = v.y;
-      } else {
-        re[t] = 0.f;
-        im[t] = 0.f;
-      }
-    }
-  }
-}
-
 template <int BB>
 struct Frag {
   float ar[BB], ai[BB], an[BB];
   float wr[4], wi[4];
 };
 
+// four consecutive complex weights (vector load; idx a multiple of 4)
+template <int DT>
+__device__ __forceinline__ void load_w4v(const void *w, size_t idx, float (&re)[4], float (&im)[4]) {
+  if constexpr (DT == DT_F32) {
+    const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(w) + 2 * idx);
+    const float4 u = p[0], v = p[1];
+    re[0] = u.x; im[0] = u.y; re[1] = u.z; im[1] = u.w;
+    re[2] = v.x; im[2] = v.y; re[3] = v.z; im[3] = v.w;
+  } else {
+    const uint4 u = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(w) + 2 * idx);
+    const uint32_t q[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if constexpr (DT == DT_F16) {
+        half2_t h = __builtin_bit_cast(half2_t, q[t]);
+        re[t] = (float)h.x;
+        im[t] = (float)h.y;
+      } else {
+        re[t] = __uint_as_float(q[t] << 16);
+        im[t] = __uint_as_float(q[t] & 0xffff0000u);
+      }
+    }
+  }
+}
+
+// Operands of one input channel i. Loads are unconditional (out-of-range
+// lanes read element 0 and select zero) so they stay in flight together.
 template <int BB, int DT>
 __device__ __forceinline__ void load_frag(const ContractArgs &a, int i, int mode, bool mode_ok, int b0, int nn,
                                           int ol, int nw, bool vec, Frag<BB> &f) {
@@ -71,25 +60,27 @@ __device__ __forceinline__ void load_frag(const ContractArgs &a, int i, int mode
 #pragma unroll
   for (int bb = 0; bb < BB; ++bb) {
     const int b = b0 + 4 * bb + nn;
-    float2 xv = make_float2(0.f, 0.f);
-    if (mode_ok && b < B) xv = a.xh[((size_t)b * Ci + i) * K + mode];
-    f.ar[bb] = xv.x;
-    f.ai[bb] = xv.y;
+    const bool ok = mode_ok && b < B;
+    const float2 xv = a.xh[ok ? ((size_t)b * Ci + i) * K + mode : 0];
+    f.ar[bb] = ok ? xv.x : 0.f;
+    f.ai[bb] = ok ? xv.y : 0.f;
   }
   const size_t widx = ((size_t)(mode_ok ? mode : 0) * Ci + i) * Co + ol;
   if (vec) {
-    load_w4<DT>(a.w, widx, nw, f.wr, f.wi);
+    const bool ok = nw == 4;
+    load_w4v<DT>(a.w, ok ? widx : 0, f.wr, f.wi);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f.wr[t] = ok ? f.wr[t] : 0.f;
+      f.wi[t] = ok ? f.wi[t] : 0.f;
+    }
   } else {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      if (t < nw) {
-        const float2 v = load_pair<DT>(a.w, 2 * (widx + t));
-        f.wr[t] = v.x;
-        f.wi[t] = v.y;
-      } else {
-        f.wr[t] = 0.f;
-        f.wi[t] = 0.f;
-      }
+      const bool ok = t < nw;
+      const float2 v = load_pair<DT>(a.w, 2 * (ok ? widx + t : 0));
+      f.wr[t] = ok ? v.x : 0.f;
+      f.wi[t] = ok ? v.y : 0.f;
     }
   }
 }

@@ -61,6 +61,80 @@ std::vector<float2> twiddles(int n) {
   return t;
 }
 
+uint16_t half_bits(double v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+
+uint16_t bf16_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+float bf16_value(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+
+// cos and sin of 2 pi k / n (k reduced mod n in integers, quarter turns exact)
+void cos_sin_2pi(long k, long n, double &c, double &s) {
+  const long r = ((k % n) + n) % n;
+  const long q = (4 * r) / n, rem = 4 * r - q * n;
+  const double a = (M_PI / 2.0) * (double)rem / (double)n;
+  const double ca = std::cos(a), sa = std::sin(a);
+  switch (q) {
+    case 0: c = ca; s = sa; break;
+    case 1: c = -sa; s = ca; break;
+    case 2: c = -ca; s = -sa; break;
+    default: c = sa; s = -ca; break;
+  }
+}
+
+// Forward row-DFT fragments (B operand, K = w, N = c = 2 ky + re/im):
+// [nt][kb][lane][8], value T[w][c] = cos / -sin (2 pi ky w / W), zero for
+// ky >= m2. Split into a high and (bf16 only) a low part.
+void fwd_fragments(int W, int m2, int NT, bool bf, std::vector<uint16_t> &hi, std::vector<uint16_t> &lo) {
+  const int KB = W / 32;
+  hi.assign((size_t)NT * KB * 64 * 8, 0);
+  lo.assign(hi.size(), 0);
+  for (int nt = 0; nt < NT; ++nt)
+    for (int kb = 0; kb < KB; ++kb)
+      for (int l = 0; l < 64; ++l)
+        for (int i = 0; i < 8; ++i) {
+          const int w = kb * 32 + 8 * (l / 16) + i, c = nt * 16 + l % 16, ky = c / 2;
+          double v = 0.0;
+          if (ky < m2) {
+            double cs, sn;
+            cos_sin_2pi((long)ky * w, W, cs, sn);
+            v = (c & 1) ? -sn : cs;
+          }
+          const size_t at = (((size_t)nt * KB + kb) * 64 + l) * 8 + i;
+          if (bf) {
+            const uint16_t h = bf16_bits((float)v);
+            hi[at] = h;
+            lo[at] = bf16_bits((float)(v - (double)bf16_value(h)));
+          } else {
+            hi[at] = half_bits(v);
+          }
+        }
+}
+
+// Inverse row fragments (B operand, K = c, N = w): [wt][kb][lane][8],
+// value T'[c][w] = g cos / -g sin (2 pi ky w / W), g = 1 for ky = 0, else 2.
+void inv_fragments(int W, int m2, int KBT, std::vector<uint16_t> &tb) {
+  const int NWT = W / 16;
+  tb.assign((size_t)NWT * KBT * 64 * 8, 0);
+  for (int wt = 0; wt < NWT; ++wt)
+    for (int kb = 0; kb < KBT; ++kb)
+      for (int l = 0; l < 64; ++l)
+        for (int i = 0; i < 8; ++i) {
+          const int w = wt * 16 + l % 16, c = kb * 32 + 8 * (l / 16) + i, ky = c / 2;
+          double v = 0.0;
+          if (ky < m2) {
+            double cs, sn;
+            cos_sin_2pi((long)ky * w, W, cs, sn);
+            const double g = ky == 0 ? 1.0 : 2.0;
+            v = (c & 1) ? -g * sn : g * cs;
+          }
+          tb[(((size_t)wt * KBT + kb) * 64 + l) * 8 + i] = half_bits(v);
+        }
+}
+
 }  // namespace
 
 struct fno_plan_s {
@@ -76,6 +150,10 @@ struct fno_plan_s {
   int xN = 0, xm = 0, xMP = 0;
   size_t lds_axis = 0;
   int bb = 1, split = 1;
+  // row stage on MFMA (fp16 / bf16 storage, planes with H >= 64, W >= 64)
+  bool mx = false;
+  int mx_nt = 0, mx_kbt = 0;
+  uint4 *tf = nullptr, *tf_lo = nullptr, *tb = nullptr;
   float2 *tw_h = nullptr, *tw_w = nullptr, *tw_x = nullptr;
   float2 *xh = nullptr, *yh = nullptr, *tbuf = nullptr;
   void *mem = nullptr;
@@ -140,6 +218,13 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
   p.ppw_i = plane_ppw(false, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_i);
   p.lds_fwd = plane_fwd_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP, p.ppw_f);
   p.lds_inv = plane_inv_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP, p.ppw_i);
+  p.mx = mx_supported(p.pH, p.pW, p.pm2, (int)dtype);
+  if (p.mx) {
+    p.mx_nt = mx_ntiles(p.pm2);
+    p.mx_kbt = p.pm2 <= 16 ? 1 : 2;
+    p.lds_fwd = mx_fwd_lds_bytes(p.pH, p.pW, p.pm2);
+    p.lds_inv = mx_inv_lds_bytes(p.pH, p.pW, p.pm1, p.pm2);
+  }
   if (p.lds_fwd > kMaxLds || p.lds_inv > kMaxLds) return FNO_ERR_UNSUPPORTED;
   if (ndim == 3) {
     p.lds_axis = axis_fwd_lds_bytes(p.xN, p.xm, p.xMP);
@@ -248,6 +333,14 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   const size_t o_xh = off; off += al(n_xh * sizeof(float2));
   const size_t o_yh = off; off += al(n_yh * sizeof(float2));
   const size_t o_t = off; off += al(n_t * sizeof(float2));
+  std::vector<uint16_t> tfh, tfl, tbv;
+  if (p->mx) {
+    fwd_fragments(p->pW, p->pm2, p->mx_nt, p->dtype == FNO_BF16, tfh, tfl);
+    inv_fragments(p->pW, p->pm2, p->mx_kbt, tbv);
+  }
+  const size_t o_tf = off; off += al(tfh.size() * 2);
+  const size_t o_tfl = off; off += al(p->dtype == FNO_BF16 ? tfl.size() * 2 : 0);
+  const size_t o_tb = off; off += al(tbv.size() * 2);
   p->ws_bytes = off;
   hipError_t e = hipMalloc(&p->mem, off);
   if (e != hipSuccess) {
@@ -263,6 +356,11 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   p->xh = (float2 *)(base + o_xh);
   p->yh = (float2 *)(base + o_yh);
   p->tbuf = n_t ? (float2 *)(base + o_t) : nullptr;
+  if (p->mx) {
+    p->tf = (uint4 *)(base + o_tf);
+    p->tf_lo = p->dtype == FNO_BF16 ? (uint4 *)(base + o_tfl) : nullptr;
+    p->tb = (uint4 *)(base + o_tb);
+  }
 
   std::vector<float2> th = twiddles(nth), tw = twiddles(ntw);
   e = hipMemcpy(p->tw_h, th.data(), nth * sizeof(float2), hipMemcpyHostToDevice);
@@ -271,8 +369,16 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
     std::vector<float2> tx = twiddles(ntx);
     e = hipMemcpy(p->tw_x, tx.data(), ntx * sizeof(float2), hipMemcpyHostToDevice);
   }
-  if (e == hipSuccess) e = plane_prepare(true, p->pMP, p->rpt, p->dtype, p->lds_fwd);
-  if (e == hipSuccess) e = plane_prepare(false, p->pMP, p->rpt, p->dtype, p->lds_inv);
+  if (e == hipSuccess && p->mx) {
+    e = hipMemcpy(p->tf, tfh.data(), tfh.size() * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess && p->tf_lo) e = hipMemcpy(p->tf_lo, tfl.data(), tfl.size() * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(p->tb, tbv.data(), tbv.size() * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = mx_prepare(true, p->pMP, p->pm2, p->pW, p->dtype, p->lds_fwd);
+    if (e == hipSuccess) e = mx_prepare(false, p->pMP, p->pm2, p->pW, p->dtype, p->lds_inv);
+  } else {
+    if (e == hipSuccess) e = plane_prepare(true, p->pMP, p->rpt, p->dtype, p->lds_fwd);
+    if (e == hipSuccess) e = plane_prepare(false, p->pMP, p->rpt, p->dtype, p->lds_inv);
+  }
   if (e == hipSuccess && ndim == 3) e = axis_fwd_prepare(p->xMP, p->lds_axis);
   if (e == hipSuccess) e = contract_prepare(p->bb, p->dtype, contract_lds_bytes(p->bb, p->split));
   if (e != hipSuccess) {
@@ -310,6 +416,23 @@ static hipError_t run_one(fno_plan_t p, int kind, const void *x, const void *w, 
   const int nd = p->ndim;
   switch (kind) {
     case L_FWD_PLANE: {
+      if (p->mx) {
+        PlaneMxFwdArgs m;
+        m.x = x;
+        m.out = nd == 2 ? p->xh : p->tbuf;
+        m.tw_h = p->tw_h;
+        m.tf = p->tf;
+        m.tf_lo = p->tf_lo;
+        m.nplanes = p->B * p->Ci * (nd == 3 ? p->xN : 1);
+        m.H = p->pH;
+        m.W = p->pW;
+        m.m1 = p->pm1;
+        m.m2 = p->pm2;
+        m.PH = p->pH / p->pMP;
+        m.rc = p->rc;
+        m.scale = nd == 2 ? 1.0f / ((float)p->pH * (float)p->pW) : 1.0f;
+        return launch_plane_mx_fwd(m, p->pMP, p->dtype, p->lds_fwd, s);
+      }
       PlaneFwdArgs a;
       a.x = x;
       a.out = nd == 2 ? p->xh : p->tbuf;
@@ -365,6 +488,20 @@ static hipError_t run_one(fno_plan_t p, int kind, const void *x, const void *w, 
       return launch_axis_inv(a, p->xMP, s);
     }
     case L_INV_PLANE: {
+      if (p->mx) {
+        PlaneMxInvArgs m;
+        m.in = nd == 2 ? p->yh : p->tbuf;
+        m.y = y;
+        m.tw_h = p->tw_h;
+        m.tb = p->tb;
+        m.nplanes = p->B * p->Co * (nd == 3 ? p->xN : 1);
+        m.H = p->pH;
+        m.W = p->pW;
+        m.m1 = p->pm1;
+        m.m2 = p->pm2;
+        m.PH = p->pH / p->pMP;
+        return launch_plane_mx_inv(m, p->pMP, p->dtype, p->lds_inv, s);
+      }
       PlaneInvArgs a;
       a.in = nd == 2 ? p->yh : p->tbuf;
       a.y = y;
@@ -384,13 +521,13 @@ static hipError_t run_one(fno_plan_t p, int kind, const void *x, const void *w, 
   return hipErrorInvalidValue;
 }
 
-static const char *launch_name(int kind) {
+static const char *launch_name(int kind, bool mx) {
   switch (kind) {
-    case L_FWD_PLANE: return "fno_fwd_plane";
+    case L_FWD_PLANE: return mx ? "fno_fwd_plane_mx" : "fno_fwd_plane";
     case L_FWD_AXIS: return "fno_fwd_axis";
     case L_CONTRACT: return "fno_contract";
     case L_INV_AXIS: return "fno_inv_axis";
-    case L_INV_PLANE: return "fno_inv_plane";
+    case L_INV_PLANE: return mx ? "fno_inv_plane_mx" : "fno_inv_plane";
   }
   return "?";
 }
@@ -434,7 +571,7 @@ fno_status_t fno_plan_num_launches(fno_plan_t plan, int *n) {
 
 fno_status_t fno_plan_launch_name(fno_plan_t plan, int index, const char **name) {
   if (!plan || !name || index < 0 || index >= (int)plan->launches.size()) return FNO_ERR_INVALID_ARG;
-  *name = launch_name(plan->launches[index]);
+  *name = launch_name(plan->launches[index], plan->mx);
   return FNO_OK;
 }
 

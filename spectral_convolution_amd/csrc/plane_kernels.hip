@@ -23,64 +23,10 @@
 // per (column, residue), partial sums reduced the same way. LDS holds the
 // row spectra (H x m2 per plane), one staging chunk and the twiddle tables.
 
-#include "common.hpp"
+#include "plane_common.hpp"
 
 namespace fno {
 
-static constexpr int kThreads = 256;
-
-// the value held by another lane of the same 16-lane row (DPP control CTRL)
-template <int CTRL>
-__device__ __forceinline__ float dpp_get(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over each group of T consecutive lanes (T a power of two <= 64, groups
-// aligned to multiples of T); every lane of a group receives the group sum.
-// Butterfly order: lane ^ 1, ^ 2 (quad permutes), ^ 4 (half-row mirror, valid
-// once quads agree), ^ 8 (row mirror), then ^ 16, ^ 32 through LDS permutes.
-__device__ __forceinline__ float lane_group_sum(float v, int T) {
-  if (T >= 2) v += dpp_get<0xB1>(v);    // quad_perm [1,0,3,2]
-  if (T >= 4) v += dpp_get<0x4E>(v);    // quad_perm [2,3,0,1]
-  if (T >= 8) v += dpp_get<0x141>(v);   // row_half_mirror
-  if (T >= 16) v += dpp_get<0x140>(v);  // row_mirror
-  if (T >= 32) v += __shfl_xor(v, 16, 64);
-  if (T >= 64) v += __shfl_xor(v, 32, 64);
-  return v;
-}
-
-__device__ __forceinline__ float2 lane_group_sum(float2 v, int T) {
-  return make_float2(lane_group_sum(v.x, T), lane_group_sum(v.y, T));
-}
-
-template <int CTRL, int N>
-__device__ __forceinline__ void dpp_add_all(float2 (&S)[N]) {
-  static_for<0, N>([&](auto kk) {
-    constexpr int k = decltype(kk)::value;
-    S[k].x += dpp_get<CTRL>(S[k].x);
-    S[k].y += dpp_get<CTRL>(S[k].y);
-  });
-}
-
-template <int N>
-__device__ __forceinline__ void shfl_add_all(float2 (&S)[N], int s) {
-  static_for<0, N>([&](auto kk) {
-    constexpr int k = decltype(kk)::value;
-    S[k].x += __shfl_xor(S[k].x, s, 64);
-    S[k].y += __shfl_xor(S[k].y, s, 64);
-  });
-}
-
-// lane_group_sum applied to a whole array: one uniform branch per level
-template <int N>
-__device__ __forceinline__ void group_sum_all(float2 (&S)[N], int T) {
-  if (T >= 2) dpp_add_all<0xB1>(S);
-  if (T >= 4) dpp_add_all<0x4E>(S);
-  if (T >= 8) dpp_add_all<0x141>(S);
-  if (T >= 16) dpp_add_all<0x140>(S);
-  if (T >= 32) shfl_add_all(S, 16);
-  if (T >= 64) shfl_add_all(S, 32);
-}
 
 // residues per thread along the row axis (two per complex FFT)
 int plane_rpt(int MP, int PW) {
@@ -134,24 +80,42 @@ struct ChunkVec {
   static constexpr int N = 2 * MP / V;                      // vectors per thread per chunk
 };
 
+// V consecutive storage elements (V * element size = 4, 8 or 16 bytes) as
+// one load, widened to fp32
 template <int DT, int V>
 __device__ __forceinline__ void gload_vec(const void *base, size_t idx, float (&v)[V]) {
   if constexpr (DT == DT_F32) {
+    static_assert(V == 2 || V == 4, "fp32 vector of 2 or 4");
     if constexpr (V == 4) {
       const float4 u = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + idx);
       v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
     } else {
-      static_for<0, V / 2>([&](auto cc) {
-        constexpr int c = decltype(cc)::value;
-        const float2 u = *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(base) + idx + 2 * c);
-        v[2 * c] = u.x; v[2 * c + 1] = u.y;
-      });
+      const float2 u = *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(base) + idx);
+      v[0] = u.x; v[1] = u.y;
     }
   } else {
+    static_assert(V == 2 || V == 4 || V == 8, "16-bit vector of 2, 4 or 8");
+    const uint16_t *p = reinterpret_cast<const uint16_t *>(base) + idx;
+    uint32_t w[V / 2];
+    if constexpr (V == 8) {
+      const uint4 u = *reinterpret_cast<const uint4 *>(p);
+      w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+    } else if constexpr (V == 4) {
+      const uint2 u = *reinterpret_cast<const uint2 *>(p);
+      w[0] = u.x; w[1] = u.y;
+    } else {
+      w[0] = *reinterpret_cast<const uint32_t *>(p);
+    }
     static_for<0, V / 2>([&](auto cc) {
       constexpr int c = decltype(cc)::value;
-      const float2 u = load_pair<DT>(base, idx + 2 * c);
-      v[2 * c] = u.x; v[2 * c + 1] = u.y;
+      if constexpr (DT == DT_F16) {
+        const half2_t h = __builtin_bit_cast(half2_t, w[c]);
+        v[2 * c] = (float)h.x;
+        v[2 * c + 1] = (float)h.y;
+      } else {
+        v[2 * c] = __uint_as_float(w[c] << 16);
+        v[2 * c + 1] = __uint_as_float(w[c] & 0xffff0000u);
+      }
     });
   }
 }
@@ -201,7 +165,10 @@ __global__ __launch_bounds__(kThreads) void fno_fwd_plane(PlaneFwdArgs a) {
       constexpr int v = decltype(vv)::value;
       const int e = (v * kThreads + tid) * CV::V;  // element within the chunk
       const int row = c * CH + e / W;
-      if (row < nrows) gload_vec<DT, CV::V>(a.x, gbase + (size_t)c * CH * W + e, pre[v]);
+      // rows past the workgroup's planes read row 0 instead (branch-free;
+      // their values are never used)
+      const size_t off = row < nrows ? (size_t)c * CH * W + e : (size_t)(e % W);
+      gload_vec<DT, CV::V>(a.x, gbase + off, pre[v]);
     });
   };
   fetch(0);
@@ -252,87 +219,8 @@ __global__ __launch_bounds__(kThreads) void fno_fwd_plane(PlaneFwdArgs a) {
     __syncthreads();
   }
 
-  // ---- column stage: c2c along H on the m2 retained columns, kx corners.
-  // One residue per thread (PH <= 64 lanes per column); for MP <= 2, where
-  // PH can exceed 64, RC residues per thread accumulate before the reduction.
-  const int RC = a.rc, Tc = PH / RC;
-  const int K = 2 * m1 * m2;
-  const float sc = a.scale * 0.5f;
-  for (int u = tid; u < nlive * m2 * Tc; u += kThreads) {
-    const int g = u / Tc, t = u - g * Tc;
-    const int pl = g / m2, ky = g - pl * m2;
-    const bool live = true;
-    const float2 *col = R + (size_t)pl * H * m2p + ky;
-    float2 *op = a.out + (size_t)(live ? plane0 + pl : 0) * K + ky;
-    // corner 0: kx = j (j < m1) -> row j; corner 1: kx = H - MP + j
-    // (j >= MP - m1) -> row 2*m1 - MP + j
-    if constexpr (MP > 2) {
-      // one residue per thread; the two corners are formed and reduced in turn
-      const int r = t;
-      float2 z[MP];
-      static_for<0, MP>([&](auto qq) {
-        constexpr int q = decltype(qq)::value;
-        z[q] = col[(size_t)(r + q * PH) * m2p];
-      });
-      fft_reg<MP, false>(z);
-      float2 O[MP];
-      static_for<0, MP>([&](auto jj) {
-        constexpr int j = decltype(jj)::value;
-        O[j] = j < m1 ? cmul(z[bitrev(j, LG)], twh[(j * r) & (H - 1)]) : make_float2(0.f, 0.f);
-      });
-      group_sum_all(O, Tc);
-      if (live && t == 0)
-        static_for<0, MP>([&](auto jj) {
-          constexpr int j = decltype(jj)::value;
-          if (j < m1) op[(size_t)j * m2] = make_float2(O[j].x * sc, O[j].y * sc);
-        });
-      static_for<0, MP>([&](auto jj) {
-        constexpr int j = decltype(jj)::value;
-        O[j] = j >= MP - m1 ? cmul(z[bitrev(j, LG)], twh[((H - MP + j) * r) & (H - 1)]) : make_float2(0.f, 0.f);
-      });
-      group_sum_all(O, Tc);
-      if (live && t == 0)
-        static_for<0, MP>([&](auto jj) {
-          constexpr int j = decltype(jj)::value;
-          if (j >= MP - m1) op[(size_t)(2 * m1 - MP + j) * m2] = make_float2(O[j].x * sc, O[j].y * sc);
-        });
-    } else {
-      // MP <= 2: RC residues per thread accumulate first
-      float2 Olo[MP], Ohi[MP];
-      static_for<0, MP>([&](auto jj) {
-        Olo[decltype(jj)::value] = make_float2(0.f, 0.f);
-        Ohi[decltype(jj)::value] = make_float2(0.f, 0.f);
-      });
-      for (int rr = 0; rr < RC; ++rr) {
-        const int r = t * RC + rr;
-        float2 z[MP];
-        static_for<0, MP>([&](auto qq) {
-          constexpr int q = decltype(qq)::value;
-          z[q] = col[(size_t)(r + q * PH) * m2p];
-        });
-        fft_reg<MP, false>(z);
-        static_for<0, MP>([&](auto jj) {
-          constexpr int j = decltype(jj)::value;
-          const float2 d = z[bitrev(j, LG)];
-          if (j < m1) Olo[j] = cfma(d, twh[(j * r) & (H - 1)], Olo[j]);
-          if (j >= MP - m1) Ohi[j] = cfma(d, twh[((H - MP + j) * r) & (H - 1)], Ohi[j]);
-        });
-      }
-      static_for<0, MP>([&](auto jj) {
-        constexpr int j = decltype(jj)::value;
-        if (j < m1) {
-          float2 v = Olo[j];
-          v = lane_group_sum(v, Tc);
-          if (live && t == 0) op[(size_t)j * m2] = make_float2(v.x * sc, v.y * sc);
-        }
-        if (j >= MP - m1) {
-          float2 v = Ohi[j];
-          v = lane_group_sum(v, Tc);
-          if (live && t == 0) op[(size_t)(2 * m1 - MP + j) * m2] = make_float2(v.x * sc, v.y * sc);
-        }
-      });
-    }
-  }
+  // ---- column stage: c2c along H on the m2 retained columns, kx corners
+  fwd_col_stage<MP>(R, nlive, plane0, H, m1, m2, PH, a.rc, twh, a.out, a.scale * 0.5f);
 }
 
 template <int MP, int DT>
@@ -356,26 +244,7 @@ __global__ __launch_bounds__(kThreads) void fno_inv_plane(PlaneInvArgs a) {
   __syncthreads();
 
   // ---- column stage (input pruned): Z[r + PH q][ky] from the 2*m1 rows
-  for (int u = tid; u < nlive * PH * m2; u += kThreads) {
-    const int g = u / m2, ky = u - g * m2;
-    const int pl = g / PH, r = g - pl * PH;
-    const float2 *yp = Yh + (size_t)pl * K + ky;
-    const float2 wc = twh[(MP * r) & (H - 1)];  // exp(-2 pi i r / PH)
-    float2 e[MP];
-    static_for<0, MP>([&](auto jj) {
-      constexpr int j = decltype(jj)::value;
-      float2 s = make_float2(0.f, 0.f);
-      if (j < m1) s = yp[j * m2];
-      if (j >= MP - m1) s = cfma(yp[(2 * m1 - MP + j) * m2], wc, s);
-      e[j] = cmulc(s, twh[(j * r) & (H - 1)]);
-    });
-    fft_reg<MP, true>(e);
-    float2 *zp = Zb + (size_t)pl * H * m2p + ky;
-    static_for<0, MP>([&](auto qq) {
-      constexpr int q = decltype(qq)::value;
-      zp[(size_t)(r + q * PH) * m2p] = e[bitrev(q, LG)];
-    });
-  }
+  inv_col_stage<MP>(Yh, Zb, nlive, H, m1, m2, PH, twh);
   __syncthreads();
 
   // ---- row stage (c2r): two adjacent residues per thread in one complex

@@ -42,27 +42,39 @@ __device__ __forceinline__ float load1(const void *p, size_t i) {
   else return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(p)[i] << 16);
 }
 
-// four consecutive elements p[i..i+3]: one vector access when all four are in
-// range and the run is 4-element aligned (al), else element by element
-template <int DT>
-__device__ __forceinline__ void load4(const void *p, size_t i, int n, bool al, float (&v)[4]) {
-  if (n >= 4 && al) {
+// Four consecutive elements p[base + p0 .. +3] of a row of P elements, zeros
+// where ok is false or past the row's end. The loads are unconditional (a
+// masked lane reads element 0 of the buffer and discards it) so that the
+// compiler can keep several of them in flight. AL: P is a multiple of 4, so a
+// run is either whole or entirely past the end and one vector load serves it.
+template <int DT, bool AL>
+__device__ __forceinline__ void load4(const void *p, size_t base, long p0, long P, bool ok, float (&v)[4]) {
+  if constexpr (AL) {
+    const bool in = ok && p0 < P;
+    const size_t i = in ? base + (size_t)p0 : 0;
+    float u[4];
     if constexpr (DT == DT_F32) {
-      const float4 u = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(p) + i);
-      v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+      const float4 q = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(p) + i);
+      u[0] = q.x; u[1] = q.y; u[2] = q.z; u[3] = q.w;
     } else {
-      const uint2 u = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(p) + i);
+      const uint2 q = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(p) + i);
       if constexpr (DT == DT_F16) {
-        const half2_t h0 = __builtin_bit_cast(half2_t, u.x), h1 = __builtin_bit_cast(half2_t, u.y);
-        v[0] = (float)h0.x; v[1] = (float)h0.y; v[2] = (float)h1.x; v[3] = (float)h1.y;
+        const half2_t h0 = __builtin_bit_cast(half2_t, q.x), h1 = __builtin_bit_cast(half2_t, q.y);
+        u[0] = (float)h0.x; u[1] = (float)h0.y; u[2] = (float)h1.x; u[3] = (float)h1.y;
       } else {
-        v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
-        v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+        u[0] = __uint_as_float(q.x << 16); u[1] = __uint_as_float(q.x & 0xffff0000u);
+        u[2] = __uint_as_float(q.y << 16); u[3] = __uint_as_float(q.y & 0xffff0000u);
       }
     }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[t] = in ? u[t] : 0.f;
   } else {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) v[t] = t < n ? load1<DT>(p, i + t) : 0.f;
+    for (int t = 0; t < 4; ++t) {
+      const bool in = ok && p0 + t < P;
+      const float u = load1<DT>(p, in ? base + (size_t)(p0 + t) : 0);
+      v[t] = in ? u : 0.f;
+    }
   }
 }
 
@@ -99,7 +111,7 @@ __device__ void stage_weights(const void *A, int O, int I, int o0, int Ipad, flo
   }
 }
 
-template <int DT>
+template <int DT, bool AL>
 __global__ __launch_bounds__(kPwThreads) void fno_channel_mix(MixArgs a) {
   __shared__ float w[kOB * kMaxI];
   __shared__ float bias[kOB];
@@ -114,21 +126,22 @@ __global__ __launch_bounds__(kPwThreads) void fno_channel_mix(MixArgs a) {
   __syncthreads();
 
   const int kr = lane >> 4, n = lane & 15;
-  const bool al = (P & 3) == 0;
   const size_t xb = (size_t)b * I * P, yb = (size_t)b * O * P;
   const long ntiles = (P + 63) / 64;
   for (long tile = (long)blockIdx.x * 4 + wv; tile < ntiles; tile += (long)gridDim.x * 4) {
     const long p0 = tile * 64 + 4 * n;
-    const int np = (int)min((long)4, max(0L, P - p0));
     v4f acc[4][4];
 #pragma unroll
     for (int mo = 0; mo < 4; ++mo)
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc[mo][t] = v4f{0.f, 0.f, 0.f, 0.f};
+    // channel k0 + kr, fetched one step ahead of its MFMAs
+    float xn[4];
+    load4<DT, AL>(a.x, xb + (size_t)(kr < I ? kr : 0) * P, p0, P, kr < I, xn);
     for (int k0 = 0; k0 < Ipad; k0 += 4) {
-      const int i = k0 + kr;
-      float xv[4];
-      load4<DT>(a.x, xb + (size_t)(i < I ? i : 0) * P + p0, i < I ? np : 0, al, xv);
+      const int i = k0 + kr, inext = i + 4;
+      float xv[4] = {xn[0], xn[1], xn[2], xn[3]};
+      load4<DT, AL>(a.x, xb + (size_t)(inext < I ? inext : 0) * P, p0, P, inext < I, xn);
 #pragma unroll
       for (int mo = 0; mo < 4; ++mo) {
         const float av = w[(16 * mo + n) * Ipad + i];
@@ -138,25 +151,27 @@ __global__ __launch_bounds__(kPwThreads) void fno_channel_mix(MixArgs a) {
       }
     }
     // accumulator register j of lane l: row 4*(l/16) + j, column l%16
+    float ad[4][4][4];
+#pragma unroll
+    for (int mo = 0; mo < 4; ++mo)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int o = o0 + 16 * mo + 4 * kr + j;
+        load4<DT, AL>(a.add ? a.add : a.x, yb + (size_t)(o < O ? o : 0) * P, p0, P, a.add && o < O, ad[mo][j]);
+      }
 #pragma unroll
     for (int mo = 0; mo < 4; ++mo)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int ol = 16 * mo + 4 * kr + j, o = o0 + ol;
-        if (o >= O || np <= 0) continue;
-        float v[4] = {acc[mo][0][j] + bias[ol], acc[mo][1][j] + bias[ol], acc[mo][2][j] + bias[ol],
-                      acc[mo][3][j] + bias[ol]};
-        if (a.add) {
-          float ad[4];
-          load4<DT>(a.add, yb + (size_t)o * P + p0, np, al, ad);
+        if (o >= O || p0 >= P) continue;
+        float v[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) v[t] += ad[t];
+        for (int t = 0; t < 4; ++t) {
+          v[t] = acc[mo][t][j] + bias[ol] + ad[mo][j][t];
+          if (a.act == 1) v[t] = gelu(v[t]);
         }
-        if (a.act == 1) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) v[t] = gelu(v[t]);
-        }
-        store4<DT>(a.y, yb + (size_t)o * P + p0, np, al, v);
+        store4<DT>(a.y, yb + (size_t)o * P + p0, (int)min((long)4, P - p0), AL, v);
       }
   }
 }
@@ -164,7 +179,7 @@ __global__ __launch_bounds__(kPwThreads) void fno_channel_mix(MixArgs a) {
 static constexpr int kMaxJ = 128;
 static constexpr int kMaxC = 4;
 
-template <int DT>
+template <int DT, bool AL>
 __global__ __launch_bounds__(kPwThreads) void fno_projection(ProjArgs a) {
   __shared__ float q1w[kMaxJ * 64];  // [J][Ipad], Ipad <= 64
   __shared__ float q1b[kMaxJ];
@@ -188,13 +203,20 @@ __global__ __launch_bounds__(kPwThreads) void fno_projection(ProjArgs a) {
   __syncthreads();
 
   const int kr = lane >> 4, n = lane & 15;
-  const bool al = (P & 3) == 0;
   const size_t xb = (size_t)b * I * P, yb = (size_t)b * C * P;
   const long ntiles = (P + 63) / 64;
   for (long tile = (long)blockIdx.x * 4 + wv; tile < ntiles; tile += (long)gridDim.x * 4) {
     const long p0 = tile * 64 + 4 * n;
     const int np = (int)min((long)4, max(0L, P - p0));
     float part[kMaxC][4];
+    // the whole input column (I <= 64 channels: 16 steps of 4) is fetched
+    // once per tile, before the first MFMA, and reused by both hidden chunks
+    float xs[16][4];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int i = 4 * k + kr;
+      load4<DT, AL>(a.x, xb + (size_t)(i < I ? i : 0) * P, p0, P, i < I, xs[k]);
+    }
 #pragma unroll
     for (int c = 0; c < kMaxC; ++c)
 #pragma unroll
@@ -205,16 +227,16 @@ __global__ __launch_bounds__(kPwThreads) void fno_projection(ProjArgs a) {
       for (int mo = 0; mo < 4; ++mo)
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[mo][t] = v4f{0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < Ipad; k0 += 4) {
-        const int i = k0 + kr;
-        float xv[4];
-        load4<DT>(a.x, xb + (size_t)(i < I ? i : 0) * P + p0, i < I ? np : 0, al, xv);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (4 * k >= Ipad) break;
+        const int i = 4 * k + kr;
 #pragma unroll
         for (int mo = 0; mo < 4; ++mo) {
           const float av = q1w[(jc + 16 * mo + n) * Ipad + i];
 #pragma unroll
           for (int t = 0; t < 4; ++t)
-            acc[mo][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, xv[t], acc[mo][t], 0, 0, 0);
+            acc[mo][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, xs[k][t], acc[mo][t], 0, 0, 0);
         }
       }
 #pragma unroll
@@ -242,7 +264,7 @@ __global__ __launch_bounds__(kPwThreads) void fno_projection(ProjArgs a) {
     if (kr == 0 && np > 0) {
       for (int c = 0; c < C; ++c) {
         float v[4] = {part[c][0], part[c][1], part[c][2], part[c][3]};
-        store4<DT>(a.y, yb + (size_t)c * P + p0, np, al, v);
+        store4<DT>(a.y, yb + (size_t)c * P + p0, np, AL, v);
       }
     }
   }
@@ -261,9 +283,13 @@ hipError_t launch_channel_mix(const void *x, const void *A, const void *bias, co
   MixArgs a{x, A, bias, add, y, B, I, O, P, act};
   dim3 grid(pw_blocks(P), (O + kOB - 1) / kOB, B);
   void *args[] = {(void *)&a};
-  const void *k = dtype == DT_F32 ? (const void *)fno_channel_mix<DT_F32>
-                  : dtype == DT_F16 ? (const void *)fno_channel_mix<DT_F16>
-                                    : (const void *)fno_channel_mix<DT_BF16>;
+  const bool al = (P & 3) == 0;
+  const void *k = dtype == DT_F32 ? (al ? (const void *)fno_channel_mix<DT_F32, true>
+                                        : (const void *)fno_channel_mix<DT_F32, false>)
+                  : dtype == DT_F16 ? (al ? (const void *)fno_channel_mix<DT_F16, true>
+                                          : (const void *)fno_channel_mix<DT_F16, false>)
+                                    : (al ? (const void *)fno_channel_mix<DT_BF16, true>
+                                          : (const void *)fno_channel_mix<DT_BF16, false>);
   return hipLaunchKernel(k, grid, dim3(kPwThreads), args, 0, s);
 }
 
@@ -272,9 +298,13 @@ hipError_t launch_projection(const void *x, const void *Q1, const void *q1, cons
   ProjArgs a{x, Q1, q1, Q2, q2, y, B, I, J, C, P};
   dim3 grid(pw_blocks(P), 1, B);
   void *args[] = {(void *)&a};
-  const void *k = dtype == DT_F32 ? (const void *)fno_projection<DT_F32>
-                  : dtype == DT_F16 ? (const void *)fno_projection<DT_F16>
-                                    : (const void *)fno_projection<DT_BF16>;
+  const bool al = (P & 3) == 0;
+  const void *k = dtype == DT_F32 ? (al ? (const void *)fno_projection<DT_F32, true>
+                                        : (const void *)fno_projection<DT_F32, false>)
+                  : dtype == DT_F16 ? (al ? (const void *)fno_projection<DT_F16, true>
+                                          : (const void *)fno_projection<DT_F16, false>)
+                                    : (al ? (const void *)fno_projection<DT_BF16, true>
+                                          : (const void *)fno_projection<DT_BF16, false>);
   return hipLaunchKernel(k, grid, dim3(kPwThreads), args, 0, s);
 }
 

@@ -130,6 +130,10 @@ def test_launch_structure():
     try:
         assert [fno.fno_plan_launch_name(p2, i) for i in range(fno.fno_plan_num_launches(p2))] == \
             ["fno_fwd_plane", "fno_contract", "fno_inv_plane"]
+        p4 = fno.fno_plan_create(2, 1, 2, 2, (128, 128), (16, 16), "f16", 0)
+        assert fno.fno_plan_launch_name(p4, 0) == "fno_fwd_plane_mx"
+        assert fno.fno_plan_launch_name(p4, 2) == "fno_inv_plane_mx"
+        fno.fno_plan_destroy(p4)
         assert fno.fno_plan_num_launches(p3) == 5
         assert fno.fno_plan_workspace_bytes(p2) > 0
     finally:
