@@ -83,23 +83,29 @@ struct PlaneInvArgs {
   int ppw;  // planes per workgroup
 };
 
-// Plane transforms whose row stage runs on MFMA (fp16 / bf16 storage).
+// Plane transforms of fp16 / bf16 planes as matrix-core products
+// (H in [64, 256], W in {64, 128, 256}, m1, m2 <= 32). Fragment tables hold
+// 8 halves per lane in MFMA operand order.
 struct PlaneMxFwdArgs {
   const void *x;
-  float2 *out;
-  const float2 *tw_h;
-  const uint4 *tf;     // row DFT fragments [NT][W/32][64 lanes] (8 halves each)
+  float2 *out;         // [nplanes][2 m1][m2] complex, times `scale`
+  const float2 *tw_h;  // exp(-2 pi i k / H), k < H
+  const uint4 *tf;     // row DFT, B operand [NT][W/32][64]
   const uint4 *tf_lo;  // bf16 only: low parts of the same fragments
-  int nplanes, H, W, m1, m2, PH, rc;
+  const uint4 *ef;     // column DFT of a 64-row block, A operand [MT][4][64]
+  int nplanes, H, W, m1, m2;
+  int nt, mt, nn, lgW;  // column tiles of R, m-tiles of X, 16-wide ky tiles, log2 W
   float scale;
 };
 
 struct PlaneMxInvArgs {
-  const float2 *in;
+  const float2 *in;    // [nplanes][2 m1][m2] complex
   void *y;
-  const float2 *tw_h;
-  const uint4 *tb;  // inverse row fragments [W/16][KBT][64 lanes] (fp16)
-  int nplanes, H, W, m1, m2, PH;
+  const float2 *tw_h;  // exp(-2 pi i k / H), k < H
+  const uint4 *ef;     // inverse column DFT of a 64-row block, A operand [8][kb1][64]
+  const uint4 *tb;     // inverse row DFT, B operand [W/16][nn][64]
+  int nplanes, H, W, m1, m2;
+  int nn, kb1, lg4m1;  // 16-wide ky tiles, 32-deep blocks of 4 m1, ceil(log2(4 m1))
 };
 
 // Pruned c2c DFT along a strided axis: in [vol][N][C] -> out [vol][2*m][C]
@@ -131,12 +137,12 @@ hipError_t plane_prepare(bool fwd, int MP, int rpt, int dtype, size_t lds);
 hipError_t launch_plane_fwd(const PlaneFwdArgs &a, int MP, int rpt, int dtype, size_t lds, hipStream_t s);
 hipError_t launch_plane_inv(const PlaneInvArgs &a, int MP, int rpt, int dtype, size_t lds, hipStream_t s);
 int mx_ntiles(int m2);
-bool mx_supported(int H, int W, int m2, int dtype);
-size_t mx_fwd_lds_bytes(int H, int W, int m2);
-size_t mx_inv_lds_bytes(int H, int W, int m1, int m2);
-hipError_t mx_prepare(bool fwd, int MP, int m2, int W, int dtype, size_t lds);
-hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int MP, int dtype, size_t lds, hipStream_t s);
-hipError_t launch_plane_mx_inv(const PlaneMxInvArgs &a, int MP, int dtype, size_t lds, hipStream_t s);
+bool mx_supported(int H, int W, int m1, int m2, int dtype);
+size_t mx_fwd_lds_bytes(int H, int W);
+size_t mx_inv_lds_bytes(int H, int W);
+hipError_t mx_prepare(bool fwd, int W, int dtype, size_t lds);
+hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int dtype, size_t lds, hipStream_t s);
+hipError_t launch_plane_mx_inv(const PlaneMxInvArgs &a, int dtype, size_t lds, hipStream_t s);
 hipError_t axis_fwd_prepare(int MP, size_t lds);
 hipError_t launch_axis_fwd(const AxisArgs &a, int MP, size_t lds, hipStream_t s);
 hipError_t launch_axis_inv(const AxisArgs &a, int MP, hipStream_t s);

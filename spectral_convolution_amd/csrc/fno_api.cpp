@@ -135,6 +135,57 @@ void inv_fragments(int W, int m2, int KBT, std::vector<uint16_t> &tb) {
         }
 }
 
+// Column DFT of one 64-row block, forward (A operand, M = (q, re/im),
+// K = (j, re/im)): [mt][kb][lane][8]. Row m = 2q + po, column k = 2j + pi of
+// the real form of e^{-i theta}, theta = 2 pi kx(q) j / H:
+// [[cos, sin], [-sin, cos]]; zero rows for q >= 2 m1.
+void fwd_col_fragments(int H, int m1, int MT, std::vector<uint16_t> &ef) {
+  ef.assign((size_t)MT * 4 * 64 * 8, 0);
+  for (int mt = 0; mt < MT; ++mt)
+    for (int kb = 0; kb < 4; ++kb)
+      for (int l = 0; l < 64; ++l)
+        for (int i = 0; i < 8; ++i) {
+          const int m = mt * 16 + l % 16, k = kb * 32 + 8 * (l / 16) + i;
+          const int q = m >> 1, po = m & 1, j = k >> 1, pi = k & 1;
+          double v = 0.0;
+          if (q < 2 * m1) {
+            const int kx = q < m1 ? q : H - 2 * m1 + q;
+            double cs, sn;
+            cos_sin_2pi((long)kx * j, H, cs, sn);
+            v = po == 0 ? (pi == 0 ? cs : sn) : (pi == 0 ? -sn : cs);
+          }
+          ef[(((size_t)mt * 4 + kb) * 64 + l) * 8 + i] = half_bits(v);
+        }
+}
+
+// Column DFT of one 64-row block, inverse (A operand, M = (j, re/im),
+// K = (q, re/im)): [8][kb1][lane][8], real form of e^{+i theta}:
+// [[cos, -sin], [sin, cos]]; zero columns for q >= 2 m1.
+void inv_col_fragments(int H, int m1, int KB1, std::vector<uint16_t> &ef) {
+  ef.assign((size_t)8 * KB1 * 64 * 8, 0);
+  for (int mt = 0; mt < 8; ++mt)
+    for (int kb = 0; kb < KB1; ++kb)
+      for (int l = 0; l < 64; ++l)
+        for (int i = 0; i < 8; ++i) {
+          const int m = mt * 16 + l % 16, k = kb * 32 + 8 * (l / 16) + i;
+          const int j = m >> 1, po = m & 1, q = k >> 1, pi = k & 1;
+          double v = 0.0;
+          if (q < 2 * m1) {
+            const int kx = q < m1 ? q : H - 2 * m1 + q;
+            double cs, sn;
+            cos_sin_2pi((long)kx * j, H, cs, sn);
+            v = po == 0 ? (pi == 0 ? cs : -sn) : (pi == 0 ? sn : cs);
+          }
+          ef[(((size_t)mt * KB1 + kb) * 64 + l) * 8 + i] = half_bits(v);
+        }
+}
+
+static int ceil_log2(int v) {
+  int e = 0;
+  while ((1 << e) < v) ++e;
+  return e;
+}
+
 }  // namespace
 
 struct fno_plan_s {
@@ -152,8 +203,8 @@ struct fno_plan_s {
   int bb = 1, split = 1;
   // row stage on MFMA (fp16 / bf16 storage, planes with H >= 64, W >= 64)
   bool mx = false;
-  int mx_nt = 0, mx_kbt = 0;
-  uint4 *tf = nullptr, *tf_lo = nullptr, *tb = nullptr;
+  int mx_nt = 0, mx_mt = 0, mx_nn = 0, mx_kb1 = 0, mx_lgW = 0, mx_lg4m1 = 0;
+  uint4 *tf = nullptr, *tf_lo = nullptr, *tb = nullptr, *ef_f = nullptr, *ef_i = nullptr;
   float2 *tw_h = nullptr, *tw_w = nullptr, *tw_x = nullptr;
   float2 *xh = nullptr, *yh = nullptr, *tbuf = nullptr;
   void *mem = nullptr;
@@ -218,12 +269,16 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
   p.ppw_i = plane_ppw(false, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_i);
   p.lds_fwd = plane_fwd_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP, p.ppw_f);
   p.lds_inv = plane_inv_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP, p.ppw_i);
-  p.mx = mx_supported(p.pH, p.pW, p.pm2, (int)dtype);
+  p.mx = mx_supported(p.pH, p.pW, p.pm1, p.pm2, (int)dtype);
   if (p.mx) {
     p.mx_nt = mx_ntiles(p.pm2);
-    p.mx_kbt = p.pm2 <= 16 ? 1 : 2;
-    p.lds_fwd = mx_fwd_lds_bytes(p.pH, p.pW, p.pm2);
-    p.lds_inv = mx_inv_lds_bytes(p.pH, p.pW, p.pm1, p.pm2);
+    p.mx_mt = (p.pm1 + 3) / 4;
+    p.mx_nn = (p.pm2 + 15) / 16;
+    p.mx_kb1 = (p.pm1 + 7) / 8;
+    p.mx_lgW = ceil_log2(p.pW);
+    p.mx_lg4m1 = ceil_log2(4 * p.pm1);
+    p.lds_fwd = mx_fwd_lds_bytes(p.pH, p.pW);
+    p.lds_inv = mx_inv_lds_bytes(p.pH, p.pW);
   }
   if (p.lds_fwd > kMaxLds || p.lds_inv > kMaxLds) return FNO_ERR_UNSUPPORTED;
   if (ndim == 3) {
@@ -333,14 +388,18 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   const size_t o_xh = off; off += al(n_xh * sizeof(float2));
   const size_t o_yh = off; off += al(n_yh * sizeof(float2));
   const size_t o_t = off; off += al(n_t * sizeof(float2));
-  std::vector<uint16_t> tfh, tfl, tbv;
+  std::vector<uint16_t> tfh, tfl, tbv, efv, eiv;
   if (p->mx) {
     fwd_fragments(p->pW, p->pm2, p->mx_nt, p->dtype == FNO_BF16, tfh, tfl);
-    inv_fragments(p->pW, p->pm2, p->mx_kbt, tbv);
+    inv_fragments(p->pW, p->pm2, p->mx_nn, tbv);
+    fwd_col_fragments(p->pH, p->pm1, p->mx_mt, efv);
+    inv_col_fragments(p->pH, p->pm1, p->mx_kb1, eiv);
   }
   const size_t o_tf = off; off += al(tfh.size() * 2);
   const size_t o_tfl = off; off += al(p->dtype == FNO_BF16 ? tfl.size() * 2 : 0);
   const size_t o_tb = off; off += al(tbv.size() * 2);
+  const size_t o_ef = off; off += al(efv.size() * 2);
+  const size_t o_ei = off; off += al(eiv.size() * 2);
   p->ws_bytes = off;
   hipError_t e = hipMalloc(&p->mem, off);
   if (e != hipSuccess) {
@@ -360,6 +419,8 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
     p->tf = (uint4 *)(base + o_tf);
     p->tf_lo = p->dtype == FNO_BF16 ? (uint4 *)(base + o_tfl) : nullptr;
     p->tb = (uint4 *)(base + o_tb);
+    p->ef_f = (uint4 *)(base + o_ef);
+    p->ef_i = (uint4 *)(base + o_ei);
   }
 
   std::vector<float2> th = twiddles(nth), tw = twiddles(ntw);
@@ -373,8 +434,10 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
     e = hipMemcpy(p->tf, tfh.data(), tfh.size() * 2, hipMemcpyHostToDevice);
     if (e == hipSuccess && p->tf_lo) e = hipMemcpy(p->tf_lo, tfl.data(), tfl.size() * 2, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(p->tb, tbv.data(), tbv.size() * 2, hipMemcpyHostToDevice);
-    if (e == hipSuccess) e = mx_prepare(true, p->pMP, p->pm2, p->pW, p->dtype, p->lds_fwd);
-    if (e == hipSuccess) e = mx_prepare(false, p->pMP, p->pm2, p->pW, p->dtype, p->lds_inv);
+    if (e == hipSuccess) e = hipMemcpy(p->ef_f, efv.data(), efv.size() * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(p->ef_i, eiv.data(), eiv.size() * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = mx_prepare(true, p->pW, p->dtype, p->lds_fwd);
+    if (e == hipSuccess) e = mx_prepare(false, p->pW, p->dtype, p->lds_inv);
   } else {
     if (e == hipSuccess) e = plane_prepare(true, p->pMP, p->rpt, p->dtype, p->lds_fwd);
     if (e == hipSuccess) e = plane_prepare(false, p->pMP, p->rpt, p->dtype, p->lds_inv);
@@ -423,15 +486,18 @@ static hipError_t run_one(fno_plan_t p, int kind, const void *x, const void *w, 
         m.tw_h = p->tw_h;
         m.tf = p->tf;
         m.tf_lo = p->tf_lo;
+        m.ef = p->ef_f;
         m.nplanes = p->B * p->Ci * (nd == 3 ? p->xN : 1);
         m.H = p->pH;
         m.W = p->pW;
         m.m1 = p->pm1;
         m.m2 = p->pm2;
-        m.PH = p->pH / p->pMP;
-        m.rc = p->rc;
+        m.nt = p->mx_nt;
+        m.mt = p->mx_mt;
+        m.nn = p->mx_nn;
+        m.lgW = p->mx_lgW;
         m.scale = nd == 2 ? 1.0f / ((float)p->pH * (float)p->pW) : 1.0f;
-        return launch_plane_mx_fwd(m, p->pMP, p->dtype, p->lds_fwd, s);
+        return launch_plane_mx_fwd(m, p->dtype, p->lds_fwd, s);
       }
       PlaneFwdArgs a;
       a.x = x;
@@ -494,13 +560,16 @@ static hipError_t run_one(fno_plan_t p, int kind, const void *x, const void *w, 
         m.y = y;
         m.tw_h = p->tw_h;
         m.tb = p->tb;
+        m.ef = p->ef_i;
         m.nplanes = p->B * p->Co * (nd == 3 ? p->xN : 1);
         m.H = p->pH;
         m.W = p->pW;
         m.m1 = p->pm1;
         m.m2 = p->pm2;
-        m.PH = p->pH / p->pMP;
-        return launch_plane_mx_inv(m, p->pMP, p->dtype, p->lds_inv, s);
+        m.nn = p->mx_nn;
+        m.kb1 = p->mx_kb1;
+        m.lg4m1 = p->mx_lg4m1;
+        return launch_plane_mx_inv(m, p->dtype, p->lds_inv, s);
       }
       PlaneInvArgs a;
       a.in = nd == 2 ? p->yh : p->tbuf;

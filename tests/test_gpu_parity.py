@@ -51,6 +51,13 @@ SMALL = [
     ("rag3d-a", _cfg("r", 3, 2, 3, 5, (16, 32, 16), (3, 5, 2), "uniform"), "f32"),
     ("rag3d-b", _cfg("r", 3, 1, 4, 4, (8, 8, 8), (4, 4, 4), "uniform"), "f16"),
     ("rag3d-c", _cfg("r", 3, 3, 2, 1, (32, 16, 64), (16, 8, 5), "uniform"), "bf16"),
+    # fp16 / bf16 planes on the matrix-core path: partial tiles in every
+    # product, the largest and smallest mode counts, 3D slabs
+    ("mx-2d-rag", _cfg("r", 2, 3, 5, 2, (128, 64), (13, 5), "uniform"), "bf16"),
+    ("mx-2d-m1max", _cfg("r", 2, 1, 2, 3, (64, 256), (32, 32), "uniform"), "f16"),
+    ("mx-2d-m1", _cfg("r", 2, 2, 3, 1, (64, 64), (1, 1), "uniform"), "bf16"),
+    ("mx-2d-c4", _cfg("r", 2, 1, 4, 4, (256, 256), (24, 24)), "f16"),
+    ("mx-3d", _cfg("r", 3, 1, 3, 2, (8, 64, 128), (3, 12, 20), "uniform"), "f16"),
 ]
 
 
@@ -65,6 +72,22 @@ def test_parity_small(case):
     err = rel_l2(got, ref)
     print(f"[parity] {name} rel_l2={err:.3e}", flush=True)
     assert err <= TOL[dtype], f"{name}: rel L2 {err:.3e} > {TOL[dtype]}"
+
+
+@pytest.mark.parametrize("dtype,scale", [("f16", 2.0 ** -12), ("f16", 2.0 ** 10), ("bf16", 2.0 ** -60),
+                                         ("bf16", 2.0 ** 60)])
+def test_parity_magnitude(dtype, scale):
+    """The half-precision plane products rescale by powers of two chosen from
+    the data; inputs far from unit magnitude must keep the same accuracy."""
+    cfg = _cfg("m", 2, 2, 3, 3, (128, 128), (16, 16), seed=7)
+    inp = wl.layer_inputs(cfg, dtype)
+    xs = wl.round_to_storage(inp["x64"] * scale, dtype)
+    x64 = wl.storage_to_float64(xs, dtype)
+    got, _ = run_layer(2, 2, 3, 3, cfg.grid, cfg.modes, dtype, xs, inp["w"])
+    ref = oracle.spectral_conv2d(x64, inp["w64"], *cfg.modes)
+    err = rel_l2(got, ref)
+    print(f"[parity-mag] {dtype} scale={scale:.3g} rel_l2={err:.3e}", flush=True)
+    assert err <= TOL[dtype]
 
 
 FULL = [("c1", "f32", (0, 15)), ("c1", "f16", (0, 15)), ("c2", "f16", (0, 31)),
