@@ -18,12 +18,19 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (quiet NaN preserved)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits, round to nearest even (one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// two fp32 -> packed bf16 pair (a in the low half), round to nearest even
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  bf16x2_t v;
+  v.x = (__bf16)a;
+  v.y = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Load two adjacent storage elements p[0], p[1] as fp32 (p 2-element aligned).
@@ -51,7 +58,7 @@ __device__ __forceinline__ void store_pair(void *base, size_t idx, float a, floa
     h.y = (_Float16)b;
     *reinterpret_cast<half2_t *>(reinterpret_cast<_Float16 *>(base) + idx) = h;
   } else {
-    uint32_t v = f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+    uint32_t v = f32x2_to_bf16x2(a, b);
     *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(base) + idx) = v;
   }
 }
@@ -90,8 +97,7 @@ struct PlaneMxFwdArgs {
   const void *x;
   float2 *out;         // [nplanes][2 m1][m2] complex, times `scale`
   const float2 *tw_h;  // exp(-2 pi i k / H), k < H
-  const uint4 *tf;     // row DFT, B operand [NT][W/32][64]
-  const uint4 *tf_lo;  // bf16 only: low parts of the same fragments
+  const uint4 *tf;     // row DFT, A operand of the transposed product [NT][W/32][64]
   const uint4 *ef;     // column DFT of a 64-row block, A operand [MT][4][64]
   int nplanes, H, W, m1, m2;
   int nt, mt, nn, lgW;  // column tiles of R, m-tiles of X, 16-wide ky tiles, log2 W
@@ -140,9 +146,10 @@ int mx_ntiles(int m2);
 bool mx_supported(int H, int W, int m1, int m2, int dtype);
 size_t mx_fwd_lds_bytes(int H, int W);
 size_t mx_inv_lds_bytes(int H, int W);
-hipError_t mx_prepare(bool fwd, int W, int dtype, size_t lds);
-hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int dtype, size_t lds, hipStream_t s);
-hipError_t launch_plane_mx_inv(const PlaneMxInvArgs &a, int dtype, size_t lds, hipStream_t s);
+hipError_t mx_prepare(bool fwd, int W, int m2, int dtype, size_t lds);
+hipError_t mx_grid(bool fwd, int W, int m2, int dtype, size_t lds, int device, int nplanes, int *grid);
+hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int grid, int dtype, size_t lds, hipStream_t s);
+hipError_t launch_plane_mx_inv(const PlaneMxInvArgs &a, int grid, int dtype, size_t lds, hipStream_t s);
 hipError_t axis_fwd_prepare(int MP, size_t lds);
 hipError_t launch_axis_fwd(const AxisArgs &a, int MP, size_t lds, hipStream_t s);
 hipError_t launch_axis_inv(const AxisArgs &a, int MP, hipStream_t s);
@@ -151,6 +158,10 @@ int contract_pick_split(int B, int Ci, int Co, int K, int bb);
 size_t contract_lds_bytes(int bb, int S);
 hipError_t contract_prepare(int bb, int dtype, size_t lds);
 hipError_t launch_contract(const ContractArgs &a, int bb, int S, int dtype, hipStream_t s);
+bool contract_mx_supported(int dtype, int Co, int K);
+size_t contract_mx_lds_bytes(int dtype, int B);
+hipError_t contract_mx_prepare(int dtype, int B);
+hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s);
 
 hipError_t launch_channel_mix(const void *x, const void *A, const void *bias, const void *add, void *y, int B,
                               int I, int O, long P, int act, int dtype, hipStream_t s);

@@ -1,0 +1,264 @@
+// contract_mx.hip - the per-mode complex channel contraction for fp16 / bf16
+// storage on bf16 matrix cores.
+//
+// For every retained mode k: Yh[k] (B x Co) = Xh[k] (B x Ci) * W[k] (Ci x Co),
+// complex, no conjugation, fp32 accumulation (TurboFNO write-up, sections
+// 2.2 and 3.2: the per-mode weight einsum, run on matrix cores). In real form
+// each mode is one product with K = (i, re/im) and N = (o, re/im):
+//   A[b][(i,0)] = Re X, A[b][(i,1)] = Im X,
+//   B[(i,0)][(o,0)] = Re W, B[(i,1)][(o,0)] = -Im W,
+//   B[(i,0)][(o,1)] = Im W, B[(i,1)][(o,1)] = Re W.
+//
+// Operands are split into bf16 parts so that the products are exact to fp32
+// level: the fp32 spectra as hi + lo (16 significant bits), fp16 weights as
+// hi + lo (exact: 11 bits), bf16 weights as they are. Products: Xh Wh + Xl Wh
+// (+ Xh Wl for fp16 weights) on v_mfma_f32_16x16x32_bf16.
+//
+// A workgroup owns 8 consecutive modes x 16 or 32 batch rows x 32 output
+// channels and streams the input channels in stages of 16: the spectra rows
+// [b][i][8 modes] (64 contiguous bytes) and weight rows [mode][i][32 o]
+// (128 bytes) are loaded with 16-byte accesses one stage ahead into
+// registers, split and transposed into LDS as MFMA fragments, and multiplied
+// there. The results leave through LDS as rows of 8 modes of Yh[b][o][k].
+
+#include "common.hpp"
+
+namespace fno {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+
+constexpr int kCT = 256;  // threads per workgroup (4 waves, 2 modes each)
+constexpr int kMB = 8;    // modes per workgroup
+constexpr int kIC = 16;   // input channels per stage (one 32-deep block of K)
+constexpr int kOT = 32;   // output channels per workgroup (four 16-column tiles of N)
+constexpr int kSP = 40;   // halves per staged fragment row (32 + 8 pad: conflict-free reads)
+
+__device__ __forceinline__ v4f mma_bf(u32x4 a, u32x4 b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
+}
+
+// (re, im) fp32 -> packed bf16 pairs hi = (bf16(re), bf16(im)), lo = the
+// rounding remainders, each rounded to nearest even
+__device__ __forceinline__ void split_pair(float re, float im, uint32_t &hi, uint32_t &lo) {
+  hi = f32x2_to_bf16x2(re, im);
+  lo = f32x2_to_bf16x2(re - __uint_as_float(hi << 16), im - __uint_as_float(hi & 0xffff0000u));
+}
+
+template <int DT, int MT>
+struct CmxShape {
+  static constexpr int BT = 16 * MT;                        // batch rows per workgroup
+  static constexpr int HL = DT == DT_F16 ? 2 : 1;          // weight parts
+  static constexpr int XU = kMB * BT * kIC * 8 / (16 * kCT);   // 16-byte spectra units per thread and stage
+  static constexpr int WU = kMB * kIC * kOT * 4 / (16 * kCT);  // 16-byte weight units per thread and stage
+  static constexpr int XS = kMB * 2 * BT * kSP;             // halves of the spectra stage
+  static constexpr int WS = kMB * HL * kOT * kSP;           // halves of the weight stage
+};
+
+template <int DT, int MT>
+__device__ __forceinline__ void cmx_fetch(const ContractArgs &a, int st, int k0, int b0, int o0, int tid,
+                                          u32x4 (&px)[CmxShape<DT, MT>::XU], u32x4 (&pw)[CmxShape<DT, MT>::WU]) {
+  using S = CmxShape<DT, MT>;
+  const int K = a.K, Ci = a.Ci, Co = a.Co, B = a.B;
+#pragma unroll
+  for (int v = 0; v < S::XU; ++v) {
+    const int u = v * kCT + tid;
+    const int row = u >> 2, c = u & 3;  // row = (b, i), i fastest; c: modes 2c, 2c + 1
+    const int b = b0 + row / kIC, i = st * kIC + row % kIC, mode = k0 + 2 * c;
+    const bool ok = b < B && i < Ci && mode < K;
+    const u32x4 t = *reinterpret_cast<const u32x4 *>(a.xh + (ok ? ((size_t)b * Ci + i) * K + mode : 0));
+    px[v] = ok ? t : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int v = 0; v < S::WU; ++v) {
+    const int u = v * kCT + tid;
+    const int row = u >> 3, c = u & 7;  // row = (mode, i), i fastest; c: outputs 4c .. 4c + 3
+    const int mode = k0 + row / kIC, i = st * kIC + row % kIC, o = o0 + 4 * c;
+    const bool ok = mode < K && i < Ci && o < Co;
+    const u32x4 t = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.w) +
+                                                     (ok ? (((size_t)mode * Ci + i) * Co + o) * 2 : 0));
+    pw[v] = ok ? t : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// split and transpose one stage into fragment rows:
+//   xs[mode][part][b][2 i + re/im], ws[mode][part][o][2 i + re/im]
+template <int DT, int MT>
+__device__ __forceinline__ void cmx_put(uint16_t *xs, uint16_t *ws, int tid, const u32x4 (&px)[CmxShape<DT, MT>::XU],
+                                        const u32x4 (&pw)[CmxShape<DT, MT>::WU]) {
+  using S = CmxShape<DT, MT>;
+#pragma unroll
+  for (int v = 0; v < S::XU; ++v) {
+    const int u = v * kCT + tid;
+    const int row = u >> 2, c = u & 3;
+    const int b = row / kIC, i = row % kIC;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      uint32_t hi, lo;
+      split_pair(__uint_as_float(px[v][2 * t]), __uint_as_float(px[v][2 * t + 1]), hi, lo);
+      const int m = 2 * c + t;
+      reinterpret_cast<uint32_t *>(xs + ((m * 2 + 0) * S::BT + b) * kSP)[i] = hi;
+      reinterpret_cast<uint32_t *>(xs + ((m * 2 + 1) * S::BT + b) * kSP)[i] = lo;
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < S::WU; ++v) {
+    const int u = v * kCT + tid;
+    const int row = u >> 3, c = u & 7;
+    const int m = row / kIC, i = row % kIC;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int o = 4 * c + t;
+      if constexpr (DT == DT_F16) {
+        // each half converted on its own: reading both lanes of a bit-cast
+        // half2 vector here produced wrong values on gfx950
+        const float re = (float)__builtin_bit_cast(_Float16, (uint16_t)(pw[v][t] & 0xffffu));
+        const float im = (float)__builtin_bit_cast(_Float16, (uint16_t)(pw[v][t] >> 16));
+        uint32_t hi, lo;
+        split_pair(re, im, hi, lo);
+        reinterpret_cast<uint32_t *>(ws + ((m * 2 + 0) * kOT + o) * kSP)[i] = hi;
+        reinterpret_cast<uint32_t *>(ws + ((m * 2 + 1) * kOT + o) * kSP)[i] = lo;
+      } else {
+        reinterpret_cast<uint32_t *>(ws + (m * kOT + o) * kSP)[i] = pw[v][t];
+      }
+    }
+  }
+}
+
+// B fragment of output column n = 16 nt + l % 16 = (o, part) from raw
+// (Re W, Im W) pairs of four consecutive input channels: part 0 takes
+// (Re, -Im), part 1 takes (Im, Re)
+__device__ __forceinline__ u32x4 w_form(u32x4 raw, bool part1) {
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = part1 ? __builtin_amdgcn_alignbit(raw[j], raw[j], 16) : raw[j] ^ 0x80000000u;
+  return o;
+}
+
+template <int DT, int MT>
+__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(2))) void fno_contract_mx(ContractArgs a) {
+  using S = CmxShape<DT, MT>;
+  extern __shared__ uint16_t sm[];
+  uint16_t *xs = sm;
+  uint16_t *ws = xs + S::XS;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int K = a.K, Co = a.Co, B = a.B;
+  const int k0 = blockIdx.x * kMB, b0 = blockIdx.y * S::BT, o0 = blockIdx.z * kOT;
+  const int nst = (a.Ci + kIC - 1) / kIC;
+  const bool part1 = lane & 1;
+
+  v4f acc[2][MT][4];
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[mm][mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 px[S::XU], pw[S::WU];
+  cmx_fetch<DT, MT>(a, 0, k0, b0, o0, tid, px, pw);
+  for (int st = 0; st < nst; ++st) {
+    cmx_put<DT, MT>(xs, ws, tid, px, pw);
+    if (st + 1 < nst) cmx_fetch<DT, MT>(a, st + 1, k0, b0, o0, tid, px, pw);
+    __syncthreads();
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const int m = 2 * wv + mm;
+      u32x4 af[MT][2];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          af[mt][p] = *reinterpret_cast<const u32x4 *>(xs + ((m * 2 + p) * S::BT + mt * 16 + (lane & 15)) * kSP +
+                                                       8 * (lane >> 4));
+#pragma unroll
+      for (int nh = 0; nh < 2; ++nh) {  // two halves of the output tiles
+        u32x4 bf[2][S::HL];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int p = 0; p < S::HL; ++p)
+            bf[t][p] = *reinterpret_cast<const u32x4 *>(
+                ws + ((m * S::HL + p) * kOT + (2 * nh + t) * 8 + ((lane & 15) >> 1)) * kSP + 8 * (lane >> 4));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int p = 0; p < S::HL; ++p) bf[t][p] = w_form(bf[t][p], part1);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            v4f &c = acc[mm][mt][2 * nh + t];
+            c = mma_bf(af[mt][0], bf[t][0], c);
+            c = mma_bf(af[mt][1], bf[t][0], c);
+            if constexpr (S::HL == 2) c = mma_bf(af[mt][0], bf[t][1], c);
+          }
+      }
+    }
+    __syncthreads();
+  }
+
+  // results -> LDS ys[b][o][8 modes] (re, im) -> rows of 8 modes of Yh
+  float *ys = reinterpret_cast<float *>(sm);
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int n = nt * 16 + (lane & 15), o = n >> 1, part = n & 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int b = mt * 16 + 4 * (lane >> 4) + j;
+          ys[((b * kOT + o) * kMB + 2 * wv + mm) * 2 + part] = acc[mm][mt][nt][j];
+        }
+      }
+  __syncthreads();
+  constexpr int YU = S::BT * kOT * kMB * 8 / 16 / kCT;  // 16-byte result units per thread
+#pragma unroll
+  for (int v = 0; v < YU; ++v) {
+    const int u = v * kCT + tid;
+    const int row = u >> 2, c = u & 3;  // row = (b, o); c: modes 2c, 2c + 1
+    const int b = b0 + row / kOT, o = o0 + row % kOT, mode = k0 + 2 * c;
+    if (b < B && o < Co && mode < K)
+      *reinterpret_cast<u32x4 *>(a.yh + ((size_t)b * Co + o) * K + mode) = reinterpret_cast<const u32x4 *>(ys)[u];
+  }
+}
+
+// -------------------------------------------------------------- launchers
+
+bool contract_mx_supported(int dtype, int Co, int K) {
+  return (dtype == DT_F16 || dtype == DT_BF16) && (Co & 3) == 0 && (K & 1) == 0;
+}
+
+static const void *contract_mx_kernel(int dtype, int B) {
+  const bool one = B <= 16;
+  if (dtype == DT_F16) return one ? (const void *)fno_contract_mx<DT_F16, 1> : (const void *)fno_contract_mx<DT_F16, 2>;
+  if (dtype == DT_BF16) return one ? (const void *)fno_contract_mx<DT_BF16, 1> : (const void *)fno_contract_mx<DT_BF16, 2>;
+  return nullptr;
+}
+
+size_t contract_mx_lds_bytes(int dtype, int B) {
+  const int BT = B <= 16 ? 16 : 32, HL = dtype == DT_F16 ? 2 : 1;
+  const size_t stage = ((size_t)kMB * 2 * BT * kSP + (size_t)kMB * HL * kOT * kSP) * 2;
+  const size_t out = (size_t)BT * kOT * kMB * 8;
+  return stage > out ? stage : out;
+}
+
+hipError_t contract_mx_prepare(int dtype, int B) {
+  const void *k = contract_mx_kernel(dtype, B);
+  if (!k) return hipErrorInvalidValue;
+  return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)contract_mx_lds_bytes(dtype, B));
+}
+
+hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s) {
+  const void *k = contract_mx_kernel(dtype, a.B);
+  if (!k) return hipErrorInvalidValue;
+  const int BT = a.B <= 16 ? 16 : 32;
+  dim3 grid((a.K + kMB - 1) / kMB, (a.B + BT - 1) / BT, (a.Co + kOT - 1) / kOT);
+  void *args[] = {(void *)&a};
+  return hipLaunchKernel(k, grid, dim3(kCT), args, contract_mx_lds_bytes(dtype, a.B), s);
+}
+
+}  // namespace fno

@@ -63,14 +63,6 @@ std::vector<float2> twiddles(int n) {
 
 uint16_t half_bits(double v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
 
-uint16_t bf16_bits(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-float bf16_value(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
-
 // cos and sin of 2 pi k / n (k reduced mod n in integers, quarter turns exact)
 void cos_sin_2pi(long k, long n, double &c, double &s) {
   const long r = ((k % n) + n) % n;
@@ -85,13 +77,13 @@ void cos_sin_2pi(long k, long n, double &c, double &s) {
   }
 }
 
-// Forward row-DFT fragments (B operand, K = w, N = c = 2 ky + re/im):
-// [nt][kb][lane][8], value T[w][c] = cos / -sin (2 pi ky w / W), zero for
-// ky >= m2. Split into a high and (bf16 only) a low part.
-void fwd_fragments(int W, int m2, int NT, bool bf, std::vector<uint16_t> &hi, std::vector<uint16_t> &lo) {
+// Forward row-DFT fragments, [nt][kb][lane][8] fp16: lane l of tile nt,
+// block kb holds T[w][c] for c = 16 nt + l % 16 and w = 32 kb + 8 (l / 16) + i,
+// T[w][2 ky] = cos(2 pi ky w / W), T[w][2 ky + 1] = -sin(..), zero for
+// ky >= m2 (the A operand of the transposed row product R^T = T^T x^T).
+void fwd_fragments(int W, int m2, int NT, std::vector<uint16_t> &hi) {
   const int KB = W / 32;
   hi.assign((size_t)NT * KB * 64 * 8, 0);
-  lo.assign(hi.size(), 0);
   for (int nt = 0; nt < NT; ++nt)
     for (int kb = 0; kb < KB; ++kb)
       for (int l = 0; l < 64; ++l)
@@ -103,14 +95,7 @@ void fwd_fragments(int W, int m2, int NT, bool bf, std::vector<uint16_t> &hi, st
             cos_sin_2pi((long)ky * w, W, cs, sn);
             v = (c & 1) ? -sn : cs;
           }
-          const size_t at = (((size_t)nt * KB + kb) * 64 + l) * 8 + i;
-          if (bf) {
-            const uint16_t h = bf16_bits((float)v);
-            hi[at] = h;
-            lo[at] = bf16_bits((float)(v - (double)bf16_value(h)));
-          } else {
-            hi[at] = half_bits(v);
-          }
+          hi[(((size_t)nt * KB + kb) * 64 + l) * 8 + i] = half_bits(v);
         }
 }
 
@@ -201,10 +186,11 @@ struct fno_plan_s {
   int xN = 0, xm = 0, xMP = 0;
   size_t lds_axis = 0;
   int bb = 1, split = 1;
+  bool cmx = false;  // fp16 / bf16 contraction on bf16 matrix cores
   // row stage on MFMA (fp16 / bf16 storage, planes with H >= 64, W >= 64)
   bool mx = false;
-  int mx_nt = 0, mx_mt = 0, mx_nn = 0, mx_kb1 = 0, mx_lgW = 0, mx_lg4m1 = 0;
-  uint4 *tf = nullptr, *tf_lo = nullptr, *tb = nullptr, *ef_f = nullptr, *ef_i = nullptr;
+  int mx_nt = 0, mx_mt = 0, mx_nn = 0, mx_kb1 = 0, mx_lgW = 0, mx_lg4m1 = 0, mx_grid_f = 0, mx_grid_i = 0;
+  uint4 *tf = nullptr, *tb = nullptr, *ef_f = nullptr, *ef_i = nullptr;
   float2 *tw_h = nullptr, *tw_w = nullptr, *tw_x = nullptr;
   float2 *xh = nullptr, *yh = nullptr, *tbuf = nullptr;
   void *mem = nullptr;
@@ -294,6 +280,7 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
     return FNO_ERR_UNSUPPORTED;
   p.bb = contract_pick_bb(batch, c_out, p.K);
   p.split = contract_pick_split(batch, c_in, c_out, p.K, p.bb);
+  p.cmx = contract_mx_supported((int)dtype, c_out, p.K);
   if (ndim == 2) {
     p.launches = {L_FWD_PLANE, L_CONTRACT, L_INV_PLANE};
   } else {
@@ -388,15 +375,14 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   const size_t o_xh = off; off += al(n_xh * sizeof(float2));
   const size_t o_yh = off; off += al(n_yh * sizeof(float2));
   const size_t o_t = off; off += al(n_t * sizeof(float2));
-  std::vector<uint16_t> tfh, tfl, tbv, efv, eiv;
+  std::vector<uint16_t> tfh, tbv, efv, eiv;
   if (p->mx) {
-    fwd_fragments(p->pW, p->pm2, p->mx_nt, p->dtype == FNO_BF16, tfh, tfl);
+    fwd_fragments(p->pW, p->pm2, p->mx_nt, tfh);
     inv_fragments(p->pW, p->pm2, p->mx_nn, tbv);
     fwd_col_fragments(p->pH, p->pm1, p->mx_mt, efv);
     inv_col_fragments(p->pH, p->pm1, p->mx_kb1, eiv);
   }
   const size_t o_tf = off; off += al(tfh.size() * 2);
-  const size_t o_tfl = off; off += al(p->dtype == FNO_BF16 ? tfl.size() * 2 : 0);
   const size_t o_tb = off; off += al(tbv.size() * 2);
   const size_t o_ef = off; off += al(efv.size() * 2);
   const size_t o_ei = off; off += al(eiv.size() * 2);
@@ -417,7 +403,6 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   p->tbuf = n_t ? (float2 *)(base + o_t) : nullptr;
   if (p->mx) {
     p->tf = (uint4 *)(base + o_tf);
-    p->tf_lo = p->dtype == FNO_BF16 ? (uint4 *)(base + o_tfl) : nullptr;
     p->tb = (uint4 *)(base + o_tb);
     p->ef_f = (uint4 *)(base + o_ef);
     p->ef_i = (uint4 *)(base + o_ei);
@@ -432,18 +417,24 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   }
   if (e == hipSuccess && p->mx) {
     e = hipMemcpy(p->tf, tfh.data(), tfh.size() * 2, hipMemcpyHostToDevice);
-    if (e == hipSuccess && p->tf_lo) e = hipMemcpy(p->tf_lo, tfl.data(), tfl.size() * 2, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(p->tb, tbv.data(), tbv.size() * 2, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(p->ef_f, efv.data(), efv.size() * 2, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(p->ef_i, eiv.data(), eiv.size() * 2, hipMemcpyHostToDevice);
-    if (e == hipSuccess) e = mx_prepare(true, p->pW, p->dtype, p->lds_fwd);
-    if (e == hipSuccess) e = mx_prepare(false, p->pW, p->dtype, p->lds_inv);
+    if (e == hipSuccess) e = mx_prepare(true, p->pW, p->pm2, p->dtype, p->lds_fwd);
+    if (e == hipSuccess) e = mx_prepare(false, p->pW, p->pm2, p->dtype, p->lds_inv);
+    if (e == hipSuccess)
+      e = mx_grid(true, p->pW, p->pm2, p->dtype, p->lds_fwd, p->device, p->B * p->Ci * (ndim == 3 ? p->xN : 1),
+                  &p->mx_grid_f);
+    if (e == hipSuccess)
+      e = mx_grid(false, p->pW, p->pm2, p->dtype, p->lds_inv, p->device, p->B * p->Co * (ndim == 3 ? p->xN : 1),
+                  &p->mx_grid_i);
   } else {
     if (e == hipSuccess) e = plane_prepare(true, p->pMP, p->rpt, p->dtype, p->lds_fwd);
     if (e == hipSuccess) e = plane_prepare(false, p->pMP, p->rpt, p->dtype, p->lds_inv);
   }
   if (e == hipSuccess && ndim == 3) e = axis_fwd_prepare(p->xMP, p->lds_axis);
-  if (e == hipSuccess) e = contract_prepare(p->bb, p->dtype, contract_lds_bytes(p->bb, p->split));
+  if (e == hipSuccess)
+    e = p->cmx ? contract_mx_prepare(p->dtype, p->B) : contract_prepare(p->bb, p->dtype, contract_lds_bytes(p->bb, p->split));
   if (e != hipSuccess) {
     (void)hipFree(p->mem);
     delete p;
@@ -485,7 +476,6 @@ static hipError_t run_one(fno_plan_t p, int kind, const void *x, const void *w, 
         m.out = nd == 2 ? p->xh : p->tbuf;
         m.tw_h = p->tw_h;
         m.tf = p->tf;
-        m.tf_lo = p->tf_lo;
         m.ef = p->ef_f;
         m.nplanes = p->B * p->Ci * (nd == 3 ? p->xN : 1);
         m.H = p->pH;
@@ -497,7 +487,7 @@ static hipError_t run_one(fno_plan_t p, int kind, const void *x, const void *w, 
         m.nn = p->mx_nn;
         m.lgW = p->mx_lgW;
         m.scale = nd == 2 ? 1.0f / ((float)p->pH * (float)p->pW) : 1.0f;
-        return launch_plane_mx_fwd(m, p->dtype, p->lds_fwd, s);
+        return launch_plane_mx_fwd(m, p->mx_grid_f, p->dtype, p->lds_fwd, s);
       }
       PlaneFwdArgs a;
       a.x = x;
@@ -538,7 +528,7 @@ static hipError_t run_one(fno_plan_t p, int kind, const void *x, const void *w, 
       a.Ci = p->Ci;
       a.Co = p->Co;
       a.K = p->K;
-      return launch_contract(a, p->bb, p->split, p->dtype, s);
+      return p->cmx ? launch_contract_mx(a, p->dtype, s) : launch_contract(a, p->bb, p->split, p->dtype, s);
     }
     case L_INV_AXIS: {
       AxisArgs a;
@@ -569,7 +559,7 @@ static hipError_t run_one(fno_plan_t p, int kind, const void *x, const void *w, 
         m.nn = p->mx_nn;
         m.kb1 = p->mx_kb1;
         m.lg4m1 = p->mx_lg4m1;
-        return launch_plane_mx_inv(m, p->dtype, p->lds_inv, s);
+        return launch_plane_mx_inv(m, p->mx_grid_i, p->dtype, p->lds_inv, s);
       }
       PlaneInvArgs a;
       a.in = nd == 2 ? p->yh : p->tbuf;

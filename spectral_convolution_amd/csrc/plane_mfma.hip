@@ -14,22 +14,26 @@
 // with T[w][2ky] = cos(2 pi ky w / W), T[w][2ky+1] = -sin(..), and T'
 // carrying the c2r weights (1 for ky = 0, whose imaginary part drops out, 2
 // otherwise). kx(q) = q for q < m1 and H - 2 m1 + q above (the two corners).
-// All four run on v_mfma_f32_16x16x32_{f16,bf16} with fp32 accumulation.
+// All four run on v_mfma_f32_16x16x32_f16 with fp32 accumulation.
 //
 // Rows are streamed in rounds of 64. The column product of one round uses
 // the same 64-row twiddle block for every round: the round offset h0 only
 // multiplies mode q by e^{-+2 pi i kx(q) h0 / H}, which is applied to the
 // per-round partial sums (forward) or to the spectra (inverse) on the VALU.
 // So a workgroup holds one 64-row stage of x or y, one round of R or Z, and
-// its twiddle fragments in registers: about 45-55 KB of LDS, two workgroups
-// of 8 waves per CU.
+// its twiddle fragments in registers: about 45-55 KB of LDS and ~240 VGPRs,
+// two workgroups of 4 waves per CU. Both kernels are persistent (one
+// workgroup per resident slot, planes strided by the grid), so the rows of
+// the next plane are in flight while the current one is multiplied.
 //
-// Precision. x (fp16) is exact as an MFMA operand; bf16 x is multiplied by a
-// two-term bf16 split of T. R, Z and the spectra are rounded to fp16 after a
-// power-of-two scale derived from a bound (the round's max |x| times W, or
-// the plane's max |Y| times 4 m1), which keeps every fp16 operand below 2^15
-// and far above the subnormal range for data of any sensible magnitude; the
-// scale is undone in fp32. Twiddles are rounded to fp16.
+// Precision. fp16 x is exact as an MFMA operand; bf16 x is scaled per row by
+// a power of two into fp16 range, which is exact for every element within
+// 2^28 of the row's largest (bf16 has fewer mantissa bits than fp16). R, Z
+// and the spectra are rounded to fp16 after a power-of-two scale derived from
+// a bound (the round's largest |x| times W, or the plane's largest |Y| times
+// 4 m1), which keeps every fp16 operand below 2^15 and far above the
+// subnormal range; every scale is undone in fp32. Twiddles are rounded to
+// fp16.
 //
 // One fragment of v_mfma_f32_16x16x32 (A: 16 x 32, B: 32 x 16): lane l holds
 // row / column l % 16 and the eight consecutive k = 8 (l / 16) .. +7;
@@ -41,19 +45,13 @@ namespace fno {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 
-constexpr int kGT = 512;   // threads per workgroup (8 waves)
 constexpr int kRows = 64;  // rows per round
 constexpr int kRBP = 136;  // halves per row of a B-operand round buffer (128 + pad)
 constexpr int kZBP = 72;   // halves per row of the inverse Z buffer (64 + pad)
 
 __device__ __forceinline__ v4f mma(u32x4 a, u32x4 b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ v4f mma_bf(u32x4 a, u32x4 b, v4f c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ uint16_t h16(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
@@ -95,296 +93,391 @@ __device__ __forceinline__ float pow2f(int e) {
 
 // ------------------------------------------------------------------ forward
 
+constexpr int kFT = 256;  // threads per workgroup of both plane kernels (4 waves)
+
+// rows of global round g of this workgroup: plane blockIdx.x + (g >> lgr)
+// * gridDim.x, rows 64 (g mod 2^lgr) .. +63; KB 16-byte units per thread
 template <int KB>
-__device__ __forceinline__ void fwd_fetch(const u32x4 *xp, int r, int tid, u32x4 (&p)[KB / 2]) {
-  constexpr int WU = 4 * KB;  // 16-byte units per row
-  const u32x4 *src = xp + (size_t)r * kRows * WU + tid;
+__device__ __forceinline__ void fwd_fetch(const uint16_t *x, int g, int lgr, int H, int tid, u32x4 (&p)[KB]) {
+  constexpr int W = 32 * KB, WU = 4 * KB;
+  const size_t plane = (size_t)blockIdx.x + (size_t)(g >> lgr) * gridDim.x;
+  const int r = g & ((1 << lgr) - 1);
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(x + plane * H * W) + (size_t)r * kRows * WU + tid;
 #pragma unroll
-  for (int v = 0; v < KB / 2; ++v) p[v] = src[v * kGT];
+  for (int v = 0; v < KB; ++v) p[v] = src[v * kFT];
+}
+
+// eight bf16 -> eight fp16 times 2^sig (exact while the result is normal)
+__device__ __forceinline__ u32x4 bf16_to_f16_scaled(u32x4 d, float sc) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(d[i] << 16) * sc, hi = __uint_as_float(d[i] & 0xffff0000u) * sc;
+    o[i] = h16x2(lo, hi);
+  }
+  return o;
 }
 
 struct FwdShape {
-  int H, m1, m2, NT, MT, NN, lgW;
+  int H, m1, m2, NT, MT, NN, lgW, lgr, total;  // lgr: log2 rounds per plane; total: rounds of this workgroup
 };
 
-// One round of 64 rows: stage them, row product into R (fp16, scaled), then
-// the column product of R against the 64-row twiddle block, phase-shifted
-// and accumulated into X.
-template <int DT, int KB>
-__device__ __forceinline__ void fwd_round(int r, int rounds, const FwdShape &s, u32x4 (&p)[KB / 2],
-                                          const u32x4 *xp, u32x4 *stage, uint16_t *rb, const float2 *twh,
-                                          uint32_t *mxs, const u32x4 (&th)[KB],
-                                          const u32x4 (&tl)[DT == DT_BF16 ? KB : 1], const u32x4 (&ef)[4],
-                                          float2 (&X)[2][2]) {
+// One round of 64 rows:
+//  1. stage the rows in LDS as fp16 (bf16 rows scaled by a power of two per
+//     row into fp16 range), note the largest exponent of the round;
+//  2. row product, transposed: R^T[c][h] = sum_w T[w][c] x[h][w] with the
+//     twiddles as the register-held A operand (two 16-column tiles of R per
+//     wave) and x as B, so each staged fragment feeds two products; R is
+//     scaled by a power of two (undone in 4) and stored as fp16 pairs;
+//  3. column product of R against the 64-row twiddle block (two m-tiles of
+//     modes per wave), phase-shifted by the round offset into X.
+template <int DT, int KB, bool TWO>
+__device__ __forceinline__ void fwd_round(int g, const FwdShape &s, u32x4 (&p)[KB], const PlaneMxFwdArgs &a,
+                                          u32x4 *stage, uint16_t *rb, const float2 *twh, int *rsig, int *mxs,
+                                          const u32x4 (&th)[TWO ? 2 : 1][KB], const u32x4 (&ef)[2][4],
+                                          float2 (&X)[2][2][2]) {
   constexpr bool BF = DT == DT_BF16;
   constexpr int WU = 4 * KB, PITCH = WU + 1;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r = g & ((1 << s.lgr) - 1);
 
-  uint32_t mb = 0;
+  int emax = -1000;
 #pragma unroll
-  for (int v = 0; v < KB / 2; ++v) {
-    const int e = v * kGT + tid;
+  for (int v = 0; v < KB; ++v) {
+    const int e = v * kFT + tid;
     const int row = e / WU, cu = e - row * WU;
-    stage[row * PITCH + cu] = p[v];
-    mb = max(mb, absmax_bits(p[v]));
+    u32x4 d = p[v];
+    uint32_t m = absmax_bits(d);
+    if constexpr (BF) {
+#pragma unroll
+      for (int o = 1; o < WU; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+      const int eh = (int)max(m >> 7, 1u) - 126;  // row max < 2^eh
+      const int sig = max(-120, min(120, 14 - eh));
+      d = bf16_to_f16_scaled(d, pow2f(sig));
+      if ((tid & (WU - 1)) == 0) rsig[row] = m ? sig : 0;
+      emax = max(emax, m ? eh : -1000);
+    } else {
+      emax = max(emax, m ? (int)max(m >> 10, 1u) - 14 : -1000);
+    }
+    stage[row * PITCH + cu] = d;
   }
-  mb = wave_max_u32(mb);
-  if (lane == 0) mxs[(r & 1) * 8 + wv] = mb;
-  if (r + 2 < rounds) fwd_fetch<KB>(xp, r + 2, tid, p);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) emax = max(emax, __shfl_xor(emax, o, 64));
+  if (lane == 0) mxs[(g & 1) * 4 + wv] = emax;
+  if (g + 1 < s.total) fwd_fetch<KB>(reinterpret_cast<const uint16_t *>(a.x), g + 1, s.lgr, s.H, tid, p);
   __syncthreads();
 
-  // scale: |R| <= W max|x| < 2^(e + lgW); R * 2^(15 - e - lgW) < 2^15
-  uint32_t mall = 0;
+  // |R| <= W max|x| < 2^(emax + lgW): R * 2^(15 - emax - lgW) < 2^15
+  int er = -1000;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) mall = max(mall, mxs[(r & 1) * 8 + i]);
-  int e;
-  if constexpr (BF) e = (int)max(mall >> 7, 1u) - 126;
-  else e = (int)max(mall >> 10, 1u) - 14;
-  const int se = mall ? 15 - e - s.lgW : 0;
-  const float sc = pow2f(se), isc = pow2f(-se);
+  for (int i = 0; i < 4; ++i) er = max(er, mxs[(g & 1) * 4 + i]);
+  const int se = er > -1000 ? max(-120, min(120, 15 - er - s.lgW)) : 0;
+  const float isc = pow2f(-se);
 
-  // row product: column tile nt of R for the stripes of this wave
-  const int nt = wv % s.NT;
-  for (int st = wv / s.NT; st < 4; st += 8 / s.NT) {
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    const u32x4 *ar = stage + (st * 16 + (lane & 15)) * PITCH + (lane >> 4);
+  // row product: c-tiles ct0 (, ct0 + 1) x stripes of this wave; all
+  // fragments of a stripe are read before its products are issued
+  {
+    const int G = s.NT == 4 ? 2 : 1;
+    const int ct0 = (wv % G) * 2;
+    for (int st = wv / G; st < 4; st += 4 / G) {
+      const u32x4 *br = stage + (st * 16 + (lane & 15)) * PITCH + (lane >> 4);
+      u32x4 bv[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const u32x4 av = ar[kb * 4];
-      if constexpr (BF) {
-        acc = mma_bf(av, th[kb], acc);
-        acc = mma_bf(av, tl[kb], acc);
-      } else {
-        acc = mma(av, th[kb], acc);
+      for (int kb = 0; kb < KB; ++kb) bv[kb] = br[kb * 4];
+      __builtin_amdgcn_sched_barrier(0);  // keep all reads ahead of the products
+      v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        acc0 = mma(th[0][kb], bv[kb], acc0);
+        if constexpr (TWO) acc1 = mma(th[1][kb], bv[kb], acc1);
+      }
+      const int h = st * 16 + (lane & 15);
+      const float f = BF ? pow2f(se - rsig[h]) : pow2f(se);
+      uint32_t *col = reinterpret_cast<uint32_t *>(rb) + h;
+#pragma unroll
+      for (int t = 0; t < (TWO ? 2 : 1); ++t) {
+        const v4f &acc = t == 0 ? acc0 : acc1;
+        const int ky0 = 8 * (ct0 + t) + 2 * (lane >> 4);
+        if (ky0 < s.m2) col[ky0 * (kRBP / 2)] = h16x2(acc[0] * f, acc[1] * f);
+        if (ky0 + 1 < s.m2) col[(ky0 + 1) * (kRBP / 2)] = h16x2(acc[2] * f, acc[3] * f);
       }
     }
-    const int c = nt * 16 + (lane & 15);
-    if (c < 2 * s.m2) {
-      uint16_t *dst = rb + (c >> 1) * kRBP + 2 * (st * 16 + 4 * (lane >> 4)) + (c & 1);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dst[2 * j] = h16(acc[j] * sc);
-    }
   }
   __syncthreads();
 
-  // column product: m-tile wv (modes q0, q0 + 1 per lane), all ky tiles
-  if (wv < s.MT) {
-    const int q0 = 8 * wv + 2 * (lane >> 4);
-    float2 ph[2];
+  // column product: m-tiles 2 wv, 2 wv + 1 (modes q0, q0 + 1 per lane each)
+  if (2 * wv < s.MT) {
+    float2 ph[2][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int q = q0 + t;
-      const int kx = q < s.m1 ? q : s.H - 2 * s.m1 + q;
-      ph[t] = twh[(kx * kRows * r) & (s.H - 1)];
-    }
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int q = 8 * (2 * wv + mi) + 2 * (lane >> 4) + t;
+        const int kx = q < s.m1 ? q : s.H - 2 * s.m1 + q;
+        ph[mi][t] = twh[(kx * kRows * r) & (s.H - 1)];
+      }
 #pragma unroll
     for (int nn = 0; nn < 2; ++nn) {
       if (nn < s.NN) {
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
         const u32x4 *br = reinterpret_cast<const u32x4 *>(rb + (nn * 16 + (lane & 15)) * kRBP) + (lane >> 4);
+        u32x4 bv[4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc = mma(ef[kb], br[kb * 4], acc);
+        for (int kb = 0; kb < 4; ++kb) bv[kb] = br[kb * 4];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const float yr = acc[2 * t] * isc, yi = acc[2 * t + 1] * isc;
-          X[nn][t].x += yr * ph[t].x - yi * ph[t].y;
-          X[nn][t].y += yr * ph[t].y + yi * ph[t].x;
+        for (int mi = 0; mi < 2; ++mi) {
+          v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) acc = mma(ef[mi][kb], bv[kb], acc);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const float yr = acc[2 * t] * isc, yi = acc[2 * t + 1] * isc;
+            X[mi][nn][t].x += yr * ph[mi][t].x - yi * ph[mi][t].y;
+            X[mi][nn][t].y += yr * ph[mi][t].y + yi * ph[mi][t].x;
+          }
         }
       }
+    }
+    // last round of a plane: scale, store the modes, start the next plane
+    if (r == (1 << s.lgr) - 1) {
+      const size_t plane = (size_t)blockIdx.x + (size_t)(g >> s.lgr) * gridDim.x;
+      float2 *op = a.out + plane * (2 * s.m1 * s.m2);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int nn = 0; nn < 2; ++nn) {
+          const int ky = nn * 16 + (lane & 15);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int q = 8 * (2 * wv + mi) + 2 * (lane >> 4) + t;
+            if (nn < s.NN && ky < s.m2 && q < 2 * s.m1)
+              op[q * s.m2 + ky] = make_float2(X[mi][nn][t].x * a.scale, X[mi][nn][t].y * a.scale);
+            X[mi][nn][t] = make_float2(0.f, 0.f);
+          }
+        }
     }
   }
 }
 
-template <int DT, int KB>
-__global__ __launch_bounds__(kGT) void fno_fwd_plane_mx(PlaneMxFwdArgs a) {
-  constexpr bool BF = DT == DT_BF16;
-  constexpr int W = 32 * KB, WU = 4 * KB, PITCH = WU + 1;
+// Persistent: workgroup b transforms planes b, b + gridDim.x, ...; its rounds
+// form one stream, the next one in flight while the current one is
+// multiplied, across plane boundaries. TWO: R has more than one 16-column
+// tile, and each wave computes two of them.
+template <int DT, int KB, bool TWO>
+__global__ __launch_bounds__(kFT) void fno_fwd_plane_mx(PlaneMxFwdArgs a) {
+  constexpr int WU = 4 * KB, PITCH = WU + 1;
   extern __shared__ u32x4 lds[];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const FwdShape s{a.H, a.m1, a.m2, a.nt, a.mt, a.nn, a.lgW};
+  const int lgr = a.H == 256 ? 2 : a.H == 128 ? 1 : 0;
+  const int nmine = (a.nplanes - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const FwdShape s{a.H, a.m1, a.m2, a.nt, a.mt, a.nn, a.lgW, lgr, nmine << lgr};
   u32x4 *stage = lds;                                                    // [64][PITCH]
   uint16_t *rb = reinterpret_cast<uint16_t *>(stage + kRows * PITCH);    // [32][kRBP]
   float2 *twh = reinterpret_cast<float2 *>(rb + 32 * kRBP);              // [H]
-  uint32_t *mxs = reinterpret_cast<uint32_t *>(twh + s.H);               // [2][8]
-  for (int v = tid; v < s.H; v += kGT) twh[v] = a.tw_h[v];
+  int *rsig = reinterpret_cast<int *>(twh + s.H);                        // [64]
+  int *mxs = rsig + kRows;                                               // [2][4]
+  for (int v = tid; v < s.H; v += kFT) twh[v] = a.tw_h[v];
 
-  const int plane = blockIdx.x;
-  const u32x4 *xp = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.x) + (size_t)plane * s.H * W);
-
-  // row twiddles of this wave's column tile; column twiddles of its m-tile
-  const int nt = wv % s.NT;
-  u32x4 th[KB], tl[BF ? KB : 1];
+  // row twiddles (A operand) of this wave's c-tiles; column twiddles of its m-tiles
+  const int G = s.NT == 4 ? 2 : 1;
+  u32x4 th[TWO ? 2 : 1][KB];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    th[kb] = reinterpret_cast<const u32x4 *>(a.tf)[((size_t)nt * KB + kb) * 64 + lane];
-    if constexpr (BF) tl[kb] = reinterpret_cast<const u32x4 *>(a.tf_lo)[((size_t)nt * KB + kb) * 64 + lane];
+  for (int t = 0; t < (TWO ? 2 : 1); ++t) {
+    const int ct = min((wv % G) * 2 + t, s.NT - 1);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) th[t][kb] = reinterpret_cast<const u32x4 *>(a.tf)[((size_t)ct * KB + kb) * 64 + lane];
   }
-  const int mt = wv < s.MT ? wv : 0;
-  u32x4 ef[4];
+  u32x4 ef[2][4];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) ef[kb] = reinterpret_cast<const u32x4 *>(a.ef)[((size_t)mt * 4 + kb) * 64 + lane];
+  for (int mi = 0; mi < 2; ++mi) {
+    const int mt = min(2 * wv + mi, s.MT - 1);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) ef[mi][kb] = reinterpret_cast<const u32x4 *>(a.ef)[((size_t)mt * 4 + kb) * 64 + lane];
+  }
 
-  float2 X[2][2];
+  float2 X[2][2][2];
 #pragma unroll
-  for (int nn = 0; nn < 2; ++nn)
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) X[nn][t] = make_float2(0.f, 0.f);
+    for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) X[mi][nn][t] = make_float2(0.f, 0.f);
 
-  const int rounds = s.H / kRows;
-  u32x4 pa[KB / 2], pb[KB / 2];
-  fwd_fetch<KB>(xp, 0, tid, pa);
-  if (rounds > 1) fwd_fetch<KB>(xp, 1, tid, pb);
+  const uint16_t *x = reinterpret_cast<const uint16_t *>(a.x);
+  u32x4 pa[KB];
+  if (s.total > 0) fwd_fetch<KB>(x, 0, lgr, s.H, tid, pa);
   __syncthreads();
-  for (int r = 0; r < rounds; r += 2) {
-    fwd_round<DT, KB>(r, rounds, s, pa, xp, stage, rb, twh, mxs, th, tl, ef, X);
-    if (r + 1 < rounds) fwd_round<DT, KB>(r + 1, rounds, s, pb, xp, stage, rb, twh, mxs, th, tl, ef, X);
-  }
-
-  if (wv < s.MT) {
-    const int K = 2 * s.m1 * s.m2;
-    float2 *op = a.out + (size_t)plane * K;
-#pragma unroll
-    for (int nn = 0; nn < 2; ++nn) {
-      const int ky = nn * 16 + (lane & 15);
-      if (nn < s.NN && ky < s.m2) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int q = 8 * wv + 2 * (lane >> 4) + t;
-          if (q < 2 * s.m1) op[q * s.m2 + ky] = make_float2(X[nn][t].x * a.scale, X[nn][t].y * a.scale);
-        }
-      }
-    }
-  }
+  for (int g = 0; g < s.total; ++g) fwd_round<DT, KB, TWO>(g, s, pa, a, stage, rb, twh, rsig, mxs, th, ef, X);
 }
 
 // ------------------------------------------------------------------ inverse
 
+// spectra of one plane into registers: value tid + 256 i, zero past K
+template <int NY>
+__device__ __forceinline__ void inv_load(const float2 *in, size_t plane, int K, int tid, float2 (&yv)[NY]) {
+  const float2 *ip = in + plane * K;
+#pragma unroll
+  for (int i = 0; i < NY; ++i) {
+    const int v = tid + i * kFT;
+    const bool ok = v < K;
+    const float2 t = ip[ok ? v : 0];
+    yv[i] = ok ? t : make_float2(0.f, 0.f);
+  }
+}
+
+// Persistent: workgroup b transforms planes b, b + gridDim.x, ...; the
+// spectra of the next plane load while the current one is transformed. Per
+// round of 64 output rows:
+//  1. phase-rotate the spectra by the round offset, scale, fp16 into LDS;
+//  2. Z = E' Y (two m-tiles of rows per wave), fp16 into LDS;
+//  3. y^T[w][h] = sum_c T'[c][w] Z[h][c] with the twiddles as the
+//     register-held A operand, so each lane holds four consecutive outputs
+//     of a row; unscaled, rounded to the storage dtype into the out stage;
+//  4. coalesced 16-byte stores of the 64 rows.
 template <int DT, int KB>
-__global__ __launch_bounds__(kGT) void fno_inv_plane_mx(PlaneMxInvArgs a) {
+__global__ __launch_bounds__(kFT) void fno_inv_plane_mx(PlaneMxInvArgs a) {
   constexpr int W = 32 * KB, WU = 4 * KB, PITCH = WU + 1;
-  constexpr int NTW = W / 16;                  // output column tiles
-  constexpr int NBW = NTW >= 8 ? NTW / 8 : 1;  // column tiles per wave
-  constexpr int NY = 4;                        // spectra values per thread (K <= 2048)
+  constexpr int NTW = W / 16;   // output column tiles
+  constexpr int NPW = NTW / 4;  // column tiles per wave
+  constexpr int NY = 8;         // spectra values per thread (K <= 2048)
   extern __shared__ u32x4 lds[];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, m1 = a.m1, m2 = a.m2, NN = a.nn, KB1 = a.kb1;
   const int K = 2 * m1 * m2;
+  const int nmine = (a.nplanes - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   u32x4 *ostage = lds;                                                      // [64][PITCH]
   uint16_t *yb = reinterpret_cast<uint16_t *>(ostage + kRows * PITCH);      // [32][kRBP]
   uint16_t *zb = yb + 32 * kRBP;                                            // [64][kZBP]
   float2 *twh = reinterpret_cast<float2 *>(zb + kRows * kZBP);              // [H]
-  float *ymx = reinterpret_cast<float *>(twh + H);                          // [8]
+  float *ymx = reinterpret_cast<float *>(twh + H);                          // [2][4]
 
-  for (int v = tid; v < 32 * kRBP / 2; v += kGT) reinterpret_cast<uint32_t *>(yb)[v] = 0u;
-  for (int v = tid; v < H; v += kGT) twh[v] = a.tw_h[v];
+  float2 yv[NY], yn[NY];
+  if (nmine > 0) inv_load<NY>(a.in, blockIdx.x, K, tid, yv);
+  for (int v = tid; v < 32 * kRBP / 2; v += kFT) reinterpret_cast<uint32_t *>(yb)[v] = 0u;
+  for (int v = tid; v < H; v += kFT) twh[v] = a.tw_h[v];
 
-  const int plane = blockIdx.x;
-  const float2 *ip = a.in + (size_t)plane * K;
-  float2 yv[NY];
-  float mloc = 0.f;
+  // E' fragments of m-tiles 2 wv, 2 wv + 1 (rows j = 16 wv .. 16 wv + 15)
+  u32x4 ef[2][4];
 #pragma unroll
-  for (int i = 0; i < NY; ++i) {
-    const int v = tid + i * kGT;
-    const bool ok = v < K;
-    const float2 t = ip[ok ? v : 0];
-    yv[i] = ok ? t : make_float2(0.f, 0.f);
-    mloc = fmaxf(mloc, fmaxf(fabsf(yv[i].x), fabsf(yv[i].y)));
-  }
-  mloc = wave_max_f32(mloc);
-  if (lane == 0) ymx[wv] = mloc;
-
-  // E' fragments of m-tile wv (rows j = 8 wv .. 8 wv + 7, both parts)
-  u32x4 ef[4];
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const u32x4 t = reinterpret_cast<const u32x4 *>(a.ef)[((size_t)wv * KB1 + (kb < KB1 ? kb : 0)) * 64 + lane];
-    ef[kb] = kb < KB1 ? t : u32x4{0u, 0u, 0u, 0u};
-  }
-  // T' fragments of this wave's output column tiles
-  u32x4 tb[NBW][2];
+    for (int kb = 0; kb < 4; ++kb) {
+      const u32x4 t =
+          reinterpret_cast<const u32x4 *>(a.ef)[((size_t)(2 * wv + mi) * KB1 + (kb < KB1 ? kb : 0)) * 64 + lane];
+      ef[mi][kb] = kb < KB1 ? t : u32x4{0u, 0u, 0u, 0u};
+    }
+  // T' fragments (A operand) of output column tiles wv, wv + 4, ...
+  u32x4 tb[NPW][2];
 #pragma unroll
-  for (int b = 0; b < NBW; ++b) {
-    const int ntl = NTW >= 8 ? wv + 8 * b : wv % NTW;
+  for (int i = 0; i < NPW; ++i)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const u32x4 t = reinterpret_cast<const u32x4 *>(a.tb)[((size_t)ntl * NN + (kb < NN ? kb : 0)) * 64 + lane];
-      tb[b][kb] = kb < NN ? t : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 t = reinterpret_cast<const u32x4 *>(a.tb)[((size_t)(wv + 4 * i) * NN + (kb < NN ? kb : 0)) * 64 + lane];
+      tb[i][kb] = kb < NN ? t : u32x4{0u, 0u, 0u, 0u};
     }
-  }
-  __syncthreads();
 
-  // |Z| <= sum_q (|Re Y| + |Im Y|) <= 4 m1 max|Y| < 2^(e + lg4m1)
-  float ym = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ym = fmaxf(ym, ymx[i]);
-  int e = 0;
-  if (ym > 0.f) (void)frexpf(ym, &e);
-  const int se = ym > 0.f ? 15 - e - a.lg4m1 : 0;
-  const float sc = pow2f(se), isc = pow2f(-se);
-
-  uint4 *yp = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.y) + (size_t)plane * H * W);
   const int rounds = H / kRows;
-  for (int r = 0; r < rounds; ++r) {
-    // spectra of the round: Y[q][ky] e^{+2 pi i kx(q) h0 / H}, scaled, fp16
+  for (int pi = 0; pi < nmine; ++pi) {
+    const size_t plane = (size_t)blockIdx.x + (size_t)pi * gridDim.x;
+    float mloc = 0.f;
 #pragma unroll
-    for (int i = 0; i < NY; ++i) {
-      const int v = tid + i * kGT;
-      if (v < K) {
-        const int q = v / m2, ky = v - q * m2;
-        const int kx = q < m1 ? q : H - 2 * m1 + q;
-        const float2 w = twh[(kx * kRows * r) & (H - 1)];  // e^{-i theta}
-        const float zr = (yv[i].x * w.x + yv[i].y * w.y) * sc;
-        const float zi = (yv[i].y * w.x - yv[i].x * w.y) * sc;
-        reinterpret_cast<uint32_t *>(yb + ky * kRBP)[q] = h16x2(zr, zi);
-      }
-    }
+    for (int i = 0; i < NY; ++i) mloc = fmaxf(mloc, fmaxf(fabsf(yv[i].x), fabsf(yv[i].y)));
+    mloc = wave_max_f32(mloc);
+    if (lane == 0) ymx[(pi & 1) * 4 + wv] = mloc;
+    if (pi + 1 < nmine) inv_load<NY>(a.in, plane + gridDim.x, K, tid, yn);
     __syncthreads();
 
-    // Z = E' Y for rows j = 8 wv .. +7 (m-tile wv), all ky tiles; fp16 into zb
+    // |Z| <= sum_q (|Re Y| + |Im Y|) <= 4 m1 max|Y| < 2^(e + lg4m1)
+    float ym = 0.f;
 #pragma unroll
-    for (int nn = 0; nn < 2; ++nn) {
-      if (nn < NN) {
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
-        const u32x4 *br = reinterpret_cast<const u32x4 *>(yb + (nn * 16 + (lane & 15)) * kRBP) + (lane >> 4);
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          if (kb < KB1) acc = mma(ef[kb], br[kb * 4], acc);
-        const int j0 = 8 * wv + 2 * (lane >> 4), ky = nn * 16 + (lane & 15);
-        reinterpret_cast<uint32_t *>(zb + j0 * kZBP)[ky] = h16x2(acc[0], acc[1]);
-        reinterpret_cast<uint32_t *>(zb + (j0 + 1) * kZBP)[ky] = h16x2(acc[2], acc[3]);
-      }
-    }
-    __syncthreads();
+    for (int i = 0; i < 4; ++i) ym = fmaxf(ym, ymx[(pi & 1) * 4 + i]);
+    int e = 0;
+    if (ym > 0.f) (void)frexpf(ym, &e);
+    const int se = ym > 0.f ? max(-120, min(120, 15 - e - a.lg4m1)) : 0;
+    const float sc = pow2f(se), isc = pow2f(-se);
 
-    // y = Z T' for this wave's tiles, unscaled and rounded into the out stage
-    uint16_t *os = reinterpret_cast<uint16_t *>(ostage);
+    uint4 *yp = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.y) + plane * H * W);
+    for (int r = 0; r < rounds; ++r) {
+      // 1. spectra of the round: Y[q][ky] e^{+2 pi i kx(q) h0 / H}, scaled, fp16
 #pragma unroll
-    for (int b = 0; b < NBW; ++b) {
-      const int ntl = NTW >= 8 ? wv + 8 * b : wv % NTW;
-      const int mstep = NTW >= 8 ? 1 : 8 / NTW;
-      for (int mtl = NTW >= 8 ? 0 : wv / NTW; mtl < 4; mtl += mstep) {
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
-        const u32x4 *ar = reinterpret_cast<const u32x4 *>(zb + (mtl * 16 + (lane & 15)) * kZBP) + (lane >> 4);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          if (kb < NN) acc = mma(ar[kb * 4], tb[b][kb], acc);
-        uint16_t *dst = os + (mtl * 16 + 4 * (lane >> 4)) * PITCH * 8 + ntl * 16 + (lane & 15);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float v = acc[j] * isc;
-          dst[j * PITCH * 8] = DT == DT_F16 ? h16(v) : (uint16_t)f32_to_bf16(v);
+      for (int i = 0; i < NY; ++i) {
+        const int v = tid + i * kFT;
+        if (v < K) {
+          const int q = v / m2, ky = v - q * m2;
+          const int kx = q < m1 ? q : H - 2 * m1 + q;
+          const float2 w = twh[(kx * kRows * r) & (H - 1)];  // e^{-i theta}
+          const float zr = (yv[i].x * w.x + yv[i].y * w.y) * sc;
+          const float zi = (yv[i].y * w.x - yv[i].x * w.y) * sc;
+          reinterpret_cast<uint32_t *>(yb + ky * kRBP)[q] = h16x2(zr, zi);
         }
       }
-    }
-    __syncthreads();
+      __syncthreads();
 
-    // 64 rows x W halves: coalesced 16-byte stores
+      // 2. Z = E' Y, rows 16 wv .. 16 wv + 15, all ky tiles; fp16 into zb
 #pragma unroll
-    for (int v = 0; v < KB / 2; ++v) {
-      const int e2 = v * kGT + tid;
-      const int row = e2 / WU, cu = e2 - row * WU;
-      yp[(size_t)r * kRows * WU + e2] = reinterpret_cast<const uint4 *>(ostage)[row * PITCH + cu];
+      for (int nn = 0; nn < 2; ++nn) {
+        if (nn < NN) {
+          const u32x4 *br = reinterpret_cast<const u32x4 *>(yb + (nn * 16 + (lane & 15)) * kRBP) + (lane >> 4);
+          u32x4 bv[4];
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) bv[kb] = br[(kb < KB1 ? kb : 0) * 4];
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int mi = 0; mi < 2; ++mi) {
+            v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+              if (kb < KB1) acc = mma(ef[mi][kb], bv[kb], acc);
+            const int j0 = 8 * (2 * wv + mi) + 2 * (lane >> 4), ky = nn * 16 + (lane & 15);
+            reinterpret_cast<uint32_t *>(zb + j0 * kZBP)[ky] = h16x2(acc[0], acc[1]);
+            reinterpret_cast<uint32_t *>(zb + (j0 + 1) * kZBP)[ky] = h16x2(acc[2], acc[3]);
+          }
+        }
+      }
+      __syncthreads();
+
+      // 3. y^T = T'^T Z^T: lane gets y[h][w .. w + 3], h = 16 mt + l % 16
+      uint16_t *os = reinterpret_cast<uint16_t *>(ostage);
+      u32x4 bz[4][2];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const u32x4 *zr = reinterpret_cast<const u32x4 *>(zb + (mt * 16 + (lane & 15)) * kZBP) + (lane >> 4);
+        bz[mt][0] = zr[0];
+        bz[mt][1] = zr[NN > 1 ? 4 : 0];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int h = mt * 16 + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < NPW; ++i) {
+          v4f acc = {0.f, 0.f, 0.f, 0.f};
+          acc = mma(tb[i][0], bz[mt][0], acc);
+          if (NN > 1) acc = mma(tb[i][1], bz[mt][1], acc);
+          const int w = (wv + 4 * i) * 16 + 4 * (lane >> 4);
+          uint2 o;
+          if constexpr (DT == DT_F16) {
+            o.x = h16x2(acc[0] * isc, acc[1] * isc);
+            o.y = h16x2(acc[2] * isc, acc[3] * isc);
+          } else {
+            o.x = f32x2_to_bf16x2(acc[0] * isc, acc[1] * isc);
+            o.y = f32x2_to_bf16x2(acc[2] * isc, acc[3] * isc);
+          }
+          *reinterpret_cast<uint2 *>(os + h * PITCH * 8 + w) = o;
+        }
+      }
+      __syncthreads();
+
+      // 4. 64 rows x W halves: coalesced 16-byte stores
+#pragma unroll
+      for (int v = 0; v < KB; ++v) {
+        const int e2 = v * kFT + tid;
+        const int row = e2 / WU, cu = e2 - row * WU;
+        yp[(size_t)r * kRows * WU + e2] = reinterpret_cast<const uint4 *>(ostage)[row * PITCH + cu];
+      }
     }
+#pragma unroll
+    for (int i = 0; i < NY; ++i) yv[i] = yn[i];
   }
 }
 
@@ -398,47 +491,69 @@ bool mx_supported(int H, int W, int m1, int m2, int dtype) {
 int mx_ntiles(int m2) { return m2 <= 8 ? 1 : m2 <= 16 ? 2 : 4; }
 
 size_t mx_fwd_lds_bytes(int H, int W) {
-  return (size_t)kRows * (W / 8 + 1) * 16 + (size_t)32 * kRBP * 2 + (size_t)H * 8 + 64;
+  return (size_t)kRows * (W / 8 + 1) * 16 + (size_t)32 * kRBP * 2 + (size_t)H * 8 + (size_t)(kRows + 8) * 4;
 }
 
 size_t mx_inv_lds_bytes(int H, int W) {
-  return (size_t)kRows * (W / 8 + 1) * 16 + (size_t)32 * kRBP * 2 + (size_t)kRows * kZBP * 2 + (size_t)H * 8 + 32;
+  return (size_t)kRows * (W / 8 + 1) * 16 + (size_t)32 * kRBP * 2 + (size_t)kRows * kZBP * 2 + (size_t)H * 8 + 64;
+}
+
+template <int DT, int KB>
+static const void *mx_kernel_kb(bool fwd, bool two) {
+  if (!fwd) return (const void *)fno_inv_plane_mx<DT, KB>;
+  return two ? (const void *)fno_fwd_plane_mx<DT, KB, true> : (const void *)fno_fwd_plane_mx<DT, KB, false>;
 }
 
 template <int DT>
-static const void *mx_kernel_dt(bool fwd, int W) {
+static const void *mx_kernel_dt(bool fwd, int W, bool two) {
   switch (W) {
-    case 64: return fwd ? (const void *)fno_fwd_plane_mx<DT, 2> : (const void *)fno_inv_plane_mx<DT, 2>;
-    case 128: return fwd ? (const void *)fno_fwd_plane_mx<DT, 4> : (const void *)fno_inv_plane_mx<DT, 4>;
-    case 256: return fwd ? (const void *)fno_fwd_plane_mx<DT, 8> : (const void *)fno_inv_plane_mx<DT, 8>;
+    case 64: return mx_kernel_kb<DT, 2>(fwd, two);
+    case 128: return mx_kernel_kb<DT, 4>(fwd, two);
+    case 256: return mx_kernel_kb<DT, 8>(fwd, two);
   }
   return nullptr;
 }
 
-static const void *mx_kernel(bool fwd, int W, int dtype) {
-  if (dtype == DT_F16) return mx_kernel_dt<DT_F16>(fwd, W);
-  if (dtype == DT_BF16) return mx_kernel_dt<DT_BF16>(fwd, W);
+// m2 > 8: R has two or four 16-column tiles
+static const void *mx_kernel(bool fwd, int W, int m2, int dtype) {
+  const bool two = m2 > 8;
+  if (dtype == DT_F16) return mx_kernel_dt<DT_F16>(fwd, W, two);
+  if (dtype == DT_BF16) return mx_kernel_dt<DT_BF16>(fwd, W, two);
   return nullptr;
 }
 
-hipError_t mx_prepare(bool fwd, int W, int dtype, size_t lds) {
-  const void *k = mx_kernel(fwd, W, dtype);
+hipError_t mx_prepare(bool fwd, int W, int m2, int dtype, size_t lds) {
+  const void *k = mx_kernel(fwd, W, m2, dtype);
   if (!k) return hipErrorInvalidValue;
   return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
-hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int dtype, size_t lds, hipStream_t s) {
-  const void *k = mx_kernel(true, a.W, dtype);
+// workgroups of a persistent plane kernel: as many as are resident at once
+// on the device (never more than planes)
+hipError_t mx_grid(bool fwd, int W, int m2, int dtype, size_t lds, int device, int nplanes, int *grid) {
+  const void *k = mx_kernel(fwd, W, m2, dtype);
   if (!k) return hipErrorInvalidValue;
-  void *args[] = {(void *)&a};
-  return hipLaunchKernel(k, dim3(a.nplanes), dim3(kGT), args, lds, s);
+  int per_cu = 0, ncu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kFT, lds);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return e;
+  long g = (long)(per_cu > 0 ? per_cu : 1) * (ncu > 0 ? ncu : 1);
+  *grid = (int)(g < nplanes ? g : nplanes);
+  return hipSuccess;
 }
 
-hipError_t launch_plane_mx_inv(const PlaneMxInvArgs &a, int dtype, size_t lds, hipStream_t s) {
-  const void *k = mx_kernel(false, a.W, dtype);
-  if (!k) return hipErrorInvalidValue;
+hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int grid, int dtype, size_t lds, hipStream_t s) {
+  const void *k = mx_kernel(true, a.W, a.m2, dtype);
+  if (!k || grid < 1) return hipErrorInvalidValue;
   void *args[] = {(void *)&a};
-  return hipLaunchKernel(k, dim3(a.nplanes), dim3(kGT), args, lds, s);
+  return hipLaunchKernel(k, dim3(grid), dim3(kFT), args, lds, s);
+}
+
+hipError_t launch_plane_mx_inv(const PlaneMxInvArgs &a, int grid, int dtype, size_t lds, hipStream_t s) {
+  const void *k = mx_kernel(false, a.W, a.m2, dtype);
+  if (!k || grid < 1) return hipErrorInvalidValue;
+  void *args[] = {(void *)&a};
+  return hipLaunchKernel(k, dim3(grid), dim3(kFT), args, lds, s);
 }
 
 }  // namespace fno

@@ -58,6 +58,10 @@ SMALL = [
     ("mx-2d-m1", _cfg("r", 2, 2, 3, 1, (64, 64), (1, 1), "uniform"), "bf16"),
     ("mx-2d-c4", _cfg("r", 2, 1, 4, 4, (256, 256), (24, 24)), "f16"),
     ("mx-3d", _cfg("r", 3, 1, 3, 2, (8, 64, 128), (3, 12, 20), "uniform"), "f16"),
+    # fp16 / bf16 contraction on matrix cores: ragged batch, channel and mode
+    # tiles (two batch tiles, partial input stages, partial output tiles)
+    ("cmx-rag-f16", _cfg("r", 2, 33, 20, 36, (64, 64), (6, 5), "uniform"), "f16"),
+    ("cmx-rag-bf16", _cfg("r", 2, 17, 33, 12, (64, 128), (9, 7), "uniform"), "bf16"),
 ]
 
 
@@ -79,11 +83,11 @@ def test_parity_small(case):
 def test_parity_magnitude(dtype, scale):
     """The half-precision plane products rescale by powers of two chosen from
     the data; inputs far from unit magnitude must keep the same accuracy."""
-    cfg = _cfg("m", 2, 2, 3, 3, (128, 128), (16, 16), seed=7)
+    cfg = _cfg("m", 2, 2, 3, 4, (128, 128), (16, 16), seed=7)
     inp = wl.layer_inputs(cfg, dtype)
     xs = wl.round_to_storage(inp["x64"] * scale, dtype)
     x64 = wl.storage_to_float64(xs, dtype)
-    got, _ = run_layer(2, 2, 3, 3, cfg.grid, cfg.modes, dtype, xs, inp["w"])
+    got, _ = run_layer(2, 2, 3, 4, cfg.grid, cfg.modes, dtype, xs, inp["w"])
     ref = oracle.spectral_conv2d(x64, inp["w64"], *cfg.modes)
     err = rel_l2(got, ref)
     print(f"[parity-mag] {dtype} scale={scale:.3g} rel_l2={err:.3e}", flush=True)
