@@ -90,15 +90,15 @@ struct PlaneInvArgs {
   int ppw;  // planes per workgroup
 };
 
-// Plane transforms of fp16 / bf16 planes as matrix-core products
-// (H in [64, 256], W in {64, 128, 256}, m1, m2 <= 32). Fragment tables hold
-// 8 halves per lane in MFMA operand order.
+// Plane transforms as matrix-core products (H in [64, 256], W in {64, 128,
+// 256} (fp32: {64, 128}), m1, m2 <= 32). Fragment tables hold 8 fp16 per lane
+// in MFMA operand order; fp32 plans add the fp16 remainders (*_lo).
 struct PlaneMxFwdArgs {
   const void *x;
   float2 *out;         // [nplanes][2 m1][m2] complex, times `scale`
   const float2 *tw_h;  // exp(-2 pi i k / H), k < H
-  const uint4 *tf;     // row DFT, A operand of the transposed product [NT][W/32][64]
-  const uint4 *ef;     // column DFT of a 64-row block, A operand [MT][4][64]
+  const uint4 *tf, *tf_lo;  // row DFT, A operand of the transposed product [NT][W/32][64]
+  const uint4 *ef, *ef_lo;  // column DFT of a 64-row block, A operand [MT][4][64]
   int nplanes, H, W, m1, m2;
   int nt, mt, nn, lgW;  // column tiles of R, m-tiles of X, 16-wide ky tiles, log2 W
   float scale;
@@ -108,8 +108,8 @@ struct PlaneMxInvArgs {
   const float2 *in;    // [nplanes][2 m1][m2] complex
   void *y;
   const float2 *tw_h;  // exp(-2 pi i k / H), k < H
-  const uint4 *ef;     // inverse column DFT of a 64-row block, A operand [8][kb1][64]
-  const uint4 *tb;     // inverse row DFT, B operand [W/16][nn][64]
+  const uint4 *ef, *ef_lo;  // inverse column DFT of a 64-row block, A operand [8][kb1][64]
+  const uint4 *tb, *tb_lo;  // inverse row DFT, A operand of the transposed product [W/16][nn][64]
   int nplanes, H, W, m1, m2;
   int nn, kb1, lg4m1;  // 16-wide ky tiles, 32-deep blocks of 4 m1, ceil(log2(4 m1))
 };
@@ -144,10 +144,10 @@ hipError_t launch_plane_fwd(const PlaneFwdArgs &a, int MP, int rpt, int dtype, s
 hipError_t launch_plane_inv(const PlaneInvArgs &a, int MP, int rpt, int dtype, size_t lds, hipStream_t s);
 int mx_ntiles(int m2);
 bool mx_supported(int H, int W, int m1, int m2, int dtype);
-size_t mx_fwd_lds_bytes(int H, int W);
-size_t mx_inv_lds_bytes(int H, int W);
-hipError_t mx_prepare(bool fwd, int W, int m2, int dtype, size_t lds);
-hipError_t mx_grid(bool fwd, int W, int m2, int dtype, size_t lds, int device, int nplanes, int *grid);
+size_t mx_fwd_lds_bytes(int H, int W, int dtype);
+size_t mx_inv_lds_bytes(int H, int W, int dtype);
+hipError_t mx_prepare(bool fwd, int W, int m1, int m2, int dtype, size_t lds);
+hipError_t mx_grid(bool fwd, int W, int m1, int m2, int dtype, size_t lds, int device, int nplanes, int *grid);
 hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int grid, int dtype, size_t lds, hipStream_t s);
 hipError_t launch_plane_mx_inv(const PlaneMxInvArgs &a, int grid, int dtype, size_t lds, hipStream_t s);
 hipError_t axis_fwd_prepare(int MP, size_t lds);

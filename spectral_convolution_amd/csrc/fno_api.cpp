@@ -63,6 +63,18 @@ std::vector<float2> twiddles(int n) {
 
 uint16_t half_bits(double v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
 
+// fp16 parts of table values: hi = fp16(v) and, when lo is given,
+// lo = fp16(v - hi) (fp32 plans carry both)
+void half_parts(const std::vector<double> &v, std::vector<uint16_t> &hi, std::vector<uint16_t> *lo) {
+  hi.resize(v.size());
+  if (lo) lo->resize(v.size());
+  for (size_t i = 0; i < v.size(); ++i) {
+    const _Float16 h = (_Float16)v[i];
+    hi[i] = __builtin_bit_cast(uint16_t, h);
+    if (lo) (*lo)[i] = half_bits(v[i] - (double)h);
+  }
+}
+
 // cos and sin of 2 pi k / n (k reduced mod n in integers, quarter turns exact)
 void cos_sin_2pi(long k, long n, double &c, double &s) {
   const long r = ((k % n) + n) % n;
@@ -81,7 +93,7 @@ void cos_sin_2pi(long k, long n, double &c, double &s) {
 // block kb holds T[w][c] for c = 16 nt + l % 16 and w = 32 kb + 8 (l / 16) + i,
 // T[w][2 ky] = cos(2 pi ky w / W), T[w][2 ky + 1] = -sin(..), zero for
 // ky >= m2 (the A operand of the transposed row product R^T = T^T x^T).
-void fwd_fragments(int W, int m2, int NT, std::vector<uint16_t> &hi) {
+void fwd_fragments(int W, int m2, int NT, std::vector<double> &hi) {
   const int KB = W / 32;
   hi.assign((size_t)NT * KB * 64 * 8, 0);
   for (int nt = 0; nt < NT; ++nt)
@@ -95,13 +107,13 @@ void fwd_fragments(int W, int m2, int NT, std::vector<uint16_t> &hi) {
             cos_sin_2pi((long)ky * w, W, cs, sn);
             v = (c & 1) ? -sn : cs;
           }
-          hi[(((size_t)nt * KB + kb) * 64 + l) * 8 + i] = half_bits(v);
+          hi[(((size_t)nt * KB + kb) * 64 + l) * 8 + i] = v;
         }
 }
 
 // Inverse row fragments (B operand, K = c, N = w): [wt][kb][lane][8],
 // value T'[c][w] = g cos / -g sin (2 pi ky w / W), g = 1 for ky = 0, else 2.
-void inv_fragments(int W, int m2, int KBT, std::vector<uint16_t> &tb) {
+void inv_fragments(int W, int m2, int KBT, std::vector<double> &tb) {
   const int NWT = W / 16;
   tb.assign((size_t)NWT * KBT * 64 * 8, 0);
   for (int wt = 0; wt < NWT; ++wt)
@@ -116,7 +128,7 @@ void inv_fragments(int W, int m2, int KBT, std::vector<uint16_t> &tb) {
             const double g = ky == 0 ? 1.0 : 2.0;
             v = (c & 1) ? -g * sn : g * cs;
           }
-          tb[(((size_t)wt * KBT + kb) * 64 + l) * 8 + i] = half_bits(v);
+          tb[(((size_t)wt * KBT + kb) * 64 + l) * 8 + i] = v;
         }
 }
 
@@ -124,7 +136,7 @@ void inv_fragments(int W, int m2, int KBT, std::vector<uint16_t> &tb) {
 // K = (j, re/im)): [mt][kb][lane][8]. Row m = 2q + po, column k = 2j + pi of
 // the real form of e^{-i theta}, theta = 2 pi kx(q) j / H:
 // [[cos, sin], [-sin, cos]]; zero rows for q >= 2 m1.
-void fwd_col_fragments(int H, int m1, int MT, std::vector<uint16_t> &ef) {
+void fwd_col_fragments(int H, int m1, int MT, std::vector<double> &ef) {
   ef.assign((size_t)MT * 4 * 64 * 8, 0);
   for (int mt = 0; mt < MT; ++mt)
     for (int kb = 0; kb < 4; ++kb)
@@ -139,14 +151,14 @@ void fwd_col_fragments(int H, int m1, int MT, std::vector<uint16_t> &ef) {
             cos_sin_2pi((long)kx * j, H, cs, sn);
             v = po == 0 ? (pi == 0 ? cs : sn) : (pi == 0 ? -sn : cs);
           }
-          ef[(((size_t)mt * 4 + kb) * 64 + l) * 8 + i] = half_bits(v);
+          ef[(((size_t)mt * 4 + kb) * 64 + l) * 8 + i] = v;
         }
 }
 
 // Column DFT of one 64-row block, inverse (A operand, M = (j, re/im),
 // K = (q, re/im)): [8][kb1][lane][8], real form of e^{+i theta}:
 // [[cos, -sin], [sin, cos]]; zero columns for q >= 2 m1.
-void inv_col_fragments(int H, int m1, int KB1, std::vector<uint16_t> &ef) {
+void inv_col_fragments(int H, int m1, int KB1, std::vector<double> &ef) {
   ef.assign((size_t)8 * KB1 * 64 * 8, 0);
   for (int mt = 0; mt < 8; ++mt)
     for (int kb = 0; kb < KB1; ++kb)
@@ -161,7 +173,7 @@ void inv_col_fragments(int H, int m1, int KB1, std::vector<uint16_t> &ef) {
             cos_sin_2pi((long)kx * j, H, cs, sn);
             v = po == 0 ? (pi == 0 ? cs : -sn) : (pi == 0 ? sn : cs);
           }
-          ef[(((size_t)mt * KB1 + kb) * 64 + l) * 8 + i] = half_bits(v);
+          ef[(((size_t)mt * KB1 + kb) * 64 + l) * 8 + i] = v;
         }
 }
 
@@ -191,6 +203,7 @@ struct fno_plan_s {
   bool mx = false;
   int mx_nt = 0, mx_mt = 0, mx_nn = 0, mx_kb1 = 0, mx_lgW = 0, mx_lg4m1 = 0, mx_grid_f = 0, mx_grid_i = 0;
   uint4 *tf = nullptr, *tb = nullptr, *ef_f = nullptr, *ef_i = nullptr;
+  uint4 *tf_lo = nullptr, *tb_lo = nullptr, *ef_f_lo = nullptr, *ef_i_lo = nullptr;  // fp32 plans
   float2 *tw_h = nullptr, *tw_w = nullptr, *tw_x = nullptr;
   float2 *xh = nullptr, *yh = nullptr, *tbuf = nullptr;
   void *mem = nullptr;
@@ -263,8 +276,8 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
     p.mx_kb1 = (p.pm1 + 7) / 8;
     p.mx_lgW = ceil_log2(p.pW);
     p.mx_lg4m1 = ceil_log2(4 * p.pm1);
-    p.lds_fwd = mx_fwd_lds_bytes(p.pH, p.pW);
-    p.lds_inv = mx_inv_lds_bytes(p.pH, p.pW);
+    p.lds_fwd = mx_fwd_lds_bytes(p.pH, p.pW, (int)dtype);
+    p.lds_inv = mx_inv_lds_bytes(p.pH, p.pW, (int)dtype);
   }
   if (p.lds_fwd > kMaxLds || p.lds_inv > kMaxLds) return FNO_ERR_UNSUPPORTED;
   if (ndim == 3) {
@@ -375,17 +388,26 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   const size_t o_xh = off; off += al(n_xh * sizeof(float2));
   const size_t o_yh = off; off += al(n_yh * sizeof(float2));
   const size_t o_t = off; off += al(n_t * sizeof(float2));
-  std::vector<uint16_t> tfh, tbv, efv, eiv;
+  std::vector<uint16_t> tfh, tfl, tbh, tbl, efh, efl, eih, eil;
   if (p->mx) {
-    fwd_fragments(p->pW, p->pm2, p->mx_nt, tfh);
-    inv_fragments(p->pW, p->pm2, p->mx_nn, tbv);
-    fwd_col_fragments(p->pH, p->pm1, p->mx_mt, efv);
-    inv_col_fragments(p->pH, p->pm1, p->mx_kb1, eiv);
+    const bool sp = p->dtype == FNO_F32;
+    std::vector<double> v;
+    fwd_fragments(p->pW, p->pm2, p->mx_nt, v);
+    half_parts(v, tfh, sp ? &tfl : nullptr);
+    inv_fragments(p->pW, p->pm2, p->mx_nn, v);
+    half_parts(v, tbh, sp ? &tbl : nullptr);
+    fwd_col_fragments(p->pH, p->pm1, p->mx_mt, v);
+    half_parts(v, efh, sp ? &efl : nullptr);
+    inv_col_fragments(p->pH, p->pm1, p->mx_kb1, v);
+    half_parts(v, eih, sp ? &eil : nullptr);
   }
-  const size_t o_tf = off; off += al(tfh.size() * 2);
-  const size_t o_tb = off; off += al(tbv.size() * 2);
-  const size_t o_ef = off; off += al(efv.size() * 2);
-  const size_t o_ei = off; off += al(eiv.size() * 2);
+  // fragment tables: hi parts, then (fp32) lo parts, each 256-byte aligned
+  std::vector<uint16_t> *tabs[8] = {&tfh, &tbh, &efh, &eih, &tfl, &tbl, &efl, &eil};
+  size_t o_tab[8];
+  for (int t = 0; t < 8; ++t) {
+    o_tab[t] = off;
+    off += al(tabs[t]->size() * 2);
+  }
   p->ws_bytes = off;
   hipError_t e = hipMalloc(&p->mem, off);
   if (e != hipSuccess) {
@@ -401,12 +423,16 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   p->xh = (float2 *)(base + o_xh);
   p->yh = (float2 *)(base + o_yh);
   p->tbuf = n_t ? (float2 *)(base + o_t) : nullptr;
-  if (p->mx) {
-    p->tf = (uint4 *)(base + o_tf);
-    p->tb = (uint4 *)(base + o_tb);
-    p->ef_f = (uint4 *)(base + o_ef);
-    p->ef_i = (uint4 *)(base + o_ei);
-  }
+  uint4 *tab_ptr[8] = {};
+  for (int t = 0; t < 8; ++t) tab_ptr[t] = tabs[t]->empty() ? nullptr : (uint4 *)(base + o_tab[t]);
+  p->tf = tab_ptr[0];
+  p->tb = tab_ptr[1];
+  p->ef_f = tab_ptr[2];
+  p->ef_i = tab_ptr[3];
+  p->tf_lo = tab_ptr[4];
+  p->tb_lo = tab_ptr[5];
+  p->ef_f_lo = tab_ptr[6];
+  p->ef_i_lo = tab_ptr[7];
 
   std::vector<float2> th = twiddles(nth), tw = twiddles(ntw);
   e = hipMemcpy(p->tw_h, th.data(), nth * sizeof(float2), hipMemcpyHostToDevice);
@@ -416,17 +442,15 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
     e = hipMemcpy(p->tw_x, tx.data(), ntx * sizeof(float2), hipMemcpyHostToDevice);
   }
   if (e == hipSuccess && p->mx) {
-    e = hipMemcpy(p->tf, tfh.data(), tfh.size() * 2, hipMemcpyHostToDevice);
-    if (e == hipSuccess) e = hipMemcpy(p->tb, tbv.data(), tbv.size() * 2, hipMemcpyHostToDevice);
-    if (e == hipSuccess) e = hipMemcpy(p->ef_f, efv.data(), efv.size() * 2, hipMemcpyHostToDevice);
-    if (e == hipSuccess) e = hipMemcpy(p->ef_i, eiv.data(), eiv.size() * 2, hipMemcpyHostToDevice);
-    if (e == hipSuccess) e = mx_prepare(true, p->pW, p->pm2, p->dtype, p->lds_fwd);
-    if (e == hipSuccess) e = mx_prepare(false, p->pW, p->pm2, p->dtype, p->lds_inv);
+    for (int t = 0; t < 8 && e == hipSuccess; ++t)
+      if (tab_ptr[t]) e = hipMemcpy(tab_ptr[t], tabs[t]->data(), tabs[t]->size() * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = mx_prepare(true, p->pW, p->pm1, p->pm2, p->dtype, p->lds_fwd);
+    if (e == hipSuccess) e = mx_prepare(false, p->pW, p->pm1, p->pm2, p->dtype, p->lds_inv);
     if (e == hipSuccess)
-      e = mx_grid(true, p->pW, p->pm2, p->dtype, p->lds_fwd, p->device, p->B * p->Ci * (ndim == 3 ? p->xN : 1),
+      e = mx_grid(true, p->pW, p->pm1, p->pm2, p->dtype, p->lds_fwd, p->device, p->B * p->Ci * (ndim == 3 ? p->xN : 1),
                   &p->mx_grid_f);
     if (e == hipSuccess)
-      e = mx_grid(false, p->pW, p->pm2, p->dtype, p->lds_inv, p->device, p->B * p->Co * (ndim == 3 ? p->xN : 1),
+      e = mx_grid(false, p->pW, p->pm1, p->pm2, p->dtype, p->lds_inv, p->device, p->B * p->Co * (ndim == 3 ? p->xN : 1),
                   &p->mx_grid_i);
   } else {
     if (e == hipSuccess) e = plane_prepare(true, p->pMP, p->rpt, p->dtype, p->lds_fwd);
@@ -476,7 +500,9 @@ static hipError_t run_one(fno_plan_t p, int kind, const void *x, const void *w, 
         m.out = nd == 2 ? p->xh : p->tbuf;
         m.tw_h = p->tw_h;
         m.tf = p->tf;
+        m.tf_lo = p->tf_lo;
         m.ef = p->ef_f;
+        m.ef_lo = p->ef_f_lo;
         m.nplanes = p->B * p->Ci * (nd == 3 ? p->xN : 1);
         m.H = p->pH;
         m.W = p->pW;
@@ -550,7 +576,9 @@ static hipError_t run_one(fno_plan_t p, int kind, const void *x, const void *w, 
         m.y = y;
         m.tw_h = p->tw_h;
         m.tb = p->tb;
+        m.tb_lo = p->tb_lo;
         m.ef = p->ef_i;
+        m.ef_lo = p->ef_i_lo;
         m.nplanes = p->B * p->Co * (nd == 3 ? p->xN : 1);
         m.H = p->pH;
         m.W = p->pW;

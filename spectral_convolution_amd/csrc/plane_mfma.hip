@@ -60,17 +60,20 @@ __device__ __forceinline__ uint32_t h16x2(float lo, float hi) {
   return (uint32_t)h16(lo) | ((uint32_t)h16(hi) << 16);
 }
 
-// largest magnitude field of eight packed 16-bit floats (sign cleared); for
-// finite fp16 and bf16 values the unsigned order of these bits is the order
-// of the magnitudes
-__device__ __forceinline__ uint32_t absmax_bits(u32x4 v) {
-  uint32_t m = 0;
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// running maximum of the magnitude fields (sign cleared) of eight packed
+// 16-bit floats, two lanes at a time (v_pk_max_u16); for finite fp16 and
+// bf16 values the unsigned order of these bits is the order of magnitudes
+__device__ __forceinline__ u16x2 absmax_acc(u16x2 m, u32x4 v) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m = max(m, v[i] & 0x7fffu);
-    m = max(m, (v[i] >> 16) & 0x7fffu);
-  }
+  for (int i = 0; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v[i] & 0x7fff7fffu));
   return m;
+}
+
+__device__ __forceinline__ uint32_t absmax_bits(u32x4 v) {
+  const u16x2 m = absmax_acc(u16x2{0, 0}, v);
+  return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
@@ -95,16 +98,44 @@ __device__ __forceinline__ float pow2f(int e) {
 
 constexpr int kFT = 256;  // threads per workgroup of both plane kernels (4 waves)
 
+// Storage policy: fp32 planes are carried as fp16 hi + lo parts (two
+// operands, three products per pair, hi*hi + hi*lo + lo*hi); fp16 and bf16
+// planes as one fp16 part.
+template <int DT>
+struct MxPol {
+  static constexpr bool SP = DT == DT_F32;  // split operands
+  static constexpr int NP = SP ? 2 : 1;     // fp16 parts per operand
+  static constexpr int ES = SP ? 4 : 2;     // storage bytes per element
+};
+
+__device__ __forceinline__ v4f mma_sp(const u32x4 (&a)[2], const u32x4 (&b)[2], v4f c, bool sp) {
+  c = mma(a[0], b[0], c);
+  if (sp) {
+    c = mma(a[0], b[1], c);
+    c = mma(a[1], b[0], c);
+  }
+  return c;
+}
+
+// fp32 -> fp16 hi, fp16 lo = fp16(v - hi), packed for two values
+__device__ __forceinline__ void split2(float v0, float v1, uint32_t &hi, uint32_t &lo) {
+  const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
+  hi = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+  lo = h16x2(v0 - (float)h0, v1 - (float)h1);
+}
+
 // rows of global round g of this workgroup: plane blockIdx.x + (g >> lgr)
-// * gridDim.x, rows 64 (g mod 2^lgr) .. +63; KB 16-byte units per thread
-template <int KB>
-__device__ __forceinline__ void fwd_fetch(const uint16_t *x, int g, int lgr, int H, int tid, u32x4 (&p)[KB]) {
-  constexpr int W = 32 * KB, WU = 4 * KB;
+// * gridDim.x, rows 64 (g mod 2^lgr) .. +63; FU 16-byte units per thread
+template <int DT, int KB>
+__device__ __forceinline__ void fwd_fetch(const void *x, int g, int lgr, int H, int tid,
+                                          u32x4 (&p)[KB * MxPol<DT>::ES / 2]) {
+  constexpr int W = 32 * KB, UR = W * MxPol<DT>::ES / 16;  // 16-byte units per row
   const size_t plane = (size_t)blockIdx.x + (size_t)(g >> lgr) * gridDim.x;
   const int r = g & ((1 << lgr) - 1);
-  const u32x4 *src = reinterpret_cast<const u32x4 *>(x + plane * H * W) + (size_t)r * kRows * WU + tid;
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(x) + plane * H * W * MxPol<DT>::ES) +
+                     (size_t)r * kRows * UR + tid;
 #pragma unroll
-  for (int v = 0; v < KB; ++v) p[v] = src[v * kFT];
+  for (int v = 0; v < KB * MxPol<DT>::ES / 2; ++v) p[v] = src[v * kFT];
 }
 
 // eight bf16 -> eight fp16 times 2^sig (exact while the result is normal)
@@ -122,49 +153,86 @@ struct FwdShape {
   int H, m1, m2, NT, MT, NN, lgW, lgr, total;  // lgr: log2 rounds per plane; total: rounds of this workgroup
 };
 
+template <int DT, int KB, bool TWO, int MPW>
+struct FwdRegs {
+  static constexpr int NP = MxPol<DT>::NP;
+  u32x4 th[TWO ? 2 : 1][NP][KB];  // row twiddles (A operand) of this wave's c-tiles
+  u32x4 ef[MPW][NP][4];           // column twiddles (A operand) of this wave's m-tiles
+};
+
 // One round of 64 rows:
-//  1. stage the rows in LDS as fp16 (bf16 rows scaled by a power of two per
-//     row into fp16 range), note the largest exponent of the round;
+//  1. stage the rows in LDS as fp16 (bf16 and fp32 rows scaled by a power of
+//     two per row into fp16 range; fp32 as hi + lo), note the largest
+//     exponent of the round;
 //  2. row product, transposed: R^T[c][h] = sum_w T[w][c] x[h][w] with the
 //     twiddles as the register-held A operand (two 16-column tiles of R per
 //     wave) and x as B, so each staged fragment feeds two products; R is
-//     scaled by a power of two (undone in 4) and stored as fp16 pairs;
+//     scaled by a power of two (undone in 3) and stored as fp16 pairs;
 //  3. column product of R against the 64-row twiddle block (two m-tiles of
 //     modes per wave), phase-shifted by the round offset into X.
-template <int DT, int KB, bool TWO>
-__device__ __forceinline__ void fwd_round(int g, const FwdShape &s, u32x4 (&p)[KB], const PlaneMxFwdArgs &a,
-                                          u32x4 *stage, uint16_t *rb, const float2 *twh, int *rsig, int *mxs,
-                                          const u32x4 (&th)[TWO ? 2 : 1][KB], const u32x4 (&ef)[2][4],
-                                          float2 (&X)[2][2][2]) {
-  constexpr bool BF = DT == DT_BF16;
-  constexpr int WU = 4 * KB, PITCH = WU + 1;
+template <int DT, int KB, bool TWO, int MPW>
+__device__ __forceinline__ void fwd_round(int g, const FwdShape &s, u32x4 (&p)[KB * MxPol<DT>::ES / 2],
+                                          const PlaneMxFwdArgs &a, u32x4 *stage, uint16_t *rb, const float2 *twh,
+                                          int *rsig, int *mxs, const FwdRegs<DT, KB, TWO, MPW> &R,
+                                          float2 (&X)[MPW][2][2]) {
+  using P = MxPol<DT>;
+  constexpr bool BF = DT == DT_BF16, SP = P::SP;
+  constexpr int NP = P::NP;
+  constexpr int W = 32 * KB, WU = 4 * KB, PITCH = WU + 1;  // stage row: W halves, PITCH 16-byte units
+  constexpr int UR = W * P::ES / 16, FU = KB * P::ES / 2;
+  constexpr int STG = kRows * PITCH;                         // units per stage part
+  constexpr int RBS = 32 * kRBP;                             // halves per R part
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = g & ((1 << s.lgr) - 1);
 
   int emax = -1000;
+  u16x2 mrun = {0, 0};
 #pragma unroll
-  for (int v = 0; v < KB; ++v) {
+  for (int v = 0; v < FU; ++v) {
     const int e = v * kFT + tid;
-    const int row = e / WU, cu = e - row * WU;
-    u32x4 d = p[v];
-    uint32_t m = absmax_bits(d);
-    if constexpr (BF) {
+    const int row = e / UR, cu = e - row * UR;
+    const u32x4 d = p[v];
+    if constexpr (SP) {
+      // four fp32 of the row: scale by the row's power of two, split
+      uint32_t m = 0;
 #pragma unroll
-      for (int o = 1; o < WU; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+      for (int i = 0; i < 4; ++i) m = max(m, d[i] & 0x7fffffffu);
+#pragma unroll
+      for (int o = 1; o < UR; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+      const int eh = (int)max(m >> 23, 1u) - 126;  // row max < 2^eh
+      const int sig = max(-120, min(120, 14 - eh));
+      const float sc = pow2f(sig);
+      uint32_t h0, l0, h1, l1;
+      split2(__uint_as_float(d[0]) * sc, __uint_as_float(d[1]) * sc, h0, l0);
+      split2(__uint_as_float(d[2]) * sc, __uint_as_float(d[3]) * sc, h1, l1);
+      uint2 *hp = reinterpret_cast<uint2 *>(stage + row * PITCH) + cu;
+      uint2 *lp = reinterpret_cast<uint2 *>(stage + STG + row * PITCH) + cu;
+      *hp = make_uint2(h0, h1);
+      *lp = make_uint2(l0, l1);
+      if ((tid & (UR - 1)) == 0) rsig[row] = m ? sig : 0;
+      emax = max(emax, m ? eh : -1000);
+    } else if constexpr (BF) {
+      uint32_t m = absmax_bits(d);
+#pragma unroll
+      for (int o = 1; o < UR; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
       const int eh = (int)max(m >> 7, 1u) - 126;  // row max < 2^eh
       const int sig = max(-120, min(120, 14 - eh));
-      d = bf16_to_f16_scaled(d, pow2f(sig));
-      if ((tid & (WU - 1)) == 0) rsig[row] = m ? sig : 0;
+      stage[row * PITCH + cu] = bf16_to_f16_scaled(d, pow2f(sig));
+      if ((tid & (UR - 1)) == 0) rsig[row] = m ? sig : 0;
       emax = max(emax, m ? eh : -1000);
     } else {
-      emax = max(emax, m ? (int)max(m >> 10, 1u) - 14 : -1000);
+      mrun = absmax_acc(mrun, d);
+      stage[row * PITCH + cu] = d;
     }
-    stage[row * PITCH + cu] = d;
+  }
+  if constexpr (!BF && !SP) {
+    const uint32_t m = max((uint32_t)mrun.x, (uint32_t)mrun.y);
+    emax = m ? (int)max(m >> 10, 1u) - 14 : -1000;
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) emax = max(emax, __shfl_xor(emax, o, 64));
   if (lane == 0) mxs[(g & 1) * 4 + wv] = emax;
-  if (g + 1 < s.total) fwd_fetch<KB>(reinterpret_cast<const uint16_t *>(a.x), g + 1, s.lgr, s.H, tid, p);
+  if (g + 1 < s.total) fwd_fetch<DT, KB>(a.x, g + 1, s.lgr, s.H, tid, p);
   __syncthreads();
 
   // |R| <= W max|x| < 2^(emax + lgW): R * 2^(15 - emax - lgW) < 2^15
@@ -181,38 +249,56 @@ __device__ __forceinline__ void fwd_round(int g, const FwdShape &s, u32x4 (&p)[K
     const int ct0 = (wv % G) * 2;
     for (int st = wv / G; st < 4; st += 4 / G) {
       const u32x4 *br = stage + (st * 16 + (lane & 15)) * PITCH + (lane >> 4);
-      u32x4 bv[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) bv[kb] = br[kb * 4];
-      __builtin_amdgcn_sched_barrier(0);  // keep all reads ahead of the products
+      // fragments are read in groups of KG blocks ahead of their products
+      constexpr int KG = SP && KB > 2 ? 2 : KB;
       v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        acc0 = mma(th[0][kb], bv[kb], acc0);
-        if constexpr (TWO) acc1 = mma(th[1][kb], bv[kb], acc1);
+      for (int k0 = 0; k0 < KB; k0 += KG) {
+        u32x4 bv[KG][2];
+#pragma unroll
+        for (int kb = 0; kb < KG; ++kb)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) bv[kb][q] = q < NP ? br[q * STG + (k0 + kb) * 4] : bv[kb][0];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < KG; ++kb) {
+          const u32x4 t0[2] = {R.th[0][0][k0 + kb], R.th[0][NP - 1][k0 + kb]};
+          acc0 = mma_sp(t0, bv[kb], acc0, SP);
+          if constexpr (TWO) {
+            const u32x4 t1[2] = {R.th[1][0][k0 + kb], R.th[1][NP - 1][k0 + kb]};
+            acc1 = mma_sp(t1, bv[kb], acc1, SP);
+          }
+        }
       }
       const int h = st * 16 + (lane & 15);
-      const float f = BF ? pow2f(se - rsig[h]) : pow2f(se);
+      const float f = (BF || SP) ? pow2f(se - rsig[h]) : pow2f(se);
       uint32_t *col = reinterpret_cast<uint32_t *>(rb) + h;
 #pragma unroll
       for (int t = 0; t < (TWO ? 2 : 1); ++t) {
         const v4f &acc = t == 0 ? acc0 : acc1;
         const int ky0 = 8 * (ct0 + t) + 2 * (lane >> 4);
-        if (ky0 < s.m2) col[ky0 * (kRBP / 2)] = h16x2(acc[0] * f, acc[1] * f);
-        if (ky0 + 1 < s.m2) col[(ky0 + 1) * (kRBP / 2)] = h16x2(acc[2] * f, acc[3] * f);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (ky0 + j < s.m2) {
+            uint32_t hi, lo;
+            split2(acc[2 * j] * f, acc[2 * j + 1] * f, hi, lo);
+            col[(ky0 + j) * (kRBP / 2)] = hi;
+            if constexpr (SP) col[RBS / 2 + (ky0 + j) * (kRBP / 2)] = lo;
+          }
+        }
       }
     }
   }
   __syncthreads();
 
-  // column product: m-tiles 2 wv, 2 wv + 1 (modes q0, q0 + 1 per lane each)
-  if (2 * wv < s.MT) {
-    float2 ph[2][2];
+  // column product: m-tiles MPW wv .. (modes q0, q0 + 1 per lane each)
+  if (MPW * wv < s.MT) {
+    float2 ph[MPW][2];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < MPW; ++mi)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int q = 8 * (2 * wv + mi) + 2 * (lane >> 4) + t;
+        const int q = 8 * (MPW * wv + mi) + 2 * (lane >> 4) + t;
         const int kx = q < s.m1 ? q : s.H - 2 * s.m1 + q;
         ph[mi][t] = twh[(kx * kRows * r) & (s.H - 1)];
       }
@@ -220,15 +306,20 @@ __device__ __forceinline__ void fwd_round(int g, const FwdShape &s, u32x4 (&p)[K
     for (int nn = 0; nn < 2; ++nn) {
       if (nn < s.NN) {
         const u32x4 *br = reinterpret_cast<const u32x4 *>(rb + (nn * 16 + (lane & 15)) * kRBP) + (lane >> 4);
-        u32x4 bv[4];
+        u32x4 bv[4][2];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) bv[kb] = br[kb * 4];
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) bv[kb][q] = q < NP ? br[q * (RBS / 8) + kb * 4] : bv[kb][0];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
+        for (int mi = 0; mi < MPW; ++mi) {
           v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb) acc = mma(ef[mi][kb], bv[kb], acc);
+          for (int kb = 0; kb < 4; ++kb) {
+            const u32x4 e2[2] = {R.ef[mi][0][kb], R.ef[mi][NP - 1][kb]};
+            acc = mma_sp(e2, bv[kb], acc, SP);
+          }
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const float yr = acc[2 * t] * isc, yi = acc[2 * t + 1] * isc;
@@ -243,13 +334,13 @@ __device__ __forceinline__ void fwd_round(int g, const FwdShape &s, u32x4 (&p)[K
       const size_t plane = (size_t)blockIdx.x + (size_t)(g >> s.lgr) * gridDim.x;
       float2 *op = a.out + plane * (2 * s.m1 * s.m2);
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < MPW; ++mi)
 #pragma unroll
         for (int nn = 0; nn < 2; ++nn) {
           const int ky = nn * 16 + (lane & 15);
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            const int q = 8 * (2 * wv + mi) + 2 * (lane >> 4) + t;
+            const int q = 8 * (MPW * wv + mi) + 2 * (lane >> 4) + t;
             if (nn < s.NN && ky < s.m2 && q < 2 * s.m1)
               op[q * s.m2 + ky] = make_float2(X[mi][nn][t].x * a.scale, X[mi][nn][t].y * a.scale);
             X[mi][nn][t] = make_float2(0.f, 0.f);
@@ -262,52 +353,58 @@ __device__ __forceinline__ void fwd_round(int g, const FwdShape &s, u32x4 (&p)[K
 // Persistent: workgroup b transforms planes b, b + gridDim.x, ...; its rounds
 // form one stream, the next one in flight while the current one is
 // multiplied, across plane boundaries. TWO: R has more than one 16-column
-// tile, and each wave computes two of them.
-template <int DT, int KB, bool TWO>
-__global__ __launch_bounds__(kFT) void fno_fwd_plane_mx(PlaneMxFwdArgs a) {
+// tile, and each wave computes two of them. MPW: m-tiles of modes per wave
+// (1 for up to 16 kx per corner, else 2).
+template <int DT, int KB, bool TWO, int MPW>
+__global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(2))) void fno_fwd_plane_mx(PlaneMxFwdArgs a) {
+  using P = MxPol<DT>;
+  constexpr int NP = P::NP;
   constexpr int WU = 4 * KB, PITCH = WU + 1;
   extern __shared__ u32x4 lds[];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int lgr = a.H == 256 ? 2 : a.H == 128 ? 1 : 0;
   const int nmine = (a.nplanes - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   const FwdShape s{a.H, a.m1, a.m2, a.nt, a.mt, a.nn, a.lgW, lgr, nmine << lgr};
-  u32x4 *stage = lds;                                                    // [64][PITCH]
-  uint16_t *rb = reinterpret_cast<uint16_t *>(stage + kRows * PITCH);    // [32][kRBP]
-  float2 *twh = reinterpret_cast<float2 *>(rb + 32 * kRBP);              // [H]
-  int *rsig = reinterpret_cast<int *>(twh + s.H);                        // [64]
-  int *mxs = rsig + kRows;                                               // [2][4]
+  u32x4 *stage = lds;                                                         // [NP][64][PITCH]
+  uint16_t *rb = reinterpret_cast<uint16_t *>(stage + NP * kRows * PITCH);    // [NP][32][kRBP]
+  float2 *twh = reinterpret_cast<float2 *>(rb + NP * 32 * kRBP);              // [H]
+  int *rsig = reinterpret_cast<int *>(twh + s.H);                             // [64]
+  int *mxs = rsig + kRows;                                                    // [2][4]
   for (int v = tid; v < s.H; v += kFT) twh[v] = a.tw_h[v];
 
-  // row twiddles (A operand) of this wave's c-tiles; column twiddles of its m-tiles
+  FwdRegs<DT, KB, TWO, MPW> R;
   const int G = s.NT == 4 ? 2 : 1;
-  u32x4 th[TWO ? 2 : 1][KB];
 #pragma unroll
   for (int t = 0; t < (TWO ? 2 : 1); ++t) {
     const int ct = min((wv % G) * 2 + t, s.NT - 1);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) th[t][kb] = reinterpret_cast<const u32x4 *>(a.tf)[((size_t)ct * KB + kb) * 64 + lane];
+    for (int q = 0; q < NP; ++q)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        R.th[t][q][kb] = reinterpret_cast<const u32x4 *>(q ? a.tf_lo : a.tf)[((size_t)ct * KB + kb) * 64 + lane];
   }
-  u32x4 ef[2][4];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-    const int mt = min(2 * wv + mi, s.MT - 1);
+  for (int mi = 0; mi < MPW; ++mi) {
+    const int mt = min(MPW * wv + mi, s.MT - 1);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) ef[mi][kb] = reinterpret_cast<const u32x4 *>(a.ef)[((size_t)mt * 4 + kb) * 64 + lane];
+    for (int q = 0; q < NP; ++q)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        R.ef[mi][q][kb] = reinterpret_cast<const u32x4 *>(q ? a.ef_lo : a.ef)[((size_t)mt * 4 + kb) * 64 + lane];
   }
 
-  float2 X[2][2][2];
+  float2 X[MPW][2][2];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < MPW; ++mi)
 #pragma unroll
     for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
       for (int t = 0; t < 2; ++t) X[mi][nn][t] = make_float2(0.f, 0.f);
 
-  const uint16_t *x = reinterpret_cast<const uint16_t *>(a.x);
-  u32x4 pa[KB];
-  if (s.total > 0) fwd_fetch<KB>(x, 0, lgr, s.H, tid, pa);
+  u32x4 pa[KB * P::ES / 2];
+  if (s.total > 0) fwd_fetch<DT, KB>(a.x, 0, lgr, s.H, tid, pa);
   __syncthreads();
-  for (int g = 0; g < s.total; ++g) fwd_round<DT, KB, TWO>(g, s, pa, a, stage, rb, twh, rsig, mxs, th, ef, X);
+  for (int g = 0; g < s.total; ++g) fwd_round<DT, KB, TWO, MPW>(g, s, pa, a, stage, rb, twh, rsig, mxs, R, X);
 }
 
 // ------------------------------------------------------------------ inverse
@@ -334,47 +431,57 @@ __device__ __forceinline__ void inv_load(const float2 *in, size_t plane, int K, 
 //     register-held A operand, so each lane holds four consecutive outputs
 //     of a row; unscaled, rounded to the storage dtype into the out stage;
 //  4. coalesced 16-byte stores of the 64 rows.
+// fp32 planes carry the spectra, Z and the twiddles as fp16 hi + lo.
 template <int DT, int KB>
 __global__ __launch_bounds__(kFT) void fno_inv_plane_mx(PlaneMxInvArgs a) {
-  constexpr int W = 32 * KB, WU = 4 * KB, PITCH = WU + 1;
-  constexpr int NTW = W / 16;   // output column tiles
-  constexpr int NPW = NTW / 4;  // column tiles per wave
-  constexpr int NY = 8;         // spectra values per thread (K <= 2048)
+  using P = MxPol<DT>;
+  constexpr bool SP = P::SP;
+  constexpr int NP = P::NP;
+  constexpr int W = 32 * KB;
+  constexpr int UR = W * P::ES / 16, OP = UR + 1;  // 16-byte units per output row, stage pitch
+  constexpr int FU = KB * P::ES / 2;               // 16-byte output units per thread and round
+  constexpr int NTW = W / 16;                      // output column tiles
+  constexpr int NPW = NTW / 4;                     // column tiles per wave
+  constexpr int NY = 8;                            // spectra values per thread (K <= 2048)
+  constexpr int YBS = 32 * kRBP, ZBS = kRows * kZBP;  // halves per part
   extern __shared__ u32x4 lds[];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, m1 = a.m1, m2 = a.m2, NN = a.nn, KB1 = a.kb1;
   const int K = 2 * m1 * m2;
   const int nmine = (a.nplanes - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-  u32x4 *ostage = lds;                                                      // [64][PITCH]
-  uint16_t *yb = reinterpret_cast<uint16_t *>(ostage + kRows * PITCH);      // [32][kRBP]
-  uint16_t *zb = yb + 32 * kRBP;                                            // [64][kZBP]
-  float2 *twh = reinterpret_cast<float2 *>(zb + kRows * kZBP);              // [H]
+  u32x4 *ostage = lds;                                                      // [64][OP]
+  uint16_t *yb = reinterpret_cast<uint16_t *>(ostage + kRows * OP);         // [NP][32][kRBP]
+  uint16_t *zb = yb + NP * YBS;                                             // [NP][64][kZBP]
+  float2 *twh = reinterpret_cast<float2 *>(zb + NP * ZBS);                  // [H]
   float *ymx = reinterpret_cast<float *>(twh + H);                          // [2][4]
 
   float2 yv[NY], yn[NY];
   if (nmine > 0) inv_load<NY>(a.in, blockIdx.x, K, tid, yv);
-  for (int v = tid; v < 32 * kRBP / 2; v += kFT) reinterpret_cast<uint32_t *>(yb)[v] = 0u;
+  for (int v = tid; v < NP * YBS / 2; v += kFT) reinterpret_cast<uint32_t *>(yb)[v] = 0u;
   for (int v = tid; v < H; v += kFT) twh[v] = a.tw_h[v];
 
   // E' fragments of m-tiles 2 wv, 2 wv + 1 (rows j = 16 wv .. 16 wv + 15)
-  u32x4 ef[2][4];
+  u32x4 ef[2][4][NP];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const u32x4 t =
-          reinterpret_cast<const u32x4 *>(a.ef)[((size_t)(2 * wv + mi) * KB1 + (kb < KB1 ? kb : 0)) * 64 + lane];
-      ef[mi][kb] = kb < KB1 ? t : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int q = 0; q < NP; ++q) {
+        const u32x4 t = reinterpret_cast<const u32x4 *>(q ? a.ef_lo : a.ef)[((size_t)(2 * wv + mi) * KB1 + (kb < KB1 ? kb : 0)) * 64 + lane];
+        ef[mi][kb][q] = kb < KB1 ? t : u32x4{0u, 0u, 0u, 0u};
+      }
   // T' fragments (A operand) of output column tiles wv, wv + 4, ...
-  u32x4 tb[NPW][2];
+  u32x4 tb[NPW][2][NP];
 #pragma unroll
   for (int i = 0; i < NPW; ++i)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const u32x4 t = reinterpret_cast<const u32x4 *>(a.tb)[((size_t)(wv + 4 * i) * NN + (kb < NN ? kb : 0)) * 64 + lane];
-      tb[i][kb] = kb < NN ? t : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int q = 0; q < NP; ++q) {
+        const u32x4 t = reinterpret_cast<const u32x4 *>(q ? a.tb_lo : a.tb)[((size_t)(wv + 4 * i) * NN + (kb < NN ? kb : 0)) * 64 + lane];
+        tb[i][kb][q] = kb < NN ? t : u32x4{0u, 0u, 0u, 0u};
+      }
 
   const int rounds = H / kRows;
   for (int pi = 0; pi < nmine; ++pi) {
@@ -396,7 +503,7 @@ __global__ __launch_bounds__(kFT) void fno_inv_plane_mx(PlaneMxInvArgs a) {
     const int se = ym > 0.f ? max(-120, min(120, 15 - e - a.lg4m1)) : 0;
     const float sc = pow2f(se), isc = pow2f(-se);
 
-    uint4 *yp = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.y) + plane * H * W);
+    u32x4 *yp = reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(a.y) + plane * H * W * P::ES);
     for (int r = 0; r < rounds; ++r) {
       // 1. spectra of the round: Y[q][ky] e^{+2 pi i kx(q) h0 / H}, scaled, fp16
 #pragma unroll
@@ -408,7 +515,10 @@ __global__ __launch_bounds__(kFT) void fno_inv_plane_mx(PlaneMxInvArgs a) {
           const float2 w = twh[(kx * kRows * r) & (H - 1)];  // e^{-i theta}
           const float zr = (yv[i].x * w.x + yv[i].y * w.y) * sc;
           const float zi = (yv[i].y * w.x - yv[i].x * w.y) * sc;
-          reinterpret_cast<uint32_t *>(yb + ky * kRBP)[q] = h16x2(zr, zi);
+          uint32_t hi, lo;
+          split2(zr, zi, hi, lo);
+          reinterpret_cast<uint32_t *>(yb + ky * kRBP)[q] = hi;
+          if constexpr (SP) reinterpret_cast<uint32_t *>(yb + YBS + ky * kRBP)[q] = lo;
         }
       }
       __syncthreads();
@@ -418,62 +528,81 @@ __global__ __launch_bounds__(kFT) void fno_inv_plane_mx(PlaneMxInvArgs a) {
       for (int nn = 0; nn < 2; ++nn) {
         if (nn < NN) {
           const u32x4 *br = reinterpret_cast<const u32x4 *>(yb + (nn * 16 + (lane & 15)) * kRBP) + (lane >> 4);
-          u32x4 bv[4];
+          u32x4 bv[4][2];
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb) bv[kb] = br[(kb < KB1 ? kb : 0) * 4];
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) bv[kb][q] = q < NP ? br[q * (YBS / 8) + (kb < KB1 ? kb : 0) * 4] : bv[kb][0];
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int mi = 0; mi < 2; ++mi) {
             v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
-              if (kb < KB1) acc = mma(ef[mi][kb], bv[kb], acc);
+              if (kb < KB1) {
+                const u32x4 e2[2] = {ef[mi][kb][0], ef[mi][kb][NP - 1]};
+                acc = mma_sp(e2, bv[kb], acc, SP);
+              }
             const int j0 = 8 * (2 * wv + mi) + 2 * (lane >> 4), ky = nn * 16 + (lane & 15);
-            reinterpret_cast<uint32_t *>(zb + j0 * kZBP)[ky] = h16x2(acc[0], acc[1]);
-            reinterpret_cast<uint32_t *>(zb + (j0 + 1) * kZBP)[ky] = h16x2(acc[2], acc[3]);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+              uint32_t hi, lo;
+              split2(acc[2 * jj], acc[2 * jj + 1], hi, lo);
+              reinterpret_cast<uint32_t *>(zb + (j0 + jj) * kZBP)[ky] = hi;
+              if constexpr (SP) reinterpret_cast<uint32_t *>(zb + ZBS + (j0 + jj) * kZBP)[ky] = lo;
+            }
           }
         }
       }
       __syncthreads();
 
       // 3. y^T = T'^T Z^T: lane gets y[h][w .. w + 3], h = 16 mt + l % 16
-      uint16_t *os = reinterpret_cast<uint16_t *>(ostage);
-      u32x4 bz[4][2];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const u32x4 *zr = reinterpret_cast<const u32x4 *>(zb + (mt * 16 + (lane & 15)) * kZBP) + (lane >> 4);
-        bz[mt][0] = zr[0];
-        bz[mt][1] = zr[NN > 1 ? 4 : 0];
-      }
-      __builtin_amdgcn_sched_barrier(0);
+        u32x4 bz[2][2];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) bz[kb][q] = q < NP ? zr[q * (ZBS / 8) + (NN > 1 ? kb : 0) * 4] : bz[kb][0];
+        __builtin_amdgcn_sched_barrier(0);
         const int h = mt * 16 + (lane & 15);
 #pragma unroll
         for (int i = 0; i < NPW; ++i) {
           v4f acc = {0.f, 0.f, 0.f, 0.f};
-          acc = mma(tb[i][0], bz[mt][0], acc);
-          if (NN > 1) acc = mma(tb[i][1], bz[mt][1], acc);
-          const int w = (wv + 4 * i) * 16 + 4 * (lane >> 4);
-          uint2 o;
-          if constexpr (DT == DT_F16) {
-            o.x = h16x2(acc[0] * isc, acc[1] * isc);
-            o.y = h16x2(acc[2] * isc, acc[3] * isc);
-          } else {
-            o.x = f32x2_to_bf16x2(acc[0] * isc, acc[1] * isc);
-            o.y = f32x2_to_bf16x2(acc[2] * isc, acc[3] * isc);
+          {
+            const u32x4 t2[2] = {tb[i][0][0], tb[i][0][NP - 1]};
+            acc = mma_sp(t2, bz[0], acc, SP);
           }
-          *reinterpret_cast<uint2 *>(os + h * PITCH * 8 + w) = o;
+          if (NN > 1) {
+            const u32x4 t2[2] = {tb[i][1][0], tb[i][1][NP - 1]};
+            acc = mma_sp(t2, bz[1], acc, SP);
+          }
+          const int w = (wv + 4 * i) * 16 + 4 * (lane >> 4);
+          if constexpr (SP) {
+            ostage[h * OP + w / 4] = u32x4{__float_as_uint(acc[0] * isc), __float_as_uint(acc[1] * isc),
+                                           __float_as_uint(acc[2] * isc), __float_as_uint(acc[3] * isc)};
+          } else {
+            uint2 o;
+            if constexpr (DT == DT_F16) {
+              o.x = h16x2(acc[0] * isc, acc[1] * isc);
+              o.y = h16x2(acc[2] * isc, acc[3] * isc);
+            } else {
+              o.x = f32x2_to_bf16x2(acc[0] * isc, acc[1] * isc);
+              o.y = f32x2_to_bf16x2(acc[2] * isc, acc[3] * isc);
+            }
+            reinterpret_cast<uint2 *>(ostage + h * OP)[w / 4] = o;
+          }
         }
       }
       __syncthreads();
 
-      // 4. 64 rows x W halves: coalesced 16-byte stores
+      // 4. 64 rows x W elements: coalesced 16-byte stores
 #pragma unroll
-      for (int v = 0; v < KB; ++v) {
+      for (int v = 0; v < FU; ++v) {
         const int e2 = v * kFT + tid;
-        const int row = e2 / WU, cu = e2 - row * WU;
-        yp[(size_t)r * kRows * WU + e2] = reinterpret_cast<const uint4 *>(ostage)[row * PITCH + cu];
+        const int row = e2 / UR, cu = e2 - row * UR;
+        yp[(size_t)r * kRows * UR + e2] = ostage[row * OP + cu];
       }
     }
 #pragma unroll
@@ -484,54 +613,67 @@ __global__ __launch_bounds__(kFT) void fno_inv_plane_mx(PlaneMxInvArgs a) {
 // --------------------------------------------------------------- launchers
 
 bool mx_supported(int H, int W, int m1, int m2, int dtype) {
-  return (dtype == DT_F16 || dtype == DT_BF16) && H >= kRows && H <= 256 && W >= 64 && W <= 256 && m1 <= 32 &&
-         m2 <= 32 && 2 * m1 <= H;
+  // fp32 carries hi + lo twiddle parts in registers: narrower planes, fewer modes
+  const int wmax = dtype == DT_F32 ? 128 : 256, m1max = dtype == DT_F32 ? 16 : 32;
+  return (dtype == DT_F16 || dtype == DT_BF16 || dtype == DT_F32) && H >= kRows && H <= 256 && W >= 64 &&
+         W <= wmax && m1 <= m1max && m2 <= 32 && 2 * m1 <= H;
 }
 
 int mx_ntiles(int m2) { return m2 <= 8 ? 1 : m2 <= 16 ? 2 : 4; }
 
-size_t mx_fwd_lds_bytes(int H, int W) {
-  return (size_t)kRows * (W / 8 + 1) * 16 + (size_t)32 * kRBP * 2 + (size_t)H * 8 + (size_t)(kRows + 8) * 4;
+size_t mx_fwd_lds_bytes(int H, int W, int dtype) {
+  const size_t np = dtype == DT_F32 ? 2 : 1;
+  return np * kRows * (W / 8 + 1) * 16 + np * 32 * kRBP * 2 + (size_t)H * 8 + (size_t)(kRows + 8) * 4;
 }
 
-size_t mx_inv_lds_bytes(int H, int W) {
-  return (size_t)kRows * (W / 8 + 1) * 16 + (size_t)32 * kRBP * 2 + (size_t)kRows * kZBP * 2 + (size_t)H * 8 + 64;
+size_t mx_inv_lds_bytes(int H, int W, int dtype) {
+  const size_t np = dtype == DT_F32 ? 2 : 1, es = dtype == DT_F32 ? 4 : 2;
+  return (size_t)kRows * (W * es / 16 + 1) * 16 + np * (32 * kRBP + (size_t)kRows * kZBP) * 2 + (size_t)H * 8 + 64;
 }
 
 template <int DT, int KB>
-static const void *mx_kernel_kb(bool fwd, bool two) {
+static const void *mx_kernel_kb(bool fwd, bool two, bool m2pw) {
   if (!fwd) return (const void *)fno_inv_plane_mx<DT, KB>;
-  return two ? (const void *)fno_fwd_plane_mx<DT, KB, true> : (const void *)fno_fwd_plane_mx<DT, KB, false>;
+  if constexpr (DT == DT_F32) {
+    if (m2pw) return nullptr;  // fp32 plans keep m1 <= 16
+  } else if (m2pw) {
+    return two ? (const void *)fno_fwd_plane_mx<DT, KB, true, 2> : (const void *)fno_fwd_plane_mx<DT, KB, false, 2>;
+  }
+  return two ? (const void *)fno_fwd_plane_mx<DT, KB, true, 1> : (const void *)fno_fwd_plane_mx<DT, KB, false, 1>;
 }
 
 template <int DT>
-static const void *mx_kernel_dt(bool fwd, int W, bool two) {
+static const void *mx_kernel_dt(bool fwd, int W, bool two, bool m2pw) {
   switch (W) {
-    case 64: return mx_kernel_kb<DT, 2>(fwd, two);
-    case 128: return mx_kernel_kb<DT, 4>(fwd, two);
-    case 256: return mx_kernel_kb<DT, 8>(fwd, two);
+    case 64: return mx_kernel_kb<DT, 2>(fwd, two, m2pw);
+    case 128: return mx_kernel_kb<DT, 4>(fwd, two, m2pw);
+    case 256:
+      if constexpr (DT == DT_F32) return nullptr;
+      else return mx_kernel_kb<DT, 8>(fwd, two, m2pw);
   }
   return nullptr;
 }
 
-// m2 > 8: R has two or four 16-column tiles
-static const void *mx_kernel(bool fwd, int W, int m2, int dtype) {
-  const bool two = m2 > 8;
-  if (dtype == DT_F16) return mx_kernel_dt<DT_F16>(fwd, W, two);
-  if (dtype == DT_BF16) return mx_kernel_dt<DT_BF16>(fwd, W, two);
+// m2 > 8: R has two or four 16-column tiles; m1 > 16: more than four
+// m-tiles of modes, two per wave
+static const void *mx_kernel(bool fwd, int W, int m1, int m2, int dtype) {
+  const bool two = m2 > 8, m2pw = m1 > 16;
+  if (dtype == DT_F16) return mx_kernel_dt<DT_F16>(fwd, W, two, m2pw);
+  if (dtype == DT_BF16) return mx_kernel_dt<DT_BF16>(fwd, W, two, m2pw);
+  if (dtype == DT_F32) return mx_kernel_dt<DT_F32>(fwd, W, two, m2pw);
   return nullptr;
 }
 
-hipError_t mx_prepare(bool fwd, int W, int m2, int dtype, size_t lds) {
-  const void *k = mx_kernel(fwd, W, m2, dtype);
+hipError_t mx_prepare(bool fwd, int W, int m1, int m2, int dtype, size_t lds) {
+  const void *k = mx_kernel(fwd, W, m1, m2, dtype);
   if (!k) return hipErrorInvalidValue;
   return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
 // workgroups of a persistent plane kernel: as many as are resident at once
 // on the device (never more than planes)
-hipError_t mx_grid(bool fwd, int W, int m2, int dtype, size_t lds, int device, int nplanes, int *grid) {
-  const void *k = mx_kernel(fwd, W, m2, dtype);
+hipError_t mx_grid(bool fwd, int W, int m1, int m2, int dtype, size_t lds, int device, int nplanes, int *grid) {
+  const void *k = mx_kernel(fwd, W, m1, m2, dtype);
   if (!k) return hipErrorInvalidValue;
   int per_cu = 0, ncu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kFT, lds);
@@ -543,14 +685,14 @@ hipError_t mx_grid(bool fwd, int W, int m2, int dtype, size_t lds, int device, i
 }
 
 hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int grid, int dtype, size_t lds, hipStream_t s) {
-  const void *k = mx_kernel(true, a.W, a.m2, dtype);
+  const void *k = mx_kernel(true, a.W, a.m1, a.m2, dtype);
   if (!k || grid < 1) return hipErrorInvalidValue;
   void *args[] = {(void *)&a};
   return hipLaunchKernel(k, dim3(grid), dim3(kFT), args, lds, s);
 }
 
 hipError_t launch_plane_mx_inv(const PlaneMxInvArgs &a, int grid, int dtype, size_t lds, hipStream_t s) {
-  const void *k = mx_kernel(false, a.W, a.m2, dtype);
+  const void *k = mx_kernel(false, a.W, a.m1, a.m2, dtype);
   if (!k || grid < 1) return hipErrorInvalidValue;
   void *args[] = {(void *)&a};
   return hipLaunchKernel(k, dim3(grid), dim3(kFT), args, lds, s);
