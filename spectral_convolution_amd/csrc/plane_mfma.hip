@@ -117,6 +117,39 @@ __device__ __forceinline__ v4f mma_sp(const u32x4 (&a)[2], const u32x4 (&b)[2], 
   return c;
 }
 
+// Accumulator chains: a dependent MFMA waits for its predecessor's result,
+// so products are spread over independent accumulators (hi*hi and the two
+// cross terms apart; with KS, even and odd K blocks apart) and summed at the
+// end.
+template <bool KS>
+struct AccN {
+  v4f c[2][KS ? 2 : 1];  // [cross terms][odd block]
+  __device__ __forceinline__ AccN() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < (KS ? 2 : 1); ++j) c[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ void add(const u32x4 (&a)[2], const u32x4 (&b)[2], int kb, bool sp) {
+    const int j = KS ? (kb & 1) : 0;
+    c[0][j] = mma(a[0], b[0], c[0][j]);
+    if (sp) {
+      c[1][j] = mma(a[0], b[1], c[1][j]);
+      c[1][j] = mma(a[1], b[0], c[1][j]);
+    }
+  }
+  __device__ __forceinline__ v4f sum(bool sp) const {
+    v4f r = c[0][0];
+    if (KS) r += c[0][KS ? 1 : 0];
+    if (sp) {
+      r += c[1][0];
+      if (KS) r += c[1][KS ? 1 : 0];
+    }
+    return r;
+  }
+};
+using Acc4 = AccN<true>;
+
 // fp32 -> fp16 hi, fp16 lo = fp16(v - hi), packed for two values
 __device__ __forceinline__ void split2(float v0, float v1, uint32_t &hi, uint32_t &lo) {
   const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
@@ -124,18 +157,26 @@ __device__ __forceinline__ void split2(float v0, float v1, uint32_t &hi, uint32_
   lo = h16x2(v0 - (float)h0, v1 - (float)h1);
 }
 
+constexpr int kFW = 512;  // threads per workgroup of the forward kernel (8 waves)
+constexpr int kPF = 3;    // rounds in flight per workgroup (register ring)
+
 // rows of global round g of this workgroup: plane blockIdx.x + (g >> lgr)
 // * gridDim.x, rows 64 (g mod 2^lgr) .. +63; FU 16-byte units per thread
 template <int DT, int KB>
-__device__ __forceinline__ void fwd_fetch(const void *x, int g, int lgr, int H, int tid,
-                                          u32x4 (&p)[KB * MxPol<DT>::ES / 2]) {
-  constexpr int W = 32 * KB, UR = W * MxPol<DT>::ES / 16;  // 16-byte units per row
+struct FwdIO {
+  static constexpr int W = 32 * KB, UR = W * MxPol<DT>::ES / 16;  // 16-byte units per row
+  static constexpr int FU = kRows * UR / kFW;                      // units per thread and round
+};
+
+template <int DT, int KB>
+__device__ __forceinline__ void fwd_fetch(const void *x, int g, int lgr, int H, int tid, u32x4 (&p)[FwdIO<DT, KB>::FU]) {
+  using IO = FwdIO<DT, KB>;
   const size_t plane = (size_t)blockIdx.x + (size_t)(g >> lgr) * gridDim.x;
   const int r = g & ((1 << lgr) - 1);
-  const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(x) + plane * H * W * MxPol<DT>::ES) +
-                     (size_t)r * kRows * UR + tid;
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(x) + plane * H * IO::W * MxPol<DT>::ES) +
+                     (size_t)r * kRows * IO::UR + tid;
 #pragma unroll
-  for (int v = 0; v < KB * MxPol<DT>::ES / 2; ++v) p[v] = src[v * kFT];
+  for (int v = 0; v < IO::FU; ++v) p[v] = src[v * kFW];
 }
 
 // eight bf16 -> eight fp16 times 2^sig (exact while the result is normal)
@@ -153,47 +194,58 @@ struct FwdShape {
   int H, m1, m2, NT, MT, NN, lgW, lgr, total;  // lgr: log2 rounds per plane; total: rounds of this workgroup
 };
 
-template <int DT, int KB, bool TWO, int MPW>
+template <int DT, int KB, bool TWO>
 struct FwdRegs {
   static constexpr int NP = MxPol<DT>::NP;
   u32x4 th[TWO ? 2 : 1][NP][KB];  // row twiddles (A operand) of this wave's c-tiles
-  u32x4 ef[MPW][NP][4];           // column twiddles (A operand) of this wave's m-tiles
+  u32x4 ef[NP][4];                // column twiddles (A operand) of this wave's m-tile
 };
 
-// One round of 64 rows:
-//  1. stage the rows in LDS as fp16 (bf16 and fp32 rows scaled by a power of
-//     two per row into fp16 range; fp32 as hi + lo), note the largest
-//     exponent of the round;
-//  2. row product, transposed: R^T[c][h] = sum_w T[w][c] x[h][w] with the
-//     twiddles as the register-held A operand (two 16-column tiles of R per
-//     wave) and x as B, so each staged fragment feeds two products; R is
-//     scaled by a power of two (undone in 3) and stored as fp16 pairs;
-//  3. column product of R against the 64-row twiddle block (two m-tiles of
-//     modes per wave), phase-shifted by the round offset into X.
-template <int DT, int KB, bool TWO, int MPW>
-__device__ __forceinline__ void fwd_round(int g, const FwdShape &s, u32x4 (&p)[KB * MxPol<DT>::ES / 2],
-                                          const PlaneMxFwdArgs &a, u32x4 *stage, uint16_t *rb, const float2 *twh,
-                                          int *rsig, int *mxs, const FwdRegs<DT, KB, TWO, MPW> &R,
-                                          float2 (&X)[MPW][2][2]) {
+// LDS of the forward kernel: two buffers of each per-round stage, so that
+// one barrier per round suffices (round g writes buffer g & 1 while round
+// g - 1's buffer is still being read)
+template <int DT, int KB>
+struct FwdLds {
+  static constexpr int NP = MxPol<DT>::NP;
+  static constexpr int PITCH = 4 * KB + 1;       // staged row: W halves + pad, in 16-byte units
+  static constexpr int STG = kRows * PITCH;      // units per stage part
+  static constexpr int RBS = 32 * kRBP;          // halves per R part
+  u32x4 *stage;   // [2][NP][64][PITCH]
+  uint16_t *rb;   // [2][NP][32][kRBP]
+  float2 *twh;    // [H]
+  int *rsig;      // [2][64] per-row scale exponents
+  int *mxs;       // [2][8] per-wave largest exponents
+  __device__ __forceinline__ FwdLds(u32x4 *lds, int H) {
+    stage = lds;
+    rb = reinterpret_cast<uint16_t *>(stage + 2 * NP * STG);
+    twh = reinterpret_cast<float2 *>(rb + 2 * NP * RBS);
+    rsig = reinterpret_cast<int *>(twh + H);
+    mxs = rsig + 2 * kRows;
+  }
+};
+
+// 1. stage the rows of round g in LDS buffer g & 1 as fp16 (bf16 and fp32
+//    rows scaled by a power of two per row into fp16 range; fp32 as hi + lo)
+//    and record the round's largest exponent; then reuse the registers for
+//    round g + kPF.
+template <int DT, int KB>
+__device__ __forceinline__ void fwd_put(int g, const FwdShape &s, u32x4 (&p)[FwdIO<DT, KB>::FU],
+                                        const PlaneMxFwdArgs &a, const FwdLds<DT, KB> &L) {
   using P = MxPol<DT>;
   constexpr bool BF = DT == DT_BF16, SP = P::SP;
-  constexpr int NP = P::NP;
-  constexpr int W = 32 * KB, WU = 4 * KB, PITCH = WU + 1;  // stage row: W halves, PITCH 16-byte units
-  constexpr int UR = W * P::ES / 16, FU = KB * P::ES / 2;
-  constexpr int STG = kRows * PITCH;                         // units per stage part
-  constexpr int RBS = 32 * kRBP;                             // halves per R part
+  constexpr int PITCH = FwdLds<DT, KB>::PITCH, STG = FwdLds<DT, KB>::STG;
+  constexpr int UR = FwdIO<DT, KB>::UR, FU = FwdIO<DT, KB>::FU;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int r = g & ((1 << s.lgr) - 1);
-
+  u32x4 *stage = L.stage + (g & 1) * P::NP * STG;
+  int *rsig = L.rsig + (g & 1) * kRows;
   int emax = -1000;
   u16x2 mrun = {0, 0};
 #pragma unroll
   for (int v = 0; v < FU; ++v) {
-    const int e = v * kFT + tid;
+    const int e = v * kFW + tid;
     const int row = e / UR, cu = e - row * UR;
     const u32x4 d = p[v];
     if constexpr (SP) {
-      // four fp32 of the row: scale by the row's power of two, split
       uint32_t m = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) m = max(m, d[i] & 0x7fffffffu);
@@ -205,10 +257,8 @@ __device__ __forceinline__ void fwd_round(int g, const FwdShape &s, u32x4 (&p)[K
       uint32_t h0, l0, h1, l1;
       split2(__uint_as_float(d[0]) * sc, __uint_as_float(d[1]) * sc, h0, l0);
       split2(__uint_as_float(d[2]) * sc, __uint_as_float(d[3]) * sc, h1, l1);
-      uint2 *hp = reinterpret_cast<uint2 *>(stage + row * PITCH) + cu;
-      uint2 *lp = reinterpret_cast<uint2 *>(stage + STG + row * PITCH) + cu;
-      *hp = make_uint2(h0, h1);
-      *lp = make_uint2(l0, l1);
+      reinterpret_cast<uint2 *>(stage + row * PITCH)[cu] = make_uint2(h0, h1);
+      reinterpret_cast<uint2 *>(stage + STG + row * PITCH)[cu] = make_uint2(l0, l1);
       if ((tid & (UR - 1)) == 0) rsig[row] = m ? sig : 0;
       emax = max(emax, m ? eh : -1000);
     } else if constexpr (BF) {
@@ -231,148 +281,191 @@ __device__ __forceinline__ void fwd_round(int g, const FwdShape &s, u32x4 (&p)[K
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) emax = max(emax, __shfl_xor(emax, o, 64));
-  if (lane == 0) mxs[(g & 1) * 4 + wv] = emax;
-  if (g + 1 < s.total) fwd_fetch<DT, KB>(a.x, g + 1, s.lgr, s.H, tid, p);
-  __syncthreads();
+  if (lane == 0) L.mxs[(g & 1) * 8 + wv] = emax;
+  if (g + kPF < s.total) fwd_fetch<DT, KB>(a.x, g + kPF, s.lgr, s.H, tid, p);
+}
 
-  // |R| <= W max|x| < 2^(emax + lgW): R * 2^(15 - emax - lgW) < 2^15
+// round g's R scale exponent: |R| <= W max|x| < 2^(emax + lgW), so
+// R 2^se < 2^15
+template <int DT, int KB>
+__device__ __forceinline__ int fwd_scale(int g, const FwdShape &s, const FwdLds<DT, KB> &L) {
   int er = -1000;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) er = max(er, mxs[(g & 1) * 4 + i]);
-  const int se = er > -1000 ? max(-120, min(120, 15 - er - s.lgW)) : 0;
-  const float isc = pow2f(-se);
+  for (int i = 0; i < 8; ++i) er = max(er, L.mxs[(g & 1) * 8 + i]);
+  return er > -1000 ? max(-120, min(120, 15 - er - s.lgW)) : 0;
+}
 
-  // row product: c-tiles ct0 (, ct0 + 1) x stripes of this wave; all
-  // fragments of a stripe are read before its products are issued
-  {
-    const int G = s.NT == 4 ? 2 : 1;
-    const int ct0 = (wv % G) * 2;
-    for (int st = wv / G; st < 4; st += 4 / G) {
-      const u32x4 *br = stage + (st * 16 + (lane & 15)) * PITCH + (lane >> 4);
-      // fragments are read in groups of KG blocks ahead of their products
-      constexpr int KG = SP && KB > 2 ? 2 : KB;
-      v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+// 2. row product of round g, transposed: R^T[c][h] = sum_w T[w][c] x[h][w]
+//    with the twiddles as the register-held A operand (two 16-column tiles
+//    of R per wave) and the staged rows as B; R scaled by 2^se (undone in
+//    fwd_col) into fp16 pairs of LDS buffer g & 1.
+template <int DT, int KB, bool TWO>
+__device__ __forceinline__ void fwd_row(int g, int se, const FwdShape &s, const FwdLds<DT, KB> &L,
+                                        const FwdRegs<DT, KB, TWO> &R) {
+  using P = MxPol<DT>;
+  constexpr bool BF = DT == DT_BF16, SP = P::SP;
+  constexpr int NP = P::NP;
+  constexpr int PITCH = FwdLds<DT, KB>::PITCH, STG = FwdLds<DT, KB>::STG, RBS = FwdLds<DT, KB>::RBS;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const u32x4 *stage = L.stage + (g & 1) * NP * STG;
+  const int *rsig = L.rsig + (g & 1) * kRows;
+  uint16_t *rb = L.rb + (g & 1) * NP * RBS;
+  const int G = s.NT == 4 ? 2 : 1;
+  const int ct0 = (wv % G) * 2;
+  // fragments are read in groups of KG blocks ahead of their products
+  constexpr int KG = SP && KB > 2 ? 2 : KB;
+  for (int st = wv / G; st < 4; st += 8 / G) {
+    const u32x4 *br = stage + (st * 16 + (lane & 15)) * PITCH + (lane >> 4);
+    Acc4 a0, a1;
 #pragma unroll
-      for (int k0 = 0; k0 < KB; k0 += KG) {
-        u32x4 bv[KG][2];
+    for (int k0 = 0; k0 < KB; k0 += KG) {
+      u32x4 bv[KG][2];
 #pragma unroll
-        for (int kb = 0; kb < KG; ++kb)
+      for (int kb = 0; kb < KG; ++kb)
 #pragma unroll
-          for (int q = 0; q < 2; ++q) bv[kb][q] = q < NP ? br[q * STG + (k0 + kb) * 4] : bv[kb][0];
-        __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < 2; ++q) bv[kb][q] = q < NP ? br[q * STG + (k0 + kb) * 4] : bv[kb][0];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kb = 0; kb < KG; ++kb) {
-          const u32x4 t0[2] = {R.th[0][0][k0 + kb], R.th[0][NP - 1][k0 + kb]};
-          acc0 = mma_sp(t0, bv[kb], acc0, SP);
-          if constexpr (TWO) {
-            const u32x4 t1[2] = {R.th[1][0][k0 + kb], R.th[1][NP - 1][k0 + kb]};
-            acc1 = mma_sp(t1, bv[kb], acc1, SP);
-          }
-        }
-      }
-      const int h = st * 16 + (lane & 15);
-      const float f = (BF || SP) ? pow2f(se - rsig[h]) : pow2f(se);
-      uint32_t *col = reinterpret_cast<uint32_t *>(rb) + h;
-#pragma unroll
-      for (int t = 0; t < (TWO ? 2 : 1); ++t) {
-        const v4f &acc = t == 0 ? acc0 : acc1;
-        const int ky0 = 8 * (ct0 + t) + 2 * (lane >> 4);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if (ky0 + j < s.m2) {
-            uint32_t hi, lo;
-            split2(acc[2 * j] * f, acc[2 * j + 1] * f, hi, lo);
-            col[(ky0 + j) * (kRBP / 2)] = hi;
-            if constexpr (SP) col[RBS / 2 + (ky0 + j) * (kRBP / 2)] = lo;
-          }
+      for (int kb = 0; kb < KG; ++kb) {
+        const u32x4 t0[2] = {R.th[0][0][k0 + kb], R.th[0][NP - 1][k0 + kb]};
+        a0.add(t0, bv[kb], kb, SP);
+        if constexpr (TWO) {
+          const u32x4 t1[2] = {R.th[1][0][k0 + kb], R.th[1][NP - 1][k0 + kb]};
+          a1.add(t1, bv[kb], kb, SP);
         }
       }
     }
-  }
-  __syncthreads();
-
-  // column product: m-tiles MPW wv .. (modes q0, q0 + 1 per lane each)
-  if (MPW * wv < s.MT) {
-    float2 ph[MPW][2];
+    const v4f acc0 = a0.sum(SP), acc1 = TWO ? a1.sum(SP) : acc0;
+    const int h = st * 16 + (lane & 15);
+    const float f = (BF || SP) ? pow2f(se - rsig[h]) : pow2f(se);
+    uint32_t *col = reinterpret_cast<uint32_t *>(rb) + h;
 #pragma unroll
-    for (int mi = 0; mi < MPW; ++mi)
+    for (int t = 0; t < (TWO ? 2 : 1); ++t) {
+      const v4f &acc = t == 0 ? acc0 : acc1;
+      const int ky0 = 8 * (ct0 + t) + 2 * (lane >> 4);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int q = 8 * (MPW * wv + mi) + 2 * (lane >> 4) + t;
-        const int kx = q < s.m1 ? q : s.H - 2 * s.m1 + q;
-        ph[mi][t] = twh[(kx * kRows * r) & (s.H - 1)];
-      }
-#pragma unroll
-    for (int nn = 0; nn < 2; ++nn) {
-      if (nn < s.NN) {
-        const u32x4 *br = reinterpret_cast<const u32x4 *>(rb + (nn * 16 + (lane & 15)) * kRBP) + (lane >> 4);
-        u32x4 bv[4][2];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int q = 0; q < 2; ++q) bv[kb][q] = q < NP ? br[q * (RBS / 8) + kb * 4] : bv[kb][0];
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int mi = 0; mi < MPW; ++mi) {
-          v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            const u32x4 e2[2] = {R.ef[mi][0][kb], R.ef[mi][NP - 1][kb]};
-            acc = mma_sp(e2, bv[kb], acc, SP);
-          }
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const float yr = acc[2 * t] * isc, yi = acc[2 * t + 1] * isc;
-            X[mi][nn][t].x += yr * ph[mi][t].x - yi * ph[mi][t].y;
-            X[mi][nn][t].y += yr * ph[mi][t].y + yi * ph[mi][t].x;
-          }
+      for (int j = 0; j < 2; ++j) {
+        if (ky0 + j < s.m2) {
+          uint32_t hi, lo;
+          split2(acc[2 * j] * f, acc[2 * j + 1] * f, hi, lo);
+          col[(ky0 + j) * (kRBP / 2)] = hi;
+          if constexpr (SP) col[RBS / 2 + (ky0 + j) * (kRBP / 2)] = lo;
         }
       }
-    }
-    // last round of a plane: scale, store the modes, start the next plane
-    if (r == (1 << s.lgr) - 1) {
-      const size_t plane = (size_t)blockIdx.x + (size_t)(g >> s.lgr) * gridDim.x;
-      float2 *op = a.out + plane * (2 * s.m1 * s.m2);
-#pragma unroll
-      for (int mi = 0; mi < MPW; ++mi)
-#pragma unroll
-        for (int nn = 0; nn < 2; ++nn) {
-          const int ky = nn * 16 + (lane & 15);
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int q = 8 * (MPW * wv + mi) + 2 * (lane >> 4) + t;
-            if (nn < s.NN && ky < s.m2 && q < 2 * s.m1)
-              op[q * s.m2 + ky] = make_float2(X[mi][nn][t].x * a.scale, X[mi][nn][t].y * a.scale);
-            X[mi][nn][t] = make_float2(0.f, 0.f);
-          }
-        }
     }
   }
 }
 
-// Persistent: workgroup b transforms planes b, b + gridDim.x, ...; its rounds
-// form one stream, the next one in flight while the current one is
-// multiplied, across plane boundaries. TWO: R has more than one 16-column
-// tile, and each wave computes two of them. MPW: m-tiles of modes per wave
-// (1 for up to 16 kx per corner, else 2).
-template <int DT, int KB, bool TWO, int MPW>
-__global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(2))) void fno_fwd_plane_mx(PlaneMxFwdArgs a) {
+// 3. column product of round g's R against the 64-row twiddle block (m-tile
+//    wv of the modes), phase-shifted by the round offset and unscaled into X;
+//    after the last round of a plane, X is scaled, stored and reset.
+template <int DT, int KB, bool TWO>
+__device__ __forceinline__ void fwd_col(int g, int se, const FwdShape &s, const PlaneMxFwdArgs &a,
+                                        const FwdLds<DT, KB> &L, const FwdRegs<DT, KB, TWO> &R, float2 (&X)[2][2]) {
   using P = MxPol<DT>;
+  constexpr bool SP = P::SP;
   constexpr int NP = P::NP;
-  constexpr int WU = 4 * KB, PITCH = WU + 1;
+  constexpr int RBS = FwdLds<DT, KB>::RBS;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (wv >= s.MT) return;
+  const int r = g & ((1 << s.lgr) - 1);
+  const uint16_t *rb = L.rb + (g & 1) * NP * RBS;
+  const float isc = pow2f(-se);
+  float2 ph[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int q = 8 * wv + 2 * (lane >> 4) + t;
+    const int kx = q < s.m1 ? q : s.H - 2 * s.m1 + q;
+    ph[t] = L.twh[(kx * kRows * r) & (s.H - 1)];
+  }
+  // fragments of NB ky tiles at a time (both for fp16 parts, one for
+  // hi + lo parts), then their products as independent chains
+  constexpr int NB = SP ? 1 : 2;
+#pragma unroll
+  for (int n0 = 0; n0 < 2; n0 += NB) {
+    if (n0 < s.NN) {
+      u32x4 bv[NB][4][2];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int nn = n0 + i < s.NN ? n0 + i : n0;
+        const u32x4 *br = reinterpret_cast<const u32x4 *>(rb + (nn * 16 + (lane & 15)) * kRBP) + (lane >> 4);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) bv[i][kb][q] = q < NP ? br[q * (RBS / 8) + kb * 4] : bv[i][kb][0];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      Acc4 ac[NB];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const u32x4 e2[2] = {R.ef[0][kb], R.ef[NP - 1][kb]};
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+          if (n0 + i < s.NN) ac[i].add(e2, bv[i][kb], kb, SP);
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        if (n0 + i < s.NN) {
+          const v4f acc = ac[i].sum(SP);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const float yr = acc[2 * t] * isc, yi = acc[2 * t + 1] * isc;
+            X[n0 + i][t].x += yr * ph[t].x - yi * ph[t].y;
+            X[n0 + i][t].y += yr * ph[t].y + yi * ph[t].x;
+          }
+        }
+      }
+    }
+  }
+  if (r == (1 << s.lgr) - 1) {
+    const size_t plane = (size_t)blockIdx.x + (size_t)(g >> s.lgr) * gridDim.x;
+    float2 *op = a.out + plane * (2 * s.m1 * s.m2);
+#pragma unroll
+    for (int nn = 0; nn < 2; ++nn) {
+      const int ky = nn * 16 + (lane & 15);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int q = 8 * wv + 2 * (lane >> 4) + t;
+        if (nn < s.NN && ky < s.m2 && q < 2 * s.m1)
+          op[q * s.m2 + ky] = make_float2(X[nn][t].x * a.scale, X[nn][t].y * a.scale);
+        X[nn][t] = make_float2(0.f, 0.f);
+      }
+    }
+  }
+}
+
+// One pipeline step: stage round g, one barrier, then round g's row product
+// and round g - 1's column product (different LDS buffers).
+template <int DT, int KB, bool TWO>
+__device__ __forceinline__ void fwd_step(int g, int &se_prev, const FwdShape &s, u32x4 (&p)[FwdIO<DT, KB>::FU],
+                                         const PlaneMxFwdArgs &a, const FwdLds<DT, KB> &L,
+                                         const FwdRegs<DT, KB, TWO> &R, float2 (&X)[2][2]) {
+  fwd_put<DT, KB>(g, s, p, a, L);
+  __syncthreads();
+  const int se = fwd_scale<DT, KB>(g, s, L);
+  fwd_row<DT, KB, TWO>(g, se, s, L, R);
+  if (g > 0) fwd_col<DT, KB, TWO>(g - 1, se_prev, s, a, L, R, X);
+  se_prev = se;
+}
+
+// Persistent: workgroup b transforms planes b, b + gridDim.x, ...; its rounds
+// form one stream with kPF rounds in flight in a register ring, across plane
+// boundaries. One workgroup of 8 waves per CU. TWO: R has more than one
+// 16-column tile, and each wave computes two of them.
+template <int DT, int KB, bool TWO>
+__global__ __launch_bounds__(kFW) void fno_fwd_plane_mx(PlaneMxFwdArgs a) {
+  using P = MxPol<DT>;
+  using IO = FwdIO<DT, KB>;
+  constexpr int NP = P::NP;
   extern __shared__ u32x4 lds[];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int lgr = a.H == 256 ? 2 : a.H == 128 ? 1 : 0;
   const int nmine = (a.nplanes - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   const FwdShape s{a.H, a.m1, a.m2, a.nt, a.mt, a.nn, a.lgW, lgr, nmine << lgr};
-  u32x4 *stage = lds;                                                         // [NP][64][PITCH]
-  uint16_t *rb = reinterpret_cast<uint16_t *>(stage + NP * kRows * PITCH);    // [NP][32][kRBP]
-  float2 *twh = reinterpret_cast<float2 *>(rb + NP * 32 * kRBP);              // [H]
-  int *rsig = reinterpret_cast<int *>(twh + s.H);                             // [64]
-  int *mxs = rsig + kRows;                                                    // [2][4]
-  for (int v = tid; v < s.H; v += kFT) twh[v] = a.tw_h[v];
+  const FwdLds<DT, KB> L(lds, s.H);
+  for (int v = tid; v < s.H; v += kFW) L.twh[v] = a.tw_h[v];
 
-  FwdRegs<DT, KB, TWO, MPW> R;
+  FwdRegs<DT, KB, TWO> R;
   const int G = s.NT == 4 ? 2 : 1;
 #pragma unroll
   for (int t = 0; t < (TWO ? 2 : 1); ++t) {
@@ -383,28 +476,35 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(2))) void f
       for (int kb = 0; kb < KB; ++kb)
         R.th[t][q][kb] = reinterpret_cast<const u32x4 *>(q ? a.tf_lo : a.tf)[((size_t)ct * KB + kb) * 64 + lane];
   }
-#pragma unroll
-  for (int mi = 0; mi < MPW; ++mi) {
-    const int mt = min(MPW * wv + mi, s.MT - 1);
+  {
+    const int mt = min(wv, s.MT - 1);
 #pragma unroll
     for (int q = 0; q < NP; ++q)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-        R.ef[mi][q][kb] = reinterpret_cast<const u32x4 *>(q ? a.ef_lo : a.ef)[((size_t)mt * 4 + kb) * 64 + lane];
+        R.ef[q][kb] = reinterpret_cast<const u32x4 *>(q ? a.ef_lo : a.ef)[((size_t)mt * 4 + kb) * 64 + lane];
   }
 
-  float2 X[MPW][2][2];
+  float2 X[2][2];
 #pragma unroll
-  for (int mi = 0; mi < MPW; ++mi)
+  for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
-    for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) X[mi][nn][t] = make_float2(0.f, 0.f);
+    for (int t = 0; t < 2; ++t) X[nn][t] = make_float2(0.f, 0.f);
 
-  u32x4 pa[KB * P::ES / 2];
-  if (s.total > 0) fwd_fetch<DT, KB>(a.x, 0, lgr, s.H, tid, pa);
-  __syncthreads();
-  for (int g = 0; g < s.total; ++g) fwd_round<DT, KB, TWO, MPW>(g, s, pa, a, stage, rb, twh, rsig, mxs, R, X);
+  u32x4 p0[IO::FU], p1[IO::FU], p2[IO::FU];
+  if (s.total > 0) fwd_fetch<DT, KB>(a.x, 0, lgr, s.H, tid, p0);
+  if (s.total > 1) fwd_fetch<DT, KB>(a.x, 1, lgr, s.H, tid, p1);
+  if (s.total > 2) fwd_fetch<DT, KB>(a.x, 2, lgr, s.H, tid, p2);
+  int se_prev = 0;
+  for (int g = 0; g < s.total; g += kPF) {
+    fwd_step<DT, KB, TWO>(g, se_prev, s, p0, a, L, R, X);
+    if (g + 1 < s.total) fwd_step<DT, KB, TWO>(g + 1, se_prev, s, p1, a, L, R, X);
+    if (g + 2 < s.total) fwd_step<DT, KB, TWO>(g + 2, se_prev, s, p2, a, L, R, X);
+  }
+  if (s.total > 0) {
+    __syncthreads();
+    fwd_col<DT, KB, TWO>(s.total - 1, se_prev, s, a, L, R, X);
+  }
 }
 
 // ------------------------------------------------------------------ inverse
@@ -433,7 +533,7 @@ __device__ __forceinline__ void inv_load(const float2 *in, size_t plane, int K, 
 //  4. coalesced 16-byte stores of the 64 rows.
 // fp32 planes carry the spectra, Z and the twiddles as fp16 hi + lo.
 template <int DT, int KB>
-__global__ __launch_bounds__(kFT) void fno_inv_plane_mx(PlaneMxInvArgs a) {
+__global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(2))) void fno_inv_plane_mx(PlaneMxInvArgs a) {
   using P = MxPol<DT>;
   constexpr bool SP = P::SP;
   constexpr int NP = P::NP;
@@ -534,15 +634,19 @@ __global__ __launch_bounds__(kFT) void fno_inv_plane_mx(PlaneMxInvArgs a) {
 #pragma unroll
             for (int q = 0; q < 2; ++q) bv[kb][q] = q < NP ? br[q * (YBS / 8) + (kb < KB1 ? kb : 0) * 4] : bv[kb][0];
           __builtin_amdgcn_sched_barrier(0);
+          AccN<!SP> ac[2];
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+            if (kb < KB1) {
+#pragma unroll
+              for (int mi = 0; mi < 2; ++mi) {
+                const u32x4 e2[2] = {ef[mi][kb][0], ef[mi][kb][NP - 1]};
+                ac[mi].add(e2, bv[kb], kb, SP);
+              }
+            }
 #pragma unroll
           for (int mi = 0; mi < 2; ++mi) {
-            v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-              if (kb < KB1) {
-                const u32x4 e2[2] = {ef[mi][kb][0], ef[mi][kb][NP - 1]};
-                acc = mma_sp(e2, bv[kb], acc, SP);
-              }
+            const v4f acc = ac[mi].sum(SP);
             const int j0 = 8 * (2 * wv + mi) + 2 * (lane >> 4), ky = nn * 16 + (lane & 15);
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
@@ -556,42 +660,52 @@ __global__ __launch_bounds__(kFT) void fno_inv_plane_mx(PlaneMxInvArgs a) {
       }
       __syncthreads();
 
-      // 3. y^T = T'^T Z^T: lane gets y[h][w .. w + 3], h = 16 mt + l % 16
+      // 3. y^T = T'^T Z^T: lane gets y[h][w .. w + 3], h = 16 mt + l % 16;
+      // the Z fragments of MB m-tiles are read ahead of their products
+      constexpr int MB = SP ? 1 : 4;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const u32x4 *zr = reinterpret_cast<const u32x4 *>(zb + (mt * 16 + (lane & 15)) * kZBP) + (lane >> 4);
-        u32x4 bz[2][2];
+      for (int m0 = 0; m0 < 4; m0 += MB) {
+        u32x4 bz[MB][2][2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int mi = 0; mi < MB; ++mi) {
+          const u32x4 *zr = reinterpret_cast<const u32x4 *>(zb + ((m0 + mi) * 16 + (lane & 15)) * kZBP) + (lane >> 4);
 #pragma unroll
-          for (int q = 0; q < 2; ++q) bz[kb][q] = q < NP ? zr[q * (ZBS / 8) + (NN > 1 ? kb : 0) * 4] : bz[kb][0];
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) bz[mi][kb][q] = q < NP ? zr[q * (ZBS / 8) + (NN > 1 ? kb : 0) * 4] : bz[mi][kb][0];
+        }
         __builtin_amdgcn_sched_barrier(0);
-        const int h = mt * 16 + (lane & 15);
 #pragma unroll
-        for (int i = 0; i < NPW; ++i) {
-          v4f acc = {0.f, 0.f, 0.f, 0.f};
-          {
-            const u32x4 t2[2] = {tb[i][0][0], tb[i][0][NP - 1]};
-            acc = mma_sp(t2, bz[0], acc, SP);
-          }
-          if (NN > 1) {
-            const u32x4 t2[2] = {tb[i][1][0], tb[i][1][NP - 1]};
-            acc = mma_sp(t2, bz[1], acc, SP);
-          }
-          const int w = (wv + 4 * i) * 16 + 4 * (lane >> 4);
-          if constexpr (SP) {
-            ostage[h * OP + w / 4] = u32x4{__float_as_uint(acc[0] * isc), __float_as_uint(acc[1] * isc),
-                                           __float_as_uint(acc[2] * isc), __float_as_uint(acc[3] * isc)};
-          } else {
-            uint2 o;
-            if constexpr (DT == DT_F16) {
-              o.x = h16x2(acc[0] * isc, acc[1] * isc);
-              o.y = h16x2(acc[2] * isc, acc[3] * isc);
-            } else {
-              o.x = f32x2_to_bf16x2(acc[0] * isc, acc[1] * isc);
-              o.y = f32x2_to_bf16x2(acc[2] * isc, acc[3] * isc);
+        for (int mi = 0; mi < MB; ++mi) {
+          const int h = (m0 + mi) * 16 + (lane & 15);
+          AccN<false> ac[NPW];  // NPW tiles already give independent chains
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            if (kb == 0 || NN > 1) {
+#pragma unroll
+              for (int i = 0; i < NPW; ++i) {
+                const u32x4 t2[2] = {tb[i][kb][0], tb[i][kb][NP - 1]};
+                ac[i].add(t2, bz[mi][kb], kb, SP);
+              }
             }
-            reinterpret_cast<uint2 *>(ostage + h * OP)[w / 4] = o;
+#pragma unroll
+          for (int i = 0; i < NPW; ++i) {
+            const v4f acc = ac[i].sum(SP);
+            const int w = (wv + 4 * i) * 16 + 4 * (lane >> 4);
+            if constexpr (SP) {
+              ostage[h * OP + w / 4] = u32x4{__float_as_uint(acc[0] * isc), __float_as_uint(acc[1] * isc),
+                                             __float_as_uint(acc[2] * isc), __float_as_uint(acc[3] * isc)};
+            } else {
+              uint2 o;
+              if constexpr (DT == DT_F16) {
+                o.x = h16x2(acc[0] * isc, acc[1] * isc);
+                o.y = h16x2(acc[2] * isc, acc[3] * isc);
+              } else {
+                o.x = f32x2_to_bf16x2(acc[0] * isc, acc[1] * isc);
+                o.y = f32x2_to_bf16x2(acc[2] * isc, acc[3] * isc);
+              }
+              reinterpret_cast<uint2 *>(ostage + h * OP)[w / 4] = o;
+            }
           }
         }
       }
@@ -614,7 +728,7 @@ __global__ __launch_bounds__(kFT) void fno_inv_plane_mx(PlaneMxInvArgs a) {
 
 bool mx_supported(int H, int W, int m1, int m2, int dtype) {
   // fp32 carries hi + lo twiddle parts in registers: narrower planes, fewer modes
-  const int wmax = dtype == DT_F32 ? 128 : 256, m1max = dtype == DT_F32 ? 16 : 32;
+  const int wmax = dtype == DT_F32 ? 128 : 256, m1max = 32;
   return (dtype == DT_F16 || dtype == DT_BF16 || dtype == DT_F32) && H >= kRows && H <= 256 && W >= 64 &&
          W <= wmax && m1 <= m1max && m2 <= 32 && 2 * m1 <= H;
 }
@@ -623,7 +737,7 @@ int mx_ntiles(int m2) { return m2 <= 8 ? 1 : m2 <= 16 ? 2 : 4; }
 
 size_t mx_fwd_lds_bytes(int H, int W, int dtype) {
   const size_t np = dtype == DT_F32 ? 2 : 1;
-  return np * kRows * (W / 8 + 1) * 16 + np * 32 * kRBP * 2 + (size_t)H * 8 + (size_t)(kRows + 8) * 4;
+  return 2 * np * kRows * (W / 8 + 1) * 16 + 2 * np * 32 * kRBP * 2 + (size_t)H * 8 + (size_t)(2 * kRows + 16) * 4;
 }
 
 size_t mx_inv_lds_bytes(int H, int W, int dtype) {
@@ -632,35 +746,30 @@ size_t mx_inv_lds_bytes(int H, int W, int dtype) {
 }
 
 template <int DT, int KB>
-static const void *mx_kernel_kb(bool fwd, bool two, bool m2pw) {
+static const void *mx_kernel_kb(bool fwd, bool two) {
   if (!fwd) return (const void *)fno_inv_plane_mx<DT, KB>;
-  if constexpr (DT == DT_F32) {
-    if (m2pw) return nullptr;  // fp32 plans keep m1 <= 16
-  } else if (m2pw) {
-    return two ? (const void *)fno_fwd_plane_mx<DT, KB, true, 2> : (const void *)fno_fwd_plane_mx<DT, KB, false, 2>;
-  }
-  return two ? (const void *)fno_fwd_plane_mx<DT, KB, true, 1> : (const void *)fno_fwd_plane_mx<DT, KB, false, 1>;
+  return two ? (const void *)fno_fwd_plane_mx<DT, KB, true> : (const void *)fno_fwd_plane_mx<DT, KB, false>;
 }
 
 template <int DT>
-static const void *mx_kernel_dt(bool fwd, int W, bool two, bool m2pw) {
+static const void *mx_kernel_dt(bool fwd, int W, bool two) {
   switch (W) {
-    case 64: return mx_kernel_kb<DT, 2>(fwd, two, m2pw);
-    case 128: return mx_kernel_kb<DT, 4>(fwd, two, m2pw);
+    case 64: return mx_kernel_kb<DT, 2>(fwd, two);
+    case 128: return mx_kernel_kb<DT, 4>(fwd, two);
     case 256:
       if constexpr (DT == DT_F32) return nullptr;
-      else return mx_kernel_kb<DT, 8>(fwd, two, m2pw);
+      else return mx_kernel_kb<DT, 8>(fwd, two);
   }
   return nullptr;
 }
 
-// m2 > 8: R has two or four 16-column tiles; m1 > 16: more than four
-// m-tiles of modes, two per wave
+// m2 > 8: R has two or four 16-column tiles
 static const void *mx_kernel(bool fwd, int W, int m1, int m2, int dtype) {
-  const bool two = m2 > 8, m2pw = m1 > 16;
-  if (dtype == DT_F16) return mx_kernel_dt<DT_F16>(fwd, W, two, m2pw);
-  if (dtype == DT_BF16) return mx_kernel_dt<DT_BF16>(fwd, W, two, m2pw);
-  if (dtype == DT_F32) return mx_kernel_dt<DT_F32>(fwd, W, two, m2pw);
+  (void)m1;
+  const bool two = m2 > 8;
+  if (dtype == DT_F16) return mx_kernel_dt<DT_F16>(fwd, W, two);
+  if (dtype == DT_BF16) return mx_kernel_dt<DT_BF16>(fwd, W, two);
+  if (dtype == DT_F32) return mx_kernel_dt<DT_F32>(fwd, W, two);
   return nullptr;
 }
 
@@ -676,7 +785,7 @@ hipError_t mx_grid(bool fwd, int W, int m1, int m2, int dtype, size_t lds, int d
   const void *k = mx_kernel(fwd, W, m1, m2, dtype);
   if (!k) return hipErrorInvalidValue;
   int per_cu = 0, ncu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kFT, lds);
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, fwd ? kFW : kFT, lds);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, device);
   if (e != hipSuccess) return e;
   long g = (long)(per_cu > 0 ? per_cu : 1) * (ncu > 0 ? ncu : 1);
@@ -688,7 +797,7 @@ hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int grid, int dtype, siz
   const void *k = mx_kernel(true, a.W, a.m1, a.m2, dtype);
   if (!k || grid < 1) return hipErrorInvalidValue;
   void *args[] = {(void *)&a};
-  return hipLaunchKernel(k, dim3(grid), dim3(kFT), args, lds, s);
+  return hipLaunchKernel(k, dim3(grid), dim3(kFW), args, lds, s);
 }
 
 hipError_t launch_plane_mx_inv(const PlaneMxInvArgs &a, int grid, int dtype, size_t lds, hipStream_t s) {
