@@ -54,10 +54,12 @@ __device__ __forceinline__ v4f mma(u32x4 a, u32x4 b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint16_t h16(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// two fp32 -> packed fp16 pair, round to nearest even (one v_cvt_pk_f16_f32)
 __device__ __forceinline__ uint32_t h16x2(float lo, float hi) {
-  return (uint32_t)h16(lo) | ((uint32_t)h16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
 }
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -76,16 +78,32 @@ __device__ __forceinline__ uint32_t absmax_bits(u32x4 v) {
   return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+// maximum over the 16 lanes of each DPP row, in every lane of the row:
+// exchanges with lane ^ 1, lane ^ 2 (quad permutes), then the mirrored lane
+// of the half row and of the row (every source lane exists, so the bound
+// control that zeroes missing ones never applies; it lets each move fold
+// into its v_max as one DPP instruction)
+__device__ __forceinline__ int row16_max(int v) {
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0xb1, 0xf, 0xf, true));   // quad_perm [1, 0, 3, 2]
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4e, 0xf, 0xf, true));   // quad_perm [2, 3, 0, 1]
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x141, 0xf, 0xf, true));  // row_half_mirror
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x140, 0xf, 0xf, true));  // row_mirror
   return v;
 }
 
+// maximum over the wave, uniform: rows reduced by DPP, the four row results
+// read into scalars
+__device__ __forceinline__ int wave_max_i32(int v) {
+  v = row16_max(v);
+  const int a = max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16));
+  const int b = max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48));
+  return max(a, b);
+}
+
+// maximum of non-negative floats over the wave (their bit patterns order
+// the same way as signed integers)
 __device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  return __int_as_float(wave_max_i32(__float_as_int(v)));
 }
 
 // 2^e as an fp32 with e clamped to a range where it and 2^-e are normal
@@ -152,31 +170,34 @@ using Acc4 = AccN<true>;
 
 // fp32 -> fp16 hi, fp16 lo = fp16(v - hi), packed for two values
 __device__ __forceinline__ void split2(float v0, float v1, uint32_t &hi, uint32_t &lo) {
-  const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
-  hi = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-  lo = h16x2(v0 - (float)h0, v1 - (float)h1);
+  const f32x2 v = {v0, v1};
+  const f16x2 h = __builtin_convertvector(v, f16x2);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(v - __builtin_convertvector(h, f32x2), f16x2));
 }
 
-constexpr int kFW = 512;  // threads per workgroup of the forward kernel (8 waves)
-constexpr int kPF = 3;    // rounds in flight per workgroup (register ring)
+constexpr int kPF = 3;  // rounds in flight per workgroup (register ring)
 
 // rows of global round g of this workgroup: plane blockIdx.x + (g >> lgr)
-// * gridDim.x, rows 64 (g mod 2^lgr) .. +63; FU 16-byte units per thread
-template <int DT, int KB>
+// * gridDim.x, rows 64 (g mod 2^lgr) .. +63; FU 16-byte units per thread of
+// a workgroup of NW waves
+template <int DT, int KB, int NW>
 struct FwdIO {
+  static constexpr int NT = NW * 64;                               // threads
   static constexpr int W = 32 * KB, UR = W * MxPol<DT>::ES / 16;  // 16-byte units per row
-  static constexpr int FU = kRows * UR / kFW;                      // units per thread and round
+  static constexpr int FU = kRows * UR / NT;                       // units per thread and round
 };
 
-template <int DT, int KB>
-__device__ __forceinline__ void fwd_fetch(const void *x, int g, int lgr, int H, int tid, u32x4 (&p)[FwdIO<DT, KB>::FU]) {
-  using IO = FwdIO<DT, KB>;
+template <int DT, int KB, int NW>
+__device__ __forceinline__ void fwd_fetch(const void *x, int g, int lgr, int H, int tid,
+                                          u32x4 (&p)[FwdIO<DT, KB, NW>::FU]) {
+  using IO = FwdIO<DT, KB, NW>;
   const size_t plane = (size_t)blockIdx.x + (size_t)(g >> lgr) * gridDim.x;
   const int r = g & ((1 << lgr) - 1);
   const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(x) + plane * H * IO::W * MxPol<DT>::ES) +
                      (size_t)r * kRows * IO::UR + tid;
 #pragma unroll
-  for (int v = 0; v < IO::FU; ++v) p[v] = src[v * kFW];
+  for (int v = 0; v < IO::FU; ++v) p[v] = src[v * IO::NT];
 }
 
 // eight bf16 -> eight fp16 times 2^sig (exact while the result is normal)
@@ -194,10 +215,10 @@ struct FwdShape {
   int H, m1, m2, NT, MT, NN, lgW, lgr, total;  // lgr: log2 rounds per plane; total: rounds of this workgroup
 };
 
-template <int DT, int KB, bool TWO>
+template <int DT, int KB, int CPW>
 struct FwdRegs {
   static constexpr int NP = MxPol<DT>::NP;
-  u32x4 th[TWO ? 2 : 1][NP][KB];  // row twiddles (A operand) of this wave's c-tiles
+  u32x4 th[CPW][NP][KB];  // row twiddles (A operand) of this wave's c-tiles
   u32x4 ef[NP][4];                // column twiddles (A operand) of this wave's m-tile
 };
 
@@ -213,108 +234,135 @@ struct FwdLds {
   u32x4 *stage;   // [2][NP][64][PITCH]
   uint16_t *rb;   // [2][NP][32][kRBP]
   float2 *twh;    // [H]
-  int *rsig;      // [2][64] per-row scale exponents
-  int *mxs;       // [2][8] per-wave largest exponents
+  int *mxs;       // [2][8] per-wave largest exponents of a round
   __device__ __forceinline__ FwdLds(u32x4 *lds, int H) {
     stage = lds;
     rb = reinterpret_cast<uint16_t *>(stage + 2 * NP * STG);
     twh = reinterpret_cast<float2 *>(rb + 2 * NP * RBS);
-    rsig = reinterpret_cast<int *>(twh + H);
-    mxs = rsig + 2 * kRows;
+    mxs = reinterpret_cast<int *>(twh + H);
   }
 };
 
-// 1. stage the rows of round g in LDS buffer g & 1 as fp16 (bf16 and fp32
-//    rows scaled by a power of two per row into fp16 range; fp32 as hi + lo)
-//    and record the round's largest exponent; then reuse the registers for
-//    round g + kPF.
-template <int DT, int KB>
-__device__ __forceinline__ void fwd_put(int g, const FwdShape &s, u32x4 (&p)[FwdIO<DT, KB>::FU],
-                                        const PlaneMxFwdArgs &a, const FwdLds<DT, KB> &L) {
+// largest exponent e of a round's magnitudes (all < 2^e), from the running
+// maximum of one thread's share: fp16 / bf16 magnitude bits, or fp32 bits
+template <int DT>
+__device__ __forceinline__ int fwd_exp(uint32_t m) {
+  if (!m) return -1000;
+  if constexpr (DT == DT_F32) return (int)max(m >> 23, 1u) - 126;
+  else if constexpr (DT == DT_BF16) return (int)max(m >> 7, 1u) - 126;
+  else return (int)max(m >> 10, 1u) - 14;
+}
+
+template <int DT, int FU>
+__device__ __forceinline__ uint32_t fwd_absmax(const u32x4 (&p)[FU]) {
+  if constexpr (DT == DT_F32) {
+    float m = 0.f;
+#pragma unroll
+    for (int v = 0; v < FU; ++v) m = fmaxf(fmaxf(m, fmaxf(fabsf(__uint_as_float(p[v][0])), fabsf(__uint_as_float(p[v][1])))),
+                                          fmaxf(fabsf(__uint_as_float(p[v][2])), fabsf(__uint_as_float(p[v][3]))));
+    return __float_as_uint(m);
+  } else {
+    u16x2 m = {0, 0};
+#pragma unroll
+    for (int v = 0; v < FU; ++v) m = absmax_acc(m, p[v]);
+    return max((uint32_t)m.x, (uint32_t)m.y);
+  }
+}
+
+// record this wave's largest exponent of the round whose rows are in p
+template <int DT, int KB, int NW>
+__device__ __forceinline__ void fwd_note(int g, const u32x4 (&p)[FwdIO<DT, KB, NW>::FU], const FwdLds<DT, KB> &L) {
+  const int e = fwd_exp<DT>((uint32_t)wave_max_i32((int)fwd_absmax<DT, FwdIO<DT, KB, NW>::FU>(p)));
+  if ((threadIdx.x & 63) == 0) L.mxs[(g & 1) * 8 + (threadIdx.x >> 6)] = e;
+}
+
+// largest exponent of round g over the workgroup's waves
+template <int DT, int KB, int NW>
+__device__ __forceinline__ int fwd_round_exp(int g, const FwdLds<DT, KB> &L) {
+  int er = -1000;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) er = max(er, L.mxs[(g & 1) * 8 + i]);
+  return er;
+}
+
+// 1. stage the rows of round g (registers p) in LDS buffer g & 1 as fp16,
+//    then reuse p for round g + kPF. fp16 rows go as they are, and their
+//    largest exponent is noted for the R scale. bf16 and fp32 rows are
+//    scaled by 2^sig into fp16 range (fp32 as hi + lo parts), with sig from
+//    the round's largest exponent, noted one step earlier; this step notes
+//    that of round g + 1 (registers pn). Returns sig.
+template <int DT, int KB, int NW>
+__device__ __forceinline__ int fwd_put(int g, const FwdShape &s, u32x4 (&p)[FwdIO<DT, KB, NW>::FU],
+                                       const u32x4 (&pn)[FwdIO<DT, KB, NW>::FU], const PlaneMxFwdArgs &a,
+                                       const FwdLds<DT, KB> &L) {
   using P = MxPol<DT>;
   constexpr bool BF = DT == DT_BF16, SP = P::SP;
   constexpr int PITCH = FwdLds<DT, KB>::PITCH, STG = FwdLds<DT, KB>::STG;
-  constexpr int UR = FwdIO<DT, KB>::UR, FU = FwdIO<DT, KB>::FU;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  constexpr int UR = FwdIO<DT, KB, NW>::UR, FU = FwdIO<DT, KB, NW>::FU, NT = FwdIO<DT, KB, NW>::NT;
+  const int tid = threadIdx.x;
   u32x4 *stage = L.stage + (g & 1) * P::NP * STG;
-  int *rsig = L.rsig + (g & 1) * kRows;
-  int emax = -1000;
-  u16x2 mrun = {0, 0};
+  int sig = 0;
+  if constexpr (BF || SP) {
+    const int er = fwd_round_exp<DT, KB, NW>(g, L);
+    sig = er > -1000 ? max(-120, min(120, 14 - er)) : 0;  // round max * 2^sig < 2^15
+  }
+  const float sc = pow2f(sig);
 #pragma unroll
   for (int v = 0; v < FU; ++v) {
-    const int e = v * kFW + tid;
+    const int e = v * NT + tid;
     const int row = e / UR, cu = e - row * UR;
     const u32x4 d = p[v];
     if constexpr (SP) {
-      uint32_t m = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) m = max(m, d[i] & 0x7fffffffu);
-#pragma unroll
-      for (int o = 1; o < UR; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
-      const int eh = (int)max(m >> 23, 1u) - 126;  // row max < 2^eh
-      const int sig = max(-120, min(120, 14 - eh));
-      const float sc = pow2f(sig);
       uint32_t h0, l0, h1, l1;
       split2(__uint_as_float(d[0]) * sc, __uint_as_float(d[1]) * sc, h0, l0);
       split2(__uint_as_float(d[2]) * sc, __uint_as_float(d[3]) * sc, h1, l1);
       reinterpret_cast<uint2 *>(stage + row * PITCH)[cu] = make_uint2(h0, h1);
       reinterpret_cast<uint2 *>(stage + STG + row * PITCH)[cu] = make_uint2(l0, l1);
-      if ((tid & (UR - 1)) == 0) rsig[row] = m ? sig : 0;
-      emax = max(emax, m ? eh : -1000);
     } else if constexpr (BF) {
-      uint32_t m = absmax_bits(d);
-#pragma unroll
-      for (int o = 1; o < UR; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
-      const int eh = (int)max(m >> 7, 1u) - 126;  // row max < 2^eh
-      const int sig = max(-120, min(120, 14 - eh));
-      stage[row * PITCH + cu] = bf16_to_f16_scaled(d, pow2f(sig));
-      if ((tid & (UR - 1)) == 0) rsig[row] = m ? sig : 0;
-      emax = max(emax, m ? eh : -1000);
+      stage[row * PITCH + cu] = bf16_to_f16_scaled(d, sc);
     } else {
-      mrun = absmax_acc(mrun, d);
       stage[row * PITCH + cu] = d;
     }
   }
-  if constexpr (!BF && !SP) {
-    const uint32_t m = max((uint32_t)mrun.x, (uint32_t)mrun.y);
-    emax = m ? (int)max(m >> 10, 1u) - 14 : -1000;
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) emax = max(emax, __shfl_xor(emax, o, 64));
-  if (lane == 0) L.mxs[(g & 1) * 8 + wv] = emax;
-  if (g + kPF < s.total) fwd_fetch<DT, KB>(a.x, g + kPF, s.lgr, s.H, tid, p);
+  if constexpr (BF || SP) fwd_note<DT, KB, NW>(g + 1, pn, L);
+  else fwd_note<DT, KB, NW>(g, p, L);
+  // unconditional, so that the compiler counts loads exactly; past the end
+  // it re-reads the last round (an L2 hit), never used
+  fwd_fetch<DT, KB, NW>(a.x, min(g + kPF, s.total - 1), s.lgr, s.H, tid, p);
+  return sig;
 }
 
-// round g's R scale exponent: |R| <= W max|x| < 2^(emax + lgW), so
-// R 2^se < 2^15
-template <int DT, int KB>
+// round g's R scale exponent: |R| <= W max|x| < 2^(e + lgW), so R 2^se <
+// 2^15; for staged bf16 / fp32 rows (max < 2^15) that is -lgW
+template <int DT, int KB, int NW>
 __device__ __forceinline__ int fwd_scale(int g, const FwdShape &s, const FwdLds<DT, KB> &L) {
-  int er = -1000;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) er = max(er, L.mxs[(g & 1) * 8 + i]);
+  if constexpr (DT == DT_BF16 || DT == DT_F32) return -s.lgW;
+  const int er = fwd_round_exp<DT, KB, NW>(g, L);
   return er > -1000 ? max(-120, min(120, 15 - er - s.lgW)) : 0;
 }
 
 // 2. row product of round g, transposed: R^T[c][h] = sum_w T[w][c] x[h][w]
-//    with the twiddles as the register-held A operand (two 16-column tiles
+//    with the twiddles as the register-held A operand (CPW 16-column tiles
 //    of R per wave) and the staged rows as B; R scaled by 2^se (undone in
-//    fwd_col) into fp16 pairs of LDS buffer g & 1.
-template <int DT, int KB, bool TWO>
+//    fwd_col) into fp16 pairs of LDS buffer g & 1. The jobs (16-row block,
+//    group of CPW c-tiles) are dealt to the NW waves round-robin; NW is a
+//    multiple of the groups per block, so a wave's c-tiles never change.
+template <int DT, int KB, int CPW, int NW>
 __device__ __forceinline__ void fwd_row(int g, int se, const FwdShape &s, const FwdLds<DT, KB> &L,
-                                        const FwdRegs<DT, KB, TWO> &R) {
+                                        const FwdRegs<DT, KB, CPW> &R) {
+  constexpr bool TWO = CPW == 2;
   using P = MxPol<DT>;
   constexpr bool BF = DT == DT_BF16, SP = P::SP;
   constexpr int NP = P::NP;
   constexpr int PITCH = FwdLds<DT, KB>::PITCH, STG = FwdLds<DT, KB>::STG, RBS = FwdLds<DT, KB>::RBS;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const u32x4 *stage = L.stage + (g & 1) * NP * STG;
-  const int *rsig = L.rsig + (g & 1) * kRows;
   uint16_t *rb = L.rb + (g & 1) * NP * RBS;
-  const int G = s.NT == 4 ? 2 : 1;
-  const int ct0 = (wv % G) * 2;
+  const int G = s.NT / CPW;  // c-tile groups per 16-row block
+  const int ct0 = (wv % G) * CPW;
   // fragments are read in groups of KG blocks ahead of their products
   constexpr int KG = SP && KB > 2 ? 2 : KB;
-  for (int st = wv / G; st < 4; st += 8 / G) {
+  for (int st = wv / G; st < 4; st += NW / G) {
     const u32x4 *br = stage + (st * 16 + (lane & 15)) * PITCH + (lane >> 4);
     Acc4 a0, a1;
 #pragma unroll
@@ -337,7 +385,7 @@ __device__ __forceinline__ void fwd_row(int g, int se, const FwdShape &s, const 
     }
     const v4f acc0 = a0.sum(SP), acc1 = TWO ? a1.sum(SP) : acc0;
     const int h = st * 16 + (lane & 15);
-    const float f = (BF || SP) ? pow2f(se - rsig[h]) : pow2f(se);
+    const float f = pow2f(se);
     uint32_t *col = reinterpret_cast<uint32_t *>(rb) + h;
 #pragma unroll
     for (int t = 0; t < (TWO ? 2 : 1); ++t) {
@@ -359,9 +407,9 @@ __device__ __forceinline__ void fwd_row(int g, int se, const FwdShape &s, const 
 // 3. column product of round g's R against the 64-row twiddle block (m-tile
 //    wv of the modes), phase-shifted by the round offset and unscaled into X;
 //    after the last round of a plane, X is scaled, stored and reset.
-template <int DT, int KB, bool TWO>
+template <int DT, int KB, int CPW>
 __device__ __forceinline__ void fwd_col(int g, int se, const FwdShape &s, const PlaneMxFwdArgs &a,
-                                        const FwdLds<DT, KB> &L, const FwdRegs<DT, KB, TWO> &R, float2 (&X)[2][2]) {
+                                        const FwdLds<DT, KB> &L, const FwdRegs<DT, KB, CPW> &R, float2 (&X)[2][2]) {
   using P = MxPol<DT>;
   constexpr bool SP = P::SP;
   constexpr int NP = P::NP;
@@ -436,26 +484,29 @@ __device__ __forceinline__ void fwd_col(int g, int se, const FwdShape &s, const 
 
 // One pipeline step: stage round g, one barrier, then round g's row product
 // and round g - 1's column product (different LDS buffers).
-template <int DT, int KB, bool TWO>
-__device__ __forceinline__ void fwd_step(int g, int &se_prev, const FwdShape &s, u32x4 (&p)[FwdIO<DT, KB>::FU],
-                                         const PlaneMxFwdArgs &a, const FwdLds<DT, KB> &L,
-                                         const FwdRegs<DT, KB, TWO> &R, float2 (&X)[2][2]) {
-  fwd_put<DT, KB>(g, s, p, a, L);
+// se_prev: total scale exponent of round g - 1's R (staging and R scale)
+template <int DT, int KB, int CPW, int NW>
+__device__ __forceinline__ void fwd_step(int g, int &se_prev, const FwdShape &s, u32x4 (&p)[FwdIO<DT, KB, NW>::FU],
+                                         const u32x4 (&pn)[FwdIO<DT, KB, NW>::FU], const PlaneMxFwdArgs &a,
+                                         const FwdLds<DT, KB> &L, const FwdRegs<DT, KB, CPW> &R, float2 (&X)[2][2]) {
+  const int sig = fwd_put<DT, KB, NW>(g, s, p, pn, a, L);
   __syncthreads();
-  const int se = fwd_scale<DT, KB>(g, s, L);
-  fwd_row<DT, KB, TWO>(g, se, s, L, R);
-  if (g > 0) fwd_col<DT, KB, TWO>(g - 1, se_prev, s, a, L, R, X);
-  se_prev = se;
+  const int se = fwd_scale<DT, KB, NW>(g, s, L);
+  fwd_row<DT, KB, CPW, NW>(g, se, s, L, R);
+  if (g > 0) fwd_col<DT, KB, CPW>(g - 1, se_prev, s, a, L, R, X);
+  se_prev = se + sig;
 }
 
 // Persistent: workgroup b transforms planes b, b + gridDim.x, ...; its rounds
 // form one stream with kPF rounds in flight in a register ring, across plane
-// boundaries. One workgroup of 8 waves per CU. TWO: R has more than one
-// 16-column tile, and each wave computes two of them.
-template <int DT, int KB, bool TWO>
-__global__ __launch_bounds__(kFW) void fno_fwd_plane_mx(PlaneMxFwdArgs a) {
+// boundaries. NW waves per workgroup: 8 (one workgroup per CU) for wide or
+// split-operand planes and more than four m-tiles, else 4 (two or more per
+// CU). CPW: R c-tiles per wave in the row product (2 only when that still
+// gives every wave a job).
+template <int DT, int KB, int CPW, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void fno_fwd_plane_mx(PlaneMxFwdArgs a) {
   using P = MxPol<DT>;
-  using IO = FwdIO<DT, KB>;
+  using IO = FwdIO<DT, KB, NW>;
   constexpr int NP = P::NP;
   extern __shared__ u32x4 lds[];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -463,13 +514,13 @@ __global__ __launch_bounds__(kFW) void fno_fwd_plane_mx(PlaneMxFwdArgs a) {
   const int nmine = (a.nplanes - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   const FwdShape s{a.H, a.m1, a.m2, a.nt, a.mt, a.nn, a.lgW, lgr, nmine << lgr};
   const FwdLds<DT, KB> L(lds, s.H);
-  for (int v = tid; v < s.H; v += kFW) L.twh[v] = a.tw_h[v];
+  for (int v = tid; v < s.H; v += IO::NT) L.twh[v] = a.tw_h[v];
 
-  FwdRegs<DT, KB, TWO> R;
-  const int G = s.NT == 4 ? 2 : 1;
+  FwdRegs<DT, KB, CPW> R;
+  const int G = s.NT / CPW;
 #pragma unroll
-  for (int t = 0; t < (TWO ? 2 : 1); ++t) {
-    const int ct = min((wv % G) * 2 + t, s.NT - 1);
+  for (int t = 0; t < CPW; ++t) {
+    const int ct = min((wv % G) * CPW + t, s.NT - 1);
 #pragma unroll
     for (int q = 0; q < NP; ++q)
 #pragma unroll
@@ -491,20 +542,39 @@ __global__ __launch_bounds__(kFW) void fno_fwd_plane_mx(PlaneMxFwdArgs a) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) X[nn][t] = make_float2(0.f, 0.f);
 
+  if (s.total < 1) return;
+  // Every fetch is unconditional (clamped to the last round) and the loop
+  // runs whole ring turns only, with the remainder after it: a path that
+  // left the loop early but reached its head would make the compiler wait
+  // for all loads in flight there, draining the ring every turn.
+  // The table loads complete first and the ring's loads are issued in ring
+  // order, so the wait at the loop head is the same from either edge.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
   u32x4 p0[IO::FU], p1[IO::FU], p2[IO::FU];
-  if (s.total > 0) fwd_fetch<DT, KB>(a.x, 0, lgr, s.H, tid, p0);
-  if (s.total > 1) fwd_fetch<DT, KB>(a.x, 1, lgr, s.H, tid, p1);
-  if (s.total > 2) fwd_fetch<DT, KB>(a.x, 2, lgr, s.H, tid, p2);
-  int se_prev = 0;
-  for (int g = 0; g < s.total; g += kPF) {
-    fwd_step<DT, KB, TWO>(g, se_prev, s, p0, a, L, R, X);
-    if (g + 1 < s.total) fwd_step<DT, KB, TWO>(g + 1, se_prev, s, p1, a, L, R, X);
-    if (g + 2 < s.total) fwd_step<DT, KB, TWO>(g + 2, se_prev, s, p2, a, L, R, X);
-  }
-  if (s.total > 0) {
+  fwd_fetch<DT, KB, NW>(a.x, 0, lgr, s.H, tid, p0);
+  __builtin_amdgcn_sched_barrier(0);
+  fwd_fetch<DT, KB, NW>(a.x, min(1, s.total - 1), lgr, s.H, tid, p1);
+  __builtin_amdgcn_sched_barrier(0);
+  fwd_fetch<DT, KB, NW>(a.x, min(2, s.total - 1), lgr, s.H, tid, p2);
+  __builtin_amdgcn_sched_barrier(0);
+  // scaled dtypes: round 0's largest exponent before its staging
+  if constexpr (P::SP || DT == DT_BF16) {
+    fwd_note<DT, KB, NW>(0, p0, L);
     __syncthreads();
-    fwd_col<DT, KB, TWO>(s.total - 1, se_prev, s, a, L, R, X);
   }
+  int se_prev = 0;
+  const int full = s.total - s.total % kPF;
+  int g = 0;
+  for (; g < full; g += kPF) {
+    fwd_step<DT, KB, CPW, NW>(g, se_prev, s, p0, p1, a, L, R, X);
+    fwd_step<DT, KB, CPW, NW>(g + 1, se_prev, s, p1, p2, a, L, R, X);
+    fwd_step<DT, KB, CPW, NW>(g + 2, se_prev, s, p2, p0, a, L, R, X);
+  }
+  if (g < s.total) fwd_step<DT, KB, CPW, NW>(g, se_prev, s, p0, p1, a, L, R, X);
+  if (g + 1 < s.total) fwd_step<DT, KB, CPW, NW>(g + 1, se_prev, s, p1, p2, a, L, R, X);
+  __syncthreads();
+  fwd_col<DT, KB, CPW>(s.total - 1, se_prev, s, a, L, R, X);
 }
 
 // ------------------------------------------------------------------ inverse
@@ -737,7 +807,7 @@ int mx_ntiles(int m2) { return m2 <= 8 ? 1 : m2 <= 16 ? 2 : 4; }
 
 size_t mx_fwd_lds_bytes(int H, int W, int dtype) {
   const size_t np = dtype == DT_F32 ? 2 : 1;
-  return 2 * np * kRows * (W / 8 + 1) * 16 + 2 * np * 32 * kRBP * 2 + (size_t)H * 8 + (size_t)(2 * kRows + 16) * 4;
+  return 2 * np * kRows * (W / 8 + 1) * 16 + 2 * np * 32 * kRBP * 2 + (size_t)H * 8 + 16 * 4;
 }
 
 size_t mx_inv_lds_bytes(int H, int W, int dtype) {
@@ -745,31 +815,47 @@ size_t mx_inv_lds_bytes(int H, int W, int dtype) {
   return (size_t)kRows * (W * es / 16 + 1) * 16 + np * (32 * kRBP + (size_t)kRows * kZBP) * 2 + (size_t)H * 8 + 64;
 }
 
+// Forward workgroup shape: 8 waves where one workgroup per CU is all the
+// LDS or the m-tiles allow (W = 256, split-operand W = 128, more than four
+// m-tiles), else 4; two R c-tiles per wave only if every wave still gets a
+// row-product job (4 row blocks x c-tile groups >= waves).
+struct FwdCfg {
+  int nw, cpw;
+};
+
+static FwdCfg fwd_cfg(int W, int m1, int m2, int dtype) {
+  const int kb = W / 32, mt = (m1 + 3) / 4, nt = mx_ntiles(m2);
+  const bool sp = dtype == DT_F32;
+  const int nw = (kb == 8 || (sp && kb == 4) || mt > 4) ? 8 : 4;
+  return {nw, nt >= 2 && 2 * nt >= nw ? 2 : 1};
+}
+
 template <int DT, int KB>
-static const void *mx_kernel_kb(bool fwd, bool two) {
+static const void *mx_kernel_kb(bool fwd, FwdCfg c) {
   if (!fwd) return (const void *)fno_inv_plane_mx<DT, KB>;
-  return two ? (const void *)fno_fwd_plane_mx<DT, KB, true> : (const void *)fno_fwd_plane_mx<DT, KB, false>;
+  if (c.nw == 8)
+    return c.cpw == 2 ? (const void *)fno_fwd_plane_mx<DT, KB, 2, 8> : (const void *)fno_fwd_plane_mx<DT, KB, 1, 8>;
+  if constexpr (KB == 8 || (DT == DT_F32 && KB == 4)) return nullptr;  // always 8 waves
+  else return c.cpw == 2 ? (const void *)fno_fwd_plane_mx<DT, KB, 2, 4> : (const void *)fno_fwd_plane_mx<DT, KB, 1, 4>;
 }
 
 template <int DT>
-static const void *mx_kernel_dt(bool fwd, int W, bool two) {
+static const void *mx_kernel_dt(bool fwd, int W, FwdCfg c) {
   switch (W) {
-    case 64: return mx_kernel_kb<DT, 2>(fwd, two);
-    case 128: return mx_kernel_kb<DT, 4>(fwd, two);
+    case 64: return mx_kernel_kb<DT, 2>(fwd, c);
+    case 128: return mx_kernel_kb<DT, 4>(fwd, c);
     case 256:
       if constexpr (DT == DT_F32) return nullptr;
-      else return mx_kernel_kb<DT, 8>(fwd, two);
+      else return mx_kernel_kb<DT, 8>(fwd, c);
   }
   return nullptr;
 }
 
-// m2 > 8: R has two or four 16-column tiles
 static const void *mx_kernel(bool fwd, int W, int m1, int m2, int dtype) {
-  (void)m1;
-  const bool two = m2 > 8;
-  if (dtype == DT_F16) return mx_kernel_dt<DT_F16>(fwd, W, two);
-  if (dtype == DT_BF16) return mx_kernel_dt<DT_BF16>(fwd, W, two);
-  if (dtype == DT_F32) return mx_kernel_dt<DT_F32>(fwd, W, two);
+  const FwdCfg c = fwd_cfg(W, m1, m2, dtype);
+  if (dtype == DT_F16) return mx_kernel_dt<DT_F16>(fwd, W, c);
+  if (dtype == DT_BF16) return mx_kernel_dt<DT_BF16>(fwd, W, c);
+  if (dtype == DT_F32) return mx_kernel_dt<DT_F32>(fwd, W, c);
   return nullptr;
 }
 
@@ -785,7 +871,8 @@ hipError_t mx_grid(bool fwd, int W, int m1, int m2, int dtype, size_t lds, int d
   const void *k = mx_kernel(fwd, W, m1, m2, dtype);
   if (!k) return hipErrorInvalidValue;
   int per_cu = 0, ncu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, fwd ? kFW : kFT, lds);
+  const int threads = fwd ? fwd_cfg(W, m1, m2, dtype).nw * 64 : kFT;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, threads, lds);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, device);
   if (e != hipSuccess) return e;
   long g = (long)(per_cu > 0 ? per_cu : 1) * (ncu > 0 ? ncu : 1);
@@ -797,7 +884,7 @@ hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int grid, int dtype, siz
   const void *k = mx_kernel(true, a.W, a.m1, a.m2, dtype);
   if (!k || grid < 1) return hipErrorInvalidValue;
   void *args[] = {(void *)&a};
-  return hipLaunchKernel(k, dim3(grid), dim3(kFW), args, lds, s);
+  return hipLaunchKernel(k, dim3(grid), dim3(fwd_cfg(a.W, a.m1, a.m2, dtype).nw * 64), args, lds, s);
 }
 
 hipError_t launch_plane_mx_inv(const PlaneMxInvArgs &a, int grid, int dtype, size_t lds, hipStream_t s) {
