@@ -143,7 +143,19 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(2))) void f
   uint16_t *ws = xs + S::XS;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int K = a.K, Co = a.Co, B = a.B;
-  const int k0 = blockIdx.x * kMB, b0 = blockIdx.y * S::BT, o0 = blockIdx.z * kOT;
+  // Workgroup id -> (mode block, batch block, output tile). Consecutive ids
+  // go to different XCDs (ids equal mod 8 share one XCD and its L2). Each
+  // XCD takes one contiguous range of (mode, batch) blocks, output tiles
+  // fastest: the tiles of a block, and neighbouring mode blocks (the two
+  // halves of each 128-byte line of spectra), run on one XCD at about the
+  // same time, so repeated reads hit its L2.
+  const int NO = (Co + kOT - 1) / kOT, NKB = ((K + kMB - 1) / kMB) * ((B + S::BT - 1) / S::BT);
+  const int per = (NKB + 7) / 8;  // blocks per XCD
+  const int rest = (int)blockIdx.x >> 3;
+  const int tkb = ((int)blockIdx.x & 7) * per + rest / NO;
+  if (rest / NO >= per || tkb >= NKB) return;  // padding of the last XCD's range
+  const int NK = (K + kMB - 1) / kMB;
+  const int k0 = (tkb % NK) * kMB, b0 = (tkb / NK) * S::BT, o0 = (rest % NO) * kOT;
   const int nst = (a.Ci + kIC - 1) / kIC;
   const bool part1 = lane & 1;
 
@@ -256,7 +268,10 @@ hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s) {
   const void *k = contract_mx_kernel(dtype, a.B);
   if (!k) return hipErrorInvalidValue;
   const int BT = a.B <= 16 ? 16 : 32;
-  dim3 grid((a.K + kMB - 1) / kMB, (a.B + BT - 1) / BT, (a.Co + kOT - 1) / kOT);
+  const long nkb = (long)((a.K + kMB - 1) / kMB) * ((a.B + BT - 1) / BT), no = (a.Co + kOT - 1) / kOT;
+  const long n = (nkb + 7) / 8 * 8 * no;
+  if (n > 0x7fffffffL) return hipErrorInvalidValue;
+  dim3 grid((unsigned)n);
   void *args[] = {(void *)&a};
   return hipLaunchKernel(k, grid, dim3(kCT), args, contract_mx_lds_bytes(dtype, a.B), s);
 }

@@ -47,6 +47,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
 constexpr int kRows = 64;  // rows per round
+constexpr int kMaxH = 256; // largest plane height
 constexpr int kRBP = 136;  // halves per row of a B-operand round buffer (128 + pad)
 constexpr int kZBP = 72;   // halves per row of the inverse Z buffer (64 + pad)
 
@@ -514,7 +515,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int nmine = (a.nplanes - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   const FwdShape s{a.H, a.m1, a.m2, a.nt, a.mt, a.nn, a.lgW, lgr, nmine << lgr};
   const FwdLds<DT, KB> L(lds, s.H);
-  for (int v = tid; v < s.H; v += IO::NT) L.twh[v] = a.tw_h[v];
+  if (s.total < 1) return;
+
+  // Round 0's rows are requested first and the twiddle tables next (L2
+  // hits), so that the two latencies overlap; both are waited for, then
+  // rounds 1 and 2 go out in ring order. Every fetch is unconditional
+  // (clamped to the last round) and the loop below runs whole ring turns
+  // only, with the remainder after it: a path that left the loop early but
+  // reached its head would make the compiler wait for all loads in flight
+  // there, draining the ring every turn.
+  u32x4 p0[IO::FU], p1[IO::FU], p2[IO::FU];
+  fwd_fetch<DT, KB, NW>(a.x, 0, lgr, s.H, tid, p0);
+  __builtin_amdgcn_sched_barrier(0);
 
   FwdRegs<DT, KB, CPW> R;
   const int G = s.NT / CPW;
@@ -536,28 +548,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         R.ef[q][kb] = reinterpret_cast<const u32x4 *>(q ? a.ef_lo : a.ef)[((size_t)mt * 4 + kb) * 64 + lane];
   }
 
-  float2 X[2][2];
+  float2 tw[(kMaxH + IO::NT - 1) / IO::NT];
 #pragma unroll
-  for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) X[nn][t] = make_float2(0.f, 0.f);
-
-  if (s.total < 1) return;
-  // Every fetch is unconditional (clamped to the last round) and the loop
-  // runs whole ring turns only, with the remainder after it: a path that
-  // left the loop early but reached its head would make the compiler wait
-  // for all loads in flight there, draining the ring every turn.
-  // The table loads complete first and the ring's loads are issued in ring
-  // order, so the wait at the loop head is the same from either edge.
+  for (int i = 0; i < (kMaxH + IO::NT - 1) / IO::NT; ++i) {
+    const int v = tid + i * IO::NT;
+    if (v < s.H) tw[i] = a.tw_h[v];
+  }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-  __builtin_amdgcn_sched_barrier(0);
-  u32x4 p0[IO::FU], p1[IO::FU], p2[IO::FU];
-  fwd_fetch<DT, KB, NW>(a.x, 0, lgr, s.H, tid, p0);
   __builtin_amdgcn_sched_barrier(0);
   fwd_fetch<DT, KB, NW>(a.x, min(1, s.total - 1), lgr, s.H, tid, p1);
   __builtin_amdgcn_sched_barrier(0);
   fwd_fetch<DT, KB, NW>(a.x, min(2, s.total - 1), lgr, s.H, tid, p2);
   __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < (kMaxH + IO::NT - 1) / IO::NT; ++i) {
+    const int v = tid + i * IO::NT;
+    if (v < s.H) L.twh[v] = tw[i];
+  }
+  float2 X[2][2];
+#pragma unroll
+  for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) X[nn][t] = make_float2(0.f, 0.f);
   // scaled dtypes: round 0's largest exponent before its staging
   if constexpr (P::SP || DT == DT_BF16) {
     fwd_note<DT, KB, NW>(0, p0, L);
@@ -586,9 +598,8 @@ __device__ __forceinline__ void inv_load(const float2 *in, size_t plane, int K, 
 #pragma unroll
   for (int i = 0; i < NY; ++i) {
     const int v = tid + i * kFT;
-    const bool ok = v < K;
-    const float2 t = ip[ok ? v : 0];
-    yv[i] = ok ? t : make_float2(0.f, 0.f);
+    const float2 t = ip[min(v, K - 1)];
+    yv[i] = v < K ? t : make_float2(0.f, 0.f);
   }
 }
 
@@ -661,7 +672,6 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(2))) void f
     for (int i = 0; i < NY; ++i) mloc = fmaxf(mloc, fmaxf(fabsf(yv[i].x), fabsf(yv[i].y)));
     mloc = wave_max_f32(mloc);
     if (lane == 0) ymx[(pi & 1) * 4 + wv] = mloc;
-    if (pi + 1 < nmine) inv_load<NY>(a.in, plane + gridDim.x, K, tid, yn);
     __syncthreads();
 
     // |Z| <= sum_q (|Re Y| + |Im Y|) <= 4 m1 max|Y| < 2^(e + lg4m1)
@@ -674,7 +684,7 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(2))) void f
     const float sc = pow2f(se), isc = pow2f(-se);
 
     u32x4 *yp = reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(a.y) + plane * H * W * P::ES);
-    for (int r = 0; r < rounds; ++r) {
+    auto round = [&](int r) {
       // 1. spectra of the round: Y[q][ky] e^{+2 pi i kx(q) h0 / H}, scaled, fp16
 #pragma unroll
       for (int i = 0; i < NY; ++i) {
@@ -788,7 +798,13 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(2))) void f
         const int row = e2 / UR, cu = e2 - row * UR;
         yp[(size_t)r * kRows * UR + e2] = ostage[row * OP + cu];
       }
-    }
+    };
+    for (int r = 0; r + 1 < rounds; ++r) round(r);
+    // The next plane's spectra (after the last plane, this one's again,
+    // unused) are requested before the last round: only that round's stores
+    // are issued after them, so the copy below waits for nothing else.
+    inv_load<NY>(a.in, pi + 1 < nmine ? plane + gridDim.x : plane, K, tid, yn);
+    round(rounds - 1);
 #pragma unroll
     for (int i = 0; i < NY; ++i) yv[i] = yn[i];
   }
