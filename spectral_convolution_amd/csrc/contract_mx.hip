@@ -33,6 +33,8 @@ constexpr int kMB = 8;    // modes per workgroup
 constexpr int kIC = 16;   // input channels per stage (one 32-deep block of K)
 constexpr int kOT = 32;   // output channels per workgroup (four 16-column tiles of N)
 constexpr int kSP = 40;   // halves per staged fragment row (32 + 8 pad: conflict-free reads)
+constexpr int kYO = 20;   // floats per output-channel row of the result stage (16 + 4 pad)
+constexpr int kYB = kOT * kYO + 4;  // floats per batch row of the result stage
 
 __device__ __forceinline__ v4f mma_bf(u32x4 a, u32x4 b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
@@ -51,7 +53,8 @@ struct CmxShape {
   static constexpr int HL = DT == DT_F16 ? 2 : 1;          // weight parts
   static constexpr int XU = kMB * BT * kIC * 8 / (16 * kCT);   // 16-byte spectra units per thread and stage
   static constexpr int WU = kMB * kIC * kOT * 4 / (16 * kCT);  // 16-byte weight units per thread and stage
-  static constexpr int XS = kMB * 2 * BT * kSP;             // halves of the spectra stage
+  static constexpr int XB = BT * kSP;                        // halves of one (mode, part) block
+  static constexpr int XS = kMB * 2 * XB;                    // halves of the spectra stage
   static constexpr int WS = kMB * HL * kOT * kSP;           // halves of the weight stage
 };
 
@@ -81,6 +84,18 @@ __device__ __forceinline__ void cmx_fetch(const ContractArgs &a, int st, int k0,
   }
 }
 
+// Row of batch row b in the spectra block of mode m: rotated by 4 rows per
+// mode pair, so that the four mode pairs one store instruction touches
+// start 16 banks apart (4 rows of 20 words).
+template <int MT>
+__device__ __forceinline__ int xrow(int m, int b) { return (b + 4 * (m >> 1)) & (16 * MT - 1); }
+
+// Column of input channel i in weight row o: rows of output channels 16 ..
+// 31 are rotated by 8 columns (two whole 16-byte fragment chunks), so that
+// the eight output groups one store instruction touches fall on distinct
+// banks.
+__device__ __forceinline__ int wcol(int i, int o) { return (i + ((o >> 4) & 1) * 8) & (kIC - 1); }
+
 // split and transpose one stage into fragment rows:
 //   xs[mode][part][b][2 i + re/im], ws[mode][part][o][2 i + re/im]
 template <int DT, int MT>
@@ -97,8 +112,8 @@ __device__ __forceinline__ void cmx_put(uint16_t *xs, uint16_t *ws, int tid, con
       uint32_t hi, lo;
       split_pair(__uint_as_float(px[v][2 * t]), __uint_as_float(px[v][2 * t + 1]), hi, lo);
       const int m = 2 * c + t;
-      reinterpret_cast<uint32_t *>(xs + ((m * 2 + 0) * S::BT + b) * kSP)[i] = hi;
-      reinterpret_cast<uint32_t *>(xs + ((m * 2 + 1) * S::BT + b) * kSP)[i] = lo;
+      reinterpret_cast<uint32_t *>(xs + (m * 2 + 0) * S::XB + xrow<MT>(m, b) * kSP)[i] = hi;
+      reinterpret_cast<uint32_t *>(xs + (m * 2 + 1) * S::XB + xrow<MT>(m, b) * kSP)[i] = lo;
     }
   }
 #pragma unroll
@@ -116,10 +131,10 @@ __device__ __forceinline__ void cmx_put(uint16_t *xs, uint16_t *ws, int tid, con
         const float im = (float)__builtin_bit_cast(_Float16, (uint16_t)(pw[v][t] >> 16));
         uint32_t hi, lo;
         split_pair(re, im, hi, lo);
-        reinterpret_cast<uint32_t *>(ws + ((m * 2 + 0) * kOT + o) * kSP)[i] = hi;
-        reinterpret_cast<uint32_t *>(ws + ((m * 2 + 1) * kOT + o) * kSP)[i] = lo;
+        reinterpret_cast<uint32_t *>(ws + ((m * 2 + 0) * kOT + o) * kSP)[wcol(i, o)] = hi;
+        reinterpret_cast<uint32_t *>(ws + ((m * 2 + 1) * kOT + o) * kSP)[wcol(i, o)] = lo;
       } else {
-        reinterpret_cast<uint32_t *>(ws + (m * kOT + o) * kSP)[i] = pw[v][t];
+        reinterpret_cast<uint32_t *>(ws + (m * kOT + o) * kSP)[wcol(i, o)] = pw[v][t];
       }
     }
   }
@@ -181,7 +196,7 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(2))) void f
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int p = 0; p < 2; ++p)
-          af[mt][p] = *reinterpret_cast<const u32x4 *>(xs + ((m * 2 + p) * S::BT + mt * 16 + (lane & 15)) * kSP +
+          af[mt][p] = *reinterpret_cast<const u32x4 *>(xs + (m * 2 + p) * S::XB + xrow<MT>(m, mt * 16 + (lane & 15)) * kSP +
                                                        8 * (lane >> 4));
 #pragma unroll
       for (int nh = 0; nh < 2; ++nh) {  // two halves of the output tiles
@@ -191,7 +206,8 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(2))) void f
 #pragma unroll
           for (int p = 0; p < S::HL; ++p)
             bf[t][p] = *reinterpret_cast<const u32x4 *>(
-                ws + ((m * S::HL + p) * kOT + (2 * nh + t) * 8 + ((lane & 15) >> 1)) * kSP + 8 * (lane >> 4));
+                ws + ((m * S::HL + p) * kOT + (2 * nh + t) * 8 + ((lane & 15) >> 1)) * kSP +
+              2 * wcol(4 * (lane >> 4), 16 * nh));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -211,30 +227,36 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(2))) void f
     __syncthreads();
   }
 
-  // results -> LDS ys[b][o][8 modes] (re, im) -> rows of 8 modes of Yh
+  // results -> LDS ys[b][o][8 modes] (re, im) -> rows of 8 modes of Yh, 16
+  // batch rows at a time; row pitches of kYO and kYB floats keep the
+  // stores to at most two lanes per bank
   float *ys = reinterpret_cast<float *>(sm);
 #pragma unroll
-  for (int mm = 0; mm < 2; ++mm)
+  for (int mt = 0; mt < MT; ++mt) {
+    if (mt > 0) __syncthreads();
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const int n = nt * 16 + (lane & 15), o = n >> 1, part = n & 1;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int b = mt * 16 + 4 * (lane >> 4) + j;
-          ys[((b * kOT + o) * kMB + 2 * wv + mm) * 2 + part] = acc[mm][mt][nt][j];
+          const int b = 4 * (lane >> 4) + j;
+          ys[b * kYB + o * kYO + (2 * wv + mm) * 2 + part] = acc[mm][mt][nt][j];
         }
       }
-  __syncthreads();
-  constexpr int YU = S::BT * kOT * kMB * 8 / 16 / kCT;  // 16-byte result units per thread
+    __syncthreads();
+    constexpr int YU = 16 * kOT * kMB * 8 / 16 / kCT;  // 16-byte result units per thread
 #pragma unroll
-  for (int v = 0; v < YU; ++v) {
-    const int u = v * kCT + tid;
-    const int row = u >> 2, c = u & 3;  // row = (b, o); c: modes 2c, 2c + 1
-    const int b = b0 + row / kOT, o = o0 + row % kOT, mode = k0 + 2 * c;
-    if (b < B && o < Co && mode < K)
-      *reinterpret_cast<u32x4 *>(a.yh + ((size_t)b * Co + o) * K + mode) = reinterpret_cast<const u32x4 *>(ys)[u];
+    for (int v = 0; v < YU; ++v) {
+      const int u = v * kCT + tid;
+      const int row = u >> 2, c = u & 3;  // row = (b, o); c: modes 2c, 2c + 1
+      const int bl = row / kOT, ol = row % kOT;
+      const int b = b0 + mt * 16 + bl, o = o0 + ol, mode = k0 + 2 * c;
+      if (b < B && o < Co && mode < K)
+        *reinterpret_cast<u32x4 *>(a.yh + ((size_t)b * Co + o) * K + mode) =
+            *reinterpret_cast<const u32x4 *>(ys + bl * kYB + ol * kYO + 4 * c);
+    }
   }
 }
 
@@ -254,7 +276,7 @@ static const void *contract_mx_kernel(int dtype, int B) {
 size_t contract_mx_lds_bytes(int dtype, int B) {
   const int BT = B <= 16 ? 16 : 32, HL = dtype == DT_F16 ? 2 : 1;
   const size_t stage = ((size_t)kMB * 2 * BT * kSP + (size_t)kMB * HL * kOT * kSP) * 2;
-  const size_t out = (size_t)BT * kOT * kMB * 8;
+  const size_t out = (size_t)16 * kYB * 4;
   return stage > out ? stage : out;
 }
 

@@ -167,7 +167,6 @@ struct AccN {
     return r;
   }
 };
-using Acc4 = AccN<true>;
 
 // fp32 -> fp16 hi, fp16 lo = fp16(v - hi), packed for two values
 __device__ __forceinline__ void split2(float v0, float v1, uint32_t &hi, uint32_t &lo) {
@@ -365,7 +364,7 @@ __device__ __forceinline__ void fwd_row(int g, int se, const FwdShape &s, const 
   constexpr int KG = SP && KB > 2 ? 2 : KB;
   for (int st = wv / G; st < 4; st += NW / G) {
     const u32x4 *br = stage + (st * 16 + (lane & 15)) * PITCH + (lane >> 4);
-    Acc4 a0, a1;
+    AccN<!TWO> a0, a1;  // two tiles already give independent chains
 #pragma unroll
     for (int k0 = 0; k0 < KB; k0 += KG) {
       u32x4 bv[KG][2];
@@ -444,7 +443,7 @@ __device__ __forceinline__ void fwd_col(int g, int se, const FwdShape &s, const 
           for (int q = 0; q < 2; ++q) bv[i][kb][q] = q < NP ? br[q * (RBS / 8) + kb * 4] : bv[i][kb][0];
       }
       __builtin_amdgcn_sched_barrier(0);
-      Acc4 ac[NB];
+      AccN<SP> ac[NB];  // two ky tiles give independent chains unless split
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const u32x4 e2[2] = {R.ef[0][kb], R.ef[NP - 1][kb]};

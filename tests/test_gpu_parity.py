@@ -58,6 +58,15 @@ SMALL = [
     ("mx-2d-m1", _cfg("r", 2, 2, 3, 1, (64, 64), (1, 1), "uniform"), "bf16"),
     ("mx-2d-c4", _cfg("r", 2, 1, 4, 4, (256, 256), (24, 24)), "f16"),
     ("mx-3d", _cfg("r", 3, 1, 3, 2, (8, 64, 128), (3, 12, 20), "uniform"), "f16"),
+    # forward workgroup shapes: 8 waves for more than four m-tiles with one
+    # or two R c-tiles per wave, 4 waves with one, split fp32 operands on
+    # every shape they take
+    ("mx-nw8-cpw1", _cfg("r", 2, 2, 3, 2, (64, 64), (20, 12), "uniform"), "f16"),
+    ("mx-nw8-cpw2", _cfg("r", 2, 1, 2, 3, (128, 128), (24, 20), "uniform"), "bf16"),
+    ("mx-w256-cpw1", _cfg("r", 2, 1, 3, 2, (64, 256), (9, 14), "uniform"), "f16"),
+    ("mx-f32-nt4", _cfg("r", 2, 2, 2, 3, (64, 128), (10, 24), "uniform"), "f32"),
+    ("mx-f32-nw8", _cfg("r", 2, 1, 3, 2, (128, 64), (18, 7), "uniform"), "f32"),
+    ("mx-f32-nt1", _cfg("r", 2, 3, 2, 2, (64, 64), (5, 8), "uniform"), "f32"),
     # fp16 / bf16 contraction on matrix cores: ragged batch, channel and mode
     # tiles (two batch tiles, partial input stages, partial output tiles)
     ("cmx-rag-f16", _cfg("r", 2, 33, 20, 36, (64, 64), (6, 5), "uniform"), "f16"),
