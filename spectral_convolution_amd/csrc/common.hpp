@@ -156,7 +156,7 @@ hipError_t launch_axis_inv(const AxisArgs &a, int MP, hipStream_t s);
 int contract_pick_bb(int B, int Co, int K);
 int contract_pick_split(int B, int Ci, int Co, int K, int bb);
 size_t contract_lds_bytes(int bb, int S);
-hipError_t contract_prepare(int bb, int dtype, size_t lds);
+hipError_t contract_prepare(int bb, int dtype, int Co, size_t lds);
 hipError_t launch_contract(const ContractArgs &a, int bb, int S, int dtype, hipStream_t s);
 bool contract_mx_supported(int dtype, int Co, int K);
 size_t contract_mx_lds_bytes(int dtype, int B);

@@ -51,46 +51,42 @@ __device__ __forceinline__ void load_w4v(const void *w, size_t idx, float (&re)[
   }
 }
 
-// Operands of one input channel i. Loads are unconditional (out-of-range
-// lanes read element 0 and select zero) so they stay in flight together.
-template <int BB, int DT>
+// Operands of one input channel i. Lanes whose batch row, mode or output
+// channel is out of range read element 0 instead: their values only enter
+// products of outputs that are never stored (the 4x4 blocks are per mode,
+// rows per batch row, columns per output channel), so they need no zeroing,
+// and no load waits for an earlier one's value.
+template <int BB, int DT, bool VEC>
 __device__ __forceinline__ void load_frag(const ContractArgs &a, int i, int mode, bool mode_ok, int b0, int nn,
-                                          int ol, int nw, bool vec, Frag<BB> &f) {
+                                          int ol, int nw, Frag<BB> &f) {
   const int K = a.K, Ci = a.Ci, Co = a.Co, B = a.B;
 #pragma unroll
   for (int bb = 0; bb < BB; ++bb) {
     const int b = b0 + 4 * bb + nn;
     const bool ok = mode_ok && b < B;
     const float2 xv = a.xh[ok ? ((size_t)b * Ci + i) * K + mode : 0];
-    f.ar[bb] = ok ? xv.x : 0.f;
-    f.ai[bb] = ok ? xv.y : 0.f;
+    f.ar[bb] = xv.x;
+    f.ai[bb] = xv.y;
   }
   const size_t widx = ((size_t)(mode_ok ? mode : 0) * Ci + i) * Co + ol;
-  if (vec) {
-    const bool ok = nw == 4;
-    load_w4v<DT>(a.w, ok ? widx : 0, f.wr, f.wi);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f.wr[t] = ok ? f.wr[t] : 0.f;
-      f.wi[t] = ok ? f.wi[t] : 0.f;
-    }
+  if constexpr (VEC) {
+    load_w4v<DT>(a.w, nw == 4 ? widx : 0, f.wr, f.wi);
   } else {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const bool ok = t < nw;
-      const float2 v = load_pair<DT>(a.w, 2 * (ok ? widx + t : 0));
-      f.wr[t] = ok ? v.x : 0.f;
-      f.wi[t] = ok ? v.y : 0.f;
+      const float2 v = load_pair<DT>(a.w, 2 * (t < nw ? widx + t : 0));
+      f.wr[t] = v.x;
+      f.wi[t] = v.y;
     }
   }
 }
 
 // The input-channel sum is split over the S waves of a workgroup (wave s
-// takes channels [s*Ci/S, (s+1)*Ci/S)); each wave prefetches the operands of
-// its next channel while the MFMAs of the current one run. Partial sums meet
-// in LDS and wave 0 adds them in wave order, so results do not depend on
-// timing.
-template <int BB, int DT>
+// takes channels [s*Ci/S, (s+1)*Ci/S)); each wave keeps the operands of its
+// next channels in flight while the MFMAs of the current one run. Partial
+// sums meet in LDS, and each wave adds up and stores a share of them.
+// VEC: Co is a multiple of 4, each lane's four weights load as one vector.
+template <int BB, int DT, bool VEC>
 __global__ __launch_bounds__(512) void fno_contract(ContractArgs a) {
   extern __shared__ float red[];
   const int lane = threadIdx.x & 63, s = threadIdx.x >> 6, S = blockDim.x >> 6;
@@ -102,7 +98,6 @@ __global__ __launch_bounds__(512) void fno_contract(ContractArgs a) {
   const bool mode_ok = mode < K;
   const int ol = o0 + 4 * nn;  // first of this lane's 4 output channels
   const int nw = mode_ok ? min(4, max(0, Co - ol)) : 0;
-  const bool vec = (Co & 3) == 0;
   const int i0 = (Ci * s) / S, i1 = (Ci * (s + 1)) / S;
 
   v4f accr[BB][4], acci[BB][4];
@@ -114,69 +109,87 @@ __global__ __launch_bounds__(512) void fno_contract(ContractArgs a) {
       acci[bb][ob] = v4f{0.f, 0.f, 0.f, 0.f};
     }
 
-  Frag<BB> cur, nxt;
-  if (i0 < i1) load_frag<BB, DT>(a, i0, mode, mode_ok, b0, nn, ol, nw, vec, cur);
-  for (int i = i0; i < i1; ++i) {
-    if (i + 1 < i1) load_frag<BB, DT>(a, i + 1, mode, mode_ok, b0, nn, ol, nw, vec, nxt);
+  // A ring of D + 1 channels' operands in flight: channel i's products run
+  // while channels i + 1 .. i + D load, and the slot just used is refilled
+  // with channel i + D + 1. Loads are unconditional (clamped to the last
+  // channel; repeats are never multiplied) so the compiler's waits count
+  // them exactly.
+  constexpr int D = BB == 1 ? 3 : BB == 2 ? 2 : 1;
+  if (i0 < i1) {
+    Frag<BB> ring[D + 1];
 #pragma unroll
-    for (int bb = 0; bb < BB; ++bb) cur.an[bb] = -cur.ai[bb];
+    for (int k = 0; k <= D; ++k) load_frag<BB, DT, VEC>(a, min(i0 + k, i1 - 1), mode, mode_ok, b0, nn, ol, nw, ring[k]);
+    for (int i = i0; i < i1; i += D + 1) {
+#pragma unroll
+      for (int k = 0; k <= D; ++k) {
+        Frag<BB> &cur = ring[k];
+        if (i + k < i1) {
+#pragma unroll
+          for (int bb = 0; bb < BB; ++bb) cur.an[bb] = -cur.ai[bb];
+#pragma unroll
+          for (int bb = 0; bb < BB; ++bb)
+#pragma unroll
+            for (int ob = 0; ob < 4; ++ob) {
+              accr[bb][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(cur.ar[bb], cur.wr[ob], accr[bb][ob], 0, 0, 0);
+              accr[bb][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(cur.an[bb], cur.wi[ob], accr[bb][ob], 0, 0, 0);
+              acci[bb][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(cur.ar[bb], cur.wi[ob], acci[bb][ob], 0, 0, 0);
+              acci[bb][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(cur.ai[bb], cur.wr[ob], acci[bb][ob], 0, 0, 0);
+            }
+        }
+        load_frag<BB, DT, VEC>(a, min(i + k + D + 1, i1 - 1), mode, mode_ok, b0, nn, ol, nw, cur);
+      }
+    }
+  }
+
+  // accumulator register j of lane l holds block l/4, row j, column l%4:
+  // mode, batch row b0 + 4 bb + j, output channel ol + ob
+  if (S == 1) {
+    if (!mode_ok) return;
 #pragma unroll
     for (int bb = 0; bb < BB; ++bb)
 #pragma unroll
       for (int ob = 0; ob < 4; ++ob) {
-        accr[bb][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(cur.ar[bb], cur.wr[ob], accr[bb][ob], 0, 0, 0);
-        accr[bb][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(cur.an[bb], cur.wi[ob], accr[bb][ob], 0, 0, 0);
-        acci[bb][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(cur.ar[bb], cur.wi[ob], acci[bb][ob], 0, 0, 0);
-        acci[bb][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(cur.ai[bb], cur.wr[ob], acci[bb][ob], 0, 0, 0);
+        const int o = ol + ob;
+        if (o >= Co) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int b = b0 + 4 * bb + j;
+          if (b < B) a.yh[((size_t)b * Co + o) * K + mode] = make_float2(accr[bb][ob][j], acci[bb][ob][j]);
+        }
       }
-    cur = nxt;
+    return;
   }
-
-  if (S > 1) {
-    // partial sums of waves 1..S-1 -> LDS [wave-1][reg][lane]
-    constexpr int NR = BB * 4 * 8;
-    if (s > 0) {
-      float *dst = red + (size_t)(s - 1) * NR * 64 + lane;
+  // Every wave's partial sums -> LDS red[wave][pair][re / im][lane], pair =
+  // (bb, ob, j); then wave s adds up pairs [s NP / S, (s + 1) NP / S) over
+  // the waves in wave order (results do not depend on timing) and stores
+  // them.
+  constexpr int NP = BB * 16;  // (re, im) pairs per lane
+  {
+    float *dst = red + (size_t)s * NP * 2 * 64 + lane;
 #pragma unroll
-      for (int bb = 0; bb < BB; ++bb)
+    for (int bb = 0; bb < BB; ++bb)
 #pragma unroll
-        for (int ob = 0; ob < 4; ++ob)
+      for (int ob = 0; ob < 4; ++ob)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            dst[((bb * 4 + ob) * 8 + j) * 64] = accr[bb][ob][j];
-            dst[((bb * 4 + ob) * 8 + 4 + j) * 64] = acci[bb][ob][j];
-          }
-    }
-    __syncthreads();
-    if (s > 0) return;
-    for (int w = 1; w < S; ++w) {
-      const float *src = red + (size_t)(w - 1) * NR * 64 + lane;
-#pragma unroll
-      for (int bb = 0; bb < BB; ++bb)
-#pragma unroll
-        for (int ob = 0; ob < 4; ++ob)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            accr[bb][ob][j] += src[((bb * 4 + ob) * 8 + j) * 64];
-            acci[bb][ob][j] += src[((bb * 4 + ob) * 8 + 4 + j) * 64];
-          }
-    }
+        for (int j = 0; j < 4; ++j) {
+          const int q = (bb * 4 + ob) * 4 + j;
+          dst[(2 * q) * 64] = accr[bb][ob][j];
+          dst[(2 * q + 1) * 64] = acci[bb][ob][j];
+        }
   }
-
-  // accumulator register j of lane l holds block l/4, row j, column l%4
+  __syncthreads();
   if (!mode_ok) return;
-#pragma unroll
-  for (int bb = 0; bb < BB; ++bb)
-#pragma unroll
-    for (int ob = 0; ob < 4; ++ob) {
-      const int o = ol + ob;
-      if (o >= Co) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int b = b0 + 4 * bb + j;
-        if (b < B) a.yh[((size_t)b * Co + o) * K + mode] = make_float2(accr[bb][ob][j], acci[bb][ob][j]);
-      }
+  const int per = NP / S;
+  for (int q = s * per; q < (s + 1) * per; ++q) {
+    float re = 0.f, im = 0.f;
+    for (int w = 0; w < S; ++w) {
+      re += red[((size_t)w * NP * 2 + 2 * q) * 64 + lane];
+      im += red[((size_t)w * NP * 2 + 2 * q + 1) * 64 + lane];
     }
+    const int j = q & 3, ob = (q >> 2) & 3, bb = q >> 4;
+    const int o = ol + ob, b = b0 + 4 * bb + j;
+    if (o < Co && b < B) a.yh[((size_t)b * Co + o) * K + mode] = make_float2(re, im);
+  }
 }
 
 int contract_pick_bb(int B, int Co, int K) {
@@ -190,14 +203,19 @@ int contract_pick_bb(int B, int Co, int K) {
   return 1;
 }
 
-template <int BB>
-static const void *contract_kernel(int dtype) {
+template <int BB, bool VEC>
+static const void *contract_kernel_v(int dtype) {
   switch (dtype) {
-    case DT_F32: return (const void *)fno_contract<BB, DT_F32>;
-    case DT_F16: return (const void *)fno_contract<BB, DT_F16>;
-    case DT_BF16: return (const void *)fno_contract<BB, DT_BF16>;
+    case DT_F32: return (const void *)fno_contract<BB, DT_F32, VEC>;
+    case DT_F16: return (const void *)fno_contract<BB, DT_F16, VEC>;
+    case DT_BF16: return (const void *)fno_contract<BB, DT_BF16, VEC>;
   }
   return nullptr;
+}
+
+template <int BB>
+static const void *contract_kernel(int dtype, int Co) {
+  return (Co & 3) == 0 ? contract_kernel_v<BB, true>(dtype) : contract_kernel_v<BB, false>(dtype);
 }
 
 int contract_pick_split(int B, int Ci, int Co, int K, int bb) {
@@ -209,16 +227,17 @@ int contract_pick_split(int B, int Ci, int Co, int K, int bb) {
   return S;
 }
 
-size_t contract_lds_bytes(int bb, int S) { return (size_t)(S - 1) * bb * 32 * 64 * sizeof(float); }
+size_t contract_lds_bytes(int bb, int S) { return S > 1 ? (size_t)S * bb * 32 * 64 * sizeof(float) : 0; }
 
-hipError_t contract_prepare(int bb, int dtype, size_t lds) {
-  const void *k = bb == 4 ? contract_kernel<4>(dtype) : bb == 2 ? contract_kernel<2>(dtype) : contract_kernel<1>(dtype);
+hipError_t contract_prepare(int bb, int dtype, int Co, size_t lds) {
+  const void *k = bb == 4 ? contract_kernel<4>(dtype, Co) : bb == 2 ? contract_kernel<2>(dtype, Co) : contract_kernel<1>(dtype, Co);
   if (!k) return hipErrorInvalidValue;
   return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
 hipError_t launch_contract(const ContractArgs &a, int bb, int S, int dtype, hipStream_t s) {
-  const void *k = bb == 4 ? contract_kernel<4>(dtype) : bb == 2 ? contract_kernel<2>(dtype) : contract_kernel<1>(dtype);
+  const void *k = bb == 4 ? contract_kernel<4>(dtype, a.Co) : bb == 2 ? contract_kernel<2>(dtype, a.Co)
+                                                           : contract_kernel<1>(dtype, a.Co);
   if (!k) return hipErrorInvalidValue;
   dim3 grid((a.K + 15) / 16, (a.B + 4 * bb - 1) / (4 * bb), (a.Co + 15) / 16);
   void *args[] = {(void *)&a};

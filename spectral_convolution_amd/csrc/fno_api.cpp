@@ -458,7 +458,7 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   }
   if (e == hipSuccess && ndim == 3) e = axis_fwd_prepare(p->xMP, p->lds_axis);
   if (e == hipSuccess)
-    e = p->cmx ? contract_mx_prepare(p->dtype, p->B) : contract_prepare(p->bb, p->dtype, contract_lds_bytes(p->bb, p->split));
+    e = p->cmx ? contract_mx_prepare(p->dtype, p->B) : contract_prepare(p->bb, p->dtype, p->Co, contract_lds_bytes(p->bb, p->split));
   if (e != hipSuccess) {
     (void)hipFree(p->mem);
     delete p;
