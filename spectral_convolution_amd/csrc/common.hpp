@@ -145,7 +145,7 @@ hipError_t launch_plane_inv(const PlaneInvArgs &a, int MP, int rpt, int dtype, s
 int mx_ntiles(int m2);
 bool mx_supported(int H, int W, int m1, int m2, int dtype);
 size_t mx_fwd_lds_bytes(int H, int W, int dtype);
-size_t mx_inv_lds_bytes(int H, int W, int dtype);
+size_t mx_inv_lds_bytes(int H, int W, int m1, int m2, int dtype);
 hipError_t mx_prepare(bool fwd, int W, int m1, int m2, int dtype, size_t lds);
 hipError_t mx_grid(bool fwd, int W, int m1, int m2, int dtype, size_t lds, int device, int nplanes, int *grid);
 hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int grid, int dtype, size_t lds, hipStream_t s);

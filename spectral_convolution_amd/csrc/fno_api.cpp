@@ -277,7 +277,7 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
     p.mx_lgW = ceil_log2(p.pW);
     p.mx_lg4m1 = ceil_log2(4 * p.pm1);
     p.lds_fwd = mx_fwd_lds_bytes(p.pH, p.pW, (int)dtype);
-    p.lds_inv = mx_inv_lds_bytes(p.pH, p.pW, (int)dtype);
+    p.lds_inv = mx_inv_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, (int)dtype);
   }
   if (p.lds_fwd > kMaxLds || p.lds_inv > kMaxLds) return FNO_ERR_UNSUPPORTED;
   if (ndim == 3) {

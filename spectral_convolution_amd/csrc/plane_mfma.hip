@@ -590,6 +590,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
 // ------------------------------------------------------------------ inverse
 
+// Inverse sizes: up to 32 kx per corner and 32 ky, or (SM) up to 16 of each.
+// The spectra buffer holds YR ky rows of 2 (2 m1) halves plus 8 of padding,
+// Z 64 rows of 2 m2 halves plus 8: pitches of 36 or 20 words (and 68 for
+// the large spectra rows), which keep the 16-row fragment reads on
+// distinct banks.
+template <bool SM>
+struct InvGeom {
+  static constexpr int NY = SM ? 2 : 8;         // spectra values per thread (K <= 512 or 2048)
+  static constexpr int KBM = SM ? 2 : 4;        // k-blocks of E' Y
+  static constexpr int NNM = SM ? 1 : 2;        // ky tiles
+  static constexpr int YR = SM ? 16 : 32;       // ky rows of the spectra buffer
+  static constexpr int YP = SM ? 72 : kRBP;     // halves per spectra row
+  static constexpr int ZP = SM ? 40 : kZBP;     // halves per Z row
+};
+
 // spectra of one plane into registers: value tid + 256 i, zero past K
 template <int NY>
 __device__ __forceinline__ void inv_load(const float2 *in, size_t plane, int K, int tid, float2 (&yv)[NY]) {
@@ -612,9 +627,13 @@ __device__ __forceinline__ void inv_load(const float2 *in, size_t plane, int K, 
 //     of a row; unscaled, rounded to the storage dtype into the out stage;
 //  4. coalesced 16-byte stores of the 64 rows.
 // fp32 planes carry the spectra, Z and the twiddles as fp16 hi + lo.
-template <int DT, int KB>
-__global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(2))) void fno_inv_plane_mx(PlaneMxInvArgs a) {
+// SM: at most 16 kx per corner and 16 ky, so the spectra, Z and the
+// fragment registers take their smaller sizes (fewer registers and LDS,
+// more workgroups per CU).
+template <int DT, int KB, bool SM>
+__global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(SM ? 3 : 2))) void fno_inv_plane_mx(PlaneMxInvArgs a) {
   using P = MxPol<DT>;
+  using G = InvGeom<SM>;
   constexpr bool SP = P::SP;
   constexpr int NP = P::NP;
   constexpr int W = 32 * KB;
@@ -622,16 +641,18 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(2))) void f
   constexpr int FU = KB * P::ES / 2;               // 16-byte output units per thread and round
   constexpr int NTW = W / 16;                      // output column tiles
   constexpr int NPW = NTW / 4;                     // column tiles per wave
-  constexpr int NY = 8;                            // spectra values per thread (K <= 2048)
-  constexpr int YBS = 32 * kRBP, ZBS = kRows * kZBP;  // halves per part
+  constexpr int NY = G::NY;                        // spectra values per thread
+  constexpr int KBM = G::KBM, NNM = G::NNM;        // most k-blocks of E' Y, ky tiles
+  constexpr int YP = G::YP, ZP = G::ZP;            // pitches (halves) of the spectra and Z rows
+  constexpr int YBS = G::YR * YP, ZBS = kRows * ZP;  // halves per part
   extern __shared__ u32x4 lds[];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, m1 = a.m1, m2 = a.m2, NN = a.nn, KB1 = a.kb1;
   const int K = 2 * m1 * m2;
   const int nmine = (a.nplanes - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   u32x4 *ostage = lds;                                                      // [64][OP]
-  uint16_t *yb = reinterpret_cast<uint16_t *>(ostage + kRows * OP);         // [NP][32][kRBP]
-  uint16_t *zb = yb + NP * YBS;                                             // [NP][64][kZBP]
+  uint16_t *yb = reinterpret_cast<uint16_t *>(ostage + kRows * OP);         // [NP][YR][YP]
+  uint16_t *zb = yb + NP * YBS;                                             // [NP][64][ZP]
   float2 *twh = reinterpret_cast<float2 *>(zb + NP * ZBS);                  // [H]
   float *ymx = reinterpret_cast<float *>(twh + H);                          // [2][4]
 
@@ -641,22 +662,22 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(2))) void f
   for (int v = tid; v < H; v += kFT) twh[v] = a.tw_h[v];
 
   // E' fragments of m-tiles 2 wv, 2 wv + 1 (rows j = 16 wv .. 16 wv + 15)
-  u32x4 ef[2][4][NP];
+  u32x4 ef[2][KBM][NP];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < KBM; ++kb)
 #pragma unroll
       for (int q = 0; q < NP; ++q) {
         const u32x4 t = reinterpret_cast<const u32x4 *>(q ? a.ef_lo : a.ef)[((size_t)(2 * wv + mi) * KB1 + (kb < KB1 ? kb : 0)) * 64 + lane];
         ef[mi][kb][q] = kb < KB1 ? t : u32x4{0u, 0u, 0u, 0u};
       }
   // T' fragments (A operand) of output column tiles wv, wv + 4, ...
-  u32x4 tb[NPW][2][NP];
+  u32x4 tb[NPW][NNM][NP];
 #pragma unroll
   for (int i = 0; i < NPW; ++i)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NNM; ++kb)
 #pragma unroll
       for (int q = 0; q < NP; ++q) {
         const u32x4 t = reinterpret_cast<const u32x4 *>(q ? a.tb_lo : a.tb)[((size_t)(wv + 4 * i) * NN + (kb < NN ? kb : 0)) * 64 + lane];
@@ -696,26 +717,26 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(2))) void f
           const float zi = (yv[i].y * w.x - yv[i].x * w.y) * sc;
           uint32_t hi, lo;
           split2(zr, zi, hi, lo);
-          reinterpret_cast<uint32_t *>(yb + ky * kRBP)[q] = hi;
-          if constexpr (SP) reinterpret_cast<uint32_t *>(yb + YBS + ky * kRBP)[q] = lo;
+          reinterpret_cast<uint32_t *>(yb + ky * YP)[q] = hi;
+          if constexpr (SP) reinterpret_cast<uint32_t *>(yb + YBS + ky * YP)[q] = lo;
         }
       }
       __syncthreads();
 
       // 2. Z = E' Y, rows 16 wv .. 16 wv + 15, all ky tiles; fp16 into zb
 #pragma unroll
-      for (int nn = 0; nn < 2; ++nn) {
+      for (int nn = 0; nn < NNM; ++nn) {
         if (nn < NN) {
-          const u32x4 *br = reinterpret_cast<const u32x4 *>(yb + (nn * 16 + (lane & 15)) * kRBP) + (lane >> 4);
-          u32x4 bv[4][2];
+          const u32x4 *br = reinterpret_cast<const u32x4 *>(yb + (nn * 16 + (lane & 15)) * YP) + (lane >> 4);
+          u32x4 bv[KBM][2];
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
+          for (int kb = 0; kb < KBM; ++kb)
 #pragma unroll
             for (int q = 0; q < 2; ++q) bv[kb][q] = q < NP ? br[q * (YBS / 8) + (kb < KB1 ? kb : 0) * 4] : bv[kb][0];
           __builtin_amdgcn_sched_barrier(0);
           AccN<!SP> ac[2];
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
+          for (int kb = 0; kb < KBM; ++kb)
             if (kb < KB1) {
 #pragma unroll
               for (int mi = 0; mi < 2; ++mi) {
@@ -731,8 +752,8 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(2))) void f
             for (int jj = 0; jj < 2; ++jj) {
               uint32_t hi, lo;
               split2(acc[2 * jj], acc[2 * jj + 1], hi, lo);
-              reinterpret_cast<uint32_t *>(zb + (j0 + jj) * kZBP)[ky] = hi;
-              if constexpr (SP) reinterpret_cast<uint32_t *>(zb + ZBS + (j0 + jj) * kZBP)[ky] = lo;
+              reinterpret_cast<uint32_t *>(zb + (j0 + jj) * ZP)[ky] = hi;
+              if constexpr (SP) reinterpret_cast<uint32_t *>(zb + ZBS + (j0 + jj) * ZP)[ky] = lo;
             }
           }
         }
@@ -744,12 +765,12 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(2))) void f
       constexpr int MB = SP ? 1 : 4;
 #pragma unroll
       for (int m0 = 0; m0 < 4; m0 += MB) {
-        u32x4 bz[MB][2][2];
+        u32x4 bz[MB][NNM][2];
 #pragma unroll
         for (int mi = 0; mi < MB; ++mi) {
-          const u32x4 *zr = reinterpret_cast<const u32x4 *>(zb + ((m0 + mi) * 16 + (lane & 15)) * kZBP) + (lane >> 4);
+          const u32x4 *zr = reinterpret_cast<const u32x4 *>(zb + ((m0 + mi) * 16 + (lane & 15)) * ZP) + (lane >> 4);
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < NNM; ++kb)
 #pragma unroll
             for (int q = 0; q < 2; ++q) bz[mi][kb][q] = q < NP ? zr[q * (ZBS / 8) + (NN > 1 ? kb : 0) * 4] : bz[mi][kb][0];
         }
@@ -759,7 +780,7 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(2))) void f
           const int h = (m0 + mi) * 16 + (lane & 15);
           AccN<false> ac[NPW];  // NPW tiles already give independent chains
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < NNM; ++kb)
             if (kb == 0 || NN > 1) {
 #pragma unroll
               for (int i = 0; i < NPW; ++i) {
@@ -825,9 +846,18 @@ size_t mx_fwd_lds_bytes(int H, int W, int dtype) {
   return 2 * np * kRows * (W / 8 + 1) * 16 + 2 * np * 32 * kRBP * 2 + (size_t)H * 8 + 16 * 4;
 }
 
-size_t mx_inv_lds_bytes(int H, int W, int dtype) {
+static bool inv_small(int m1, int m2) { return m1 <= 16 && m2 <= 16; }
+
+template <bool SM>
+static size_t inv_lds(int H, int W, int dtype) {
+  using G = InvGeom<SM>;
   const size_t np = dtype == DT_F32 ? 2 : 1, es = dtype == DT_F32 ? 4 : 2;
-  return (size_t)kRows * (W * es / 16 + 1) * 16 + np * (32 * kRBP + (size_t)kRows * kZBP) * 2 + (size_t)H * 8 + 64;
+  return (size_t)kRows * (W * es / 16 + 1) * 16 + np * ((size_t)G::YR * G::YP + (size_t)kRows * G::ZP) * 2 +
+         (size_t)H * 8 + 64;
+}
+
+size_t mx_inv_lds_bytes(int H, int W, int m1, int m2, int dtype) {
+  return inv_small(m1, m2) ? inv_lds<true>(H, W, dtype) : inv_lds<false>(H, W, dtype);
 }
 
 // Forward workgroup shape: 8 waves where one workgroup per CU is all the
@@ -846,8 +876,8 @@ static FwdCfg fwd_cfg(int W, int m1, int m2, int dtype) {
 }
 
 template <int DT, int KB>
-static const void *mx_kernel_kb(bool fwd, FwdCfg c) {
-  if (!fwd) return (const void *)fno_inv_plane_mx<DT, KB>;
+static const void *mx_kernel_kb(bool fwd, FwdCfg c, bool small) {
+  if (!fwd) return small ? (const void *)fno_inv_plane_mx<DT, KB, true> : (const void *)fno_inv_plane_mx<DT, KB, false>;
   if (c.nw == 8)
     return c.cpw == 2 ? (const void *)fno_fwd_plane_mx<DT, KB, 2, 8> : (const void *)fno_fwd_plane_mx<DT, KB, 1, 8>;
   if constexpr (KB == 8 || (DT == DT_F32 && KB == 4)) return nullptr;  // always 8 waves
@@ -855,22 +885,23 @@ static const void *mx_kernel_kb(bool fwd, FwdCfg c) {
 }
 
 template <int DT>
-static const void *mx_kernel_dt(bool fwd, int W, FwdCfg c) {
+static const void *mx_kernel_dt(bool fwd, int W, FwdCfg c, bool small) {
   switch (W) {
-    case 64: return mx_kernel_kb<DT, 2>(fwd, c);
-    case 128: return mx_kernel_kb<DT, 4>(fwd, c);
+    case 64: return mx_kernel_kb<DT, 2>(fwd, c, small);
+    case 128: return mx_kernel_kb<DT, 4>(fwd, c, small);
     case 256:
       if constexpr (DT == DT_F32) return nullptr;
-      else return mx_kernel_kb<DT, 8>(fwd, c);
+      else return mx_kernel_kb<DT, 8>(fwd, c, small);
   }
   return nullptr;
 }
 
 static const void *mx_kernel(bool fwd, int W, int m1, int m2, int dtype) {
   const FwdCfg c = fwd_cfg(W, m1, m2, dtype);
-  if (dtype == DT_F16) return mx_kernel_dt<DT_F16>(fwd, W, c);
-  if (dtype == DT_BF16) return mx_kernel_dt<DT_BF16>(fwd, W, c);
-  if (dtype == DT_F32) return mx_kernel_dt<DT_F32>(fwd, W, c);
+  const bool small = inv_small(m1, m2);
+  if (dtype == DT_F16) return mx_kernel_dt<DT_F16>(fwd, W, c, small);
+  if (dtype == DT_BF16) return mx_kernel_dt<DT_BF16>(fwd, W, c, small);
+  if (dtype == DT_F32) return mx_kernel_dt<DT_F32>(fwd, W, c, small);
   return nullptr;
 }
 
