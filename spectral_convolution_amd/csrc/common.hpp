@@ -159,6 +159,7 @@ size_t contract_lds_bytes(int bb, int S);
 hipError_t contract_prepare(int bb, int dtype, int Co, size_t lds);
 hipError_t launch_contract(const ContractArgs &a, int bb, int S, int dtype, hipStream_t s);
 bool contract_mx_supported(int dtype, int Co, int K);
+long contract_mx_workgroups(int B, int Co, int K);
 size_t contract_mx_lds_bytes(int dtype, int B);
 hipError_t contract_mx_prepare(int dtype, int B);
 hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s);

@@ -266,6 +266,11 @@ bool contract_mx_supported(int dtype, int Co, int K) {
   return (dtype == DT_F16 || dtype == DT_BF16) && (Co & 3) == 0 && (K & 1) == 0;
 }
 
+long contract_mx_workgroups(int B, int Co, int K) {
+  const long BT = B <= 16 ? 16 : 32;
+  return (long)((K + kMB - 1) / kMB) * ((B + BT - 1) / BT) * ((Co + kOT - 1) / kOT);
+}
+
 static const void *contract_mx_kernel(int dtype, int B) {
   const bool one = B <= 16;
   if (dtype == DT_F16) return one ? (const void *)fno_contract_mx<DT_F16, 1> : (const void *)fno_contract_mx<DT_F16, 2>;

@@ -293,7 +293,11 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
     return FNO_ERR_UNSUPPORTED;
   p.bb = contract_pick_bb(batch, c_out, p.K);
   p.split = contract_pick_split(batch, c_in, c_out, p.K, p.bb);
-  p.cmx = contract_mx_supported((int)dtype, c_out, p.K);
+  // The matrix-core contraction gives each workgroup a block of 8 modes x
+  // 16 or 32 batch rows x 32 output channels; with fewer blocks than the
+  // 256 compute units it leaves most of the chip idle, and the per-mode
+  // kernel (one wave per 16 modes, channels split over waves) is faster.
+  p.cmx = contract_mx_supported((int)dtype, c_out, p.K) && contract_mx_workgroups(batch, c_out, p.K) >= 256;
   if (ndim == 2) {
     p.launches = {L_FWD_PLANE, L_CONTRACT, L_INV_PLANE};
   } else {

@@ -69,8 +69,8 @@ SMALL = [
     ("mx-f32-nt1", _cfg("r", 2, 3, 2, 2, (64, 64), (5, 8), "uniform"), "f32"),
     # fp16 / bf16 contraction on matrix cores: ragged batch, channel and mode
     # tiles (two batch tiles, partial input stages, partial output tiles)
-    ("cmx-rag-f16", _cfg("r", 2, 33, 20, 36, (64, 64), (6, 5), "uniform"), "f16"),
-    ("cmx-rag-bf16", _cfg("r", 2, 17, 33, 12, (64, 128), (9, 7), "uniform"), "bf16"),
+    ("cmx-rag-f16", _cfg("r", 2, 33, 20, 36, (128, 128), (30, 31), "uniform"), "f16"),
+    ("cmx-rag-bf16", _cfg("r", 2, 40, 33, 12, (128, 128), (31, 30), "uniform"), "bf16"),
 ]
 
 
