@@ -67,6 +67,7 @@ SMALL = [
     ("mx-f32-nt4", _cfg("r", 2, 2, 2, 3, (64, 128), (10, 24), "uniform"), "f32"),
     ("mx-f32-nw8", _cfg("r", 2, 1, 3, 2, (128, 64), (18, 7), "uniform"), "f32"),
     ("mx-f32-nt1", _cfg("r", 2, 3, 2, 2, (64, 64), (5, 8), "uniform"), "f32"),
+    ("mx-f32-m2", _cfg("r", 2, 2, 2, 3, (64, 64), (20, 20), "uniform"), "f32"),
     # fp16 / bf16 contraction on matrix cores: ragged batch, channel and mode
     # tiles (two batch tiles, partial input stages, partial output tiles)
     ("cmx-rag-f16", _cfg("r", 2, 33, 20, 36, (128, 128), (30, 31), "uniform"), "f16"),
