@@ -1,5 +1,5 @@
-// plane_mfma.hip - plane transforms of fp16 / bf16 planes as two streamed
-// matrix-core contractions each way.
+// plane_mfma.hip - plane transforms of fp16 / bf16 / fp32 planes as two
+// streamed matrix-core contractions each way.
 //
 // The layer keeps m2 of the W/2+1 row frequencies and 2 m1 of the H column
 // frequencies (TurboFNO write-up, sections 2.1 and 3.1: truncation means the
@@ -20,20 +20,22 @@
 // the same 64-row twiddle block for every round: the round offset h0 only
 // multiplies mode q by e^{-+2 pi i kx(q) h0 / H}, which is applied to the
 // per-round partial sums (forward) or to the spectra (inverse) on the VALU.
-// So a workgroup holds one 64-row stage of x or y, one round of R or Z, and
-// its twiddle fragments in registers: about 45-55 KB of LDS and ~240 VGPRs,
-// two workgroups of 4 waves per CU. Both kernels are persistent (one
+// So a workgroup holds 64-row stages of x or y, rounds of R or Z, and its
+// twiddle fragments in registers. Both kernels are persistent (one
 // workgroup per resident slot, planes strided by the grid), so the rows of
-// the next plane are in flight while the current one is multiplied.
+// the next rounds or plane are in flight while the current one is
+// multiplied; the forward keeps three rounds in a register ring.
 //
-// Precision. fp16 x is exact as an MFMA operand; bf16 x is scaled per row by
-// a power of two into fp16 range, which is exact for every element within
-// 2^28 of the row's largest (bf16 has fewer mantissa bits than fp16). R, Z
-// and the spectra are rounded to fp16 after a power-of-two scale derived from
-// a bound (the round's largest |x| times W, or the plane's largest |Y| times
-// 4 m1), which keeps every fp16 operand below 2^15 and far above the
-// subnormal range; every scale is undone in fp32. Twiddles are rounded to
-// fp16.
+// Precision. fp16 x is exact as an MFMA operand; bf16 and fp32 x are scaled
+// by one power of two per 64-row round into fp16 range (fp32 as an fp16 hi
+// part and an fp16 remainder), which keeps every element within 2^28 of the
+// round's largest exact (bf16) or to about 22 bits (fp32); smaller ones add
+// negligibly to any output. R, Z and the spectra are rounded to fp16 (fp32
+// planes: hi + lo) after a power-of-two scale derived from a bound (the
+// round's largest |x| times W, or the plane's largest |Y| times 4 m1), which
+// keeps every fp16 operand below 2^15 and far above the subnormal range;
+// every scale is undone in fp32. Twiddles are rounded to fp16 (fp32 planes:
+// hi + lo).
 //
 // One fragment of v_mfma_f32_16x16x32 (A: 16 x 32, B: 32 x 16): lane l holds
 // row / column l % 16 and the eight consecutive k = 8 (l / 16) .. +7;
@@ -115,7 +117,7 @@ __device__ __forceinline__ float pow2f(int e) {
 
 // ------------------------------------------------------------------ forward
 
-constexpr int kFT = 256;  // threads per workgroup of both plane kernels (4 waves)
+constexpr int kFT = 256;  // threads per workgroup of the inverse plane kernel (4 waves)
 
 // Storage policy: fp32 planes are carried as fp16 hi + lo parts (two
 // operands, three products per pair, hi*hi + hi*lo + lo*hi); fp16 and bf16
@@ -196,8 +198,10 @@ __device__ __forceinline__ void fwd_fetch(const void *x, int g, int lgr, int H, 
   const int r = g & ((1 << lgr) - 1);
   const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(x) + plane * H * IO::W * MxPol<DT>::ES) +
                      (size_t)r * kRows * IO::UR + tid;
+  // x is read once: non-temporal loads keep it from displacing the
+  // spectra and tables the next kernels read from the caches
 #pragma unroll
-  for (int v = 0; v < IO::FU; ++v) p[v] = src[v * IO::NT];
+  for (int v = 0; v < IO::FU; ++v) p[v] = __builtin_nontemporal_load(src + v * IO::NT);
 }
 
 // eight bf16 -> eight fp16 times 2^sig (exact while the result is normal)
@@ -618,8 +622,8 @@ __device__ __forceinline__ void inv_load(const float2 *in, size_t plane, int K, 
 }
 
 // Persistent: workgroup b transforms planes b, b + gridDim.x, ...; the
-// spectra of the next plane load while the current one is transformed. Per
-// round of 64 output rows:
+// spectra of the next plane are requested before the current plane's last
+// round. Per round of 64 output rows:
 //  1. phase-rotate the spectra by the round offset, scale, fp16 into LDS;
 //  2. Z = E' Y (two m-tiles of rows per wave), fp16 into LDS;
 //  3. y^T[w][h] = sum_c T'[c][w] Z[h][c] with the twiddles as the
@@ -811,12 +815,13 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(SM ? 3 : 2)
       }
       __syncthreads();
 
-      // 4. 64 rows x W elements: coalesced 16-byte stores
+      // 4. 64 rows x W elements: coalesced 16-byte stores, non-temporal (y
+      // is not read again here; it should not displace cached spectra)
 #pragma unroll
       for (int v = 0; v < FU; ++v) {
         const int e2 = v * kFT + tid;
         const int row = e2 / UR, cu = e2 - row * UR;
-        yp[(size_t)r * kRows * UR + e2] = ostage[row * OP + cu];
+        __builtin_nontemporal_store(ostage[row * OP + cu], yp + (size_t)r * kRows * UR + e2);
       }
     };
     for (int r = 0; r + 1 < rounds; ++r) round(r);
