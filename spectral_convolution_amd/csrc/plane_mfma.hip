@@ -76,11 +76,6 @@ __device__ __forceinline__ u16x2 absmax_acc(u16x2 m, u32x4 v) {
   return m;
 }
 
-__device__ __forceinline__ uint32_t absmax_bits(u32x4 v) {
-  const u16x2 m = absmax_acc(u16x2{0, 0}, v);
-  return max((uint32_t)m.x, (uint32_t)m.y);
-}
-
 // maximum over the 16 lanes of each DPP row, in every lane of the row:
 // exchanges with lane ^ 1, lane ^ 2 (quad permutes), then the mirrored lane
 // of the half row and of the row (every source lane exists, so the bound
@@ -128,15 +123,6 @@ struct MxPol {
   static constexpr int NP = SP ? 2 : 1;     // fp16 parts per operand
   static constexpr int ES = SP ? 4 : 2;     // storage bytes per element
 };
-
-__device__ __forceinline__ v4f mma_sp(const u32x4 (&a)[2], const u32x4 (&b)[2], v4f c, bool sp) {
-  c = mma(a[0], b[0], c);
-  if (sp) {
-    c = mma(a[0], b[1], c);
-    c = mma(a[1], b[0], c);
-  }
-  return c;
-}
 
 // Accumulator chains: a dependent MFMA waits for its predecessor's result,
 // so products are spread over independent accumulators (hi*hi and the two

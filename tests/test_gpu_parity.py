@@ -124,6 +124,28 @@ def test_parity_full_size_sampled(case):
     assert np.isfinite(got).all()
 
 
+# many planes per persistent workgroup: the forward's register ring and the
+# inverse's spectra prefetch cross plane boundaries many times
+MANY = [("many-f16-64", _cfg("r", 2, 8, 96, 80, (64, 64), (20, 11), "uniform"), "f16", (0, 7)),
+        ("many-bf16-128", _cfg("r", 2, 4, 70, 90, (128, 128), (9, 24), "uniform"), "bf16", (1, 3)),
+        ("many-f32-64x128", _cfg("r", 2, 6, 64, 64, (64, 128), (16, 16), "uniform"), "f32", (0, 5))]
+
+
+@pytest.mark.parametrize("case", MANY, ids=[c[0] for c in MANY])
+def test_parity_many_planes(case):
+    name, cfg, dtype, samples = case
+    print(f"[parity-many] {name} dtype={dtype} B={cfg.batch} Ci={cfg.c_in} Co={cfg.c_out}", flush=True)
+    inp = wl.layer_inputs(cfg, dtype)
+    got, _ = run_layer(cfg.ndim, cfg.batch, cfg.c_in, cfg.c_out, cfg.grid, cfg.modes, dtype,
+                       inp["x"], inp["w"])
+    idx = list(samples)
+    ref = _oracle(cfg, inp["x64"][idx], inp["w64"])
+    err = rel_l2(got[idx], ref)
+    print(f"[parity-many] {name} rel_l2={err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+    assert np.isfinite(got).all()
+
+
 def test_intermediate_spectra():
     cfg = _cfg("s", 2, 2, 3, 4, (64, 128), (6, 11), "uniform")
     inp = wl.layer_inputs(cfg, "f32")
