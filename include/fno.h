@@ -32,8 +32,9 @@
  *
  * Ownership. The caller owns x, w and y and keeps them alive until the work
  * queued on `stream` has finished. The plan owns its twiddle tables and its
- * spectra workspace (allocated by fno_plan_create, freed by
- * fno_plan_destroy). Execution calls allocate nothing.
+ * spectra workspace and a buffer for the conjugate-transposed weights of the
+ * backward pass (allocated by fno_plan_create, freed by fno_plan_destroy).
+ * Execution calls allocate nothing.
  *
  * Execution calls are asynchronous on `stream` (a hipStream_t; NULL is the
  * null stream) and return as soon as the kernels are queued. One plan runs
@@ -92,6 +93,41 @@ fno_status_t fno_spectral_conv2d(fno_plan_t plan, const void *x, const void *w,
 /* One 3D layer (3D plan only); as fno_spectral_conv2d. */
 fno_status_t fno_spectral_conv3d(fno_plan_t plan, const void *x, const void *w,
                                  void *y, void *stream);
+
+/* ---- backward pass -------------------------------------------------------
+ * Gradients of a scalar loss L through the layer (TurboFNO write-up,
+ * section 4.3: the layer is a PyTorch autograd Function, so its backward
+ * returns dL/dx and dL/dw given dL/dy). The layer is linear in x and in w,
+ * so, with Gh[b][o][k] = forward spectra of grad_y (scaled as in the
+ * forward) and Xh those of x:
+ *   grad_x = the layer applied to grad_y with every mode's weight matrix
+ *            replaced by its conjugate transpose (c_out -> c_in channels);
+ *   grad_w[k][i][o] = prod(grid) * gamma_k * sum_b conj(Xh[b][i][k]) Gh[b][o][k],
+ *            gamma_k = 1 when the last-axis mode index of k is 0, else 2.
+ * A complex weight's gradient is dL/dRe(w) + i dL/dIm(w) (the PyTorch
+ * convention); these equal PyTorch autograd through rfft2 -> einsum ->
+ * irfft2.
+ *   x      [B][Ci][grid] as in the forward; needed only for grad_w
+ *   w      as in the forward; needed only for grad_x
+ *   grad_y [B][Co][grid], dL/dy
+ *   grad_x [B][Ci][grid] out, or NULL to skip
+ *   grad_w same layout as w, out, or NULL to skip
+ * All in the plan's dtype (gradients are rounded to it from fp32), 16-byte
+ * aligned; outputs must not overlap any other argument. INVALID_ARG when
+ * both outputs are NULL or an input an output needs is NULL, or on a plan of
+ * the other ndim. Uses the plan's workspace (one call in flight per plan,
+ * forward or backward); asynchronous on `stream`; allocates nothing. */
+fno_status_t fno_spectral_conv2d_backward(fno_plan_t plan, const void *x,
+                                          const void *w, const void *grad_y,
+                                          void *grad_x, void *grad_w,
+                                          void *stream);
+
+/* 3D backward (3D plan only); as fno_spectral_conv2d_backward with the 3D
+ * layouts and gamma taken from the kz index. */
+fno_status_t fno_spectral_conv3d_backward(fno_plan_t plan, const void *x,
+                                          const void *w, const void *grad_y,
+                                          void *grad_x, void *grad_w,
+                                          void *stream);
 
 /* Free the plan's device memory after synchronising its device.
  * fno_plan_destroy(NULL) returns FNO_OK. Destroying a plan twice is

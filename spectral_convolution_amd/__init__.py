@@ -14,7 +14,7 @@ __all__ = [
     "fno_plan_create", "fno_spectral_conv2d", "fno_spectral_conv3d",
     "fno_plan_destroy", "fno_status_string", "fno_plan_workspace_bytes",
     "fno_plan_num_launches", "fno_plan_launch_name", "fno_plan_run_launch",
-    "fno_plan_spectra", "SpectralConv", "FnoError", "DTYPES",
+    "fno_plan_spectra", "fno_spectral_conv2d_backward", "fno_spectral_conv3d_backward", "SpectralConv", "FnoError", "DTYPES",
     "fno_channel_mix", "fno_projection", "fno_model2d_create", "fno_model2d_forward",
     "fno_model2d_destroy", "Model2d",
 ]
@@ -112,6 +112,38 @@ def fno_spectral_conv3d(plan, x, w, y, stream=None):
     _check_tensors(plan, x, w, y)
     check(lib().fno_spectral_conv3d(plan.handle, _ptr(x), _ptr(w), _ptr(y),
                                     _stream(stream, plan.device)), "fno_spectral_conv3d")
+
+
+def _check_backward(plan, x, w, gy, gx, gw):
+    import torch
+    td = _torch_dtype(plan.dtype)
+    for name, t, shape in (("x", x, plan.x_shape()), ("w", w, plan.w_shape()),
+                           ("grad_y", gy, plan.y_shape()), ("grad_x", gx, plan.x_shape()),
+                           ("grad_w", gw, plan.w_shape())):
+        if t is None or isinstance(t, int):
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor, a device pointer or None")
+        if t.dtype != td:
+            raise ValueError(f"{name} dtype {t.dtype} != plan dtype {td}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {tuple(shape)}")
+
+
+def fno_spectral_conv2d_backward(plan, x, w, grad_y, grad_x, grad_w, stream=None):
+    """Gradients of the 2D layer (see include/fno.h); grad_x or grad_w may be None."""
+    _check_backward(plan, x, w, grad_y, grad_x, grad_w)
+    check(lib().fno_spectral_conv2d_backward(plan.handle, _ptr(x), _ptr(w), _ptr(grad_y), _ptr(grad_x),
+                                             _ptr(grad_w), _stream(stream, plan.device)),
+          "fno_spectral_conv2d_backward")
+
+
+def fno_spectral_conv3d_backward(plan, x, w, grad_y, grad_x, grad_w, stream=None):
+    """Gradients of the 3D layer; as fno_spectral_conv2d_backward."""
+    _check_backward(plan, x, w, grad_y, grad_x, grad_w)
+    check(lib().fno_spectral_conv3d_backward(plan.handle, _ptr(x), _ptr(w), _ptr(grad_y), _ptr(grad_x),
+                                             _ptr(grad_w), _stream(stream, plan.device)),
+          "fno_spectral_conv3d_backward")
 
 
 def fno_plan_destroy(plan):

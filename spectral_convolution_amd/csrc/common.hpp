@@ -132,6 +132,17 @@ struct ContractArgs {
   int B, Ci, Co, K;
 };
 
+// Weight gradient: dw[k][i][o] = scale * gamma(k) * sum_b conj(xs[b][i][k])
+// gs[b][o][k], gamma(k) = 1 when k % mlast == 0 (last-axis mode index 0),
+// else 2.
+struct GradWArgs {
+  const float2 *xs;  // [B][Ci][K]
+  const float2 *gs;  // [B][Co][K]
+  void *dw;          // [K][Ci][Co][2] storage dtype
+  int B, Ci, Co, K, mlast;
+  float scale;
+};
+
 // host launchers (defined next to their kernels)
 int plane_rpt(int MP, int PW);
 int plane_rc(int H, int MP);
@@ -163,6 +174,13 @@ long contract_mx_workgroups(int B, int Co, int K);
 size_t contract_mx_lds_bytes(int dtype, int B);
 hipError_t contract_mx_prepare(int dtype, int B);
 hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s);
+
+hipError_t launch_conj_transpose(const void *w, void *wh, int K, int Ci, int Co, int dtype, hipStream_t s);
+int gradw_pick_ib(int B, int Ci, int Co, int K);
+int gradw_pick_split(int B, int Ci, int Co, int K, int ib);
+size_t gradw_lds_bytes(int ib, int S);
+hipError_t gradw_prepare(int ib, int dtype, size_t lds);
+hipError_t launch_grad_w(const GradWArgs &a, int ib, int S, int dtype, hipStream_t s);
 
 hipError_t launch_channel_mix(const void *x, const void *A, const void *bias, const void *add, void *y, int B,
                               int I, int O, long P, int act, int dtype, hipStream_t s);

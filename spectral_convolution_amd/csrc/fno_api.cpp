@@ -9,11 +9,18 @@
 //   fno_fwd_plane(slabs) -> fno_fwd_axis(X) -> fno_contract ->
 //   fno_inv_axis(X) -> fno_inv_plane(slabs)
 // Spectra between launches live in the plan's workspace (complex fp32).
+//
+// The backward pass (gradients of x and w from g = dL/dy) reuses the same
+// kernels: dx is the layer applied to g with every mode's weight replaced by
+// its conjugate transpose (fno_conj_transpose, then forward planes of g,
+// the contraction from Co to Ci channels, inverse planes); dw is a per-mode
+// reduction over the batch of conj(forward(x)) * forward(g) (fno_grad_w).
 
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -199,6 +206,15 @@ struct fno_plan_s {
   size_t lds_axis = 0;
   int bb = 1, split = 1;
   bool cmx = false;  // fp16 / bf16 contraction on bf16 matrix cores
+  // backward: the adjoint contraction (Co -> Ci channels), the weight
+  // gradient, plane transforms over the other channel count (forward of g
+  // over Co channels, inverse over Ci)
+  int bb_a = 1, split_a = 1, gw_ib = 1, gw_split = 1;
+  bool cmx_a = false;
+  int ppw_fg = 1, ppw_ib = 1;
+  size_t lds_fg = 0, lds_ib = 0;
+  int mx_grid_fg = 0, mx_grid_ib = 0;
+  void *wh = nullptr;  // conjugate-transposed weights [K][Co][Ci][2], storage dtype
   // row stage on MFMA (fp16 / bf16 storage, planes with H >= 64, W >= 64)
   bool mx = false;
   int mx_nt = 0, mx_mt = 0, mx_nn = 0, mx_kb1 = 0, mx_lgW = 0, mx_lg4m1 = 0, mx_grid_f = 0, mx_grid_i = 0;
@@ -298,6 +314,17 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
   // 256 compute units it leaves most of the chip idle, and the per-mode
   // kernel (one wave per 16 modes, channels split over waves) is faster.
   p.cmx = contract_mx_supported((int)dtype, c_out, p.K) && contract_mx_workgroups(batch, c_out, p.K) >= 256;
+  p.bb_a = contract_pick_bb(batch, c_in, p.K);
+  p.split_a = contract_pick_split(batch, c_out, c_in, p.K, p.bb_a);
+  p.cmx_a = contract_mx_supported((int)dtype, c_in, p.K) && contract_mx_workgroups(batch, c_in, p.K) >= 256;
+  p.gw_ib = gradw_pick_ib(batch, c_in, c_out, p.K);
+  p.gw_split = gradw_pick_split(batch, c_in, c_out, p.K, p.gw_ib);
+  if ((c_in + 4 * p.gw_ib - 1) / (4 * p.gw_ib) > 65535 || (c_out + 15) / 16 > 65535) return FNO_ERR_UNSUPPORTED;
+  p.ppw_fg = plane_ppw(true, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_i);
+  p.ppw_ib = plane_ppw(false, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_f);
+  p.lds_fg = p.mx ? p.lds_fwd : plane_fwd_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP, p.ppw_fg);
+  p.lds_ib = p.mx ? p.lds_inv : plane_inv_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP, p.ppw_ib);
+  if (p.lds_fg > kMaxLds || p.lds_ib > kMaxLds) return FNO_ERR_UNSUPPORTED;
   if (ndim == 2) {
     p.launches = {L_FWD_PLANE, L_CONTRACT, L_INV_PLANE};
   } else {
@@ -392,6 +419,7 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   const size_t o_xh = off; off += al(n_xh * sizeof(float2));
   const size_t o_yh = off; off += al(n_yh * sizeof(float2));
   const size_t o_t = off; off += al(n_t * sizeof(float2));
+  const size_t o_wh = off; off += al((size_t)p->K * p->Ci * p->Co * 2 * (p->dtype == FNO_F32 ? 4 : 2));
   std::vector<uint16_t> tfh, tfl, tbh, tbl, efh, efl, eih, eil;
   if (p->mx) {
     const bool sp = p->dtype == FNO_F32;
@@ -427,6 +455,7 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   p->xh = (float2 *)(base + o_xh);
   p->yh = (float2 *)(base + o_yh);
   p->tbuf = n_t ? (float2 *)(base + o_t) : nullptr;
+  p->wh = base + o_wh;
   uint4 *tab_ptr[8] = {};
   for (int t = 0; t < 8; ++t) tab_ptr[t] = tabs[t]->empty() ? nullptr : (uint4 *)(base + o_tab[t]);
   p->tf = tab_ptr[0];
@@ -456,13 +485,27 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
     if (e == hipSuccess)
       e = mx_grid(false, p->pW, p->pm1, p->pm2, p->dtype, p->lds_inv, p->device, p->B * p->Co * (ndim == 3 ? p->xN : 1),
                   &p->mx_grid_i);
+    if (e == hipSuccess)
+      e = mx_grid(true, p->pW, p->pm1, p->pm2, p->dtype, p->lds_fwd, p->device, p->B * p->Co * (ndim == 3 ? p->xN : 1),
+                  &p->mx_grid_fg);
+    if (e == hipSuccess)
+      e = mx_grid(false, p->pW, p->pm1, p->pm2, p->dtype, p->lds_inv, p->device, p->B * p->Ci * (ndim == 3 ? p->xN : 1),
+                  &p->mx_grid_ib);
   } else {
-    if (e == hipSuccess) e = plane_prepare(true, p->pMP, p->rpt, p->dtype, p->lds_fwd);
-    if (e == hipSuccess) e = plane_prepare(false, p->pMP, p->rpt, p->dtype, p->lds_inv);
+    // one kernel serves both channel counts: allow the larger LDS of the two
+    if (e == hipSuccess) e = plane_prepare(true, p->pMP, p->rpt, p->dtype, std::max(p->lds_fwd, p->lds_fg));
+    if (e == hipSuccess) e = plane_prepare(false, p->pMP, p->rpt, p->dtype, std::max(p->lds_inv, p->lds_ib));
   }
   if (e == hipSuccess && ndim == 3) e = axis_fwd_prepare(p->xMP, p->lds_axis);
+  // the forward and the adjoint contraction may be one kernel: every
+  // non-matrix-core variant is allowed the larger LDS of the two
+  const size_t lds_c = std::max(p->cmx ? 0 : contract_lds_bytes(p->bb, p->split),
+                                p->cmx_a ? 0 : contract_lds_bytes(p->bb_a, p->split_a));
+  if (e == hipSuccess) e = p->cmx ? contract_mx_prepare(p->dtype, p->B) : contract_prepare(p->bb, p->dtype, p->Co, lds_c);
   if (e == hipSuccess)
-    e = p->cmx ? contract_mx_prepare(p->dtype, p->B) : contract_prepare(p->bb, p->dtype, p->Co, contract_lds_bytes(p->bb, p->split));
+    e = p->cmx_a ? contract_mx_prepare(p->dtype, p->B) : contract_prepare(p->bb_a, p->dtype, p->Ci, lds_c);
+  // every tile choice needs at most 64 KiB; the cap is per kernel, shared by all plans
+  if (e == hipSuccess) e = gradw_prepare(p->gw_ib, p->dtype, 64 * 1024);
   if (e != hipSuccess) {
     (void)hipFree(p->mem);
     delete p;
@@ -494,120 +537,145 @@ static fno_status_t check_exec(fno_plan_t p, int ndim, const void *x, const void
   return FNO_OK;
 }
 
-static hipError_t run_one(fno_plan_t p, int kind, const void *x, const void *w, void *y, hipStream_t s) {
+// Launch helpers, parameterised by source, channel count and destination so
+// the forward and the backward pass share them. nchan is Ci or Co; the
+// persistent grid and planes-per-workgroup were sized for that count.
+
+// plane transforms of `nchan` channels: 2D x -> spectra dst; 3D slabs -> tbuf
+static hipError_t fwd_plane_launch(fno_plan_t p, const void *x, int nchan, float2 *dst, hipStream_t s) {
   const int nd = p->ndim;
+  const bool own = nchan == p->Ci;
+  if (p->mx) {
+    PlaneMxFwdArgs m;
+    m.x = x;
+    m.out = nd == 2 ? dst : p->tbuf;
+    m.tw_h = p->tw_h;
+    m.tf = p->tf;
+    m.tf_lo = p->tf_lo;
+    m.ef = p->ef_f;
+    m.ef_lo = p->ef_f_lo;
+    m.nplanes = p->B * nchan * (nd == 3 ? p->xN : 1);
+    m.H = p->pH;
+    m.W = p->pW;
+    m.m1 = p->pm1;
+    m.m2 = p->pm2;
+    m.nt = p->mx_nt;
+    m.mt = p->mx_mt;
+    m.nn = p->mx_nn;
+    m.lgW = p->mx_lgW;
+    m.scale = nd == 2 ? 1.0f / ((float)p->pH * (float)p->pW) : 1.0f;
+    return launch_plane_mx_fwd(m, own ? p->mx_grid_f : p->mx_grid_fg, p->dtype, p->lds_fwd, s);
+  }
+  PlaneFwdArgs a;
+  a.x = x;
+  a.out = nd == 2 ? dst : p->tbuf;
+  a.tw_h = p->tw_h;
+  a.tw_w = p->tw_w;
+  a.nplanes = p->B * nchan * (nd == 3 ? p->xN : 1);
+  a.H = p->pH;
+  a.W = p->pW;
+  a.m1 = p->pm1;
+  a.m2 = p->pm2;
+  a.PH = p->pH / p->pMP;
+  a.PW = p->pW / p->pMP;
+  a.ppw = own ? p->ppw_f : p->ppw_fg;
+  a.rc = p->rc;
+  a.scale = nd == 2 ? 1.0f / ((float)p->pH * (float)p->pW) : 1.0f;
+  return launch_plane_fwd(a, p->pMP, p->rpt, p->dtype, own ? p->lds_fwd : p->lds_fg, s);
+}
+
+// 3D outer axis, forward: tbuf ([B nchan][X][C]) -> spectra dst, scaled 1/N
+static hipError_t fwd_axis_launch(fno_plan_t p, int nchan, float2 *dst, hipStream_t s) {
+  AxisArgs a;
+  a.in = p->tbuf;
+  a.out = dst;
+  a.tw = p->tw_x;
+  a.nvol = p->B * nchan;
+  a.N = p->xN;
+  a.m = p->xm;
+  a.P = p->xN / p->xMP;
+  a.C = 2 * p->modes[1] * p->modes[2];
+  a.scale = 1.0f / ((float)p->grid[0] * (float)p->grid[1] * (float)p->grid[2]);
+  return launch_axis_fwd(a, p->xMP, p->lds_axis, s);
+}
+
+// contraction: forward (Ci -> Co with w) or adjoint (Co -> Ci with W^H)
+static hipError_t contract_launch(fno_plan_t p, const float2 *in, const void *w, float2 *out, bool adjoint,
+                                  hipStream_t s) {
+  ContractArgs a;
+  a.xh = in;
+  a.w = w;
+  a.yh = out;
+  a.B = p->B;
+  a.Ci = adjoint ? p->Co : p->Ci;
+  a.Co = adjoint ? p->Ci : p->Co;
+  a.K = p->K;
+  if (adjoint)
+    return p->cmx_a ? launch_contract_mx(a, p->dtype, s) : launch_contract(a, p->bb_a, p->split_a, p->dtype, s);
+  return p->cmx ? launch_contract_mx(a, p->dtype, s) : launch_contract(a, p->bb, p->split, p->dtype, s);
+}
+
+// 3D outer axis, inverse: spectra src ([B nchan][K]) -> tbuf
+static hipError_t inv_axis_launch(fno_plan_t p, const float2 *src, int nchan, hipStream_t s) {
+  AxisArgs a;
+  a.in = src;
+  a.out = p->tbuf;
+  a.tw = p->tw_x;
+  a.nvol = p->B * nchan;
+  a.N = p->xN;
+  a.m = p->xm;
+  a.P = p->xN / p->xMP;
+  a.C = 2 * p->modes[1] * p->modes[2];
+  a.scale = 1.0f;
+  return launch_axis_inv(a, p->xMP, s);
+}
+
+// inverse plane transforms of `nchan` channels: 2D spectra src -> y; 3D tbuf -> y
+static hipError_t inv_plane_launch(fno_plan_t p, const float2 *src, int nchan, void *y, hipStream_t s) {
+  const int nd = p->ndim;
+  const bool own = nchan == p->Co;
+  if (p->mx) {
+    PlaneMxInvArgs m;
+    m.in = nd == 2 ? src : p->tbuf;
+    m.y = y;
+    m.tw_h = p->tw_h;
+    m.tb = p->tb;
+    m.tb_lo = p->tb_lo;
+    m.ef = p->ef_i;
+    m.ef_lo = p->ef_i_lo;
+    m.nplanes = p->B * nchan * (nd == 3 ? p->xN : 1);
+    m.H = p->pH;
+    m.W = p->pW;
+    m.m1 = p->pm1;
+    m.m2 = p->pm2;
+    m.nn = p->mx_nn;
+    m.kb1 = p->mx_kb1;
+    m.lg4m1 = p->mx_lg4m1;
+    return launch_plane_mx_inv(m, own ? p->mx_grid_i : p->mx_grid_ib, p->dtype, p->lds_inv, s);
+  }
+  PlaneInvArgs a;
+  a.in = nd == 2 ? src : p->tbuf;
+  a.y = y;
+  a.tw_h = p->tw_h;
+  a.tw_w = p->tw_w;
+  a.nplanes = p->B * nchan * (nd == 3 ? p->xN : 1);
+  a.H = p->pH;
+  a.W = p->pW;
+  a.m1 = p->pm1;
+  a.m2 = p->pm2;
+  a.PH = p->pH / p->pMP;
+  a.PW = p->pW / p->pMP;
+  a.ppw = own ? p->ppw_i : p->ppw_ib;
+  return launch_plane_inv(a, p->pMP, p->rpt, p->dtype, own ? p->lds_inv : p->lds_ib, s);
+}
+
+static hipError_t run_one(fno_plan_t p, int kind, const void *x, const void *w, void *y, hipStream_t s) {
   switch (kind) {
-    case L_FWD_PLANE: {
-      if (p->mx) {
-        PlaneMxFwdArgs m;
-        m.x = x;
-        m.out = nd == 2 ? p->xh : p->tbuf;
-        m.tw_h = p->tw_h;
-        m.tf = p->tf;
-        m.tf_lo = p->tf_lo;
-        m.ef = p->ef_f;
-        m.ef_lo = p->ef_f_lo;
-        m.nplanes = p->B * p->Ci * (nd == 3 ? p->xN : 1);
-        m.H = p->pH;
-        m.W = p->pW;
-        m.m1 = p->pm1;
-        m.m2 = p->pm2;
-        m.nt = p->mx_nt;
-        m.mt = p->mx_mt;
-        m.nn = p->mx_nn;
-        m.lgW = p->mx_lgW;
-        m.scale = nd == 2 ? 1.0f / ((float)p->pH * (float)p->pW) : 1.0f;
-        return launch_plane_mx_fwd(m, p->mx_grid_f, p->dtype, p->lds_fwd, s);
-      }
-      PlaneFwdArgs a;
-      a.x = x;
-      a.out = nd == 2 ? p->xh : p->tbuf;
-      a.tw_h = p->tw_h;
-      a.tw_w = p->tw_w;
-      a.nplanes = p->B * p->Ci * (nd == 3 ? p->xN : 1);
-      a.H = p->pH;
-      a.W = p->pW;
-      a.m1 = p->pm1;
-      a.m2 = p->pm2;
-      a.PH = p->pH / p->pMP;
-      a.PW = p->pW / p->pMP;
-      a.ppw = p->ppw_f;
-      a.rc = p->rc;
-      a.scale = nd == 2 ? 1.0f / ((float)p->pH * (float)p->pW) : 1.0f;
-      return launch_plane_fwd(a, p->pMP, p->rpt, p->dtype, p->lds_fwd, s);
-    }
-    case L_FWD_AXIS: {
-      AxisArgs a;
-      a.in = p->tbuf;
-      a.out = p->xh;
-      a.tw = p->tw_x;
-      a.nvol = p->B * p->Ci;
-      a.N = p->xN;
-      a.m = p->xm;
-      a.P = p->xN / p->xMP;
-      a.C = 2 * p->modes[1] * p->modes[2];
-      a.scale = 1.0f / ((float)p->grid[0] * (float)p->grid[1] * (float)p->grid[2]);
-      return launch_axis_fwd(a, p->xMP, p->lds_axis, s);
-    }
-    case L_CONTRACT: {
-      ContractArgs a;
-      a.xh = p->xh;
-      a.w = w;
-      a.yh = p->yh;
-      a.B = p->B;
-      a.Ci = p->Ci;
-      a.Co = p->Co;
-      a.K = p->K;
-      return p->cmx ? launch_contract_mx(a, p->dtype, s) : launch_contract(a, p->bb, p->split, p->dtype, s);
-    }
-    case L_INV_AXIS: {
-      AxisArgs a;
-      a.in = p->yh;
-      a.out = p->tbuf;
-      a.tw = p->tw_x;
-      a.nvol = p->B * p->Co;
-      a.N = p->xN;
-      a.m = p->xm;
-      a.P = p->xN / p->xMP;
-      a.C = 2 * p->modes[1] * p->modes[2];
-      a.scale = 1.0f;
-      return launch_axis_inv(a, p->xMP, s);
-    }
-    case L_INV_PLANE: {
-      if (p->mx) {
-        PlaneMxInvArgs m;
-        m.in = nd == 2 ? p->yh : p->tbuf;
-        m.y = y;
-        m.tw_h = p->tw_h;
-        m.tb = p->tb;
-        m.tb_lo = p->tb_lo;
-        m.ef = p->ef_i;
-        m.ef_lo = p->ef_i_lo;
-        m.nplanes = p->B * p->Co * (nd == 3 ? p->xN : 1);
-        m.H = p->pH;
-        m.W = p->pW;
-        m.m1 = p->pm1;
-        m.m2 = p->pm2;
-        m.nn = p->mx_nn;
-        m.kb1 = p->mx_kb1;
-        m.lg4m1 = p->mx_lg4m1;
-        return launch_plane_mx_inv(m, p->mx_grid_i, p->dtype, p->lds_inv, s);
-      }
-      PlaneInvArgs a;
-      a.in = nd == 2 ? p->yh : p->tbuf;
-      a.y = y;
-      a.tw_h = p->tw_h;
-      a.tw_w = p->tw_w;
-      a.nplanes = p->B * p->Co * (nd == 3 ? p->xN : 1);
-      a.H = p->pH;
-      a.W = p->pW;
-      a.m1 = p->pm1;
-      a.m2 = p->pm2;
-      a.PH = p->pH / p->pMP;
-      a.PW = p->pW / p->pMP;
-      a.ppw = p->ppw_i;
-      return launch_plane_inv(a, p->pMP, p->rpt, p->dtype, p->lds_inv, s);
-    }
+    case L_FWD_PLANE: return fwd_plane_launch(p, x, p->Ci, p->xh, s);
+    case L_FWD_AXIS: return fwd_axis_launch(p, p->Ci, p->xh, s);
+    case L_CONTRACT: return contract_launch(p, p->xh, w, p->yh, false, s);
+    case L_INV_AXIS: return inv_axis_launch(p, p->yh, p->Co, s);
+    case L_INV_PLANE: return inv_plane_launch(p, p->yh, p->Co, y, s);
   }
   return hipErrorInvalidValue;
 }
@@ -638,6 +706,61 @@ static fno_status_t exec(fno_plan_t p, int ndim, const void *x, const void *w, v
   return FNO_OK;
 }
 
+// Gradients: every launch is stream-ordered on `stream`; the spectra
+// workspace holds forward(x) and forward(g), then the adjoint-contracted
+// spectra; wh holds W^H.
+static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const void *w, const void *gy, void *gx,
+                                  void *gw, void *stream) {
+  if (!p || p->ndim != ndim) return FNO_ERR_INVALID_ARG;
+  if (!gy || (!gx && !gw)) return FNO_ERR_INVALID_ARG;
+  if ((gw && !x) || (gx && !w)) return FNO_ERR_INVALID_ARG;
+  if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)gy | (uintptr_t)gx | (uintptr_t)gw) & 15) return FNO_ERR_INVALID_ARG;
+  size_t pts = 1;
+  for (int d = 0; d < p->ndim; ++d) pts *= (size_t)p->grid[d];
+  const size_t es = elem_bytes(p->dtype);
+  const size_t nx = (size_t)p->B * p->Ci * pts * es, ny = (size_t)p->B * p->Co * pts * es;
+  const size_t nw = (size_t)p->K * p->Ci * p->Co * 2 * es;
+  if (gx && (overlap(gx, nx, gy, ny) || (x && overlap(gx, nx, x, nx)) || overlap(gx, nx, w, nw)))
+    return FNO_ERR_INVALID_ARG;
+  if (gw && (overlap(gw, nw, gy, ny) || overlap(gw, nw, x, nx) || (w && overlap(gw, nw, w, nw)) ||
+             (gx && overlap(gw, nw, gx, nx))))
+    return FNO_ERR_INVALID_ARG;
+  DeviceGuard g(p->device);
+  if (g.err != hipSuccess) return FNO_ERR_DEVICE;
+  hipStream_t s = (hipStream_t)stream;
+  const bool d3 = ndim == 3;
+  hipError_t e = hipSuccess;
+  auto step = [&](hipError_t r) {
+    if (e == hipSuccess) e = r == hipSuccess ? hipGetLastError() : r;
+  };
+  if (gw) {
+    step(fwd_plane_launch(p, x, p->Ci, p->xh, s));
+    if (d3 && e == hipSuccess) step(fwd_axis_launch(p, p->Ci, p->xh, s));
+  }
+  if (e == hipSuccess) step(fwd_plane_launch(p, gy, p->Co, p->yh, s));
+  if (d3 && e == hipSuccess) step(fwd_axis_launch(p, p->Co, p->yh, s));
+  if (gw && e == hipSuccess) {
+    GradWArgs a;
+    a.xs = p->xh;
+    a.gs = p->yh;
+    a.dw = gw;
+    a.B = p->B;
+    a.Ci = p->Ci;
+    a.Co = p->Co;
+    a.K = p->K;
+    a.mlast = p->modes[ndim - 1];
+    a.scale = (float)pts;
+    step(launch_grad_w(a, p->gw_ib, p->gw_split, p->dtype, s));
+  }
+  if (gx) {
+    if (e == hipSuccess) step(launch_conj_transpose(w, p->wh, p->K, p->Ci, p->Co, p->dtype, s));
+    if (e == hipSuccess) step(contract_launch(p, p->yh, p->wh, p->xh, true, s));
+    if (d3 && e == hipSuccess) step(inv_axis_launch(p, p->xh, p->Ci, s));
+    if (e == hipSuccess) step(inv_plane_launch(p, p->xh, p->Ci, gx, s));
+  }
+  return map_err(e);
+}
+
 extern "C" {
 
 fno_status_t fno_spectral_conv2d(fno_plan_t plan, const void *x, const void *w, void *y, void *stream) {
@@ -646,6 +769,16 @@ fno_status_t fno_spectral_conv2d(fno_plan_t plan, const void *x, const void *w, 
 
 fno_status_t fno_spectral_conv3d(fno_plan_t plan, const void *x, const void *w, void *y, void *stream) {
   return exec(plan, 3, x, w, y, stream, -1);
+}
+
+fno_status_t fno_spectral_conv2d_backward(fno_plan_t plan, const void *x, const void *w, const void *grad_y,
+                                          void *grad_x, void *grad_w, void *stream) {
+  return exec_backward(plan, 2, x, w, grad_y, grad_x, grad_w, stream);
+}
+
+fno_status_t fno_spectral_conv3d_backward(fno_plan_t plan, const void *x, const void *w, const void *grad_y,
+                                          void *grad_x, void *grad_w, void *stream) {
+  return exec_backward(plan, 3, x, w, grad_y, grad_x, grad_w, stream);
 }
 
 fno_status_t fno_plan_workspace_bytes(fno_plan_t plan, size_t *bytes) {

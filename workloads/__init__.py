@@ -12,6 +12,7 @@ from .generate import (  # noqa: F401
     bf16_bits_to_float64,
     complex_to_interleaved,
     gaussian_random_field,
+    layer_grad_output,
     layer_inputs,
     model_inputs,
     round_to_storage,

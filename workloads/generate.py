@@ -137,6 +137,23 @@ def layer_inputs(cfg: LayerConfig, dtype: str, batch: int = None,
     return {"x": xs, "w": ws, "x64": x64, "w64": w64, "dtype": dtype}
 
 
+def layer_grad_output(cfg: LayerConfig, dtype: str, batch: int = None,
+                      seed: int = None):
+    """Seeded dL/dy for the layer's backward pass: drawn like x (uniform or a
+    Gaussian random field of the same spectrum) with c_out channels, from its
+    own stream (seed + 1000 unless given). Returns ``g`` (storage form) and
+    ``g64`` (float64 copy of the stored values)."""
+    b = cfg.batch if batch is None else batch
+    rng = np.random.default_rng((cfg.seed + 1000) if seed is None else seed)
+    lead = (b, cfg.c_out)
+    if cfg.input_kind == "uniform":
+        g = rng.uniform(-1.0, 1.0, size=lead + tuple(cfg.grid))
+    else:
+        g = gaussian_random_field(rng, lead, tuple(cfg.grid))
+    gs = round_to_storage(g, dtype)
+    return {"g": gs, "g64": storage_to_float64(gs, dtype)}
+
+
 def model_inputs(cfg: ModelConfig, batch: int = None, grid: tuple = None,
                  seed: int = None):
     """Seeded input and random-init parameters of the full FNO2d model.
