@@ -15,7 +15,14 @@ it. Prints one JSON line:
 * cpu_baseline: the float64 oracle timed on this host's cores on the same
   workload;
 * configs: the same layers/s and GB/s figures for the 128^2 fp16, 256^2
-  fp16 / bf16 and 64^3 fp32 layers.
+  fp16 / bf16 and 64^3 fp32 layers;
+* latency: per-call latency (mean, std, min over individually timed calls)
+  of the 128^2 fp32 layer shape at batch 1, 2, 4, 8, launched eagerly and
+  replayed from a captured HIP graph, with the throughput gain from batch 1
+  to 8;
+* backward: the layer's backward pass (grad_x and grad_w from dL/dy) on the
+  128^2 fp32, 256^2 fp16 and 64^3 fp32 layers, as backward passes/s and GB/s
+  from its minimal bytes (read x, w, dL/dy once, write grad_x, grad_w once).
 """
 
 import argparse
@@ -99,6 +106,114 @@ class Layer:
     def close(self):
         self.fno.fno_plan_destroy(self.plan)
         self.sets = []
+
+
+class Backward:
+    """Plan plus rotating device buffer sets for the backward pass of one
+    workload."""
+
+    def __init__(self, cfg, dtype):
+        import torch
+        import spectral_convolution_amd as fno
+        import workloads as wl
+        self.fno, self.cfg, self.dtype = fno, cfg, dtype
+        inp = wl.layer_inputs(cfg, dtype)
+        gout = wl.layer_grad_output(cfg, dtype)
+        self.plan = fno.fno_plan_create(cfg.ndim, cfg.batch, cfg.c_in, cfg.c_out, cfg.grid,
+                                        cfg.modes, dtype, 0)
+        x0, w0, g0 = (to_device(inp["x"], dtype), to_device(inp["w"], dtype),
+                      to_device(gout["g"], dtype))
+        self.nsets = max(1, math.ceil(ROTATE_BYTES / backward_minimal_bytes(cfg, dtype)))
+        self.sets = []
+        for i in range(self.nsets):
+            x, w, g = (x0, w0, g0) if i == 0 else (x0.clone(), w0.clone(), g0.clone())
+            self.sets.append((x, w, g, torch.empty_like(x), torch.empty_like(w)))
+        self.call = (fno.fno_spectral_conv2d_backward if cfg.ndim == 2
+                     else fno.fno_spectral_conv3d_backward)
+        self.stream = torch.cuda.current_stream()
+
+    def step(self, i):
+        x, w, g, gx, gw = self.sets[i % self.nsets]
+        self.call(self.plan, x, w, g, gx, gw, self.stream)
+
+    def close(self):
+        self.fno.fno_plan_destroy(self.plan)
+        self.sets = []
+
+
+def backward_minimal_bytes(cfg, dtype):
+    """Read x, w and dL/dy once; write grad_x and grad_w once."""
+    s = 4 if dtype == "f32" else 2
+    pts = int(np.prod(cfg.grid))
+    w = cfg.n_modes * cfg.c_in * cfg.c_out * 2 * s
+    return 2 * cfg.batch * cfg.c_in * pts * s + cfg.batch * cfg.c_out * pts * s + 2 * w
+
+
+def measure_backward(cfg, dtype, steps, warmup):
+    bw = Backward(cfg, dtype)
+    try:
+        ms = _time_loop(bw.step, steps, warmup, bw.stream)
+        gbps = backward_minimal_bytes(cfg, dtype) / (ms * 1e-3) / 1e9
+        return {"workload": cfg.name, "dtype": dtype, "ms_per_backward": ms,
+                "backward_per_s": 1000.0 / ms, "minimal_bytes": backward_minimal_bytes(cfg, dtype),
+                "gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS}
+    finally:
+        bw.close()
+
+
+def _latencies(fn, n, warmup, stream):
+    """Per-call latency in µs: each call between its own pair of events,
+    synchronised before the next."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+        b.synchronize()
+    t = np.array([a.elapsed_time(b) * 1000.0 for a, b in ev])
+    return {"mean": float(t.mean()), "std": float(t.std()), "min": float(t.min()),
+            "p50": float(np.median(t)), "p99": float(np.percentile(t, 99))}
+
+
+def latency_sweep(n=200, warmup=20):
+    """The 128^2 fp32 layer (Ci=Co=32, modes 16x16) at batch 1..8: eager
+    calls and replays of a captured graph of one call."""
+    import torch
+    import spectral_convolution_amd as fno
+    import workloads as wl
+    base = wl.CONFIGS["c1"]
+    out = []
+    for B in (1, 2, 4, 8):
+        inp = wl.layer_inputs(base, "f32", batch=B)
+        plan = fno.fno_plan_create(2, B, base.c_in, base.c_out, base.grid, base.modes, "f32", 0)
+        try:
+            x, w = to_device(inp["x"], "f32"), to_device(inp["w"], "f32")
+            y = torch.empty(plan.y_shape(), dtype=x.dtype, device=x.device)
+            stream = torch.cuda.current_stream()
+            eager = _latencies(lambda i: fno.fno_spectral_conv2d(plan, x, w, y, stream), n, warmup, stream)
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                fno.fno_spectral_conv2d(plan, x, w, y)
+            stream.wait_stream(side)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                fno.fno_spectral_conv2d(plan, x, w, y)
+            torch.cuda.synchronize()
+            replay = _latencies(lambda i: graph.replay(), n, warmup, torch.cuda.current_stream())
+            del graph
+            out.append({"batch": B, "eager_us": eager, "graph_us": replay,
+                        "samples_per_s": B / (replay["mean"] * 1e-6)})
+        finally:
+            torch.cuda.synchronize()
+            fno.fno_plan_destroy(plan)
+    return {"workload": "FNO2d spectral-conv layer, fp32, Cin=Cout=32, 128x128, modes 16x16",
+            "calls_per_batch": n, "sweep": out,
+            "throughput_gain_b1_to_b8": out[-1]["samples_per_s"] / out[0]["samples_per_s"]}
 
 
 def _time_loop(fn, steps, warmup, stream):
@@ -206,6 +321,10 @@ def main():
     ap.add_argument("--dtype", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-latency", action="store_true")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only time the backward pass of --config/--dtype (profiling runs)")
     ap.add_argument("--copy-only", type=int, default=0, metavar="BYTES",
                     help="only time a device-to-device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -224,6 +343,9 @@ def main():
         return
     cfg = wl.CONFIGS[args.config]
     dtype = args.dtype or cfg.dtypes[0]
+    if args.backward_only:
+        print(json.dumps({"backward": [measure_backward(cfg, dtype, args.steps, args.warmup)]}))
+        return
     main_res = measure(cfg, dtype, args.steps, args.warmup)
     dom = max(main_res["kernels"], key=lambda k: k["ms"])
     out = {
@@ -253,6 +375,19 @@ def main():
             print(f"[bench] {name} {dt}: {r['layers_per_s']:.1f} layers/s, {r['gbps']:.0f} GB/s",
                   file=sys.stderr, flush=True)
         out["configs"] = extra
+    if not args.no_backward:
+        bwd = []
+        for name, dt in (("c1", "f32"), ("c2", "f16"), ("c3", "f32")):
+            r = measure_backward(wl.CONFIGS[name], dt, max(20, args.steps // 2), max(5, args.warmup // 2))
+            bwd.append(r)
+            print(f"[bench] backward {name} {dt}: {r['backward_per_s']:.1f} /s, {r['gbps']:.0f} GB/s",
+                  file=sys.stderr, flush=True)
+        out["backward"] = bwd
+    if not args.no_latency:
+        out["latency"] = latency_sweep()
+        print("[bench] latency " + ", ".join(
+            f"B={r['batch']}: {r['graph_us']['mean']:.1f}±{r['graph_us']['std']:.1f} us"
+            for r in out["latency"]["sweep"]), file=sys.stderr, flush=True)
     out["copy_1gib"] = copy_bandwidth(1 << 30)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, dtype)
