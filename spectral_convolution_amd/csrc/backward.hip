@@ -70,199 +70,160 @@ hipError_t launch_conj_transpose(const void *w, void *wh, int K, int Ci, int Co,
 
 // ------------------------------------------------------------ dw kernel
 //
-// Instruction: v_mfma_f32_4x4x1_16b_f32, 16 blocks of 4 x 4 per wave, the
-// blocks being 16 consecutive modes (so every load of a lane group is a run
-// of 16 consecutive complex spectra, coalesced in the plane-major layout).
-// The batch is the reduction dimension, one MFMA step per batch row. Lane l
-// works on mode k0 + l/4; as the A operand it carries input channel
-// i0 + 4 ib + l%4 (conj Xs), as the B operand output channel
-// o0 + 4 (l%4) + ob (Gs, ob = 0..3, one MFMA each). In real form
-//   Re dw += Xr Gr + Xi Gi,   Im dw += Xr Gi + (-Xi) Gr.
-// A wave covers 16 modes x 4 IB input x 16 output channels; the batch sum
-// is split over the S waves of a workgroup and met in LDS.
+// Per mode k the weight gradient is a real-form product with the batch as
+// the reduction dimension:
+//   Re dw[k] = Xr^T Gr + Xi^T Gi,   Im dw[k] = Xr^T Gi + (-Xi)^T Gr
+// (X = Xs[.][.][k] as B x Ci, G = Gs[.][.][k] as B x Co). Instruction:
+// v_mfma_f32_16x16x4f32 (fp32 operands, fp32 accumulation), one 16 x 16
+// (i, o) tile of one mode and four batch rows per instruction.
+//
+// A workgroup (4 waves) owns 16 consecutive modes x 32 input x 32 output
+// channels and streams the batch in stages of 4 rows. Each stage's spectra
+// rows ([b][i][16 modes] and [b][o][16 modes], 128 contiguous bytes each)
+// are loaded with 16-byte accesses one stage ahead into registers and
+// stored into LDS per mode as [mode][b][channel] (float2), so a fragment
+// read is 16 consecutive channels per lane group. Wave w multiplies modes
+// 4w .. 4w + 3, all four 16 x 16 tiles. Rows past the batch, channels and
+// modes past their ends load as zeros.
 
-template <int IB>
-struct GwFrag {
-  float xr[IB], xi[IB], xn[IB];
-  float gr[4], gi[4];
-};
+constexpr int kGwT = 256;   // threads per workgroup
+constexpr int kGwM = 16;    // modes per workgroup
+constexpr int kGwC = 32;    // input (and output) channels per workgroup
+constexpr int kGwB = 4;     // batch rows per stage (one MFMA k-step)
+constexpr int kGwP = kGwC + 1;            // float2 per batch row of a staged mode (32 + pad)
+constexpr int kGwS = kGwB * kGwP + 1;     // float2 per staged mode (+ pad: stores spread over banks)
+constexpr int kGwU = kGwB * kGwC * kGwM / 2 / kGwT;  // 16-byte units per thread and operand (= 4)
 
-// Operands of batch row b. Lanes whose mode or channel is out of range read
-// element 0: their values reach only outputs that are never stored.
-template <int IB>
-__device__ __forceinline__ void gw_load(const GradWArgs &a, int b, int mode, bool mode_ok, int i0, int nn, int o0,
-                                        GwFrag<IB> &f) {
-  const int K = a.K, Ci = a.Ci, Co = a.Co;
+typedef unsigned gw_u32x4 __attribute__((ext_vector_type(4)));
+
+// one stage of one operand: rows (b, c) of 16 modes, c fastest, from
+// src[b][c][K] (nc channels); unit u = (row, mode pair)
+__device__ __forceinline__ void gw_fetch(const float2 *src, int nc, int K, int B, int st, int k0, int c0, int tid,
+                                         gw_u32x4 (&p)[kGwU]) {
 #pragma unroll
-  for (int ib = 0; ib < IB; ++ib) {
-    const int i = i0 + 4 * ib + nn;
-    const bool ok = mode_ok && i < Ci;
-    const float2 v = a.xs[ok ? ((size_t)b * Ci + i) * K + mode : 0];
-    f.xr[ib] = v.x;
-    f.xi[ib] = v.y;
-  }
-#pragma unroll
-  for (int ob = 0; ob < 4; ++ob) {
-    const int o = o0 + 4 * nn + ob;
-    const bool ok = mode_ok && o < Co;
-    const float2 v = a.gs[ok ? ((size_t)b * Co + o) * K + mode : 0];
-    f.gr[ob] = v.x;
-    f.gi[ob] = v.y;
+  for (int v = 0; v < kGwU; ++v) {
+    const int u = v * kGwT + tid;
+    const int row = u >> 3, pr = u & 7;
+    const int b = st * kGwB + row / kGwC, c = c0 + row % kGwC, mode = k0 + 2 * pr;
+    const bool ok = b < B && c < nc && mode < K;
+    const gw_u32x4 t = *reinterpret_cast<const gw_u32x4 *>(src + (ok ? ((size_t)b * nc + c) * K + mode : 0));
+    p[v] = ok ? t : gw_u32x4{0u, 0u, 0u, 0u};
   }
 }
 
-template <int IB, int DT>
-__global__ __launch_bounds__(512) void fno_grad_w(GradWArgs a) {
-  extern __shared__ float red[];
-  const int lane = threadIdx.x & 63, s = threadIdx.x >> 6, S = blockDim.x >> 6;
-  const int blk = lane >> 2, nn = lane & 3;
+__device__ __forceinline__ void gw_put(float2 *stage, int tid, const gw_u32x4 (&p)[kGwU]) {
+#pragma unroll
+  for (int v = 0; v < kGwU; ++v) {
+    const int u = v * kGwT + tid;
+    const int row = u >> 3, pr = u & 7;
+    const int b = row / kGwC, c = row % kGwC;
+    stage[(2 * pr) * kGwS + b * kGwP + c] = make_float2(__uint_as_float(p[v][0]), __uint_as_float(p[v][1]));
+    stage[(2 * pr + 1) * kGwS + b * kGwP + c] = make_float2(__uint_as_float(p[v][2]), __uint_as_float(p[v][3]));
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kGwT) __attribute__((amdgpu_waves_per_eu(2))) void fno_grad_w(GradWArgs a) {
+  __shared__ float2 xs[kGwM * kGwS], gs[kGwM * kGwS];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int K = a.K, Ci = a.Ci, Co = a.Co, B = a.B;
-  const int mode = blockIdx.x * 16 + blk;
-  const int i0 = blockIdx.y * 4 * IB;
-  const int o0 = blockIdx.z * 16;
-  const bool mode_ok = mode < K;
-  const int b0 = (B * s) / S, b1 = (B * (s + 1)) / S;
+  // workgroups of one mode block are gridDim.x apart: with gridDim.x a
+  // multiple of 8 they share an XCD (and its L2), where the second read of
+  // each spectra row hits
+  const int k0 = blockIdx.x * kGwM;
+  const int nto = (Co + kGwC - 1) / kGwC;
+  const int i0 = (blockIdx.y / nto) * kGwC, o0 = (blockIdx.y % nto) * kGwC;
+  const int nst = (B + kGwB - 1) / kGwB;
 
-  v4f accr[IB][4], acci[IB][4];
+  v4f accr[4][2][2], acci[4][2][2];
 #pragma unroll
-  for (int ib = 0; ib < IB; ++ib)
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int ob = 0; ob < 4; ++ob) {
-      accr[ib][ob] = v4f{0.f, 0.f, 0.f, 0.f};
-      acci[ib][ob] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
-
-  // ring of D + 1 batch rows in flight; loads are clamped to the last row of
-  // the wave's range (repeats are never multiplied)
-  constexpr int D = IB == 1 ? 3 : IB == 2 ? 2 : 1;
-  if (b0 < b1) {
-    GwFrag<IB> ring[D + 1];
+    for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-    for (int k = 0; k <= D; ++k) gw_load<IB>(a, min(b0 + k, b1 - 1), mode, mode_ok, i0, nn, o0, ring[k]);
-    for (int b = b0; b < b1; b += D + 1) {
-#pragma unroll
-      for (int k = 0; k <= D; ++k) {
-        GwFrag<IB> &cur = ring[k];
-        if (b + k < b1) {
-#pragma unroll
-          for (int ib = 0; ib < IB; ++ib) cur.xn[ib] = -cur.xi[ib];
-#pragma unroll
-          for (int ib = 0; ib < IB; ++ib)
-#pragma unroll
-            for (int ob = 0; ob < 4; ++ob) {
-              accr[ib][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(cur.xr[ib], cur.gr[ob], accr[ib][ob], 0, 0, 0);
-              accr[ib][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(cur.xi[ib], cur.gi[ob], accr[ib][ob], 0, 0, 0);
-              acci[ib][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(cur.xr[ib], cur.gi[ob], acci[ib][ob], 0, 0, 0);
-              acci[ib][ob] = __builtin_amdgcn_mfma_f32_4x4x1f32(cur.xn[ib], cur.gr[ob], acci[ib][ob], 0, 0, 0);
-            }
-        }
-        gw_load<IB>(a, min(b + k + D + 1, b1 - 1), mode, mode_ok, i0, nn, o0, cur);
+      for (int to = 0; to < 2; ++to) {
+        accr[m][ti][to] = v4f{0.f, 0.f, 0.f, 0.f};
+        acci[m][ti][to] = v4f{0.f, 0.f, 0.f, 0.f};
       }
+
+  gw_u32x4 px[kGwU], pg[kGwU];
+  gw_fetch(a.xs, Ci, K, B, 0, k0, i0, tid, px);
+  gw_fetch(a.gs, Co, K, B, 0, k0, o0, tid, pg);
+  for (int st = 0; st < nst; ++st) {
+    gw_put(xs, tid, px);
+    gw_put(gs, tid, pg);
+    if (st + 1 < nst) {
+      gw_fetch(a.xs, Ci, K, B, st + 1, k0, i0, tid, px);
+      gw_fetch(a.gs, Co, K, B, st + 1, k0, o0, tid, pg);
     }
+    __syncthreads();
+    // fragment of lane l: batch row l / 16, channel 16 t + l % 16
+    const int fo = (lane >> 4) * kGwP + (lane & 15);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int mm = 4 * wv + m;
+      float2 x[2], g[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        x[t] = xs[mm * kGwS + fo + 16 * t];
+        g[t] = gs[mm * kGwS + fo + 16 * t];
+      }
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int to = 0; to < 2; ++to) {
+          v4f &cr = accr[m][ti][to], &ci = acci[m][ti][to];
+          cr = __builtin_amdgcn_mfma_f32_16x16x4f32(x[ti].x, g[to].x, cr, 0, 0, 0);
+          cr = __builtin_amdgcn_mfma_f32_16x16x4f32(x[ti].y, g[to].y, cr, 0, 0, 0);
+          ci = __builtin_amdgcn_mfma_f32_16x16x4f32(x[ti].x, g[to].y, ci, 0, 0, 0);
+          ci = __builtin_amdgcn_mfma_f32_16x16x4f32(-x[ti].y, g[to].x, ci, 0, 0, 0);
+        }
+    }
+    __syncthreads();
   }
 
-  // accumulator register j of lane l holds block l/4 (the mode), row j
-  // (input channel i0 + 4 ib + j), column l%4 (output channel o0 + 4 (l%4) + ob)
-  const float sc = a.scale * ((mode % a.mlast) == 0 ? 1.0f : 2.0f);
-  if (S == 1) {
-    if (!mode_ok) return;
+  // accumulator register j of lane l: row 4 (l / 16) + j (input channel),
+  // column l % 16 (output channel); 16 lanes store 16 consecutive outputs
 #pragma unroll
-    for (int ib = 0; ib < IB; ++ib)
+  for (int m = 0; m < 4; ++m) {
+    const int mode = k0 + 4 * wv + m;
+    if (mode >= K) continue;
+    const float sc = a.scale * ((mode % a.mlast) == 0 ? 1.0f : 2.0f);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = i0 + 4 * ib + j;
-        if (i >= Ci) continue;
+    for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-        for (int ob = 0; ob < 4; ++ob) {
-          const int o = o0 + 4 * nn + ob;
-          if (o < Co) store_pair<DT>(a.dw, 2 * (((size_t)mode * Ci + i) * Co + o), sc * accr[ib][ob][j], sc * acci[ib][ob][j]);
-        }
-      }
-    return;
-  }
-  // partial sums of every wave -> red[wave][pair][re / im][lane], pair =
-  // (ib, ob, j); wave s adds up pairs [s NP / S, (s + 1) NP / S) over the
-  // waves in wave order (results do not depend on timing) and stores them
-  constexpr int NP = IB * 16;
-  {
-    float *dst = red + (size_t)s * NP * 2 * 64 + lane;
-#pragma unroll
-    for (int ib = 0; ib < IB; ++ib)
-#pragma unroll
-      for (int ob = 0; ob < 4; ++ob)
+      for (int to = 0; to < 2; ++to) {
+        const int o = o0 + 16 * to + (lane & 15);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int q = (ib * 4 + ob) * 4 + j;
-          dst[(2 * q) * 64] = accr[ib][ob][j];
-          dst[(2 * q + 1) * 64] = acci[ib][ob][j];
+          const int i = i0 + 16 * ti + 4 * (lane >> 4) + j;
+          if (i < Ci && o < Co)
+            store_pair<DT>(a.dw, 2 * (((size_t)mode * Ci + i) * Co + o), sc * accr[m][ti][to][j],
+                           sc * acci[m][ti][to][j]);
         }
-  }
-  __syncthreads();
-  if (!mode_ok) return;
-  const int per = NP / S;
-  for (int q = s * per; q < (s + 1) * per; ++q) {
-    float re = 0.f, im = 0.f;
-    for (int v = 0; v < S; ++v) {
-      re += red[((size_t)v * NP * 2 + 2 * q) * 64 + lane];
-      im += red[((size_t)v * NP * 2 + 2 * q + 1) * 64 + lane];
-    }
-    const int j = q & 3, ob = (q >> 2) & 3, ib = q >> 4;
-    const int i = i0 + 4 * ib + j, o = o0 + 4 * nn + ob;
-    if (i < Ci && o < Co) store_pair<DT>(a.dw, 2 * (((size_t)mode * Ci + i) * Co + o), sc * re, sc * im);
+      }
   }
 }
 
-int gradw_pick_ib(int B, int Ci, int Co, int K) {
-  // widest input-channel tile that still leaves >= 1024 waves
-  (void)B;
-  const long tiles_k = (K + 15) / 16, tiles_o = (Co + 15) / 16;
-  for (int ib = 4; ib > 1; ib >>= 1) {
-    if (2 * ib >= Ci) continue;  // a narrower tile already covers the channels
-    const long waves = tiles_k * tiles_o * ((Ci + 4 * ib - 1) / (4 * ib));
-    if (waves >= 1024) return ib;
-  }
-  return 1;
-}
-
-int gradw_pick_split(int B, int Ci, int Co, int K, int ib) {
-  // waves per workgroup sharing one tile: enough waves to fill the chip, at
-  // least four batch rows per wave
-  const long waves = (long)((K + 15) / 16) * ((Co + 15) / 16) * ((Ci + 4 * ib - 1) / (4 * ib));
-  int S = 1;
-  while (waves * S < 2048 && S < 8 && B >= 8 * S) S *= 2;
-  return S;
-}
-
-size_t gradw_lds_bytes(int ib, int S) { return S > 1 ? (size_t)S * ib * 32 * 64 * sizeof(float) : 0; }
-
-template <int IB>
 static const void *gradw_kernel(int dtype) {
   switch (dtype) {
-    case DT_F32: return (const void *)fno_grad_w<IB, DT_F32>;
-    case DT_F16: return (const void *)fno_grad_w<IB, DT_F16>;
-    case DT_BF16: return (const void *)fno_grad_w<IB, DT_BF16>;
+    case DT_F32: return (const void *)fno_grad_w<DT_F32>;
+    case DT_F16: return (const void *)fno_grad_w<DT_F16>;
+    case DT_BF16: return (const void *)fno_grad_w<DT_BF16>;
   }
   return nullptr;
 }
 
-static const void *gradw_kernel(int ib, int dtype) {
-  return ib == 4 ? gradw_kernel<4>(dtype) : ib == 2 ? gradw_kernel<2>(dtype) : gradw_kernel<1>(dtype);
-}
+bool gradw_supported(int K) { return (K & 1) == 0; }
 
-hipError_t gradw_prepare(int ib, int dtype, size_t lds) {
-  const void *k = gradw_kernel(ib, dtype);
-  if (!k) return hipErrorInvalidValue;
-  return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-}
-
-hipError_t launch_grad_w(const GradWArgs &a, int ib, int S, int dtype, hipStream_t s) {
-  const void *k = gradw_kernel(ib, dtype);
-  if (!k) return hipErrorInvalidValue;
-  const long gy = (a.Ci + 4 * ib - 1) / (4 * ib), gz = (a.Co + 15) / 16;
-  if (gy > 65535 || gz > 65535) return hipErrorInvalidValue;
-  dim3 grid((a.K + 15) / 16, (unsigned)gy, (unsigned)gz);
+hipError_t launch_grad_w(const GradWArgs &a, int dtype, hipStream_t s) {
+  const void *k = gradw_kernel(dtype);
+  if (!k || !gradw_supported(a.K)) return hipErrorInvalidValue;
+  const long gy = (long)((a.Ci + kGwC - 1) / kGwC) * ((a.Co + kGwC - 1) / kGwC);
+  if (gy > 65535) return hipErrorInvalidValue;
+  dim3 grid((a.K + kGwM - 1) / kGwM, (unsigned)gy);
   void *args[] = {(void *)&a};
-  return hipLaunchKernel(k, grid, dim3(64 * S), args, gradw_lds_bytes(ib, S), s);
+  return hipLaunchKernel(k, grid, dim3(kGwT), args, 0, s);
 }
 
 }  // namespace fno

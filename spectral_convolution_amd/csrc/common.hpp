@@ -176,11 +176,8 @@ hipError_t contract_mx_prepare(int dtype, int B);
 hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s);
 
 hipError_t launch_conj_transpose(const void *w, void *wh, int K, int Ci, int Co, int dtype, hipStream_t s);
-int gradw_pick_ib(int B, int Ci, int Co, int K);
-int gradw_pick_split(int B, int Ci, int Co, int K, int ib);
-size_t gradw_lds_bytes(int ib, int S);
-hipError_t gradw_prepare(int ib, int dtype, size_t lds);
-hipError_t launch_grad_w(const GradWArgs &a, int ib, int S, int dtype, hipStream_t s);
+bool gradw_supported(int K);
+hipError_t launch_grad_w(const GradWArgs &a, int dtype, hipStream_t s);
 
 hipError_t launch_channel_mix(const void *x, const void *A, const void *bias, const void *add, void *y, int B,
                               int I, int O, long P, int act, int dtype, hipStream_t s);

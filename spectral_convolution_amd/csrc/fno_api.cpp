@@ -209,7 +209,7 @@ struct fno_plan_s {
   // backward: the adjoint contraction (Co -> Ci channels), the weight
   // gradient, plane transforms over the other channel count (forward of g
   // over Co channels, inverse over Ci)
-  int bb_a = 1, split_a = 1, gw_ib = 1, gw_split = 1;
+  int bb_a = 1, split_a = 1;
   bool cmx_a = false;
   int ppw_fg = 1, ppw_ib = 1;
   size_t lds_fg = 0, lds_ib = 0;
@@ -317,9 +317,7 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
   p.bb_a = contract_pick_bb(batch, c_in, p.K);
   p.split_a = contract_pick_split(batch, c_out, c_in, p.K, p.bb_a);
   p.cmx_a = contract_mx_supported((int)dtype, c_in, p.K) && contract_mx_workgroups(batch, c_in, p.K) >= 256;
-  p.gw_ib = gradw_pick_ib(batch, c_in, c_out, p.K);
-  p.gw_split = gradw_pick_split(batch, c_in, c_out, p.K, p.gw_ib);
-  if ((c_in + 4 * p.gw_ib - 1) / (4 * p.gw_ib) > 65535 || (c_out + 15) / 16 > 65535) return FNO_ERR_UNSUPPORTED;
+  if (!gradw_supported(p.K) || (long)((c_in + 31) / 32) * ((c_out + 31) / 32) > 65535) return FNO_ERR_UNSUPPORTED;
   p.ppw_fg = plane_ppw(true, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_i);
   p.ppw_ib = plane_ppw(false, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_f);
   p.lds_fg = p.mx ? p.lds_fwd : plane_fwd_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP, p.ppw_fg);
@@ -504,8 +502,6 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   if (e == hipSuccess) e = p->cmx ? contract_mx_prepare(p->dtype, p->B) : contract_prepare(p->bb, p->dtype, p->Co, lds_c);
   if (e == hipSuccess)
     e = p->cmx_a ? contract_mx_prepare(p->dtype, p->B) : contract_prepare(p->bb_a, p->dtype, p->Ci, lds_c);
-  // every tile choice needs at most 64 KiB; the cap is per kernel, shared by all plans
-  if (e == hipSuccess) e = gradw_prepare(p->gw_ib, p->dtype, 64 * 1024);
   if (e != hipSuccess) {
     (void)hipFree(p->mem);
     delete p;
@@ -750,7 +746,7 @@ static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const v
     a.K = p->K;
     a.mlast = p->modes[ndim - 1];
     a.scale = (float)pts;
-    step(launch_grad_w(a, p->gw_ib, p->gw_split, p->dtype, s));
+    step(launch_grad_w(a, p->dtype, s));
   }
   if (gx) {
     if (e == hipSuccess) step(launch_conj_transpose(w, p->wh, p->K, p->Ci, p->Co, p->dtype, s));
