@@ -207,13 +207,15 @@ def latency_sweep(n=200, warmup=20):
             replay = _latencies(lambda i: graph.replay(), n, warmup, torch.cuda.current_stream())
             del graph
             out.append({"batch": B, "eager_us": eager, "graph_us": replay,
-                        "samples_per_s": B / (replay["mean"] * 1e-6)})
+                        "samples_per_s_eager": B / (eager["mean"] * 1e-6),
+                        "samples_per_s_graph": B / (replay["mean"] * 1e-6)})
         finally:
             torch.cuda.synchronize()
             fno.fno_plan_destroy(plan)
     return {"workload": "FNO2d spectral-conv layer, fp32, Cin=Cout=32, 128x128, modes 16x16",
             "calls_per_batch": n, "sweep": out,
-            "throughput_gain_b1_to_b8": out[-1]["samples_per_s"] / out[0]["samples_per_s"]}
+            "throughput_gain_b1_to_b8_eager": out[-1]["samples_per_s_eager"] / out[0]["samples_per_s_eager"],
+            "throughput_gain_b1_to_b8_graph": out[-1]["samples_per_s_graph"] / out[0]["samples_per_s_graph"]}
 
 
 def _time_loop(fn, steps, warmup, stream):
@@ -386,7 +388,8 @@ def main():
     if not args.no_latency:
         out["latency"] = latency_sweep()
         print("[bench] latency " + ", ".join(
-            f"B={r['batch']}: {r['graph_us']['mean']:.1f}±{r['graph_us']['std']:.1f} us"
+            f"B={r['batch']}: eager {r['eager_us']['mean']:.1f}±{r['eager_us']['std']:.1f} us, "
+            f"graph {r['graph_us']['mean']:.1f}±{r['graph_us']['std']:.1f} us"
             for r in out["latency"]["sweep"]), file=sys.stderr, flush=True)
     out["copy_1gib"] = copy_bandwidth(1 << 30)
     if not args.no_cpu_baseline:
