@@ -20,6 +20,9 @@ it. Prints one JSON line:
   of the 128^2 fp32 layer shape at batch 1, 2, 4, 8, launched eagerly and
   replayed from a captured HIP graph, with the throughput gain from batch 1
   to 8;
+* model: the full FNO2d forward (lift, four spectral blocks with the 1x1
+  bypass and GELU, projection; B=20, 256^2, width 64, modes 24x24, fp16
+  storage) as forwards/s and samples/s, and its per-call latency at batch 1;
 * backward: the layer's backward pass (grad_x and grad_w from dL/dy) on the
   128^2 fp32, 256^2 fp16 and 64^3 fp32 layers, as backward passes/s and GB/s
   from its minimal bytes (read x, w, dL/dy once, write grad_x, grad_w once).
@@ -218,6 +221,53 @@ def latency_sweep(n=200, warmup=20):
             "throughput_gain_b1_to_b8_graph": out[-1]["samples_per_s_graph"] / out[0]["samples_per_s_graph"]}
 
 
+class Model:
+    """FNO2d model plan with random-init parameters on the device."""
+
+    def __init__(self, cfg, batch=None):
+        import torch
+        import spectral_convolution_amd as fno
+        import workloads as wl
+        inp = wl.model_inputs(cfg, batch=batch)
+        dt = inp["dtype"]
+        self.fno, self.B = fno, inp["batch"]
+        H, W = inp["grid"]
+        self.model = fno.fno_model2d_create(self.B, (H, W), cfg.in_channels, cfg.width, cfg.n_layers,
+                                            cfg.modes, cfg.proj_hidden, cfg.out_channels, dt, 0)
+        self.params = [to_device(inp["P"], dt), to_device(inp["p"], dt)]
+        for L in inp["layers"]:
+            self.params += [to_device(L["spectral"], dt), to_device(L["W"], dt), to_device(L["b"], dt)]
+        self.params += [to_device(inp[k], dt) for k in ("Q1", "q1", "Q2", "q2")]
+        self.f = to_device(inp["features"], dt)
+        self.out = torch.empty((self.B, cfg.out_channels, H, W), dtype=self.f.dtype, device=self.f.device)
+        self.stream = torch.cuda.current_stream()
+
+    def step(self, i):
+        self.fno.fno_model2d_forward(self.model, self.f, self.params, self.out, self.stream)
+
+    def close(self):
+        self.fno.fno_model2d_destroy(self.model)
+
+
+def measure_model(steps, warmup):
+    import workloads as wl
+    cfg = wl.CONFIGS["c4"]
+    m = Model(cfg)
+    try:
+        ms = _time_loop(m.step, steps, warmup, m.stream)
+        res = {"workload": "FNO2d forward, B=20, 256x256, lift 3->64, 4 x (spectral conv 64->64 modes "
+                           "24x24 + 1x1 conv + GELU), projection 64->128->1, fp16 storage",
+               "ms_per_forward": ms, "samples_per_s": m.B / (ms * 1e-3)}
+    finally:
+        m.close()
+    m1 = Model(cfg, batch=1)
+    try:
+        res["latency_b1_us"] = _latencies(m1.step, 100, 10, m1.stream)
+    finally:
+        m1.close()
+    return res
+
+
 def _time_loop(fn, steps, warmup, stream):
     import torch
     for i in range(warmup):
@@ -325,6 +375,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-latency", action="store_true")
+    ap.add_argument("--no-model", action="store_true")
     ap.add_argument("--backward-only", action="store_true",
                     help="only time the backward pass of --config/--dtype (profiling runs)")
     ap.add_argument("--copy-only", type=int, default=0, metavar="BYTES",
@@ -385,6 +436,10 @@ def main():
             print(f"[bench] backward {name} {dt}: {r['backward_per_s']:.1f} /s, {r['gbps']:.0f} GB/s",
                   file=sys.stderr, flush=True)
         out["backward"] = bwd
+    if not args.no_model:
+        out["model"] = measure_model(max(10, args.steps // 10), max(3, args.warmup // 4))
+        print(f"[bench] model: {out['model']['ms_per_forward']:.3f} ms per B=20 forward, "
+              f"B=1 latency {out['model']['latency_b1_us']['mean']:.1f} us", file=sys.stderr, flush=True)
     if not args.no_latency:
         out["latency"] = latency_sweep()
         print("[bench] latency " + ", ".join(
