@@ -376,6 +376,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-latency", action="store_true")
     ap.add_argument("--no-model", action="store_true")
+    ap.add_argument("--model-only", action="store_true", help="only time the full FNO2d forward (profiling runs)")
     ap.add_argument("--backward-only", action="store_true",
                     help="only time the backward pass of --config/--dtype (profiling runs)")
     ap.add_argument("--copy-only", type=int, default=0, metavar="BYTES",
@@ -396,6 +397,9 @@ def main():
         return
     cfg = wl.CONFIGS[args.config]
     dtype = args.dtype or cfg.dtypes[0]
+    if args.model_only:
+        print(json.dumps({"model": measure_model(args.steps, args.warmup)}))
+        return
     if args.backward_only:
         print(json.dumps({"backward": [measure_backward(cfg, dtype, args.steps, args.warmup)]}))
         return

@@ -176,6 +176,217 @@ __global__ __launch_bounds__(kPwThreads) void fno_channel_mix(MixArgs a) {
   }
 }
 
+// ------------------------------------------- half-precision channel mix
+//
+// fp16 / bf16 storage: the products of two storage values are exact in
+// fp32, so the per-pixel GEMM runs on v_mfma_f32_16x16x32_{f16,bf16} with
+// fp32 accumulation (16x the fp32 matrix rate) at no cost in accuracy. The
+// operands need the channels contiguous per lane while the activations are
+// pixel-contiguous per channel, so a workgroup stages a tile of Ipad
+// channels x 256 pixels in LDS ([i][p], coalesced 16-byte row loads of the
+// next tile in flight while the current one is multiplied) and builds the
+// A fragments from it. Orientation D[p][o] = x^T W^T: the A operand is 16
+// pixels x 32 channels, the B operand 32 channels x 16 outputs (rows of W,
+// held in registers for the whole kernel). Wave w owns pixels 64 w ..
+// 64 w + 63 of the tile and all 64 output channels of the workgroup; its
+// product rows are assigned to pixels so that every lane ends with 16
+// consecutive pixels of one output channel, and the add input and the
+// output move as 16-byte accesses. The add input is requested before the
+// products. Needs P % 8 == 0 and at most 64 input channels (wider inputs
+// would spill registers).
+
+typedef unsigned pw_u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 pw_h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 pw_b8 __attribute__((ext_vector_type(8)));
+
+constexpr int kMxPx = 256;              // pixels per workgroup tile
+constexpr int kMxPitch = kMxPx + 4;     // halves per staged channel row: the four lane groups of a
+                                        // fragment read (rows 8 apart) start 64 banks apart
+
+template <int DT>
+__device__ __forceinline__ v4f pw_mma(pw_u32x4 a, pw_u32x4 b, v4f c) {
+  if constexpr (DT == DT_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(pw_h8, a), __builtin_bit_cast(pw_h8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(pw_b8, a), __builtin_bit_cast(pw_b8, b), c, 0, 0, 0);
+}
+
+// one tile of x rows into registers: unit u = (channel u / 32, 8 pixels at
+// 8 (u % 32)); channels past I and pixels past P read as zeros
+template <int KB>
+__device__ __forceinline__ void mixmx_fetch(const uint16_t *xb, int I, long P, long pc, int tid,
+                                            pw_u32x4 (&r)[KB * 4]) {
+#pragma unroll
+  for (int v = 0; v < KB * 4; ++v) {
+    const int u = v * kPwThreads + tid;
+    const int i = u >> 5;
+    const long p = pc + 8 * (u & 31);
+    const bool ok = i < I && p < P;
+    const pw_u32x4 t = *reinterpret_cast<const pw_u32x4 *>(xb + (ok ? (size_t)i * P + p : 0));
+    r[v] = ok ? t : pw_u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <int KB>
+__device__ __forceinline__ void mixmx_put(uint16_t *xs, int tid, const pw_u32x4 (&r)[KB * 4]) {
+#pragma unroll
+  for (int v = 0; v < KB * 4; ++v) {
+    const int u = v * kPwThreads + tid;
+    uint2 *d = reinterpret_cast<uint2 *>(xs + (u >> 5) * kMxPitch + 8 * (u & 31));
+    d[0] = make_uint2(r[v][0], r[v][1]);
+    d[1] = make_uint2(r[v][2], r[v][3]);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void load4h(const void *p, size_t i, float (&v)[4]) {
+  const uint2 q = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(p) + i);
+  if constexpr (DT == DT_F16) {
+    const half2_t h0 = __builtin_bit_cast(half2_t, q.x), h1 = __builtin_bit_cast(half2_t, q.y);
+    v[0] = (float)h0.x; v[1] = (float)h0.y; v[2] = (float)h1.x; v[3] = (float)h1.y;
+  } else {
+    v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xffff0000u);
+    v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xffff0000u);
+  }
+}
+
+// eight consecutive storage halves -> fp32
+template <int DT>
+__device__ __forceinline__ void unpack8(pw_u32x4 q, float (&v)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if constexpr (DT == DT_F16) {
+      // each half converted on its own: converting both lanes of a bit-cast
+      // half2 taken from this vector gave wrong values for all but its first
+      // element on gfx950
+      v[2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(q[k] & 0xffffu));
+      v[2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(q[k] >> 16));
+    } else {
+      v[2 * k] = __uint_as_float(q[k] << 16);
+      v[2 * k + 1] = __uint_as_float(q[k] & 0xffff0000u);
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (DT == DT_F16) {
+    half2_t h;
+    h.x = (_Float16)lo;
+    h.y = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, h);
+  } else {
+    return f32x2_to_bf16x2(lo, hi);
+  }
+}
+
+template <int DT, int KB>
+__global__ __launch_bounds__(kPwThreads) __attribute__((amdgpu_waves_per_eu(2))) void fno_channel_mix_mx(MixArgs a) {
+  __shared__ uint16_t xs[KB * 32 * kMxPitch];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int o0 = blockIdx.y * kOB, b = blockIdx.z;
+  const int I = a.I, O = a.O;
+  const long P = a.P;
+  const uint16_t *xb = reinterpret_cast<const uint16_t *>(a.x) + (size_t)b * I * P;
+  const size_t yb = (size_t)b * O * P;
+
+  // B fragments: lane l holds W[o0 + 16 ot + l % 16][32 kb + 8 (l / 16) + t], t = 0..7
+  pw_u32x4 wf[4][KB];
+  const uint16_t *A = reinterpret_cast<const uint16_t *>(a.A);
+#pragma unroll
+  for (int ot = 0; ot < 4; ++ot)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int o = o0 + 16 * ot + (lane & 15);
+      uint32_t h[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int i = 32 * kb + 8 * (lane >> 4) + t;
+        h[t] = (o < O && i < I) ? A[(size_t)o * I + i] : 0u;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wf[ot][kb][q] = h[2 * q] | (h[2 * q + 1] << 16);
+    }
+  float bias[4];
+#pragma unroll
+  for (int ot = 0; ot < 4; ++ot) {
+    const int o = o0 + 16 * ot + (lane & 15);
+    bias[ot] = (a.bias && o < O) ? load1<DT>(a.bias, o) : 0.f;
+  }
+
+  // Row r of product tile pt is pixel 64 wv + 4 r + pt, so lane l's
+  // accumulators (rows 4 (l / 16) + j of every tile) are the 16 consecutive
+  // pixels 64 wv + 16 (l / 16) + 4 j + pt of output channel 16 ot + l % 16.
+  const long nch = (P + kMxPx - 1) / kMxPx;
+  pw_u32x4 r[KB * 4];
+  long pc = (long)blockIdx.x * kMxPx;
+  if (pc < P) mixmx_fetch<KB>(xb, I, P, pc, tid, r);
+  for (long c = blockIdx.x; c < nch; c += gridDim.x, pc += (long)gridDim.x * kMxPx) {
+    mixmx_put<KB>(xs, tid, r);
+    __syncthreads();
+    // this tile's add input, in flight during the products
+    const long p = pc + 64 * wv + 16 * (lane >> 4);
+    const bool pin = p < P;
+    pw_u32x4 ad[4][2];
+#pragma unroll
+    for (int ot = 0; ot < 4; ++ot) {
+      const int o = o0 + 16 * ot + (lane & 15);
+      const bool ok = a.add && pin && o < O;
+      const uint16_t *src = reinterpret_cast<const uint16_t *>(a.add ? a.add : a.x) + (ok ? yb + (size_t)o * P + p : 0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {  // P % 8 == 0: each half is wholly in or past the row
+        const bool okh = ok && p + 8 * h < P;
+        const pw_u32x4 t = *reinterpret_cast<const pw_u32x4 *>(okh ? src + 8 * h : src);
+        ad[ot][h] = okh ? t : pw_u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (c + gridDim.x < nch) mixmx_fetch<KB>(xb, I, P, pc + (long)gridDim.x * kMxPx, tid, r);
+    v4f acc[4][4];  // [pt][ot]
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      // A fragments: pixel 64 wv + 4 (l % 16) + pt, channels 32 kb + 8 (l / 16) .. + 7
+      const uint16_t *col = xs + (8 * (lane >> 4)) * kMxPitch + 64 * wv + 4 * (lane & 15) + pt;
+      pw_u32x4 af[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          af[kb][q] = (uint32_t)col[(32 * kb + 2 * q) * kMxPitch] | ((uint32_t)col[(32 * kb + 2 * q + 1) * kMxPitch] << 16);
+#pragma unroll
+      for (int ot = 0; ot < 4; ++ot) {
+        acc[pt][ot] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) acc[pt][ot] = pw_mma<DT>(af[kb], wf[ot][kb], acc[pt][ot]);
+      }
+    }
+    if (pin) {
+#pragma unroll
+      for (int ot = 0; ot < 4; ++ot) {
+        const int o = o0 + 16 * ot + (lane & 15);
+        if (o >= O) continue;
+        float v[16];
+        unpack8<DT>(ad[ot][0], *reinterpret_cast<float(*)[8]>(v));
+        unpack8<DT>(ad[ot][1], *reinterpret_cast<float(*)[8]>(v + 8));
+        pw_u32x4 out[2];
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          float t0 = v[e] + acc[e & 3][ot][e >> 2] + bias[ot];
+          float t1 = v[e + 1] + acc[(e + 1) & 3][ot][(e + 1) >> 2] + bias[ot];
+          if (a.act == 1) {
+            t0 = gelu(t0);
+            t1 = gelu(t1);
+          }
+          out[e >> 3][(e >> 1) & 3] = pack2<DT>(t0, t1);
+        }
+        pw_u32x4 *dst = reinterpret_cast<pw_u32x4 *>(reinterpret_cast<uint16_t *>(a.y) + yb + (size_t)o * P + p);
+        dst[0] = out[0];
+        if (p + 8 < P) dst[1] = out[1];
+      }
+    }
+    __syncthreads();
+  }
+}
+
 static constexpr int kMaxJ = 128;
 static constexpr int kMaxC = 4;
 
@@ -281,8 +492,18 @@ static int pw_blocks(long P) {
 hipError_t launch_channel_mix(const void *x, const void *A, const void *bias, const void *add, void *y, int B,
                               int I, int O, long P, int act, int dtype, hipStream_t s) {
   MixArgs a{x, A, bias, add, y, B, I, O, P, act};
-  dim3 grid(pw_blocks(P), (O + kOB - 1) / kOB, B);
   void *args[] = {(void *)&a};
+  if (dtype != DT_F32 && (P & 7) == 0 && I <= 64) {
+    const int KB = I <= 32 ? 1 : 2;
+    const long nch = (P + kMxPx - 1) / kMxPx;
+    dim3 g((unsigned)(nch < 4096 ? nch : 4096), (O + kOB - 1) / kOB, B);
+    const void *k = dtype == DT_F16 ? (KB == 1 ? (const void *)fno_channel_mix_mx<DT_F16, 1>
+                                               : (const void *)fno_channel_mix_mx<DT_F16, 2>)
+                                    : (KB == 1 ? (const void *)fno_channel_mix_mx<DT_BF16, 1>
+                                               : (const void *)fno_channel_mix_mx<DT_BF16, 2>);
+    return hipLaunchKernel(k, g, dim3(kPwThreads), args, 0, s);
+  }
+  dim3 grid(pw_blocks(P), (O + kOB - 1) / kOB, B);
   const bool al = (P & 3) == 0;
   const void *k = dtype == DT_F32 ? (al ? (const void *)fno_channel_mix<DT_F32, true>
                                         : (const void *)fno_channel_mix<DT_F32, false>)

@@ -23,6 +23,12 @@ def _rand(rng, shape, dtype, scale=1.0):
     ("f16", 3, 64, 64, 1000, 1, True),     # block epilogue, ragged pixel count
     ("bf16", 1, 17, 70, 259, 1, True),     # ragged channels (two output blocks)
     ("f32", 2, 128, 5, 64, 0, False),
+    # fp16 / bf16 with P % 8 == 0 run on half-precision matrix cores
+    ("f16", 2, 3, 64, 4096, 0, False),     # lift shape, one 32-channel block
+    ("bf16", 2, 64, 64, 2048, 1, True),    # block epilogue, two blocks
+    ("f16", 1, 60, 70, 520, 1, True),      # two blocks, ragged outputs, half-tile tail (P % 16 == 8)
+    ("bf16", 3, 33, 5, 8, 0, True),        # one pixel group per batch element
+    ("f16", 1, 128, 130, 768, 1, False),   # over 64 inputs: the fp32-operand kernel
 ])
 def test_channel_mix(dtype, B, I, O, P, act, add):
     import torch
