@@ -14,6 +14,8 @@
 // once per workgroup into LDS. Accumulation is fp32; outputs are rounded
 // (RNE) to the storage dtype.
 
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace fno {
@@ -96,6 +98,24 @@ __device__ __forceinline__ void store4(void *p, size_t i, int n, bool al, const 
 }
 
 __device__ __forceinline__ float gelu(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+
+// GELU for the half-precision kernels, whose outputs are rounded to 11 (fp16)
+// or 8 (bf16) significant bits: erf from Abramowitz & Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26, erf(x) = 1 - t (a1 + t (a2 + t (a3 +
+// t (a4 + t a5)))) exp(-x^2), t = 1 / (1 + p x), x >= 0, absolute error below
+// 1.5e-7; odd symmetry for x < 0. One reciprocal and one exp2 on the
+// transcendental unit instead of a full-precision erf.
+__device__ __forceinline__ float gelu_half(float v) {
+  const float x = fabsf(v) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  float q = fmaf(1.061405429f, t, -1.453152027f);
+  q = fmaf(q, t, 1.421413741f);
+  q = fmaf(q, t, -0.284496736f);
+  q = fmaf(q, t, 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(-x * x * 1.4426950408889634f);  // exp(-x^2)
+  const float erfx = fmaf(-q * t, e, 1.0f);
+  return 0.5f * v * (1.0f + copysignf(erfx, v));
+}
 
 static constexpr int kPwThreads = 256;
 static constexpr int kMaxI = 128;   // input channels held per workgroup
@@ -188,12 +208,14 @@ __global__ __launch_bounds__(kPwThreads) void fno_channel_mix(MixArgs a) {
 // A fragments from it. Orientation D[p][o] = x^T W^T: the A operand is 16
 // pixels x 32 channels, the B operand 32 channels x 16 outputs (rows of W,
 // held in registers for the whole kernel). Wave w owns pixels 64 w ..
-// 64 w + 63 of the tile and all 64 output channels of the workgroup; its
-// product rows are assigned to pixels so that every lane ends with 16
-// consecutive pixels of one output channel, and the add input and the
-// output move as 16-byte accesses. The add input is requested before the
-// products. Needs P % 8 == 0 and at most 64 input channels (wider inputs
-// would spill registers).
+// 64 w + 63 of the tile and all 64 output channels of the workgroup. The
+// fp32 results (plus bias) go through an LDS stage, 32 output channels at a
+// time, so that the add input, the fp32 add and GELU, and the output run
+// along whole rows with 16-byte accesses (8 rows x 128 contiguous bytes per
+// wave instruction); the add input is requested before the products and the
+// next tile's channels while they run. Needs
+// P % 8 == 0 and at most 64 input channels (wider inputs would spill
+// registers).
 
 typedef unsigned pw_u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 pw_h8 __attribute__((ext_vector_type(8)));
@@ -280,9 +302,16 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   }
 }
 
+constexpr int kYsPitch = kMxPx + 1;  // floats per row of the output stage: the 16 rows x 4 pixel
+                                     // groups one accumulator write touches fall on 64 distinct banks
+constexpr int kYsRows = 32;          // output channels staged at a time
+
 template <int DT, int KB>
 __global__ __launch_bounds__(kPwThreads) __attribute__((amdgpu_waves_per_eu(2))) void fno_channel_mix_mx(MixArgs a) {
-  __shared__ uint16_t xs[KB * 32 * kMxPitch];
+  constexpr int XS = KB * 32 * kMxPitch * 2, YS = kYsRows * kYsPitch * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[XS > YS ? XS : YS];
+  uint16_t *xs = reinterpret_cast<uint16_t *>(lds);
+  float *ys = reinterpret_cast<float *>(lds);  // reused after the products
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int o0 = blockIdx.y * kOB, b = blockIdx.z;
   const int I = a.I, O = a.O;
@@ -314,33 +343,40 @@ __global__ __launch_bounds__(kPwThreads) __attribute__((amdgpu_waves_per_eu(2)))
     bias[ot] = (a.bias && o < O) ? load1<DT>(a.bias, o) : 0.f;
   }
 
-  // Row r of product tile pt is pixel 64 wv + 4 r + pt, so lane l's
-  // accumulators (rows 4 (l / 16) + j of every tile) are the 16 consecutive
-  // pixels 64 wv + 16 (l / 16) + 4 j + pt of output channel 16 ot + l % 16.
-  const long nch = (P + kMxPx - 1) / kMxPx;
+  // Epilogue ownership: in staged half h (output channels o0 + 32 h ..
+  // + 31), thread t handles row er = t / 8 and pixels 8 (t % 8) + 64 k,
+  // k = 0..3: each 16-byte access of a wave covers 8 rows x 128 bytes.
+  const int er = tid >> 3, ep = 8 * (tid & 7);
+  // a contiguous run of tiles per workgroup, the next tile's channels in
+  // flight while the current one is multiplied and written
+  const long nch = (P + kMxPx - 1) / kMxPx, per = (nch + gridDim.x - 1) / gridDim.x;
+  const long c0 = (long)blockIdx.x * per, c1 = min(nch, c0 + per);
+  // the add input of the tile at pixel q (rows of this thread's epilogue)
+  auto fetch_add = [&](long q, pw_u32x4 (&ad)[2][4]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int o = o0 + 32 * h + er;
+        const long p = q + ep + 64 * k;
+        const bool ok = a.add && o < O && p < P;  // P % 8 == 0: 8 pixels wholly in or out
+        const pw_u32x4 t = *reinterpret_cast<const pw_u32x4 *>(
+            reinterpret_cast<const uint16_t *>(a.add ? a.add : a.x) + (ok ? yb + (size_t)o * P + p : 0));
+        ad[h][k] = ok ? t : pw_u32x4{0u, 0u, 0u, 0u};
+      }
+  };
   pw_u32x4 r[KB * 4];
-  long pc = (long)blockIdx.x * kMxPx;
-  if (pc < P) mixmx_fetch<KB>(xb, I, P, pc, tid, r);
-  for (long c = blockIdx.x; c < nch; c += gridDim.x, pc += (long)gridDim.x * kMxPx) {
+  long pc = c0 * kMxPx;
+  if (c0 < c1) mixmx_fetch<KB>(xb, I, P, pc, tid, r);
+  for (long c = c0; c < c1; ++c, pc += kMxPx) {
     mixmx_put<KB>(xs, tid, r);
     __syncthreads();
-    // this tile's add input, in flight during the products
-    const long p = pc + 64 * wv + 16 * (lane >> 4);
-    const bool pin = p < P;
-    pw_u32x4 ad[4][2];
-#pragma unroll
-    for (int ot = 0; ot < 4; ++ot) {
-      const int o = o0 + 16 * ot + (lane & 15);
-      const bool ok = a.add && pin && o < O;
-      const uint16_t *src = reinterpret_cast<const uint16_t *>(a.add ? a.add : a.x) + (ok ? yb + (size_t)o * P + p : 0);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {  // P % 8 == 0: each half is wholly in or past the row
-        const bool okh = ok && p + 8 * h < P;
-        const pw_u32x4 t = *reinterpret_cast<const pw_u32x4 *>(okh ? src + 8 * h : src);
-        ad[ot][h] = okh ? t : pw_u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    if (c + gridDim.x < nch) mixmx_fetch<KB>(xb, I, P, pc + (long)gridDim.x * kMxPx, tid, r);
+    pw_u32x4 ad[2][4];  // this tile's add input, in flight during the products
+    fetch_add(pc, ad);
+    if (c + 1 < c1) mixmx_fetch<KB>(xb, I, P, pc + kMxPx, tid, r);
+    // Row r of product tile pt is pixel 64 wv + 4 r + pt: lane l's
+    // accumulator j of tile pt is pixel 64 wv + 16 (l / 16) + 4 j + pt of
+    // output channel 16 ot + l % 16.
     v4f acc[4][4];  // [pt][ot]
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
@@ -359,28 +395,40 @@ __global__ __launch_bounds__(kPwThreads) __attribute__((amdgpu_waves_per_eu(2)))
         for (int kb = 0; kb < KB; ++kb) acc[pt][ot] = pw_mma<DT>(af[kb], wf[ot][kb], acc[pt][ot]);
       }
     }
-    if (pin) {
 #pragma unroll
-      for (int ot = 0; ot < 4; ++ot) {
-        const int o = o0 + 16 * ot + (lane & 15);
-        if (o >= O) continue;
-        float v[16];
-        unpack8<DT>(ad[ot][0], *reinterpret_cast<float(*)[8]>(v));
-        unpack8<DT>(ad[ot][1], *reinterpret_cast<float(*)[8]>(v + 8));
-        pw_u32x4 out[2];
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();  // the channel tile (h = 0) or the previous half (h = 1) is no longer read
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          float t0 = v[e] + acc[e & 3][ot][e >> 2] + bias[ot];
-          float t1 = v[e + 1] + acc[(e + 1) & 3][ot][(e + 1) >> 2] + bias[ot];
-          if (a.act == 1) {
-            t0 = gelu(t0);
-            t1 = gelu(t1);
+      for (int oq = 0; oq < 2; ++oq) {
+        const int ot = 2 * h + oq;
+        float *row = ys + (16 * oq + (lane & 15)) * kYsPitch + 64 * wv + 16 * (lane >> 4);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) row[4 * j + pt] = acc[pt][ot][j] + bias[ot];
+      }
+      __syncthreads();
+      const int o = o0 + 32 * h + er;
+      if (o < O) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const long p = pc + ep + 64 * k;
+          if (p >= P) continue;
+          const float *src = ys + er * kYsPitch + ep + 64 * k;
+          float v[8];
+          unpack8<DT>(ad[h][k], v);
+          pw_u32x4 out;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            float t0 = v[e] + src[e], t1 = v[e + 1] + src[e + 1];
+            if (a.act == 1) {
+              t0 = gelu_half(t0);
+              t1 = gelu_half(t1);
+            }
+            out[e >> 1] = pack2<DT>(t0, t1);
           }
-          out[e >> 3][(e >> 1) & 3] = pack2<DT>(t0, t1);
+          *reinterpret_cast<pw_u32x4 *>(reinterpret_cast<uint16_t *>(a.y) + yb + (size_t)o * P + p) = out;
         }
-        pw_u32x4 *dst = reinterpret_cast<pw_u32x4 *>(reinterpret_cast<uint16_t *>(a.y) + yb + (size_t)o * P + p);
-        dst[0] = out[0];
-        if (p + 8 < P) dst[1] = out[1];
       }
     }
     __syncthreads();
@@ -481,6 +529,138 @@ __global__ __launch_bounds__(kPwThreads) void fno_projection(ProjArgs a) {
   }
 }
 
+// ------------------------------------------- half-precision projection
+//
+// fp16 / bf16 storage, I <= 64, J <= 128, C <= 4: the first layer
+// h = GELU(Q1 x + q1) on v_mfma_f32_16x16x32_{f16,bf16} exactly as the
+// channel mix (LDS-staged channel tiles, contiguous runs of 256-pixel tiles
+// per workgroup, D[p][j] with each lane holding 16 consecutive pixels of one
+// hidden unit), in four passes of 32 hidden units. The second layer is per
+// lane: for every pixel, Q2[c][j] h[j] of the lane's hidden units, then a
+// reduce-scatter over the 16 lanes of a row group (partners lane ^ 8, ^ 4,
+// ^ 2, ^ 1, in that fixed order), after which lane e of the group holds the
+// full sum of pixel e. Outputs are stored per row as 64 consecutive pixels
+// per wave.
+
+template <int DT, int KB>
+__global__ __launch_bounds__(kPwThreads) __attribute__((amdgpu_waves_per_eu(2))) void fno_projection_mx(ProjArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[KB * 32 * kMxPitch];
+  __shared__ pw_u32x4 wfs[8][KB][64];  // B fragments of Q1, read per use
+  __shared__ float q1s[kMaxJ], q2s[kMaxC][kMaxJ], q2b[kMaxC];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int b = blockIdx.z;
+  const int I = a.I, J = a.J, C = a.C;
+  const long P = a.P;
+  const uint16_t *xb = reinterpret_cast<const uint16_t *>(a.x) + (size_t)b * I * P;
+  const size_t yb = (size_t)b * C * P;
+  for (int v = tid; v < kMaxJ; v += kPwThreads) q1s[v] = v < J ? load1<DT>(a.q1, v) : 0.f;
+  for (int v = tid; v < kMaxC * kMaxJ; v += kPwThreads) {
+    const int c = v / kMaxJ, j = v - c * kMaxJ;
+    q2s[c][j] = (c < C && j < J) ? load1<DT>(a.Q2, (size_t)c * J + j) : 0.f;
+  }
+  if (tid < kMaxC) q2b[tid] = tid < C ? load1<DT>(a.q2, tid) : 0.f;
+
+  // B fragments of Q1: lane l holds Q1[16 jt + l % 16][32 kb + 8 (l / 16) + t];
+  // wave w builds those of jt = 2 w, 2 w + 1
+  const uint16_t *Q1 = reinterpret_cast<const uint16_t *>(a.Q1);
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int jt = 2 * wv + jj, j = 16 * jt + (lane & 15);
+      uint32_t h[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int i = 32 * kb + 8 * (lane >> 4) + t;
+        h[t] = (j < J && i < I) ? Q1[(size_t)j * I + i] : 0u;
+      }
+      pw_u32x4 f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) f[q] = h[2 * q] | (h[2 * q + 1] << 16);
+      wfs[jt][kb][lane] = f;
+    }
+
+  const long nch = (P + kMxPx - 1) / kMxPx, per = (nch + gridDim.x - 1) / gridDim.x;
+  const long c0 = (long)blockIdx.x * per, c1 = min(nch, c0 + per);
+  pw_u32x4 r[KB * 4];
+  long pc = c0 * kMxPx;
+  if (c0 < c1) mixmx_fetch<KB>(xb, I, P, pc, tid, r);
+  for (long c = c0; c < c1; ++c, pc += kMxPx) {
+    mixmx_put<KB>(xs, tid, r);
+    __syncthreads();
+    if (c + 1 < c1) mixmx_fetch<KB>(xb, I, P, pc + kMxPx, tid, r);
+    float outv[kMaxC] = {0.f, 0.f, 0.f, 0.f};  // lane e of a row group: pixel e of the group
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {  // hidden units in passes of 32 (two 16-wide tiles)
+      v4f acc[4][2];  // [pt][jt within the pass]
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        // A fragments: pixel 64 wv + 4 (l % 16) + pt, channels 32 kb + 8 (l / 16) .. + 7
+        const uint16_t *col = xs + (8 * (lane >> 4)) * kMxPitch + 64 * wv + 4 * (lane & 15) + pt;
+        pw_u32x4 af[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            af[kb][q] =
+                (uint32_t)col[(32 * kb + 2 * q) * kMxPitch] | ((uint32_t)col[(32 * kb + 2 * q + 1) * kMxPitch] << 16);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          acc[pt][q] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) acc[pt][q] = pw_mma<DT>(af[kb], wfs[2 * hh + q][kb][lane], acc[pt][q]);
+        }
+      }
+      // h = GELU(acc + q1) in place; accumulator j of tile pt is pixel 4 j + pt of the group
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float bq = q1s[16 * (2 * hh + q) + (lane & 15)];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[pt][q][j] = gelu_half(acc[pt][q][j] + bq);
+      }
+#pragma unroll
+      for (int cc = 0; cc < kMaxC; ++cc) {
+        if (cc >= C) break;
+        float v[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = 0.f;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float w2 = q2s[cc][16 * (2 * hh + q) + (lane & 15)];
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[4 * j + pt] = fmaf(w2, acc[pt][q][j], v[4 * j + pt]);
+        }
+        // reduce-scatter over the 16 lanes (hidden units) of the row group
+#pragma unroll
+        for (int m = 8, n = 16; m >= 1; m >>= 1, n >>= 1) {
+          const bool up = lane & m;
+#pragma unroll
+          for (int k = 0; k < n / 2; ++k) {
+            const float keep = up ? v[k + n / 2] : v[k], send = up ? v[k] : v[k + n / 2];
+            v[k] = keep + __shfl_xor(send, m, 64);
+          }
+        }
+        outv[cc] += v[0];
+      }
+    }
+    const long p = pc + 64 * wv + 16 * (lane >> 4) + (lane & 15);
+    if (p < P) {
+#pragma unroll
+      for (int cc = 0; cc < kMaxC; ++cc) {
+        if (cc >= C) break;
+        const float y = outv[cc] + q2b[cc];
+        if constexpr (DT == DT_F16) reinterpret_cast<_Float16 *>(a.y)[yb + (size_t)cc * P + p] = (_Float16)y;
+        else reinterpret_cast<uint16_t *>(a.y)[yb + (size_t)cc * P + p] = (uint16_t)f32_to_bf16(y);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 static int pw_blocks(long P) {
@@ -495,8 +675,10 @@ hipError_t launch_channel_mix(const void *x, const void *A, const void *bias, co
   void *args[] = {(void *)&a};
   if (dtype != DT_F32 && (P & 7) == 0 && I <= 64) {
     const int KB = I <= 32 ? 1 : 2;
-    const long nch = (P + kMxPx - 1) / kMxPx;
-    dim3 g((unsigned)(nch < 4096 ? nch : 4096), (O + kOB - 1) / kOB, B);
+    // about 1024 workgroups in all (four per CU), each a contiguous run of tiles
+    const long nch = (P + kMxPx - 1) / kMxPx, rest = (long)B * ((O + kOB - 1) / kOB);
+    const long gx = std::min(nch, std::max(1L, (1024 + rest - 1) / rest));
+    dim3 g((unsigned)gx, (O + kOB - 1) / kOB, B);
     const void *k = dtype == DT_F16 ? (KB == 1 ? (const void *)fno_channel_mix_mx<DT_F16, 1>
                                                : (const void *)fno_channel_mix_mx<DT_F16, 2>)
                                     : (KB == 1 ? (const void *)fno_channel_mix_mx<DT_BF16, 1>
@@ -517,8 +699,18 @@ hipError_t launch_channel_mix(const void *x, const void *A, const void *bias, co
 hipError_t launch_projection(const void *x, const void *Q1, const void *q1, const void *Q2, const void *q2, void *y,
                              int B, int I, int J, int C, long P, int dtype, hipStream_t s) {
   ProjArgs a{x, Q1, q1, Q2, q2, y, B, I, J, C, P};
-  dim3 grid(pw_blocks(P), 1, B);
   void *args[] = {(void *)&a};
+  if (dtype != DT_F32 && (P & 7) == 0 && I <= 64 && J <= kMaxJ && C <= kMaxC) {
+    const int KB = I <= 32 ? 1 : 2;
+    const long nch = (P + kMxPx - 1) / kMxPx;
+    const long gx = std::min(nch, std::max(1L, (1024L + B - 1) / B));
+    const void *k = dtype == DT_F16 ? (KB == 1 ? (const void *)fno_projection_mx<DT_F16, 1>
+                                               : (const void *)fno_projection_mx<DT_F16, 2>)
+                                    : (KB == 1 ? (const void *)fno_projection_mx<DT_BF16, 1>
+                                               : (const void *)fno_projection_mx<DT_BF16, 2>);
+    return hipLaunchKernel(k, dim3((unsigned)gx, 1, B), dim3(kPwThreads), args, 0, s);
+  }
+  dim3 grid(pw_blocks(P), 1, B);
   const bool al = (P & 3) == 0;
   const void *k = dtype == DT_F32 ? (al ? (const void *)fno_projection<DT_F32, true>
                                         : (const void *)fno_projection<DT_F32, false>)

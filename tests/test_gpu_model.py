@@ -49,7 +49,14 @@ def test_channel_mix(dtype, B, I, O, P, act, add):
     assert rel_l2(to_float64(y), ref) <= tol
 
 
-@pytest.mark.parametrize("dtype,B,I,J,C,P", [("f16", 2, 64, 128, 1, 4096), ("f32", 1, 20, 33, 3, 333)])
+@pytest.mark.parametrize("dtype,B,I,J,C,P", [
+    ("f16", 2, 64, 128, 1, 4096),
+    ("f32", 1, 20, 33, 3, 333),
+    # fp16 / bf16 with P % 8 == 0 run on half-precision matrix cores
+    ("bf16", 2, 33, 100, 4, 520),   # two input blocks, ragged hidden units, four outputs
+    ("f16", 3, 20, 128, 2, 8),      # one pixel group per batch element
+    ("bf16", 1, 64, 128, 1, 4096),  # the network's shape
+])
 def test_projection(dtype, B, I, J, C, P):
     import torch
     rng = np.random.default_rng(6)
