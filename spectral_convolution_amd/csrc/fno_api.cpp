@@ -310,13 +310,18 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
   p.bb = contract_pick_bb(batch, c_out, p.K);
   p.split = contract_pick_split(batch, c_in, c_out, p.K, p.bb);
   // The matrix-core contraction gives each workgroup a block of 8 modes x
-  // 16 or 32 batch rows x 32 output channels; with fewer blocks than the
-  // 256 compute units it leaves most of the chip idle, and the per-mode
-  // kernel (one wave per 16 modes, channels split over waves) is faster.
-  p.cmx = contract_mx_supported((int)dtype, c_out, p.K) && contract_mx_workgroups(batch, c_out, p.K) >= 256;
+  // 16 or 32 batch rows x 32 output channels. With fewer blocks than the
+  // 256 compute units it leaves most of the chip idle, and below 16 batch
+  // rows its tiles are mostly padding; there the per-mode kernel (one wave
+  // per 16 modes, channels split over waves) is faster. Measured on the
+  // 256x256, 64-channel layer (modes 32): 9.3 vs 20.3 us at batch 1, 17.4
+  // vs 23.2 at 8, 28.2 vs 25.7 at 16, 71.8 vs 31.9 at 32.
+  p.cmx = contract_mx_supported((int)dtype, c_out, p.K) && contract_mx_workgroups(batch, c_out, p.K) >= 256 &&
+          batch >= 16;
   p.bb_a = contract_pick_bb(batch, c_in, p.K);
   p.split_a = contract_pick_split(batch, c_out, c_in, p.K, p.bb_a);
-  p.cmx_a = contract_mx_supported((int)dtype, c_in, p.K) && contract_mx_workgroups(batch, c_in, p.K) >= 256;
+  p.cmx_a = contract_mx_supported((int)dtype, c_in, p.K) && contract_mx_workgroups(batch, c_in, p.K) >= 256 &&
+            batch >= 16;
   if (!gradw_supported(p.K) || (long)((c_in + 31) / 32) * ((c_out + 31) / 32) > 65535) return FNO_ERR_UNSUPPORTED;
   p.ppw_fg = plane_ppw(true, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_i);
   p.ppw_ib = plane_ppw(false, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_f);
