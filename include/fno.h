@@ -115,7 +115,9 @@ fno_status_t fno_spectral_conv3d(fno_plan_t plan, const void *x, const void *w,
  * All in the plan's dtype (gradients are rounded to it from fp32), 16-byte
  * aligned; outputs must not overlap any other argument. INVALID_ARG when
  * both outputs are NULL or an input an output needs is NULL, or on a plan of
- * the other ndim. Uses the plan's workspace (one call in flight per plan,
+ * the other ndim; UNSUPPORTED when ceil(c_in/32) * ceil(c_out/32) exceeds
+ * 65535 (grad_w) or that product times the retained modes exceeds 2^31 - 1
+ * (grad_x). Uses the plan's workspace (one call in flight per plan,
  * forward or backward); asynchronous on `stream`; allocates nothing. */
 fno_status_t fno_spectral_conv2d_backward(fno_plan_t plan, const void *x,
                                           const void *w, const void *grad_y,

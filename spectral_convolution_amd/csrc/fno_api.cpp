@@ -322,7 +322,6 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
   p.split_a = contract_pick_split(batch, c_out, c_in, p.K, p.bb_a);
   p.cmx_a = contract_mx_supported((int)dtype, c_in, p.K) && contract_mx_workgroups(batch, c_in, p.K) >= 256 &&
             batch >= 16;
-  if (!gradw_supported(p.K) || (long)((c_in + 31) / 32) * ((c_out + 31) / 32) > 65535) return FNO_ERR_UNSUPPORTED;
   p.ppw_fg = plane_ppw(true, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_i);
   p.ppw_ib = plane_ppw(false, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_f);
   p.lds_fg = p.mx ? p.lds_fwd : plane_fwd_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP, p.ppw_fg);
@@ -726,6 +725,10 @@ static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const v
   if (gw && (overlap(gw, nw, gy, ny) || overlap(gw, nw, x, nx) || (w && overlap(gw, nw, w, nw)) ||
              (gx && overlap(gw, nw, gx, nx))))
     return FNO_ERR_INVALID_ARG;
+  // launch-shape limits of the two backward-only kernels
+  if (gw && (!gradw_supported(p->K) || (long)((p->Ci + 31) / 32) * ((p->Co + 31) / 32) > 65535))
+    return FNO_ERR_UNSUPPORTED;
+  if (gx && (long)p->K * ((p->Ci + 31) / 32) * ((p->Co + 31) / 32) > 0x7fffffffL) return FNO_ERR_UNSUPPORTED;
   DeviceGuard g(p->device);
   if (g.err != hipSuccess) return FNO_ERR_DEVICE;
   hipStream_t s = (hipStream_t)stream;
