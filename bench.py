@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused spectral-conv layers/sec + GB/s (% HBM peak) at 128², 256², 64³"
 HBM_PEAK_GBPS = 8000.0
 ROTATE_BYTES = 1 << 30
+MAX_SETS = 64
 
 
 def _bytes_per_launch(cfg, dtype):
@@ -86,7 +87,9 @@ class Layer:
                                         cfg.modes, dtype, 0)
         x0, w0 = to_device(inp["x"], dtype), to_device(inp["w"], dtype)
         per_set = cfg.minimal_bytes(dtype)
-        self.nsets = max(1, math.ceil(ROTATE_BYTES / per_set))
+        # enough sets to exceed the Infinity Cache; tiny layers stay cache-resident
+        # whatever the count, so their rotation is capped
+        self.nsets = min(MAX_SETS, max(1, math.ceil(ROTATE_BYTES / per_set)))
         self.sets = []
         for i in range(self.nsets):
             x = x0 if i == 0 else x0.clone()
@@ -126,7 +129,7 @@ class Backward:
                                         cfg.modes, dtype, 0)
         x0, w0, g0 = (to_device(inp["x"], dtype), to_device(inp["w"], dtype),
                       to_device(gout["g"], dtype))
-        self.nsets = max(1, math.ceil(ROTATE_BYTES / backward_minimal_bytes(cfg, dtype)))
+        self.nsets = min(MAX_SETS, max(1, math.ceil(ROTATE_BYTES / backward_minimal_bytes(cfg, dtype))))
         self.sets = []
         for i in range(self.nsets):
             x, w, g = (x0, w0, g0) if i == 0 else (x0.clone(), w0.clone(), g0.clone())
