@@ -537,10 +537,27 @@ __global__ __launch_bounds__(kPwThreads) void fno_projection(ProjArgs a) {
 // per workgroup, D[p][j] with each lane holding 16 consecutive pixels of one
 // hidden unit), in four passes of 32 hidden units. The second layer is per
 // lane: for every pixel, Q2[c][j] h[j] of the lane's hidden units, then a
-// reduce-scatter over the 16 lanes of a row group (partners lane ^ 8, ^ 4,
-// ^ 2, ^ 1, in that fixed order), after which lane e of the group holds the
-// full sum of pixel e. Outputs are stored per row as 64 consecutive pixels
+// reduce-scatter over the 16 lanes of a row group in four DPP steps (a fixed
+// order), after which lane e of the group holds the full sum of pixel e. Outputs are stored per row as 64 consecutive pixels
 // per wave.
+
+// One step of the 16-lane reduce-scatter: lanes whose bit log2(M) is set keep
+// values M .. 2M - 1, the others 0 .. M - 1, and add the partner's copy of
+// the kept half. Partners by DPP within a row of 16 lanes: M = 8 row_ror:8
+// (lane ^ 8), M = 4 row_half_mirror (lane ^ 7: bit 2 differs, bit 3 kept),
+// M = 2 and 1 quad permutes (lane ^ 2, lane ^ 1). Over the four steps each
+// lane's partners span all 16 lanes of its row.
+template <int M>
+__device__ __forceinline__ void rs_step(float (&v)[16], int lane) {
+  constexpr int ctrl = M == 8 ? 0x128 : M == 4 ? 0x141 : M == 2 ? 0x4e : 0xb1;
+  const bool up = lane & M;
+#pragma unroll
+  for (int k = 0; k < M; ++k) {
+    const float keep = up ? v[k + M] : v[k], send = up ? v[k] : v[k + M];
+    const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), ctrl, 0xf, 0xf, true));
+    v[k] = keep + got;
+  }
+}
 
 template <int DT, int KB>
 __global__ __launch_bounds__(kPwThreads) __attribute__((amdgpu_waves_per_eu(2))) void fno_projection_mx(ProjArgs a) {
@@ -635,15 +652,10 @@ __global__ __launch_bounds__(kPwThreads) __attribute__((amdgpu_waves_per_eu(2)))
             for (int j = 0; j < 4; ++j) v[4 * j + pt] = fmaf(w2, acc[pt][q][j], v[4 * j + pt]);
         }
         // reduce-scatter over the 16 lanes (hidden units) of the row group
-#pragma unroll
-        for (int m = 8, n = 16; m >= 1; m >>= 1, n >>= 1) {
-          const bool up = lane & m;
-#pragma unroll
-          for (int k = 0; k < n / 2; ++k) {
-            const float keep = up ? v[k + n / 2] : v[k], send = up ? v[k] : v[k + n / 2];
-            v[k] = keep + __shfl_xor(send, m, 64);
-          }
-        }
+        rs_step<8>(v, lane);
+        rs_step<4>(v, lane);
+        rs_step<2>(v, lane);
+        rs_step<1>(v, lane);
         outv[cc] += v[0];
       }
     }
