@@ -77,101 +77,113 @@ hipError_t launch_conj_transpose(const void *w, void *wh, int K, int Ci, int Co,
 // v_mfma_f32_16x16x4f32 (fp32 operands, fp32 accumulation), one 16 x 16
 // (i, o) tile of one mode and four batch rows per instruction.
 //
-// A workgroup (4 waves) owns 16 consecutive modes x 32 input x 32 output
-// channels and streams the batch in stages of 4 rows. Each stage's spectra
-// rows ([b][i][16 modes] and [b][o][16 modes], 128 contiguous bytes each)
-// are loaded with 16-byte accesses one stage ahead into registers and
-// stored into LDS per mode as [mode][b][channel] (float2), so a fragment
-// read is 16 consecutive channels per lane group. Wave w multiplies modes
-// 4w .. 4w + 3, all four 16 x 16 tiles. Rows past the batch, channels and
-// modes past their ends load as zeros.
+// A workgroup (4 waves) owns MB consecutive modes x CT input x CT output
+// channels (16 x 32 x 32, or 8 x 16 x 16 when the large tiles would leave
+// most compute units idle) and streams the batch in stages of 4 rows. Each
+// stage's spectra rows ([b][i][MB modes] and [b][o][MB modes], 8 * MB
+// contiguous bytes each) are loaded with 16-byte accesses one stage ahead
+// into registers and stored into LDS per mode as [mode][b][channel]
+// (float2), so a fragment read is 16 consecutive channels per lane group.
+// Wave w multiplies modes w MB/4 .. (w + 1) MB/4 - 1, all (CT/16)^2 tiles.
+// Rows past the batch, channels and modes past their ends load as zeros.
 
-constexpr int kGwT = 256;   // threads per workgroup
-constexpr int kGwM = 16;    // modes per workgroup
-constexpr int kGwC = 32;    // input (and output) channels per workgroup
-constexpr int kGwB = 4;     // batch rows per stage (one MFMA k-step)
-constexpr int kGwP = kGwC + 1;            // float2 per batch row of a staged mode (32 + pad)
-constexpr int kGwS = kGwB * kGwP + 1;     // float2 per staged mode (+ pad: stores spread over banks)
-constexpr int kGwU = kGwB * kGwC * kGwM / 2 / kGwT;  // 16-byte units per thread and operand (= 4)
+constexpr int kGwT = 256;  // threads per workgroup
+constexpr int kGwB = 4;    // batch rows per stage (one MFMA k-step)
+
+template <int MB, int CT>
+struct GwShape {
+  static constexpr int MW = MB / 4;                  // modes per wave
+  static constexpr int NT = CT / 16;                 // 16-wide tiles per channel axis
+  static constexpr int P = CT + 1;                   // float2 per batch row of a staged mode (+ pad)
+  static constexpr int S = kGwB * P + 1;             // float2 per staged mode (+ pad: stores spread over banks)
+  static constexpr int U = kGwB * CT * MB / 2 / kGwT;  // 16-byte units per thread and operand
+  static constexpr int PR = MB / 2;                  // mode pairs per row
+};
 
 typedef unsigned gw_u32x4 __attribute__((ext_vector_type(4)));
 
-// one stage of one operand: rows (b, c) of 16 modes, c fastest, from
+// one stage of one operand: rows (b, c) of MB modes, c fastest, from
 // src[b][c][K] (nc channels); unit u = (row, mode pair)
+template <int MB, int CT>
 __device__ __forceinline__ void gw_fetch(const float2 *src, int nc, int K, int B, int st, int k0, int c0, int tid,
-                                         gw_u32x4 (&p)[kGwU]) {
+                                         gw_u32x4 (&p)[GwShape<MB, CT>::U]) {
+  using G = GwShape<MB, CT>;
 #pragma unroll
-  for (int v = 0; v < kGwU; ++v) {
+  for (int v = 0; v < G::U; ++v) {
     const int u = v * kGwT + tid;
-    const int row = u >> 3, pr = u & 7;
-    const int b = st * kGwB + row / kGwC, c = c0 + row % kGwC, mode = k0 + 2 * pr;
+    const int row = u / G::PR, pr = u % G::PR;
+    const int b = st * kGwB + row / CT, c = c0 + row % CT, mode = k0 + 2 * pr;
     const bool ok = b < B && c < nc && mode < K;
     const gw_u32x4 t = *reinterpret_cast<const gw_u32x4 *>(src + (ok ? ((size_t)b * nc + c) * K + mode : 0));
     p[v] = ok ? t : gw_u32x4{0u, 0u, 0u, 0u};
   }
 }
 
-__device__ __forceinline__ void gw_put(float2 *stage, int tid, const gw_u32x4 (&p)[kGwU]) {
+template <int MB, int CT>
+__device__ __forceinline__ void gw_put(float2 *stage, int tid, const gw_u32x4 (&p)[GwShape<MB, CT>::U]) {
+  using G = GwShape<MB, CT>;
 #pragma unroll
-  for (int v = 0; v < kGwU; ++v) {
+  for (int v = 0; v < G::U; ++v) {
     const int u = v * kGwT + tid;
-    const int row = u >> 3, pr = u & 7;
-    const int b = row / kGwC, c = row % kGwC;
-    stage[(2 * pr) * kGwS + b * kGwP + c] = make_float2(__uint_as_float(p[v][0]), __uint_as_float(p[v][1]));
-    stage[(2 * pr + 1) * kGwS + b * kGwP + c] = make_float2(__uint_as_float(p[v][2]), __uint_as_float(p[v][3]));
+    const int row = u / G::PR, pr = u % G::PR;
+    const int b = row / CT, c = row % CT;
+    stage[(2 * pr) * G::S + b * G::P + c] = make_float2(__uint_as_float(p[v][0]), __uint_as_float(p[v][1]));
+    stage[(2 * pr + 1) * G::S + b * G::P + c] = make_float2(__uint_as_float(p[v][2]), __uint_as_float(p[v][3]));
   }
 }
 
-template <int DT>
+template <int DT, int MB, int CT>
 __global__ __launch_bounds__(kGwT) __attribute__((amdgpu_waves_per_eu(2))) void fno_grad_w(GradWArgs a) {
-  __shared__ float2 xs[kGwM * kGwS], gs[kGwM * kGwS];
+  using G = GwShape<MB, CT>;
+  constexpr int MW = G::MW, NT = G::NT;
+  __shared__ float2 xs[MB * G::S], gs[MB * G::S];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int K = a.K, Ci = a.Ci, Co = a.Co, B = a.B;
   // workgroups of one mode block are gridDim.x apart: with gridDim.x a
   // multiple of 8 they share an XCD (and its L2), where the second read of
   // each spectra row hits
-  const int k0 = blockIdx.x * kGwM;
-  const int nto = (Co + kGwC - 1) / kGwC;
-  const int i0 = (blockIdx.y / nto) * kGwC, o0 = (blockIdx.y % nto) * kGwC;
+  const int k0 = blockIdx.x * MB;
+  const int nto = (Co + CT - 1) / CT;
+  const int i0 = (blockIdx.y / nto) * CT, o0 = (blockIdx.y % nto) * CT;
   const int nst = (B + kGwB - 1) / kGwB;
 
-  v4f accr[4][2][2], acci[4][2][2];
+  v4f accr[MW][NT][NT], acci[MW][NT][NT];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < MW; ++m)
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
+    for (int ti = 0; ti < NT; ++ti)
 #pragma unroll
-      for (int to = 0; to < 2; ++to) {
+      for (int to = 0; to < NT; ++to) {
         accr[m][ti][to] = v4f{0.f, 0.f, 0.f, 0.f};
         acci[m][ti][to] = v4f{0.f, 0.f, 0.f, 0.f};
       }
 
-  gw_u32x4 px[kGwU], pg[kGwU];
-  gw_fetch(a.xs, Ci, K, B, 0, k0, i0, tid, px);
-  gw_fetch(a.gs, Co, K, B, 0, k0, o0, tid, pg);
+  gw_u32x4 px[G::U], pg[G::U];
+  gw_fetch<MB, CT>(a.xs, Ci, K, B, 0, k0, i0, tid, px);
+  gw_fetch<MB, CT>(a.gs, Co, K, B, 0, k0, o0, tid, pg);
   for (int st = 0; st < nst; ++st) {
-    gw_put(xs, tid, px);
-    gw_put(gs, tid, pg);
+    gw_put<MB, CT>(xs, tid, px);
+    gw_put<MB, CT>(gs, tid, pg);
     if (st + 1 < nst) {
-      gw_fetch(a.xs, Ci, K, B, st + 1, k0, i0, tid, px);
-      gw_fetch(a.gs, Co, K, B, st + 1, k0, o0, tid, pg);
+      gw_fetch<MB, CT>(a.xs, Ci, K, B, st + 1, k0, i0, tid, px);
+      gw_fetch<MB, CT>(a.gs, Co, K, B, st + 1, k0, o0, tid, pg);
     }
     __syncthreads();
     // fragment of lane l: batch row l / 16, channel 16 t + l % 16
-    const int fo = (lane >> 4) * kGwP + (lane & 15);
+    const int fo = (lane >> 4) * G::P + (lane & 15);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int mm = 4 * wv + m;
-      float2 x[2], g[2];
+    for (int m = 0; m < MW; ++m) {
+      const int mm = MW * wv + m;
+      float2 x[NT], g[NT];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        x[t] = xs[mm * kGwS + fo + 16 * t];
-        g[t] = gs[mm * kGwS + fo + 16 * t];
+      for (int t = 0; t < NT; ++t) {
+        x[t] = xs[mm * G::S + fo + 16 * t];
+        g[t] = gs[mm * G::S + fo + 16 * t];
       }
 #pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
+      for (int ti = 0; ti < NT; ++ti)
 #pragma unroll
-        for (int to = 0; to < 2; ++to) {
+        for (int to = 0; to < NT; ++to) {
           v4f &cr = accr[m][ti][to], &ci = acci[m][ti][to];
           cr = __builtin_amdgcn_mfma_f32_16x16x4f32(x[ti].x, g[to].x, cr, 0, 0, 0);
           cr = __builtin_amdgcn_mfma_f32_16x16x4f32(x[ti].y, g[to].y, cr, 0, 0, 0);
@@ -185,14 +197,14 @@ __global__ __launch_bounds__(kGwT) __attribute__((amdgpu_waves_per_eu(2))) void 
   // accumulator register j of lane l: row 4 (l / 16) + j (input channel),
   // column l % 16 (output channel); 16 lanes store 16 consecutive outputs
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int mode = k0 + 4 * wv + m;
+  for (int m = 0; m < MW; ++m) {
+    const int mode = k0 + MW * wv + m;
     if (mode >= K) continue;
     const float sc = a.scale * ((mode % a.mlast) == 0 ? 1.0f : 2.0f);
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
+    for (int ti = 0; ti < NT; ++ti)
 #pragma unroll
-      for (int to = 0; to < 2; ++to) {
+      for (int to = 0; to < NT; ++to) {
         const int o = o0 + 16 * to + (lane & 15);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -205,11 +217,18 @@ __global__ __launch_bounds__(kGwT) __attribute__((amdgpu_waves_per_eu(2))) void 
   }
 }
 
-static const void *gradw_kernel(int dtype) {
+// tile shape: the large one when it gives at least 256 workgroups
+static bool gradw_small_tiles(const GradWArgs &a) {
+  const long big = (long)((a.K + 15) / 16) * ((a.Ci + 31) / 32) * ((a.Co + 31) / 32);
+  return big < 256;
+}
+
+template <int MB, int CT>
+static const void *gradw_kernel_t(int dtype) {
   switch (dtype) {
-    case DT_F32: return (const void *)fno_grad_w<DT_F32>;
-    case DT_F16: return (const void *)fno_grad_w<DT_F16>;
-    case DT_BF16: return (const void *)fno_grad_w<DT_BF16>;
+    case DT_F32: return (const void *)fno_grad_w<DT_F32, MB, CT>;
+    case DT_F16: return (const void *)fno_grad_w<DT_F16, MB, CT>;
+    case DT_BF16: return (const void *)fno_grad_w<DT_BF16, MB, CT>;
   }
   return nullptr;
 }
@@ -217,11 +236,13 @@ static const void *gradw_kernel(int dtype) {
 bool gradw_supported(int K) { return (K & 1) == 0; }
 
 hipError_t launch_grad_w(const GradWArgs &a, int dtype, hipStream_t s) {
-  const void *k = gradw_kernel(dtype);
+  const bool small = gradw_small_tiles(a);
+  const int MB = small ? 8 : 16, CT = small ? 16 : 32;
+  const void *k = small ? gradw_kernel_t<8, 16>(dtype) : gradw_kernel_t<16, 32>(dtype);
   if (!k || !gradw_supported(a.K)) return hipErrorInvalidValue;
-  const long gy = (long)((a.Ci + kGwC - 1) / kGwC) * ((a.Co + kGwC - 1) / kGwC);
+  const long gy = (long)((a.Ci + CT - 1) / CT) * ((a.Co + CT - 1) / CT);
   if (gy > 65535) return hipErrorInvalidValue;
-  dim3 grid((a.K + kGwM - 1) / kGwM, (unsigned)gy);
+  dim3 grid((a.K + MB - 1) / MB, (unsigned)gy);
   void *args[] = {(void *)&a};
   return hipLaunchKernel(k, grid, dim3(kGwT), args, 0, s);
 }
