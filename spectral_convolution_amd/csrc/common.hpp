@@ -102,6 +102,11 @@ struct PlaneMxFwdArgs {
   int nplanes, H, W, m1, m2;
   int nt, mt, nn, lgW;  // column tiles of R, m-tiles of X, 16-wide ky tiles, log2 W
   float scale;
+  // two-set variant only: planes nsplit .. nplanes - 1 come from x2 and go
+  // to out2 (indices counted from nsplit)
+  const void *x2;
+  float2 *out2;
+  int nsplit;
 };
 
 struct PlaneMxInvArgs {
@@ -157,9 +162,12 @@ int mx_ntiles(int m2);
 bool mx_supported(int H, int W, int m1, int m2, int dtype);
 size_t mx_fwd_lds_bytes(int H, int W, int dtype);
 size_t mx_inv_lds_bytes(int H, int W, int m1, int m2, int dtype);
-hipError_t mx_prepare(bool fwd, int W, int m1, int m2, int dtype, size_t lds);
-hipError_t mx_grid(bool fwd, int W, int m1, int m2, int dtype, size_t lds, int device, int nplanes, int *grid);
-hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int grid, int dtype, size_t lds, hipStream_t s);
+// two: the forward kernel variant that takes two plane sets (x2 / out2 / nsplit)
+hipError_t mx_prepare(bool fwd, int W, int m1, int m2, int dtype, size_t lds, bool two = false);
+hipError_t mx_grid(bool fwd, int W, int m1, int m2, int dtype, size_t lds, int device, int nplanes, int *grid,
+                   bool two = false);
+hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int grid, int dtype, size_t lds, hipStream_t s,
+                               bool two = false);
 hipError_t launch_plane_mx_inv(const PlaneMxInvArgs &a, int grid, int dtype, size_t lds, hipStream_t s);
 hipError_t axis_fwd_prepare(int MP, size_t lds);
 hipError_t launch_axis_fwd(const AxisArgs &a, int MP, size_t lds, hipStream_t s);

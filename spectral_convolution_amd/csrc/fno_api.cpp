@@ -214,6 +214,7 @@ struct fno_plan_s {
   int ppw_fg = 1, ppw_ib = 1;
   size_t lds_fg = 0, lds_ib = 0;
   int mx_grid_fg = 0, mx_grid_ib = 0;
+  int mx_grid_fb = 0;  // forward planes of x and dL/dy in one launch (2D backward)
   void *wh = nullptr;  // conjugate-transposed weights [K][Co][Ci][2], storage dtype
   // row stage on MFMA (fp16 / bf16 storage, planes with H >= 64, W >= 64)
   bool mx = false;
@@ -493,6 +494,10 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
     if (e == hipSuccess)
       e = mx_grid(false, p->pW, p->pm1, p->pm2, p->dtype, p->lds_inv, p->device, p->B * p->Ci * (ndim == 3 ? p->xN : 1),
                   &p->mx_grid_ib);
+    if (e == hipSuccess && ndim == 2 && (long)p->B * (p->Ci + p->Co) <= 0x7fffffffL)
+      e = mx_grid(true, p->pW, p->pm1, p->pm2, p->dtype, p->lds_fwd, p->device, p->B * (p->Ci + p->Co), &p->mx_grid_fb,
+                  true);
+    if (e == hipSuccess && ndim == 2) e = mx_prepare(true, p->pW, p->pm1, p->pm2, p->dtype, p->lds_fwd, true);
   } else {
     // one kernel serves both channel counts: allow the larger LDS of the two
     if (e == hipSuccess) e = plane_prepare(true, p->pMP, p->rpt, p->dtype, std::max(p->lds_fwd, p->lds_fg));
@@ -564,6 +569,9 @@ static hipError_t fwd_plane_launch(fno_plan_t p, const void *x, int nchan, float
     m.nn = p->mx_nn;
     m.lgW = p->mx_lgW;
     m.scale = nd == 2 ? 1.0f / ((float)p->pH * (float)p->pW) : 1.0f;
+    m.x2 = m.x;
+    m.out2 = m.out;
+    m.nsplit = m.nplanes;
     return launch_plane_mx_fwd(m, own ? p->mx_grid_f : p->mx_grid_fg, p->dtype, p->lds_fwd, s);
   }
   PlaneFwdArgs a;
@@ -582,6 +590,33 @@ static hipError_t fwd_plane_launch(fno_plan_t p, const void *x, int nchan, float
   a.rc = p->rc;
   a.scale = nd == 2 ? 1.0f / ((float)p->pH * (float)p->pW) : 1.0f;
   return launch_plane_fwd(a, p->pMP, p->rpt, p->dtype, own ? p->lds_fwd : p->lds_fg, s);
+}
+
+// 2D matrix-core planes of x (Ci channels) and gy (Co channels) in one
+// launch: spectra of x to xh, of gy to yh
+static hipError_t fwd_planes_both(fno_plan_t p, const void *x, const void *gy, hipStream_t s) {
+  PlaneMxFwdArgs m;
+  m.x = x;
+  m.out = p->xh;
+  m.x2 = gy;
+  m.out2 = p->yh;
+  m.nsplit = p->B * p->Ci;
+  m.nplanes = p->B * (p->Ci + p->Co);
+  m.tw_h = p->tw_h;
+  m.tf = p->tf;
+  m.tf_lo = p->tf_lo;
+  m.ef = p->ef_f;
+  m.ef_lo = p->ef_f_lo;
+  m.H = p->pH;
+  m.W = p->pW;
+  m.m1 = p->pm1;
+  m.m2 = p->pm2;
+  m.nt = p->mx_nt;
+  m.mt = p->mx_mt;
+  m.nn = p->mx_nn;
+  m.lgW = p->mx_lgW;
+  m.scale = 1.0f / ((float)p->pH * (float)p->pW);
+  return launch_plane_mx_fwd(m, p->mx_grid_fb, p->dtype, p->lds_fwd, s, true);
 }
 
 // 3D outer axis, forward: tbuf ([B nchan][X][C]) -> spectra dst, scaled 1/N
@@ -737,12 +772,16 @@ static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const v
   auto step = [&](hipError_t r) {
     if (e == hipSuccess) e = r == hipSuccess ? hipGetLastError() : r;
   };
-  if (gw) {
-    step(fwd_plane_launch(p, x, p->Ci, p->xh, s));
-    if (d3 && e == hipSuccess) step(fwd_axis_launch(p, p->Ci, p->xh, s));
+  if (gw && p->mx && !d3 && p->mx_grid_fb > 0) {
+    step(fwd_planes_both(p, x, gy, s));  // both plane sets, one launch
+  } else {
+    if (gw) {
+      step(fwd_plane_launch(p, x, p->Ci, p->xh, s));
+      if (d3 && e == hipSuccess) step(fwd_axis_launch(p, p->Ci, p->xh, s));
+    }
+    if (e == hipSuccess) step(fwd_plane_launch(p, gy, p->Co, p->yh, s));
+    if (d3 && e == hipSuccess) step(fwd_axis_launch(p, p->Co, p->yh, s));
   }
-  if (e == hipSuccess) step(fwd_plane_launch(p, gy, p->Co, p->yh, s));
-  if (d3 && e == hipSuccess) step(fwd_axis_launch(p, p->Co, p->yh, s));
   if (gw && e == hipSuccess) {
     GradWArgs a;
     a.xs = p->xh;

@@ -176,11 +176,20 @@ struct FwdIO {
   static constexpr int FU = kRows * UR / NT;                       // units per thread and round
 };
 
-template <int DT, int KB, int NW>
-__device__ __forceinline__ void fwd_fetch(const void *x, int g, int lgr, int H, int tid,
+// TW: two plane sets in one launch (planes past nsplit from x2); compiled
+// separately so that the one-set kernels carry no selection
+template <int DT, int KB, int NW, bool TW>
+__device__ __forceinline__ void fwd_fetch(const PlaneMxFwdArgs &a, int g, int lgr, int H, int tid,
                                           u32x4 (&p)[FwdIO<DT, KB, NW>::FU]) {
   using IO = FwdIO<DT, KB, NW>;
-  const size_t plane = (size_t)blockIdx.x + (size_t)(g >> lgr) * gridDim.x;
+  size_t plane = (size_t)blockIdx.x + (size_t)(g >> lgr) * gridDim.x;
+  const void *x = a.x;
+  if constexpr (TW) {
+    if (plane >= (size_t)a.nsplit) {  // the second plane set (uniform per workgroup)
+      x = a.x2;
+      plane -= a.nsplit;
+    }
+  }
   const int r = g & ((1 << lgr) - 1);
   const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(x) + plane * H * IO::W * MxPol<DT>::ES) +
                      (size_t)r * kRows * IO::UR + tid;
@@ -281,7 +290,7 @@ __device__ __forceinline__ int fwd_round_exp(int g, const FwdLds<DT, KB> &L) {
 //    scaled by 2^sig into fp16 range (fp32 as hi + lo parts), with sig from
 //    the round's largest exponent, noted one step earlier; this step notes
 //    that of round g + 1 (registers pn). Returns sig.
-template <int DT, int KB, int NW>
+template <int DT, int KB, int NW, bool TW>
 __device__ __forceinline__ int fwd_put(int g, const FwdShape &s, u32x4 (&p)[FwdIO<DT, KB, NW>::FU],
                                        const u32x4 (&pn)[FwdIO<DT, KB, NW>::FU], const PlaneMxFwdArgs &a,
                                        const FwdLds<DT, KB> &L) {
@@ -318,7 +327,7 @@ __device__ __forceinline__ int fwd_put(int g, const FwdShape &s, u32x4 (&p)[FwdI
   else fwd_note<DT, KB, NW>(g, p, L);
   // unconditional, so that the compiler counts loads exactly; past the end
   // it re-reads the last round (an L2 hit), never used
-  fwd_fetch<DT, KB, NW>(a.x, min(g + kPF, s.total - 1), s.lgr, s.H, tid, p);
+  fwd_fetch<DT, KB, NW, TW>(a, min(g + kPF, s.total - 1), s.lgr, s.H, tid, p);
   return sig;
 }
 
@@ -397,7 +406,7 @@ __device__ __forceinline__ void fwd_row(int g, int se, const FwdShape &s, const 
 // 3. column product of round g's R against the 64-row twiddle block (m-tile
 //    wv of the modes), phase-shifted by the round offset and unscaled into X;
 //    after the last round of a plane, X is scaled, stored and reset.
-template <int DT, int KB, int CPW>
+template <int DT, int KB, int CPW, bool TW>
 __device__ __forceinline__ void fwd_col(int g, int se, const FwdShape &s, const PlaneMxFwdArgs &a,
                                         const FwdLds<DT, KB> &L, const FwdRegs<DT, KB, CPW> &R, float2 (&X)[2][2]) {
   using P = MxPol<DT>;
@@ -458,6 +467,9 @@ __device__ __forceinline__ void fwd_col(int g, int se, const FwdShape &s, const 
   if (r == (1 << s.lgr) - 1) {
     const size_t plane = (size_t)blockIdx.x + (size_t)(g >> s.lgr) * gridDim.x;
     float2 *op = a.out + plane * (2 * s.m1 * s.m2);
+    if constexpr (TW) {
+      if (plane >= (size_t)a.nsplit) op = a.out2 + (plane - a.nsplit) * (2 * s.m1 * s.m2);
+    }
 #pragma unroll
     for (int nn = 0; nn < 2; ++nn) {
       const int ky = nn * 16 + (lane & 15);
@@ -475,15 +487,15 @@ __device__ __forceinline__ void fwd_col(int g, int se, const FwdShape &s, const 
 // One pipeline step: stage round g, one barrier, then round g's row product
 // and round g - 1's column product (different LDS buffers).
 // se_prev: total scale exponent of round g - 1's R (staging and R scale)
-template <int DT, int KB, int CPW, int NW>
+template <int DT, int KB, int CPW, int NW, bool TW>
 __device__ __forceinline__ void fwd_step(int g, int &se_prev, const FwdShape &s, u32x4 (&p)[FwdIO<DT, KB, NW>::FU],
                                          const u32x4 (&pn)[FwdIO<DT, KB, NW>::FU], const PlaneMxFwdArgs &a,
                                          const FwdLds<DT, KB> &L, const FwdRegs<DT, KB, CPW> &R, float2 (&X)[2][2]) {
-  const int sig = fwd_put<DT, KB, NW>(g, s, p, pn, a, L);
+  const int sig = fwd_put<DT, KB, NW, TW>(g, s, p, pn, a, L);
   __syncthreads();
   const int se = fwd_scale<DT, KB, NW>(g, s, L);
   fwd_row<DT, KB, CPW, NW>(g, se, s, L, R);
-  if (g > 0) fwd_col<DT, KB, CPW>(g - 1, se_prev, s, a, L, R, X);
+  if (g > 0) fwd_col<DT, KB, CPW, TW>(g - 1, se_prev, s, a, L, R, X);
   se_prev = se + sig;
 }
 
@@ -493,7 +505,7 @@ __device__ __forceinline__ void fwd_step(int g, int &se_prev, const FwdShape &s,
 // split-operand planes and more than four m-tiles, else 4 (two or more per
 // CU). CPW: R c-tiles per wave in the row product (2 only when that still
 // gives every wave a job).
-template <int DT, int KB, int CPW, int NW>
+template <int DT, int KB, int CPW, int NW, bool TW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void fno_fwd_plane_mx(PlaneMxFwdArgs a) {
   using P = MxPol<DT>;
   using IO = FwdIO<DT, KB, NW>;
@@ -514,7 +526,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // reached its head would make the compiler wait for all loads in flight
   // there, draining the ring every turn.
   u32x4 p0[IO::FU], p1[IO::FU], p2[IO::FU];
-  fwd_fetch<DT, KB, NW>(a.x, 0, lgr, s.H, tid, p0);
+  fwd_fetch<DT, KB, NW, TW>(a, 0, lgr, s.H, tid, p0);
   __builtin_amdgcn_sched_barrier(0);
 
   FwdRegs<DT, KB, CPW> R;
@@ -545,9 +557,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   __builtin_amdgcn_sched_barrier(0);
-  fwd_fetch<DT, KB, NW>(a.x, min(1, s.total - 1), lgr, s.H, tid, p1);
+  fwd_fetch<DT, KB, NW, TW>(a, min(1, s.total - 1), lgr, s.H, tid, p1);
   __builtin_amdgcn_sched_barrier(0);
-  fwd_fetch<DT, KB, NW>(a.x, min(2, s.total - 1), lgr, s.H, tid, p2);
+  fwd_fetch<DT, KB, NW, TW>(a, min(2, s.total - 1), lgr, s.H, tid, p2);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < (kMaxH + IO::NT - 1) / IO::NT; ++i) {
@@ -568,14 +580,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int full = s.total - s.total % kPF;
   int g = 0;
   for (; g < full; g += kPF) {
-    fwd_step<DT, KB, CPW, NW>(g, se_prev, s, p0, p1, a, L, R, X);
-    fwd_step<DT, KB, CPW, NW>(g + 1, se_prev, s, p1, p2, a, L, R, X);
-    fwd_step<DT, KB, CPW, NW>(g + 2, se_prev, s, p2, p0, a, L, R, X);
+    fwd_step<DT, KB, CPW, NW, TW>(g, se_prev, s, p0, p1, a, L, R, X);
+    fwd_step<DT, KB, CPW, NW, TW>(g + 1, se_prev, s, p1, p2, a, L, R, X);
+    fwd_step<DT, KB, CPW, NW, TW>(g + 2, se_prev, s, p2, p0, a, L, R, X);
   }
-  if (g < s.total) fwd_step<DT, KB, CPW, NW>(g, se_prev, s, p0, p1, a, L, R, X);
-  if (g + 1 < s.total) fwd_step<DT, KB, CPW, NW>(g + 1, se_prev, s, p1, p2, a, L, R, X);
+  if (g < s.total) fwd_step<DT, KB, CPW, NW, TW>(g, se_prev, s, p0, p1, a, L, R, X);
+  if (g + 1 < s.total) fwd_step<DT, KB, CPW, NW, TW>(g + 1, se_prev, s, p1, p2, a, L, R, X);
   __syncthreads();
-  fwd_col<DT, KB, CPW>(s.total - 1, se_prev, s, a, L, R, X);
+  fwd_col<DT, KB, CPW, TW>(s.total - 1, se_prev, s, a, L, R, X);
 }
 
 // ------------------------------------------------------------------ inverse
@@ -866,46 +878,53 @@ static FwdCfg fwd_cfg(int W, int m1, int m2, int dtype) {
   return {nw, nt >= 2 && 2 * nt >= nw ? 2 : 1};
 }
 
-template <int DT, int KB>
-static const void *mx_kernel_kb(bool fwd, FwdCfg c, bool small) {
-  if (!fwd) return small ? (const void *)fno_inv_plane_mx<DT, KB, true> : (const void *)fno_inv_plane_mx<DT, KB, false>;
+template <int DT, int KB, bool TW>
+static const void *mx_fwd_kernel(FwdCfg c) {
   if (c.nw == 8)
-    return c.cpw == 2 ? (const void *)fno_fwd_plane_mx<DT, KB, 2, 8> : (const void *)fno_fwd_plane_mx<DT, KB, 1, 8>;
+    return c.cpw == 2 ? (const void *)fno_fwd_plane_mx<DT, KB, 2, 8, TW> : (const void *)fno_fwd_plane_mx<DT, KB, 1, 8, TW>;
   if constexpr (KB == 8 || (DT == DT_F32 && KB == 4)) return nullptr;  // always 8 waves
-  else return c.cpw == 2 ? (const void *)fno_fwd_plane_mx<DT, KB, 2, 4> : (const void *)fno_fwd_plane_mx<DT, KB, 1, 4>;
+  else return c.cpw == 2 ? (const void *)fno_fwd_plane_mx<DT, KB, 2, 4, TW> : (const void *)fno_fwd_plane_mx<DT, KB, 1, 4, TW>;
+}
+
+template <int DT, int KB>
+static const void *mx_kernel_kb(bool fwd, FwdCfg c, bool small, bool two) {
+  if (!fwd) return small ? (const void *)fno_inv_plane_mx<DT, KB, true> : (const void *)fno_inv_plane_mx<DT, KB, false>;
+  return two ? mx_fwd_kernel<DT, KB, true>(c) : mx_fwd_kernel<DT, KB, false>(c);
 }
 
 template <int DT>
-static const void *mx_kernel_dt(bool fwd, int W, FwdCfg c, bool small) {
+static const void *mx_kernel_dt(bool fwd, int W, FwdCfg c, bool small, bool two) {
   switch (W) {
-    case 64: return mx_kernel_kb<DT, 2>(fwd, c, small);
-    case 128: return mx_kernel_kb<DT, 4>(fwd, c, small);
+    case 64: return mx_kernel_kb<DT, 2>(fwd, c, small, two);
+    case 128: return mx_kernel_kb<DT, 4>(fwd, c, small, two);
     case 256:
       if constexpr (DT == DT_F32) return nullptr;
-      else return mx_kernel_kb<DT, 8>(fwd, c, small);
+      else return mx_kernel_kb<DT, 8>(fwd, c, small, two);
   }
   return nullptr;
 }
 
-static const void *mx_kernel(bool fwd, int W, int m1, int m2, int dtype) {
+// two: the forward kernel that takes two plane sets (fwd only)
+static const void *mx_kernel(bool fwd, int W, int m1, int m2, int dtype, bool two = false) {
   const FwdCfg c = fwd_cfg(W, m1, m2, dtype);
   const bool small = inv_small(m1, m2);
-  if (dtype == DT_F16) return mx_kernel_dt<DT_F16>(fwd, W, c, small);
-  if (dtype == DT_BF16) return mx_kernel_dt<DT_BF16>(fwd, W, c, small);
-  if (dtype == DT_F32) return mx_kernel_dt<DT_F32>(fwd, W, c, small);
+  if (dtype == DT_F16) return mx_kernel_dt<DT_F16>(fwd, W, c, small, two);
+  if (dtype == DT_BF16) return mx_kernel_dt<DT_BF16>(fwd, W, c, small, two);
+  if (dtype == DT_F32) return mx_kernel_dt<DT_F32>(fwd, W, c, small, two);
   return nullptr;
 }
 
-hipError_t mx_prepare(bool fwd, int W, int m1, int m2, int dtype, size_t lds) {
-  const void *k = mx_kernel(fwd, W, m1, m2, dtype);
+hipError_t mx_prepare(bool fwd, int W, int m1, int m2, int dtype, size_t lds, bool two) {
+  const void *k = mx_kernel(fwd, W, m1, m2, dtype, two);
   if (!k) return hipErrorInvalidValue;
   return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
 // workgroups of a persistent plane kernel: as many as are resident at once
 // on the device (never more than planes)
-hipError_t mx_grid(bool fwd, int W, int m1, int m2, int dtype, size_t lds, int device, int nplanes, int *grid) {
-  const void *k = mx_kernel(fwd, W, m1, m2, dtype);
+hipError_t mx_grid(bool fwd, int W, int m1, int m2, int dtype, size_t lds, int device, int nplanes, int *grid,
+                   bool two) {
+  const void *k = mx_kernel(fwd, W, m1, m2, dtype, two);
   if (!k) return hipErrorInvalidValue;
   int per_cu = 0, ncu = 0;
   const int threads = fwd ? fwd_cfg(W, m1, m2, dtype).nw * 64 : kFT;
@@ -917,8 +936,8 @@ hipError_t mx_grid(bool fwd, int W, int m1, int m2, int dtype, size_t lds, int d
   return hipSuccess;
 }
 
-hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int grid, int dtype, size_t lds, hipStream_t s) {
-  const void *k = mx_kernel(true, a.W, a.m1, a.m2, dtype);
+hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int grid, int dtype, size_t lds, hipStream_t s, bool two) {
+  const void *k = mx_kernel(true, a.W, a.m1, a.m2, dtype, two);
   if (!k || grid < 1) return hipErrorInvalidValue;
   void *args[] = {(void *)&a};
   return hipLaunchKernel(k, dim3(grid), dim3(fwd_cfg(a.W, a.m1, a.m2, dtype).nw * 64), args, lds, s);
