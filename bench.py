@@ -370,8 +370,10 @@ def cpu_baseline(cfg, dtype, min_seconds=10.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # 100 warm-up and 1000 timed launches per workload (the timed region
+    # of the 128^2 layer is then ~30 ms, of the 256^2 layers ~0.16 s)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="c1")
     ap.add_argument("--dtype", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -430,7 +432,7 @@ def main():
         for name, dt in (("c1", "f16"), ("c2", "f16"), ("c2", "bf16"), ("c3", "f32"), ("c0", "f32")):
             if name == cfg.name and dt == dtype:
                 continue
-            r = measure(wl.CONFIGS[name], dt, max(20, args.steps // 2), max(5, args.warmup // 2))
+            r = measure(wl.CONFIGS[name], dt, args.steps, args.warmup)
             extra.append(r)
             print(f"[bench] {name} {dt}: {r['layers_per_s']:.1f} layers/s, {r['gbps']:.0f} GB/s",
                   file=sys.stderr, flush=True)
