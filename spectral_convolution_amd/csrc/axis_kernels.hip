@@ -108,7 +108,7 @@ static const void *axis_kernel(bool fwd, int MP) {
 hipError_t axis_fwd_prepare(int MP, size_t lds) {
   const void *k = axis_kernel(true, MP);
   if (!k) return hipErrorInvalidValue;
-  return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  return raise_lds_cap(k, lds);
 }
 
 hipError_t launch_axis_fwd(const AxisArgs &a, int MP, size_t lds, hipStream_t s) {

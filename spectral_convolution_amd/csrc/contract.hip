@@ -232,7 +232,7 @@ size_t contract_lds_bytes(int bb, int S) { return S > 1 ? (size_t)S * bb * 32 * 
 hipError_t contract_prepare(int bb, int dtype, int Co, size_t lds) {
   const void *k = bb == 4 ? contract_kernel<4>(dtype, Co) : bb == 2 ? contract_kernel<2>(dtype, Co) : contract_kernel<1>(dtype, Co);
   if (!k) return hipErrorInvalidValue;
-  return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  return raise_lds_cap(k, lds);
 }
 
 hipError_t launch_contract(const ContractArgs &a, int bb, int S, int dtype, hipStream_t s) {

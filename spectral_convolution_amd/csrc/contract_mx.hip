@@ -288,7 +288,7 @@ size_t contract_mx_lds_bytes(int dtype, int B) {
 hipError_t contract_mx_prepare(int dtype, int B) {
   const void *k = contract_mx_kernel(dtype, B);
   if (!k) return hipErrorInvalidValue;
-  return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)contract_mx_lds_bytes(dtype, B));
+  return raise_lds_cap(k, contract_mx_lds_bytes(dtype, B));
 }
 
 hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s) {

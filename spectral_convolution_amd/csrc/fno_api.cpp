@@ -22,6 +22,8 @@
 #include <cstdint>
 #include <algorithm>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -29,6 +31,21 @@
 #include "common.hpp"
 
 using namespace fno;
+
+namespace fno {
+
+hipError_t raise_lds_cap(const void *k, size_t lds) {
+  static std::mutex mu;
+  static std::map<const void *, size_t> caps;
+  std::lock_guard<std::mutex> lock(mu);
+  size_t &cap = caps[k];
+  if (lds <= cap) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess) cap = lds;
+  return e;
+}
+
+}  // namespace fno
 
 namespace {
 

@@ -339,7 +339,7 @@ static const void *plane_kernel(bool fwd, int MP, int rpt, int dtype) {
 hipError_t plane_prepare(bool fwd, int MP, int rpt, int dtype, size_t lds) {
   const void *k = plane_kernel(fwd, MP, rpt, dtype);
   if (!k) return hipErrorInvalidValue;
-  return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  return raise_lds_cap(k, lds);
 }
 
 hipError_t launch_plane_fwd(const PlaneFwdArgs &a, int MP, int rpt, int dtype, size_t lds, hipStream_t s) {

@@ -917,7 +917,7 @@ static const void *mx_kernel(bool fwd, int W, int m1, int m2, int dtype, bool tw
 hipError_t mx_prepare(bool fwd, int W, int m1, int m2, int dtype, size_t lds, bool two) {
   const void *k = mx_kernel(fwd, W, m1, m2, dtype, two);
   if (!k) return hipErrorInvalidValue;
-  return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  return raise_lds_cap(k, lds);
 }
 
 // workgroups of a persistent plane kernel: as many as are resident at once

@@ -146,6 +146,40 @@ def test_parity_many_planes(case):
     assert np.isfinite(got).all()
 
 
+# Several plans alive at once that share kernel instantiations but need
+# different amounts of LDS: each kernel's LDS allowance is per kernel, not per
+# plan, so preparing a smaller plan after a larger one must not shrink it.
+LIVE = [
+    ("live-f32", [_cfg("a", 2, 2, 3, 2, (64, 256), (20, 24), "uniform"),
+                  _cfg("b", 2, 1, 2, 3, (64, 64), (5, 8), "uniform")], "f32"),
+    ("live-f16", [_cfg("a", 2, 1, 4, 4, (256, 256), (24, 24), "uniform"),
+                  _cfg("b", 2, 33, 20, 36, (128, 128), (30, 31), "uniform"),
+                  _cfg("c", 2, 2, 3, 1, (64, 64), (1, 1), "uniform")], "f16"),
+    ("live-3d", [_cfg("a", 3, 1, 4, 4, (32, 64, 64), (8, 16, 16), "uniform"),
+                 _cfg("b", 3, 1, 2, 2, (8, 8, 8), (2, 2, 2), "uniform")], "f32"),
+]
+
+
+@pytest.mark.parametrize("case", LIVE, ids=[c[0] for c in LIVE])
+def test_parity_live_plans(case):
+    name, cfgs, dtype = case
+    plans = [fno.fno_plan_create(c.ndim, c.batch, c.c_in, c.c_out, c.grid, c.modes, dtype, 0)
+             for c in cfgs]
+    try:
+        # run in creation order: every plan after the first was prepared later
+        for c, plan in zip(cfgs, plans):
+            print(f"[parity-live] {name} grid={c.grid} modes={c.modes} B={c.batch}", flush=True)
+            inp = wl.layer_inputs(c, dtype)
+            got, _ = run_layer(c.ndim, c.batch, c.c_in, c.c_out, c.grid, c.modes, dtype,
+                               inp["x"], inp["w"], plan=plan)
+            err = rel_l2(got, _oracle(c, inp["x64"], inp["w64"]))
+            print(f"[parity-live] {name} rel_l2={err:.3e}", flush=True)
+            assert err <= TOL[dtype]
+    finally:
+        for plan in plans:
+            fno.fno_plan_destroy(plan)
+
+
 def test_intermediate_spectra():
     cfg = _cfg("s", 2, 2, 3, 4, (64, 128), (6, 11), "uniform")
     inp = wl.layer_inputs(cfg, "f32")
