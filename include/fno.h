@@ -131,6 +131,36 @@ fno_status_t fno_spectral_conv3d_backward(fno_plan_t plan, const void *x,
                                           void *grad_x, void *grad_w,
                                           void *stream);
 
+/* Weight layouts of a PyTorch FNO module, for fno_weights_pack / _unpack.
+ *
+ * FNO_WEIGHTS_SPLIT: the TurboFNO write-up's form (section 2.2: a weight of
+ *   shape (modes_x, modes_y, in_ch, out_ch); section 4.3: passed to the
+ *   autograd Function as weight_real and weight_imag). Two real arrays,
+ *   each shaped like w without its last axis: 2D [2*m1][m2][Ci][Co],
+ *   3D [2*m1][2*m2][m3][Ci][Co].
+ * FNO_WEIGHTS_CORNERS: one complex array per spectrum corner, channels
+ *   first, stacked: 2D [2][Ci][Co][m1][m2][2] with the low kx corner first;
+ *   3D [4][Ci][Co][m1][m2][m3][2] with corners (lo, lo), (hi, lo), (lo, hi),
+ *   (hi, hi) in (kx, ky). (re, im) interleaved, i.e. the float view of a
+ *   complex tensor; the high corner's index 0 is kx = N - m. */
+typedef enum { FNO_WEIGHTS_SPLIT = 0, FNO_WEIGHTS_CORNERS = 1 } fno_weight_layout_t;
+
+/* Copy a module's weights into the layer's w (pack) or w back out into the
+ * module's layout (unpack; e.g. grad_w of the backward pass). Elements are
+ * moved, never converted: all arrays are in the plan's dtype, on its device,
+ * and a pack followed by an unpack returns the input bit for bit.
+ *   layout  FNO_WEIGHTS_SPLIT: re and im are the two real arrays.
+ *           FNO_WEIGHTS_CORNERS: re is the interleaved array, im is NULL.
+ *   w       [...][Ci][Co][2] as in the forward; out for pack, in for unpack
+ * Asynchronous on `stream`; allocates nothing. INVALID_ARG: NULL plan, w or
+ * re; im NULL for the split layout or not NULL for the corner layout; an
+ * unknown layout; a pointer not aligned to the element size; w overlapping
+ * re or im (unpack: re overlapping im). */
+fno_status_t fno_weights_pack(fno_plan_t plan, int layout, const void *src_re,
+                              const void *src_im, void *w, void *stream);
+fno_status_t fno_weights_unpack(fno_plan_t plan, int layout, const void *w,
+                                void *dst_re, void *dst_im, void *stream);
+
 /* Free the plan's device memory after synchronising its device.
  * fno_plan_destroy(NULL) returns FNO_OK. Destroying a plan twice is
  * undefined. */

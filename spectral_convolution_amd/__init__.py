@@ -15,6 +15,7 @@ __all__ = [
     "fno_plan_destroy", "fno_status_string", "fno_plan_workspace_bytes",
     "fno_plan_num_launches", "fno_plan_launch_name", "fno_plan_run_launch",
     "fno_plan_spectra", "fno_spectral_conv2d_backward", "fno_spectral_conv3d_backward", "SpectralConv", "FnoError", "DTYPES",
+    "fno_weights_pack", "fno_weights_unpack", "SpectralConvFunction", "spectral_conv",
     "fno_channel_mix", "fno_projection", "fno_model2d_create", "fno_model2d_forward",
     "fno_model2d_destroy", "Model2d",
 ]
@@ -69,6 +70,14 @@ class Plan:
         if self.ndim == 2:
             return (2 * self.modes[0], self.modes[1], self.c_in, self.c_out, 2)
         return (2 * self.modes[0], 2 * self.modes[1], self.modes[2], self.c_in, self.c_out, 2)
+
+    def split_shape(self):
+        """Shape of each of weight_real / weight_imag (modes first)."""
+        return self.w_shape()[:-1]
+
+    def corners_shape(self):
+        """Shape of the stacked per-corner weights, channels first, (re, im) last."""
+        return (2 if self.ndim == 2 else 4, self.c_in, self.c_out) + self.modes + (2,)
 
 
 def fno_status_string(status):
@@ -144,6 +153,113 @@ def fno_spectral_conv3d_backward(plan, x, w, grad_y, grad_x, grad_w, stream=None
     check(lib().fno_spectral_conv3d_backward(plan.handle, _ptr(x), _ptr(w), _ptr(grad_y), _ptr(grad_x),
                                              _ptr(grad_w), _stream(stream, plan.device)),
           "fno_spectral_conv3d_backward")
+
+
+_LAYOUTS = {"split": 0, "corners": 1}
+
+
+def _check_repack(plan, layout, w, re, im):
+    import torch
+    if layout not in _LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(_LAYOUTS)}")
+    td = _torch_dtype(plan.dtype)
+    shape = plan.split_shape() if layout == "split" else plan.corners_shape()
+    if layout == "corners" and im is not None:
+        raise ValueError("the corner layout is one interleaved array: pass im=None")
+    if layout == "split" and im is None:
+        raise ValueError("the split layout needs both re and im")
+    checks = [("w", w, plan.w_shape()), ("re", re, shape)] + ([("im", im, shape)] if im is not None else [])
+    for name, t, want in checks:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor")
+        if t.dtype != td:
+            raise ValueError(f"{name} dtype {t.dtype} != plan dtype {td}")
+        if tuple(t.shape) != tuple(want):
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {tuple(want)}")
+
+
+def _as_real(t):
+    import torch
+    return torch.view_as_real(t) if isinstance(t, torch.Tensor) and t.is_complex() else t
+
+
+def fno_weights_pack(plan, layout, re, im, w, stream=None):
+    """Copy a module's weights into the layer's w. layout "split": re / im of
+    plan.split_shape(); "corners": one array of plan.corners_shape() (or the
+    complex tensor it is the float view of) and im=None."""
+    re = _as_real(re)
+    _check_repack(plan, layout, w, re, im)
+    check(lib().fno_weights_pack(plan.handle, _LAYOUTS[layout], _ptr(re), _ptr(im), _ptr(w),
+                                 _stream(stream, plan.device)), "fno_weights_pack")
+
+
+def fno_weights_unpack(plan, layout, w, re, im, stream=None):
+    """Copy w (or a weight gradient in w's layout) out into a module's layout."""
+    re = _as_real(re)
+    _check_repack(plan, layout, w, re, im)
+    check(lib().fno_weights_unpack(plan.handle, _LAYOUTS[layout], _ptr(w), _ptr(re), _ptr(im),
+                                   _stream(stream, plan.device)), "fno_weights_unpack")
+
+
+def _autograd_function():
+    import torch
+
+    class SpectralConvFunction(torch.autograd.Function):
+        """The layer as a PyTorch autograd Function on split weights, the
+        integration the TurboFNO write-up describes (section 4.3): forward
+        takes (input, weight_real, weight_imag), backward returns the three
+        gradients. Weight gradients follow PyTorch's convention for a complex
+        weight w = weight_real + i weight_imag (dL/dRe, dL/dIm). Every step runs
+        in the library's kernels; torch only allocates the tensors."""
+
+        @staticmethod
+        def forward(ctx, x, weight_real, weight_imag, plan):
+            w = torch.empty(plan.w_shape(), dtype=x.dtype, device=x.device)
+            fno_weights_pack(plan, "split", weight_real, weight_imag, w)
+            y = torch.empty(plan.y_shape(), dtype=x.dtype, device=x.device)
+            (fno_spectral_conv2d if plan.ndim == 2 else fno_spectral_conv3d)(plan, x, w, y)
+            ctx.plan = plan
+            ctx.save_for_backward(x, w)
+            return y
+
+        @staticmethod
+        def backward(ctx, grad_y):
+            x, w = ctx.saved_tensors
+            plan = ctx.plan
+            need_x, need_re, need_im = ctx.needs_input_grad[:3]
+            gx = torch.empty_like(x) if need_x else None
+            gw = torch.empty_like(w) if (need_re or need_im) else None
+            if gx is None and gw is None:
+                return None, None, None, None
+            f = fno_spectral_conv2d_backward if plan.ndim == 2 else fno_spectral_conv3d_backward
+            f(plan, x if gw is not None else None, w if gx is not None else None, grad_y.contiguous(), gx, gw)
+            g_re = g_im = None
+            if gw is not None:
+                g_re = torch.empty(plan.split_shape(), dtype=w.dtype, device=w.device)
+                g_im = torch.empty_like(g_re)
+                fno_weights_unpack(plan, "split", gw, g_re, g_im)
+            return gx, g_re if need_re else None, g_im if need_im else None, None
+
+    return SpectralConvFunction
+
+
+_FUNCTION = None
+
+
+def __getattr__(name):
+    # the autograd Function subclasses a torch class; build it on first use so
+    # importing the binding does not import torch
+    global _FUNCTION
+    if name == "SpectralConvFunction":
+        if _FUNCTION is None:
+            _FUNCTION = _autograd_function()
+        return _FUNCTION
+    raise AttributeError(name)
+
+
+def spectral_conv(plan, x, weight_real, weight_imag):
+    """y = layer(x; weight_real + i weight_imag), differentiable in all three."""
+    return __getattr__("SpectralConvFunction").apply(x, weight_real, weight_imag, plan)
 
 
 def fno_plan_destroy(plan):

@@ -21,6 +21,8 @@ SIGNATURES = {
     "fno_spectral_conv3d": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "fno_spectral_conv2d_backward": (_c_int, [_c_void_p] * 7),
     "fno_spectral_conv3d_backward": (_c_int, [_c_void_p] * 7),
+    "fno_weights_pack": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "fno_weights_unpack": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "fno_plan_destroy": (_c_int, [_c_void_p]),
     "fno_status_string": (ctypes.c_char_p, [_c_int]),
     "fno_plan_workspace_bytes": (_c_int, [_c_void_p, ctypes.POINTER(_c_size_t)]),

@@ -148,6 +148,15 @@ struct GradWArgs {
   float scale;
 };
 
+// Weight repacking between the layer's w and a module's layout.
+enum : int { W_SPLIT = 0, W_CORNERS = 1 };
+struct WeightsArgs {
+  void *w;       // [K][Ci][Co][2] storage dtype
+  void *re, *im; // W_SPLIT: [K][Ci][Co] each; W_CORNERS: re = [corner][Ci][Co][modes in corner][2], im unused
+  long n;        // K * Ci * Co
+  int layout, unpack, ndim, Ci, Co, m1, m2, m3, mc;  // mc: modes in one corner
+};
+
 // Allow kernel k at least `lds` bytes of dynamic LDS. The attribute belongs
 // to the kernel, not to a plan, and several live plans can share one
 // kernel, so the cap only ever grows (a later, smaller plan must not lower
@@ -189,6 +198,7 @@ size_t contract_mx_lds_bytes(int dtype, int B);
 hipError_t contract_mx_prepare(int dtype, int B);
 hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s);
 
+hipError_t launch_weights_repack(const WeightsArgs &a, int dtype, hipStream_t s);
 hipError_t launch_conj_transpose(const void *w, void *wh, int K, int Ci, int Co, int dtype, hipStream_t s);
 bool gradw_supported(int K);
 hipError_t launch_grad_w(const GradWArgs &a, int dtype, hipStream_t s);

@@ -821,7 +821,47 @@ static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const v
   return map_err(e);
 }
 
+// Copy between w and a module's weight layout (unpack: w -> user arrays).
+static fno_status_t repack(fno_plan_t p, int layout, void *w, void *re, void *im, bool unpack, void *stream) {
+  if (!p || !w || !re) return FNO_ERR_INVALID_ARG;
+  if (layout != FNO_WEIGHTS_SPLIT && layout != FNO_WEIGHTS_CORNERS) return FNO_ERR_INVALID_ARG;
+  if ((layout == FNO_WEIGHTS_SPLIT) != (im != nullptr)) return FNO_ERR_INVALID_ARG;
+  const size_t es = elem_bytes(p->dtype);
+  if (((uintptr_t)w | (uintptr_t)re | (uintptr_t)im) & (es - 1)) return FNO_ERR_INVALID_ARG;
+  const size_t n = (size_t)p->K * p->Ci * p->Co;
+  const size_t nw = 2 * n * es, nr = (layout == FNO_WEIGHTS_SPLIT ? n : 2 * n) * es;
+  if (overlap(w, nw, re, nr) || (im && (overlap(w, nw, im, nr) || (unpack && overlap(re, nr, im, nr)))))
+    return FNO_ERR_INVALID_ARG;
+  WeightsArgs a{};
+  a.w = w;
+  a.re = re;
+  a.im = im;
+  a.n = (long)n;
+  a.layout = layout == FNO_WEIGHTS_SPLIT ? W_SPLIT : W_CORNERS;
+  a.unpack = unpack ? 1 : 0;
+  a.ndim = p->ndim;
+  a.Ci = p->Ci;
+  a.Co = p->Co;
+  a.m1 = p->modes[0];
+  a.m2 = p->modes[1];
+  a.m3 = p->ndim == 3 ? p->modes[2] : 1;
+  a.mc = a.m1 * a.m2 * a.m3;
+  DeviceGuard g(p->device);
+  if (g.err != hipSuccess) return FNO_ERR_DEVICE;
+  return map_err(launch_weights_repack(a, p->dtype, (hipStream_t)stream));
+}
+
 extern "C" {
+
+fno_status_t fno_weights_pack(fno_plan_t plan, int layout, const void *src_re, const void *src_im, void *w,
+                              void *stream) {
+  return repack(plan, layout, w, const_cast<void *>(src_re), const_cast<void *>(src_im), false, stream);
+}
+
+fno_status_t fno_weights_unpack(fno_plan_t plan, int layout, const void *w, void *dst_re, void *dst_im,
+                                void *stream) {
+  return repack(plan, layout, const_cast<void *>(w), dst_re, dst_im, true, stream);
+}
 
 fno_status_t fno_spectral_conv2d(fno_plan_t plan, const void *x, const void *w, void *y, void *stream) {
   return exec(plan, 2, x, w, y, stream, -1);

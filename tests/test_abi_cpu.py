@@ -84,6 +84,8 @@ def test_null_arguments(L):
     assert L.fno_spectral_conv3d(None, p, p, p, None) == INVALID
     assert L.fno_spectral_conv2d_backward(None, p, p, p, p, p, None) == INVALID
     assert L.fno_spectral_conv3d_backward(None, p, p, p, p, p, None) == INVALID
+    assert L.fno_weights_pack(None, 0, p, p, p, None) == INVALID
+    assert L.fno_weights_unpack(None, 1, p, p, None, None) == INVALID
     n = ctypes.c_int()
     assert L.fno_plan_num_launches(None, ctypes.byref(n)) == INVALID
     sz = ctypes.c_size_t()
