@@ -146,6 +146,30 @@ def test_parity_many_planes(case):
     assert np.isfinite(got).all()
 
 
+# The largest axis (256) and the largest retained-mode count (32 per axis)
+# on every kernel family: the VALU plane path at its widest register FFT
+# (fp32, 256 wide), the 3D x-axis pass over 256 slabs, the matrix-core plane
+# path inside a 3D plan at 256 x 256, and a 256-long x axis with 32 kx.
+MAXIMA = [
+    ("max2d-valu-f32", _cfg("x", 2, 1, 2, 1, (256, 256), (32, 32), "uniform"), "f32"),
+    ("max3d-axis-f32", _cfg("x", 3, 1, 1, 2, (256, 64, 256), (32, 16, 32), "uniform"), "f32"),
+    ("max3d-mx-f16", _cfg("x", 3, 1, 2, 1, (64, 256, 256), (32, 32, 32), "uniform"), "f16"),
+    ("max3d-mx-bf16", _cfg("x", 3, 1, 1, 1, (256, 128, 128), (32, 32, 32), "uniform"), "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", MAXIMA, ids=[c[0] for c in MAXIMA])
+def test_parity_maximum_sizes(case):
+    name, cfg, dtype = case
+    print(f"[parity-max] {name} grid={cfg.grid} modes={cfg.modes}", flush=True)
+    inp = wl.layer_inputs(cfg, dtype)
+    got, _ = run_layer(cfg.ndim, cfg.batch, cfg.c_in, cfg.c_out, cfg.grid, cfg.modes, dtype,
+                       inp["x"], inp["w"])
+    err = rel_l2(got, _oracle(cfg, inp["x64"], inp["w64"]))
+    print(f"[parity-max] {name} rel_l2={err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+
+
 # Several plans alive at once that share kernel instantiations but need
 # different amounts of LDS: each kernel's LDS allowance is per kernel, not per
 # plan, so preparing a smaller plan after a larger one must not shrink it.
