@@ -14,8 +14,12 @@ it. Prints one JSON line:
   average launch time (HIP events on the stream it runs on);
 * cpu_baseline: the float64 oracle timed on this host's cores on the same
   workload;
-* configs: the same layers/s and GB/s figures for the 128^2 fp16, 256^2
-  fp16 / bf16 and 64^3 fp32 layers;
+* per_layer_us: the distribution (p50, mean, std, min) of single layers
+  inside the rotating back-to-back loop, and hot_single_set_layers_per_s:
+  the same loop on one buffer set (which the Infinity Cache may serve;
+  labelled, never the headline);
+* configs: the same figures for the 128^2 fp16, 256^2 fp16 / bf16, 64^3
+  fp32 and 16^2 fp32 layers;
 * latency: per-call latency (mean, std, min over individually timed calls)
   of the 128^2 fp32 layer shape at batch 1, 2, 4, 8, launched eagerly and
   replayed from a captured HIP graph, with the throughput gain from batch 1
@@ -286,6 +290,21 @@ def _time_loop(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps  # ms per call
 
 
+def _per_call(fn, n, stream):
+    """Per-call times in µs inside a back-to-back stream of calls: one event
+    between consecutive calls, no synchronisation until the end."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record(stream)
+    for i in range(n):
+        fn(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t = np.array([ev[i].elapsed_time(ev[i + 1]) * 1000.0 for i in range(n)])
+    return {"mean": float(t.mean()), "std": float(t.std()), "min": float(t.min()),
+            "p50": float(np.median(t)), "n": n}
+
+
 def _kernel_times(lay, steps, warmup):
     """Average duration of each launch of the layer: `steps` back-to-back
     launches of that kernel alone (rotating buffer sets) between two HIP
@@ -302,6 +321,12 @@ def measure(cfg, dtype, steps, warmup, per_kernel=True):
                "layers_per_s": 1000.0 / ms,
                "gbps": cfg.minimal_bytes(dtype) / (ms * 1e-3) / 1e9}
         res["hbm_frac"] = res["gbps"] / HBM_PEAK_GBPS
+        # distribution of single layers inside the rotating back-to-back loop
+        res["per_layer_us"] = _per_call(lay.step, min(steps, 500), lay.stream)
+        # one buffer set reused: x, w and y may then be served from the
+        # Infinity Cache, so this is not the HBM-bound figure
+        hot = _time_loop(lambda i: lay.step(0), steps, max(2, warmup // 4), lay.stream)
+        res["hot_single_set_layers_per_s"] = 1000.0 / hot
         if per_kernel:
             bpl = _bytes_per_launch(cfg, dtype)
             kms = _kernel_times(lay, steps, max(2, warmup // 4))
@@ -426,6 +451,8 @@ def main():
                      "traffic": measured_traffic(dom["kernel"], cfg.name, dtype),
                      "bytes_per_launch": dom["bytes"], "ms_per_launch": dom["ms"]},
         "kernels": main_res["kernels"],
+        "per_layer_us": main_res["per_layer_us"],
+        "hot_single_set_layers_per_s": main_res["hot_single_set_layers_per_s"],
     }
     if not args.no_extra:
         extra = []
@@ -434,7 +461,10 @@ def main():
                 continue
             r = measure(wl.CONFIGS[name], dt, args.steps, args.warmup)
             extra.append(r)
-            print(f"[bench] {name} {dt}: {r['layers_per_s']:.1f} layers/s, {r['gbps']:.0f} GB/s",
+            d = r["per_layer_us"]
+            print(f"[bench] {name} {dt}: {r['layers_per_s']:.1f} layers/s, {r['gbps']:.0f} GB/s; "
+                  f"per layer p50 {d['p50']:.1f} us (mean {d['mean']:.1f}, std {d['std']:.1f}, "
+                  f"min {d['min']:.1f}); one buffer set {r['hot_single_set_layers_per_s']:.0f} layers/s",
                   file=sys.stderr, flush=True)
         out["configs"] = extra
     if not args.no_backward:
