@@ -378,7 +378,10 @@ def cpu_baseline(cfg, dtype, min_seconds=10.0):
     inp = wl.layer_inputs(cfg, dtype)
     f = oracle.spectral_conv2d if cfg.ndim == 2 else oracle.spectral_conv3d
     with threadpool_limits(limits=cores):
-        used = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        pools = threadpool_info()
+        used = max([p.get("num_threads", 1) for p in pools] + [1])
+        blas = ", ".join(sorted({f"{p.get('internal_api', '?')} {p.get('version') or ''}".strip()
+                                 for p in pools if p.get("user_api") == "blas"})) or "unknown"
         f(inp["x64"], inp["w64"], *cfg.modes)  # warm-up
         n, t0 = 0, time.perf_counter()
         while True:
@@ -389,7 +392,7 @@ def cpu_baseline(cfg, dtype, min_seconds=10.0):
                 break
     return {"value": n / el, "unit": "layers/s", "cores": int(used), "kind": "oracle",
             "sample": f"whole {cfg.name} {dtype} layer (B={cfg.batch}), {n} runs in {el:.1f} s "
-                      f"after one warm-up, float64 numpy, host affinity {cores} cores"}
+                      f"after one warm-up, float64 numpy (BLAS: {blas}), host affinity {cores} cores"}
 
 
 def main():
