@@ -160,7 +160,8 @@ struct WeightsArgs {
 // Allow kernel k at least `lds` bytes of dynamic LDS. The attribute belongs
 // to the kernel, not to a plan, and several live plans can share one
 // kernel, so the cap only ever grows (a later, smaller plan must not lower
-// it under an earlier one's launches). Thread-safe.
+// it under an earlier one's launches). Kept per device (the current one).
+// Thread-safe.
 hipError_t raise_lds_cap(const void *k, size_t lds);
 
 // host launchers (defined next to their kernels)

@@ -24,6 +24,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <utility>
 #include <new>
 #include <vector>
 
@@ -36,9 +37,11 @@ namespace fno {
 
 hipError_t raise_lds_cap(const void *k, size_t lds) {
   static std::mutex mu;
-  static std::map<const void *, size_t> caps;
+  static std::map<std::pair<int, const void *>, size_t> caps;  // (device, kernel) -> allowance
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
   std::lock_guard<std::mutex> lock(mu);
-  size_t &cap = caps[k];
+  size_t &cap = caps[{dev, k}];
   if (lds <= cap) return hipSuccess;
   const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e == hipSuccess) cap = lds;
