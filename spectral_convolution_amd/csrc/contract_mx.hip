@@ -14,27 +14,28 @@
 // hi + lo (exact: 11 bits), bf16 weights as they are. Products: Xh Wh + Xl Wh
 // (+ Xh Wl for fp16 weights) on v_mfma_f32_16x16x32_bf16.
 //
-// A workgroup owns 8 consecutive modes x 16 or 32 batch rows x 32 output
-// channels and streams the input channels in stages of 16: the spectra rows
-// [b][i][8 modes] (64 contiguous bytes) and weight rows [mode][i][32 o]
+// A workgroup owns MB = 8 (or 4) consecutive modes x 16 or 32 batch rows x
+// 32 output channels and streams the input channels in stages of 16: the
+// spectra rows [b][i][MB modes] (8 MB contiguous bytes) and weight rows [mode][i][32 o]
 // (128 bytes) are loaded with 16-byte accesses one stage ahead into
 // registers, split and transposed into LDS as MFMA fragments, and multiplied
-// there. The results leave through LDS as rows of 8 modes of Yh[b][o][k].
+// there. The results leave through LDS as rows of MB modes of Yh[b][o][k].
+// Four-mode workgroups (half the LDS and registers, so more of them fit on a
+// CU) are used when eight-mode ones would leave resident slots empty.
 
 #include "common.hpp"
+
+#include <algorithm>
 
 namespace fno {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 
-constexpr int kCT = 256;  // threads per workgroup (4 waves, 2 modes each)
-constexpr int kMB = 8;    // modes per workgroup
+constexpr int kCT = 256;  // threads per workgroup (4 waves, MB / 4 modes each)
 constexpr int kIC = 16;   // input channels per stage (one 32-deep block of K)
 constexpr int kOT = 32;   // output channels per workgroup (four 16-column tiles of N)
 constexpr int kSP = 40;   // halves per staged fragment row (32 + 8 pad: conflict-free reads)
-constexpr int kYO = 20;   // floats per output-channel row of the result stage (16 + 4 pad)
-constexpr int kYB = kOT * kYO + 4;  // floats per batch row of the result stage
 
 __device__ __forceinline__ v4f mma_bf(u32x4 a, u32x4 b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
@@ -47,26 +48,31 @@ __device__ __forceinline__ void split_pair(float re, float im, uint32_t &hi, uin
   lo = f32x2_to_bf16x2(re - __uint_as_float(hi << 16), im - __uint_as_float(hi & 0xffff0000u));
 }
 
-template <int DT, int MT>
+template <int DT, int MT, int MB>
 struct CmxShape {
+  static constexpr int MW = MB / 4;                         // modes per wave
+  static constexpr int UX = MB / 2;                         // 16-byte units (two modes) per spectra / result row
+  static constexpr int YO = 2 * MB + 4;                     // floats per output-channel row of the result stage (+ 4 pad)
+  static constexpr int YB = kOT * YO + 4;                   // floats per batch row of the result stage
   static constexpr int BT = 16 * MT;                        // batch rows per workgroup
   static constexpr int HL = DT == DT_F16 ? 2 : 1;          // weight parts
-  static constexpr int XU = kMB * BT * kIC * 8 / (16 * kCT);   // 16-byte spectra units per thread and stage
-  static constexpr int WU = kMB * kIC * kOT * 4 / (16 * kCT);  // 16-byte weight units per thread and stage
+  static constexpr int XU = MB * BT * kIC * 8 / (16 * kCT);   // 16-byte spectra units per thread and stage
+  static constexpr int WU = MB * kIC * kOT * 4 / (16 * kCT);  // 16-byte weight units per thread and stage
   static constexpr int XB = BT * kSP;                        // halves of one (mode, part) block
-  static constexpr int XS = kMB * 2 * XB;                    // halves of the spectra stage
-  static constexpr int WS = kMB * HL * kOT * kSP;           // halves of the weight stage
+  static constexpr int XS = MB * 2 * XB;                    // halves of the spectra stage
+  static constexpr int WS = MB * HL * kOT * kSP;           // halves of the weight stage
 };
 
-template <int DT, int MT>
+template <int DT, int MT, int MB>
 __device__ __forceinline__ void cmx_fetch(const ContractArgs &a, int st, int k0, int b0, int o0, int tid,
-                                          u32x4 (&px)[CmxShape<DT, MT>::XU], u32x4 (&pw)[CmxShape<DT, MT>::WU]) {
-  using S = CmxShape<DT, MT>;
+                                          u32x4 (&px)[CmxShape<DT, MT, MB>::XU],
+                                          u32x4 (&pw)[CmxShape<DT, MT, MB>::WU]) {
+  using S = CmxShape<DT, MT, MB>;
   const int K = a.K, Ci = a.Ci, Co = a.Co, B = a.B;
 #pragma unroll
   for (int v = 0; v < S::XU; ++v) {
     const int u = v * kCT + tid;
-    const int row = u >> 2, c = u & 3;  // row = (b, i), i fastest; c: modes 2c, 2c + 1
+    const int row = u / S::UX, c = u % S::UX;  // row = (b, i), i fastest; c: modes 2c, 2c + 1
     const int b = b0 + row / kIC, i = st * kIC + row % kIC, mode = k0 + 2 * c;
     const bool ok = b < B && i < Ci && mode < K;
     const u32x4 t = *reinterpret_cast<const u32x4 *>(a.xh + (ok ? ((size_t)b * Ci + i) * K + mode : 0));
@@ -98,14 +104,14 @@ __device__ __forceinline__ int wcol(int i, int o) { return (i + ((o >> 4) & 1) *
 
 // split and transpose one stage into fragment rows:
 //   xs[mode][part][b][2 i + re/im], ws[mode][part][o][2 i + re/im]
-template <int DT, int MT>
-__device__ __forceinline__ void cmx_put(uint16_t *xs, uint16_t *ws, int tid, const u32x4 (&px)[CmxShape<DT, MT>::XU],
-                                        const u32x4 (&pw)[CmxShape<DT, MT>::WU]) {
-  using S = CmxShape<DT, MT>;
+template <int DT, int MT, int MB>
+__device__ __forceinline__ void cmx_put(uint16_t *xs, uint16_t *ws, int tid, const u32x4 (&px)[CmxShape<DT, MT, MB>::XU],
+                                        const u32x4 (&pw)[CmxShape<DT, MT, MB>::WU]) {
+  using S = CmxShape<DT, MT, MB>;
 #pragma unroll
   for (int v = 0; v < S::XU; ++v) {
     const int u = v * kCT + tid;
-    const int row = u >> 2, c = u & 3;
+    const int row = u / S::UX, c = u % S::UX;
     const int b = row / kIC, i = row % kIC;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -150,9 +156,16 @@ __device__ __forceinline__ u32x4 w_form(u32x4 raw, bool part1) {
   return o;
 }
 
-template <int DT, int MT>
-__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(2))) void fno_contract_mx(ContractArgs a) {
-  using S = CmxShape<DT, MT>;
+// Waves per SIMD the register allocation targets: two for eight-mode
+// workgroups (the LDS allows two per CU), three (fp16 weights, split in two
+// parts) or four for four-mode ones.
+template <int DT, int MB>
+constexpr int cmx_waves() { return MB == 8 ? 2 : DT == DT_F16 ? 3 : 4; }
+
+template <int DT, int MT, int MB>
+__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<DT, MB>()))) void fno_contract_mx(
+    ContractArgs a) {
+  using S = CmxShape<DT, MT, MB>;
   extern __shared__ uint16_t sm[];
   uint16_t *xs = sm;
   uint16_t *ws = xs + S::XS;
@@ -164,33 +177,33 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(2))) void f
   // fastest: the tiles of a block, and neighbouring mode blocks (the two
   // halves of each 128-byte line of spectra), run on one XCD at about the
   // same time, so repeated reads hit its L2.
-  const int NO = (Co + kOT - 1) / kOT, NKB = ((K + kMB - 1) / kMB) * ((B + S::BT - 1) / S::BT);
+  const int NO = (Co + kOT - 1) / kOT, NKB = ((K + MB - 1) / MB) * ((B + S::BT - 1) / S::BT);
   const int per = (NKB + 7) / 8;  // blocks per XCD
   const int rest = (int)blockIdx.x >> 3;
   const int tkb = ((int)blockIdx.x & 7) * per + rest / NO;
   if (rest / NO >= per || tkb >= NKB) return;  // padding of the last XCD's range
-  const int NK = (K + kMB - 1) / kMB;
-  const int k0 = (tkb % NK) * kMB, b0 = (tkb / NK) * S::BT, o0 = (rest % NO) * kOT;
+  const int NK = (K + MB - 1) / MB;
+  const int k0 = (tkb % NK) * MB, b0 = (tkb / NK) * S::BT, o0 = (rest % NO) * kOT;
   const int nst = (a.Ci + kIC - 1) / kIC;
   const bool part1 = lane & 1;
 
-  v4f acc[2][MT][4];
+  v4f acc[S::MW][MT][4];
 #pragma unroll
-  for (int mm = 0; mm < 2; ++mm)
+  for (int mm = 0; mm < S::MW; ++mm)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) acc[mm][mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
   u32x4 px[S::XU], pw[S::WU];
-  cmx_fetch<DT, MT>(a, 0, k0, b0, o0, tid, px, pw);
+  cmx_fetch<DT, MT, MB>(a, 0, k0, b0, o0, tid, px, pw);
   for (int st = 0; st < nst; ++st) {
-    cmx_put<DT, MT>(xs, ws, tid, px, pw);
-    if (st + 1 < nst) cmx_fetch<DT, MT>(a, st + 1, k0, b0, o0, tid, px, pw);
+    cmx_put<DT, MT, MB>(xs, ws, tid, px, pw);
+    if (st + 1 < nst) cmx_fetch<DT, MT, MB>(a, st + 1, k0, b0, o0, tid, px, pw);
     __syncthreads();
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      const int m = 2 * wv + mm;
+    for (int mm = 0; mm < S::MW; ++mm) {
+      const int m = S::MW * wv + mm;
       u32x4 af[MT][2];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -228,34 +241,34 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(2))) void f
   }
 
   // results -> LDS ys[b][o][8 modes] (re, im) -> rows of 8 modes of Yh, 16
-  // batch rows at a time; row pitches of kYO and kYB floats keep the
+  // batch rows at a time; row pitches of YO and YB floats keep the
   // stores to at most two lanes per bank
   float *ys = reinterpret_cast<float *>(sm);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     if (mt > 0) __syncthreads();
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm)
+    for (int mm = 0; mm < S::MW; ++mm)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const int n = nt * 16 + (lane & 15), o = n >> 1, part = n & 1;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int b = 4 * (lane >> 4) + j;
-          ys[b * kYB + o * kYO + (2 * wv + mm) * 2 + part] = acc[mm][mt][nt][j];
+          ys[b * S::YB + o * S::YO + (S::MW * wv + mm) * 2 + part] = acc[mm][mt][nt][j];
         }
       }
     __syncthreads();
-    constexpr int YU = 16 * kOT * kMB * 8 / 16 / kCT;  // 16-byte result units per thread
+    constexpr int YU = 16 * kOT * MB * 8 / 16 / kCT;  // 16-byte result units per thread
 #pragma unroll
     for (int v = 0; v < YU; ++v) {
       const int u = v * kCT + tid;
-      const int row = u >> 2, c = u & 3;  // row = (b, o); c: modes 2c, 2c + 1
+      const int row = u / S::UX, c = u % S::UX;  // row = (b, o); c: modes 2c, 2c + 1
       const int bl = row / kOT, ol = row % kOT;
       const int b = b0 + mt * 16 + bl, o = o0 + ol, mode = k0 + 2 * c;
       if (b < B && o < Co && mode < K)
         *reinterpret_cast<u32x4 *>(a.yh + ((size_t)b * Co + o) * K + mode) =
-            *reinterpret_cast<const u32x4 *>(ys + bl * kYB + ol * kYO + 4 * c);
+            *reinterpret_cast<const u32x4 *>(ys + bl * S::YB + ol * S::YO + 4 * c);
     }
   }
 }
@@ -266,41 +279,65 @@ bool contract_mx_supported(int dtype, int Co, int K) {
   return (dtype == DT_F16 || dtype == DT_BF16) && (Co & 3) == 0 && (K & 1) == 0;
 }
 
+// Eight-mode workgroups (the tiling the plan's choice of this kernel is
+// measured on)
 long contract_mx_workgroups(int B, int Co, int K) {
   const long BT = B <= 16 ? 16 : 32;
-  return (long)((K + kMB - 1) / kMB) * ((B + BT - 1) / BT) * ((Co + kOT - 1) / kOT);
+  return (long)((K + 7) / 8) * ((B + BT - 1) / BT) * ((Co + kOT - 1) / kOT);
 }
 
-static const void *contract_mx_kernel(int dtype, int B) {
+// Modes per workgroup: 8 unless that leaves resident slots empty (two
+// eight-mode workgroups fit on each of the 256 CUs); then 4, which doubles
+// the workgroups. Measured: the FNO2d layer (B = 20, 64 -> 64 channels,
+// modes 24 x 24: 288 eight-mode workgroups) runs faster with 4, the 256^2
+// layer (B = 32, 64 channels, 32 x 32 modes: 512) slower.
+static int cmx_modes(int B, int Co, int K) { return contract_mx_workgroups(B, Co, K) < 512 ? 4 : 8; }
+
+template <int DT>
+static const void *contract_mx_kernel_dt(int B, int mb) {
   const bool one = B <= 16;
-  if (dtype == DT_F16) return one ? (const void *)fno_contract_mx<DT_F16, 1> : (const void *)fno_contract_mx<DT_F16, 2>;
-  if (dtype == DT_BF16) return one ? (const void *)fno_contract_mx<DT_BF16, 1> : (const void *)fno_contract_mx<DT_BF16, 2>;
+  if (mb == 4) return one ? (const void *)fno_contract_mx<DT, 1, 4> : (const void *)fno_contract_mx<DT, 2, 4>;
+  return one ? (const void *)fno_contract_mx<DT, 1, 8> : (const void *)fno_contract_mx<DT, 2, 8>;
+}
+
+static const void *contract_mx_kernel(int dtype, int B, int mb) {
+  if (dtype == DT_F16) return contract_mx_kernel_dt<DT_F16>(B, mb);
+  if (dtype == DT_BF16) return contract_mx_kernel_dt<DT_BF16>(B, mb);
   return nullptr;
 }
 
-size_t contract_mx_lds_bytes(int dtype, int B) {
+static size_t contract_mx_lds_bytes(int dtype, int B, int mb) {
   const int BT = B <= 16 ? 16 : 32, HL = dtype == DT_F16 ? 2 : 1;
-  const size_t stage = ((size_t)kMB * 2 * BT * kSP + (size_t)kMB * HL * kOT * kSP) * 2;
-  const size_t out = (size_t)16 * kYB * 4;
+  const size_t stage = ((size_t)mb * 2 * BT * kSP + (size_t)mb * HL * kOT * kSP) * 2;
+  const size_t out = (size_t)16 * (kOT * (2 * mb + 4) + 4) * 4;
   return stage > out ? stage : out;
 }
 
+size_t contract_mx_lds_bytes(int dtype, int B) {
+  return std::max(contract_mx_lds_bytes(dtype, B, 4), contract_mx_lds_bytes(dtype, B, 8));
+}
+
 hipError_t contract_mx_prepare(int dtype, int B) {
-  const void *k = contract_mx_kernel(dtype, B);
-  if (!k) return hipErrorInvalidValue;
-  return raise_lds_cap(k, contract_mx_lds_bytes(dtype, B));
+  for (int mb : {4, 8}) {
+    const void *k = contract_mx_kernel(dtype, B, mb);
+    if (!k) return hipErrorInvalidValue;
+    const hipError_t e = raise_lds_cap(k, contract_mx_lds_bytes(dtype, B, mb));
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s) {
-  const void *k = contract_mx_kernel(dtype, a.B);
+  const int mb = cmx_modes(a.B, a.Co, a.K);
+  const void *k = contract_mx_kernel(dtype, a.B, mb);
   if (!k) return hipErrorInvalidValue;
   const int BT = a.B <= 16 ? 16 : 32;
-  const long nkb = (long)((a.K + kMB - 1) / kMB) * ((a.B + BT - 1) / BT), no = (a.Co + kOT - 1) / kOT;
+  const long nkb = (long)((a.K + mb - 1) / mb) * ((a.B + BT - 1) / BT), no = (a.Co + kOT - 1) / kOT;
   const long n = (nkb + 7) / 8 * 8 * no;
   if (n > 0x7fffffffL) return hipErrorInvalidValue;
   dim3 grid((unsigned)n);
   void *args[] = {(void *)&a};
-  return hipLaunchKernel(k, grid, dim3(kCT), args, contract_mx_lds_bytes(dtype, a.B), s);
+  return hipLaunchKernel(k, grid, dim3(kCT), args, contract_mx_lds_bytes(dtype, a.B, mb), s);
 }
 
 }  // namespace fno

@@ -72,6 +72,11 @@ SMALL = [
     # tiles (two batch tiles, partial input stages, partial output tiles)
     ("cmx-rag-f16", _cfg("r", 2, 33, 20, 36, (128, 128), (30, 31), "uniform"), "f16"),
     ("cmx-rag-bf16", _cfg("r", 2, 40, 33, 12, (128, 128), (31, 30), "uniform"), "bf16"),
+    # four-mode workgroups (fewer than two eight-mode workgroups per CU):
+    # one and two batch tiles, fp16 and bf16 weights
+    ("cmx-mb4-f16", _cfg("r", 2, 16, 64, 64, (128, 128), (24, 24), "uniform"), "f16"),
+    ("cmx-mb4-f16-b20", _cfg("r", 2, 20, 24, 64, (128, 128), (24, 24), "uniform"), "f16"),
+    ("cmx-mb4-bf16-b20", _cfg("r", 2, 20, 40, 64, (64, 128), (28, 21), "uniform"), "bf16"),
 ]
 
 
