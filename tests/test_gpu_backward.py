@@ -74,6 +74,9 @@ SMALL = [
     ("mx-3d", _cfg("r", 3, 1, 3, 2, (8, 64, 128), (3, 12, 20), "uniform"), "f16"),
     ("cmx-rag-f16", _cfg("r", 2, 33, 20, 36, (128, 128), (30, 31), "uniform"), "f16"),
     ("cmx-rag-bf16", _cfg("r", 2, 40, 36, 12, (128, 128), (31, 30), "uniform"), "bf16"),
+    # the adjoint contraction (64 output channels) on four-mode workgroups,
+    # the forward one (24 output channels) below the matrix-core size
+    ("cmx-mb4-adjoint-f16", _cfg("r", 2, 20, 64, 24, (128, 128), (24, 24), "uniform"), "f16"),
     # weight-gradient tiles: wide batch split over waves, channel tails
     ("gw-split", _cfg("r", 2, 64, 6, 10, (64, 64), (4, 6), "uniform"), "f32"),
     ("gw-ib4", _cfg("r", 2, 4, 48, 40, (64, 64), (20, 28), "uniform"), "f32"),
