@@ -223,7 +223,10 @@ def _autograd_function():
             return y
 
         @staticmethod
+        @torch.autograd.function.once_differentiable
         def backward(ctx, grad_y):
+            # first derivatives only: a second backward raises instead of
+            # silently returning no higher-order terms
             x, w = ctx.saved_tensors
             plan = ctx.plan
             need_x, need_re, need_im = ctx.needs_input_grad[:3]

@@ -177,6 +177,11 @@ def test_autograd_function(case):
         fno.spectral_conv(plan, x2, re, im).backward(g)
         torch.cuda.synchronize()
         assert rel_l2(to_float64(re.grad) + 1j * to_float64(im.grad), dw_ref) <= TOL[dtype]
+        # first derivatives only: differentiating the backward raises
+        (gx,) = torch.autograd.grad(fno.spectral_conv(plan, x, re, im), x, g, create_graph=True)
+        with pytest.raises(RuntimeError):
+            gx.sum().backward()
+        torch.cuda.synchronize()
     finally:
         fno.fno_plan_destroy(plan)
 
