@@ -5,6 +5,7 @@ before any HIP call)."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -90,3 +91,26 @@ def test_null_arguments(L):
     assert L.fno_plan_num_launches(None, ctypes.byref(n)) == INVALID
     sz = ctypes.c_size_t()
     assert L.fno_plan_workspace_bytes(None, ctypes.byref(sz)) == INVALID
+
+
+def test_plain_c_program_builds_and_links(tmp_path):
+    """The header is plain C (c99, pedantic, no warnings) and a C program
+    links against the library and calls it (destroying a NULL plan needs no
+    GPU)."""
+    import shutil
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "use_fno.c"
+    src.write_text('#include "fno.h"\n'
+                   "int main(void) {\n"
+                   "  fno_plan_t plan = 0;\n"
+                   "  return fno_plan_destroy(plan) == FNO_OK ? 0 : 1;\n"
+                   "}\n")
+    exe = tmp_path / "use_fno"
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I",
+                        os.path.join(ROOT, "include"), str(src), "-L", libdir, "-lfno",
+                        f"-Wl,-rpath,{libdir}", "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert subprocess.run([str(exe)], timeout=60).returncode == 0
