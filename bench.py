@@ -1,35 +1,39 @@
-"""Benchmark of the fused-path FNO spectral-convolution layer on one MI355X.
+"""Benchmark of the FNO spectral-convolution layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config c1] [--dtype f32]
+    python bench.py [--steps K] [--warmup W] [--config c2] [--dtype f16]
 
 A step is one whole layer (every launch of the path) over one batch of
 synthetic input already resident in HBM. Buffer sets are rotated so that the
 whole working set exceeds 1 GiB and the 256 MB Infinity Cache cannot serve
-it. Prints one JSON line:
+it. Before the W warm-up steps of every timed loop the same calls run untimed
+for --settle-ms (default 300 ms): after an idle period the device's power
+management first runs kernels fast for about a millisecond and then slows
+every kernel in steps by up to ~25 % for a few milliseconds before settling,
+so a short timed region that starts from idle measures that transient instead
+of the sustained rate. Prints one JSON line:
 
-* value: layers/s on the main workload (default: the 128x128 fp32 layer,
-  B=16, Cin=Cout=32, modes 16x16), plus GB/s and the fraction of the 8 TB/s
-  HBM peak from the minimal bytes (read x + read w + write y once);
-* roofline: the dominant kernel's algorithmic bytes per launch over its
-  average launch time (HIP events on the stream it runs on);
-* cpu_baseline: the float64 oracle timed on this host's cores on the same
-  workload;
-* per_layer_us: the distribution (p50, mean, std, min) of single layers
-  inside the rotating back-to-back loop, and hot_single_set_layers_per_s:
-  the same loop on one buffer set (which the Infinity Cache may serve;
-  labelled, never the headline);
-* configs: the same figures for the 128^2 fp16, 256^2 fp16 / bf16, 64^3
-  fp32 and 16^2 fp32 layers;
-* latency: per-call latency (mean, std, min over individually timed calls)
-  of the 128^2 fp32 layer shape at batch 1, 2, 4, 8, launched eagerly and
-  replayed from a captured HIP graph, with the throughput gain from batch 1
-  to 8;
-* model: the full FNO2d forward (lift, four spectral blocks with the 1x1
-  bypass and GELU, projection; B=20, 256^2, width 64, modes 24x24, fp16
-  storage) as forwards/s and samples/s, and its per-call latency at batch 1;
-* backward: the layer's backward pass (grad_x and grad_w from dL/dy) on the
-  128^2 fp32, 256^2 fp16 and 64^3 fp32 layers, as backward passes/s and GB/s
-  from its minimal bytes (read x, w, dL/dy once, write grad_x, grad_w once).
+* value: layers/s on the headline workload (default: the 256x256 fp16 layer,
+  B=32, Cin=Cout=64, modes 32x32), GB/s and the fraction of the 8 TB/s HBM
+  peak from the layer's minimal bytes (read x + read w + write y once);
+* roofline: the layer's dominant kernel, its algorithmic bytes per launch
+  (the compulsory bytes of its own step: x for the forward planes, w for the
+  contraction, y for the inverse planes) over its average launch time (HIP
+  events on the stream it runs on), the spectra-inclusive rate beside it, and
+  the measured HBM traffic per launch from the committed counter summary;
+* cpu_baseline: the float64 oracle timed on this host's cores on a bounded
+  sample of the headline workload (whole batch elements), scaled to layers/s;
+* metric_configs: the same three objects (layer rate, roofline,
+  cpu_baseline) for every workload the metric is quoted on: 128x128 fp32 and
+  fp16, 256x256 fp16 and bf16, 64^3 fp32;
+* per_layer_us / hot_single_set_layers_per_s: the distribution of single
+  layers inside the rotating back-to-back loop, and the same loop on one
+  buffer set (which the Infinity Cache may serve; never the headline);
+* configs: the 16x16 fp32 layer (launch-bound);
+* latency: per-call latency of the 128^2 fp32 layer shape at batch 1, 2, 4, 8,
+  launched eagerly and replayed from a captured HIP graph;
+* model: the full FNO2d forward (B=20, 256^2, width 64, modes 24x24, fp16);
+* backward: the layer's backward pass on the 128^2 fp32, 256^2 fp16 and 64^3
+  fp32 layers, from its minimal bytes (read x, w, dL/dy, write grad_x, grad_w).
 """
 
 import argparse
@@ -50,24 +54,41 @@ ROTATE_BYTES = 1 << 30
 MAX_SETS = 64
 
 
-def _bytes_per_launch(cfg, dtype):
-    """Algorithmic bytes of each launch: its compulsory input and output."""
+SETTLE_MS = 300.0
+SPECTRA_BYTES = 8  # complex fp32 spectra in the plan workspace
+
+
+def _kernel_bytes(cfg, dtype, name):
+    """Bytes of one launch of kernel `name`: (algorithmic, exchange).
+
+    Algorithmic bytes are the compulsory bytes of the kernel's own step of
+    the layer: x for the forward planes, w for the contraction, y for the
+    inverse planes, nothing for the 3D outer-axis passes. Exchange bytes are
+    the spectra (and 3D slab transforms) it also writes or reads."""
     s = 4 if dtype == "f32" else 2
     pts = int(np.prod(cfg.grid))
     x = cfg.batch * cfg.c_in * pts * s
     y = cfg.batch * cfg.c_out * pts * s
     w = cfg.n_modes * cfg.c_in * cfg.c_out * 2 * s
-    xh = cfg.batch * cfg.c_in * cfg.n_modes * 8
-    yh = cfg.batch * cfg.c_out * cfg.n_modes * 8
+    xh = cfg.batch * cfg.c_in * cfg.n_modes * SPECTRA_BYTES
+    yh = cfg.batch * cfg.c_out * cfg.n_modes * SPECTRA_BYTES
     if cfg.ndim == 2:
-        return {"fno_fwd_plane": x + xh, "fno_fwd_plane_mx": x + xh, "fno_contract": xh + w + yh,
-                "fno_inv_plane": yh + y, "fno_inv_plane_mx": yh + y}
-    C = 2 * cfg.modes[1] * cfg.modes[2]
-    ti = cfg.batch * cfg.c_in * cfg.grid[0] * C * 8
-    to = cfg.batch * cfg.c_out * cfg.grid[0] * C * 8
-    return {"fno_fwd_plane": x + ti, "fno_fwd_plane_mx": x + ti, "fno_fwd_axis": ti + xh,
-            "fno_contract": xh + w + yh, "fno_inv_axis": yh + to, "fno_inv_plane": to + y,
-            "fno_inv_plane_mx": to + y}
+        ti = to = None
+    else:
+        C = 2 * cfg.modes[1] * cfg.modes[2]
+        ti = cfg.batch * cfg.c_in * cfg.grid[0] * C * 8
+        to = cfg.batch * cfg.c_out * cfg.grid[0] * C * 8
+    if name.startswith("fno_fwd_plane"):
+        return x, (xh if ti is None else ti)
+    if name.startswith("fno_fwd_axis"):
+        return 0, ti + xh
+    if name.startswith("fno_contract"):
+        return w, xh + yh
+    if name.startswith("fno_inv_axis"):
+        return 0, yh + to
+    if name.startswith("fno_inv_plane"):
+        return y, (yh if to is None else to)
+    raise KeyError(name)
 
 
 def to_device(arr, dtype, device="cuda:0"):
@@ -159,10 +180,10 @@ def backward_minimal_bytes(cfg, dtype):
     return 2 * cfg.batch * cfg.c_in * pts * s + cfg.batch * cfg.c_out * pts * s + 2 * w
 
 
-def measure_backward(cfg, dtype, steps, warmup):
+def measure_backward(cfg, dtype, steps, warmup, settle_ms=SETTLE_MS):
     bw = Backward(cfg, dtype)
     try:
-        ms = _time_loop(bw.step, steps, warmup, bw.stream)
+        ms = _time_loop(bw.step, steps, warmup, bw.stream, settle_ms)
         gbps = backward_minimal_bytes(cfg, dtype) / (ms * 1e-3) / 1e9
         return {"workload": cfg.name, "dtype": dtype, "ms_per_backward": ms,
                 "backward_per_s": 1000.0 / ms, "minimal_bytes": backward_minimal_bytes(cfg, dtype),
@@ -256,12 +277,12 @@ class Model:
         self.fno.fno_model2d_destroy(self.model)
 
 
-def measure_model(steps, warmup):
+def measure_model(steps, warmup, settle_ms=SETTLE_MS):
     import workloads as wl
     cfg = wl.CONFIGS["c4"]
     m = Model(cfg)
     try:
-        ms = _time_loop(m.step, steps, warmup, m.stream)
+        ms = _time_loop(m.step, steps, warmup, m.stream, settle_ms)
         res = {"workload": "FNO2d forward, B=20, 256x256, lift 3->64, 4 x (spectral conv 64->64 modes "
                            "24x24 + 1x1 conv + GELU), projection 64->128->1, fp16 storage",
                "ms_per_forward": ms, "samples_per_s": m.B / (ms * 1e-3)}
@@ -275,8 +296,31 @@ def measure_model(steps, warmup):
     return res
 
 
-def _time_loop(fn, steps, warmup, stream):
+def _settle(fn, ms, stream):
+    """Run fn(i) untimed for `ms` milliseconds of wall time, keeping about
+    eight calls queued on the device (waits on an event recorded eight calls
+    earlier), so the device never idles while the host loops."""
     import torch
+    if ms <= 0:
+        return 0
+    pending = []
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1000.0 < ms:
+        fn(n)
+        n += 1
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        pending.append(ev)
+        if len(pending) > 8:
+            pending.pop(0).synchronize()
+    return n
+
+
+def _time_loop(fn, steps, warmup, stream, settle_ms=0.0):
+    """ms per call of `steps` back-to-back calls between two HIP events on
+    `stream`, after `settle_ms` of untimed calls and `warmup` warm-up calls."""
+    import torch
+    _settle(fn, settle_ms, stream)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -290,10 +334,11 @@ def _time_loop(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps  # ms per call
 
 
-def _per_call(fn, n, stream):
+def _per_call(fn, n, stream, settle_ms=0.0):
     """Per-call times in µs inside a back-to-back stream of calls: one event
     between consecutive calls, no synchronisation until the end."""
     import torch
+    _settle(fn, settle_ms, stream)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
     ev[0].record(stream)
     for i in range(n):
@@ -305,33 +350,50 @@ def _per_call(fn, n, stream):
             "p50": float(np.median(t)), "n": n}
 
 
-def _kernel_times(lay, steps, warmup):
-    """Average duration of each launch of the layer: `steps` back-to-back
-    launches of that kernel alone (rotating buffer sets) between two HIP
-    events recorded on the plan's stream."""
-    return [_time_loop(lambda i, idx=idx: lay.launch(idx, i), steps, warmup, lay.stream)
+def _kernel_times(lay, steps, warmup, settle_ms):
+    """Average duration of each launch of the layer: max(steps, 200)
+    back-to-back launches of that kernel alone (rotating buffer sets) between
+    two HIP events recorded on the plan's stream, the stream the kernel runs
+    on (at least 200, so one stalled launch cannot dominate the average)."""
+    n = max(steps, 200)
+    return [_time_loop(lambda i, idx=idx: lay.launch(idx, i), n, warmup, lay.stream, settle_ms)
             for idx in range(len(lay.names))]
 
 
-def measure(cfg, dtype, steps, warmup, per_kernel=True):
+def _roofline(cfg, dtype, kernels):
+    """Roofline object of the layer's dominant (longest) kernel."""
+    dom = max(kernels, key=lambda k: k["ms"])
+    return {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["gbps"], "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": dom["gbps"] / HBM_PEAK_GBPS,
+            "traffic": measured_traffic(dom["kernel"], cfg.name, dtype),
+            "algorithmic_bytes": dom["algorithmic_bytes"], "exchange_bytes": dom["exchange_bytes"],
+            "ms_per_launch": dom["ms"], "achieved_with_exchange": dom["gbps_with_exchange"]}
+
+
+def measure(cfg, dtype, steps, warmup, settle_ms=SETTLE_MS, per_kernel=True):
     lay = Layer(cfg, dtype)
     try:
-        ms = _time_loop(lay.step, steps, warmup, lay.stream)
-        res = {"workload": cfg.name, "dtype": dtype, "ms_per_layer": ms,
-               "layers_per_s": 1000.0 / ms,
+        ms = _time_loop(lay.step, steps, warmup, lay.stream, settle_ms)
+        res = {"workload": cfg.name, "description": cfg.description, "dtype": dtype, "ms_per_layer": ms,
+               "layers_per_s": 1000.0 / ms, "minimal_bytes": cfg.minimal_bytes(dtype),
                "gbps": cfg.minimal_bytes(dtype) / (ms * 1e-3) / 1e9}
         res["hbm_frac"] = res["gbps"] / HBM_PEAK_GBPS
         # distribution of single layers inside the rotating back-to-back loop
-        res["per_layer_us"] = _per_call(lay.step, min(steps, 500), lay.stream)
+        res["per_layer_us"] = _per_call(lay.step, min(steps, 500), lay.stream, settle_ms)
         # one buffer set reused: x, w and y may then be served from the
         # Infinity Cache, so this is not the HBM-bound figure
-        hot = _time_loop(lambda i: lay.step(0), steps, max(2, warmup // 4), lay.stream)
+        hot = _time_loop(lambda i: lay.step(0), steps, max(2, warmup // 4), lay.stream, settle_ms)
         res["hot_single_set_layers_per_s"] = 1000.0 / hot
         if per_kernel:
-            bpl = _bytes_per_launch(cfg, dtype)
-            kms = _kernel_times(lay, steps, max(2, warmup // 4))
-            res["kernels"] = [{"kernel": name, "ms": t, "bytes": bpl[name], "gbps": bpl[name] / (t * 1e-3) / 1e9}
-                              for name, t in zip(lay.names, kms)]
+            kms = _kernel_times(lay, steps, max(2, warmup // 4), settle_ms)
+            res["kernels"] = []
+            for name, t in zip(lay.names, kms):
+                alg, exch = _kernel_bytes(cfg, dtype, name)
+                g = alg / (t * 1e-3) / 1e9
+                res["kernels"].append({"kernel": name, "ms": t, "algorithmic_bytes": alg,
+                                       "exchange_bytes": exch, "gbps": g, "frac": g / HBM_PEAK_GBPS,
+                                       "gbps_with_exchange": (alg + exch) / (t * 1e-3) / 1e9})
+            res["roofline"] = _roofline(cfg, dtype, res["kernels"])
         return res
     finally:
         lay.close()
@@ -369,13 +431,18 @@ def copy_bandwidth(nbytes, steps=20, warmup=3):
     return {"bytes_copied": nbytes, "ms": ms, "gbps": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
-def cpu_baseline(cfg, dtype, min_seconds=10.0):
-    """The float64 oracle on this host's cores, repeated for ~min_seconds."""
+def cpu_baseline(cfg, dtype, budget_s=8.0):
+    """The float64 oracle, as it stands, on this host's cores. Batch elements
+    of the layer are independent, so it runs on one batch element of the
+    workload (same grid, channels, modes and weights shape) for about
+    budget_s seconds after one warm-up, and the rate is scaled to layers/s of
+    the full batch."""
     import oracle
     import workloads as wl
     from threadpoolctl import threadpool_info, threadpool_limits
     cores = len(os.sched_getaffinity(0))
-    inp = wl.layer_inputs(cfg, dtype)
+    nb = 1
+    inp = wl.layer_inputs(cfg, dtype, batch=nb)
     f = oracle.spectral_conv2d if cfg.ndim == 2 else oracle.spectral_conv3d
     with threadpool_limits(limits=cores):
         pools = threadpool_info()
@@ -388,24 +455,53 @@ def cpu_baseline(cfg, dtype, min_seconds=10.0):
             f(inp["x64"], inp["w64"], *cfg.modes)
             n += 1
             el = time.perf_counter() - t0
-            if el >= min_seconds:
+            if el >= budget_s:
                 break
-    return {"value": n / el, "unit": "layers/s", "cores": int(used), "kind": "oracle",
-            "sample": f"whole {cfg.name} {dtype} layer (B={cfg.batch}), {n} runs in {el:.1f} s "
-                      f"after one warm-up, float64 numpy (BLAS: {blas}), host affinity {cores} cores"}
+    rate = n * nb / cfg.batch / el
+    return {"value": rate, "unit": "layers/s", "cores": int(used), "kind": "oracle",
+            "sample": f"{cfg.name} layer ({cfg.description}) on {nb} of its {cfg.batch} batch elements, "
+                      f"{n} runs in {el:.1f} s after one warm-up, scaled by {nb}/{cfg.batch} to layers/s; "
+                      f"float64 numpy (BLAS: {blas}), host affinity {cores} cores",
+            "gbps_minimal_bytes": cfg.minimal_bytes(dtype) * rate / 1e9}
+
+
+ARITHMETIC = {
+    "f32": "f32 storage; transforms on f16 hi+lo split MFMA operands (about 22 significant bits), "
+           "contraction on f32 MFMA, f32 accumulation throughout",
+    "f16": "f16 storage; transforms on f16 MFMA operands scaled by powers of two, contraction on bf16 "
+           "hi+lo split MFMA operands (f32-level products), f32 accumulation throughout",
+    "bf16": "bf16 storage; transforms on f16 MFMA operands scaled by powers of two, contraction on bf16 "
+            "hi+lo split MFMA operands (f32-level products), f32 accumulation throughout",
+}
+DTYPE_LABEL = {"f32": "f32 (f16 hi+lo MFMA, f32 acc)", "f16": "f16 (MFMA, f32 acc)",
+               "bf16": "bf16 storage (f16 MFMA, f32 acc)"}
+
+# every workload the metric is quoted on: 128^2, 256^2 and 64^3 layers
+METRIC_CONFIGS = [("c2", "f16"), ("c2", "bf16"), ("c1", "f32"), ("c1", "f16"), ("c3", "f32")]
+
+
+def _summary(r):
+    d = r["per_layer_us"]
+    rf = r["roofline"]
+    return (f"{r['workload']} {r['dtype']}: {r['layers_per_s']:.1f} layers/s, {r['gbps']:.0f} GB/s "
+            f"({100 * r['hbm_frac']:.1f} % of 8 TB/s); per layer p50 {d['p50']:.1f} us (mean {d['mean']:.1f}, "
+            f"std {d['std']:.1f}, min {d['min']:.1f}); dominant {rf['kernel']} {1000 * rf['ms_per_launch']:.1f} us "
+            f"= {rf['achieved']:.0f} GB/s algorithmic ({100 * rf['frac']:.1f} %)")
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     # 100 warm-up and 1000 timed launches per workload (the timed region
-    # of the 128^2 layer is then ~30 ms, of the 256^2 layers ~0.16 s)
+    # of the 256^2 layers is then ~0.15 s)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", default="c1")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed calls before every warm-up (device power-state settle)")
+    ap.add_argument("--config", default="c2")
     ap.add_argument("--dtype", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-latency", action="store_true")
     ap.add_argument("--no-model", action="store_true")
@@ -430,56 +526,67 @@ def main():
         return
     cfg = wl.CONFIGS[args.config]
     dtype = args.dtype or cfg.dtypes[0]
+    settle = args.settle_ms
     if args.model_only:
-        print(json.dumps({"model": measure_model(args.steps, args.warmup)}))
+        print(json.dumps({"model": measure_model(args.steps, args.warmup, settle)}))
         return
     if args.backward_only:
-        print(json.dumps({"backward": [measure_backward(cfg, dtype, args.steps, args.warmup)]}))
+        print(json.dumps({"backward": [measure_backward(cfg, dtype, args.steps, args.warmup, settle)]}))
         return
-    main_res = measure(cfg, dtype, args.steps, args.warmup)
-    dom = max(main_res["kernels"], key=lambda k: k["ms"])
+    main_res = measure(cfg, dtype, args.steps, args.warmup, settle)
+    print("[bench] " + _summary(main_res), file=sys.stderr, flush=True)
     out = {
         "metric": METRIC, "value": main_res["layers_per_s"], "unit": "layers/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": main_res["ms_per_layer"], "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32" if dtype == "f32" else f"{dtype} storage, f32 compute",
+        "vs_baseline": None, "dtype": DTYPE_LABEL[dtype], "arithmetic": ARITHMETIC[dtype],
         "data": "synthetic (seeded Gaussian random fields; random weights)",
         "config": {"workload": cfg.description, "name": cfg.name, "batch": cfg.batch,
                    "c_in": cfg.c_in, "c_out": cfg.c_out, "grid": list(cfg.grid),
                    "modes": list(cfg.modes), "storage": dtype,
                    "minimal_bytes": cfg.minimal_bytes(dtype)},
         "gbps": main_res["gbps"], "hbm_frac": main_res["hbm_frac"],
-        "roofline": {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["gbps"],
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dom["gbps"] / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(dom["kernel"], cfg.name, dtype),
-                     "bytes_per_launch": dom["bytes"], "ms_per_launch": dom["ms"]},
+        "roofline": main_res["roofline"],
         "kernels": main_res["kernels"],
         "per_layer_us": main_res["per_layer_us"],
         "hot_single_set_layers_per_s": main_res["hot_single_set_layers_per_s"],
+        "settle_ms": settle,
     }
+    results = {(cfg.name, dtype): main_res}
     if not args.no_extra:
-        extra = []
-        for name, dt in (("c1", "f16"), ("c2", "f16"), ("c2", "bf16"), ("c3", "f32"), ("c0", "f32")):
-            if name == cfg.name and dt == dtype:
+        for name, dt in METRIC_CONFIGS + [("c0", "f32")]:
+            if (name, dt) in results:
                 continue
-            r = measure(wl.CONFIGS[name], dt, args.steps, args.warmup)
-            extra.append(r)
-            d = r["per_layer_us"]
-            print(f"[bench] {name} {dt}: {r['layers_per_s']:.1f} layers/s, {r['gbps']:.0f} GB/s; "
-                  f"per layer p50 {d['p50']:.1f} us (mean {d['mean']:.1f}, std {d['std']:.1f}, "
-                  f"min {d['min']:.1f}); one buffer set {r['hot_single_set_layers_per_s']:.0f} layers/s",
+            r = measure(wl.CONFIGS[name], dt, args.steps, args.warmup, settle)
+            results[(name, dt)] = r
+            print("[bench] " + _summary(r), file=sys.stderr, flush=True)
+    cpu = {}
+    if not args.no_cpu_baseline:
+        for name, dt in [(cfg.name, dtype)] + METRIC_CONFIGS:
+            if name in cpu or (name, dt) not in results:
+                continue
+            cpu[name] = cpu_baseline(wl.CONFIGS[name], dt)
+            print(f"[bench] oracle {name}: {cpu[name]['value']:.3f} layers/s on {cpu[name]['cores']} cores",
                   file=sys.stderr, flush=True)
-        out["configs"] = extra
+        out["cpu_baseline"] = cpu.get(cfg.name)
+    out["metric_configs"] = []
+    for key in METRIC_CONFIGS:
+        if key in results:
+            r = dict(results[key])
+            r["cpu_baseline"] = cpu.get(key[0])
+            r["dtype_label"] = DTYPE_LABEL[key[1]]
+            out["metric_configs"].append(r)
+    out["configs"] = [results[k] for k in results if k not in METRIC_CONFIGS and k != (cfg.name, dtype)]
     if not args.no_backward:
         bwd = []
         for name, dt in (("c1", "f32"), ("c2", "f16"), ("c3", "f32")):
-            r = measure_backward(wl.CONFIGS[name], dt, max(20, args.steps // 2), max(5, args.warmup // 2))
+            r = measure_backward(wl.CONFIGS[name], dt, max(20, args.steps // 2), max(5, args.warmup // 2), settle)
             bwd.append(r)
             print(f"[bench] backward {name} {dt}: {r['backward_per_s']:.1f} /s, {r['gbps']:.0f} GB/s",
                   file=sys.stderr, flush=True)
         out["backward"] = bwd
     if not args.no_model:
-        out["model"] = measure_model(max(10, args.steps // 10), max(3, args.warmup // 4))
+        out["model"] = measure_model(max(10, args.steps // 10), max(3, args.warmup // 4), settle)
         print(f"[bench] model: {out['model']['ms_per_forward']:.3f} ms per B=20 forward, "
               f"B=1 latency {out['model']['latency_b1_us']['mean']:.1f} us", file=sys.stderr, flush=True)
     if not args.no_latency:
@@ -489,8 +596,6 @@ def main():
             f"graph {r['graph_us']['mean']:.1f}±{r['graph_us']['std']:.1f} us"
             for r in out["latency"]["sweep"]), file=sys.stderr, flush=True)
     out["copy_1gib"] = copy_bandwidth(1 << 30)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, dtype)
     print(json.dumps(out), flush=True)
 
 

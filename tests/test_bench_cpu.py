@@ -36,16 +36,40 @@ def test_backward_minimal_bytes():
 
 
 def test_per_launch_bytes_2d():
-    # forward planes: x + forward spectra; contraction: spectra in + w + spectra out;
-    # inverse planes: spectra + y (complex fp32 spectra, 8 bytes per mode)
+    # algorithmic bytes of each step: x for the forward planes, w for the
+    # contraction, y for the inverse planes; the spectra they exchange
+    # (complex fp32, 8 bytes per mode) are counted apart
     cfg = wl.CONFIGS["c2"]
-    b = bench._bytes_per_launch(cfg, "f16")
     x = 32 * 64 * 256 * 256 * 2
     xh = 32 * 64 * 2 * 32 * 32 * 8
     w = 2 * 32 * 32 * 64 * 64 * 4
-    assert b["fno_fwd_plane_mx"] == x + xh
-    assert b["fno_contract"] == xh + w + xh
-    assert b["fno_inv_plane_mx"] == xh + x
+    assert bench._kernel_bytes(cfg, "f16", "fno_fwd_plane_mx") == (x, xh)
+    assert bench._kernel_bytes(cfg, "f16", "fno_contract_mx") == (w, 2 * xh)
+    assert bench._kernel_bytes(cfg, "f16", "fno_inv_plane_mx") == (x, xh)
+
+
+def test_per_launch_bytes_3d():
+    # 64^3 fp32: the outer-axis passes move only slab transforms and spectra
+    cfg = wl.CONFIGS["c3"]
+    x = 4 * 32 * 64 ** 3 * 4
+    w = 4 * 16 ** 3 * 32 * 32 * 8
+    t = 4 * 32 * 64 * (2 * 16 * 16) * 8
+    xh = 4 * 32 * 4 * 16 ** 3 * 8
+    assert bench._kernel_bytes(cfg, "f32", "fno_fwd_plane_mx") == (x, t)
+    assert bench._kernel_bytes(cfg, "f32", "fno_fwd_axis") == (0, t + xh)
+    assert bench._kernel_bytes(cfg, "f32", "fno_contract") == (w, 2 * xh)
+    assert bench._kernel_bytes(cfg, "f32", "fno_inv_plane_mx") == (x, t)
+
+
+def test_roofline_takes_the_longest_kernel():
+    cfg = wl.CONFIGS["c2"]
+    ks = [{"kernel": "a", "ms": 0.05, "gbps": 5000.0, "algorithmic_bytes": 1, "exchange_bytes": 2,
+           "gbps_with_exchange": 6000.0},
+          {"kernel": "fno_fwd_plane_mx", "ms": 0.06, "gbps": 4000.0, "algorithmic_bytes": 3,
+           "exchange_bytes": 4, "gbps_with_exchange": 4500.0}]
+    r = bench._roofline(cfg, "f16", ks)
+    assert r["kernel"] == "fno_fwd_plane_mx" and r["frac"] == 0.5 and r["peak"] == 8000.0
+    assert set(r) >= {"bound", "achieved", "peak", "unit", "frac", "traffic"}
 
 
 def test_more_than_one_gpu_is_refused():
