@@ -161,6 +161,27 @@ fno_status_t fno_weights_pack(fno_plan_t plan, int layout, const void *src_re,
 fno_status_t fno_weights_unpack(fno_plan_t plan, int layout, const void *w,
                                 void *dst_re, void *dst_im, void *stream);
 
+/* ---- allocation-free execution ------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Runs the
+ * same kernels as fno_spectral_conv2d / fno_spectral_conv3d (2D or 3D as the
+ * plan says) with the same arguments, preconditions and results, but the
+ * forward and contracted spectra (and, in 3D, the slab transforms) go
+ * through one static device array of FNO_NOALLOC_SCRATCH_BYTES inside the
+ * library instead of the plan's workspace. Calls no allocating routine.
+ * Each GPU the library runs on holds its own copy of that array until the
+ * process ends; every call on one GPU shares it, so calls that overlap in
+ * time on one GPU (different streams, or concurrent with another thread's
+ * call) race and must be ordered by the caller. Nothing in the array needs
+ * to start at zero: every call writes what it reads.
+ * UNSUPPORTED when the plan's exchange buffers (complex fp32, each 256-byte
+ * aligned: batch*c_in*K + batch*c_out*K values, plus in 3D
+ * batch*max(c_in,c_out)*X*2*m2*m3) exceed FNO_NOALLOC_SCRATCH_BYTES;
+ * otherwise errors as fno_spectral_conv2d. */
+#define FNO_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+fno_status_t fno_spectral_conv_noalloc(fno_plan_t plan, const void *x,
+                                       const void *w, void *y, void *stream);
+
 /* Free the plan's device memory after synchronising its device.
  * fno_plan_destroy(NULL) returns FNO_OK. Destroying a plan twice is
  * undefined. */

@@ -123,6 +123,15 @@ def fno_spectral_conv3d(plan, x, w, y, stream=None):
                                     _stream(stream, plan.device)), "fno_spectral_conv3d")
 
 
+def fno_spectral_conv_noalloc(plan, x, w, y, stream=None):
+    """The layer (2D or 3D as the plan says) with its exchange buffers in
+    the library's static scratch array instead of the plan's workspace; see
+    fno_spectral_conv_noalloc in include/fno.h."""
+    _check_tensors(plan, x, w, y)
+    check(lib().fno_spectral_conv_noalloc(plan.handle, _ptr(x), _ptr(w), _ptr(y),
+                                          _stream(stream, plan.device)), "fno_spectral_conv_noalloc")
+
+
 def _check_backward(plan, x, w, gy, gx, gw):
     import torch
     td = _torch_dtype(plan.dtype)

@@ -10,6 +10,7 @@ FNO_OK = 0
 STATUS_NAMES = {0: "FNO_OK", 1: "FNO_ERR_INVALID_ARG", 2: "FNO_ERR_UNSUPPORTED",
                 3: "FNO_ERR_OUT_OF_MEMORY", 4: "FNO_ERR_DEVICE"}
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # FNO_NOALLOC_SCRATCH_BYTES
 
 # every symbol include/fno.h declares, with its ctypes signature
 _c_int, _c_void_p, _c_size_t = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
@@ -19,6 +20,7 @@ SIGNATURES = {
                                  _IntP, _IntP, _c_int, _c_int]),
     "fno_spectral_conv2d": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "fno_spectral_conv3d": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "fno_spectral_conv_noalloc": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "fno_spectral_conv2d_backward": (_c_int, [_c_void_p] * 7),
     "fno_spectral_conv3d_backward": (_c_int, [_c_void_p] * 7),
     "fno_weights_pack": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),

@@ -562,18 +562,28 @@ static fno_status_t check_exec(fno_plan_t p, int ndim, const void *x, const void
   return FNO_OK;
 }
 
+// Device buffers the launches exchange data through: the forward and
+// contracted spectra and, in 3D, the slab transforms between the plane and
+// the outer-axis passes. The plan's own workspace normally; the library's
+// static scratch array for fno_spectral_conv_noalloc.
+struct Bufs {
+  float2 *xh, *yh, *tbuf;
+};
+
+static Bufs plan_bufs(fno_plan_t p) { return {p->xh, p->yh, p->tbuf}; }
+
 // Launch helpers, parameterised by source, channel count and destination so
 // the forward and the backward pass share them. nchan is Ci or Co; the
 // persistent grid and planes-per-workgroup were sized for that count.
 
 // plane transforms of `nchan` channels: 2D x -> spectra dst; 3D slabs -> tbuf
-static hipError_t fwd_plane_launch(fno_plan_t p, const void *x, int nchan, float2 *dst, hipStream_t s) {
+static hipError_t fwd_plane_launch(fno_plan_t p, const Bufs &b, const void *x, int nchan, float2 *dst, hipStream_t s) {
   const int nd = p->ndim;
   const bool own = nchan == p->Ci;
   if (p->mx) {
     PlaneMxFwdArgs m;
     m.x = x;
-    m.out = nd == 2 ? dst : p->tbuf;
+    m.out = nd == 2 ? dst : b.tbuf;
     m.tw_h = p->tw_h;
     m.tf = p->tf;
     m.tf_lo = p->tf_lo;
@@ -596,7 +606,7 @@ static hipError_t fwd_plane_launch(fno_plan_t p, const void *x, int nchan, float
   }
   PlaneFwdArgs a;
   a.x = x;
-  a.out = nd == 2 ? dst : p->tbuf;
+  a.out = nd == 2 ? dst : b.tbuf;
   a.tw_h = p->tw_h;
   a.tw_w = p->tw_w;
   a.nplanes = p->B * nchan * (nd == 3 ? p->xN : 1);
@@ -614,12 +624,12 @@ static hipError_t fwd_plane_launch(fno_plan_t p, const void *x, int nchan, float
 
 // 2D matrix-core planes of x (Ci channels) and gy (Co channels) in one
 // launch: spectra of x to xh, of gy to yh
-static hipError_t fwd_planes_both(fno_plan_t p, const void *x, const void *gy, hipStream_t s) {
+static hipError_t fwd_planes_both(fno_plan_t p, const Bufs &b, const void *x, const void *gy, hipStream_t s) {
   PlaneMxFwdArgs m;
   m.x = x;
-  m.out = p->xh;
+  m.out = b.xh;
   m.x2 = gy;
-  m.out2 = p->yh;
+  m.out2 = b.yh;
   m.nsplit = p->B * p->Ci;
   m.nplanes = p->B * (p->Ci + p->Co);
   m.tw_h = p->tw_h;
@@ -640,9 +650,9 @@ static hipError_t fwd_planes_both(fno_plan_t p, const void *x, const void *gy, h
 }
 
 // 3D outer axis, forward: tbuf ([B nchan][X][C]) -> spectra dst, scaled 1/N
-static hipError_t fwd_axis_launch(fno_plan_t p, int nchan, float2 *dst, hipStream_t s) {
+static hipError_t fwd_axis_launch(fno_plan_t p, const Bufs &b, int nchan, float2 *dst, hipStream_t s) {
   AxisArgs a;
-  a.in = p->tbuf;
+  a.in = b.tbuf;
   a.out = dst;
   a.tw = p->tw_x;
   a.nvol = p->B * nchan;
@@ -671,10 +681,10 @@ static hipError_t contract_launch(fno_plan_t p, const float2 *in, const void *w,
 }
 
 // 3D outer axis, inverse: spectra src ([B nchan][K]) -> tbuf
-static hipError_t inv_axis_launch(fno_plan_t p, const float2 *src, int nchan, hipStream_t s) {
+static hipError_t inv_axis_launch(fno_plan_t p, const Bufs &b, const float2 *src, int nchan, hipStream_t s) {
   AxisArgs a;
   a.in = src;
-  a.out = p->tbuf;
+  a.out = b.tbuf;
   a.tw = p->tw_x;
   a.nvol = p->B * nchan;
   a.N = p->xN;
@@ -686,12 +696,12 @@ static hipError_t inv_axis_launch(fno_plan_t p, const float2 *src, int nchan, hi
 }
 
 // inverse plane transforms of `nchan` channels: 2D spectra src -> y; 3D tbuf -> y
-static hipError_t inv_plane_launch(fno_plan_t p, const float2 *src, int nchan, void *y, hipStream_t s) {
+static hipError_t inv_plane_launch(fno_plan_t p, const Bufs &b, const float2 *src, int nchan, void *y, hipStream_t s) {
   const int nd = p->ndim;
   const bool own = nchan == p->Co;
   if (p->mx) {
     PlaneMxInvArgs m;
-    m.in = nd == 2 ? src : p->tbuf;
+    m.in = nd == 2 ? src : b.tbuf;
     m.y = y;
     m.tw_h = p->tw_h;
     m.tb = p->tb;
@@ -709,7 +719,7 @@ static hipError_t inv_plane_launch(fno_plan_t p, const float2 *src, int nchan, v
     return launch_plane_mx_inv(m, own ? p->mx_grid_i : p->mx_grid_ib, p->dtype, p->lds_inv, s);
   }
   PlaneInvArgs a;
-  a.in = nd == 2 ? src : p->tbuf;
+  a.in = nd == 2 ? src : b.tbuf;
   a.y = y;
   a.tw_h = p->tw_h;
   a.tw_w = p->tw_w;
@@ -724,13 +734,14 @@ static hipError_t inv_plane_launch(fno_plan_t p, const float2 *src, int nchan, v
   return launch_plane_inv(a, p->pMP, p->rpt, p->dtype, own ? p->lds_inv : p->lds_ib, s);
 }
 
-static hipError_t run_one(fno_plan_t p, int kind, const void *x, const void *w, void *y, hipStream_t s) {
+static hipError_t run_one(fno_plan_t p, const Bufs &b, int kind, const void *x, const void *w, void *y,
+                          hipStream_t s) {
   switch (kind) {
-    case L_FWD_PLANE: return fwd_plane_launch(p, x, p->Ci, p->xh, s);
-    case L_FWD_AXIS: return fwd_axis_launch(p, p->Ci, p->xh, s);
-    case L_CONTRACT: return contract_launch(p, p->xh, w, p->yh, false, s);
-    case L_INV_AXIS: return inv_axis_launch(p, p->yh, p->Co, s);
-    case L_INV_PLANE: return inv_plane_launch(p, p->yh, p->Co, y, s);
+    case L_FWD_PLANE: return fwd_plane_launch(p, b, x, p->Ci, b.xh, s);
+    case L_FWD_AXIS: return fwd_axis_launch(p, b, p->Ci, b.xh, s);
+    case L_CONTRACT: return contract_launch(p, b.xh, w, b.yh, false, s);
+    case L_INV_AXIS: return inv_axis_launch(p, b, b.yh, p->Co, s);
+    case L_INV_PLANE: return inv_plane_launch(p, b, b.yh, p->Co, y, s);
   }
   return hipErrorInvalidValue;
 }
@@ -746,19 +757,71 @@ static const char *launch_name(int kind, bool mx) {
   return "?";
 }
 
+// Queue the layer's launches (or only launch `only`) with the exchange
+// buffers b; the caller has checked the arguments and made the plan's
+// device current.
+static fno_status_t exec_with(fno_plan_t p, const Bufs &b, const void *x, const void *w, void *y, hipStream_t s,
+                              int only) {
+  for (size_t i = 0; i < p->launches.size(); ++i) {
+    if (only >= 0 && (int)i != only) continue;
+    hipError_t e = run_one(p, b, p->launches[i], x, w, y, s);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return map_err(e);
+  }
+  return FNO_OK;
+}
+
 static fno_status_t exec(fno_plan_t p, int ndim, const void *x, const void *w, void *y, void *stream, int only) {
   fno_status_t st = check_exec(p, ndim, x, w, y);
   if (st != FNO_OK) return st;
   DeviceGuard g(p->device);
   if (g.err != hipSuccess) return FNO_ERR_DEVICE;
-  hipStream_t s = (hipStream_t)stream;
-  for (size_t i = 0; i < p->launches.size(); ++i) {
-    if (only >= 0 && (int)i != only) continue;
-    hipError_t e = run_one(p, p->launches[i], x, w, y, s);
-    if (e == hipSuccess) e = hipGetLastError();
-    if (e != hipSuccess) return map_err(e);
+  return exec_with(p, plan_bufs(p), x, w, y, (hipStream_t)stream, only);
+}
+
+// ---- allocation-free execution ------------------------------------------
+// The exchange buffers of fno_spectral_conv_noalloc live in this file-scope
+// device array. Every GPU the library runs on holds its own copy, at its own
+// address, until the process ends. In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is looked up once per
+// device (hipGetSymbolAddress with that device current) and only that
+// address is ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[FNO_NOALLOC_SCRATCH_BYTES];
+
+// device address of `scratch` on `dev` (which must be current), looked up
+// on the first call for that device
+static hipError_t scratch_address(int dev, unsigned char **out) {
+  static std::mutex mu;
+  static std::map<int, unsigned char *> addr;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it != addr.end()) {
+    *out = it->second;
+    return hipSuccess;
   }
-  return FNO_OK;
+  unsigned char *ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress((void **)&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (!ptr) return hipErrorInvalidSymbol;
+  addr[dev] = ptr;
+  *out = ptr;
+  return hipSuccess;
+}
+
+// the plan's exchange buffers carved out of a region at `base` (NULL: only
+// count); returns the bytes they take, each piece 256-byte aligned
+static size_t carve(fno_plan_t p, unsigned char *base, Bufs *b) {
+  auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  const size_t n_xh = (size_t)p->B * p->Ci * p->K, n_yh = (size_t)p->B * p->Co * p->K;
+  const size_t n_t = p->tbuf ? (size_t)p->B * (p->Ci > p->Co ? p->Ci : p->Co) * p->xN * 2 * p->modes[1] * p->modes[2] : 0;
+  const size_t o_xh = 0, o_yh = o_xh + al(n_xh * sizeof(float2)), o_t = o_yh + al(n_yh * sizeof(float2));
+  const size_t total = o_t + al(n_t * sizeof(float2));
+  if (base && b) {
+    b->xh = (float2 *)(base + o_xh);
+    b->yh = (float2 *)(base + o_yh);
+    b->tbuf = n_t ? (float2 *)(base + o_t) : nullptr;
+  }
+  return total;
 }
 
 // Gradients: every launch is stream-ordered on `stream`; the spectra
@@ -788,19 +851,20 @@ static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const v
   if (g.err != hipSuccess) return FNO_ERR_DEVICE;
   hipStream_t s = (hipStream_t)stream;
   const bool d3 = ndim == 3;
+  const Bufs b = plan_bufs(p);
   hipError_t e = hipSuccess;
   auto step = [&](hipError_t r) {
     if (e == hipSuccess) e = r == hipSuccess ? hipGetLastError() : r;
   };
   if (gw && p->mx && !d3 && p->mx_grid_fb > 0) {
-    step(fwd_planes_both(p, x, gy, s));  // both plane sets, one launch
+    step(fwd_planes_both(p, b, x, gy, s));  // both plane sets, one launch
   } else {
     if (gw) {
-      step(fwd_plane_launch(p, x, p->Ci, p->xh, s));
-      if (d3 && e == hipSuccess) step(fwd_axis_launch(p, p->Ci, p->xh, s));
+      step(fwd_plane_launch(p, b, x, p->Ci, b.xh, s));
+      if (d3 && e == hipSuccess) step(fwd_axis_launch(p, b, p->Ci, b.xh, s));
     }
-    if (e == hipSuccess) step(fwd_plane_launch(p, gy, p->Co, p->yh, s));
-    if (d3 && e == hipSuccess) step(fwd_axis_launch(p, p->Co, p->yh, s));
+    if (e == hipSuccess) step(fwd_plane_launch(p, b, gy, p->Co, b.yh, s));
+    if (d3 && e == hipSuccess) step(fwd_axis_launch(p, b, p->Co, b.yh, s));
   }
   if (gw && e == hipSuccess) {
     GradWArgs a;
@@ -818,8 +882,8 @@ static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const v
   if (gx) {
     if (e == hipSuccess) step(launch_conj_transpose(w, p->wh, p->K, p->Ci, p->Co, p->dtype, s));
     if (e == hipSuccess) step(contract_launch(p, p->yh, p->wh, p->xh, true, s));
-    if (d3 && e == hipSuccess) step(inv_axis_launch(p, p->xh, p->Ci, s));
-    if (e == hipSuccess) step(inv_plane_launch(p, p->xh, p->Ci, gx, s));
+    if (d3 && e == hipSuccess) step(inv_axis_launch(p, b, p->xh, p->Ci, s));
+    if (e == hipSuccess) step(inv_plane_launch(p, b, p->xh, p->Ci, gx, s));
   }
   return map_err(e);
 }
@@ -882,6 +946,20 @@ fno_status_t fno_spectral_conv2d_backward(fno_plan_t plan, const void *x, const 
 fno_status_t fno_spectral_conv3d_backward(fno_plan_t plan, const void *x, const void *w, const void *grad_y,
                                           void *grad_x, void *grad_w, void *stream) {
   return exec_backward(plan, 3, x, w, grad_y, grad_x, grad_w, stream);
+}
+
+fno_status_t fno_spectral_conv_noalloc(fno_plan_t plan, const void *x, const void *w, void *y, void *stream) {
+  if (!plan) return FNO_ERR_INVALID_ARG;
+  fno_status_t st = check_exec(plan, plan->ndim, x, w, y);
+  if (st != FNO_OK) return st;
+  if (carve(plan, nullptr, nullptr) > (size_t)FNO_NOALLOC_SCRATCH_BYTES) return FNO_ERR_UNSUPPORTED;
+  DeviceGuard g(plan->device);
+  if (g.err != hipSuccess) return FNO_ERR_DEVICE;
+  unsigned char *base = nullptr;
+  if (scratch_address(plan->device, &base) != hipSuccess) return FNO_ERR_DEVICE;
+  Bufs b;
+  carve(plan, base, &b);
+  return exec_with(plan, b, x, w, y, (hipStream_t)stream, -1);
 }
 
 fno_status_t fno_plan_workspace_bytes(fno_plan_t plan, size_t *bytes) {

@@ -114,3 +114,8 @@ def test_plain_c_program_builds_and_links(tmp_path):
                         f"-Wl,-rpath,{libdir}", "-o", str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     assert subprocess.run([str(exe)], timeout=60).returncode == 0
+
+
+def test_noalloc_rejects_null_plan_on_host(L):
+    # argument checks run before any HIP call, so no GPU is needed
+    assert L.fno_spectral_conv_noalloc(None, None, None, None, None) == INVALID

@@ -1,0 +1,71 @@
+"""The allocation-free entry point (fno_spectral_conv_noalloc) against the
+plan-workspace entry point on the same inputs, through the C ABI.
+
+Both run the same kernels on the same inputs, so their outputs must agree bit
+for bit; they differ only in where the spectra live (the library's static
+scratch array instead of the plan's workspace). Two calls in a row, the second
+on a smaller layer, check that a call leaves nothing behind that the next one
+depends on; each output is also held to the oracle's tolerance.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import spectral_convolution_amd as fno
+import workloads as wl
+from gpu_util import TOL, rel_l2, to_device, to_float64
+
+pytestmark = pytest.mark.gpu
+
+# (ndim, batch, c_in, c_out, grid, modes, dtype, kind): the larger layer first
+CASES = [
+    [(2, 8, 32, 32, (128, 128), (16, 16), "f32", "grf"), (2, 2, 5, 3, (64, 32), (7, 5), "f32", "uniform")],
+    [(2, 16, 32, 32, (128, 128), (16, 16), "f16", "grf"), (2, 3, 4, 6, (64, 64), (9, 12), "bf16", "uniform")],
+    [(3, 2, 8, 8, (32, 32, 32), (8, 8, 8), "f32", "grf"), (3, 1, 3, 2, (16, 16, 16), (4, 5, 3), "f32", "uniform")],
+]
+
+
+def _run(shape, seed):
+    import torch
+    ndim, B, Ci, Co, grid, modes, dtype, kind = shape
+    cfg = wl.LayerConfig("noalloc", ndim, B, Ci, Co, tuple(grid), tuple(modes), (dtype,), seed, kind)
+    inp = wl.layer_inputs(cfg, dtype)
+    plan = fno.fno_plan_create(ndim, B, Ci, Co, grid, modes, dtype, 0)
+    try:
+        x, w = to_device(inp["x"], dtype), to_device(inp["w"], dtype)
+        y_ref = torch.empty(plan.y_shape(), dtype=x.dtype, device=x.device)
+        y_na = torch.full(plan.y_shape(), float("nan"), dtype=x.dtype, device=x.device)
+        (fno.fno_spectral_conv2d if ndim == 2 else fno.fno_spectral_conv3d)(plan, x, w, y_ref)
+        fno.fno_spectral_conv_noalloc(plan, x, w, y_na)
+        torch.cuda.synchronize()
+        a, b = to_float64(y_ref), to_float64(y_na)
+    finally:
+        fno.fno_plan_destroy(plan)
+    f = oracle.spectral_conv2d if ndim == 2 else oracle.spectral_conv3d
+    ref = f(inp["x64"], inp["w64"], *modes)
+    return a, b, ref, dtype
+
+
+@pytest.mark.parametrize("pair", CASES, ids=["2d-f32", "2d-f16-then-bf16", "3d-f32"])
+def test_noalloc_matches_workspace_path(pair):
+    for k, shape in enumerate(pair):
+        print(f"noalloc case {shape} call {k}", flush=True)
+        a, b, ref, dtype = _run(shape, seed=40 + k)
+        assert np.array_equal(a, b), f"call {k}: max |diff| {np.max(np.abs(a - b))}"
+        assert rel_l2(b, ref) <= TOL[dtype]
+
+
+def test_noalloc_rejects_oversize():
+    import torch
+    # 64 x 64 x 2048 complex fp32 spectra each way = 128 MiB > 64 MiB
+    plan = fno.fno_plan_create(2, 64, 64, 64, (256, 256), (32, 32), "f16", 0)
+    try:
+        x = torch.zeros(plan.x_shape(), dtype=torch.float16, device="cuda:0")
+        w = torch.zeros(plan.w_shape(), dtype=torch.float16, device="cuda:0")
+        y = torch.empty(plan.y_shape(), dtype=torch.float16, device="cuda:0")
+        with pytest.raises(fno.FnoError) as e:
+            fno.fno_spectral_conv_noalloc(plan, x, w, y)
+        assert e.value.status == 2  # FNO_ERR_UNSUPPORTED
+    finally:
+        fno.fno_plan_destroy(plan)
