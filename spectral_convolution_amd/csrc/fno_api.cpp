@@ -297,8 +297,15 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
   } else {
     p.K = 2 * modes[0] * modes[1];
   }
-  const int np_f = batch * c_in * (ndim == 3 ? grid[0] : 1);
-  const int np_i = batch * c_out * (ndim == 3 ? grid[0] : 1);
+  // plane and element counts in 64 bits, checked before any use: batch and
+  // channels may each be up to 65535, whose product overflows an int
+  long pts = 1;
+  for (int d = 0; d < ndim; ++d) pts *= grid[d];
+  const long cmax = c_in > c_out ? c_in : c_out;
+  const long planes = (long)batch * cmax * (ndim == 3 ? grid[0] : 1);
+  if (planes > 0x7fffffffL || (double)batch * cmax * (double)pts > 1e12) return FNO_ERR_UNSUPPORTED;
+  const int np_f = (int)((long)batch * c_in * (ndim == 3 ? grid[0] : 1));
+  const int np_i = (int)((long)batch * c_out * (ndim == 3 ? grid[0] : 1));
   p.rpt = plane_rpt(p.pMP, p.pW / p.pMP);
   p.rc = plane_rc(p.pH, p.pMP);
   p.ppw_f = plane_ppw(true, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_f);
@@ -322,12 +329,6 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
     if (p.lds_axis > kMaxLds) return FNO_ERR_UNSUPPORTED;
     if ((long)batch * (c_in > c_out ? c_in : c_out) > 65535) return FNO_ERR_UNSUPPORTED;
   }
-  // element counts must stay well inside 64-bit / 32-bit grid limits
-  long pts = 1;
-  for (int d = 0; d < ndim; ++d) pts *= grid[d];
-  const long planes = (long)batch * (c_in > c_out ? c_in : c_out) * (ndim == 3 ? grid[0] : 1);
-  if (planes > 0x7fffffffL || (double)batch * (c_in > c_out ? c_in : c_out) * pts > 1e12)
-    return FNO_ERR_UNSUPPORTED;
   p.bb = contract_pick_bb(batch, c_out, p.K);
   p.split = contract_pick_split(batch, c_in, c_out, p.K, p.bb);
   // The matrix-core contraction gives each workgroup a block of 8 modes x

@@ -65,6 +65,10 @@ def _create(L, ndim, batch, ci, co, grid, modes, dtype=0, device=0):
     ((2, 2, 4, 4, (16, 128), (4, 16)), UNSUPPORTED),    # MP = 16 > H/2 = 8
     ((3, 2, 4, 4, (16, 16, 16), (4, 4, 9)), INVALID),   # m3 > Z/2
     ((2, 2, 4, 4, (16, 16), (4, 4), 7), INVALID),       # dtype
+    # batch * channels overflows a 32-bit int: rejected before any use
+    ((2, 65535, 65535, 4, (16, 16), (4, 4)), UNSUPPORTED),
+    ((2, 65535, 4, 65535, (64, 64), (4, 4)), UNSUPPORTED),
+    ((3, 65535, 65535, 65535, (8, 8, 8), (4, 4, 4)), UNSUPPORTED),
 ])
 def test_plan_create_rejects_on_host(L, args, expect):
     st, h = _create(L, *args)
