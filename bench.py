@@ -88,6 +88,8 @@ def _kernel_bytes(cfg, dtype, name):
         return 0, yh + to
     if name.startswith("fno_inv_plane"):
         return y, (yh if to is None else to)
+    if name.startswith("fno_layer_fused"):
+        return x + w + y, 2 * (xh + yh)
     raise KeyError(name)
 
 
@@ -133,6 +135,16 @@ class Layer:
     def launch(self, idx, i):
         x, w, y = self.sets[i % self.nsets]
         self.fno.fno_plan_run_launch(self.plan, idx, x, w, y, self.stream)
+
+    def set_shape(self, shape):
+        """Select a launch shape; False when the plan has no such shape."""
+        try:
+            self.fno.fno_plan_set_launch_shape(self.plan, shape)
+        except self.fno.FnoError:
+            return False
+        self.names = [self.fno.fno_plan_launch_name(self.plan, i)
+                      for i in range(self.fno.fno_plan_num_launches(self.plan))]
+        return True
 
     def close(self):
         self.fno.fno_plan_destroy(self.plan)
@@ -212,7 +224,9 @@ def _latencies(fn, n, warmup, stream):
 
 def latency_sweep(n=200, warmup=20):
     """The 128^2 fp32 layer (Ci=Co=32, modes 16x16) at batch 1..8: eager
-    calls and replays of a captured graph of one call."""
+    calls in the plan's default launch shape (three kernels) and as one
+    cooperative launch, and replays of a captured graph of one call (the
+    three kernels: a captured call never takes the cooperative launch)."""
     import torch
     import spectral_convolution_amd as fno
     import workloads as wl
@@ -225,6 +239,10 @@ def latency_sweep(n=200, warmup=20):
             x, w = to_device(inp["x"], "f32"), to_device(inp["w"], "f32")
             y = torch.empty(plan.y_shape(), dtype=x.dtype, device=x.device)
             stream = torch.cuda.current_stream()
+            shape = fno.fno_plan_get_launch_shape(plan)
+            fno.fno_plan_set_launch_shape(plan, "fused")
+            eager_fused = _latencies(lambda i: fno.fno_spectral_conv2d(plan, x, w, y, stream), n, warmup, stream)
+            fno.fno_plan_set_launch_shape(plan, shape)
             eager = _latencies(lambda i: fno.fno_spectral_conv2d(plan, x, w, y, stream), n, warmup, stream)
             side = torch.cuda.Stream()
             side.wait_stream(stream)
@@ -237,7 +255,8 @@ def latency_sweep(n=200, warmup=20):
             torch.cuda.synchronize()
             replay = _latencies(lambda i: graph.replay(), n, warmup, torch.cuda.current_stream())
             del graph
-            out.append({"batch": B, "eager_us": eager, "graph_us": replay,
+            out.append({"batch": B, "launch_shape": shape, "eager_us": eager, "eager_fused_us": eager_fused,
+                        "graph_us": replay,
                         "samples_per_s_eager": B / (eager["mean"] * 1e-6),
                         "samples_per_s_graph": B / (replay["mean"] * 1e-6)})
         finally:
@@ -384,16 +403,33 @@ def measure(cfg, dtype, steps, warmup, settle_ms=SETTLE_MS, per_kernel=True):
         # Infinity Cache, so this is not the HBM-bound figure
         hot = _time_loop(lambda i: lay.step(0), steps, max(2, warmup // 4), lay.stream, settle_ms)
         res["hot_single_set_layers_per_s"] = 1000.0 / hot
+        shape = lay.fno.fno_plan_get_launch_shape(lay.plan)
+        res["launch_shape"] = shape
+        # ablation: the layer in each launch shape the plan has (one
+        # cooperative launch, or the three stand-alone kernels)
+        res["launch_shapes"] = {}
+        for sh in ("fused", "separate"):
+            if not lay.set_shape(sh):
+                continue
+            t = _time_loop(lay.step, steps, warmup, lay.stream, settle_ms)
+            res["launch_shapes"][sh] = {"ms_per_layer": t, "layers_per_s": 1000.0 / t,
+                                        "launches_per_layer": len(lay.names)}
         if per_kernel:
-            kms = _kernel_times(lay, steps, max(2, warmup // 4), settle_ms)
+            # every kernel of both shapes alone; the roofline takes the
+            # dominant kernel of the shape the layer runs in
             res["kernels"] = []
-            for name, t in zip(lay.names, kms):
-                alg, exch = _kernel_bytes(cfg, dtype, name)
-                g = alg / (t * 1e-3) / 1e9
-                res["kernels"].append({"kernel": name, "ms": t, "algorithmic_bytes": alg,
-                                       "exchange_bytes": exch, "gbps": g, "frac": g / HBM_PEAK_GBPS,
-                                       "gbps_with_exchange": (alg + exch) / (t * 1e-3) / 1e9})
-            res["roofline"] = _roofline(cfg, dtype, res["kernels"])
+            for sh in ("separate", "fused"):
+                if not lay.set_shape(sh):
+                    continue
+                kms = _kernel_times(lay, steps, max(2, warmup // 4), settle_ms)
+                for name, t in zip(lay.names, kms):
+                    alg, exch = _kernel_bytes(cfg, dtype, name)
+                    g = alg / (t * 1e-3) / 1e9
+                    res["kernels"].append({"kernel": name, "launch_shape": sh, "ms": t, "algorithmic_bytes": alg,
+                                           "exchange_bytes": exch, "gbps": g, "frac": g / HBM_PEAK_GBPS,
+                                           "gbps_with_exchange": (alg + exch) / (t * 1e-3) / 1e9})
+            res["roofline"] = _roofline(cfg, dtype, [k for k in res["kernels"] if k["launch_shape"] == shape])
+        lay.set_shape(shape)
         return res
     finally:
         lay.close()
@@ -483,7 +519,9 @@ METRIC_CONFIGS = [("c2", "f16"), ("c2", "bf16"), ("c1", "f32"), ("c1", "f16"), (
 def _summary(r):
     d = r["per_layer_us"]
     rf = r["roofline"]
-    return (f"{r['workload']} {r['dtype']}: {r['layers_per_s']:.1f} layers/s, {r['gbps']:.0f} GB/s "
+    shp = ", ".join(f"{k} {v['layers_per_s']:.0f}/s" for k, v in r.get("launch_shapes", {}).items())
+    return (f"{r['workload']} {r['dtype']} [{r.get('launch_shape')}; {shp}]: {r['layers_per_s']:.1f} layers/s, "
+            f"{r['gbps']:.0f} GB/s "
             f"({100 * r['hbm_frac']:.1f} % of 8 TB/s); per layer p50 {d['p50']:.1f} us (mean {d['mean']:.1f}, "
             f"std {d['std']:.1f}, min {d['min']:.1f}); dominant {rf['kernel']} {1000 * rf['ms_per_launch']:.1f} us "
             f"= {rf['achieved']:.0f} GB/s algorithmic ({100 * rf['frac']:.1f} %)")
@@ -592,7 +630,8 @@ def main():
     if not args.no_latency:
         out["latency"] = latency_sweep()
         print("[bench] latency " + ", ".join(
-            f"B={r['batch']}: eager {r['eager_us']['mean']:.1f}±{r['eager_us']['std']:.1f} us, "
+            f"B={r['batch']}: eager ({r['launch_shape']}) {r['eager_us']['mean']:.1f}±{r['eager_us']['std']:.1f} us, "
+            f"eager (fused) {r['eager_fused_us']['mean']:.1f} us, "
             f"graph {r['graph_us']['mean']:.1f}±{r['graph_us']['std']:.1f} us"
             for r in out["latency"]["sweep"]), file=sys.stderr, flush=True)
     out["copy_1gib"] = copy_bandwidth(1 << 30)

@@ -208,6 +208,45 @@ fno_status_t fno_plan_launch_name(fno_plan_t plan, int index,
 fno_status_t fno_plan_run_launch(fno_plan_t plan, int index, const void *x,
                                  const void *w, void *y, void *stream);
 
+/* ---- launch shape --------------------------------------------------------
+ * A 2D layer call runs either as three stream-ordered kernels (forward
+ * planes, contraction, inverse planes) or as one persistent cooperative
+ * launch whose workgroups run the same three phases joined by two grid-wide
+ * barriers (TurboFNO write-up, section 3.4: FFT -> GEMM -> iFFT in one fused
+ * kernel; section 5.2: the three-kernel split measured as the slower mode).
+ * Both agree with the reference to the same tolerance; they split the
+ * contraction's input-channel sums differently, so they are not bit for bit
+ * equal. A single-launch variant exists for 2D plans with VALU planes whose
+ * next_pow2(max mode) is 4, 8 or 16, or matrix-core planes with W of 64 or
+ * 128 and at most 16 modes per axis, on devices with cooperative launches.
+ * Every plan starts in FNO_LAUNCH_SEPARATE, which measures faster on MI355X
+ * at every size the single launch exists for. Calls queued while the stream
+ * is being captured into a graph always use the three kernels; backward
+ * calls always do.
+ *
+ * FNO_LAUNCH_FUSED_STALL_TEST exists only to exercise the error path: the
+ * barriers wait for one workgroup more than the grid has, every wait gives
+ * up after a few hundred polls, the kernel finishes with meaningless output
+ * and fno_plan_check then reports FNO_ERR_DEVICE.
+ */
+typedef enum {
+  FNO_LAUNCH_SEPARATE = 0,
+  FNO_LAUNCH_FUSED = 1,
+  FNO_LAUNCH_FUSED_STALL_TEST = 2
+} fno_launch_shape_t;
+
+/* Select the launch shape of the plan's later forward calls. INVALID_ARG:
+ * NULL plan or an unknown shape; UNSUPPORTED: a single-launch shape on a plan
+ * without a single-launch variant. Not thread-safe against concurrent calls
+ * on the same plan. */
+fno_status_t fno_plan_set_launch_shape(fno_plan_t plan, int shape);
+fno_status_t fno_plan_get_launch_shape(fno_plan_t plan, int *shape);
+
+/* Wait for the plan's device to finish its queued work, then report whether
+ * a single-launch call's barrier wait gave up since the last check
+ * (FNO_ERR_DEVICE; the barrier state is then reset) or FNO_OK. Synchronous. */
+fno_status_t fno_plan_check(fno_plan_t plan);
+
 /* Device pointer to the plan's forward spectra (which = 0, complex fp32
  * [B][Ci][K], already scaled by 1/prod(grid)) or to the contracted spectra
  * (which = 1, complex fp32 [B][Co][K]); K = 2*m1*m2 (2D) or 4*m1*m2*m3 (3D),

@@ -312,6 +312,27 @@ def fno_plan_spectra(plan, which):
     return p.value
 
 
+LAUNCH_SHAPES = {"separate": 0, "fused": 1, "fused_stall_test": 2}
+
+
+def fno_plan_set_launch_shape(plan, shape):
+    """Launch shape of the plan's forward calls: "separate" (three kernels),
+    "fused" (one cooperative launch) or "fused_stall_test" (error-path test)."""
+    check(lib().fno_plan_set_launch_shape(plan.handle, LAUNCH_SHAPES[shape]), "fno_plan_set_launch_shape")
+
+
+def fno_plan_get_launch_shape(plan):
+    n = ctypes.c_int()
+    check(lib().fno_plan_get_launch_shape(plan.handle, ctypes.byref(n)), "fno_plan_get_launch_shape")
+    return {v: k for k, v in LAUNCH_SHAPES.items()}[n.value]
+
+
+def fno_plan_check(plan):
+    """Wait for the device; raises FnoError(FNO_ERR_DEVICE) if a single-launch
+    call's barrier wait gave up since the last check."""
+    check(lib().fno_plan_check(plan.handle), "fno_plan_check")
+
+
 class SpectralConv:
     """Owns a plan; call with (x, w[, y]) torch tensors on the plan's device."""
 

@@ -18,9 +18,9 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfno.so")
 
-SOURCES = ["plane_kernels.hip", "plane_mfma.hip", "axis_kernels.hip", "contract.hip", "contract_mx.hip", "backward.hip", "weights.hip", "pointwise.hip", "fno_api.cpp",
+SOURCES = ["plane_kernels.hip", "plane_mfma.hip", "axis_kernels.hip", "contract.hip", "contract_mx.hip", "backward.hip", "weights.hip", "pointwise.hip", "fused.hip", "fno_api.cpp",
            "fno_model.cpp"]
-HEADERS = ["common.hpp", "fft_reg.hpp", "plane_common.hpp"]
+HEADERS = ["common.hpp", "fft_reg.hpp", "plane_common.hpp", "plane_valu.hpp", "plane_mfma.hpp", "contract.hpp"]
 
 ARCH = "gfx950"
 CFLAGS = [

@@ -157,6 +157,46 @@ struct WeightsArgs {
   int layout, unpack, ndim, Ci, Co, m1, m2, m3, mc;  // mc: modes in one corner
 };
 
+// The whole 2D layer as one launch (forward planes, contraction, inverse
+// planes joined by grid barriers). Barrier state lives in the plan's
+// workspace: `count` workgroups arrived at the current barrier (zero between
+// barriers), `gen` completed barriers, `err` set when a wait gave up; each
+// on its own 128-byte line.
+struct FusedBarrier {
+  unsigned count, pad0[31], gen, pad1[31], err, pad2[31];
+};
+
+struct FusedValuArgs {
+  PlaneFwdArgs fwd;
+  ContractArgs ctr;
+  PlaneInvArgs inv;
+  FusedBarrier *bar;
+  unsigned nbar;  // workgroups a barrier waits for (the grid size)
+  unsigned spin;  // polls before a barrier wait gives up
+};
+
+struct FusedMxArgs {
+  PlaneMxFwdArgs fwd;
+  ContractArgs ctr;
+  PlaneMxInvArgs inv;
+  FusedBarrier *bar;
+  unsigned nbar;
+  unsigned spin;
+};
+
+// what selects the single-launch kernel variant
+struct FusedShape {
+  bool mx;           // matrix-core planes, else VALU planes
+  int dtype, W, m1, m2, MP, Co;
+};
+
+bool fused_supported(const FusedShape &f);
+size_t fused_lds_bytes(const FusedShape &f, size_t lds_fwd, size_t lds_inv);
+// raises the kernel's LDS allowance and returns the largest co-resident grid
+hipError_t fused_prepare(const FusedShape &f, size_t lds, int device, int *grid);
+// args: FusedValuArgs or FusedMxArgs as f.mx says; a cooperative launch
+hipError_t launch_layer_fused(const FusedShape &f, const void *args, int grid, size_t lds, hipStream_t s);
+
 // Allow kernel k at least `lds` bytes of dynamic LDS. The attribute belongs
 // to the kernel, not to a plan, and several live plans can share one
 // kernel, so the cap only ever grows (a later, smaller plan must not lower

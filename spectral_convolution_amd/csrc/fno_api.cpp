@@ -57,7 +57,14 @@ constexpr int kMinAxis = 8;
 constexpr int kMaxRegFFT = 32;
 constexpr size_t kMaxLds = 160 * 1024;
 
-enum LaunchKind { L_FWD_PLANE, L_FWD_AXIS, L_CONTRACT, L_INV_AXIS, L_INV_PLANE };
+enum LaunchKind { L_FWD_PLANE, L_FWD_AXIS, L_CONTRACT, L_INV_AXIS, L_INV_PLANE, L_FUSED };
+
+// Grid-barrier waits of the single-launch layer: polls before giving up
+// (each poll sleeps ~128 clocks and reads the barrier word from memory, so
+// this is of the order of a second), and the tiny bound of the stall test.
+constexpr unsigned kBarrierSpin = 1u << 20;
+constexpr unsigned kStallTestSpin = 256;
+
 
 bool is_pow2(long v) { return v > 0 && (v & (v - 1)) == 0; }
 int next_pow2(int v) {
@@ -243,10 +250,23 @@ struct fno_plan_s {
   uint4 *tf_lo = nullptr, *tb_lo = nullptr, *ef_f_lo = nullptr, *ef_i_lo = nullptr;  // fp32 plans
   float2 *tw_h = nullptr, *tw_w = nullptr, *tw_x = nullptr;
   float2 *xh = nullptr, *yh = nullptr, *tbuf = nullptr;
+  // single-launch layer (2D): variant, availability, current launch shape,
+  // co-resident grid, LDS, barrier words (in the workspace)
+  FusedShape fshape{};
+  bool fused_ok = false;
+  int shape = FNO_LAUNCH_SEPARATE;
+  int fused_grid = 0;
+  size_t lds_fused = 0;
+  FusedBarrier *bar = nullptr;
   void *mem = nullptr;
   size_t ws_bytes = 0;
-  std::vector<int> launches;
+  std::vector<int> launches;      // the current launch shape's launches
+  std::vector<int> sep_launches;  // the stand-alone kernels' sequence
 };
+
+static void set_launches(fno_plan_s &p) {
+  p.launches = p.shape == FNO_LAUNCH_SEPARATE ? p.sep_launches : std::vector<int>{L_FUSED};
+}
 
 static fno_status_t map_err(hipError_t e) {
   if (e == hipSuccess) return FNO_OK;
@@ -350,10 +370,21 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
   p.lds_ib = p.mx ? p.lds_inv : plane_inv_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP, p.ppw_ib);
   if (p.lds_fg > kMaxLds || p.lds_ib > kMaxLds) return FNO_ERR_UNSUPPORTED;
   if (ndim == 2) {
-    p.launches = {L_FWD_PLANE, L_CONTRACT, L_INV_PLANE};
+    p.sep_launches = {L_FWD_PLANE, L_CONTRACT, L_INV_PLANE};
   } else {
-    p.launches = {L_FWD_PLANE, L_FWD_AXIS, L_CONTRACT, L_INV_AXIS, L_INV_PLANE};
+    p.sep_launches = {L_FWD_PLANE, L_FWD_AXIS, L_CONTRACT, L_INV_AXIS, L_INV_PLANE};
   }
+  // the single launch: 2D only, for the plane variants it is built for
+  if (ndim == 2) {
+    p.fshape = FusedShape{p.mx, (int)dtype, p.pW, p.pm1, p.pm2, p.pMP, c_out};
+    p.fused_ok = fused_supported(p.fshape);
+    p.lds_fused = fused_lds_bytes(p.fshape, p.lds_fwd, p.lds_inv);
+    if (p.lds_fused > kMaxLds) p.fused_ok = false;
+  }
+  // three launches by default: measured faster than the single launch at
+  // every size it exists for (the cooperative launch alone costs ~19 us)
+  p.shape = FNO_LAUNCH_SEPARATE;
+  set_launches(p);
   return FNO_OK;
 }
 
@@ -444,6 +475,7 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   const size_t o_yh = off; off += al(n_yh * sizeof(float2));
   const size_t o_t = off; off += al(n_t * sizeof(float2));
   const size_t o_wh = off; off += al((size_t)p->K * p->Ci * p->Co * 2 * (p->dtype == FNO_F32 ? 4 : 2));
+  const size_t o_bar = off; off += al(sizeof(FusedBarrier));
   std::vector<uint16_t> tfh, tfl, tbh, tbl, efh, efl, eih, eil;
   if (p->mx) {
     const bool sp = p->dtype == FNO_F32;
@@ -480,6 +512,7 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   p->yh = (float2 *)(base + o_yh);
   p->tbuf = n_t ? (float2 *)(base + o_t) : nullptr;
   p->wh = base + o_wh;
+  p->bar = (FusedBarrier *)(base + o_bar);
   uint4 *tab_ptr[8] = {};
   for (int t = 0; t < 8; ++t) tab_ptr[t] = tabs[t]->empty() ? nullptr : (uint4 *)(base + o_tab[t]);
   p->tf = tab_ptr[0];
@@ -492,7 +525,8 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   p->ef_i_lo = tab_ptr[7];
 
   std::vector<float2> th = twiddles(nth), tw = twiddles(ntw);
-  e = hipMemcpy(p->tw_h, th.data(), nth * sizeof(float2), hipMemcpyHostToDevice);
+  e = hipMemset(p->bar, 0, sizeof(FusedBarrier));
+  if (e == hipSuccess) e = hipMemcpy(p->tw_h, th.data(), nth * sizeof(float2), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(p->tw_w, tw.data(), ntw * sizeof(float2), hipMemcpyHostToDevice);
   if (e == hipSuccess && ntx) {
     std::vector<float2> tx = twiddles(ntx);
@@ -532,6 +566,23 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   if (e == hipSuccess) e = p->cmx ? contract_mx_prepare(p->dtype, p->B) : contract_prepare(p->bb, p->dtype, p->Co, lds_c);
   if (e == hipSuccess)
     e = p->cmx_a ? contract_mx_prepare(p->dtype, p->B) : contract_prepare(p->bb_a, p->dtype, p->Ci, lds_c);
+  if (e == hipSuccess && p->fused_ok) {
+    // the largest co-resident grid, trimmed to the most work units of a phase
+    int cap = 0;
+    const hipError_t ef = fused_prepare(p->fshape, p->lds_fused, p->device, &cap);
+    if (ef == hipSuccess) {
+      const long planes = (long)p->B * std::max(p->Ci, p->Co);
+      const long units_p = p->mx ? planes : (planes + std::min(p->ppw_f, p->ppw_i) - 1) / std::min(p->ppw_f, p->ppw_i);
+      const long units_c = (long)((p->K + 15) / 16) * ((p->B + 3) / 4) * ((p->Co + 15) / 16);
+      p->fused_grid = (int)std::min<long>(cap, std::max(units_p, units_c));
+    } else if (ef == hipErrorNotSupported) {
+      p->fused_ok = false;  // no cooperative launch on this device: three launches
+      p->shape = FNO_LAUNCH_SEPARATE;
+      set_launches(*p);
+    } else {
+      e = ef;
+    }
+  }
   if (e != hipSuccess) {
     (void)hipFree(p->mem);
     delete p;
@@ -577,34 +628,39 @@ static Bufs plan_bufs(fno_plan_t p) { return {p->xh, p->yh, p->tbuf}; }
 // the forward and the backward pass share them. nchan is Ci or Co; the
 // persistent grid and planes-per-workgroup were sized for that count.
 
-// plane transforms of `nchan` channels: 2D x -> spectra dst; 3D slabs -> tbuf
-static hipError_t fwd_plane_launch(fno_plan_t p, const Bufs &b, const void *x, int nchan, float2 *dst, hipStream_t s) {
+// Argument blocks of the launches, shared by the stand-alone kernels and the
+// single-launch layer.
+
+// matrix-core forward planes of `nchan` channels: 2D x -> spectra dst; 3D slabs -> tbuf
+static PlaneMxFwdArgs mx_fwd_args(fno_plan_t p, const Bufs &b, const void *x, int nchan, float2 *dst) {
   const int nd = p->ndim;
-  const bool own = nchan == p->Ci;
-  if (p->mx) {
-    PlaneMxFwdArgs m;
-    m.x = x;
-    m.out = nd == 2 ? dst : b.tbuf;
-    m.tw_h = p->tw_h;
-    m.tf = p->tf;
-    m.tf_lo = p->tf_lo;
-    m.ef = p->ef_f;
-    m.ef_lo = p->ef_f_lo;
-    m.nplanes = p->B * nchan * (nd == 3 ? p->xN : 1);
-    m.H = p->pH;
-    m.W = p->pW;
-    m.m1 = p->pm1;
-    m.m2 = p->pm2;
-    m.nt = p->mx_nt;
-    m.mt = p->mx_mt;
-    m.nn = p->mx_nn;
-    m.lgW = p->mx_lgW;
-    m.scale = nd == 2 ? 1.0f / ((float)p->pH * (float)p->pW) : 1.0f;
-    m.x2 = m.x;
-    m.out2 = m.out;
-    m.nsplit = m.nplanes;
-    return launch_plane_mx_fwd(m, own ? p->mx_grid_f : p->mx_grid_fg, p->dtype, p->lds_fwd, s);
-  }
+  PlaneMxFwdArgs m;
+  m.x = x;
+  m.out = nd == 2 ? dst : b.tbuf;
+  m.tw_h = p->tw_h;
+  m.tf = p->tf;
+  m.tf_lo = p->tf_lo;
+  m.ef = p->ef_f;
+  m.ef_lo = p->ef_f_lo;
+  m.nplanes = p->B * nchan * (nd == 3 ? p->xN : 1);
+  m.H = p->pH;
+  m.W = p->pW;
+  m.m1 = p->pm1;
+  m.m2 = p->pm2;
+  m.nt = p->mx_nt;
+  m.mt = p->mx_mt;
+  m.nn = p->mx_nn;
+  m.lgW = p->mx_lgW;
+  m.scale = nd == 2 ? 1.0f / ((float)p->pH * (float)p->pW) : 1.0f;
+  m.x2 = m.x;
+  m.out2 = m.out;
+  m.nsplit = m.nplanes;
+  return m;
+}
+
+// VALU forward planes, as above
+static PlaneFwdArgs valu_fwd_args(fno_plan_t p, const Bufs &b, const void *x, int nchan, float2 *dst) {
+  const int nd = p->ndim;
   PlaneFwdArgs a;
   a.x = x;
   a.out = nd == 2 ? dst : b.tbuf;
@@ -617,10 +673,20 @@ static hipError_t fwd_plane_launch(fno_plan_t p, const Bufs &b, const void *x, i
   a.m2 = p->pm2;
   a.PH = p->pH / p->pMP;
   a.PW = p->pW / p->pMP;
-  a.ppw = own ? p->ppw_f : p->ppw_fg;
+  a.ppw = nchan == p->Ci ? p->ppw_f : p->ppw_fg;
   a.rc = p->rc;
   a.scale = nd == 2 ? 1.0f / ((float)p->pH * (float)p->pW) : 1.0f;
-  return launch_plane_fwd(a, p->pMP, p->rpt, p->dtype, own ? p->lds_fwd : p->lds_fg, s);
+  return a;
+}
+
+// plane transforms of `nchan` channels: 2D x -> spectra dst; 3D slabs -> tbuf
+static hipError_t fwd_plane_launch(fno_plan_t p, const Bufs &b, const void *x, int nchan, float2 *dst, hipStream_t s) {
+  const bool own = nchan == p->Ci;
+  if (p->mx)
+    return launch_plane_mx_fwd(mx_fwd_args(p, b, x, nchan, dst), own ? p->mx_grid_f : p->mx_grid_fg, p->dtype,
+                               p->lds_fwd, s);
+  return launch_plane_fwd(valu_fwd_args(p, b, x, nchan, dst), p->pMP, p->rpt, p->dtype, own ? p->lds_fwd : p->lds_fg,
+                          s);
 }
 
 // 2D matrix-core planes of x (Ci channels) and gy (Co channels) in one
@@ -665,9 +731,7 @@ static hipError_t fwd_axis_launch(fno_plan_t p, const Bufs &b, int nchan, float2
   return launch_axis_fwd(a, p->xMP, p->lds_axis, s);
 }
 
-// contraction: forward (Ci -> Co with w) or adjoint (Co -> Ci with W^H)
-static hipError_t contract_launch(fno_plan_t p, const float2 *in, const void *w, float2 *out, bool adjoint,
-                                  hipStream_t s) {
+static ContractArgs contract_args(fno_plan_t p, const float2 *in, const void *w, float2 *out, bool adjoint) {
   ContractArgs a;
   a.xh = in;
   a.w = w;
@@ -676,6 +740,13 @@ static hipError_t contract_launch(fno_plan_t p, const float2 *in, const void *w,
   a.Ci = adjoint ? p->Co : p->Ci;
   a.Co = adjoint ? p->Ci : p->Co;
   a.K = p->K;
+  return a;
+}
+
+// contraction: forward (Ci -> Co with w) or adjoint (Co -> Ci with W^H)
+static hipError_t contract_launch(fno_plan_t p, const float2 *in, const void *w, float2 *out, bool adjoint,
+                                  hipStream_t s) {
+  const ContractArgs a = contract_args(p, in, w, out, adjoint);
   if (adjoint)
     return p->cmx_a ? launch_contract_mx(a, p->dtype, s) : launch_contract(a, p->bb_a, p->split_a, p->dtype, s);
   return p->cmx ? launch_contract_mx(a, p->dtype, s) : launch_contract(a, p->bb, p->split, p->dtype, s);
@@ -696,29 +767,31 @@ static hipError_t inv_axis_launch(fno_plan_t p, const Bufs &b, const float2 *src
   return launch_axis_inv(a, p->xMP, s);
 }
 
-// inverse plane transforms of `nchan` channels: 2D spectra src -> y; 3D tbuf -> y
-static hipError_t inv_plane_launch(fno_plan_t p, const Bufs &b, const float2 *src, int nchan, void *y, hipStream_t s) {
+// matrix-core inverse planes of `nchan` channels: 2D spectra src -> y; 3D tbuf -> y
+static PlaneMxInvArgs mx_inv_args(fno_plan_t p, const Bufs &b, const float2 *src, int nchan, void *y) {
   const int nd = p->ndim;
-  const bool own = nchan == p->Co;
-  if (p->mx) {
-    PlaneMxInvArgs m;
-    m.in = nd == 2 ? src : b.tbuf;
-    m.y = y;
-    m.tw_h = p->tw_h;
-    m.tb = p->tb;
-    m.tb_lo = p->tb_lo;
-    m.ef = p->ef_i;
-    m.ef_lo = p->ef_i_lo;
-    m.nplanes = p->B * nchan * (nd == 3 ? p->xN : 1);
-    m.H = p->pH;
-    m.W = p->pW;
-    m.m1 = p->pm1;
-    m.m2 = p->pm2;
-    m.nn = p->mx_nn;
-    m.kb1 = p->mx_kb1;
-    m.lg4m1 = p->mx_lg4m1;
-    return launch_plane_mx_inv(m, own ? p->mx_grid_i : p->mx_grid_ib, p->dtype, p->lds_inv, s);
-  }
+  PlaneMxInvArgs m;
+  m.in = nd == 2 ? src : b.tbuf;
+  m.y = y;
+  m.tw_h = p->tw_h;
+  m.tb = p->tb;
+  m.tb_lo = p->tb_lo;
+  m.ef = p->ef_i;
+  m.ef_lo = p->ef_i_lo;
+  m.nplanes = p->B * nchan * (nd == 3 ? p->xN : 1);
+  m.H = p->pH;
+  m.W = p->pW;
+  m.m1 = p->pm1;
+  m.m2 = p->pm2;
+  m.nn = p->mx_nn;
+  m.kb1 = p->mx_kb1;
+  m.lg4m1 = p->mx_lg4m1;
+  return m;
+}
+
+// VALU inverse planes, as above
+static PlaneInvArgs valu_inv_args(fno_plan_t p, const Bufs &b, const float2 *src, int nchan, void *y) {
+  const int nd = p->ndim;
   PlaneInvArgs a;
   a.in = nd == 2 ? src : b.tbuf;
   a.y = y;
@@ -731,8 +804,33 @@ static hipError_t inv_plane_launch(fno_plan_t p, const Bufs &b, const float2 *sr
   a.m2 = p->pm2;
   a.PH = p->pH / p->pMP;
   a.PW = p->pW / p->pMP;
-  a.ppw = own ? p->ppw_i : p->ppw_ib;
-  return launch_plane_inv(a, p->pMP, p->rpt, p->dtype, own ? p->lds_inv : p->lds_ib, s);
+  a.ppw = nchan == p->Co ? p->ppw_i : p->ppw_ib;
+  return a;
+}
+
+// inverse plane transforms of `nchan` channels: 2D spectra src -> y; 3D tbuf -> y
+static hipError_t inv_plane_launch(fno_plan_t p, const Bufs &b, const float2 *src, int nchan, void *y, hipStream_t s) {
+  const bool own = nchan == p->Co;
+  if (p->mx)
+    return launch_plane_mx_inv(mx_inv_args(p, b, src, nchan, y), own ? p->mx_grid_i : p->mx_grid_ib, p->dtype,
+                               p->lds_inv, s);
+  return launch_plane_inv(valu_inv_args(p, b, src, nchan, y), p->pMP, p->rpt, p->dtype, own ? p->lds_inv : p->lds_ib,
+                          s);
+}
+
+// the whole 2D layer as one cooperative launch
+static hipError_t fused_launch(fno_plan_t p, const Bufs &b, const void *x, const void *w, void *y, hipStream_t s) {
+  const bool stall = p->shape == FNO_LAUNCH_FUSED_STALL_TEST;
+  const unsigned nbar = (unsigned)p->fused_grid + (stall ? 1u : 0u);
+  const unsigned spin = stall ? kStallTestSpin : kBarrierSpin;
+  const ContractArgs c = contract_args(p, b.xh, w, b.yh, false);
+  if (p->mx) {
+    const FusedMxArgs a{mx_fwd_args(p, b, x, p->Ci, b.xh), c, mx_inv_args(p, b, b.yh, p->Co, y), p->bar, nbar, spin};
+    return launch_layer_fused(p->fshape, &a, p->fused_grid, p->lds_fused, s);
+  }
+  const FusedValuArgs a{valu_fwd_args(p, b, x, p->Ci, b.xh), c, valu_inv_args(p, b, b.yh, p->Co, y), p->bar, nbar,
+                        spin};
+  return launch_layer_fused(p->fshape, &a, p->fused_grid, p->lds_fused, s);
 }
 
 static hipError_t run_one(fno_plan_t p, const Bufs &b, int kind, const void *x, const void *w, void *y,
@@ -743,6 +841,7 @@ static hipError_t run_one(fno_plan_t p, const Bufs &b, int kind, const void *x, 
     case L_CONTRACT: return contract_launch(p, b.xh, w, b.yh, false, s);
     case L_INV_AXIS: return inv_axis_launch(p, b, b.yh, p->Co, s);
     case L_INV_PLANE: return inv_plane_launch(p, b, b.yh, p->Co, y, s);
+    case L_FUSED: return fused_launch(p, b, x, w, y, s);
   }
   return hipErrorInvalidValue;
 }
@@ -754,6 +853,7 @@ static const char *launch_name(int kind, bool mx) {
     case L_CONTRACT: return "fno_contract";
     case L_INV_AXIS: return "fno_inv_axis";
     case L_INV_PLANE: return mx ? "fno_inv_plane_mx" : "fno_inv_plane";
+    case L_FUSED: return mx ? "fno_layer_fused_mx" : "fno_layer_fused";
   }
   return "?";
 }
@@ -763,9 +863,17 @@ static const char *launch_name(int kind, bool mx) {
 // device current.
 static fno_status_t exec_with(fno_plan_t p, const Bufs &b, const void *x, const void *w, void *y, hipStream_t s,
                               int only) {
-  for (size_t i = 0; i < p->launches.size(); ++i) {
+  const std::vector<int> *L = &p->launches;
+  if (p->shape != FNO_LAUNCH_SEPARATE && only < 0) {
+    // a cooperative launch is not recorded into a captured graph here: under
+    // capture the layer is queued as its stand-alone kernels
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return FNO_ERR_DEVICE;
+    if (cs != hipStreamCaptureStatusNone) L = &p->sep_launches;
+  }
+  for (size_t i = 0; i < L->size(); ++i) {
     if (only >= 0 && (int)i != only) continue;
-    hipError_t e = run_one(p, b, p->launches[i], x, w, y, s);
+    hipError_t e = run_one(p, b, (*L)[i], x, w, y, s);
     if (e == hipSuccess) e = hipGetLastError();
     if (e != hipSuccess) return map_err(e);
   }
@@ -985,6 +1093,35 @@ fno_status_t fno_plan_run_launch(fno_plan_t plan, int index, const void *x, cons
                                  void *stream) {
   if (!plan || index < 0 || index >= (int)plan->launches.size()) return FNO_ERR_INVALID_ARG;
   return exec(plan, plan->ndim, x, w, y, stream, index);
+}
+
+fno_status_t fno_plan_set_launch_shape(fno_plan_t plan, int shape) {
+  if (!plan) return FNO_ERR_INVALID_ARG;
+  if (shape != FNO_LAUNCH_SEPARATE && shape != FNO_LAUNCH_FUSED && shape != FNO_LAUNCH_FUSED_STALL_TEST)
+    return FNO_ERR_INVALID_ARG;
+  if (shape != FNO_LAUNCH_SEPARATE && !plan->fused_ok) return FNO_ERR_UNSUPPORTED;
+  plan->shape = shape;
+  set_launches(*plan);
+  return FNO_OK;
+}
+
+fno_status_t fno_plan_get_launch_shape(fno_plan_t plan, int *shape) {
+  if (!plan || !shape) return FNO_ERR_INVALID_ARG;
+  *shape = plan->shape;
+  return FNO_OK;
+}
+
+fno_status_t fno_plan_check(fno_plan_t plan) {
+  if (!plan) return FNO_ERR_INVALID_ARG;
+  DeviceGuard g(plan->device);
+  if (g.err != hipSuccess) return FNO_ERR_DEVICE;
+  if (hipDeviceSynchronize() != hipSuccess) return FNO_ERR_DEVICE;
+  FusedBarrier h{};
+  if (hipMemcpy(&h, plan->bar, sizeof h, hipMemcpyDeviceToHost) != hipSuccess) return FNO_ERR_DEVICE;
+  if (!h.err) return FNO_OK;
+  // a barrier wait gave up: its state is unknown, start it afresh
+  if (hipMemset(plan->bar, 0, sizeof(FusedBarrier)) != hipSuccess) return FNO_ERR_DEVICE;
+  return FNO_ERR_DEVICE;
 }
 
 fno_status_t fno_plan_spectra(fno_plan_t plan, int which, void **ptr) {

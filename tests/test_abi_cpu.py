@@ -123,3 +123,10 @@ def test_plain_c_program_builds_and_links(tmp_path):
 def test_noalloc_rejects_null_plan_on_host(L):
     # argument checks run before any HIP call, so no GPU is needed
     assert L.fno_spectral_conv_noalloc(None, None, None, None, None) == INVALID
+
+
+def test_launch_shape_calls_reject_null_plan_on_host(L):
+    n = ctypes.c_int()
+    assert L.fno_plan_set_launch_shape(None, 1) == INVALID
+    assert L.fno_plan_get_launch_shape(None, ctypes.byref(n)) == INVALID
+    assert L.fno_plan_check(None) == INVALID

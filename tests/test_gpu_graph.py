@@ -1,7 +1,9 @@
 """Graph capture of the layer and its backward: a HIP graph captured from one
 call (through torch.cuda.graph, on the capture stream the binding picks up)
-replays to results bitwise equal to the eager call, every replay, with eager
-work and synchronisations between the replays."""
+replays to results bitwise equal to the eager call of the same kernels, every
+replay, with eager work and synchronisations between the replays. A plan in
+the single-launch shape queues its three stand-alone kernels while the stream
+is being captured."""
 
 import numpy as np
 import pytest
@@ -45,10 +47,15 @@ def test_graph_replay_matches_eager(ndim, dtype):
         gx, gw = torch.empty_like(x), torch.empty_like(w)
         fwd = fno.fno_spectral_conv2d if ndim == 2 else fno.fno_spectral_conv3d
         bwd = fno.fno_spectral_conv2d_backward if ndim == 2 else fno.fno_spectral_conv3d_backward
+        # under capture a single-launch plan queues its three stand-alone
+        # kernels, so the eager reference runs those too
+        shape = fno.fno_plan_get_launch_shape(plan)
+        fno.fno_plan_set_launch_shape(plan, "separate")
         fwd(plan, x, w, y)
         bwd(plan, x, w, gy, gx, gw)
         torch.cuda.synchronize()
         ref = (y.clone(), gx.clone(), gw.clone())
+        fno.fno_plan_set_launch_shape(plan, shape)
         g_fwd = _capture(lambda: fwd(plan, x, w, y))
         g_bwd = _capture(lambda: bwd(plan, x, w, gy, gx, gw))
         for rep in range(3):

@@ -246,17 +246,33 @@ def test_deterministic_bitwise():
     assert np.array_equal(a, b)
 
 
+def _names(plan):
+    return [fno.fno_plan_launch_name(plan, i) for i in range(fno.fno_plan_num_launches(plan))]
+
+
 def test_launch_structure():
     p2 = fno.fno_plan_create(2, 2, 4, 4, (16, 16), (4, 4), "f32", 0)
     p3 = fno.fno_plan_create(3, 1, 2, 2, (8, 8, 8), (2, 2, 2), "f32", 0)
     try:
-        assert [fno.fno_plan_launch_name(p2, i) for i in range(fno.fno_plan_num_launches(p2))] == \
-            ["fno_fwd_plane", "fno_contract", "fno_inv_plane"]
+        # three launches by default; one on request where a variant exists
+        assert fno.fno_plan_get_launch_shape(p2) == "separate"
+        assert _names(p2) == ["fno_fwd_plane", "fno_contract", "fno_inv_plane"]
+        fno.fno_plan_set_launch_shape(p2, "fused")
+        assert _names(p2) == ["fno_layer_fused"]
         p4 = fno.fno_plan_create(2, 1, 2, 2, (128, 128), (16, 16), "f16", 0)
         assert fno.fno_plan_launch_name(p4, 0) == "fno_fwd_plane_mx"
         assert fno.fno_plan_launch_name(p4, 2) == "fno_inv_plane_mx"
+        fno.fno_plan_set_launch_shape(p4, "fused")
+        assert _names(p4) == ["fno_layer_fused_mx"]
         fno.fno_plan_destroy(p4)
+        # no single-launch variant for 256-wide planes
+        p5 = fno.fno_plan_create(2, 1, 2, 2, (256, 256), (16, 16), "f16", 0)
+        with pytest.raises(fno.FnoError):
+            fno.fno_plan_set_launch_shape(p5, "fused")
+        fno.fno_plan_destroy(p5)
         assert fno.fno_plan_num_launches(p3) == 5
+        with pytest.raises(fno.FnoError):
+            fno.fno_plan_set_launch_shape(p3, "fused")  # no single launch in 3D
         assert fno.fno_plan_workspace_bytes(p2) > 0
     finally:
         fno.fno_plan_destroy(p2)
