@@ -56,8 +56,22 @@ extern "C" {
 
 typedef struct fno_plan_s *fno_plan_t;
 
-/* Storage dtype of x, w and y. Arithmetic is fp32 throughout (fp32
- * accumulation in the contraction); fp16 / bf16 are storage formats. */
+/* Storage dtype of x, w and y. Every sum accumulates in fp32; the operands
+ * of the products are:
+ *   FNO_F32   transforms: fp16 matrix-core products of hi + lo parts (each
+ *             fp32 operand split into two fp16, about 22 significant bits);
+ *             contraction: fp32 matrix-core products; spectra exchanged
+ *             between launches as complex fp32.
+ *   FNO_F16, FNO_BF16  transforms: fp16 matrix-core products of inputs,
+ *             intermediate row / column results and twiddles, each scaled by
+ *             a power of two chosen from a bound so no fp16 operand overflows
+ *             or loses precision to the subnormal range; contraction: bf16
+ *             matrix-core products of hi + lo parts (exact products of the
+ *             exchanged spectra and the weights); 2D layers on 64..256-wide
+ *             planes with batch >= 16 exchange the spectra as fp16 with
+ *             power-of-two exponents, others as complex fp32.
+ * Planes below 64 rows or columns take register FFTs in fp32 instead of
+ * matrix-core transforms. */
 typedef enum { FNO_F32 = 0, FNO_F16 = 1, FNO_BF16 = 2 } fno_dtype_t;
 
 typedef enum {
@@ -247,11 +261,18 @@ fno_status_t fno_plan_get_launch_shape(fno_plan_t plan, int *shape);
  * (FNO_ERR_DEVICE; the barrier state is then reset) or FNO_OK. Synchronous. */
 fno_status_t fno_plan_check(fno_plan_t plan);
 
-/* Device pointer to the plan's forward spectra (which = 0, complex fp32
- * [B][Ci][K], already scaled by 1/prod(grid)) or to the contracted spectra
- * (which = 1, complex fp32 [B][Co][K]); K = 2*m1*m2 (2D) or 4*m1*m2*m3 (3D),
- * modes ordered as in w. Valid after an execution call has finished. */
+/* Device pointer to the plan's forward spectra (which = 0, [B][Ci][K],
+ * already scaled by 1/prod(grid)) or to the contracted spectra (which = 1,
+ * [B][Co][K]); K = 2*m1*m2 (2D) or 4*m1*m2*m3 (3D), modes ordered as in w.
+ * Valid after a forward execution call has finished. Their format is what
+ * fno_plan_spectra_format reports: 0, complex fp32; 1 (the half exchange of
+ * fp16 / bf16 plans), pairs of fp16 (re, im) scaled by powers of two, the
+ * exponents at which = 2 (int32 [B][Ci], one per forward plane) and
+ * which = 3 (int8 [B][Co][ceil(K/4)], one per group of four contracted
+ * modes); a value is the stored pair times 2^-exponent. which 2 and 3 are
+ * INVALID_ARG for format 0. */
 fno_status_t fno_plan_spectra(fno_plan_t plan, int which, void **ptr);
+fno_status_t fno_plan_spectra_format(fno_plan_t plan, int *half);
 
 /* ---- the full FNO2d network ---------------------------------------------
  * The layer inside its model (TurboFNO write-up, sections 1 and 4.3: the

@@ -306,10 +306,18 @@ def fno_plan_run_launch(plan, index, x, w, y, stream=None):
 
 
 def fno_plan_spectra(plan, which):
-    """Device pointer of the forward (0) or contracted (1) spectra workspace."""
+    """Device pointer of the forward (0) or contracted (1) spectra workspace,
+    or (half exchange only) of their exponents (2, 3)."""
     p = ctypes.c_void_p()
     check(lib().fno_plan_spectra(plan.handle, which, ctypes.byref(p)), "fno_plan_spectra")
     return p.value
+
+
+def fno_plan_spectra_format(plan):
+    """0: complex fp32 spectra; 1: fp16 pairs with power-of-two exponents."""
+    n = ctypes.c_int()
+    check(lib().fno_plan_spectra_format(plan.handle, ctypes.byref(n)), "fno_plan_spectra_format")
+    return n.value
 
 
 LAUNCH_SHAPES = {"separate": 0, "fused": 1, "fused_stall_test": 2}

@@ -32,6 +32,7 @@ SIGNATURES = {
     "fno_plan_launch_name": (_c_int, [_c_void_p, _c_int, ctypes.POINTER(ctypes.c_char_p)]),
     "fno_plan_run_launch": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "fno_plan_spectra": (_c_int, [_c_void_p, _c_int, ctypes.POINTER(_c_void_p)]),
+    "fno_plan_spectra_format": (_c_int, [_c_void_p, _IntP]),
     "fno_plan_set_launch_shape": (_c_int, [_c_void_p, _c_int]),
     "fno_plan_get_launch_shape": (_c_int, [_c_void_p, _IntP]),
     "fno_plan_check": (_c_int, [_c_void_p]),

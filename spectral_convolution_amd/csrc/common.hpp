@@ -33,6 +33,12 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// 2^e as an fp32 with e clamped to a range where it and 2^-e are normal
+__device__ __forceinline__ float pow2f(int e) {
+  e = max(-120, min(120, e));
+  return __uint_as_float((uint32_t)(e + 127) << 23);
+}
+
 // Load two adjacent storage elements p[0], p[1] as fp32 (p 2-element aligned).
 template <int DT>
 __device__ __forceinline__ float2 load_pair(const void *base, size_t idx) {
@@ -107,6 +113,11 @@ struct PlaneMxFwdArgs {
   const void *x2;
   float2 *out2;
   int nsplit;
+  // half exchange (one-set variant only; NULL: complex fp32 to out): the
+  // spectra as fp16 (re, im) pairs [nplanes][2 m1][m2], each plane scaled by
+  // 2^oexp[plane] (the spectra are out16 * 2^-oexp)
+  uint32_t *out16;
+  int *oexp;
 };
 
 struct PlaneMxInvArgs {
@@ -117,6 +128,11 @@ struct PlaneMxInvArgs {
   const uint4 *tb, *tb_lo;  // inverse row DFT, A operand of the transposed product [W/16][nn][64]
   int nplanes, H, W, m1, m2;
   int nn, kb1, lg4m1;  // 16-wide ky tiles, 32-deep blocks of 4 m1, ceil(log2(4 m1))
+  // half exchange (NULL: complex fp32 from in): fp16 (re, im) pairs
+  // [nplanes][K], each group of four modes scaled by 2^iexp[plane][k / 4]
+  // (iexp has ceil(K / 4) entries per plane)
+  const uint32_t *in16;
+  const signed char *iexp;
 };
 
 // Pruned c2c DFT along a strided axis: in [vol][N][C] -> out [vol][2*m][C]
@@ -135,6 +151,13 @@ struct ContractArgs {
   const void *w;     // [K][Ci][Co][2] storage dtype
   float2 *yh;        // [B][Co][K]
   int B, Ci, Co, K;
+  // half exchange (matrix-core contraction only; used when xh16 is not
+  // NULL): the spectra in the layouts of PlaneMxFwdArgs::out16 / oexp and
+  // PlaneMxInvArgs::in16 / iexp
+  const uint32_t *xh16;
+  const int *xexp;
+  uint32_t *yh16;
+  signed char *yexp;
 };
 
 // Weight gradient: dw[k][i][o] = scale * gamma(k) * sum_b conj(xs[b][i][k])

@@ -14,6 +14,13 @@
 // hi + lo (exact: 11 bits), bf16 weights as they are. Products: Xh Wh + Xl Wh
 // (+ Xh Wl for fp16 weights) on v_mfma_f32_16x16x32_bf16.
 //
+// Half exchange (HX): the spectra arrive as fp16 pairs with one power-of-two
+// exponent per (b, i) plane and leave as fp16 pairs with one exponent per
+// group of four modes of a (b, o) row, chosen from the group's largest
+// magnitude so that every value is below 2^14 and, down to 2^-28 of that
+// largest, a normal fp16. An fp16 value splits into bf16 hi + lo exactly, so
+// the products stay exact; only the roundings to fp16 are added.
+//
 // A workgroup owns MB = 8 (or 4) consecutive modes x 16 or 32 batch rows x
 // 32 output channels and streams the input channels in stages of 16: the
 // spectra rows [b][i][MB modes] (8 MB contiguous bytes) and weight rows [mode][i][32 o]
@@ -36,6 +43,12 @@ constexpr int kCT = 256;  // threads per workgroup (4 waves, MB / 4 modes each)
 constexpr int kIC = 16;   // input channels per stage (one 32-deep block of K)
 constexpr int kOT = 32;   // output channels per workgroup (four 16-column tiles of N)
 constexpr int kSP = 40;   // halves per staged fragment row (32 + 8 pad: conflict-free reads)
+
+// two fp32 -> packed fp16 pair (a in the low half), round to nearest even
+__device__ __forceinline__ uint32_t f16x2_rne(float a, float b) {
+  const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)a), hi = __builtin_bit_cast(uint16_t, (_Float16)b);
+  return lo | (hi << 16);
+}
 
 __device__ __forceinline__ v4f mma_bf(u32x4 a, u32x4 b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
@@ -63,7 +76,9 @@ struct CmxShape {
   static constexpr int WS = MB * HL * kOT * kSP;           // halves of the weight stage
 };
 
-template <int DT, int MT, int MB>
+// px[v]: two modes of one (b, i) row; fp32: (re, im, re, im) bits; HX: two
+// fp16 pairs and the row's exponent
+template <int DT, int MT, int MB, bool HX>
 __device__ __forceinline__ void cmx_fetch(const ContractArgs &a, int st, int k0, int b0, int o0, int tid,
                                           u32x4 (&px)[CmxShape<DT, MT, MB>::XU],
                                           u32x4 (&pw)[CmxShape<DT, MT, MB>::WU]) {
@@ -75,8 +90,15 @@ __device__ __forceinline__ void cmx_fetch(const ContractArgs &a, int st, int k0,
     const int row = u / S::UX, c = u % S::UX;  // row = (b, i), i fastest; c: modes 2c, 2c + 1
     const int b = b0 + row / kIC, i = st * kIC + row % kIC, mode = k0 + 2 * c;
     const bool ok = b < B && i < Ci && mode < K;
-    const u32x4 t = *reinterpret_cast<const u32x4 *>(a.xh + (ok ? ((size_t)b * Ci + i) * K + mode : 0));
-    px[v] = ok ? t : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (HX) {
+      const size_t r = ok ? (size_t)b * Ci + i : 0;
+      const uint2 t = *reinterpret_cast<const uint2 *>(a.xh16 + (ok ? r * K + mode : 0));
+      const int e = a.xexp[r];
+      px[v] = ok ? u32x4{t.x, t.y, (uint32_t)e, 0u} : u32x4{0u, 0u, 0u, 0u};
+    } else {
+      const u32x4 t = *reinterpret_cast<const u32x4 *>(a.xh + (ok ? ((size_t)b * Ci + i) * K + mode : 0));
+      px[v] = ok ? t : u32x4{0u, 0u, 0u, 0u};
+    }
   }
 #pragma unroll
   for (int v = 0; v < S::WU; ++v) {
@@ -104,7 +126,7 @@ __device__ __forceinline__ int wcol(int i, int o) { return (i + ((o >> 4) & 1) *
 
 // split and transpose one stage into fragment rows:
 //   xs[mode][part][b][2 i + re/im], ws[mode][part][o][2 i + re/im]
-template <int DT, int MT, int MB>
+template <int DT, int MT, int MB, bool HX>
 __device__ __forceinline__ void cmx_put(uint16_t *xs, uint16_t *ws, int tid, const u32x4 (&px)[CmxShape<DT, MT, MB>::XU],
                                         const u32x4 (&pw)[CmxShape<DT, MT, MB>::WU]) {
   using S = CmxShape<DT, MT, MB>;
@@ -113,10 +135,18 @@ __device__ __forceinline__ void cmx_put(uint16_t *xs, uint16_t *ws, int tid, con
     const int u = v * kCT + tid;
     const int row = u / S::UX, c = u % S::UX;
     const int b = row / kIC, i = row % kIC;
+    const float sc = HX ? pow2f(-(int)px[v][2]) : 1.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       uint32_t hi, lo;
-      split_pair(__uint_as_float(px[v][2 * t]), __uint_as_float(px[v][2 * t + 1]), hi, lo);
+      if constexpr (HX) {
+        // each half converted on its own (see the weight split below)
+        const float re = (float)__builtin_bit_cast(_Float16, (uint16_t)(px[v][t] & 0xffffu)) * sc;
+        const float im = (float)__builtin_bit_cast(_Float16, (uint16_t)(px[v][t] >> 16)) * sc;
+        split_pair(re, im, hi, lo);
+      } else {
+        split_pair(__uint_as_float(px[v][2 * t]), __uint_as_float(px[v][2 * t + 1]), hi, lo);
+      }
       const int m = 2 * c + t;
       reinterpret_cast<uint32_t *>(xs + (m * 2 + 0) * S::XB + xrow<MT>(m, b) * kSP)[i] = hi;
       reinterpret_cast<uint32_t *>(xs + (m * 2 + 1) * S::XB + xrow<MT>(m, b) * kSP)[i] = lo;
@@ -162,7 +192,7 @@ __device__ __forceinline__ u32x4 w_form(u32x4 raw, bool part1) {
 template <int DT, int MB>
 constexpr int cmx_waves() { return MB == 8 ? 2 : DT == DT_F16 ? 3 : 4; }
 
-template <int DT, int MT, int MB>
+template <int DT, int MT, int MB, bool HX>
 __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<DT, MB>()))) void fno_contract_mx(
     ContractArgs a) {
   using S = CmxShape<DT, MT, MB>;
@@ -196,10 +226,10 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<D
       for (int nt = 0; nt < 4; ++nt) acc[mm][mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
   u32x4 px[S::XU], pw[S::WU];
-  cmx_fetch<DT, MT, MB>(a, 0, k0, b0, o0, tid, px, pw);
+  cmx_fetch<DT, MT, MB, HX>(a, 0, k0, b0, o0, tid, px, pw);
   for (int st = 0; st < nst; ++st) {
-    cmx_put<DT, MT, MB>(xs, ws, tid, px, pw);
-    if (st + 1 < nst) cmx_fetch<DT, MT, MB>(a, st + 1, k0, b0, o0, tid, px, pw);
+    cmx_put<DT, MT, MB, HX>(xs, ws, tid, px, pw);
+    if (st + 1 < nst) cmx_fetch<DT, MT, MB, HX>(a, st + 1, k0, b0, o0, tid, px, pw);
     __syncthreads();
 #pragma unroll
     for (int mm = 0; mm < S::MW; ++mm) {
@@ -259,16 +289,47 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<D
         }
       }
     __syncthreads();
-    constexpr int YU = 16 * kOT * MB * 8 / 16 / kCT;  // 16-byte result units per thread
+    if constexpr (HX) {
+      // groups of four modes of one (b, o) row: largest magnitude ->
+      // exponent, fp16 pairs scaled by it (a group cut by K keeps two modes)
+      constexpr int GR = MB / 4;                    // groups per row
+      constexpr int YG = 16 * kOT * GR / kCT;       // groups per thread
+      const int KQ = (K + 3) >> 2;
 #pragma unroll
-    for (int v = 0; v < YU; ++v) {
-      const int u = v * kCT + tid;
-      const int row = u / S::UX, c = u % S::UX;  // row = (b, o); c: modes 2c, 2c + 1
-      const int bl = row / kOT, ol = row % kOT;
-      const int b = b0 + mt * 16 + bl, o = o0 + ol, mode = k0 + 2 * c;
-      if (b < B && o < Co && mode < K)
-        *reinterpret_cast<u32x4 *>(a.yh + ((size_t)b * Co + o) * K + mode) =
-            *reinterpret_cast<const u32x4 *>(ys + bl * S::YB + ol * S::YO + 4 * c);
+      for (int v = 0; v < YG; ++v) {
+        const int u = v * kCT + tid;
+        const int row = u / GR, c = u % GR;
+        const int bl = row / kOT, ol = row % kOT;
+        const int b = b0 + mt * 16 + bl, o = o0 + ol, mode = k0 + 4 * c;
+        if (b < B && o < Co && mode < K) {
+          const float *src = ys + bl * S::YB + ol * S::YO + 8 * c;
+          const float4 p0 = *reinterpret_cast<const float4 *>(src), p1 = *reinterpret_cast<const float4 *>(src + 4);
+          const float m = fmaxf(fmaxf(fmaxf(fabsf(p0.x), fabsf(p0.y)), fmaxf(fabsf(p0.z), fabsf(p0.w))),
+                                fmaxf(fmaxf(fabsf(p1.x), fabsf(p1.y)), fmaxf(fabsf(p1.z), fabsf(p1.w))));
+          int e = 0;
+          if (m > 0.f) (void)frexpf(m, &e);  // m < 2^e
+          const int sx = m > 0.f ? max(-120, min(120, 14 - e)) : 0;
+          const float f = pow2f(sx);
+          uint32_t *dst = a.yh16 + ((size_t)b * Co + o) * K + mode;
+          const uint2 h0 = make_uint2(f16x2_rne(p0.x * f, p0.y * f), f16x2_rne(p0.z * f, p0.w * f));
+          *reinterpret_cast<uint2 *>(dst) = h0;
+          if (mode + 2 < K)
+            *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(f16x2_rne(p1.x * f, p1.y * f), f16x2_rne(p1.z * f, p1.w * f));
+          a.yexp[((size_t)b * Co + o) * KQ + (mode >> 2)] = (signed char)sx;
+        }
+      }
+    } else {
+      constexpr int YU = 16 * kOT * MB * 8 / 16 / kCT;  // 16-byte result units per thread
+#pragma unroll
+      for (int v = 0; v < YU; ++v) {
+        const int u = v * kCT + tid;
+        const int row = u / S::UX, c = u % S::UX;  // row = (b, o); c: modes 2c, 2c + 1
+        const int bl = row / kOT, ol = row % kOT;
+        const int b = b0 + mt * 16 + bl, o = o0 + ol, mode = k0 + 2 * c;
+        if (b < B && o < Co && mode < K)
+          *reinterpret_cast<u32x4 *>(a.yh + ((size_t)b * Co + o) * K + mode) =
+              *reinterpret_cast<const u32x4 *>(ys + bl * S::YB + ol * S::YO + 4 * c);
+      }
     }
   }
 }
@@ -293,16 +354,17 @@ long contract_mx_workgroups(int B, int Co, int K) {
 // layer (B = 32, 64 channels, 32 x 32 modes: 512) slower.
 static int cmx_modes(int B, int Co, int K) { return contract_mx_workgroups(B, Co, K) < 512 ? 4 : 8; }
 
-template <int DT>
+template <int DT, bool HX>
 static const void *contract_mx_kernel_dt(int B, int mb) {
   const bool one = B <= 16;
-  if (mb == 4) return one ? (const void *)fno_contract_mx<DT, 1, 4> : (const void *)fno_contract_mx<DT, 2, 4>;
-  return one ? (const void *)fno_contract_mx<DT, 1, 8> : (const void *)fno_contract_mx<DT, 2, 8>;
+  if (mb == 4) return one ? (const void *)fno_contract_mx<DT, 1, 4, HX> : (const void *)fno_contract_mx<DT, 2, 4, HX>;
+  return one ? (const void *)fno_contract_mx<DT, 1, 8, HX> : (const void *)fno_contract_mx<DT, 2, 8, HX>;
 }
 
-static const void *contract_mx_kernel(int dtype, int B, int mb) {
-  if (dtype == DT_F16) return contract_mx_kernel_dt<DT_F16>(B, mb);
-  if (dtype == DT_BF16) return contract_mx_kernel_dt<DT_BF16>(B, mb);
+static const void *contract_mx_kernel(int dtype, int B, int mb, bool hx) {
+  if (dtype == DT_F16) return hx ? contract_mx_kernel_dt<DT_F16, true>(B, mb) : contract_mx_kernel_dt<DT_F16, false>(B, mb);
+  if (dtype == DT_BF16)
+    return hx ? contract_mx_kernel_dt<DT_BF16, true>(B, mb) : contract_mx_kernel_dt<DT_BF16, false>(B, mb);
   return nullptr;
 }
 
@@ -318,18 +380,19 @@ size_t contract_mx_lds_bytes(int dtype, int B) {
 }
 
 hipError_t contract_mx_prepare(int dtype, int B) {
-  for (int mb : {4, 8}) {
-    const void *k = contract_mx_kernel(dtype, B, mb);
-    if (!k) return hipErrorInvalidValue;
-    const hipError_t e = raise_lds_cap(k, contract_mx_lds_bytes(dtype, B, mb));
-    if (e != hipSuccess) return e;
-  }
+  for (int mb : {4, 8})
+    for (bool hx : {false, true}) {
+      const void *k = contract_mx_kernel(dtype, B, mb, hx);
+      if (!k) return hipErrorInvalidValue;
+      const hipError_t e = raise_lds_cap(k, contract_mx_lds_bytes(dtype, B, mb));
+      if (e != hipSuccess) return e;
+    }
   return hipSuccess;
 }
 
 hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s) {
   const int mb = cmx_modes(a.B, a.Co, a.K);
-  const void *k = contract_mx_kernel(dtype, a.B, mb);
+  const void *k = contract_mx_kernel(dtype, a.B, mb, a.xh16 != nullptr);
   if (!k) return hipErrorInvalidValue;
   const int BT = a.B <= 16 ? 16 : 32;
   const long nkb = (long)((a.K + mb - 1) / mb) * ((a.B + BT - 1) / BT), no = (a.Co + kOT - 1) / kOT;

@@ -233,6 +233,12 @@ struct fno_plan_s {
   size_t lds_axis = 0;
   int bb = 1, split = 1;
   bool cmx = false;  // fp16 / bf16 contraction on bf16 matrix cores
+  // half exchange of the forward layer: the spectra between its launches as
+  // fp16 pairs with power-of-two exponents (fp16 / bf16 2D plans on the
+  // matrix-core planes and contraction); the backward keeps complex fp32
+  bool hx = false;
+  int *xe = nullptr;           // [B][Ci] exponents of the forward spectra
+  signed char *ye = nullptr;   // [B][Co][ceil(K / 4)] exponents of the contracted spectra
   // backward: the adjoint contraction (Co -> Ci channels), the weight
   // gradient, plane transforms over the other channel count (forward of g
   // over Co channels, inverse over Ci)
@@ -360,6 +366,7 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
   // vs 23.2 at 8, 28.2 vs 25.7 at 16, 71.8 vs 31.9 at 32.
   p.cmx = contract_mx_supported((int)dtype, c_out, p.K) && contract_mx_workgroups(batch, c_out, p.K) >= 256 &&
           batch >= 16;
+  p.hx = dtype != FNO_F32 && ndim == 2 && p.mx && p.cmx;
   p.bb_a = contract_pick_bb(batch, c_in, p.K);
   p.split_a = contract_pick_split(batch, c_out, c_in, p.K, p.bb_a);
   p.cmx_a = contract_mx_supported((int)dtype, c_in, p.K) && contract_mx_workgroups(batch, c_in, p.K) >= 256 &&
@@ -476,6 +483,8 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   const size_t o_t = off; off += al(n_t * sizeof(float2));
   const size_t o_wh = off; off += al((size_t)p->K * p->Ci * p->Co * 2 * (p->dtype == FNO_F32 ? 4 : 2));
   const size_t o_bar = off; off += al(sizeof(FusedBarrier));
+  const size_t o_xe = off; off += al(p->hx ? (size_t)p->B * p->Ci * sizeof(int) : 0);
+  const size_t o_ye = off; off += al(p->hx ? (size_t)p->B * p->Co * ((p->K + 3) / 4) : 0);
   std::vector<uint16_t> tfh, tfl, tbh, tbl, efh, efl, eih, eil;
   if (p->mx) {
     const bool sp = p->dtype == FNO_F32;
@@ -513,6 +522,8 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   p->tbuf = n_t ? (float2 *)(base + o_t) : nullptr;
   p->wh = base + o_wh;
   p->bar = (FusedBarrier *)(base + o_bar);
+  p->xe = p->hx ? (int *)(base + o_xe) : nullptr;
+  p->ye = p->hx ? (signed char *)(base + o_ye) : nullptr;
   uint4 *tab_ptr[8] = {};
   for (int t = 0; t < 8; ++t) tab_ptr[t] = tabs[t]->empty() ? nullptr : (uint4 *)(base + o_tab[t]);
   p->tf = tab_ptr[0];
@@ -620,9 +631,11 @@ static fno_status_t check_exec(fno_plan_t p, int ndim, const void *x, const void
 // static scratch array for fno_spectral_conv_noalloc.
 struct Bufs {
   float2 *xh, *yh, *tbuf;
+  int *xe;          // half exchange: exponents of the forward spectra (fp16 pairs in xh)
+  signed char *ye;  // and of the contracted spectra (fp16 pairs in yh)
 };
 
-static Bufs plan_bufs(fno_plan_t p) { return {p->xh, p->yh, p->tbuf}; }
+static Bufs plan_bufs(fno_plan_t p) { return {p->xh, p->yh, p->tbuf, p->xe, p->ye}; }
 
 // Launch helpers, parameterised by source, channel count and destination so
 // the forward and the backward pass share them. nchan is Ci or Co; the
@@ -632,9 +645,11 @@ static Bufs plan_bufs(fno_plan_t p) { return {p->xh, p->yh, p->tbuf}; }
 // single-launch layer.
 
 // matrix-core forward planes of `nchan` channels: 2D x -> spectra dst; 3D slabs -> tbuf
-static PlaneMxFwdArgs mx_fwd_args(fno_plan_t p, const Bufs &b, const void *x, int nchan, float2 *dst) {
+static PlaneMxFwdArgs mx_fwd_args(fno_plan_t p, const Bufs &b, const void *x, int nchan, float2 *dst, bool half) {
   const int nd = p->ndim;
   PlaneMxFwdArgs m;
+  m.out16 = half ? reinterpret_cast<uint32_t *>(dst) : nullptr;
+  m.oexp = half ? b.xe : nullptr;
   m.x = x;
   m.out = nd == 2 ? dst : b.tbuf;
   m.tw_h = p->tw_h;
@@ -680,10 +695,11 @@ static PlaneFwdArgs valu_fwd_args(fno_plan_t p, const Bufs &b, const void *x, in
 }
 
 // plane transforms of `nchan` channels: 2D x -> spectra dst; 3D slabs -> tbuf
-static hipError_t fwd_plane_launch(fno_plan_t p, const Bufs &b, const void *x, int nchan, float2 *dst, hipStream_t s) {
+static hipError_t fwd_plane_launch(fno_plan_t p, const Bufs &b, const void *x, int nchan, float2 *dst, hipStream_t s,
+                                   bool half = false) {
   const bool own = nchan == p->Ci;
   if (p->mx)
-    return launch_plane_mx_fwd(mx_fwd_args(p, b, x, nchan, dst), own ? p->mx_grid_f : p->mx_grid_fg, p->dtype,
+    return launch_plane_mx_fwd(mx_fwd_args(p, b, x, nchan, dst, half), own ? p->mx_grid_f : p->mx_grid_fg, p->dtype,
                                p->lds_fwd, s);
   return launch_plane_fwd(valu_fwd_args(p, b, x, nchan, dst), p->pMP, p->rpt, p->dtype, own ? p->lds_fwd : p->lds_fg,
                           s);
@@ -699,6 +715,8 @@ static hipError_t fwd_planes_both(fno_plan_t p, const Bufs &b, const void *x, co
   m.out2 = b.yh;
   m.nsplit = p->B * p->Ci;
   m.nplanes = p->B * (p->Ci + p->Co);
+  m.out16 = nullptr;
+  m.oexp = nullptr;
   m.tw_h = p->tw_h;
   m.tf = p->tf;
   m.tf_lo = p->tf_lo;
@@ -731,8 +749,13 @@ static hipError_t fwd_axis_launch(fno_plan_t p, const Bufs &b, int nchan, float2
   return launch_axis_fwd(a, p->xMP, p->lds_axis, s);
 }
 
-static ContractArgs contract_args(fno_plan_t p, const float2 *in, const void *w, float2 *out, bool adjoint) {
+static ContractArgs contract_args(fno_plan_t p, const Bufs &b, const float2 *in, const void *w, float2 *out,
+                                  bool adjoint, bool half) {
   ContractArgs a;
+  a.xh16 = half ? reinterpret_cast<const uint32_t *>(in) : nullptr;
+  a.xexp = half ? b.xe : nullptr;
+  a.yh16 = half ? reinterpret_cast<uint32_t *>(out) : nullptr;
+  a.yexp = half ? b.ye : nullptr;
   a.xh = in;
   a.w = w;
   a.yh = out;
@@ -744,9 +767,9 @@ static ContractArgs contract_args(fno_plan_t p, const float2 *in, const void *w,
 }
 
 // contraction: forward (Ci -> Co with w) or adjoint (Co -> Ci with W^H)
-static hipError_t contract_launch(fno_plan_t p, const float2 *in, const void *w, float2 *out, bool adjoint,
-                                  hipStream_t s) {
-  const ContractArgs a = contract_args(p, in, w, out, adjoint);
+static hipError_t contract_launch(fno_plan_t p, const Bufs &b, const float2 *in, const void *w, float2 *out,
+                                  bool adjoint, hipStream_t s, bool half = false) {
+  const ContractArgs a = contract_args(p, b, in, w, out, adjoint, half);
   if (adjoint)
     return p->cmx_a ? launch_contract_mx(a, p->dtype, s) : launch_contract(a, p->bb_a, p->split_a, p->dtype, s);
   return p->cmx ? launch_contract_mx(a, p->dtype, s) : launch_contract(a, p->bb, p->split, p->dtype, s);
@@ -768,9 +791,11 @@ static hipError_t inv_axis_launch(fno_plan_t p, const Bufs &b, const float2 *src
 }
 
 // matrix-core inverse planes of `nchan` channels: 2D spectra src -> y; 3D tbuf -> y
-static PlaneMxInvArgs mx_inv_args(fno_plan_t p, const Bufs &b, const float2 *src, int nchan, void *y) {
+static PlaneMxInvArgs mx_inv_args(fno_plan_t p, const Bufs &b, const float2 *src, int nchan, void *y, bool half) {
   const int nd = p->ndim;
   PlaneMxInvArgs m;
+  m.in16 = half ? reinterpret_cast<const uint32_t *>(src) : nullptr;
+  m.iexp = half ? b.ye : nullptr;
   m.in = nd == 2 ? src : b.tbuf;
   m.y = y;
   m.tw_h = p->tw_h;
@@ -809,10 +834,11 @@ static PlaneInvArgs valu_inv_args(fno_plan_t p, const Bufs &b, const float2 *src
 }
 
 // inverse plane transforms of `nchan` channels: 2D spectra src -> y; 3D tbuf -> y
-static hipError_t inv_plane_launch(fno_plan_t p, const Bufs &b, const float2 *src, int nchan, void *y, hipStream_t s) {
+static hipError_t inv_plane_launch(fno_plan_t p, const Bufs &b, const float2 *src, int nchan, void *y, hipStream_t s,
+                                   bool half = false) {
   const bool own = nchan == p->Co;
   if (p->mx)
-    return launch_plane_mx_inv(mx_inv_args(p, b, src, nchan, y), own ? p->mx_grid_i : p->mx_grid_ib, p->dtype,
+    return launch_plane_mx_inv(mx_inv_args(p, b, src, nchan, y, half), own ? p->mx_grid_i : p->mx_grid_ib, p->dtype,
                                p->lds_inv, s);
   return launch_plane_inv(valu_inv_args(p, b, src, nchan, y), p->pMP, p->rpt, p->dtype, own ? p->lds_inv : p->lds_ib,
                           s);
@@ -823,9 +849,11 @@ static hipError_t fused_launch(fno_plan_t p, const Bufs &b, const void *x, const
   const bool stall = p->shape == FNO_LAUNCH_FUSED_STALL_TEST;
   const unsigned nbar = (unsigned)p->fused_grid + (stall ? 1u : 0u);
   const unsigned spin = stall ? kStallTestSpin : kBarrierSpin;
-  const ContractArgs c = contract_args(p, b.xh, w, b.yh, false);
+  // the single launch exchanges complex fp32 spectra
+  const ContractArgs c = contract_args(p, b, b.xh, w, b.yh, false, false);
   if (p->mx) {
-    const FusedMxArgs a{mx_fwd_args(p, b, x, p->Ci, b.xh), c, mx_inv_args(p, b, b.yh, p->Co, y), p->bar, nbar, spin};
+    const FusedMxArgs a{mx_fwd_args(p, b, x, p->Ci, b.xh, false), c, mx_inv_args(p, b, b.yh, p->Co, y, false), p->bar,
+                        nbar, spin};
     return launch_layer_fused(p->fshape, &a, p->fused_grid, p->lds_fused, s);
   }
   const FusedValuArgs a{valu_fwd_args(p, b, x, p->Ci, b.xh), c, valu_inv_args(p, b, b.yh, p->Co, y), p->bar, nbar,
@@ -836,11 +864,11 @@ static hipError_t fused_launch(fno_plan_t p, const Bufs &b, const void *x, const
 static hipError_t run_one(fno_plan_t p, const Bufs &b, int kind, const void *x, const void *w, void *y,
                           hipStream_t s) {
   switch (kind) {
-    case L_FWD_PLANE: return fwd_plane_launch(p, b, x, p->Ci, b.xh, s);
+    case L_FWD_PLANE: return fwd_plane_launch(p, b, x, p->Ci, b.xh, s, p->hx);
     case L_FWD_AXIS: return fwd_axis_launch(p, b, p->Ci, b.xh, s);
-    case L_CONTRACT: return contract_launch(p, b.xh, w, b.yh, false, s);
+    case L_CONTRACT: return contract_launch(p, b, b.xh, w, b.yh, false, s, p->hx);
     case L_INV_AXIS: return inv_axis_launch(p, b, b.yh, p->Co, s);
-    case L_INV_PLANE: return inv_plane_launch(p, b, b.yh, p->Co, y, s);
+    case L_INV_PLANE: return inv_plane_launch(p, b, b.yh, p->Co, y, s, p->hx);
     case L_FUSED: return fused_launch(p, b, x, w, y, s);
   }
   return hipErrorInvalidValue;
@@ -923,12 +951,17 @@ static size_t carve(fno_plan_t p, unsigned char *base, Bufs *b) {
   auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
   const size_t n_xh = (size_t)p->B * p->Ci * p->K, n_yh = (size_t)p->B * p->Co * p->K;
   const size_t n_t = p->tbuf ? (size_t)p->B * (p->Ci > p->Co ? p->Ci : p->Co) * p->xN * 2 * p->modes[1] * p->modes[2] : 0;
-  const size_t o_xh = 0, o_yh = o_xh + al(n_xh * sizeof(float2)), o_t = o_yh + al(n_yh * sizeof(float2));
-  const size_t total = o_t + al(n_t * sizeof(float2));
+  const size_t sb = p->hx ? 4 : sizeof(float2);  // bytes per exchanged mode
+  const size_t o_xh = 0, o_yh = o_xh + al(n_xh * sb), o_t = o_yh + al(n_yh * sb);
+  const size_t o_xe = o_t + al(n_t * sizeof(float2));
+  const size_t o_ye = o_xe + al(p->hx ? (size_t)p->B * p->Ci * sizeof(int) : 0);
+  const size_t total = o_ye + al(p->hx ? (size_t)p->B * p->Co * ((p->K + 3) / 4) : 0);
   if (base && b) {
     b->xh = (float2 *)(base + o_xh);
     b->yh = (float2 *)(base + o_yh);
     b->tbuf = n_t ? (float2 *)(base + o_t) : nullptr;
+    b->xe = p->hx ? (int *)(base + o_xe) : nullptr;
+    b->ye = p->hx ? (signed char *)(base + o_ye) : nullptr;
   }
   return total;
 }
@@ -990,7 +1023,7 @@ static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const v
   }
   if (gx) {
     if (e == hipSuccess) step(launch_conj_transpose(w, p->wh, p->K, p->Ci, p->Co, p->dtype, s));
-    if (e == hipSuccess) step(contract_launch(p, p->yh, p->wh, p->xh, true, s));
+    if (e == hipSuccess) step(contract_launch(p, b, p->yh, p->wh, p->xh, true, s));
     if (d3 && e == hipSuccess) step(inv_axis_launch(p, b, p->xh, p->Ci, s));
     if (e == hipSuccess) step(inv_plane_launch(p, b, p->xh, p->Ci, gx, s));
   }
@@ -1125,8 +1158,16 @@ fno_status_t fno_plan_check(fno_plan_t plan) {
 }
 
 fno_status_t fno_plan_spectra(fno_plan_t plan, int which, void **ptr) {
-  if (!plan || !ptr || (which != 0 && which != 1)) return FNO_ERR_INVALID_ARG;
-  *ptr = which == 0 ? (void *)plan->xh : (void *)plan->yh;
+  if (!plan || !ptr || which < 0 || which > 3) return FNO_ERR_INVALID_ARG;
+  if (which >= 2 && !plan->hx) return FNO_ERR_INVALID_ARG;
+  void *const v[4] = {plan->xh, plan->yh, plan->xe, plan->ye};
+  *ptr = v[which];
+  return FNO_OK;
+}
+
+fno_status_t fno_plan_spectra_format(fno_plan_t plan, int *half) {
+  if (!plan || !half) return FNO_ERR_INVALID_ARG;
+  *half = plan->hx ? 1 : 0;
   return FNO_OK;
 }
 

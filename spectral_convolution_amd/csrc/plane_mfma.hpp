@@ -107,12 +107,6 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   return __int_as_float(wave_max_i32(__float_as_int(v)));
 }
 
-// 2^e as an fp32 with e clamped to a range where it and 2^-e are normal
-__device__ __forceinline__ float pow2f(int e) {
-  e = max(-120, min(120, e));
-  return __uint_as_float((uint32_t)(e + 127) << 23);
-}
-
 // ------------------------------------------------------------------ forward
 
 constexpr int kFT = 256;  // threads per workgroup of the inverse plane kernel (4 waves)
@@ -295,11 +289,13 @@ __device__ __forceinline__ int fwd_round_exp(int g, const FwdLds<DT, KB> &L) {
 //    largest exponent is noted for the R scale. bf16 and fp32 rows are
 //    scaled by 2^sig into fp16 range (fp32 as hi + lo parts), with sig from
 //    the round's largest exponent, noted one step earlier; this step notes
-//    that of round g + 1 (registers pn). Returns sig.
+//    that of round g + 1 (registers pn). Returns sig; er: round g's largest
+//    exponent for bf16 / fp32 (read here, before the slot is refilled by the
+//    next step), -1000 for fp16 (read after the barrier instead).
 template <int DT, int KB, int NW, bool TW>
 __device__ __forceinline__ int fwd_put(int g, const FwdShape &s, u32x4 (&p)[FwdIO<DT, KB, NW>::FU],
                                        const u32x4 (&pn)[FwdIO<DT, KB, NW>::FU], const PlaneMxFwdArgs &a,
-                                       const FwdLds<DT, KB> &L) {
+                                       const FwdLds<DT, KB> &L, int &er_out) {
   using P = MxPol<DT>;
   constexpr bool BF = DT == DT_BF16, SP = P::SP;
   constexpr int PITCH = FwdLds<DT, KB>::PITCH, STG = FwdLds<DT, KB>::STG;
@@ -307,9 +303,11 @@ __device__ __forceinline__ int fwd_put(int g, const FwdShape &s, u32x4 (&p)[FwdI
   const int tid = threadIdx.x;
   u32x4 *stage = L.stage + (g & 1) * P::NP * STG;
   int sig = 0;
+  er_out = -1000;
   if constexpr (BF || SP) {
     const int er = fwd_round_exp<DT, KB, NW>(g, L);
     sig = er > -1000 ? max(-120, min(120, 14 - er)) : 0;  // round max * 2^sig < 2^15
+    er_out = er;
   }
   const float sc = pow2f(sig);
 #pragma unroll
@@ -411,9 +409,13 @@ __device__ __forceinline__ void fwd_row(int g, int se, const FwdShape &s, const 
 
 // 3. column product of round g's R against the 64-row twiddle block (m-tile
 //    wv of the modes), phase-shifted by the round offset and unscaled into X;
-//    after the last round of a plane, X is scaled, stored and reset.
+//    after the last round of a plane, X is scaled, stored and reset. pe: the
+//    plane's largest input exponent (every |x| < 2^pe, so every |X| < 2^pe
+//    after the 1 / (H W) scale), which sets the power-of-two scale of the
+//    half exchange: |X| 2^(14 - pe) < 2^14, and every value down to 2^-28 of
+//    the plane's largest input stays a normal fp16.
 template <int DT, int KB, int CPW, bool TW>
-__device__ __forceinline__ void fwd_col(int g, int se, const FwdShape &s, const PlaneMxFwdArgs &a,
+__device__ __forceinline__ void fwd_col(int g, int se, int pe, const FwdShape &s, const PlaneMxFwdArgs &a,
                                         const FwdLds<DT, KB> &L, const FwdRegs<DT, KB, CPW> &R, float2 (&X)[2][2]) {
   using P = MxPol<DT>;
   constexpr bool SP = P::SP;
@@ -472,6 +474,23 @@ __device__ __forceinline__ void fwd_col(int g, int se, const FwdShape &s, const 
   }
   if (r == (1 << s.lgr) - 1) {
     const size_t plane = (size_t)s.bid + (size_t)(g >> s.lgr) * s.nblk;
+    if (!TW && a.out16) {
+      const int sx = pe > -1000 ? max(-120, min(120, 14 - pe)) : 0;
+      const float f = a.scale * pow2f(sx);
+      uint32_t *op = a.out16 + plane * (2 * s.m1 * s.m2);
+#pragma unroll
+      for (int nn = 0; nn < 2; ++nn) {
+        const int ky = nn * 16 + (lane & 15);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int q = 8 * wv + 2 * (lane >> 4) + t;
+          if (nn < s.NN && ky < s.m2 && q < 2 * s.m1) op[q * s.m2 + ky] = h16x2(X[nn][t].x * f, X[nn][t].y * f);
+          X[nn][t] = make_float2(0.f, 0.f);
+        }
+      }
+      if (threadIdx.x == 0) a.oexp[plane] = sx;
+      return;
+    }
     float2 *op = a.out + plane * (2 * s.m1 * s.m2);
     if constexpr (TW) {
       if (plane >= (size_t)a.nsplit) op = a.out2 + (plane - a.nsplit) * (2 * s.m1 * s.m2);
@@ -492,17 +511,25 @@ __device__ __forceinline__ void fwd_col(int g, int se, const FwdShape &s, const 
 
 // One pipeline step: stage round g, one barrier, then round g's row product
 // and round g - 1's column product (different LDS buffers).
-// se_prev: total scale exponent of round g - 1's R (staging and R scale)
+// se_prev: total scale exponent of round g - 1's R (staging and R scale);
+// pe: largest input exponent of the rounds so far of round g - 1's plane
+// (then of round g's)
 template <int DT, int KB, int CPW, int NW, bool TW>
-__device__ __forceinline__ void fwd_step(int g, int &se_prev, const FwdShape &s, u32x4 (&p)[FwdIO<DT, KB, NW>::FU],
-                                         const u32x4 (&pn)[FwdIO<DT, KB, NW>::FU], const PlaneMxFwdArgs &a,
-                                         const FwdLds<DT, KB> &L, const FwdRegs<DT, KB, CPW> &R, float2 (&X)[2][2]) {
-  const int sig = fwd_put<DT, KB, NW, TW>(g, s, p, pn, a, L);
+__device__ __forceinline__ void fwd_step(int g, int &se_prev, int &pe, const FwdShape &s,
+                                         u32x4 (&p)[FwdIO<DT, KB, NW>::FU], const u32x4 (&pn)[FwdIO<DT, KB, NW>::FU],
+                                         const PlaneMxFwdArgs &a, const FwdLds<DT, KB> &L,
+                                         const FwdRegs<DT, KB, CPW> &R, float2 (&X)[2][2]) {
+  int eg;
+  const int sig = fwd_put<DT, KB, NW, TW>(g, s, p, pn, a, L, eg);
   __syncthreads();
   const int se = fwd_scale<DT, KB, NW>(g, s, L);
+  // fp16: round g's exponents were noted in this step's staging; their slot
+  // is refilled two steps later, after the next barrier
+  if constexpr (DT == DT_F16) eg = fwd_round_exp<DT, KB, NW>(g, L);
   fwd_row<DT, KB, CPW, NW>(g, se, s, L, R);
-  if (g > 0) fwd_col<DT, KB, CPW, TW>(g - 1, se_prev, s, a, L, R, X);
+  if (g > 0) fwd_col<DT, KB, CPW, TW>(g - 1, se_prev, pe, s, a, L, R, X);
   se_prev = se + sig;
+  pe = (g & ((1 << s.lgr) - 1)) == 0 ? eg : max(pe, eg);
 }
 
 // Persistent: workgroup b of nblk transforms planes b, b + nblk, ...; its rounds
@@ -582,18 +609,18 @@ __device__ __forceinline__ void fwd_mx_run(const PlaneMxFwdArgs &a, int bid, int
     fwd_note<DT, KB, NW>(0, p0, L);
     __syncthreads();
   }
-  int se_prev = 0;
+  int se_prev = 0, pe = -1000;
   const int full = s.total - s.total % kPF;
   int g = 0;
   for (; g < full; g += kPF) {
-    fwd_step<DT, KB, CPW, NW, TW>(g, se_prev, s, p0, p1, a, L, R, X);
-    fwd_step<DT, KB, CPW, NW, TW>(g + 1, se_prev, s, p1, p2, a, L, R, X);
-    fwd_step<DT, KB, CPW, NW, TW>(g + 2, se_prev, s, p2, p0, a, L, R, X);
+    fwd_step<DT, KB, CPW, NW, TW>(g, se_prev, pe, s, p0, p1, a, L, R, X);
+    fwd_step<DT, KB, CPW, NW, TW>(g + 1, se_prev, pe, s, p1, p2, a, L, R, X);
+    fwd_step<DT, KB, CPW, NW, TW>(g + 2, se_prev, pe, s, p2, p0, a, L, R, X);
   }
-  if (g < s.total) fwd_step<DT, KB, CPW, NW, TW>(g, se_prev, s, p0, p1, a, L, R, X);
-  if (g + 1 < s.total) fwd_step<DT, KB, CPW, NW, TW>(g + 1, se_prev, s, p1, p2, a, L, R, X);
+  if (g < s.total) fwd_step<DT, KB, CPW, NW, TW>(g, se_prev, pe, s, p0, p1, a, L, R, X);
+  if (g + 1 < s.total) fwd_step<DT, KB, CPW, NW, TW>(g + 1, se_prev, pe, s, p1, p2, a, L, R, X);
   __syncthreads();
-  fwd_col<DT, KB, CPW, TW>(s.total - 1, se_prev, s, a, L, R, X);
+  fwd_col<DT, KB, CPW, TW>(s.total - 1, se_prev, pe, s, a, L, R, X);
 }
 
 // ------------------------------------------------------------------ inverse
@@ -622,6 +649,35 @@ __device__ __forceinline__ void inv_load(const float2 *in, size_t plane, int K, 
     const int v = tid + i * kFT;
     const float2 t = ip[min(v, K - 1)];
     yv[i] = v < K ? t : make_float2(0.f, 0.f);
+  }
+}
+
+// the same from the half exchange: fp16 pairs and the exponent of each group
+// of four modes, kept raw (decoded by inv_decode once they are needed, so the
+// loads stay in flight)
+template <int NY>
+__device__ __forceinline__ void inv_load16(const uint32_t *in, const signed char *ex, size_t plane, int K, int tid,
+                                           uint32_t (&hv)[NY], int (&ev)[NY]) {
+  const uint32_t *ip = in + plane * K;
+  const signed char *ep = ex + plane * ((K + 3) >> 2);
+#pragma unroll
+  for (int i = 0; i < NY; ++i) {
+    const int v = min(tid + i * kFT, K - 1);
+    hv[i] = ip[v];
+    ev[i] = ep[v >> 2];
+  }
+}
+
+template <int NY>
+__device__ __forceinline__ void inv_decode(int K, int tid, const uint32_t (&hv)[NY], const int (&ev)[NY],
+                                           float2 (&yv)[NY]) {
+#pragma unroll
+  for (int i = 0; i < NY; ++i) {
+    // each half converted on its own (as in the contraction's weight split)
+    const float sc = pow2f(-ev[i]);
+    const float re = (float)__builtin_bit_cast(_Float16, (uint16_t)(hv[i] & 0xffffu)) * sc;
+    const float im = (float)__builtin_bit_cast(_Float16, (uint16_t)(hv[i] >> 16)) * sc;
+    yv[i] = tid + i * kFT < K ? make_float2(re, im) : make_float2(0.f, 0.f);
   }
 }
 
@@ -664,7 +720,17 @@ __device__ __forceinline__ void inv_mx_run(const PlaneMxInvArgs &a, int bid, int
   float *ymx = reinterpret_cast<float *>(twh + H);                          // [2][4]
 
   float2 yv[NY], yn[NY];
-  if (nmine > 0) inv_load<NY>(a.in, bid, K, tid, yv);
+  uint32_t hn[NY];
+  int en[NY];
+  const bool half = a.in16 != nullptr;
+  if (nmine > 0) {
+    if (half) {
+      inv_load16<NY>(a.in16, a.iexp, bid, K, tid, hn, en);
+      inv_decode<NY>(K, tid, hn, en, yv);
+    } else {
+      inv_load<NY>(a.in, bid, K, tid, yv);
+    }
+  }
   for (int v = tid; v < NP * YBS / 2; v += kFT) reinterpret_cast<uint32_t *>(yb)[v] = 0u;
   for (int v = tid; v < H; v += kFT) twh[v] = a.tw_h[v];
 
@@ -831,8 +897,10 @@ __device__ __forceinline__ void inv_mx_run(const PlaneMxInvArgs &a, int bid, int
     // The next plane's spectra (after the last plane, this one's again,
     // unused) are requested before the last round: only that round's stores
     // are issued after them, so the copy below waits for nothing else.
-    inv_load<NY>(a.in, pi + 1 < nmine ? plane + nblk : plane, K, tid, yn);
+    if (half) inv_load16<NY>(a.in16, a.iexp, pi + 1 < nmine ? plane + nblk : plane, K, tid, hn, en);
+    else inv_load<NY>(a.in, pi + 1 < nmine ? plane + nblk : plane, K, tid, yn);
     round(rounds - 1);
+    if (half) inv_decode<NY>(K, tid, hn, en, yn);
 #pragma unroll
     for (int i = 0; i < NY; ++i) yv[i] = yn[i];
   }

@@ -59,3 +59,31 @@ def read_spectra(plan, which):
     assert st == 0, f"hipMemcpy failed: {st}"
     c = host[0::2].astype(np.float64) + 1j * host[1::2].astype(np.float64)
     return c
+
+
+def _copy_from_device(ptr, host):
+    import ctypes
+    import torch
+    torch.cuda.synchronize()
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    st = hip.hipMemcpy(host.ctypes.data, ptr, host.nbytes, 2)  # device to host
+    assert st == 0, f"hipMemcpy failed: {st}"
+    return host
+
+
+def read_half_spectra(plan, which):
+    """Decode the half exchange (fp16 pairs times 2^-exponent) of the forward
+    (which 0: one exponent per plane) or contracted (1: one per four modes)
+    spectra into complex128 [B][C][K]."""
+    C = plan.c_in if which == 0 else plan.c_out
+    K = plan.n_modes
+    pairs = _copy_from_device(fno.fno_plan_spectra(plan, which), np.empty(plan.batch * C * K * 2, np.float16))
+    v = (pairs[0::2].astype(np.float64) + 1j * pairs[1::2].astype(np.float64)).reshape(plan.batch, C, K)
+    if which == 0:
+        e = _copy_from_device(fno.fno_plan_spectra(plan, 2), np.empty(plan.batch * C, np.int32))
+        return v * np.ldexp(1.0, -e.astype(np.int64)).reshape(plan.batch, C, 1)
+    kq = (K + 3) // 4
+    e = _copy_from_device(fno.fno_plan_spectra(plan, 3), np.empty(plan.batch * C * kq, np.int8))
+    e = np.repeat(e.reshape(plan.batch, C, kq).astype(np.int64), 4, axis=2)[:, :, :K]
+    return v * np.ldexp(1.0, -e)

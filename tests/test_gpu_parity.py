@@ -17,7 +17,7 @@ import pytest
 import oracle
 import spectral_convolution_amd as fno
 import workloads as wl
-from gpu_util import TOL, read_spectra, rel_l2, run_layer, to_device
+from gpu_util import TOL, read_half_spectra, read_spectra, rel_l2, run_layer, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -221,6 +221,50 @@ def test_intermediate_spectra():
         yh = read_spectra(plan, 1).reshape(2, 4, 12, 11)
         ref_y = oracle.contract(ref, inp["w64"])
         assert rel_l2(yh, ref_y) <= 1e-6
+    finally:
+        fno.fno_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_intermediate_half_spectra(dtype):
+    # fp16 / bf16 plans on the matrix-core planes and contraction exchange
+    # the spectra as fp16 pairs with power-of-two exponents; decoded, they
+    # match the oracle's spectra of the same storage-rounded inputs to the
+    # fp16 rounding (2^-11 relative) plus the transforms' own error
+    cfg = _cfg("s", 2, 16, 8, 32, (64, 64), (32, 32), "grf", seed=7)
+    inp = wl.layer_inputs(cfg, dtype)
+    plan = fno.fno_plan_create(2, 16, 8, 32, cfg.grid, cfg.modes, dtype, 0)
+    try:
+        assert fno.fno_plan_spectra_format(plan) == 1
+        y, _ = run_layer(2, 16, 8, 32, cfg.grid, cfg.modes, dtype, inp["x"], inp["w"], plan=plan)
+        xh = read_half_spectra(plan, 0).reshape(16, 8, 64, 32)
+        ref = oracle.forward2d(inp["x64"], *cfg.modes) / (64 * 64)
+        ex = rel_l2(xh, ref)
+        yh = read_half_spectra(plan, 1).reshape(16, 32, 64, 32)
+        ey = rel_l2(yh, oracle.contract(ref, inp["w64"]))
+        ez = rel_l2(y, oracle.spectral_conv2d(inp["x64"], inp["w64"], *cfg.modes))
+        print(f"[half-spectra] {dtype}: forward {ex:.2e} contracted {ey:.2e} output {ez:.2e}", flush=True)
+        assert ex <= 1e-3 and ey <= 1.5e-3 and ez <= TOL[dtype]
+    finally:
+        fno.fno_plan_destroy(plan)
+
+
+def test_half_spectra_tiny_and_large_inputs():
+    # the exponents follow the data: inputs 2^-40 and 2^+10 times the
+    # workload's (bf16 storage, far outside fp16's range either way) give the
+    # same relative error as unit-scale inputs
+    cfg = _cfg("s", 2, 16, 4, 32, (64, 64), (32, 32), "grf", seed=8)
+    inp = wl.layer_inputs(cfg, "bf16")
+    plan = fno.fno_plan_create(2, 16, 4, 32, cfg.grid, cfg.modes, "bf16", 0)
+    try:
+        errs = []
+        for sc in (2.0 ** -40, 1.0, 2.0 ** 10):
+            xs = wl.round_to_storage(inp["x64"] * sc, "bf16")
+            x64 = wl.storage_to_float64(xs, "bf16")
+            y, _ = run_layer(2, 16, 4, 32, cfg.grid, cfg.modes, "bf16", xs, inp["w"], plan=plan)
+            errs.append(rel_l2(y, oracle.spectral_conv2d(x64, inp["w64"], *cfg.modes)))
+        print(f"[half-spectra] scales 2^-40, 1, 2^10: {errs}", flush=True)
+        assert max(errs) <= TOL["bf16"]
     finally:
         fno.fno_plan_destroy(plan)
 

@@ -23,6 +23,8 @@ CASES = [
     [(2, 8, 32, 32, (128, 128), (16, 16), "f32", "grf"), (2, 2, 5, 3, (64, 32), (7, 5), "f32", "uniform")],
     [(2, 16, 32, 32, (128, 128), (16, 16), "f16", "grf"), (2, 3, 4, 6, (64, 64), (9, 12), "bf16", "uniform")],
     [(3, 2, 8, 8, (32, 32, 32), (8, 8, 8), "f32", "grf"), (3, 1, 3, 2, (16, 16, 16), (4, 5, 3), "f32", "uniform")],
+    # spectra exchanged as fp16 with exponents (matrix-core contraction)
+    [(2, 16, 8, 32, (64, 64), (32, 32), "f16", "grf"), (2, 16, 4, 32, (64, 64), (32, 32), "bf16", "uniform")],
 ]
 
 
@@ -47,7 +49,7 @@ def _run(shape, seed):
     return a, b, ref, dtype
 
 
-@pytest.mark.parametrize("pair", CASES, ids=["2d-f32", "2d-f16-then-bf16", "3d-f32"])
+@pytest.mark.parametrize("pair", CASES, ids=["2d-f32", "2d-f16-then-bf16", "3d-f32", "2d-half-exchange"])
 def test_noalloc_matches_workspace_path(pair):
     for k, shape in enumerate(pair):
         print(f"noalloc case {shape} call {k}", flush=True)
