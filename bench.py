@@ -55,23 +55,29 @@ MAX_SETS = 64
 
 
 SETTLE_MS = 300.0
-SPECTRA_BYTES = 8  # complex fp32 spectra in the plan workspace
 
 
-def _kernel_bytes(cfg, dtype, name):
+def _kernel_bytes(cfg, dtype, name, half_exchange=False):
     """Bytes of one launch of kernel `name`: (algorithmic, exchange).
 
     Algorithmic bytes are the compulsory bytes of the kernel's own step of
     the layer: x for the forward planes, w for the contraction, y for the
     inverse planes, nothing for the 3D outer-axis passes. Exchange bytes are
-    the spectra (and 3D slab transforms) it also writes or reads."""
+    the spectra (and 3D slab transforms) it also writes or reads: complex
+    fp32 (8 bytes a mode), or with the half exchange fp16 pairs (4 bytes a
+    mode) plus an int32 exponent per forward plane and an int8 one per four
+    contracted modes."""
     s = 4 if dtype == "f32" else 2
     pts = int(np.prod(cfg.grid))
     x = cfg.batch * cfg.c_in * pts * s
     y = cfg.batch * cfg.c_out * pts * s
     w = cfg.n_modes * cfg.c_in * cfg.c_out * 2 * s
-    xh = cfg.batch * cfg.c_in * cfg.n_modes * SPECTRA_BYTES
-    yh = cfg.batch * cfg.c_out * cfg.n_modes * SPECTRA_BYTES
+    if half_exchange:
+        xh = cfg.batch * cfg.c_in * (cfg.n_modes * 4 + 4)
+        yh = cfg.batch * cfg.c_out * (cfg.n_modes * 4 + (cfg.n_modes + 3) // 4)
+    else:
+        xh = cfg.batch * cfg.c_in * cfg.n_modes * 8
+        yh = cfg.batch * cfg.c_out * cfg.n_modes * 8
     if cfg.ndim == 2:
         ti = to = None
     else:
@@ -422,8 +428,9 @@ def measure(cfg, dtype, steps, warmup, settle_ms=SETTLE_MS, per_kernel=True):
                 if not lay.set_shape(sh):
                     continue
                 kms = _kernel_times(lay, steps, max(2, warmup // 4), settle_ms)
+                half = sh == "separate" and lay.fno.fno_plan_spectra_format(lay.plan) == 1
                 for name, t in zip(lay.names, kms):
-                    alg, exch = _kernel_bytes(cfg, dtype, name)
+                    alg, exch = _kernel_bytes(cfg, dtype, name, half)
                     g = alg / (t * 1e-3) / 1e9
                     res["kernels"].append({"kernel": name, "launch_shape": sh, "ms": t, "algorithmic_bytes": alg,
                                            "exchange_bytes": exch, "gbps": g, "frac": g / HBM_PEAK_GBPS,

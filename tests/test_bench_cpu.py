@@ -46,6 +46,13 @@ def test_per_launch_bytes_2d():
     assert bench._kernel_bytes(cfg, "f16", "fno_fwd_plane_mx") == (x, xh)
     assert bench._kernel_bytes(cfg, "f16", "fno_contract_mx") == (w, 2 * xh)
     assert bench._kernel_bytes(cfg, "f16", "fno_inv_plane_mx") == (x, xh)
+    # half exchange: fp16 pairs, an int32 exponent per forward plane and an
+    # int8 one per four contracted modes
+    K = 2 * 32 * 32
+    xh16 = 32 * 64 * (K * 4 + 4)
+    yh16 = 32 * 64 * (K * 4 + K // 4)
+    assert bench._kernel_bytes(cfg, "f16", "fno_fwd_plane_mx", True) == (x, xh16)
+    assert bench._kernel_bytes(cfg, "f16", "fno_contract_mx", True) == (w, xh16 + yh16)
 
 
 def test_per_launch_bytes_3d():
