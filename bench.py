@@ -298,11 +298,16 @@ class Model:
     def step(self, i):
         self.fno.fno_model2d_forward(self.model, self.f, self.params, self.out, self.stream)
 
+    def set_graph(self, on):
+        self.fno.fno_model2d_set_graph(self.model, on)
+
     def close(self):
         self.fno.fno_model2d_destroy(self.model)
 
 
 def measure_model(steps, warmup, settle_ms=SETTLE_MS):
+    """The B=20 forward (eager kernels, and replayed from the model's captured
+    HIP graph) and its batch-1 latency both ways."""
     import workloads as wl
     cfg = wl.CONFIGS["c4"]
     m = Model(cfg)
@@ -311,11 +316,17 @@ def measure_model(steps, warmup, settle_ms=SETTLE_MS):
         res = {"workload": "FNO2d forward, B=20, 256x256, lift 3->64, 4 x (spectral conv 64->64 modes "
                            "24x24 + 1x1 conv + GELU), projection 64->128->1, fp16 storage",
                "ms_per_forward": ms, "samples_per_s": m.B / (ms * 1e-3)}
+        m.set_graph(True)
+        msg = _time_loop(m.step, steps, warmup, m.stream, settle_ms)
+        res["ms_per_forward_graph"] = msg
+        res["samples_per_s_graph"] = m.B / (msg * 1e-3)
     finally:
         m.close()
     m1 = Model(cfg, batch=1)
     try:
         res["latency_b1_us"] = _latencies(m1.step, 100, 10, m1.stream)
+        m1.set_graph(True)
+        res["latency_b1_graph_us"] = _latencies(m1.step, 100, 10, m1.stream)
     finally:
         m1.close()
     return res
@@ -632,8 +643,10 @@ def main():
         out["backward"] = bwd
     if not args.no_model:
         out["model"] = measure_model(max(10, args.steps // 10), max(3, args.warmup // 4), settle)
-        print(f"[bench] model: {out['model']['ms_per_forward']:.3f} ms per B=20 forward, "
-              f"B=1 latency {out['model']['latency_b1_us']['mean']:.1f} us", file=sys.stderr, flush=True)
+        mo = out["model"]
+        print(f"[bench] model: {mo['ms_per_forward']:.3f} ms per B=20 forward ({mo['ms_per_forward_graph']:.3f} "
+              f"graph), B=1 latency {mo['latency_b1_us']['mean']:.1f} us ({mo['latency_b1_graph_us']['mean']:.1f} "
+              f"graph)", file=sys.stderr, flush=True)
     if not args.no_latency:
         out["latency"] = latency_sweep()
         print("[bench] latency " + ", ".join(

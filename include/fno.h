@@ -278,8 +278,12 @@ fno_status_t fno_plan_spectra_format(fno_plan_t plan, int *half);
  * The layer inside its model (TurboFNO write-up, sections 1 and 4.3: the
  * fused layer drops into an FNO module): lift Linear, n_layers blocks of
  * GELU(spectral conv + 1x1 conv + bias), projection Linear -> GELU -> Linear.
- * Activations are stored in the storage dtype; arithmetic is fp32. GELU is
- * the exact erf form 0.5 v (1 + erf(v / sqrt 2)). */
+ * Activations are stored in the storage dtype; sums accumulate in fp32. GELU
+ * is the erf form 0.5 v (1 + erf(v / sqrt 2)). With n_layers >= 1 the lift
+ * is folded into the first block: its weights are composed with the lift's
+ * (spectral weights with P, the 1x1 weights with P, the bias with p through
+ * both branches) and the first block runs on the feature channels, so the
+ * lifted field is never stored (the same function up to rounding). */
 
 /* Per-pixel channel mix:
  *   y[b][o][p] = act(sum_i A[o][i] x[b][i][p] + bias[o] + add[b][o][p])
@@ -306,8 +310,9 @@ typedef struct fno_model2d_s *fno_model2d_t;
 /* Plan of the network on [batch][in_channels][height][width] inputs with
  * `channels` hidden channels, spectral modes (m1, m2) in every block,
  * `proj_channels` hidden units in the projection, `out_channels` outputs.
- * Owns a spectral-conv plan and three activation buffers of
- * batch*channels*height*width elements. */
+ * Owns two spectral-conv plans (the first block's from in_channels, the
+ * others') and three activation buffers of batch*channels*height*width
+ * elements, plus the first block's folded weights. */
 fno_status_t fno_model2d_create(fno_model2d_t *model, int batch, int height,
                                 int width, int in_channels, int channels,
                                 int n_layers, int m1, int m2,
@@ -323,6 +328,15 @@ fno_status_t fno_model2d_create(fno_model2d_t *model, int batch, int height,
 fno_status_t fno_model2d_forward(fno_model2d_t model, const void *features,
                                  const void *const *params, void *out,
                                  void *stream);
+
+/* Replay the forward from a HIP graph (on = 1) or queue its kernels on every
+ * call (on = 0, the default). With replay on, the first call, and any call
+ * whose features, out or params pointers differ from the last capture's,
+ * captures the forward on the model's own stream first (synchronous with
+ * respect to the host only in that it builds the graph); later calls launch
+ * the captured graph on `stream`. Calls queued while `stream` is itself
+ * being captured always queue the kernels directly. */
+fno_status_t fno_model2d_set_graph(fno_model2d_t model, int on);
 
 /* Free the model (synchronises its device). NULL is a no-op. */
 fno_status_t fno_model2d_destroy(fno_model2d_t model);

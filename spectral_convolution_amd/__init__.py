@@ -17,7 +17,7 @@ __all__ = [
     "fno_plan_spectra", "fno_spectral_conv2d_backward", "fno_spectral_conv3d_backward", "SpectralConv", "FnoError", "DTYPES",
     "fno_weights_pack", "fno_weights_unpack", "SpectralConvFunction", "spectral_conv",
     "fno_channel_mix", "fno_projection", "fno_model2d_create", "fno_model2d_forward",
-    "fno_model2d_destroy", "Model2d",
+    "fno_model2d_destroy", "Model2d", "fno_model2d_set_graph",
 ]
 
 
@@ -426,6 +426,11 @@ def fno_model2d_forward(model, features, params, out, stream=None):
     arr = (ctypes.c_void_p * len(params))(*[_ptr(t) for t in params])
     check(lib().fno_model2d_forward(model.handle, _ptr(features), arr, _ptr(out),
                                     _stream(stream, model.device)), "fno_model2d_forward")
+
+
+def fno_model2d_set_graph(model, on=True):
+    """Replay the model's forward from a captured HIP graph (see include/fno.h)."""
+    check(lib().fno_model2d_set_graph(model.handle, 1 if on else 0), "fno_model2d_set_graph")
 
 
 def fno_model2d_destroy(model):

@@ -44,6 +44,7 @@ SIGNATURES = {
                                     _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "fno_model2d_forward": (_c_int, [_c_void_p, _c_void_p, ctypes.POINTER(_c_void_p), _c_void_p,
                                      _c_void_p]),
+    "fno_model2d_set_graph": (_c_int, [_c_void_p, _c_int]),
     "fno_model2d_destroy": (_c_int, [_c_void_p]),
 }
 

@@ -271,6 +271,9 @@ hipError_t launch_channel_mix(const void *x, const void *A, const void *bias, co
                               int I, int O, long P, int act, int dtype, hipStream_t s);
 hipError_t launch_projection(const void *x, const void *Q1, const void *q1, const void *Q2, const void *q2, void *y,
                              int B, int I, int J, int C, long P, int dtype, hipStream_t s);
+// first block's weights with the lift folded in (see pointwise.hip)
+hipError_t launch_lift_fold(const void *P, const void *p, const void *w, const void *Wb, const void *b, void *wf,
+                            void *af, void *bf, int K, int J, int C, int dtype, hipStream_t s);
 constexpr int kMixMaxIn = 128;   // channel mix: input channels
 constexpr int kProjMaxIn = 64;   // projection: input channels
 constexpr int kProjMaxHidden = 128;

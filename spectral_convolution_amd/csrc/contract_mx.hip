@@ -54,6 +54,12 @@ __device__ __forceinline__ v4f mma_bf(u32x4 a, u32x4 b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
 }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v4f mma_f16(u32x4 a, u32x4 b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
 // (re, im) fp32 -> packed bf16 pairs hi = (bf16(re), bf16(im)), lo = the
 // rounding remainders, each rounded to nearest even
 __device__ __forceinline__ void split_pair(float re, float im, uint32_t &hi, uint32_t &lo) {
@@ -61,28 +67,45 @@ __device__ __forceinline__ void split_pair(float re, float im, uint32_t &hi, uin
   lo = f32x2_to_bf16x2(re - __uint_as_float(hi << 16), im - __uint_as_float(hi & 0xffff0000u));
 }
 
-template <int DT, int MT, int MB>
+// DIRECT: fp16 weights and the half exchange multiply on fp16 matrix cores
+// as they are (no hi / lo parts): the spectra of one batch row are brought
+// to a common power-of-two scale, the row's smallest plane exponent, so one
+// product sums every input channel in one scale.
+template <int DT, int MT, int MB, bool HX>
 struct CmxShape {
+  static constexpr bool DIRECT = HX && DT == DT_F16;
   static constexpr int MW = MB / 4;                         // modes per wave
-  static constexpr int UX = MB / 2;                         // 16-byte units (two modes) per spectra / result row
+  static constexpr int UX = MB / 2;                         // units (two modes) per spectra / result row
   static constexpr int YO = 2 * MB + 4;                     // floats per output-channel row of the result stage (+ 4 pad)
   static constexpr int YB = kOT * YO + 4;                   // floats per batch row of the result stage
   static constexpr int BT = 16 * MT;                        // batch rows per workgroup
-  static constexpr int HL = DT == DT_F16 ? 2 : 1;          // weight parts
-  static constexpr int XU = MB * BT * kIC * 8 / (16 * kCT);   // 16-byte spectra units per thread and stage
+  static constexpr int XP = DIRECT ? 1 : 2;                 // spectra parts
+  static constexpr int HL = DT == DT_F16 && !DIRECT ? 2 : 1;  // weight parts
+  static constexpr int XU = MB * BT * kIC * 8 / (16 * kCT);   // spectra units (two modes) per thread and stage
   static constexpr int WU = MB * kIC * kOT * 4 / (16 * kCT);  // 16-byte weight units per thread and stage
   static constexpr int XB = BT * kSP;                        // halves of one (mode, part) block
-  static constexpr int XS = MB * 2 * XB;                    // halves of the spectra stage
+  static constexpr int XS = MB * XP * XB;                   // halves of the spectra stage
   static constexpr int WS = MB * HL * kOT * kSP;           // halves of the weight stage
+  static constexpr int LH = XS + WS > 32 * YB ? XS + WS : 32 * YB;  // halves before the row exponents (DIRECT)
 };
 
-// px[v]: two modes of one (b, i) row; fp32: (re, im, re, im) bits; HX: two
-// fp16 pairs and the row's exponent
+// one spectra unit in flight: two modes of one (b, i) row; complex fp32
+// (re, im, re, im) bits, or (HX) two fp16 pairs and the row's exponent
+template <bool HX>
+struct XReg {
+  u32x4 v;
+};
+template <>
+struct XReg<true> {
+  uint2 v;
+  int e;
+};
+
 template <int DT, int MT, int MB, bool HX>
 __device__ __forceinline__ void cmx_fetch(const ContractArgs &a, int st, int k0, int b0, int o0, int tid,
-                                          u32x4 (&px)[CmxShape<DT, MT, MB>::XU],
-                                          u32x4 (&pw)[CmxShape<DT, MT, MB>::WU]) {
-  using S = CmxShape<DT, MT, MB>;
+                                          XReg<HX> (&px)[CmxShape<DT, MT, MB, HX>::XU],
+                                          u32x4 (&pw)[CmxShape<DT, MT, MB, HX>::WU]) {
+  using S = CmxShape<DT, MT, MB, HX>;
   const int K = a.K, Ci = a.Ci, Co = a.Co, B = a.B;
 #pragma unroll
   for (int v = 0; v < S::XU; ++v) {
@@ -94,10 +117,11 @@ __device__ __forceinline__ void cmx_fetch(const ContractArgs &a, int st, int k0,
       const size_t r = ok ? (size_t)b * Ci + i : 0;
       const uint2 t = *reinterpret_cast<const uint2 *>(a.xh16 + (ok ? r * K + mode : 0));
       const int e = a.xexp[r];
-      px[v] = ok ? u32x4{t.x, t.y, (uint32_t)e, 0u} : u32x4{0u, 0u, 0u, 0u};
+      px[v].v = ok ? t : make_uint2(0u, 0u);
+      px[v].e = e;
     } else {
       const u32x4 t = *reinterpret_cast<const u32x4 *>(a.xh + (ok ? ((size_t)b * Ci + i) * K + mode : 0));
-      px[v] = ok ? t : u32x4{0u, 0u, 0u, 0u};
+      px[v].v = ok ? t : u32x4{0u, 0u, 0u, 0u};
     }
   }
 #pragma unroll
@@ -126,26 +150,43 @@ __device__ __forceinline__ int wcol(int i, int o) { return (i + ((o >> 4) & 1) *
 
 // split and transpose one stage into fragment rows:
 //   xs[mode][part][b][2 i + re/im], ws[mode][part][o][2 i + re/im]
+// sb: the batch rows' common exponents (DIRECT)
 template <int DT, int MT, int MB, bool HX>
-__device__ __forceinline__ void cmx_put(uint16_t *xs, uint16_t *ws, int tid, const u32x4 (&px)[CmxShape<DT, MT, MB>::XU],
-                                        const u32x4 (&pw)[CmxShape<DT, MT, MB>::WU]) {
-  using S = CmxShape<DT, MT, MB>;
+__device__ __forceinline__ void cmx_put(uint16_t *xs, uint16_t *ws, int tid,
+                                        const XReg<HX> (&px)[CmxShape<DT, MT, MB, HX>::XU],
+                                        const u32x4 (&pw)[CmxShape<DT, MT, MB, HX>::WU], const int *sb) {
+  using S = CmxShape<DT, MT, MB, HX>;
 #pragma unroll
   for (int v = 0; v < S::XU; ++v) {
     const int u = v * kCT + tid;
     const int row = u / S::UX, c = u % S::UX;
     const int b = row / kIC, i = row % kIC;
-    const float sc = HX ? pow2f(-(int)px[v][2]) : 1.f;
+    if constexpr (S::DIRECT) {
+      // to the row's common scale: times 2^(sb - e) <= 1, exact while the
+      // result stays a normal fp16
+      const float sc = pow2f(sb[b] - px[v].e);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t h = t ? px[v].v.y : px[v].v.x;
+        const float re = (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xffffu)) * sc;
+        const float im = (float)__builtin_bit_cast(_Float16, (uint16_t)(h >> 16)) * sc;
+        const int m = 2 * c + t;
+        reinterpret_cast<uint32_t *>(xs + m * S::XB + xrow<MT>(m, b) * kSP)[i] = f16x2_rne(re, im);
+      }
+      continue;
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       uint32_t hi, lo;
       if constexpr (HX) {
         // each half converted on its own (see the weight split below)
-        const float re = (float)__builtin_bit_cast(_Float16, (uint16_t)(px[v][t] & 0xffffu)) * sc;
-        const float im = (float)__builtin_bit_cast(_Float16, (uint16_t)(px[v][t] >> 16)) * sc;
+        const float sc = pow2f(-px[v].e);
+        const uint32_t h = t ? px[v].v.y : px[v].v.x;
+        const float re = (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xffffu)) * sc;
+        const float im = (float)__builtin_bit_cast(_Float16, (uint16_t)(h >> 16)) * sc;
         split_pair(re, im, hi, lo);
       } else {
-        split_pair(__uint_as_float(px[v][2 * t]), __uint_as_float(px[v][2 * t + 1]), hi, lo);
+        split_pair(__uint_as_float(px[v].v[2 * t]), __uint_as_float(px[v].v[2 * t + 1]), hi, lo);
       }
       const int m = 2 * c + t;
       reinterpret_cast<uint32_t *>(xs + (m * 2 + 0) * S::XB + xrow<MT>(m, b) * kSP)[i] = hi;
@@ -160,7 +201,9 @@ __device__ __forceinline__ void cmx_put(uint16_t *xs, uint16_t *ws, int tid, con
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int o = 4 * c + t;
-      if constexpr (DT == DT_F16) {
+      if constexpr (S::DIRECT) {
+        reinterpret_cast<uint32_t *>(ws + (m * kOT + o) * kSP)[wcol(i, o)] = pw[v][t];
+      } else if constexpr (DT == DT_F16) {
         // each half converted on its own: reading both lanes of a bit-cast
         // half2 vector here produced wrong values on gfx950
         const float re = (float)__builtin_bit_cast(_Float16, (uint16_t)(pw[v][t] & 0xffffu));
@@ -187,15 +230,15 @@ __device__ __forceinline__ u32x4 w_form(u32x4 raw, bool part1) {
 }
 
 // Waves per SIMD the register allocation targets: two for eight-mode
-// workgroups (the LDS allows two per CU), three (fp16 weights, split in two
-// parts) or four for four-mode ones.
-template <int DT, int MB>
-constexpr int cmx_waves() { return MB == 8 ? 2 : DT == DT_F16 ? 3 : 4; }
+// workgroups (the LDS allows two per CU with split operands), three (fp16
+// weights, split in two parts) or four for four-mode ones.
+template <int DT, int MB, bool HX>
+constexpr int cmx_waves() { return MB == 8 ? 2 : DT == DT_F16 && !HX ? 3 : 4; }
 
 template <int DT, int MT, int MB, bool HX>
-__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<DT, MB>()))) void fno_contract_mx(
+__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<DT, MB, HX>()))) void fno_contract_mx(
     ContractArgs a) {
-  using S = CmxShape<DT, MT, MB>;
+  using S = CmxShape<DT, MT, MB, HX>;
   extern __shared__ uint16_t sm[];
   uint16_t *xs = sm;
   uint16_t *ws = xs + S::XS;
@@ -217,6 +260,27 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<D
   const int nst = (a.Ci + kIC - 1) / kIC;
   const bool part1 = lane & 1;
 
+  // DIRECT: each batch row's common exponent, the smallest over its planes
+  // (the largest plane then fits fp16 and every other is scaled down)
+  int *sbl = reinterpret_cast<int *>(sm + S::LH);
+  if constexpr (S::DIRECT) {
+    int *part = reinterpret_cast<int *>(sm);  // [kCT / BT][BT] partial minima
+    constexpr int G = kCT / S::BT;
+    const int bl = tid % S::BT, grp = tid / S::BT, b = b0 + bl;
+    int e = 1 << 20;
+    if (b < B)
+      for (int i = grp; i < a.Ci; i += G) e = min(e, a.xexp[(size_t)b * a.Ci + i]);
+    part[grp * S::BT + bl] = e;
+    __syncthreads();
+    if (tid < S::BT) {
+      int m = part[tid];
+#pragma unroll
+      for (int g = 1; g < G; ++g) m = min(m, part[g * S::BT + tid]);
+      sbl[tid] = m < (1 << 20) ? m : 0;
+    }
+    __syncthreads();
+  }
+
   v4f acc[S::MW][MT][4];
 #pragma unroll
   for (int mm = 0; mm < S::MW; ++mm)
@@ -225,22 +289,23 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<D
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) acc[mm][mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 px[S::XU], pw[S::WU];
+  XReg<HX> px[S::XU];
+  u32x4 pw[S::WU];
   cmx_fetch<DT, MT, MB, HX>(a, 0, k0, b0, o0, tid, px, pw);
   for (int st = 0; st < nst; ++st) {
-    cmx_put<DT, MT, MB, HX>(xs, ws, tid, px, pw);
+    cmx_put<DT, MT, MB, HX>(xs, ws, tid, px, pw, sbl);
     if (st + 1 < nst) cmx_fetch<DT, MT, MB, HX>(a, st + 1, k0, b0, o0, tid, px, pw);
     __syncthreads();
 #pragma unroll
     for (int mm = 0; mm < S::MW; ++mm) {
       const int m = S::MW * wv + mm;
-      u32x4 af[MT][2];
+      u32x4 af[MT][S::XP];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
-          af[mt][p] = *reinterpret_cast<const u32x4 *>(xs + (m * 2 + p) * S::XB + xrow<MT>(m, mt * 16 + (lane & 15)) * kSP +
-                                                       8 * (lane >> 4));
+        for (int p = 0; p < S::XP; ++p)
+          af[mt][p] = *reinterpret_cast<const u32x4 *>(xs + (m * S::XP + p) * S::XB +
+                                                       xrow<MT>(m, mt * 16 + (lane & 15)) * kSP + 8 * (lane >> 4));
 #pragma unroll
       for (int nh = 0; nh < 2; ++nh) {  // two halves of the output tiles
         u32x4 bf[2][S::HL];
@@ -261,9 +326,13 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<D
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             v4f &c = acc[mm][mt][2 * nh + t];
-            c = mma_bf(af[mt][0], bf[t][0], c);
-            c = mma_bf(af[mt][1], bf[t][0], c);
-            if constexpr (S::HL == 2) c = mma_bf(af[mt][0], bf[t][1], c);
+            if constexpr (S::DIRECT) {
+              c = mma_f16(af[mt][0], bf[t][0], c);
+            } else {
+              c = mma_bf(af[mt][0], bf[t][0], c);
+              c = mma_bf(af[mt][S::XP - 1], bf[t][0], c);
+              if constexpr (S::HL == 2) c = mma_bf(af[mt][0], bf[t][1], c);
+            }
           }
       }
     }
@@ -308,8 +377,11 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<D
                                 fmaxf(fmaxf(fabsf(p1.x), fabsf(p1.y)), fmaxf(fabsf(p1.z), fabsf(p1.w))));
           int e = 0;
           if (m > 0.f) (void)frexpf(m, &e);  // m < 2^e
-          const int sx = m > 0.f ? max(-120, min(120, 14 - e)) : 0;
-          const float f = pow2f(sx);
+          // DIRECT: the accumulators hold the true values times 2^sb of the
+          // batch row; the stored pairs are the true values times 2^sx
+          const int rs = S::DIRECT ? sbl[mt * 16 + bl] : 0;
+          const int sx = m > 0.f ? max(-120, min(120, 14 - e + rs)) : 0;
+          const float f = pow2f(sx) * pow2f(-rs);
           uint32_t *dst = a.yh16 + ((size_t)b * Co + o) * K + mode;
           const uint2 h0 = make_uint2(f16x2_rne(p0.x * f, p0.y * f), f16x2_rne(p0.z * f, p0.w * f));
           *reinterpret_cast<uint2 *>(dst) = h0;
@@ -368,15 +440,19 @@ static const void *contract_mx_kernel(int dtype, int B, int mb, bool hx) {
   return nullptr;
 }
 
-static size_t contract_mx_lds_bytes(int dtype, int B, int mb) {
-  const int BT = B <= 16 ? 16 : 32, HL = dtype == DT_F16 ? 2 : 1;
-  const size_t stage = ((size_t)mb * 2 * BT * kSP + (size_t)mb * HL * kOT * kSP) * 2;
+static size_t contract_mx_lds_bytes(int dtype, int B, int mb, bool hx) {
+  const bool direct = hx && dtype == DT_F16;
+  const int BT = B <= 16 ? 16 : 32, XP = direct ? 1 : 2, HL = dtype == DT_F16 && !direct ? 2 : 1;
+  const size_t stage = ((size_t)mb * XP * BT * kSP + (size_t)mb * HL * kOT * kSP) * 2;
   const size_t out = (size_t)16 * (kOT * (2 * mb + 4) + 4) * 4;
-  return stage > out ? stage : out;
+  return std::max(std::max(stage, out), (size_t)kCT * 4) + (direct ? BT * 4 : 0);
 }
 
 size_t contract_mx_lds_bytes(int dtype, int B) {
-  return std::max(contract_mx_lds_bytes(dtype, B, 4), contract_mx_lds_bytes(dtype, B, 8));
+  size_t m = 0;
+  for (int mb : {4, 8})
+    for (bool hx : {false, true}) m = std::max(m, contract_mx_lds_bytes(dtype, B, mb, hx));
+  return m;
 }
 
 hipError_t contract_mx_prepare(int dtype, int B) {
@@ -384,7 +460,7 @@ hipError_t contract_mx_prepare(int dtype, int B) {
     for (bool hx : {false, true}) {
       const void *k = contract_mx_kernel(dtype, B, mb, hx);
       if (!k) return hipErrorInvalidValue;
-      const hipError_t e = raise_lds_cap(k, contract_mx_lds_bytes(dtype, B, mb));
+      const hipError_t e = raise_lds_cap(k, contract_mx_lds_bytes(dtype, B, mb, hx));
       if (e != hipSuccess) return e;
     }
   return hipSuccess;
@@ -400,7 +476,7 @@ hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s) {
   if (n > 0x7fffffffL) return hipErrorInvalidValue;
   dim3 grid((unsigned)n);
   void *args[] = {(void *)&a};
-  return hipLaunchKernel(k, grid, dim3(kCT), args, contract_mx_lds_bytes(dtype, a.B, mb), s);
+  return hipLaunchKernel(k, grid, dim3(kCT), args, contract_mx_lds_bytes(dtype, a.B, mb, a.xh16 != nullptr), s);
 }
 
 }  // namespace fno

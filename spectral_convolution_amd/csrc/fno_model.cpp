@@ -1,12 +1,20 @@
 // fno_model.cpp - the full FNO2d network on top of the spectral-conv plan and
 // the per-pixel kernels: lift -> n_layers x GELU(spectral + 1x1 + bias) ->
 // projection, every step in the library's HIP kernels, activations in the
-// storage dtype ping-ponging through three buffers the model owns.
+// storage dtype ping-ponging through buffers the model owns.
+//
+// The lift is folded into the first block (both are linear in the lifted
+// field): one small kernel composes the first block's spectral weights,
+// 1x1 weights and bias with the lift, and the first block then runs on the
+// raw feature channels, so the lifted field is never written or read. The
+// forward can be replayed from a HIP graph captured on the model's own
+// stream.
 
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 #include <new>
+#include <vector>
 
 #include "../../include/fno.h"
 #include "common.hpp"
@@ -16,9 +24,16 @@ using namespace fno;
 struct fno_model2d_s {
   int B = 0, H = 0, W = 0, in_ch = 0, ch = 0, layers = 0, m1 = 0, m2 = 0, proj = 0, out_ch = 0;
   int dtype = 0, device = 0;
-  fno_plan_t plan = nullptr;
+  fno_plan_t plan = nullptr;   // blocks 1.. (ch -> ch)
+  fno_plan_t plan0 = nullptr;  // block 0 on the features (in_ch -> ch), lift folded in
   void *mem = nullptr;
   void *act[3] = {nullptr, nullptr, nullptr};
+  void *wf = nullptr, *af = nullptr, *bf = nullptr;  // block 0's folded weights
+  // graph replay: the captured forward and the pointers it was captured for
+  bool graph = false;
+  hipStream_t cap = nullptr;
+  hipGraphExec_t exec = nullptr;
+  std::vector<const void *> key;
 };
 
 namespace {
@@ -82,13 +97,14 @@ fno_status_t fno_projection(const void *x, const void *Q1, const void *q1, const
 fno_status_t fno_model2d_destroy(fno_model2d_t m) {
   if (!m) return FNO_OK;
   fno_status_t st = fno_plan_destroy(m->plan);
-  if (m->mem) {
-    int prev = -1;
-    (void)hipGetDevice(&prev);
-    if (prev != m->device) (void)hipSetDevice(m->device);
-    if (hipFree(m->mem) != hipSuccess) st = FNO_ERR_DEVICE;
-    if (prev >= 0 && prev != m->device) (void)hipSetDevice(prev);
-  }
+  if (fno_plan_destroy(m->plan0) != FNO_OK) st = FNO_ERR_DEVICE;
+  int prev = -1;
+  (void)hipGetDevice(&prev);
+  if (prev != m->device) (void)hipSetDevice(m->device);
+  if (m->exec && hipGraphExecDestroy(m->exec) != hipSuccess) st = FNO_ERR_DEVICE;
+  if (m->cap && hipStreamDestroy(m->cap) != hipSuccess) st = FNO_ERR_DEVICE;
+  if (m->mem && hipFree(m->mem) != hipSuccess) st = FNO_ERR_DEVICE;
+  if (prev >= 0 && prev != m->device) (void)hipSetDevice(prev);
   delete m;
   return st;
 }
@@ -120,15 +136,22 @@ fno_status_t fno_model2d_create(fno_model2d_t *out, int batch, int height, int w
   m->device = device;
   const int grid[2] = {height, width}, modes[2] = {m1, m2};
   fno_status_t st = fno_plan_create(&m->plan, 2, batch, channels, channels, grid, modes, dtype, device);
+  if (st == FNO_OK && n_layers > 0)
+    st = fno_plan_create(&m->plan0, 2, batch, in_channels, channels, grid, modes, dtype, device);
   if (st != FNO_OK) {
-    delete m;
+    fno_model2d_destroy(m);
     return st;
   }
   int prev = -1;
   (void)hipGetDevice(&prev);
   if (prev != device) (void)hipSetDevice(device);
-  const size_t one = (((size_t)batch * channels * height * width * esize((int)dtype)) + 255) & ~(size_t)255;
-  hipError_t e = hipMalloc(&m->mem, 3 * one);
+  auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  const size_t es = esize((int)dtype);
+  const size_t one = al((size_t)batch * channels * height * width * es);
+  const size_t K = (size_t)2 * m1 * m2;
+  const size_t nwf = al(K * in_channels * channels * 2 * es), naf = al((size_t)channels * in_channels * es),
+               nbf = al((size_t)channels * es);
+  hipError_t e = hipMalloc(&m->mem, 3 * one + nwf + naf + nbf);
   if (prev >= 0 && prev != device) (void)hipSetDevice(prev);
   if (e != hipSuccess) {
     (void)hipGetLastError();
@@ -137,25 +160,37 @@ fno_status_t fno_model2d_create(fno_model2d_t *out, int batch, int height, int w
     return status_of(e);
   }
   for (int i = 0; i < 3; ++i) m->act[i] = (char *)m->mem + i * one;
+  m->wf = (char *)m->mem + 3 * one;
+  m->af = (char *)m->wf + nwf;
+  m->bf = (char *)m->af + naf;
   *out = m;
   return FNO_OK;
 }
 
-fno_status_t fno_model2d_forward(fno_model2d_t m, const void *features, const void *const *params, void *out,
-                                 void *stream) {
-  if (!m || !features || !params || !out) return FNO_ERR_INVALID_ARG;
-  const int np = 2 + 3 * m->layers + 4;
-  for (int i = 0; i < np; ++i)
-    if (!params[i]) return FNO_ERR_INVALID_ARG;
+// Queue the whole forward on `stream`.
+static fno_status_t enqueue_forward(fno_model2d_t m, const void *features, const void *const *params, void *out,
+                                    void *stream) {
   const long P = (long)m->H * m->W;
   const fno_dtype_t dt = (fno_dtype_t)m->dtype;
-  int prev = -1;
-  if (hipGetDevice(&prev) != hipSuccess) return FNO_ERR_DEVICE;
-  if (prev != m->device && hipSetDevice(m->device) != hipSuccess) return FNO_ERR_DEVICE;
-  fno_status_t st = fno_channel_mix(features, params[0], params[1], nullptr, m->act[0], m->B, m->in_ch, m->ch, P, 0,
-                                    dt, stream);
-  int cur = 0;
-  for (int l = 0; l < m->layers && st == FNO_OK; ++l) {
+  fno_status_t st = FNO_OK;
+  int cur = 0, l0 = 0;
+  if (m->layers > 0) {
+    // block 0 on the raw features with the lift folded in: v1 lands in act[1]
+    const void *const *lp = params + 2;
+    hipError_t e = launch_lift_fold(params[0], params[1], lp[0], lp[1], lp[2], m->wf, m->af, m->bf,
+                                    2 * m->m1 * m->m2, m->in_ch, m->ch, m->dtype, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipGetLastError();
+    st = status_of(e);
+    if (st == FNO_OK) st = fno_spectral_conv2d(m->plan0, features, m->wf, m->act[2], stream);
+    if (st == FNO_OK)
+      st = fno_channel_mix(features, m->af, m->bf, m->act[2], m->act[1], m->B, m->in_ch, m->ch, P, 1, dt, stream);
+    cur = 1;
+    l0 = 1;
+  } else {
+    st = fno_channel_mix(features, params[0], params[1], nullptr, m->act[0], m->B, m->in_ch, m->ch, P, 0, dt,
+                         stream);
+  }
+  for (int l = l0; l < m->layers && st == FNO_OK; ++l) {
     const void *const *lp = params + 2 + 3 * l;
     const int nxt = cur == 0 ? 1 : 0;
     st = fno_spectral_conv2d(m->plan, m->act[cur], lp[0], m->act[2], stream);
@@ -167,6 +202,60 @@ fno_status_t fno_model2d_forward(fno_model2d_t m, const void *features, const vo
     const void *const *pp = params + 2 + 3 * m->layers;
     st = fno_projection(m->act[cur], pp[0], pp[1], pp[2], pp[3], out, m->B, m->ch, m->proj, m->out_ch, P, dt,
                         stream);
+  }
+  return st;
+}
+
+// Capture the forward for these pointers into a graph on the model's stream
+// (replacing an earlier capture).
+static fno_status_t capture_forward(fno_model2d_t m, const void *features, const void *const *params, void *out) {
+  if (!m->cap && hipStreamCreateWithFlags(&m->cap, hipStreamNonBlocking) != hipSuccess) return FNO_ERR_DEVICE;
+  if (hipStreamBeginCapture(m->cap, hipStreamCaptureModeThreadLocal) != hipSuccess) return FNO_ERR_DEVICE;
+  const fno_status_t st = enqueue_forward(m, features, params, out, m->cap);
+  hipGraph_t g = nullptr;
+  const hipError_t e = hipStreamEndCapture(m->cap, &g);
+  if (st != FNO_OK || e != hipSuccess) {
+    if (g) (void)hipGraphDestroy(g);
+    (void)hipGetLastError();
+    return st != FNO_OK ? st : FNO_ERR_DEVICE;
+  }
+  hipGraphExec_t exec = nullptr;
+  const hipError_t ei = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (ei != hipSuccess) return FNO_ERR_DEVICE;
+  if (m->exec) (void)hipGraphExecDestroy(m->exec);
+  m->exec = exec;
+  return FNO_OK;
+}
+
+fno_status_t fno_model2d_set_graph(fno_model2d_t m, int on) {
+  if (!m || (on != 0 && on != 1)) return FNO_ERR_INVALID_ARG;
+  m->graph = on != 0;
+  return FNO_OK;
+}
+
+fno_status_t fno_model2d_forward(fno_model2d_t m, const void *features, const void *const *params, void *out,
+                                 void *stream) {
+  if (!m || !features || !params || !out) return FNO_ERR_INVALID_ARG;
+  const int np = 2 + 3 * m->layers + 4;
+  for (int i = 0; i < np; ++i)
+    if (!params[i]) return FNO_ERR_INVALID_ARG;
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) return FNO_ERR_DEVICE;
+  if (prev != m->device && hipSetDevice(m->device) != hipSuccess) return FNO_ERR_DEVICE;
+  fno_status_t st = FNO_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess) st = FNO_ERR_DEVICE;
+  if (st == FNO_OK && m->graph && cs == hipStreamCaptureStatusNone) {
+    std::vector<const void *> key{features, out};
+    key.insert(key.end(), params, params + np);
+    if (!m->exec || key != m->key) {
+      st = capture_forward(m, features, params, out);
+      m->key = st == FNO_OK ? key : std::vector<const void *>();
+    }
+    if (st == FNO_OK && hipGraphLaunch(m->exec, (hipStream_t)stream) != hipSuccess) st = FNO_ERR_DEVICE;
+  } else if (st == FNO_OK) {
+    st = enqueue_forward(m, features, params, out, stream);
   }
   if (prev != m->device) (void)hipSetDevice(prev);
   return st;

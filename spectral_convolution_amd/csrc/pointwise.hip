@@ -681,6 +681,79 @@ static int pw_blocks(long P) {
   return (int)(blocks < 4096 ? blocks : 4096);
 }
 
+// ------------------------------------------------ lift folded into block 0
+//
+// The lift v0 = P f + p (P [C][J], p [C], f the J feature channels) and the
+// first block are linear in v0, so the first block can run on f directly:
+//   spectral branch  Yh[b][o][k] = sum_j Xh_f[b][j][k] Wf[k][j][o]
+//                    + (k = DC) sum_c p[c] w[0][c][o],
+//     Wf[k][j][o] = sum_c P[c][j] w[k][c][o]  (the spectra of the constant
+//     field p[c] are p[c] at the DC mode only, which the inverse turns into
+//     the constant Re(sum_c p[c] w[0][c][o]) on every pixel);
+//   bypass           sum_c Wb[o][c] v0[c] + b[o] = sum_j Af[o][j] f[j] + bf[o],
+//     Af[o][j] = sum_c Wb[o][c] P[c][j],
+//     bf[o] = sum_c Wb[o][c] p[c] + b[o] + Re(sum_c p[c] w[0][c][o]).
+// One thread per output element, fp32 sums over c, rounded to the storage
+// dtype. v0 itself is never formed.
+struct FoldArgs {
+  const void *P, *p, *w, *Wb, *b;  // P [C][J], p [C], w [K][C][C][2], Wb [C][C], b [C]
+  void *wf, *af, *bf;              // wf [K][J][C][2], af [C][J], bf [C]
+  int K, J, C;
+};
+
+template <int DT>
+__device__ __forceinline__ void store1(void *p, size_t i, float v) {
+  if constexpr (DT == DT_F32) reinterpret_cast<float *>(p)[i] = v;
+  else if constexpr (DT == DT_F16) reinterpret_cast<_Float16 *>(p)[i] = (_Float16)v;
+  else reinterpret_cast<uint16_t *>(p)[i] = (uint16_t)f32_to_bf16(v);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kPwThreads) void fno_lift_fold(FoldArgs a) {
+  const int K = a.K, J = a.J, C = a.C;
+  const long nw = (long)K * J * C, total = nw + (long)C * J + C;
+  for (long t = (long)blockIdx.x * kPwThreads + threadIdx.x; t < total; t += (long)gridDim.x * kPwThreads) {
+    if (t < nw) {
+      const int o = (int)(t % C), j = (int)((t / C) % J);
+      const long k = t / ((long)C * J);
+      float re = 0.f, im = 0.f;
+      for (int c = 0; c < C; ++c) {
+        const float pc = load1<DT>(a.P, (size_t)c * J + j);
+        const float2 wv = load_pair<DT>(a.w, ((size_t)(k * C + c) * C + o) * 2);
+        re = fmaf(pc, wv.x, re);
+        im = fmaf(pc, wv.y, im);
+      }
+      store_pair<DT>(a.wf, (size_t)t * 2, re, im);
+    } else if (t < nw + (long)C * J) {
+      const int idx = (int)(t - nw), o = idx / J, j = idx - o * J;
+      float s = 0.f;
+      for (int c = 0; c < C; ++c) s = fmaf(load1<DT>(a.Wb, (size_t)o * C + c), load1<DT>(a.P, (size_t)c * J + j), s);
+      store1<DT>(a.af, idx, s);
+    } else {
+      const int o = (int)(t - nw - (long)C * J);
+      float s = load1<DT>(a.b, o);
+      for (int c = 0; c < C; ++c) {
+        const float pc = load1<DT>(a.p, c);
+        s = fmaf(load1<DT>(a.Wb, (size_t)o * C + c), pc, s);
+        s = fmaf(pc, load_pair<DT>(a.w, ((size_t)c * C + o) * 2).x, s);
+      }
+      store1<DT>(a.bf, o, s);
+    }
+  }
+}
+
+hipError_t launch_lift_fold(const void *P, const void *p, const void *w, const void *Wb, const void *b, void *wf,
+                            void *af, void *bf, int K, int J, int C, int dtype, hipStream_t s) {
+  FoldArgs a{P, p, w, Wb, b, wf, af, bf, K, J, C};
+  void *args[] = {(void *)&a};
+  const long total = (long)K * J * C + (long)C * J + C;
+  const unsigned g = (unsigned)std::min<long>((total + kPwThreads - 1) / kPwThreads, 4096);
+  const void *k = dtype == DT_F32 ? (const void *)fno_lift_fold<DT_F32>
+                  : dtype == DT_F16 ? (const void *)fno_lift_fold<DT_F16>
+                                    : (const void *)fno_lift_fold<DT_BF16>;
+  return hipLaunchKernel(k, dim3(g), dim3(kPwThreads), args, 0, s);
+}
+
 hipError_t launch_channel_mix(const void *x, const void *A, const void *bias, const void *add, void *y, int B,
                               int I, int O, long P, int act, int dtype, hipStream_t s) {
   MixArgs a{x, A, bias, add, y, B, I, O, P, act};
