@@ -693,8 +693,10 @@ static int pw_blocks(long P) {
 //   bypass           sum_c Wb[o][c] v0[c] + b[o] = sum_j Af[o][j] f[j] + bf[o],
 //     Af[o][j] = sum_c Wb[o][c] P[c][j],
 //     bf[o] = sum_c Wb[o][c] p[c] + b[o] + Re(sum_c p[c] w[0][c][o]).
-// One thread per output element, fp32 sums over c, rounded to the storage
-// dtype. v0 itself is never formed.
+// Threads take (k, o) pairs, consecutive o on consecutive lanes (the weight
+// rows w[k][c][0 .. C) are read coalesced, once for all J outputs of the
+// pair, in chunks of four j); the last C threads form Af and bf. fp32 sums
+// over c, rounded to the storage dtype. v0 itself is never formed.
 struct FoldArgs {
   const void *P, *p, *w, *Wb, *b;  // P [C][J], p [C], w [K][C][C][2], Wb [C][C], b [C]
   void *wf, *af, *bf;              // wf [K][J][C][2], af [C][J], bf [C]
@@ -711,26 +713,34 @@ __device__ __forceinline__ void store1(void *p, size_t i, float v) {
 template <int DT>
 __global__ __launch_bounds__(kPwThreads) void fno_lift_fold(FoldArgs a) {
   const int K = a.K, J = a.J, C = a.C;
-  const long nw = (long)K * J * C, total = nw + (long)C * J + C;
+  const long npair = (long)K * C, total = npair + C;
   for (long t = (long)blockIdx.x * kPwThreads + threadIdx.x; t < total; t += (long)gridDim.x * kPwThreads) {
-    if (t < nw) {
-      const int o = (int)(t % C), j = (int)((t / C) % J);
-      const long k = t / ((long)C * J);
-      float re = 0.f, im = 0.f;
-      for (int c = 0; c < C; ++c) {
-        const float pc = load1<DT>(a.P, (size_t)c * J + j);
-        const float2 wv = load_pair<DT>(a.w, ((size_t)(k * C + c) * C + o) * 2);
-        re = fmaf(pc, wv.x, re);
-        im = fmaf(pc, wv.y, im);
+    if (t < npair) {
+      const int o = (int)(t % C);
+      const long k = t / C;
+      for (int j0 = 0; j0 < J; j0 += 4) {
+        float re[4] = {0.f, 0.f, 0.f, 0.f}, im[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < C; ++c) {
+          const float2 wv = load_pair<DT>(a.w, ((size_t)(k * C + c) * C + o) * 2);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float pc = j0 + q < J ? load1<DT>(a.P, (size_t)c * J + j0 + q) : 0.f;
+            re[q] = fmaf(pc, wv.x, re[q]);
+            im[q] = fmaf(pc, wv.y, im[q]);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (j0 + q < J) store_pair<DT>(a.wf, (((size_t)k * J + j0 + q) * C + o) * 2, re[q], im[q]);
       }
-      store_pair<DT>(a.wf, (size_t)t * 2, re, im);
-    } else if (t < nw + (long)C * J) {
-      const int idx = (int)(t - nw), o = idx / J, j = idx - o * J;
-      float s = 0.f;
-      for (int c = 0; c < C; ++c) s = fmaf(load1<DT>(a.Wb, (size_t)o * C + c), load1<DT>(a.P, (size_t)c * J + j), s);
-      store1<DT>(a.af, idx, s);
     } else {
-      const int o = (int)(t - nw - (long)C * J);
+      // output channel o: row o of Af and bf[o]
+      const int o = (int)(t - npair);
+      for (int j = 0; j < J; ++j) {
+        float s = 0.f;
+        for (int c = 0; c < C; ++c) s = fmaf(load1<DT>(a.Wb, (size_t)o * C + c), load1<DT>(a.P, (size_t)c * J + j), s);
+        store1<DT>(a.af, (size_t)o * J + j, s);
+      }
       float s = load1<DT>(a.b, o);
       for (int c = 0; c < C; ++c) {
         const float pc = load1<DT>(a.p, c);
@@ -746,7 +756,7 @@ hipError_t launch_lift_fold(const void *P, const void *p, const void *w, const v
                             void *af, void *bf, int K, int J, int C, int dtype, hipStream_t s) {
   FoldArgs a{P, p, w, Wb, b, wf, af, bf, K, J, C};
   void *args[] = {(void *)&a};
-  const long total = (long)K * J * C + (long)C * J + C;
+  const long total = (long)K * C + C;
   const unsigned g = (unsigned)std::min<long>((total + kPwThreads - 1) / kPwThreads, 4096);
   const void *k = dtype == DT_F32 ? (const void *)fno_lift_fold<DT_F32>
                   : dtype == DT_F16 ? (const void *)fno_lift_fold<DT_F16>
