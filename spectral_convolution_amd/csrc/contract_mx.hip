@@ -42,7 +42,7 @@ typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 constexpr int kCT = 256;  // threads per workgroup (4 waves, MB / 4 modes each)
 constexpr int kIC = 16;   // input channels per stage (one 32-deep block of K)
 constexpr int kOT = 32;   // output channels per workgroup (four 16-column tiles of N)
-constexpr int kSP = 40;   // halves per staged fragment row (32 + 8 pad: conflict-free reads)
+constexpr int kSP = 48;   // halves per staged fragment row (32 + 16 pad: 6 units, conflict-free fragment reads)
 
 // two fp32 -> packed fp16 pair (a in the low half), round to nearest even
 __device__ __forceinline__ uint32_t f16x2_rne(float a, float b) {
@@ -89,6 +89,27 @@ struct CmxShape {
   static constexpr int LH = XS + WS > 32 * YB ? XS + WS : 32 * YB;  // halves before the row exponents (DIRECT)
 };
 
+// Row of batch row b in the spectra block of mode m: rotated by one row per
+// mode pair, so that the four mode pairs one store instruction touches
+// start 24, 16 or 8 banks apart (rows of 24 words).
+template <int MT>
+__device__ __forceinline__ int xrow(int m, int b) { return (b + (m >> 1)) & (16 * MT - 1); }
+
+// Row of output channel o in a mode's weight block: the two low bits of o
+// and the next two swap places, so that the four output groups (4 c + t for
+// c = 0 .. 3) one store instruction touches land 24 words apart mod 32
+// (rows of 24 words, 4 rows apart would share banks).
+__device__ __forceinline__ int wrow(int o) { return 4 * (o & 3) + ((o >> 2) & 3) + (o & ~15); }
+
+// Weight unit u of a stage: mode m, input channel i, outputs 4 c .. 4 c + 3
+// (c: two bits from u, one from bit 6), so that four lanes read 64 bytes of
+// one (mode, i) row and 32 lanes store 8 channels of 4 output groups.
+__device__ __forceinline__ void wunit(int u, int &m, int &i, int &c) {
+  c = (u & 3) + 4 * ((u >> 6) & 1);
+  i = (u >> 2) & (kIC - 1);
+  m = u >> 7;
+}
+
 // one spectra unit in flight: two modes of one (b, i) row; complex fp32
 // (re, im, re, im) bits, or (HX) two fp16 pairs and the row's exponent
 template <bool HX>
@@ -126,27 +147,15 @@ __device__ __forceinline__ void cmx_fetch(const ContractArgs &a, int st, int k0,
   }
 #pragma unroll
   for (int v = 0; v < S::WU; ++v) {
-    const int u = v * kCT + tid;
-    const int row = u >> 3, c = u & 7;  // row = (mode, i), i fastest; c: outputs 4c .. 4c + 3
-    const int mode = k0 + row / kIC, i = st * kIC + row % kIC, o = o0 + 4 * c;
+    int m, il, c;
+    wunit(v * kCT + tid, m, il, c);
+    const int mode = k0 + m, i = st * kIC + il, o = o0 + 4 * c;
     const bool ok = mode < K && i < Ci && o < Co;
     const u32x4 t = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.w) +
                                                      (ok ? (((size_t)mode * Ci + i) * Co + o) * 2 : 0));
     pw[v] = ok ? t : u32x4{0u, 0u, 0u, 0u};
   }
 }
-
-// Row of batch row b in the spectra block of mode m: rotated by 4 rows per
-// mode pair, so that the four mode pairs one store instruction touches
-// start 16 banks apart (4 rows of 20 words).
-template <int MT>
-__device__ __forceinline__ int xrow(int m, int b) { return (b + 4 * (m >> 1)) & (16 * MT - 1); }
-
-// Column of input channel i in weight row o: rows of output channels 16 ..
-// 31 are rotated by 8 columns (two whole 16-byte fragment chunks), so that
-// the eight output groups one store instruction touches fall on distinct
-// banks.
-__device__ __forceinline__ int wcol(int i, int o) { return (i + ((o >> 4) & 1) * 8) & (kIC - 1); }
 
 // split and transpose one stage into fragment rows:
 //   xs[mode][part][b][2 i + re/im], ws[mode][part][o][2 i + re/im]
@@ -195,14 +204,13 @@ __device__ __forceinline__ void cmx_put(uint16_t *xs, uint16_t *ws, int tid,
   }
 #pragma unroll
   for (int v = 0; v < S::WU; ++v) {
-    const int u = v * kCT + tid;
-    const int row = u >> 3, c = u & 7;
-    const int m = row / kIC, i = row % kIC;
+    int m, i, c;
+    wunit(v * kCT + tid, m, i, c);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int o = 4 * c + t;
+      const int o = wrow(4 * c + t);
       if constexpr (S::DIRECT) {
-        reinterpret_cast<uint32_t *>(ws + (m * kOT + o) * kSP)[wcol(i, o)] = pw[v][t];
+        reinterpret_cast<uint32_t *>(ws + (m * kOT + o) * kSP)[i] = pw[v][t];
       } else if constexpr (DT == DT_F16) {
         // each half converted on its own: reading both lanes of a bit-cast
         // half2 vector here produced wrong values on gfx950
@@ -210,10 +218,10 @@ __device__ __forceinline__ void cmx_put(uint16_t *xs, uint16_t *ws, int tid,
         const float im = (float)__builtin_bit_cast(_Float16, (uint16_t)(pw[v][t] >> 16));
         uint32_t hi, lo;
         split_pair(re, im, hi, lo);
-        reinterpret_cast<uint32_t *>(ws + ((m * 2 + 0) * kOT + o) * kSP)[wcol(i, o)] = hi;
-        reinterpret_cast<uint32_t *>(ws + ((m * 2 + 1) * kOT + o) * kSP)[wcol(i, o)] = lo;
+        reinterpret_cast<uint32_t *>(ws + ((m * 2 + 0) * kOT + o) * kSP)[i] = hi;
+        reinterpret_cast<uint32_t *>(ws + ((m * 2 + 1) * kOT + o) * kSP)[i] = lo;
       } else {
-        reinterpret_cast<uint32_t *>(ws + (m * kOT + o) * kSP)[wcol(i, o)] = pw[v][t];
+        reinterpret_cast<uint32_t *>(ws + (m * kOT + o) * kSP)[i] = pw[v][t];
       }
     }
   }
@@ -260,17 +268,31 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<D
   const int nst = (a.Ci + kIC - 1) / kIC;
   const bool part1 = lane & 1;
 
+  // Stage 0 is requested first, so that its latency overlaps the exponent
+  // minimum below.
+  XReg<HX> px[S::XU];
+  u32x4 pw[S::WU];
+  cmx_fetch<DT, MT, MB, HX>(a, 0, k0, b0, o0, tid, px, pw);
+
   // DIRECT: each batch row's common exponent, the smallest over its planes
-  // (the largest plane then fits fp16 and every other is scaled down)
+  // (the largest plane then fits fp16 and every other is scaled down); the
+  // exponents are read eight at a time, clamped in range, so that their loads
+  // are in flight together
   int *sbl = reinterpret_cast<int *>(sm + S::LH);
   if constexpr (S::DIRECT) {
     int *part = reinterpret_cast<int *>(sm);  // [kCT / BT][BT] partial minima
     constexpr int G = kCT / S::BT;
     const int bl = tid % S::BT, grp = tid / S::BT, b = b0 + bl;
+    const int *xe = a.xexp + (size_t)min(b, B - 1) * a.Ci;
     int e = 1 << 20;
-    if (b < B)
-      for (int i = grp; i < a.Ci; i += G) e = min(e, a.xexp[(size_t)b * a.Ci + i]);
-    part[grp * S::BT + bl] = e;
+    for (int i0 = grp; i0 < a.Ci; i0 += 8 * G) {
+      int t[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t[j] = xe[min(i0 + j * G, a.Ci - 1)];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e = i0 + j * G < a.Ci ? min(e, t[j]) : e;
+    }
+    part[grp * S::BT + bl] = b < B ? e : (1 << 20);
     __syncthreads();
     if (tid < S::BT) {
       int m = part[tid];
@@ -289,9 +311,6 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<D
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) acc[mm][mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  XReg<HX> px[S::XU];
-  u32x4 pw[S::WU];
-  cmx_fetch<DT, MT, MB, HX>(a, 0, k0, b0, o0, tid, px, pw);
   for (int st = 0; st < nst; ++st) {
     cmx_put<DT, MT, MB, HX>(xs, ws, tid, px, pw, sbl);
     if (st + 1 < nst) cmx_fetch<DT, MT, MB, HX>(a, st + 1, k0, b0, o0, tid, px, pw);
@@ -314,8 +333,7 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<D
 #pragma unroll
           for (int p = 0; p < S::HL; ++p)
             bf[t][p] = *reinterpret_cast<const u32x4 *>(
-                ws + ((m * S::HL + p) * kOT + (2 * nh + t) * 8 + ((lane & 15) >> 1)) * kSP +
-              2 * wcol(4 * (lane >> 4), 16 * nh));
+                ws + ((m * S::HL + p) * kOT + wrow((2 * nh + t) * 8 + ((lane & 15) >> 1))) * kSP + 8 * (lane >> 4));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < 2; ++t)

@@ -11,10 +11,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   fwd_mx_run<DT, KB, CPW, NW, TW>(a, blockIdx.x, gridDim.x, lds);
 }
 
-template <int DT, int KB, bool SM>
+template <int DT, int KB, bool SM, bool HX>
 __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(SM ? 3 : 2))) void fno_inv_plane_mx(PlaneMxInvArgs a) {
   extern __shared__ u32x4 lds[];
-  inv_mx_run<DT, KB, SM>(a, blockIdx.x, gridDim.x, lds);
+  inv_mx_run<DT, KB, SM, HX>(a, blockIdx.x, gridDim.x, lds);
 }
 
 // --------------------------------------------------------------- launchers
@@ -30,7 +30,7 @@ int mx_ntiles(int m2) { return m2 <= 8 ? 1 : m2 <= 16 ? 2 : 4; }
 
 size_t mx_fwd_lds_bytes(int H, int W, int dtype) {
   const size_t np = dtype == DT_F32 ? 2 : 1;
-  return 2 * np * kRows * (W / 8 + 1) * 16 + 2 * np * 32 * kRBP * 2 + (size_t)H * 8 + 16 * 4;
+  return 2 * np * kRows * (W / 8 + 2) * 16 + 2 * np * 32 * kRBP * 2 + (size_t)H * 8 + 16 * 4;
 }
 
 static bool inv_small(int m1, int m2) { return m1 <= 16 && m2 <= 16; }
@@ -70,38 +70,51 @@ static const void *mx_fwd_kernel(FwdCfg c) {
   else return c.cpw == 2 ? (const void *)fno_fwd_plane_mx<DT, KB, 2, 4, TW> : (const void *)fno_fwd_plane_mx<DT, KB, 1, 4, TW>;
 }
 
+template <int DT, int KB, bool HX>
+static const void *mx_inv_kernel(bool small) {
+  return small ? (const void *)fno_inv_plane_mx<DT, KB, true, HX> : (const void *)fno_inv_plane_mx<DT, KB, false, HX>;
+}
+
+// half: the inverse kernel that reads the half exchange (fp16 / bf16 only)
 template <int DT, int KB>
-static const void *mx_kernel_kb(bool fwd, FwdCfg c, bool small, bool two) {
-  if (!fwd) return small ? (const void *)fno_inv_plane_mx<DT, KB, true> : (const void *)fno_inv_plane_mx<DT, KB, false>;
+static const void *mx_kernel_kb(bool fwd, FwdCfg c, bool small, bool two, bool half) {
+  if (!fwd) {
+    if constexpr (DT == DT_F32) return half ? nullptr : mx_inv_kernel<DT, KB, false>(small);
+    else return half ? mx_inv_kernel<DT, KB, true>(small) : mx_inv_kernel<DT, KB, false>(small);
+  }
   return two ? mx_fwd_kernel<DT, KB, true>(c) : mx_fwd_kernel<DT, KB, false>(c);
 }
 
 template <int DT>
-static const void *mx_kernel_dt(bool fwd, int W, FwdCfg c, bool small, bool two) {
+static const void *mx_kernel_dt(bool fwd, int W, FwdCfg c, bool small, bool two, bool half) {
   switch (W) {
-    case 64: return mx_kernel_kb<DT, 2>(fwd, c, small, two);
-    case 128: return mx_kernel_kb<DT, 4>(fwd, c, small, two);
+    case 64: return mx_kernel_kb<DT, 2>(fwd, c, small, two, half);
+    case 128: return mx_kernel_kb<DT, 4>(fwd, c, small, two, half);
     case 256:
       if constexpr (DT == DT_F32) return nullptr;
-      else return mx_kernel_kb<DT, 8>(fwd, c, small, two);
+      else return mx_kernel_kb<DT, 8>(fwd, c, small, two, half);
   }
   return nullptr;
 }
 
-// two: the forward kernel that takes two plane sets (fwd only)
-static const void *mx_kernel(bool fwd, int W, int m1, int m2, int dtype, bool two = false) {
+// two: the forward kernel that takes two plane sets (fwd only); half: the
+// inverse kernel that reads the half exchange (inverse only)
+static const void *mx_kernel(bool fwd, int W, int m1, int m2, int dtype, bool two = false, bool half = false) {
   const FwdCfg c = fwd_cfg(W, m1, m2, dtype);
   const bool small = inv_small(m1, m2);
-  if (dtype == DT_F16) return mx_kernel_dt<DT_F16>(fwd, W, c, small, two);
-  if (dtype == DT_BF16) return mx_kernel_dt<DT_BF16>(fwd, W, c, small, two);
-  if (dtype == DT_F32) return mx_kernel_dt<DT_F32>(fwd, W, c, small, two);
+  if (dtype == DT_F16) return mx_kernel_dt<DT_F16>(fwd, W, c, small, two, half);
+  if (dtype == DT_BF16) return mx_kernel_dt<DT_BF16>(fwd, W, c, small, two, half);
+  if (dtype == DT_F32) return mx_kernel_dt<DT_F32>(fwd, W, c, small, two, half);
   return nullptr;
 }
 
 hipError_t mx_prepare(bool fwd, int W, int m1, int m2, int dtype, size_t lds, bool two) {
   const void *k = mx_kernel(fwd, W, m1, m2, dtype, two);
   if (!k) return hipErrorInvalidValue;
-  return raise_lds_cap(k, lds);
+  hipError_t e = raise_lds_cap(k, lds);
+  // the half-exchange inverse shares the LDS size of the fp32-exchange one
+  if (e == hipSuccess && !fwd && dtype != DT_F32) e = raise_lds_cap(mx_kernel(false, W, m1, m2, dtype, false, true), lds);
+  return e;
 }
 
 // workgroups of a persistent plane kernel: as many as are resident at once
@@ -113,6 +126,12 @@ hipError_t mx_grid(bool fwd, int W, int m1, int m2, int dtype, size_t lds, int d
   int per_cu = 0, ncu = 0;
   const int threads = fwd ? fwd_cfg(W, m1, m2, dtype).nw * 64 : kFT;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, threads, lds);
+  if (e == hipSuccess && !fwd && dtype != DT_F32) {  // the half-exchange variant too: the smaller of the two
+    int per_cu_h = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_h, mx_kernel(false, W, m1, m2, dtype, false, true),
+                                                     threads, lds);
+    per_cu = per_cu_h < per_cu ? per_cu_h : per_cu;
+  }
   if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, device);
   if (e != hipSuccess) return e;
   long g = (long)(per_cu > 0 ? per_cu : 1) * (ncu > 0 ? ncu : 1);
@@ -128,7 +147,7 @@ hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int grid, int dtype, siz
 }
 
 hipError_t launch_plane_mx_inv(const PlaneMxInvArgs &a, int grid, int dtype, size_t lds, hipStream_t s) {
-  const void *k = mx_kernel(false, a.W, a.m1, a.m2, dtype);
+  const void *k = mx_kernel(false, a.W, a.m1, a.m2, dtype, false, a.in16 != nullptr);
   if (!k || grid < 1) return hipErrorInvalidValue;
   void *args[] = {(void *)&a};
   return hipLaunchKernel(k, dim3(grid), dim3(kFT), args, lds, s);

@@ -53,8 +53,15 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
 constexpr int kRows = 64;  // rows per round
 constexpr int kMaxH = 256; // largest plane height
-constexpr int kRBP = 136;  // halves per row of a B-operand round buffer (128 + pad)
-constexpr int kZBP = 72;   // halves per row of the inverse Z buffer (64 + pad)
+
+// LDS row pitches. Measured on gfx950 (bank-conflict counter over single
+// access patterns): a 16-byte fragment read (lane l: row l % 16, unit l / 16)
+// is conflict-free when the row pitch is 2 mod 4 sixteen-byte units and takes
+// two or more passes for odd pitches or multiples of 4; a 32-bit store whose
+// 16-lane row blocks are 2 rows apart is conflict-free when 2 rows are 16 mod
+// 32 words. 4-byte stores go 32 lanes to a pass over 32 banks, 8-byte stores
+// 16 lanes, 16-byte stores 8 lanes.
+constexpr int kRBP = 144;  // halves per row of the forward R buffer (128 + pad): 18 units, 2 rows = 144 words
 
 __device__ __forceinline__ v4f mma(u32x4 a, u32x4 b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0, 0);
@@ -227,7 +234,7 @@ struct FwdRegs {
 template <int DT, int KB>
 struct FwdLds {
   static constexpr int NP = MxPol<DT>::NP;
-  static constexpr int PITCH = 4 * KB + 1;       // staged row: W halves + pad, in 16-byte units
+  static constexpr int PITCH = 4 * KB + 2;       // staged row: W halves + pad, in 16-byte units (2 mod 4)
   static constexpr int STG = kRows * PITCH;      // units per stage part
   static constexpr int RBS = 32 * kRBP;          // halves per R part
   u32x4 *stage;   // [2][NP][64][PITCH]
@@ -626,29 +633,51 @@ __device__ __forceinline__ void fwd_mx_run(const PlaneMxFwdArgs &a, int bid, int
 // ------------------------------------------------------------------ inverse
 
 // Inverse sizes: up to 32 kx per corner and 32 ky, or (SM) up to 16 of each.
-// The spectra buffer holds YR ky rows of 2 (2 m1) halves plus 8 of padding,
-// Z 64 rows of 2 m2 halves plus 8: pitches of 36 or 20 words (and 68 for
-// the large spectra rows), which keep the 16-row fragment reads on
-// distinct banks.
+// The spectra buffer holds YR ky rows of 2 (2 m1) halves plus 16 of padding
+// (pitch 18 or 10 units), Z 64 rows of 2 m2 halves plus 16 (pitch 10 or 6
+// units, and 2 rows apart 80 or 48 words): the fragment reads and the Z
+// stores are conflict-free.
 template <bool SM>
 struct InvGeom {
   static constexpr int NY = SM ? 2 : 8;         // spectra values per thread (K <= 512 or 2048)
   static constexpr int KBM = SM ? 2 : 4;        // k-blocks of E' Y
   static constexpr int NNM = SM ? 1 : 2;        // ky tiles
   static constexpr int YR = SM ? 16 : 32;       // ky rows of the spectra buffer
-  static constexpr int YP = SM ? 72 : kRBP;     // halves per spectra row
-  static constexpr int ZP = SM ? 40 : kZBP;     // halves per Z row
+  static constexpr int YP = SM ? 80 : 144;      // halves per spectra row
+  static constexpr int ZP = SM ? 48 : 80;       // halves per Z row
 };
 
-// spectra of one plane into registers: value tid + 256 i, zero past K
+// The spectra of a plane are dealt to the 256 threads in tiles of 8 kx rows
+// (q) by 4 ky, ky tiles fastest (2^lgk of them: ceil(m2 / 4) rounded up to a
+// power of two): value i of thread t is in tile t / 32 + 8 i, at row
+// (t / 4) % 8 and ky t % 4 of it. So the 32 lanes of one store into the
+// [ky][q] spectra buffer cover 8 consecutive q of 4 rows, on 32 distinct
+// banks (with the whole plane in one thread-column, 32 lanes wrote one q of
+// 32 rows: four or eight to a bank), and a global load still reads runs of
+// consecutive modes. 8 NY tiles hold every mode: 2 m1 / 8 <= 8 (4 for SM)
+// row tiles of at most 8 (4) ky tiles.
+struct InvMap {
+  int m1, m2, lgk;
+};
+
+// mode index (q m2 + ky) of value i of thread tid, or -1 for tile padding
+__device__ __forceinline__ int inv_mode(const InvMap &mp, int i, int tid, int &q, int &ky) {
+  const int tile = (tid >> 5) + 8 * i;
+  q = 8 * (tile >> mp.lgk) + ((tid >> 2) & 7);
+  ky = 4 * (tile & ((1 << mp.lgk) - 1)) + (tid & 3);
+  return q < 2 * mp.m1 && ky < mp.m2 ? q * mp.m2 + ky : -1;
+}
+
+// spectra of one plane into registers (zero for tile padding)
 template <int NY>
-__device__ __forceinline__ void inv_load(const float2 *in, size_t plane, int K, int tid, float2 (&yv)[NY]) {
-  const float2 *ip = in + plane * K;
+__device__ __forceinline__ void inv_load(const float2 *in, size_t plane, const InvMap &mp, int tid, float2 (&yv)[NY]) {
+  const float2 *ip = in + plane * (size_t)(2 * mp.m1 * mp.m2);
 #pragma unroll
   for (int i = 0; i < NY; ++i) {
-    const int v = tid + i * kFT;
-    const float2 t = ip[min(v, K - 1)];
-    yv[i] = v < K ? t : make_float2(0.f, 0.f);
+    int q, ky;
+    const int k = inv_mode(mp, i, tid, q, ky);
+    const float2 t = ip[max(k, 0)];
+    yv[i] = k >= 0 ? t : make_float2(0.f, 0.f);
   }
 }
 
@@ -656,20 +685,22 @@ __device__ __forceinline__ void inv_load(const float2 *in, size_t plane, int K, 
 // of four modes, kept raw (decoded by inv_decode once they are needed, so the
 // loads stay in flight)
 template <int NY>
-__device__ __forceinline__ void inv_load16(const uint32_t *in, const signed char *ex, size_t plane, int K, int tid,
-                                           uint32_t (&hv)[NY], int (&ev)[NY]) {
+__device__ __forceinline__ void inv_load16(const uint32_t *in, const signed char *ex, size_t plane, const InvMap &mp,
+                                           int tid, uint32_t (&hv)[NY], int (&ev)[NY]) {
+  const int K = 2 * mp.m1 * mp.m2;
   const uint32_t *ip = in + plane * K;
   const signed char *ep = ex + plane * ((K + 3) >> 2);
 #pragma unroll
   for (int i = 0; i < NY; ++i) {
-    const int v = min(tid + i * kFT, K - 1);
-    hv[i] = ip[v];
-    ev[i] = ep[v >> 2];
+    int q, ky;
+    const int k = max(inv_mode(mp, i, tid, q, ky), 0);
+    hv[i] = ip[k];
+    ev[i] = ep[k >> 2];
   }
 }
 
 template <int NY>
-__device__ __forceinline__ void inv_decode(int K, int tid, const uint32_t (&hv)[NY], const int (&ev)[NY],
+__device__ __forceinline__ void inv_decode(const InvMap &mp, int tid, const uint32_t (&hv)[NY], const int (&ev)[NY],
                                            float2 (&yv)[NY]) {
 #pragma unroll
   for (int i = 0; i < NY; ++i) {
@@ -677,7 +708,8 @@ __device__ __forceinline__ void inv_decode(int K, int tid, const uint32_t (&hv)[
     const float sc = pow2f(-ev[i]);
     const float re = (float)__builtin_bit_cast(_Float16, (uint16_t)(hv[i] & 0xffffu)) * sc;
     const float im = (float)__builtin_bit_cast(_Float16, (uint16_t)(hv[i] >> 16)) * sc;
-    yv[i] = tid + i * kFT < K ? make_float2(re, im) : make_float2(0.f, 0.f);
+    int q, ky;
+    yv[i] = inv_mode(mp, i, tid, q, ky) >= 0 ? make_float2(re, im) : make_float2(0.f, 0.f);
   }
 }
 
@@ -693,8 +725,10 @@ __device__ __forceinline__ void inv_decode(int K, int tid, const uint32_t (&hv)[
 // fp32 planes carry the spectra, Z and the twiddles as fp16 hi + lo.
 // SM: at most 16 kx per corner and 16 ky, so the spectra, Z and the
 // fragment registers take their smaller sizes (fewer registers and LDS,
-// more workgroups per CU).
-template <int DT, int KB, bool SM>
+// more workgroups per CU). HX: the spectra come as the half exchange (fp16
+// pairs with exponents), compiled separately so that each form keeps only
+// its own registers.
+template <int DT, int KB, bool SM, bool HX = false>
 __device__ __forceinline__ void inv_mx_run(const PlaneMxInvArgs &a, int bid, int nblk, u32x4 *lds) {
   using P = MxPol<DT>;
   using G = InvGeom<SM>;
@@ -711,8 +745,8 @@ __device__ __forceinline__ void inv_mx_run(const PlaneMxInvArgs &a, int bid, int
   constexpr int YBS = G::YR * YP, ZBS = kRows * ZP;  // halves per part
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, m1 = a.m1, m2 = a.m2, NN = a.nn, KB1 = a.kb1;
-  const int K = 2 * m1 * m2;
-  const int nmine = (a.nplanes - bid + nblk - 1) / nblk;
+  const int nk = (m2 + 3) >> 2;  // ky tiles of the spectra mapping
+  const InvMap mp{m1, m2, nk <= 1 ? 0 : nk <= 2 ? 1 : nk <= 4 ? 2 : 3};
   u32x4 *ostage = lds;                                                      // [64][OP]
   uint16_t *yb = reinterpret_cast<uint16_t *>(ostage + kRows * OP);         // [NP][YR][YP]
   uint16_t *zb = yb + NP * YBS;                                             // [NP][64][ZP]
@@ -722,13 +756,14 @@ __device__ __forceinline__ void inv_mx_run(const PlaneMxInvArgs &a, int bid, int
   float2 yv[NY], yn[NY];
   uint32_t hn[NY];
   int en[NY];
-  const bool half = a.in16 != nullptr;
-  if (nmine > 0) {
-    if (half) {
-      inv_load16<NY>(a.in16, a.iexp, bid, K, tid, hn, en);
-      inv_decode<NY>(K, tid, hn, en, yv);
+  constexpr bool half = HX;
+  int cur = bid;  // < nplanes: the grid is never larger
+  if (cur < a.nplanes) {
+    if constexpr (half) {
+      inv_load16<NY>(a.in16, a.iexp, bid, mp, tid, hn, en);
+      inv_decode<NY>(mp, tid, hn, en, yv);
     } else {
-      inv_load<NY>(a.in, bid, K, tid, yv);
+      inv_load<NY>(a.in, bid, mp, tid, yv);
     }
   }
   for (int v = tid; v < NP * YBS / 2; v += kFT) reinterpret_cast<uint32_t *>(yb)[v] = 0u;
@@ -758,8 +793,9 @@ __device__ __forceinline__ void inv_mx_run(const PlaneMxInvArgs &a, int bid, int
       }
 
   const int rounds = H / kRows;
-  for (int pi = 0; pi < nmine; ++pi) {
-    const size_t plane = (size_t)bid + (size_t)pi * nblk;
+  for (int pi = 0; cur < a.nplanes; ++pi) {
+    const size_t plane = (size_t)cur;
+    const int nxt = cur + nblk;
     float mloc = 0.f;
 #pragma unroll
     for (int i = 0; i < NY; ++i) mloc = fmaxf(mloc, fmaxf(fabsf(yv[i].x), fabsf(yv[i].y)));
@@ -781,9 +817,8 @@ __device__ __forceinline__ void inv_mx_run(const PlaneMxInvArgs &a, int bid, int
       // 1. spectra of the round: Y[q][ky] e^{+2 pi i kx(q) h0 / H}, scaled, fp16
 #pragma unroll
       for (int i = 0; i < NY; ++i) {
-        const int v = tid + i * kFT;
-        if (v < K) {
-          const int q = v / m2, ky = v - q * m2;
+        int q, ky;
+        if (inv_mode(mp, i, tid, q, ky) >= 0) {
           const int kx = q < m1 ? q : H - 2 * m1 + q;
           const float2 w = twh[(kx * kRows * r) & (H - 1)];  // e^{-i theta}
           const float zr = (yv[i].x * w.x + yv[i].y * w.y) * sc;
@@ -877,7 +912,9 @@ __device__ __forceinline__ void inv_mx_run(const PlaneMxInvArgs &a, int bid, int
                 o.x = f32x2_to_bf16x2(acc[0] * isc, acc[1] * isc);
                 o.y = f32x2_to_bf16x2(acc[2] * isc, acc[3] * isc);
               }
-              reinterpret_cast<uint2 *>(ostage + h * OP)[w / 4] = o;
+              // 8-byte slots of rows 8..15 of each 16 swapped in pairs: the
+              // 16 rows of a store then fall on distinct banks
+              reinterpret_cast<uint2 *>(ostage + h * OP)[(w / 4) ^ ((h >> 3) & 1)] = o;
             }
           }
         }
@@ -890,19 +927,25 @@ __device__ __forceinline__ void inv_mx_run(const PlaneMxInvArgs &a, int bid, int
       for (int v = 0; v < FU; ++v) {
         const int e2 = v * kFT + tid;
         const int row = e2 / UR, cu = e2 - row * UR;
-        __builtin_nontemporal_store(ostage[row * OP + cu], yp + (size_t)r * kRows * UR + e2);
+        u32x4 o = ostage[row * OP + cu];
+        if constexpr (!SP) {
+          if ((row >> 3) & 1) o = u32x4{o[2], o[3], o[0], o[1]};
+        }
+        __builtin_nontemporal_store(o, yp + (size_t)r * kRows * UR + e2);
       }
     };
     for (int r = 0; r + 1 < rounds; ++r) round(r);
     // The next plane's spectra (after the last plane, this one's again,
     // unused) are requested before the last round: only that round's stores
     // are issued after them, so the copy below waits for nothing else.
-    if (half) inv_load16<NY>(a.in16, a.iexp, pi + 1 < nmine ? plane + nblk : plane, K, tid, hn, en);
-    else inv_load<NY>(a.in, pi + 1 < nmine ? plane + nblk : plane, K, tid, yn);
+    const size_t pn = nxt < a.nplanes ? (size_t)nxt : plane;
+    if constexpr (half) inv_load16<NY>(a.in16, a.iexp, pn, mp, tid, hn, en);
+    else inv_load<NY>(a.in, pn, mp, tid, yn);
     round(rounds - 1);
-    if (half) inv_decode<NY>(K, tid, hn, en, yn);
+    if constexpr (half) inv_decode<NY>(mp, tid, hn, en, yn);
 #pragma unroll
     for (int i = 0; i < NY; ++i) yv[i] = yn[i];
+    cur = nxt;
   }
 }
 
