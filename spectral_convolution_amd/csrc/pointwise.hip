@@ -710,9 +710,14 @@ __device__ __forceinline__ void store1(void *p, size_t i, float v) {
   else reinterpret_cast<uint16_t *>(p)[i] = (uint16_t)f32_to_bf16(v);
 }
 
+constexpr int kFoldP = kProjMaxIn * kMixMaxIn;  // P entries staged in LDS (C <= 64, J <= 128)
+
 template <int DT>
 __global__ __launch_bounds__(kPwThreads) void fno_lift_fold(FoldArgs a) {
+  __shared__ float ps[kFoldP];  // P [C][J], fp32
   const int K = a.K, J = a.J, C = a.C;
+  for (int v = threadIdx.x; v < C * J; v += kPwThreads) ps[v] = load1<DT>(a.P, v);
+  __syncthreads();
   const long npair = (long)K * C, total = npair + C;
   for (long t = (long)blockIdx.x * kPwThreads + threadIdx.x; t < total; t += (long)gridDim.x * kPwThreads) {
     if (t < npair) {
@@ -720,13 +725,23 @@ __global__ __launch_bounds__(kPwThreads) void fno_lift_fold(FoldArgs a) {
       const long k = t / C;
       for (int j0 = 0; j0 < J; j0 += 4) {
         float re[4] = {0.f, 0.f, 0.f, 0.f}, im[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int c = 0; c < C; ++c) {
-          const float2 wv = load_pair<DT>(a.w, ((size_t)(k * C + c) * C + o) * 2);
+        // the weights of 16 input channels are requested together (their
+        // latencies overlap), clamped in range; past C they count as zero
+        for (int c0 = 0; c0 < C; c0 += 16) {
+          float2 wv[16];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float pc = j0 + q < J ? load1<DT>(a.P, (size_t)c * J + j0 + q) : 0.f;
-            re[q] = fmaf(pc, wv.x, re[q]);
-            im[q] = fmaf(pc, wv.y, im[q]);
+          for (int u = 0; u < 16; ++u) wv[u] = load_pair<DT>(a.w, ((size_t)(k * C + min(c0 + u, C - 1)) * C + o) * 2);
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const int c = c0 + u;
+            if (c < C) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float pc = j0 + q < J ? ps[c * J + j0 + q] : 0.f;
+                re[q] = fmaf(pc, wv[u].x, re[q]);
+                im[q] = fmaf(pc, wv[u].y, im[q]);
+              }
+            }
           }
         }
 #pragma unroll
@@ -736,16 +751,31 @@ __global__ __launch_bounds__(kPwThreads) void fno_lift_fold(FoldArgs a) {
     } else {
       // output channel o: row o of Af and bf[o]
       const int o = (int)(t - npair);
-      for (int j = 0; j < J; ++j) {
-        float s = 0.f;
-        for (int c = 0; c < C; ++c) s = fmaf(load1<DT>(a.Wb, (size_t)o * C + c), load1<DT>(a.P, (size_t)c * J + j), s);
-        store1<DT>(a.af, (size_t)o * J + j, s);
-      }
       float s = load1<DT>(a.b, o);
-      for (int c = 0; c < C; ++c) {
-        const float pc = load1<DT>(a.p, c);
-        s = fmaf(load1<DT>(a.Wb, (size_t)o * C + c), pc, s);
-        s = fmaf(pc, load_pair<DT>(a.w, ((size_t)c * C + o) * 2).x, s);
+      for (int j0 = 0; j0 < J; j0 += 4) {
+        float af[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int c0 = 0; c0 < C; c0 += 16) {
+          float wb[16], pc[16], w0[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const int c = min(c0 + u, C - 1);
+            wb[u] = load1<DT>(a.Wb, (size_t)o * C + c);
+            pc[u] = load1<DT>(a.p, c);
+            w0[u] = load_pair<DT>(a.w, ((size_t)c * C + o) * 2).x;
+          }
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const int c = c0 + u;
+            if (c < C) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) af[q] = fmaf(wb[u], j0 + q < J ? ps[c * J + j0 + q] : 0.f, af[q]);
+              if (j0 == 0) s = fmaf(pc[u], wb[u] + w0[u], s);
+            }
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (j0 + q < J) store1<DT>(a.af, (size_t)o * J + j0 + q, af[q]);
       }
       store1<DT>(a.bf, o, s);
     }
@@ -754,6 +784,7 @@ __global__ __launch_bounds__(kPwThreads) void fno_lift_fold(FoldArgs a) {
 
 hipError_t launch_lift_fold(const void *P, const void *p, const void *w, const void *Wb, const void *b, void *wf,
                             void *af, void *bf, int K, int J, int C, int dtype, hipStream_t s) {
+  if (C * J > kFoldP) return hipErrorInvalidValue;
   FoldArgs a{P, p, w, Wb, b, wf, af, bf, K, J, C};
   void *args[] = {(void *)&a};
   const long total = (long)K * C + C;
