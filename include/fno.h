@@ -283,7 +283,9 @@ fno_status_t fno_plan_spectra_format(fno_plan_t plan, int *half);
  * is folded into the first block: its weights are composed with the lift's
  * (spectral weights with P, the 1x1 weights with P, the bias with p through
  * both branches) and the first block runs on the feature channels, so the
- * lifted field is never stored (the same function up to rounding). */
+ * lifted field is never stored (the same function up to rounding). Blocks
+ * run as fno_block2d where the plans allow it (the spectral output is then
+ * not stored either), else as fno_spectral_conv2d + fno_channel_mix. */
 
 /* Per-pixel channel mix:
  *   y[b][o][p] = act(sum_i A[o][i] x[b][i][p] + bias[o] + add[b][o][p])
@@ -305,14 +307,43 @@ fno_status_t fno_projection(const void *x, const void *Q1, const void *q1,
                             int c_in, int hidden, int c_out, long pixels,
                             fno_dtype_t dtype, void *stream);
 
+/* One FNO block with the spectral branch finished in its epilogue:
+ *   y = act(spectral_conv2d(x, w) + bypass x + bias)
+ * x [batch][c_in][H][W] and w as for fno_spectral_conv2d with this 2D plan;
+ * bypass [c_out][c_in] (the block's 1x1 convolution), bias [c_out] (NULL:
+ * none), y [batch][c_out][H][W], all in the plan's dtype on its device; act:
+ * 0 none, 1 GELU (the erf form). The forward planes and the contraction run
+ * as in fno_spectral_conv2d; the inverse transform stops after its column
+ * stage (rows of fp16 values with one power-of-two scale per plane, in a
+ * buffer the plan owns), and one kernel applies the row stage and the 1x1
+ * convolution to the same accumulators per image row, then bias and act,
+ * so the spectral branch's output is never stored (TurboFNO write-up,
+ * sections 1 and 4.3 for the block; the operator-fusion page for the GEMM
+ * epilogue). Supported for fp16 / bf16 2D plans on matrix-core planes
+ * (H and W of 64, 128 or 256, m1 <= 32, m2 <= 32) with c_in <= 64;
+ * otherwise FNO_ERR_UNSUPPORTED and nothing runs. y must
+ * not overlap x or w; x, w, y 16-byte aligned. The first call allocates the
+ * plan's block buffer (batch*c_out*H*32*ceil(m2/16) halves plus batch*c_out
+ * bytes) unless fno_block2d_prepare already did; under stream capture that
+ * allocation is refused (FNO_ERR_UNSUPPORTED), so prepare before capturing.
+ * Asynchronous on `stream`; the plan's buffers serve one call at a time. */
+fno_status_t fno_block2d(fno_plan_t plan, const void *x, const void *w,
+                         const void *bypass, const void *bias, int act,
+                         void *y, void *stream);
+
+/* Allocate the block buffer fno_block2d needs (idempotent; synchronous). */
+fno_status_t fno_block2d_prepare(fno_plan_t plan);
+
 typedef struct fno_model2d_s *fno_model2d_t;
 
 /* Plan of the network on [batch][in_channels][height][width] inputs with
  * `channels` hidden channels, spectral modes (m1, m2) in every block,
  * `proj_channels` hidden units in the projection, `out_channels` outputs.
  * Owns two spectral-conv plans (the first block's from in_channels, the
- * others') and three activation buffers of batch*channels*height*width
- * elements, plus the first block's folded weights. */
+ * others'), with their fno_block2d buffers where the fused block serves
+ * them, two activation buffers of batch*channels*height*width elements (a
+ * third for the spectral output of blocks that are not fused), plus the
+ * first block's folded weights. */
 fno_status_t fno_model2d_create(fno_model2d_t *model, int batch, int height,
                                 int width, int in_channels, int channels,
                                 int n_layers, int m1, int m2,

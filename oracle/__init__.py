@@ -20,6 +20,7 @@ Functions:
   spectral.contract                   per-mode complex contraction
   spectral.inverse2d / inverse3d      closed-form inverse on retained modes
   spectral.spectral_conv2d / 3d       the whole layer
+  fno2d.fno_block2d                   one block: act(spectral conv + 1x1 + bias)
   fno2d.fno2d_forward                 the full FNO2d network (composition)
   backward.spectral_conv2d_backward   gradients of the layer (dx, dw): the
   backward.spectral_conv3d_backward   adjoints of its linear steps in reverse
@@ -35,5 +36,5 @@ from .spectral import (  # noqa: F401
     spectral_conv2d,
     spectral_conv3d,
 )
-from .fno2d import fno2d_forward, gelu  # noqa: F401
+from .fno2d import fno2d_forward, fno_block2d, gelu  # noqa: F401
 from .backward import spectral_conv2d_backward, spectral_conv3d_backward  # noqa: F401

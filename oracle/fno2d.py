@@ -27,6 +27,16 @@ def _pointwise(A: np.ndarray, v: np.ndarray, bias: np.ndarray) -> np.ndarray:
     return out.reshape(B, A.shape[0], H, W)
 
 
+def fno_block2d(v: np.ndarray, spectral: np.ndarray, W: np.ndarray,
+                b, m1: int, m2: int, act: bool = True) -> np.ndarray:
+    """One block of the module: act(spectral_conv2d(v) + W v + b), act the
+    exact GELU or the identity; spectral (2*m1, m2, Ci, Co) complex, W (Co, Ci),
+    b (Co,) or None (zero)."""
+    bias = np.zeros(W.shape[0]) if b is None else b
+    u = spectral_conv2d(v, spectral, m1, m2) + _pointwise(W, v, bias)
+    return gelu(u) if act else u
+
+
 def fno2d_forward(features: np.ndarray, P: np.ndarray, p: np.ndarray,
                   layers: list, Q1: np.ndarray, q1: np.ndarray,
                   Q2: np.ndarray, q2: np.ndarray, m1: int, m2: int):
@@ -35,7 +45,6 @@ def fno2d_forward(features: np.ndarray, P: np.ndarray, p: np.ndarray,
     Returns (B, out, H, W) float64."""
     v = _pointwise(P, features, p)
     for layer in layers:
-        s = spectral_conv2d(v, layer["spectral"], m1, m2)
-        v = gelu(s + _pointwise(layer["W"], v, layer["b"]))
+        v = fno_block2d(v, layer["spectral"], layer["W"], layer["b"], m1, m2)
     h = gelu(_pointwise(Q1, v, q1))
     return _pointwise(Q2, h, q2)

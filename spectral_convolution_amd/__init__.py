@@ -17,7 +17,7 @@ __all__ = [
     "fno_plan_spectra", "fno_spectral_conv2d_backward", "fno_spectral_conv3d_backward", "SpectralConv", "FnoError", "DTYPES",
     "fno_weights_pack", "fno_weights_unpack", "SpectralConvFunction", "spectral_conv",
     "fno_channel_mix", "fno_projection", "fno_model2d_create", "fno_model2d_forward",
-    "fno_model2d_destroy", "Model2d", "fno_model2d_set_graph",
+    "fno_model2d_destroy", "Model2d", "fno_model2d_set_graph", "fno_block2d", "fno_block2d_prepare",
 ]
 
 
@@ -130,6 +130,20 @@ def fno_spectral_conv_noalloc(plan, x, w, y, stream=None):
     _check_tensors(plan, x, w, y)
     check(lib().fno_spectral_conv_noalloc(plan.handle, _ptr(x), _ptr(w), _ptr(y),
                                           _stream(stream, plan.device)), "fno_spectral_conv_noalloc")
+
+
+def fno_block2d(plan, x, w, bypass, bias, y, act=1, stream=None):
+    """One FNO block, y = act(spectral conv(x, w) + bypass x + bias), with the
+    spectral branch finished in the epilogue; see fno_block2d in
+    include/fno.h. bypass [c_out][c_in], bias [c_out] or None."""
+    _check_tensors(plan, x, w, y)
+    check(lib().fno_block2d(plan.handle, _ptr(x), _ptr(w), _ptr(bypass), _ptr(bias), act, _ptr(y),
+                            _stream(stream, plan.device)), "fno_block2d")
+
+
+def fno_block2d_prepare(plan):
+    """Allocate the plan's block buffer now (before a graph capture)."""
+    check(lib().fno_block2d_prepare(plan.handle), "fno_block2d_prepare")
 
 
 def _check_backward(plan, x, w, gy, gx, gw):

@@ -21,6 +21,9 @@ SIGNATURES = {
     "fno_spectral_conv2d": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "fno_spectral_conv3d": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "fno_spectral_conv_noalloc": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "fno_block2d": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p,
+                             _c_void_p]),
+    "fno_block2d_prepare": (_c_int, [_c_void_p]),
     "fno_spectral_conv2d_backward": (_c_int, [_c_void_p] * 7),
     "fno_spectral_conv3d_backward": (_c_int, [_c_void_p] * 7),
     "fno_weights_pack": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),

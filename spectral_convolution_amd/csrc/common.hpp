@@ -133,6 +133,12 @@ struct PlaneMxInvArgs {
   // (iexp has ceil(K / 4) entries per plane)
   const uint32_t *in16;
   const signed char *iexp;
+  // column stage only (half storage): instead of y, the scaled fp16 Z rows
+  // go to zg [B][H][zco][32 nn] halves (plane = b zco + o) and each plane's
+  // scale exponent to zexp [nplanes] (Z = stored Z 2^-zexp)
+  uint16_t *zg;
+  signed char *zexp;
+  int zco;
 };
 
 // Pruned c2c DFT along a strided axis: in [vol][N][C] -> out [vol][2*m][C]
@@ -274,6 +280,14 @@ hipError_t launch_projection(const void *x, const void *Q1, const void *q1, cons
 // first block's weights with the lift folded in (see pointwise.hip)
 hipError_t launch_lift_fold(const void *P, const void *p, const void *w, const void *Wb, const void *b, void *wf,
                             void *af, void *bf, int K, int J, int C, int dtype, hipStream_t s);
+// inverse column stage alone (Z rows out), fp16 / bf16 planes
+hipError_t mx_cols_prepare(int m1, int m2, int dtype, size_t lds, int device, int nplanes, int *grid);
+hipError_t launch_plane_mx_cols(const PlaneMxInvArgs &a, int grid, int dtype, size_t lds, hipStream_t s);
+// FNO block epilogue: inverse row stage of the scaled Z rows + 1x1 + bias + act
+bool block_rows_supported(int dtype, int W, int Ci, int NN);
+hipError_t launch_block_rows(const uint16_t *zg, const signed char *zexp, const void *tb, const void *x,
+                             const void *wb, const void *bias, void *y, int B, int Ci, int Co, int H, int W, int NN,
+                             int act, int dtype, hipStream_t s);
 constexpr int kMixMaxIn = 128;   // channel mix: input channels
 constexpr int kProjMaxIn = 64;   // projection: input channels
 constexpr int kProjMaxHidden = 128;

@@ -264,6 +264,12 @@ struct fno_plan_s {
   int fused_grid = 0;
   size_t lds_fused = 0;
   FusedBarrier *bar = nullptr;
+  // FNO block (fno_block2d): Z rows between the column and row stages, the
+  // planes' scale exponents, allocated by fno_block2d_prepare
+  void *blk_mem = nullptr;
+  uint16_t *zbuf = nullptr;
+  signed char *zexp = nullptr;
+  int cols_grid = 0;
   void *mem = nullptr;
   size_t ws_bytes = 0;
   std::vector<int> launches;      // the current launch shape's launches
@@ -424,11 +430,12 @@ const char *fno_status_string(fno_status_t s) {
 fno_status_t fno_plan_destroy(fno_plan_t plan) {
   if (!plan) return FNO_OK;
   fno_status_t st = FNO_OK;
-  if (plan->mem) {
+  if (plan->mem || plan->blk_mem) {
     DeviceGuard g(plan->device);
     if (g.err != hipSuccess) st = FNO_ERR_DEVICE;
     if (hipDeviceSynchronize() != hipSuccess) st = FNO_ERR_DEVICE;
-    if (hipFree(plan->mem) != hipSuccess) st = FNO_ERR_DEVICE;
+    if (plan->mem && hipFree(plan->mem) != hipSuccess) st = FNO_ERR_DEVICE;
+    if (plan->blk_mem && hipFree(plan->blk_mem) != hipSuccess) st = FNO_ERR_DEVICE;
   }
   delete plan;
   return st;
@@ -811,6 +818,9 @@ static PlaneMxInvArgs mx_inv_args(fno_plan_t p, const Bufs &b, const float2 *src
   m.nn = p->mx_nn;
   m.kb1 = p->mx_kb1;
   m.lg4m1 = p->mx_lg4m1;
+  m.zg = nullptr;
+  m.zexp = nullptr;
+  m.zco = 0;
   return m;
 }
 
@@ -1102,6 +1112,75 @@ fno_status_t fno_spectral_conv_noalloc(fno_plan_t plan, const void *x, const voi
   Bufs b;
   carve(plan, base, &b);
   return exec_with(plan, b, x, w, y, (hipStream_t)stream, -1);
+}
+
+// ---- FNO block ---------------------------------------------------------
+
+// the plan's dimensions the block path needs (2D, fp16 / bf16 planes of
+// width 64 / 128 / 256 on matrix cores, at most 64 input channels)
+static bool block_ok(fno_plan_t p) {
+  return p->ndim == 2 && p->mx && p->pH == p->grid[0] && p->pW == p->grid[1] &&
+         block_rows_supported(p->dtype, p->pW, p->Ci, p->mx_nn);
+}
+
+fno_status_t fno_block2d_prepare(fno_plan_t p) {
+  if (!p) return FNO_ERR_INVALID_ARG;
+  if (!block_ok(p)) return FNO_ERR_UNSUPPORTED;
+  if (p->blk_mem) return FNO_OK;
+  DeviceGuard g(p->device);
+  if (g.err != hipSuccess) return FNO_ERR_DEVICE;
+  const size_t nz = (size_t)p->B * p->pH * p->Co * 32 * p->mx_nn * sizeof(uint16_t);
+  const size_t ne = (size_t)p->B * p->Co;
+  int grid = 0;
+  hipError_t e = mx_cols_prepare(p->pm1, p->pm2, p->dtype, p->lds_inv, p->device, p->B * p->Co, &grid);
+  if (e != hipSuccess) return map_err(e);
+  void *mem = nullptr;
+  e = hipMalloc(&mem, nz + ne);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return map_err(e);
+  }
+  p->blk_mem = mem;
+  p->zbuf = (uint16_t *)mem;
+  p->zexp = (signed char *)mem + nz;
+  p->cols_grid = grid;
+  return FNO_OK;
+}
+
+fno_status_t fno_block2d(fno_plan_t p, const void *x, const void *w, const void *bypass, const void *bias, int act,
+                         void *y, void *stream) {
+  fno_status_t st = check_exec(p, 2, x, w, y);
+  if (st != FNO_OK) return st;
+  if (!bypass || (act != 0 && act != 1)) return FNO_ERR_INVALID_ARG;
+  if (((uintptr_t)bypass | (uintptr_t)bias) & 1) return FNO_ERR_INVALID_ARG;
+  if (!block_ok(p)) return FNO_ERR_UNSUPPORTED;
+  DeviceGuard g(p->device);
+  if (g.err != hipSuccess) return FNO_ERR_DEVICE;
+  const hipStream_t s = (hipStream_t)stream;
+  if (!p->blk_mem) {
+    // allocating is not part of a captured graph: prepare first
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return FNO_ERR_DEVICE;
+    if (cs != hipStreamCaptureStatusNone) return FNO_ERR_UNSUPPORTED;
+    st = fno_block2d_prepare(p);
+    if (st != FNO_OK) return st;
+  }
+  const Bufs b = plan_bufs(p);
+  // the spectra travel between the launches in the plan's exchange format
+  hipError_t e = fwd_plane_launch(p, b, x, p->Ci, b.xh, s, p->hx);
+  if (e == hipSuccess) e = contract_launch(p, b, b.xh, w, b.yh, false, s, p->hx);
+  if (e == hipSuccess) {
+    PlaneMxInvArgs m = mx_inv_args(p, b, b.yh, p->Co, nullptr, p->hx);
+    m.zg = p->zbuf;
+    m.zexp = p->zexp;
+    m.zco = p->Co;
+    e = launch_plane_mx_cols(m, p->cols_grid, p->dtype, p->lds_inv, s);
+  }
+  if (e == hipSuccess)
+    e = launch_block_rows(p->zbuf, p->zexp, p->tb, x, bypass, bias, y, p->B, p->Ci, p->Co, p->pH, p->pW, p->mx_nn, act,
+                          p->dtype, s);
+  if (e == hipSuccess) e = hipGetLastError();
+  return map_err(e);
 }
 
 fno_status_t fno_plan_workspace_bytes(fno_plan_t plan, size_t *bytes) {

@@ -6,9 +6,13 @@
 // The lift is folded into the first block (both are linear in the lifted
 // field): one small kernel composes the first block's spectral weights,
 // 1x1 weights and bias with the lift, and the first block then runs on the
-// raw feature channels, so the lifted field is never written or read. The
-// forward can be replayed from a HIP graph captured on the model's own
-// stream.
+// raw feature channels, so the lifted field is never written or read. Where
+// the plans allow it (fp16 / bf16 on matrix-core planes, see fno_block2d)
+// every block runs as fno_block2d: the 1x1 convolution, bias and GELU are
+// applied in the inverse transform's row stage, so the spectral branch's
+// output is never stored either; otherwise a block is the layer followed by
+// the channel-mix kernel. The forward can be replayed from a HIP graph
+// captured on the model's own stream.
 
 #include <hip/hip_runtime.h>
 
@@ -26,6 +30,7 @@ struct fno_model2d_s {
   int dtype = 0, device = 0;
   fno_plan_t plan = nullptr;   // blocks 1.. (ch -> ch)
   fno_plan_t plan0 = nullptr;  // block 0 on the features (in_ch -> ch), lift folded in
+  bool fused0 = false, fused = false;  // block 0 / the other blocks run as fno_block2d
   void *mem = nullptr;
   void *act[3] = {nullptr, nullptr, nullptr};
   void *wf = nullptr, *af = nullptr, *bf = nullptr;  // block 0's folded weights
@@ -142,6 +147,24 @@ fno_status_t fno_model2d_create(fno_model2d_t *out, int batch, int height, int w
     fno_model2d_destroy(m);
     return st;
   }
+  // block buffers now (allocation cannot be part of a captured graph);
+  // a plan the fused block does not serve keeps the two-kernel block
+  if (m->plan) {
+    st = fno_block2d_prepare(m->plan);
+    m->fused = st == FNO_OK;
+    if (st != FNO_OK && st != FNO_ERR_UNSUPPORTED) {
+      fno_model2d_destroy(m);
+      return st;
+    }
+  }
+  if (m->plan0) {
+    st = fno_block2d_prepare(m->plan0);
+    m->fused0 = st == FNO_OK;
+    if (st != FNO_OK && st != FNO_ERR_UNSUPPORTED) {
+      fno_model2d_destroy(m);
+      return st;
+    }
+  }
   int prev = -1;
   (void)hipGetDevice(&prev);
   if (prev != device) (void)hipSetDevice(device);
@@ -151,7 +174,9 @@ fno_status_t fno_model2d_create(fno_model2d_t *out, int batch, int height, int w
   const size_t K = (size_t)2 * m1 * m2;
   const size_t nwf = al(K * in_channels * channels * 2 * es), naf = al((size_t)channels * in_channels * es),
                nbf = al((size_t)channels * es);
-  hipError_t e = hipMalloc(&m->mem, 3 * one + nwf + naf + nbf);
+  // the spectral branch's output buffer only for blocks that are not fused
+  const int nact = ((n_layers >= 1 && !m->fused0) || (n_layers >= 2 && !m->fused)) ? 3 : 2;
+  hipError_t e = hipMalloc(&m->mem, nact * one + nwf + naf + nbf);
   if (prev >= 0 && prev != device) (void)hipSetDevice(prev);
   if (e != hipSuccess) {
     (void)hipGetLastError();
@@ -159,8 +184,8 @@ fno_status_t fno_model2d_create(fno_model2d_t *out, int batch, int height, int w
     fno_model2d_destroy(m);
     return status_of(e);
   }
-  for (int i = 0; i < 3; ++i) m->act[i] = (char *)m->mem + i * one;
-  m->wf = (char *)m->mem + 3 * one;
+  for (int i = 0; i < nact; ++i) m->act[i] = (char *)m->mem + i * one;
+  m->wf = (char *)m->mem + nact * one;
   m->af = (char *)m->wf + nwf;
   m->bf = (char *)m->af + naf;
   *out = m;
@@ -181,9 +206,13 @@ static fno_status_t enqueue_forward(fno_model2d_t m, const void *features, const
                                     2 * m->m1 * m->m2, m->in_ch, m->ch, m->dtype, (hipStream_t)stream);
     if (e == hipSuccess) e = hipGetLastError();
     st = status_of(e);
-    if (st == FNO_OK) st = fno_spectral_conv2d(m->plan0, features, m->wf, m->act[2], stream);
-    if (st == FNO_OK)
-      st = fno_channel_mix(features, m->af, m->bf, m->act[2], m->act[1], m->B, m->in_ch, m->ch, P, 1, dt, stream);
+    if (st == FNO_OK && m->fused0) {
+      st = fno_block2d(m->plan0, features, m->wf, m->af, m->bf, 1, m->act[1], stream);
+    } else if (st == FNO_OK) {
+      st = fno_spectral_conv2d(m->plan0, features, m->wf, m->act[2], stream);
+      if (st == FNO_OK)
+        st = fno_channel_mix(features, m->af, m->bf, m->act[2], m->act[1], m->B, m->in_ch, m->ch, P, 1, dt, stream);
+    }
     cur = 1;
     l0 = 1;
   } else {
@@ -193,9 +222,13 @@ static fno_status_t enqueue_forward(fno_model2d_t m, const void *features, const
   for (int l = l0; l < m->layers && st == FNO_OK; ++l) {
     const void *const *lp = params + 2 + 3 * l;
     const int nxt = cur == 0 ? 1 : 0;
-    st = fno_spectral_conv2d(m->plan, m->act[cur], lp[0], m->act[2], stream);
-    if (st == FNO_OK)
-      st = fno_channel_mix(m->act[cur], lp[1], lp[2], m->act[2], m->act[nxt], m->B, m->ch, m->ch, P, 1, dt, stream);
+    if (m->fused) {
+      st = fno_block2d(m->plan, m->act[cur], lp[0], lp[1], lp[2], 1, m->act[nxt], stream);
+    } else {
+      st = fno_spectral_conv2d(m->plan, m->act[cur], lp[0], m->act[2], stream);
+      if (st == FNO_OK)
+        st = fno_channel_mix(m->act[cur], lp[1], lp[2], m->act[2], m->act[nxt], m->B, m->ch, m->ch, P, 1, dt, stream);
+    }
     cur = nxt;
   }
   if (st == FNO_OK) {

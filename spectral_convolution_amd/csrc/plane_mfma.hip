@@ -17,6 +17,15 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(SM ? 3 : 2)
   inv_mx_run<DT, KB, SM, HX>(a, blockIdx.x, gridDim.x, lds);
 }
 
+// The inverse column stage alone (fp16 / bf16): Z rows to a.zg for the FNO
+// block's row-stage kernel. The row-stage width does not enter the column
+// stage, so one instantiation (the 64-wide layout) serves every W.
+template <int DT, bool SM, bool HX>
+__global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(SM ? 3 : 2))) void fno_inv_cols_mx(PlaneMxInvArgs a) {
+  extern __shared__ u32x4 lds[];
+  inv_mx_run<DT, 2, SM, HX, true>(a, blockIdx.x, gridDim.x, lds);
+}
+
 // --------------------------------------------------------------- launchers
 
 bool mx_supported(int H, int W, int m1, int m2, int dtype) {
@@ -149,6 +158,44 @@ hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int grid, int dtype, siz
 hipError_t launch_plane_mx_inv(const PlaneMxInvArgs &a, int grid, int dtype, size_t lds, hipStream_t s) {
   const void *k = mx_kernel(false, a.W, a.m1, a.m2, dtype, false, a.in16 != nullptr);
   if (!k || grid < 1) return hipErrorInvalidValue;
+  void *args[] = {(void *)&a};
+  return hipLaunchKernel(k, dim3(grid), dim3(kFT), args, lds, s);
+}
+
+// column stage only
+template <int DT, bool HX>
+static const void *cols_kernel_dt(bool small) {
+  return small ? (const void *)fno_inv_cols_mx<DT, true, HX> : (const void *)fno_inv_cols_mx<DT, false, HX>;
+}
+
+static const void *cols_kernel(int m1, int m2, int dtype, bool half) {
+  const bool small = inv_small(m1, m2);
+  if (dtype == DT_F16) return half ? cols_kernel_dt<DT_F16, true>(small) : cols_kernel_dt<DT_F16, false>(small);
+  if (dtype == DT_BF16) return half ? cols_kernel_dt<DT_BF16, true>(small) : cols_kernel_dt<DT_BF16, false>(small);
+  return nullptr;
+}
+
+hipError_t mx_cols_prepare(int m1, int m2, int dtype, size_t lds, int device, int nplanes, int *grid) {
+  int per_cu = 1 << 20, ncu = 0;
+  for (bool half : {false, true}) {
+    const void *k = cols_kernel(m1, m2, dtype, half);
+    if (!k) return hipErrorInvalidValue;
+    hipError_t e = raise_lds_cap(k, lds);
+    int pc = 0;
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&pc, k, kFT, lds);
+    if (e != hipSuccess) return e;
+    per_cu = pc < per_cu ? pc : per_cu;
+  }
+  hipError_t e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return e;
+  const long g = (long)(per_cu > 0 ? per_cu : 1) * (ncu > 0 ? ncu : 1);
+  *grid = (int)(g < nplanes ? g : nplanes);
+  return hipSuccess;
+}
+
+hipError_t launch_plane_mx_cols(const PlaneMxInvArgs &a, int grid, int dtype, size_t lds, hipStream_t s) {
+  const void *k = cols_kernel(a.m1, a.m2, dtype, a.in16 != nullptr);
+  if (!k || grid < 1 || !a.zg || !a.zexp || a.zco < 1) return hipErrorInvalidValue;
   void *args[] = {(void *)&a};
   return hipLaunchKernel(k, dim3(grid), dim3(kFT), args, lds, s);
 }

@@ -727,8 +727,10 @@ __device__ __forceinline__ void inv_decode(const InvMap &mp, int tid, const uint
 // fragment registers take their smaller sizes (fewer registers and LDS,
 // more workgroups per CU). HX: the spectra come as the half exchange (fp16
 // pairs with exponents), compiled separately so that each form keeps only
-// its own registers.
-template <int DT, int KB, bool SM, bool HX = false>
+// its own registers. ZOUT (fp16 / bf16 only): steps 3 and 4 are replaced by
+// a copy of the round's Z rows (scaled fp16 pairs) to a.zg, for a consumer
+// that applies the row stage itself.
+template <int DT, int KB, bool SM, bool HX = false, bool ZOUT = false>
 __device__ __forceinline__ void inv_mx_run(const PlaneMxInvArgs &a, int bid, int nblk, u32x4 *lds) {
   using P = MxPol<DT>;
   using G = InvGeom<SM>;
@@ -788,8 +790,11 @@ __device__ __forceinline__ void inv_mx_run(const PlaneMxInvArgs &a, int bid, int
     for (int kb = 0; kb < NNM; ++kb)
 #pragma unroll
       for (int q = 0; q < NP; ++q) {
-        const u32x4 t = reinterpret_cast<const u32x4 *>(q ? a.tb_lo : a.tb)[((size_t)(wv + 4 * i) * NN + (kb < NN ? kb : 0)) * 64 + lane];
-        tb[i][kb][q] = kb < NN ? t : u32x4{0u, 0u, 0u, 0u};
+        if constexpr (!ZOUT) {
+          const u32x4 t =
+              reinterpret_cast<const u32x4 *>(q ? a.tb_lo : a.tb)[((size_t)(wv + 4 * i) * NN + (kb < NN ? kb : 0)) * 64 + lane];
+          tb[i][kb][q] = kb < NN ? t : u32x4{0u, 0u, 0u, 0u};
+        }
       }
 
   const int rounds = H / kRows;
@@ -811,6 +816,9 @@ __device__ __forceinline__ void inv_mx_run(const PlaneMxInvArgs &a, int bid, int
     if (ym > 0.f) (void)frexpf(ym, &e);
     const int se = ym > 0.f ? max(-120, min(120, 15 - e - a.lg4m1)) : 0;
     const float sc = pow2f(se), isc = pow2f(-se);
+    if constexpr (ZOUT) {
+      if (tid == 0) a.zexp[plane] = (signed char)se;
+    }
 
     u32x4 *yp = reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(a.y) + plane * H * W * P::ES);
     auto round = [&](int r) {
@@ -868,70 +876,81 @@ __device__ __forceinline__ void inv_mx_run(const PlaneMxInvArgs &a, int bid, int
       }
       __syncthreads();
 
-      // 3. y^T = T'^T Z^T: lane gets y[h][w .. w + 3], h = 16 mt + l % 16;
-      // the Z fragments of MB m-tiles are read ahead of their products
-      constexpr int MB = SP ? 1 : 4;
-#pragma unroll
-      for (int m0 = 0; m0 < 4; m0 += MB) {
-        u32x4 bz[MB][NNM][2];
-#pragma unroll
-        for (int mi = 0; mi < MB; ++mi) {
-          const u32x4 *zr = reinterpret_cast<const u32x4 *>(zb + ((m0 + mi) * 16 + (lane & 15)) * ZP) + (lane >> 4);
-#pragma unroll
-          for (int kb = 0; kb < NNM; ++kb)
-#pragma unroll
-            for (int q = 0; q < 2; ++q) bz[mi][kb][q] = q < NP ? zr[q * (ZBS / 8) + (NN > 1 ? kb : 0) * 4] : bz[mi][kb][0];
+      if constexpr (ZOUT) {
+        // Z rows h0 .. h0 + 63 of this plane (32 NN halves each) to zg
+        const size_t bb = plane / a.zco, oo = plane - bb * a.zco;
+        const int UZ = 4 * NN;  // 16-byte units per row
+        for (int u = tid; u < kRows * UZ; u += kFT) {
+          const int row = u / UZ, c = u - row * UZ;
+          const u32x4 v = *reinterpret_cast<const u32x4 *>(zb + row * ZP + 8 * c);
+          *reinterpret_cast<u32x4 *>(a.zg + (((bb * H + (size_t)r * kRows + row) * a.zco + oo) * NN * 32 + 8 * c)) = v;
         }
-        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // 3. y^T = T'^T Z^T: lane gets y[h][w .. w + 3], h = 16 mt + l % 16;
+        // the Z fragments of MB m-tiles are read ahead of their products
+        constexpr int MB = SP ? 1 : 4;
 #pragma unroll
-        for (int mi = 0; mi < MB; ++mi) {
-          const int h = (m0 + mi) * 16 + (lane & 15);
-          AccN<false> ac[NPW];  // NPW tiles already give independent chains
+        for (int m0 = 0; m0 < 4; m0 += MB) {
+          u32x4 bz[MB][NNM][2];
 #pragma unroll
-          for (int kb = 0; kb < NNM; ++kb)
-            if (kb == 0 || NN > 1) {
+          for (int mi = 0; mi < MB; ++mi) {
+            const u32x4 *zr = reinterpret_cast<const u32x4 *>(zb + ((m0 + mi) * 16 + (lane & 15)) * ZP) + (lane >> 4);
 #pragma unroll
-              for (int i = 0; i < NPW; ++i) {
-                const u32x4 t2[2] = {tb[i][kb][0], tb[i][kb][NP - 1]};
-                ac[i].add(t2, bz[mi][kb], kb, SP);
+            for (int kb = 0; kb < NNM; ++kb)
+#pragma unroll
+              for (int q = 0; q < 2; ++q) bz[mi][kb][q] = q < NP ? zr[q * (ZBS / 8) + (NN > 1 ? kb : 0) * 4] : bz[mi][kb][0];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int mi = 0; mi < MB; ++mi) {
+            const int h = (m0 + mi) * 16 + (lane & 15);
+            AccN<false> ac[NPW];  // NPW tiles already give independent chains
+#pragma unroll
+            for (int kb = 0; kb < NNM; ++kb)
+              if (kb == 0 || NN > 1) {
+#pragma unroll
+                for (int i = 0; i < NPW; ++i) {
+                  const u32x4 t2[2] = {tb[i][kb][0], tb[i][kb][NP - 1]};
+                  ac[i].add(t2, bz[mi][kb], kb, SP);
+                }
               }
-            }
 #pragma unroll
-          for (int i = 0; i < NPW; ++i) {
-            const v4f acc = ac[i].sum(SP);
-            const int w = (wv + 4 * i) * 16 + 4 * (lane >> 4);
-            if constexpr (SP) {
-              ostage[h * OP + w / 4] = u32x4{__float_as_uint(acc[0] * isc), __float_as_uint(acc[1] * isc),
-                                             __float_as_uint(acc[2] * isc), __float_as_uint(acc[3] * isc)};
-            } else {
-              uint2 o;
-              if constexpr (DT == DT_F16) {
-                o.x = h16x2(acc[0] * isc, acc[1] * isc);
-                o.y = h16x2(acc[2] * isc, acc[3] * isc);
+            for (int i = 0; i < NPW; ++i) {
+              const v4f acc = ac[i].sum(SP);
+              const int w = (wv + 4 * i) * 16 + 4 * (lane >> 4);
+              if constexpr (SP) {
+                ostage[h * OP + w / 4] = u32x4{__float_as_uint(acc[0] * isc), __float_as_uint(acc[1] * isc),
+                                               __float_as_uint(acc[2] * isc), __float_as_uint(acc[3] * isc)};
               } else {
-                o.x = f32x2_to_bf16x2(acc[0] * isc, acc[1] * isc);
-                o.y = f32x2_to_bf16x2(acc[2] * isc, acc[3] * isc);
+                uint2 o;
+                if constexpr (DT == DT_F16) {
+                  o.x = h16x2(acc[0] * isc, acc[1] * isc);
+                  o.y = h16x2(acc[2] * isc, acc[3] * isc);
+                } else {
+                  o.x = f32x2_to_bf16x2(acc[0] * isc, acc[1] * isc);
+                  o.y = f32x2_to_bf16x2(acc[2] * isc, acc[3] * isc);
+                }
+                // 8-byte slots of rows 8..15 of each 16 swapped in pairs: the
+                // 16 rows of a store then fall on distinct banks
+                reinterpret_cast<uint2 *>(ostage + h * OP)[(w / 4) ^ ((h >> 3) & 1)] = o;
               }
-              // 8-byte slots of rows 8..15 of each 16 swapped in pairs: the
-              // 16 rows of a store then fall on distinct banks
-              reinterpret_cast<uint2 *>(ostage + h * OP)[(w / 4) ^ ((h >> 3) & 1)] = o;
             }
           }
         }
-      }
-      __syncthreads();
+        __syncthreads();
 
-      // 4. 64 rows x W elements: coalesced 16-byte stores, non-temporal (y
-      // is not read again here; it should not displace cached spectra)
+        // 4. 64 rows x W elements: coalesced 16-byte stores, non-temporal (y
+        // is not read again here; it should not displace cached spectra)
 #pragma unroll
-      for (int v = 0; v < FU; ++v) {
-        const int e2 = v * kFT + tid;
-        const int row = e2 / UR, cu = e2 - row * UR;
-        u32x4 o = ostage[row * OP + cu];
-        if constexpr (!SP) {
-          if ((row >> 3) & 1) o = u32x4{o[2], o[3], o[0], o[1]};
+        for (int v = 0; v < FU; ++v) {
+          const int e2 = v * kFT + tid;
+          const int row = e2 / UR, cu = e2 - row * UR;
+          u32x4 o = ostage[row * OP + cu];
+          if constexpr (!SP) {
+            if ((row >> 3) & 1) o = u32x4{o[2], o[3], o[0], o[1]};
+          }
+          __builtin_nontemporal_store(o, yp + (size_t)r * kRows * UR + e2);
         }
-        __builtin_nontemporal_store(o, yp + (size_t)r * kRows * UR + e2);
       }
     };
     for (int r = 0; r + 1 < rounds; ++r) round(r);

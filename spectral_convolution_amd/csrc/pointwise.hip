@@ -435,6 +435,204 @@ __global__ __launch_bounds__(kPwThreads) __attribute__((amdgpu_waves_per_eu(2)))
   }
 }
 
+// ----------------------------- FNO block: inverse row stage + 1x1 + act
+//
+// One block of the FNO module, y = act(K x + Wb x + b) (TurboFNO write-up,
+// sections 1 and 4.3: the spectral layer sits inside such blocks), with the
+// spectral convolution K finished here: the inverse plane kernel's column
+// stage leaves the scaled fp16 rows of Z = E' Y ([B][H][Co][32 NN] halves,
+// one power-of-two exponent per plane), and this kernel applies the row
+// stage y = Z T' per image row and adds the 1x1 convolution in the same
+// matrix-core accumulators. With M = 16 pixels of the row and N = 16 output
+// channels, lane l holds channel o = l % 16 of pixels 4 (l / 16) .. + 3 in
+// both products: the row-stage sum is unscaled in place (one exponent per
+// lane) and the bypass products are added to the same registers; bias and
+// act follow, and the block output is the only store. The spectral branch's
+// output never leaves the chip.
+//
+// Workgroups are persistent: workgroup g takes rows g, g + G, ... of the
+// B H (batch, row) pairs for its block of 64 output channels, keeping the
+// T' and Wb fragments in registers for all of them. W / 64 waves, wave w
+// owns pixels 64 w .. 64 w + 63 (four 16-pixel tiles). A row of x (32 KC
+// channels, zero past Ci) goes through LDS [ci][px] (pitch W + 4 halves, two
+// buffers) for the bypass's A fragments; the Z fragments come straight from
+// global memory (64-byte pieces of Z rows). The next row's x and Z are
+// requested before the current row's bypass products and epilogue, so
+// they are in flight while those run; one barrier per row.
+struct BlockRowArgs {
+  const uint16_t *zg;       // [B][H][Co][32 NN] fp16 (re, im) pairs of Z, scaled
+  const signed char *zexp;  // [B][Co]: Z = stored Z * 2^-zexp
+  const pw_u32x4 *tb;       // T' fragments (A operand) [W / 16][NN][64 lanes]
+  const void *x;            // [B][Ci][H][W]
+  const void *wb;           // [Co][Ci]
+  const void *bias;         // [Co] or null
+  void *y;                  // [B][Co][H][W]
+  int B, Ci, Co, H, NN, act;
+};
+
+template <int W, int KC>
+__device__ __forceinline__ void brow_fetch_x(const BlockRowArgs &a, int row, int tid,
+                                             pw_u32x4 (&xr)[KC * 32 * (W / 8) / W]) {
+  constexpr int NT = W, XU = KC * 32 * (W / 8) / NT;
+  const uint16_t *xb = reinterpret_cast<const uint16_t *>(a.x);
+  const int b = row / a.H, h = row - b * a.H;
+#pragma unroll
+  for (int v = 0; v < XU; ++v) {
+    const int u = v * NT + tid, ci = u / (W / 8), c = u % (W / 8);
+    const bool ok = ci < a.Ci;
+    const pw_u32x4 t =
+        *reinterpret_cast<const pw_u32x4 *>(xb + (ok ? (((size_t)b * a.Ci + ci) * a.H + h) * W + 8 * c : 0));
+    xr[v] = ok ? t : pw_u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Z fragments of one row (B operand of the row stage: n = output channel,
+// k = 8 halves of its Z row) and the planes' scales
+__device__ __forceinline__ void brow_fetch_z(const BlockRowArgs &a, int row, int o0, int lane, pw_u32x4 (&zf)[4][2],
+                                             int (&ze)[4]) {
+  const int b = row / a.H, NN = a.NN, Co = a.Co;
+#pragma unroll
+  for (int ot = 0; ot < 4; ++ot) {
+    const int o = o0 + 16 * ot + (lane & 15), oc = min(o, Co - 1);
+    const uint16_t *zr = a.zg + ((size_t)row * Co + oc) * 32 * NN + 8 * (lane >> 4);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const pw_u32x4 t = *reinterpret_cast<const pw_u32x4 *>(zr + 32 * min(kb, NN - 1));
+      zf[ot][kb] = (o < Co && kb < NN) ? t : pw_u32x4{0u, 0u, 0u, 0u};
+    }
+    ze[ot] = a.zexp[(size_t)b * Co + oc];
+  }
+}
+
+template <int DT, int NW, int KC>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void fno_block_rows(BlockRowArgs a) {
+  constexpr int W = NW * 64, XP = W + 4, NT = NW * 64;
+  constexpr int XU = KC * 32 * (W / 8) / NT;  // 16-byte units of an x row per thread
+  constexpr int XB = KC * 32 * XP;            // halves per LDS row buffer
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2 * XB];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int o0 = blockIdx.y * 64;
+  const int Ci = a.Ci, Co = a.Co, H = a.H, NN = a.NN;
+  const int rows = a.B * H;
+  int row = blockIdx.x;
+  if (row >= rows) return;
+
+  // the first row's x and Z are requested before the fragments below
+  pw_u32x4 xr[XU], zf[4][2];
+  int ze[4];
+  brow_fetch_x<W, KC>(a, row, tid, xr);
+  brow_fetch_z(a, row, o0, lane, zf, ze);
+
+  // T' fragments of the wave's four pixel tiles
+  pw_u32x4 tf[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const pw_u32x4 t = a.tb[((size_t)(4 * wv + i) * NN + min(kb, NN - 1)) * 64 + lane];
+      tf[i][kb] = kb < NN ? t : pw_u32x4{0u, 0u, 0u, 0u};
+    }
+  // Wb fragments (B operand of the bypass: n = output channel, k = input
+  // channels 32 kc + 8 (l / 16) .. + 7; one 16-byte load where Ci allows)
+  // and the bias
+  pw_u32x4 wf[4][KC];
+  float bias[4];
+  const uint16_t *wb = reinterpret_cast<const uint16_t *>(a.wb);
+  const bool wvec = (Ci & 7) == 0 && (reinterpret_cast<uintptr_t>(a.wb) & 15) == 0;
+#pragma unroll
+  for (int ot = 0; ot < 4; ++ot) {
+    const int o = o0 + 16 * ot + (lane & 15);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const int c0 = 32 * kc + 8 * (lane >> 4);
+      if (wvec) {
+        const bool ok = o < Co && c0 < Ci;
+        const pw_u32x4 t = *reinterpret_cast<const pw_u32x4 *>(wb + (ok ? (size_t)o * Ci + c0 : 0));
+        wf[ot][kc] = ok ? t : pw_u32x4{0u, 0u, 0u, 0u};
+      } else {
+        uint32_t hv[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const bool ok = o < Co && c0 + t < Ci;
+          const uint32_t v = wb[ok ? (size_t)o * Ci + c0 + t : 0];
+          hv[t] = ok ? v : 0u;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wf[ot][kc][q] = hv[2 * q] | (hv[2 * q + 1] << 16);
+      }
+    }
+    bias[ot] = (a.bias && o < Co) ? load1<DT>(a.bias, o) : 0.f;
+  }
+
+  for (int it = 0; row < rows; ++it, row += gridDim.x) {
+    uint16_t *xsb = xs + (it & 1) * XB;
+    // this row's x into its LDS buffer (the buffer's previous row was read
+    // before the last barrier)
+#pragma unroll
+    for (int v = 0; v < XU; ++v) {
+      const int u = v * NT + tid, ci = u / (W / 8), c = u % (W / 8);
+      uint2 *d = reinterpret_cast<uint2 *>(xsb + ci * XP + 8 * c);
+      d[0] = make_uint2(xr[v][0], xr[v][1]);
+      d[1] = make_uint2(xr[v][2], xr[v][3]);
+    }
+    // row stage: acc[ot][i] = channel o0 + 16 ot + l % 16 at pixels
+    // 64 wv + 16 i + 4 (l / 16) + j, unscaled per lane
+    v4f acc[4][4];
+#pragma unroll
+    for (int ot = 0; ot < 4; ++ot) {
+      const float isc = pow2f(-ze[ot]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v4f c = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          if (kb < NN) c = pw_mma<DT_F16>(tf[i][kb], zf[ot][kb], c);
+        acc[ot][i] = c * isc;
+      }
+    }
+    const int b = row / H, h = row - b * H;
+    // the next row's x and Z are requested now (past the last row: this one
+    // again, unused)
+    const int nrow = row + (int)gridDim.x < rows ? row + (int)gridDim.x : row;
+    brow_fetch_x<W, KC>(a, nrow, tid, xr);
+    brow_fetch_z(a, nrow, o0, lane, zf, ze);
+    __syncthreads();
+
+    // bypass: A fragments of 16 pixels x 32 input channels from the row
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const uint16_t *col = xsb + (32 * kc + 8 * (lane >> 4)) * XP + 64 * wv + 16 * i + (lane & 15);
+        pw_u32x4 af;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) af[q] = (uint32_t)col[2 * q * XP] | ((uint32_t)col[(2 * q + 1) * XP] << 16);
+#pragma unroll
+        for (int ot = 0; ot < 4; ++ot) acc[ot][i] = pw_mma<DT>(af, wf[ot][kc], acc[ot][i]);
+      }
+
+    // bias, act, one 8-byte store of four pixels per (channel, tile)
+#pragma unroll
+    for (int ot = 0; ot < 4; ++ot) {
+      const int o = o0 + 16 * ot + (lane & 15);
+      if (o < Co) {
+        uint16_t *yr =
+            reinterpret_cast<uint16_t *>(a.y) + (((size_t)b * Co + o) * H + h) * W + 64 * wv + 4 * (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[j] = acc[ot][i][j] + bias[ot];
+            if (a.act == 1) v[j] = gelu_half(v[j]);
+          }
+          *reinterpret_cast<uint2 *>(yr + 16 * i) = make_uint2(pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3]));
+        }
+      }
+    }
+  }
+}
+
 static constexpr int kMaxJ = 128;
 static constexpr int kMaxC = 4;
 
@@ -845,6 +1043,41 @@ hipError_t launch_projection(const void *x, const void *Q1, const void *q1, cons
                                     : (al ? (const void *)fno_projection<DT_BF16, true>
                                           : (const void *)fno_projection<DT_BF16, false>);
   return hipLaunchKernel(k, grid, dim3(kPwThreads), args, 0, s);
+}
+
+
+template <int DT, int NW>
+static const void *block_rows_kernel(int KC) {
+  return KC == 1 ? (const void *)fno_block_rows<DT, NW, 1> : (const void *)fno_block_rows<DT, NW, 2>;
+}
+
+bool block_rows_supported(int dtype, int W, int Ci, int NN) {
+  return (dtype == DT_F16 || dtype == DT_BF16) && (W == 64 || W == 128 || W == 256) && Ci >= 1 && Ci <= 64 &&
+         (NN == 1 || NN == 2);
+}
+
+hipError_t launch_block_rows(const uint16_t *zg, const signed char *zexp, const void *tb, const void *x,
+                             const void *wb, const void *bias, void *y, int B, int Ci, int Co, int H, int W, int NN,
+                             int act, int dtype, hipStream_t s) {
+  if (!block_rows_supported(dtype, W, Ci, NN) || B < 1 || B > 65535 || H < 1 || Co < 1) return hipErrorInvalidValue;
+  BlockRowArgs a{zg, zexp, reinterpret_cast<const pw_u32x4 *>(tb), x, wb, bias, y, B, Ci, Co, H, NN, act};
+  void *args[] = {(void *)&a};
+  const int KC = Ci <= 32 ? 1 : 2, NW = W / 64;
+  const void *k = nullptr;
+  if (dtype == DT_F16)
+    k = NW == 1 ? block_rows_kernel<DT_F16, 1>(KC) : NW == 2 ? block_rows_kernel<DT_F16, 2>(KC) : block_rows_kernel<DT_F16, 4>(KC);
+  else
+    k = NW == 1 ? block_rows_kernel<DT_BF16, 1>(KC) : NW == 2 ? block_rows_kernel<DT_BF16, 2>(KC)
+                                                   : block_rows_kernel<DT_BF16, 4>(KC);
+  // persistent: about two workgroups per CU, rows dealt round-robin
+  int dev = 0, ncu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const long rows = (long)B * H, nob = (Co + 63) / 64;
+  if (rows > 0x7fffffffL) return hipErrorInvalidValue;
+  const long g = std::max(1L, std::min(rows, (2L * ncu + nob - 1) / nob));
+  return hipLaunchKernel(k, dim3((unsigned)g, (unsigned)nob), dim3(NW * 64), args, 0, s);
 }
 
 }  // namespace fno

@@ -78,3 +78,34 @@ def test_spectral_branch_is_added_before_gelu():
     g = np.vectorize(_gelu_scalar)
     ref = g(g(s))
     assert np.abs(got[0, 0] - ref).max() <= 1e-13
+
+
+def test_block_is_spectral_plus_pointwise():
+    # fno_block2d without act: a sinusoid the layer passes unchanged (identity
+    # spectral weights on channel 0, zero elsewhere) plus the 1x1 convolution
+    # and bias written with loops; with act, GELU of that, and a None bias is
+    # a zero bias.
+    H = W = 16
+    m1 = m2 = 4
+    hh, ww = np.meshgrid(np.arange(H), np.arange(W), indexing="ij")
+    rng = np.random.default_rng(11)
+    Ci, Co = 2, 3
+    v = np.zeros((1, Ci, H, W))
+    v[0, 0] = np.cos(2 * np.pi * (1 * hh / H + 3 * ww / W))
+    v[0, 1] = rng.standard_normal((H, W))
+    spec = np.zeros((2 * m1, m2, Ci, Co), dtype=np.complex128)
+    spec[..., 0, 0] = 1.0
+    Wb = rng.standard_normal((Co, Ci))
+    b = rng.standard_normal(Co)
+    got = oracle.fno_block2d(v, spec, Wb, b, m1, m2, act=False)
+    ref = np.zeros((1, Co, H, W))
+    for o in range(Co):
+        for h in range(H):
+            for w in range(W):
+                ref[0, o, h, w] = sum(Wb[o, i] * v[0, i, h, w] for i in range(Ci)) + b[o]
+    ref[0, 0] += v[0, 0]
+    assert np.abs(got - ref).max() <= 1e-12
+    g = np.vectorize(_gelu_scalar)
+    assert np.abs(oracle.fno_block2d(v, spec, Wb, b, m1, m2) - g(ref)).max() <= 1e-12
+    assert np.abs(oracle.fno_block2d(v, spec, Wb, None, m1, m2, act=False)
+                  - (ref - b[None, :, None, None])).max() <= 1e-12
