@@ -112,6 +112,7 @@ hipError_t axis_fwd_prepare(int MP, size_t lds) {
 }
 
 hipError_t launch_axis_fwd(const AxisArgs &a, int MP, size_t lds, hipStream_t s) {
+  FNO_BOUNDS(check_axis(a, true);)
   const void *k = axis_kernel(true, MP);
   if (!k) return hipErrorInvalidValue;
   const int CT = axis_cols(a.P);
@@ -121,6 +122,7 @@ hipError_t launch_axis_fwd(const AxisArgs &a, int MP, size_t lds, hipStream_t s)
 }
 
 hipError_t launch_axis_inv(const AxisArgs &a, int MP, hipStream_t s) {
+  FNO_BOUNDS(check_axis(a, false);)
   const void *k = axis_kernel(false, MP);
   if (!k) return hipErrorInvalidValue;
   const int CT = axis_cols(a.P);

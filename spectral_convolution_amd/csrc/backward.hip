@@ -56,6 +56,7 @@ __global__ __launch_bounds__(256) void fno_conj_transpose(const E *__restrict__ 
 }
 
 hipError_t launch_conj_transpose(const void *w, void *wh, int K, int Ci, int Co, int dtype, hipStream_t s) {
+  FNO_BOUNDS(check_conj_transpose(w, wh, K, Ci, Co, dtype);)
   const int nti = (Ci + 31) / 32, nto = (Co + 31) / 32;
   const long n = (long)K * nti * nto;
   if (n < 1 || n > 0x7fffffffL) return hipErrorInvalidValue;
@@ -236,6 +237,7 @@ static const void *gradw_kernel_t(int dtype) {
 bool gradw_supported(int K) { return (K & 1) == 0; }
 
 hipError_t launch_grad_w(const GradWArgs &a, int dtype, hipStream_t s) {
+  FNO_BOUNDS(check_grad_w(a, dtype);)
   const bool small = gradw_small_tiles(a);
   const int MB = small ? 8 : 16, CT = small ? 16 : 32;
   const void *k = small ? gradw_kernel_t<8, 16>(dtype) : gradw_kernel_t<16, 32>(dtype);

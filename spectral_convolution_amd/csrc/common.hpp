@@ -254,6 +254,7 @@ hipError_t mx_grid(bool fwd, int W, int m1, int m2, int dtype, size_t lds, int d
 hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int grid, int dtype, size_t lds, hipStream_t s,
                                bool two = false);
 hipError_t launch_plane_mx_inv(const PlaneMxInvArgs &a, int grid, int dtype, size_t lds, hipStream_t s);
+int mx_fwd_waves(int W, int m1, int m2, int dtype);
 hipError_t axis_fwd_prepare(int MP, size_t lds);
 hipError_t launch_axis_fwd(const AxisArgs &a, int MP, size_t lds, hipStream_t s);
 hipError_t launch_axis_inv(const AxisArgs &a, int MP, hipStream_t s);
@@ -294,3 +295,5 @@ constexpr int kProjMaxHidden = 128;
 constexpr int kProjMaxOut = 4;
 
 }  // namespace fno
+
+#include "bounds.hpp"

@@ -55,6 +55,7 @@ hipError_t contract_prepare(int bb, int dtype, int Co, size_t lds) {
 }
 
 hipError_t launch_contract(const ContractArgs &a, int bb, int S, int dtype, hipStream_t s) {
+  FNO_BOUNDS(check_contract(a, dtype, false);)
   const void *k = bb == 4 ? contract_kernel<4>(dtype, a.Co) : bb == 2 ? contract_kernel<2>(dtype, a.Co)
                                                            : contract_kernel<1>(dtype, a.Co);
   if (!k) return hipErrorInvalidValue;

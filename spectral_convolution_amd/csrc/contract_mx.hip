@@ -485,6 +485,7 @@ hipError_t contract_mx_prepare(int dtype, int B) {
 }
 
 hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s) {
+  FNO_BOUNDS(check_contract(a, dtype, true);)
   const int mb = cmx_modes(a.B, a.Co, a.K);
   const void *k = contract_mx_kernel(dtype, a.B, mb, a.xh16 != nullptr);
   if (!k) return hipErrorInvalidValue;

@@ -188,6 +188,7 @@ hipError_t fused_prepare(const FusedShape &f, size_t lds, int device, int *grid)
 }
 
 hipError_t launch_layer_fused(const FusedShape &f, const void *args, int grid, size_t lds, hipStream_t s) {
+  FNO_BOUNDS(check_layer_fused(f, args, grid, lds);)
   const void *k = fused_kernel(f);
   if (!k || grid < 1) return hipErrorInvalidValue;
   void *kargs[] = {const_cast<void *>(args)};

@@ -106,6 +106,7 @@ hipError_t plane_prepare(bool fwd, int MP, int rpt, int dtype, size_t lds) {
 }
 
 hipError_t launch_plane_fwd(const PlaneFwdArgs &a, int MP, int rpt, int dtype, size_t lds, hipStream_t s) {
+  FNO_BOUNDS(check_plane_fwd(a, MP, rpt, dtype, lds);)
   const void *k = plane_kernel(true, MP, rpt, dtype);
   if (!k) return hipErrorInvalidValue;
   void *args[] = {(void *)&a};
@@ -113,6 +114,7 @@ hipError_t launch_plane_fwd(const PlaneFwdArgs &a, int MP, int rpt, int dtype, s
 }
 
 hipError_t launch_plane_inv(const PlaneInvArgs &a, int MP, int rpt, int dtype, size_t lds, hipStream_t s) {
+  FNO_BOUNDS(check_plane_inv(a, MP, rpt, dtype, lds);)
   const void *k = plane_kernel(false, MP, rpt, dtype);
   if (!k) return hipErrorInvalidValue;
   void *args[] = {(void *)&a};

@@ -71,6 +71,8 @@ static FwdCfg fwd_cfg(int W, int m1, int m2, int dtype) {
   return {nw, nt >= 2 && 2 * nt >= nw ? 2 : 1};
 }
 
+int mx_fwd_waves(int W, int m1, int m2, int dtype) { return fwd_cfg(W, m1, m2, dtype).nw; }
+
 template <int DT, int KB, bool TW>
 static const void *mx_fwd_kernel(FwdCfg c) {
   if (c.nw == 8)
@@ -149,6 +151,7 @@ hipError_t mx_grid(bool fwd, int W, int m1, int m2, int dtype, size_t lds, int d
 }
 
 hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int grid, int dtype, size_t lds, hipStream_t s, bool two) {
+  FNO_BOUNDS(check_plane_mx_fwd(a, grid, dtype, lds, two);)
   const void *k = mx_kernel(true, a.W, a.m1, a.m2, dtype, two);
   if (!k || grid < 1) return hipErrorInvalidValue;
   void *args[] = {(void *)&a};
@@ -156,6 +159,7 @@ hipError_t launch_plane_mx_fwd(const PlaneMxFwdArgs &a, int grid, int dtype, siz
 }
 
 hipError_t launch_plane_mx_inv(const PlaneMxInvArgs &a, int grid, int dtype, size_t lds, hipStream_t s) {
+  FNO_BOUNDS(check_plane_mx_inv(a, grid, dtype, lds, false);)
   const void *k = mx_kernel(false, a.W, a.m1, a.m2, dtype, false, a.in16 != nullptr);
   if (!k || grid < 1) return hipErrorInvalidValue;
   void *args[] = {(void *)&a};
@@ -194,6 +198,7 @@ hipError_t mx_cols_prepare(int m1, int m2, int dtype, size_t lds, int device, in
 }
 
 hipError_t launch_plane_mx_cols(const PlaneMxInvArgs &a, int grid, int dtype, size_t lds, hipStream_t s) {
+  FNO_BOUNDS(check_plane_mx_inv(a, grid, dtype, lds, true);)
   const void *k = cols_kernel(a.m1, a.m2, dtype, a.in16 != nullptr);
   if (!k || grid < 1 || !a.zg || !a.zexp || a.zco < 1) return hipErrorInvalidValue;
   void *args[] = {(void *)&a};

@@ -983,6 +983,7 @@ __global__ __launch_bounds__(kPwThreads) void fno_lift_fold(FoldArgs a) {
 hipError_t launch_lift_fold(const void *P, const void *p, const void *w, const void *Wb, const void *b, void *wf,
                             void *af, void *bf, int K, int J, int C, int dtype, hipStream_t s) {
   if (C * J > kFoldP) return hipErrorInvalidValue;
+  FNO_BOUNDS(check_lift_fold(P, p, w, Wb, b, wf, af, bf, K, J, C, dtype);)
   FoldArgs a{P, p, w, Wb, b, wf, af, bf, K, J, C};
   void *args[] = {(void *)&a};
   const long total = (long)K * C + C;
@@ -995,6 +996,7 @@ hipError_t launch_lift_fold(const void *P, const void *p, const void *w, const v
 
 hipError_t launch_channel_mix(const void *x, const void *A, const void *bias, const void *add, void *y, int B,
                               int I, int O, long P, int act, int dtype, hipStream_t s) {
+  FNO_BOUNDS(check_channel_mix(x, A, bias, add, y, B, I, O, P, dtype);)
   MixArgs a{x, A, bias, add, y, B, I, O, P, act};
   void *args[] = {(void *)&a};
   if (dtype != DT_F32 && (P & 7) == 0 && I <= 64) {
@@ -1022,6 +1024,7 @@ hipError_t launch_channel_mix(const void *x, const void *A, const void *bias, co
 
 hipError_t launch_projection(const void *x, const void *Q1, const void *q1, const void *Q2, const void *q2, void *y,
                              int B, int I, int J, int C, long P, int dtype, hipStream_t s) {
+  FNO_BOUNDS(check_projection(x, Q1, q1, Q2, q2, y, B, I, J, C, P, dtype);)
   ProjArgs a{x, Q1, q1, Q2, q2, y, B, I, J, C, P};
   void *args[] = {(void *)&a};
   if (dtype != DT_F32 && (P & 7) == 0 && I <= 64 && J <= kMaxJ && C <= kMaxC) {
@@ -1060,6 +1063,7 @@ hipError_t launch_block_rows(const uint16_t *zg, const signed char *zexp, const 
                              const void *wb, const void *bias, void *y, int B, int Ci, int Co, int H, int W, int NN,
                              int act, int dtype, hipStream_t s) {
   if (!block_rows_supported(dtype, W, Ci, NN) || B < 1 || B > 65535 || H < 1 || Co < 1) return hipErrorInvalidValue;
+  FNO_BOUNDS(check_block_rows(zg, zexp, tb, x, wb, bias, y, B, Ci, Co, H, W, NN, dtype);)
   BlockRowArgs a{zg, zexp, reinterpret_cast<const pw_u32x4 *>(tb), x, wb, bias, y, B, Ci, Co, H, NN, act};
   void *args[] = {(void *)&a};
   const int KC = Ci <= 32 ? 1 : 2, NW = W / 64;

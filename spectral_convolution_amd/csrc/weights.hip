@@ -70,6 +70,7 @@ struct pair16 {
 };
 
 hipError_t launch_weights_repack(const WeightsArgs &a, int dtype, hipStream_t s) {
+  FNO_BOUNDS(check_weights_repack(a, dtype);)
   if (a.n < 1) return hipSuccess;
   const long blocks = (a.n + 255) / 256;
   const dim3 grid((unsigned)(blocks < 65536 ? blocks : 65536));
