@@ -406,7 +406,7 @@ def _roofline(cfg, dtype, kernels):
             "ms_per_launch": dom["ms"], "achieved_with_exchange": dom["gbps_with_exchange"]}
 
 
-def measure(cfg, dtype, steps, warmup, settle_ms=SETTLE_MS, per_kernel=True):
+def measure(cfg, dtype, steps, warmup, settle_ms=SETTLE_MS, per_kernel=True, shapes=("fused", "separate")):
     lay = Layer(cfg, dtype)
     try:
         ms = _time_loop(lay.step, steps, warmup, lay.stream, settle_ms)
@@ -422,10 +422,12 @@ def measure(cfg, dtype, steps, warmup, settle_ms=SETTLE_MS, per_kernel=True):
         res["hot_single_set_layers_per_s"] = 1000.0 / hot
         shape = lay.fno.fno_plan_get_launch_shape(lay.plan)
         res["launch_shape"] = shape
+        res["half_exchange"] = lay.fno.fno_plan_spectra_format(lay.plan) == 1
+        res["arithmetic"] = arithmetic(dtype, res["half_exchange"])
         # ablation: the layer in each launch shape the plan has (one
         # cooperative launch, or the three stand-alone kernels)
         res["launch_shapes"] = {}
-        for sh in ("fused", "separate"):
+        for sh in shapes:
             if not lay.set_shape(sh):
                 continue
             t = _time_loop(lay.step, steps, warmup, lay.stream, settle_ms)
@@ -435,7 +437,7 @@ def measure(cfg, dtype, steps, warmup, settle_ms=SETTLE_MS, per_kernel=True):
             # every kernel of both shapes alone; the roofline takes the
             # dominant kernel of the shape the layer runs in
             res["kernels"] = []
-            for sh in ("separate", "fused"):
+            for sh in [x for x in ("separate", "fused") if x in shapes]:
                 if not lay.set_shape(sh):
                     continue
                 kms = _kernel_times(lay, steps, max(2, warmup // 4), settle_ms)
@@ -465,12 +467,14 @@ def measured_traffic(kernel, cfg_name, dtype):
         return None
     text = open(path).read()
     m_b = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
-    m_s = re.search(r"^source:\s*(\S+)\s+sha256\s+([0-9a-f]{64})", text, re.M)
-    if not (m_b and m_s):
+    srcs = re.findall(r"^source:\s*(\S+)\s+sha256\s+([0-9a-f]{64})", text, re.M)
+    if not (m_b and srcs):
         return None
-    src = os.path.join(ROOT, m_s.group(1))
-    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != m_s.group(2):
-        return None
+    # every source the kernel is compiled from must be unchanged
+    for rel, digest in srcs:
+        src = os.path.join(ROOT, rel)
+        if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != digest:
+            return None
     return int(m_b.group(1))
 
 
@@ -519,14 +523,25 @@ def cpu_baseline(cfg, dtype, budget_s=8.0):
             "gbps_minimal_bytes": cfg.minimal_bytes(dtype) * rate / 1e9}
 
 
-ARITHMETIC = {
-    "f32": "f32 storage; transforms on f16 hi+lo split MFMA operands (about 22 significant bits), "
-           "contraction on f32 MFMA, f32 accumulation throughout",
-    "f16": "f16 storage; transforms on f16 MFMA operands scaled by powers of two, contraction on bf16 "
-           "hi+lo split MFMA operands (f32-level products), f32 accumulation throughout",
-    "bf16": "bf16 storage; transforms on f16 MFMA operands scaled by powers of two, contraction on bf16 "
-            "hi+lo split MFMA operands (f32-level products), f32 accumulation throughout",
-}
+def arithmetic(dtype, half_exchange):
+    """What the layer multiplies in, by storage dtype and spectra exchange
+    format (fp16 / bf16 plans from batch 16 exchange fp16 spectra and run the
+    matrix-core contraction; smaller batches keep complex fp32 spectra and
+    the fp32 contraction)."""
+    if dtype == "f32":
+        return ("f32 storage; transforms on f16 hi+lo split MFMA operands (about 22 significant bits), "
+                "contraction on f32 MFMA, f32 accumulation throughout")
+    head = (f"{dtype} storage; transforms on f16 MFMA operands scaled by powers of two, ")
+    if not half_exchange:
+        return head + "spectra exchanged as complex f32, contraction on f32 MFMA, f32 accumulation throughout"
+    if dtype == "f16":
+        return head + ("spectra exchanged as f16 pairs with power-of-two exponents, contraction on f16 MFMA "
+                       "operands (spectra at one power-of-two scale per batch row, weights as stored), "
+                       "f32 accumulation throughout")
+    return head + ("spectra exchanged as f16 pairs with power-of-two exponents, contraction on bf16 hi+lo split "
+                   "MFMA operands (exact for f16 spectra and bf16 weights), f32 accumulation throughout")
+
+
 DTYPE_LABEL = {"f32": "f32 (f16 hi+lo MFMA, f32 acc)", "f16": "f16 (MFMA, f32 acc)",
                "bf16": "bf16 storage (f16 MFMA, f32 acc)"}
 
@@ -564,6 +579,8 @@ def main():
     ap.add_argument("--model-only", action="store_true", help="only time the full FNO2d forward (profiling runs)")
     ap.add_argument("--backward-only", action="store_true",
                     help="only time the backward pass of --config/--dtype (profiling runs)")
+    ap.add_argument("--separate-only", action="store_true",
+                    help="time only the three-launch shape (profiling runs: no cooperative launch)")
     ap.add_argument("--copy-only", type=int, default=0, metavar="BYTES",
                     help="only time a device-to-device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -589,13 +606,14 @@ def main():
     if args.backward_only:
         print(json.dumps({"backward": [measure_backward(cfg, dtype, args.steps, args.warmup, settle)]}))
         return
-    main_res = measure(cfg, dtype, args.steps, args.warmup, settle)
+    shapes = ("separate",) if args.separate_only else ("fused", "separate")
+    main_res = measure(cfg, dtype, args.steps, args.warmup, settle, shapes=shapes)
     print("[bench] " + _summary(main_res), file=sys.stderr, flush=True)
     out = {
         "metric": METRIC, "value": main_res["layers_per_s"], "unit": "layers/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": main_res["ms_per_layer"], "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": DTYPE_LABEL[dtype], "arithmetic": ARITHMETIC[dtype],
+        "vs_baseline": None, "dtype": DTYPE_LABEL[dtype], "arithmetic": main_res["arithmetic"],
         "data": "synthetic (seeded Gaussian random fields; random weights)",
         "config": {"workload": cfg.description, "name": cfg.name, "batch": cfg.batch,
                    "c_in": cfg.c_in, "c_out": cfg.c_out, "grid": list(cfg.grid),
@@ -613,7 +631,7 @@ def main():
         for name, dt in METRIC_CONFIGS + [("c0", "f32")]:
             if (name, dt) in results:
                 continue
-            r = measure(wl.CONFIGS[name], dt, args.steps, args.warmup, settle)
+            r = measure(wl.CONFIGS[name], dt, args.steps, args.warmup, settle, shapes=shapes)
             results[(name, dt)] = r
             print("[bench] " + _summary(r), file=sys.stderr, flush=True)
     cpu = {}

@@ -95,3 +95,21 @@ def test_no_gpu_fails_loudly():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert r.stdout.strip() == ""
+
+
+def test_measured_traffic_needs_every_source_unchanged(tmp_path, monkeypatch):
+    # a counter summary counts only while every source it names still has the
+    # recorded digest
+    import hashlib
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "a.hip").write_text("kernel a\n")
+    (tmp_path / "b.hpp").write_text("header b\n")
+    dig = {n: hashlib.sha256((tmp_path / n).read_bytes()).hexdigest() for n in ("a.hip", "b.hpp")}
+    (tmp_path / "profiles" / "k_c9_f16_traffic.md").write_text(
+        "# HBM traffic\n\ntraffic_bytes_per_launch: 1234\n"
+        f"source: a.hip sha256 {dig['a.hip']}\nsource: b.hpp sha256 {dig['b.hpp']}\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic("k", "c9", "f16") == 1234
+    assert bench.measured_traffic("k", "c9", "f32") is None
+    (tmp_path / "b.hpp").write_text("header b, changed\n")
+    assert bench.measured_traffic("k", "c9", "f16") is None
