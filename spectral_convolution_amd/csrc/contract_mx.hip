@@ -402,9 +402,15 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<D
           const float f = pow2f(sx) * pow2f(-rs);
           uint32_t *dst = a.yh16 + ((size_t)b * Co + o) * K + mode;
           const uint2 h0 = make_uint2(f16x2_rne(p0.x * f, p0.y * f), f16x2_rne(p0.z * f, p0.w * f));
-          *reinterpret_cast<uint2 *>(dst) = h0;
-          if (mode + 2 < K)
-            *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(f16x2_rne(p1.x * f, p1.y * f), f16x2_rne(p1.z * f, p1.w * f));
+          const uint2 h1 = make_uint2(f16x2_rne(p1.x * f, p1.y * f), f16x2_rne(p1.z * f, p1.w * f));
+          if ((K & 3) == 0) {
+            // whole groups, 16-byte aligned (mode and every row start are
+            // multiples of 4): one store
+            *reinterpret_cast<uint4 *>(dst) = make_uint4(h0.x, h0.y, h1.x, h1.y);
+          } else {
+            *reinterpret_cast<uint2 *>(dst) = h0;
+            if (mode + 2 < K) *reinterpret_cast<uint2 *>(dst + 2) = h1;
+          }
           a.yexp[((size_t)b * Co + o) * KQ + (mode >> 2)] = (signed char)sx;
         }
       }
