@@ -32,8 +32,10 @@
  *
  * Ownership. The caller owns x, w and y and keeps them alive until the work
  * queued on `stream` has finished. The plan owns its twiddle tables and its
- * spectra workspace and a buffer for the conjugate-transposed weights of the
- * backward pass (allocated by fno_plan_create, freed by fno_plan_destroy).
+ * spectra workspace and, for fp16 / bf16 plans and fp32 plans with an odd
+ * c_out, a buffer for the conjugate-transposed weights of the backward pass
+ * (fp32 plans with an even c_out read w directly in the backward's adjoint
+ * contraction); all allocated by fno_plan_create, freed by fno_plan_destroy.
  * Execution calls allocate nothing.
  *
  * Execution calls are asynchronous on `stream` (a hipStream_t; NULL is the

@@ -42,6 +42,7 @@ void check_plane_mx_fwd(const PlaneMxFwdArgs &a, int grid, int dtype, size_t lds
 void check_plane_mx_inv(const PlaneMxInvArgs &a, int grid, int dtype, size_t lds, bool cols);
 void check_axis(const AxisArgs &a, bool fwd);
 void check_contract(const ContractArgs &a, int dtype, bool mx);
+void check_contract_adj(const ContractArgs &a, int bb, int S, size_t wave_bytes, size_t stage_bytes);
 void check_grad_w(const GradWArgs &a, int dtype);
 void check_conj_transpose(const void *w, const void *wh, int K, int Ci, int Co, int dtype);
 void check_weights_repack(const WeightsArgs &a, int dtype);

@@ -198,6 +198,17 @@ void check_contract(const ContractArgs &a, int dtype, bool mx) {
   else c.need("the half exchange only on the matrix-core contraction", a.xh16 == nullptr);
 }
 
+void check_contract_adj(const ContractArgs &a, int bb, int S, size_t wave_bytes, size_t stage_bytes) {
+  const Ctx c{"fno_contract_adj"};
+  spans_contract(c, a, DT_F32);
+  c.need("fp32 spectra both ways", a.xh16 == nullptr && a.yh16 == nullptr);
+  c.need("even reduction count (16-byte pairs of W)", a.Ci >= 2 && a.Ci % 2 == 0);
+  c.need("batch tile of 4 or 8 rows", bb == 1 || bb == 2);
+  c.need("S divides the 16 BB partial-sum pairs", S == 1 || S == 2 || S == 4 || S == 8);
+  c.need("a wave's LDS share holds its staging region and its partial sums",
+         wave_bytes >= stage_bytes && wave_bytes >= (size_t)bb * 16 * 2 * 64 * 4);
+}
+
 void check_grad_w(const GradWArgs &a, int dtype) {
   const Ctx c{"fno_grad_w"};
   const size_t K = (size_t)a.K;

@@ -263,6 +263,12 @@ int contract_pick_split(int B, int Ci, int Co, int K, int bb);
 size_t contract_lds_bytes(int bb, int S);
 hipError_t contract_prepare(int bb, int dtype, int Co, size_t lds);
 hipError_t launch_contract(const ContractArgs &a, int bb, int S, int dtype, hipStream_t s);
+// adjoint contraction straight from W (fp32): args as the adjoint's (Ci =
+// the layer's Co, the reduction; Co = the layer's Ci), w in the forward layout
+bool contract_adj_supported(int dtype, int c_out, int bb);
+size_t contract_adj_lds_bytes(int bb, int S);
+hipError_t contract_adj_prepare(int bb, int S);
+hipError_t launch_contract_adj(const ContractArgs &a, int bb, int S, hipStream_t s);
 bool contract_mx_supported(int dtype, int Co, int K);
 long contract_mx_workgroups(int B, int Co, int K);
 size_t contract_mx_lds_bytes(int dtype, int B);

@@ -198,3 +198,195 @@ __device__ __forceinline__ void contract_tile(const ContractArgs &a, int bx, int
 }
 
 }  // namespace fno
+
+namespace fno {
+
+// ------------------------------------------------ adjoint straight from W
+//
+// The adjoint contraction of the backward pass, Gx[k] (B x Ci) = G[k] (B x
+// Co) * W[k]^H, with W read in its forward layout [k][i][o] instead of a
+// conjugate-transposed copy. The reduction now runs over o, the contiguous
+// index of W, while the MFMA B operand wants output channels i across the
+// lanes at one o. Each wave therefore stages W through its own LDS region in
+// chunks of 16 reduction steps x 4 of its 16 output channels x its 16 modes
+// (8 KB): every (mode, channel) row piece is 16 steps = 128 contiguous bytes,
+// read by 8 lanes, so the loads move whole cache lines (smaller pieces,
+// which revisit each line, measured slower). The pieces are conjugated and
+// written transposed as [mode][step][channel]. Lane (mode, n) holds output
+// channels n + 4 ob (ob = 0..3); chunk c of a step block carries channels
+// 4 c .. 4 c + 3, i.e. every lane's ob = c, read as one 8-byte word per
+// step. The four chunks of a step block share the G operand. Waves never
+// share a region, so no workgroup barrier is needed until the partial sums
+// of a split reduction meet. The reduction of wave s covers pairs of steps
+// [P s / S, P (s + 1) / S), P = Co / 2 (Co even), so step blocks start even
+// and 16-byte pieces stay aligned; past the end of its range a wave re-reads
+// the final pair (in range) and skips those steps.
+struct AdjL {
+  static constexpr int RC = 16;        // reduction steps per chunk
+  static constexpr int P = 5;          // complex per (mode, step) row: 4 channels + 1 pad (odd: the
+                                       // transposing 8-byte stores of 16 lanes hit 32 distinct banks)
+  static constexpr int Q = 16 * P + 4;  // complex per mode block (= 4 mod 16: the 8-byte reads of four
+                                        // neighbouring modes hit distinct banks)
+  static constexpr int WAVE = 16 * Q;  // complex per wave region
+  static constexpr int NI = 8;         // load instructions per chunk (8 rows of 128 bytes each)
+};
+
+template <int BB>
+__device__ __forceinline__ void contract_tile_adj(const ContractArgs &a, int bx, int by, int bz, int S,
+                                                  float2 *stg) {
+  const int lane = threadIdx.x & 63, s = threadIdx.x >> 6;
+  const int blk = lane >> 2, nn = lane & 3;
+  // in the adjoint's terms: Cr reduction channels (the layer's Co, the last
+  // index of W), No output channels (the layer's Ci, the middle index)
+  const int K = a.K, Cr = a.Ci, No = a.Co, B = a.B;
+  const int mode = bx * 16 + blk;
+  const bool mode_ok = mode < K;
+  const int b0 = by * 4 * BB, o0 = bz * 16;
+  const int Pp = Cr >> 1;
+  const int r0s = 2 * ((Pp * s) / S), r1 = 2 * ((Pp * (s + 1)) / S);
+  float2 *Wl = stg + (size_t)s * AdjL::WAVE;
+  const float2 *w = reinterpret_cast<const float2 *>(a.w);
+
+  // load instruction j: rows 8 j .. 8 j + 7 = (mode q = row / 4, channel
+  // 4 c + row % 4), lane: row 8 j + lane / 8, steps r + 2 (lane % 8) and the
+  // next one (clamped to the last pair)
+  const int lp = lane & 7, lrow = lane >> 3;
+  auto fetch = [&](int r, int c, float4 (&v)[AdjL::NI]) {
+    const int rr = min(r + 2 * lp, Cr - 2);
+    const int o = o0 + 4 * c + (lrow & 3);
+#pragma unroll
+    for (int j = 0; j < AdjL::NI; ++j) {
+      const int m = bx * 16 + 2 * j + (lrow >> 2);
+      const bool ok = m < K && o < No;
+      v[j] = *reinterpret_cast<const float4 *>(w + (ok ? ((size_t)m * No + o) * Cr + rr : 0));
+    }
+  };
+  auto put = [&](const float4 (&v)[AdjL::NI]) {
+#pragma unroll
+    for (int j = 0; j < AdjL::NI; ++j) {
+      float2 *d = Wl + (2 * j + (lrow >> 2)) * AdjL::Q + (2 * lp) * AdjL::P + (lrow & 3);
+      d[0] = make_float2(v[j].x, -v[j].y);
+      d[AdjL::P] = make_float2(v[j].z, -v[j].w);
+    }
+  };
+  // the spectra of G for the steps of a block (A operand: batch rows)
+  auto gfetch = [&](int r, float2 (&g)[AdjL::RC][BB]) {
+#pragma unroll
+    for (int t = 0; t < AdjL::RC; ++t) {
+      const int rc = min(r + t, Cr - 1);
+#pragma unroll
+      for (int bb = 0; bb < BB; ++bb) {
+        const int b = b0 + 4 * bb + nn;
+        const bool ok = mode_ok && b < B;
+        g[t][bb] = a.xh[ok ? ((size_t)b * Cr + rc) * K + mode : 0];
+      }
+    }
+  };
+
+  v4f accr[BB][4], acci[BB][4];
+#pragma unroll
+  for (int bb = 0; bb < BB; ++bb)
+#pragma unroll
+    for (int ob = 0; ob < 4; ++ob) {
+      accr[bb][ob] = v4f{0.f, 0.f, 0.f, 0.f};
+      acci[bb][ob] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+  // products of the staged chunk c (first step r; steps past r1 skipped)
+  auto compute = [&](int r, int c, const float2 (&g)[AdjL::RC][BB]) {
+    const int nst = min(AdjL::RC, r1 - r);
+#pragma unroll
+    for (int t = 0; t < AdjL::RC; ++t) {
+      if (t < nst) {
+        const float2 u = Wl[blk * AdjL::Q + t * AdjL::P + nn];
+#pragma unroll
+        for (int bb = 0; bb < BB; ++bb) {
+          const float ar = g[t][bb].x, ai = g[t][bb].y, an = -ai;
+          v4f &cr = accr[bb][c], &ci = acci[bb][c];
+          cr = __builtin_amdgcn_mfma_f32_4x4x1f32(ar, u.x, cr, 0, 0, 0);
+          cr = __builtin_amdgcn_mfma_f32_4x4x1f32(an, u.y, cr, 0, 0, 0);
+          ci = __builtin_amdgcn_mfma_f32_4x4x1f32(ar, u.y, ci, 0, 0, 0);
+          ci = __builtin_amdgcn_mfma_f32_4x4x1f32(ai, u.x, ci, 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  if (r0s < r1) {
+    // chunks (r, c) in the order (r0s, 0..3), (r0s + 16, 0..3), ...; every
+    // W fetch is unconditional (clamped in range) so the compiler's waits
+    // count the loads in flight exactly. G of a step block is requested
+    // with the block's second chunk, while that chunk's W is in flight.
+    float4 wv[AdjL::NI];
+    float2 g[AdjL::RC][BB];
+    fetch(r0s, 0, wv);
+    for (int r0 = r0s; r0 < r1; r0 += AdjL::RC) {
+      const int rn = r0 + AdjL::RC < r1 ? r0 + AdjL::RC : r0;
+      put(wv);
+      fetch(r0, 1, wv);
+      gfetch(r0, g);
+      compute(r0, 0, g);
+      put(wv);
+      fetch(r0, 2, wv);
+      compute(r0, 1, g);
+      put(wv);
+      fetch(r0, 3, wv);
+      compute(r0, 2, g);
+      put(wv);
+      fetch(rn, 0, wv);
+      compute(r0, 3, g);
+    }
+  }
+
+  // accumulator register j of lane l: mode, batch row b0 + 4 bb + j, output
+  // channel o0 + n + 4 ob
+  if (S == 1) {
+    if (!mode_ok) return;
+#pragma unroll
+    for (int bb = 0; bb < BB; ++bb)
+#pragma unroll
+      for (int ob = 0; ob < 4; ++ob) {
+        const int o = o0 + nn + 4 * ob;
+        if (o >= No) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int b = b0 + 4 * bb + j;
+          if (b < B) a.yh[((size_t)b * No + o) * K + mode] = make_float2(accr[bb][ob][j], acci[bb][ob][j]);
+        }
+      }
+    return;
+  }
+  // split reduction: every wave's partial sums go to LDS (the staging
+  // regions, once every wave is done with its own), then wave s adds up
+  // pairs [s NP / S, (s + 1) NP / S) over the waves in wave order
+  constexpr int NP = BB * 16;
+  float *red = reinterpret_cast<float *>(stg);
+  __syncthreads();
+  {
+    float *dst = red + (size_t)s * NP * 2 * 64 + lane;
+#pragma unroll
+    for (int bb = 0; bb < BB; ++bb)
+#pragma unroll
+      for (int ob = 0; ob < 4; ++ob)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int q = (bb * 4 + ob) * 4 + j;
+          dst[(2 * q) * 64] = accr[bb][ob][j];
+          dst[(2 * q + 1) * 64] = acci[bb][ob][j];
+        }
+  }
+  __syncthreads();
+  if (!mode_ok) return;
+  const int per = NP / S;
+  for (int q = s * per; q < (s + 1) * per; ++q) {
+    float re = 0.f, im = 0.f;
+    for (int wq = 0; wq < S; ++wq) {
+      re += red[((size_t)wq * NP * 2 + 2 * q) * 64 + lane];
+      im += red[((size_t)wq * NP * 2 + 2 * q + 1) * 64 + lane];
+    }
+    const int j = q & 3, ob = (q >> 2) & 3, bb = q >> 4;
+    const int o = o0 + nn + 4 * ob, b = b0 + 4 * bb + j;
+    if (o < No && b < B) a.yh[((size_t)b * No + o) * K + mode] = make_float2(re, im);
+  }
+}
+
+}  // namespace fno

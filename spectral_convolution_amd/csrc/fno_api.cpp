@@ -244,6 +244,9 @@ struct fno_plan_s {
   // over Co channels, inverse over Ci)
   int bb_a = 1, split_a = 1;
   bool cmx_a = false;
+  // fp32 plans: the adjoint contraction reads W in its forward layout (no
+  // conjugate-transposed copy, no W^H buffer)
+  bool adj_w = false;
   int ppw_fg = 1, ppw_ib = 1;
   size_t lds_fg = 0, lds_ib = 0;
   int mx_grid_fg = 0, mx_grid_ib = 0;
@@ -377,6 +380,7 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
   p.split_a = contract_pick_split(batch, c_out, c_in, p.K, p.bb_a);
   p.cmx_a = contract_mx_supported((int)dtype, c_in, p.K) && contract_mx_workgroups(batch, c_in, p.K) >= 256 &&
             batch >= 16;
+  p.adj_w = !p.cmx_a && contract_adj_supported((int)dtype, c_out, p.bb_a);
   p.ppw_fg = plane_ppw(true, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_i);
   p.ppw_ib = plane_ppw(false, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_f);
   p.lds_fg = p.mx ? p.lds_fwd : plane_fwd_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP, p.ppw_fg);
@@ -488,7 +492,7 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   const size_t o_xh = off; off += al(n_xh * sizeof(float2));
   const size_t o_yh = off; off += al(n_yh * sizeof(float2));
   const size_t o_t = off; off += al(n_t * sizeof(float2));
-  const size_t o_wh = off; off += al((size_t)p->K * p->Ci * p->Co * 2 * (p->dtype == FNO_F32 ? 4 : 2));
+  const size_t o_wh = off; off += al(p->adj_w ? 0 : (size_t)p->K * p->Ci * p->Co * 2 * (p->dtype == FNO_F32 ? 4 : 2));
   const size_t o_bar = off; off += al(sizeof(FusedBarrier));
   const size_t o_xe = off; off += al(p->hx ? (size_t)p->B * p->Ci * sizeof(int) : 0);
   const size_t o_ye = off; off += al(p->hx ? (size_t)p->B * p->Co * ((p->K + 3) / 4) : 0);
@@ -527,7 +531,7 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   p->xh = (float2 *)(base + o_xh);
   p->yh = (float2 *)(base + o_yh);
   p->tbuf = n_t ? (float2 *)(base + o_t) : nullptr;
-  p->wh = base + o_wh;
+  p->wh = p->adj_w ? nullptr : base + o_wh;
   p->bar = (FusedBarrier *)(base + o_bar);
   p->xe = p->hx ? (int *)(base + o_xe) : nullptr;
   p->ye = p->hx ? (signed char *)(base + o_ye) : nullptr;
@@ -584,6 +588,7 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   if (e == hipSuccess) e = p->cmx ? contract_mx_prepare(p->dtype, p->B) : contract_prepare(p->bb, p->dtype, p->Co, lds_c);
   if (e == hipSuccess)
     e = p->cmx_a ? contract_mx_prepare(p->dtype, p->B) : contract_prepare(p->bb_a, p->dtype, p->Ci, lds_c);
+  if (e == hipSuccess && p->adj_w) e = contract_adj_prepare(p->bb_a, p->split_a);
   if (e == hipSuccess && p->fused_ok) {
     // the largest co-resident grid, trimmed to the most work units of a phase
     int cap = 0;
@@ -978,7 +983,8 @@ static size_t carve(fno_plan_t p, unsigned char *base, Bufs *b) {
 
 // Gradients: every launch is stream-ordered on `stream`; the spectra
 // workspace holds forward(x) and forward(g), then the adjoint-contracted
-// spectra; wh holds W^H.
+// spectra; wh holds W^H (plans whose adjoint contraction reads W directly
+// have none).
 static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const void *w, const void *gy, void *gx,
                                   void *gw, void *stream) {
   if (!p || p->ndim != ndim) return FNO_ERR_INVALID_ARG;
@@ -1032,8 +1038,13 @@ static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const v
     step(launch_grad_w(a, p->dtype, s));
   }
   if (gx) {
-    if (e == hipSuccess) step(launch_conj_transpose(w, p->wh, p->K, p->Ci, p->Co, p->dtype, s));
-    if (e == hipSuccess) step(contract_launch(p, b, p->yh, p->wh, p->xh, true, s));
+    if (p->adj_w) {
+      if (e == hipSuccess)
+        step(launch_contract_adj(contract_args(p, b, p->yh, w, p->xh, true, false), p->bb_a, p->split_a, s));
+    } else {
+      if (e == hipSuccess) step(launch_conj_transpose(w, p->wh, p->K, p->Ci, p->Co, p->dtype, s));
+      if (e == hipSuccess) step(contract_launch(p, b, p->yh, p->wh, p->xh, true, s));
+    }
     if (d3 && e == hipSuccess) step(inv_axis_launch(p, b, p->xh, p->Ci, s));
     if (e == hipSuccess) step(inv_plane_launch(p, b, p->xh, p->Ci, gx, s));
   }

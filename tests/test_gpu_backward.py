@@ -80,6 +80,14 @@ SMALL = [
     # weight-gradient tiles: wide batch split over waves, channel tails
     ("gw-split", _cfg("r", 2, 64, 6, 10, (64, 64), (4, 6), "uniform"), "f32"),
     ("gw-ib4", _cfg("r", 2, 4, 48, 40, (64, 64), (20, 28), "uniform"), "f32"),
+    # fp32 adjoint contraction reading W directly: the reduction split over
+    # two waves with partial step blocks and a partial output tile; over
+    # eight waves with partial mode, output and batch tiles. Odd c_out, or
+    # an adjoint with 8-row batch tiles, keeps the transposed copy of W
+    # (rag2d-a, rag3d-a; adj-wh-bb2).
+    ("adj-w-s2", _cfg("r", 2, 8, 64, 26, (64, 64), (32, 32), "uniform"), "f32"),
+    ("adj-w-s8", _cfg("r", 2, 3, 20, 34, (64, 64), (5, 7), "uniform"), "f32"),
+    ("adj-wh-bb2", _cfg("r", 2, 12, 72, 26, (64, 64), (32, 32), "uniform"), "f32"),
 ]
 
 
