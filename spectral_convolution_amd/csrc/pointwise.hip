@@ -101,20 +101,26 @@ __device__ __forceinline__ float gelu(float v) { return 0.5f * v * (1.0f + erff(
 
 // GELU for the half-precision kernels, whose outputs are rounded to 11 (fp16)
 // or 8 (bf16) significant bits: erf from Abramowitz & Stegun, Handbook of
-// Mathematical Functions, formula 7.1.26, erf(x) = 1 - t (a1 + t (a2 + t (a3 +
-// t (a4 + t a5)))) exp(-x^2), t = 1 / (1 + p x), x >= 0, absolute error below
-// 1.5e-7; odd symmetry for x < 0. One reciprocal and one exp2 on the
-// transcendental unit instead of a full-precision erf.
+// Mathematical Functions, formula 7.1.28, erf(x) = 1 - (1 + a1 x + ... +
+// a6 x^6)^-16 for x >= 0 (absolute error below 3e-7; evaluated in fp32 it
+// stays below 2e-6), odd symmetry for x < 0. With r = 1 - erf(|v| / sqrt 2),
+// GELU(v) = max(v, 0) - |v| r / 2. One reciprocal on the transcendental
+// unit; formula 7.1.26 needs an exponential as well, which made the
+// projection (128 hidden GELUs per pixel) 21 us slower at B = 20, 256^2.
 __device__ __forceinline__ float gelu_half(float v) {
   const float x = fabsf(v) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
-  float q = fmaf(1.061405429f, t, -1.453152027f);
-  q = fmaf(q, t, 1.421413741f);
-  q = fmaf(q, t, -0.284496736f);
-  q = fmaf(q, t, 0.254829592f);
-  const float e = __builtin_amdgcn_exp2f(-x * x * 1.4426950408889634f);  // exp(-x^2)
-  const float erfx = fmaf(-q * t, e, 1.0f);
-  return 0.5f * v * (1.0f + copysignf(erfx, v));
+  float p = fmaf(0.0000430638f, x, 0.0002765672f);
+  p = fmaf(p, x, 0.0001520143f);
+  p = fmaf(p, x, 0.0092705272f);
+  p = fmaf(p, x, 0.0422820123f);
+  p = fmaf(p, x, 0.0705230784f);
+  p = fmaf(p, x, 1.0f);
+  p = p * p;  // ^16 by four squarings; overflows to inf for large x, so r = 0
+  p = p * p;
+  p = p * p;
+  p = p * p;
+  const float r = __builtin_amdgcn_rcpf(p);
+  return fmaf(-0.5f * fabsf(v), r, fmaxf(v, 0.0f));
 }
 
 static constexpr int kPwThreads = 256;
