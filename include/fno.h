@@ -67,11 +67,15 @@ typedef struct fno_plan_s *fno_plan_t;
  *   FNO_F16, FNO_BF16  transforms: fp16 matrix-core products of inputs,
  *             intermediate row / column results and twiddles, each scaled by
  *             a power of two chosen from a bound so no fp16 operand overflows
- *             or loses precision to the subnormal range; contraction: bf16
- *             matrix-core products of hi + lo parts (exact products of the
- *             exchanged spectra and the weights); 2D layers on 64..256-wide
- *             planes with batch >= 16 exchange the spectra as fp16 with
- *             power-of-two exponents, others as complex fp32.
+ *             or loses precision to the subnormal range. 2D layers on
+ *             64..256-wide planes with batch >= 16 exchange the spectra as
+ *             fp16 with power-of-two exponents and contract them on matrix
+ *             cores: fp16 products of the spectra (brought to one
+ *             power-of-two scale per batch row) and fp16 weights as stored,
+ *             or bf16 hi + lo products for bf16 weights (exact). Other
+ *             layers exchange complex fp32 spectra and contract them with
+ *             bf16 hi + lo matrix-core products (batch >= 16) or fp32
+ *             matrix-core products.
  * Planes below 64 rows or columns take register FFTs in fp32 instead of
  * matrix-core transforms. */
 typedef enum { FNO_F32 = 0, FNO_F16 = 1, FNO_BF16 = 2 } fno_dtype_t;

@@ -1,5 +1,6 @@
 // contract.hip - the per-mode contraction on fp32 matrix cores as a
-// stand-alone kernel (one output tile per workgroup) and its launcher.
+// stand-alone kernel (one output tile per workgroup), the backward's adjoint
+// contraction that reads W in its forward layout, and their launchers.
 
 #include "contract.hpp"
 
