@@ -120,6 +120,55 @@ __device__ __forceinline__ void gw_fetch(const float2 *src, int nc, int K, int B
   }
 }
 
+// Half exchange: the spectra as fp16 (re, im) pairs, 4 modes per 16-byte
+// unit, plane (b, c) scaled by 2^exp[b][c]; decoded to fp32 on staging.
+template <int MB, int CT>
+struct GwShape16 {
+  static constexpr int N = kGwB * CT * MB / 4;        // 16-byte units of a stage and operand
+  static constexpr int U = (N + kGwT - 1) / kGwT;     // per thread (the last pass may be partial)
+  static constexpr int QR = MB / 4;                   // mode quads per row
+};
+
+template <int MB, int CT>
+__device__ __forceinline__ void gw_fetch16(const uint32_t *src, const int *ex, int nc, int K, int B, int st, int k0,
+                                           int c0, int tid, gw_u32x4 (&p)[GwShape16<MB, CT>::U],
+                                           int (&e)[GwShape16<MB, CT>::U]) {
+  using G = GwShape16<MB, CT>;
+#pragma unroll
+  for (int v = 0; v < G::U; ++v) {
+    const int u = v * kGwT + tid;
+    const int row = u / G::QR, qr = u % G::QR;
+    const int b = st * kGwB + row / CT, c = c0 + row % CT, mode = k0 + 4 * qr;
+    const bool ok = u < G::N && b < B && c < nc && mode < K;
+    const size_t r = ok ? (size_t)b * nc + c : 0;
+    const gw_u32x4 t = *reinterpret_cast<const gw_u32x4 *>(src + (ok ? r * K + mode : 0));
+    p[v] = ok ? t : gw_u32x4{0u, 0u, 0u, 0u};
+    e[v] = ex[r];
+  }
+}
+
+template <int MB, int CT>
+__device__ __forceinline__ void gw_put16(float2 *stage, int tid, const gw_u32x4 (&p)[GwShape16<MB, CT>::U],
+                                         const int (&e)[GwShape16<MB, CT>::U]) {
+  using G = GwShape<MB, CT>;
+  using H = GwShape16<MB, CT>;
+#pragma unroll
+  for (int v = 0; v < H::U; ++v) {
+    const int u = v * kGwT + tid;
+    if (u >= H::N) continue;
+    const int row = u / H::QR, qr = u % H::QR;
+    const int b = row / CT, c = row % CT;
+    const float sc = pow2f(-e[v]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      // each half converted on its own
+      const float re = (float)__builtin_bit_cast(_Float16, (uint16_t)(p[v][t] & 0xffffu)) * sc;
+      const float im = (float)__builtin_bit_cast(_Float16, (uint16_t)(p[v][t] >> 16)) * sc;
+      stage[(4 * qr + t) * G::S + b * G::P + c] = make_float2(re, im);
+    }
+  }
+}
+
 template <int MB, int CT>
 __device__ __forceinline__ void gw_put(float2 *stage, int tid, const gw_u32x4 (&p)[GwShape<MB, CT>::U]) {
   using G = GwShape<MB, CT>;
@@ -133,7 +182,7 @@ __device__ __forceinline__ void gw_put(float2 *stage, int tid, const gw_u32x4 (&
   }
 }
 
-template <int DT, int MB, int CT>
+template <int DT, int MB, int CT, bool HX>
 __global__ __launch_bounds__(kGwT) __attribute__((amdgpu_waves_per_eu(2))) void fno_grad_w(GradWArgs a) {
   using G = GwShape<MB, CT>;
   constexpr int MW = G::MW, NT = G::NT;
@@ -159,16 +208,28 @@ __global__ __launch_bounds__(kGwT) __attribute__((amdgpu_waves_per_eu(2))) void 
         acci[m][ti][to] = v4f{0.f, 0.f, 0.f, 0.f};
       }
 
-  gw_u32x4 px[G::U], pg[G::U];
-  gw_fetch<MB, CT>(a.xs, Ci, K, B, 0, k0, i0, tid, px);
-  gw_fetch<MB, CT>(a.gs, Co, K, B, 0, k0, o0, tid, pg);
-  for (int st = 0; st < nst; ++st) {
-    gw_put<MB, CT>(xs, tid, px);
-    gw_put<MB, CT>(gs, tid, pg);
-    if (st + 1 < nst) {
-      gw_fetch<MB, CT>(a.xs, Ci, K, B, st + 1, k0, i0, tid, px);
-      gw_fetch<MB, CT>(a.gs, Co, K, B, st + 1, k0, o0, tid, pg);
+  constexpr int NU = HX ? GwShape16<MB, CT>::U : G::U;
+  gw_u32x4 px[NU], pg[NU];
+  int ex[HX ? NU : 1], eg[HX ? NU : 1];
+  auto fetch = [&](int st) {
+    if constexpr (HX) {
+      gw_fetch16<MB, CT>(a.xs16, a.xexp, Ci, K, B, st, k0, i0, tid, px, ex);
+      gw_fetch16<MB, CT>(a.gs16, a.gexp, Co, K, B, st, k0, o0, tid, pg, eg);
+    } else {
+      gw_fetch<MB, CT>(a.xs, Ci, K, B, st, k0, i0, tid, px);
+      gw_fetch<MB, CT>(a.gs, Co, K, B, st, k0, o0, tid, pg);
     }
+  };
+  fetch(0);
+  for (int st = 0; st < nst; ++st) {
+    if constexpr (HX) {
+      gw_put16<MB, CT>(xs, tid, px, ex);
+      gw_put16<MB, CT>(gs, tid, pg, eg);
+    } else {
+      gw_put<MB, CT>(xs, tid, px);
+      gw_put<MB, CT>(gs, tid, pg);
+    }
+    if (st + 1 < nst) fetch(st + 1);
     __syncthreads();
     // fragment of lane l: batch row l / 16, channel 16 t + l % 16
     const int fo = (lane >> 4) * G::P + (lane & 15);
@@ -224,12 +285,14 @@ static bool gradw_small_tiles(const GradWArgs &a) {
   return big < 256;
 }
 
+// hx: the spectra arrive as the half exchange (fp16 / bf16 plans only)
 template <int MB, int CT>
-static const void *gradw_kernel_t(int dtype) {
+static const void *gradw_kernel_t(int dtype, bool hx) {
   switch (dtype) {
-    case DT_F32: return (const void *)fno_grad_w<DT_F32, MB, CT>;
-    case DT_F16: return (const void *)fno_grad_w<DT_F16, MB, CT>;
-    case DT_BF16: return (const void *)fno_grad_w<DT_BF16, MB, CT>;
+    case DT_F32: return hx ? nullptr : (const void *)fno_grad_w<DT_F32, MB, CT, false>;
+    case DT_F16: return hx ? (const void *)fno_grad_w<DT_F16, MB, CT, true> : (const void *)fno_grad_w<DT_F16, MB, CT, false>;
+    case DT_BF16:
+      return hx ? (const void *)fno_grad_w<DT_BF16, MB, CT, true> : (const void *)fno_grad_w<DT_BF16, MB, CT, false>;
   }
   return nullptr;
 }
@@ -240,8 +303,9 @@ hipError_t launch_grad_w(const GradWArgs &a, int dtype, hipStream_t s) {
   FNO_BOUNDS(check_grad_w(a, dtype);)
   const bool small = gradw_small_tiles(a);
   const int MB = small ? 8 : 16, CT = small ? 16 : 32;
-  const void *k = small ? gradw_kernel_t<8, 16>(dtype) : gradw_kernel_t<16, 32>(dtype);
-  if (!k || !gradw_supported(a.K)) return hipErrorInvalidValue;
+  const bool hx = a.xs16 != nullptr;
+  const void *k = small ? gradw_kernel_t<8, 16>(dtype, hx) : gradw_kernel_t<16, 32>(dtype, hx);
+  if (!k || !gradw_supported(a.K) || (hx && (a.K & 3))) return hipErrorInvalidValue;
   const long gy = (long)((a.Ci + CT - 1) / CT) * ((a.Co + CT - 1) / CT);
   if (gy > 65535) return hipErrorInvalidValue;
   dim3 grid((a.K + MB - 1) / MB, (unsigned)gy);

@@ -38,9 +38,13 @@ void spans_mx_fwd(const Ctx &c, const PlaneMxFwdArgs &a, int dtype, bool two) {
   const size_t n1 = two ? (size_t)a.nsplit : (size_t)a.nplanes, n2 = (size_t)a.nplanes - n1;
   c.span("x", a.x, n1 * px * es);
   if (two) c.span("x2", a.x2, n2 * px * es);
-  if (a.out16 && !two) {
-    c.span("out16", a.out16, (size_t)a.nplanes * K * 4);
-    c.span("oexp", a.oexp, (size_t)a.nplanes * 4);
+  if (a.out16) {
+    c.span("out16", a.out16, n1 * K * 4);
+    c.span("oexp", a.oexp, n1 * 4);
+    if (two) {
+      c.span("out16_2", a.out16_2, n2 * K * 4);
+      c.span("oexp2", a.oexp2, n2 * 4);
+    }
   } else {
     c.span("out", a.out, n1 * K * 8);
     if (two) c.span("out2", a.out2, n2 * K * 8);
@@ -212,8 +216,17 @@ void check_contract_adj(const ContractArgs &a, int bb, int S, size_t wave_bytes,
 void check_grad_w(const GradWArgs &a, int dtype) {
   const Ctx c{"fno_grad_w"};
   const size_t K = (size_t)a.K;
-  c.span("xs", a.xs, (size_t)a.B * a.Ci * K * 8);
-  c.span("gs", a.gs, (size_t)a.B * a.Co * K * 8);
+  if (a.xs16) {
+    c.span("xs16", a.xs16, (size_t)a.B * a.Ci * K * 4);
+    c.span("gs16", a.gs16, (size_t)a.B * a.Co * K * 4);
+    c.span("xexp", a.xexp, (size_t)a.B * a.Ci * 4);
+    c.span("gexp", a.gexp, (size_t)a.B * a.Co * 4);
+    c.need("half exchange: both operands, fp16 / bf16 plan, K % 4 == 0 (16-byte mode quads)",
+           a.gs16 && a.xexp && a.gexp && dtype != DT_F32 && a.K % 4 == 0);
+  } else {
+    c.span("xs", a.xs, (size_t)a.B * a.Ci * K * 8);
+    c.span("gs", a.gs, (size_t)a.B * a.Co * K * 8);
+  }
   c.span("dw", a.dw, K * a.Ci * a.Co * 2 * es_of(dtype));
   c.need("last-axis modes divide K", a.mlast >= 1 && a.K % a.mlast == 0);
 }

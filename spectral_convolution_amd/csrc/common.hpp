@@ -113,11 +113,14 @@ struct PlaneMxFwdArgs {
   const void *x2;
   float2 *out2;
   int nsplit;
-  // half exchange (one-set variant only; NULL: complex fp32 to out): the
-  // spectra as fp16 (re, im) pairs [nplanes][2 m1][m2], each plane scaled by
-  // 2^oexp[plane] (the spectra are out16 * 2^-oexp)
+  // half exchange (NULL: complex fp32 to out / out2): the spectra as fp16
+  // (re, im) pairs [planes][2 m1][m2], each plane scaled by 2^oexp[plane]
+  // (the spectra are out16 * 2^-oexp); out16_2 / oexp2 for the second plane
+  // set of the two-set variant (indices counted from nsplit)
   uint32_t *out16;
   int *oexp;
+  uint32_t *out16_2;
+  int *oexp2;
 };
 
 struct PlaneMxInvArgs {
@@ -172,6 +175,10 @@ struct ContractArgs {
 struct GradWArgs {
   const float2 *xs;  // [B][Ci][K]
   const float2 *gs;  // [B][Co][K]
+  // half exchange (both or neither; xs / gs unused then): fp16 (re, im)
+  // pairs in the same layouts, plane (b, c) scaled by 2^exp[b][c]
+  const uint32_t *xs16, *gs16;
+  const int *xexp, *gexp;
   void *dw;          // [K][Ci][Co][2] storage dtype
   int B, Ci, Co, K, mlast;
   float scale;

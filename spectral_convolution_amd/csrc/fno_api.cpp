@@ -239,6 +239,13 @@ struct fno_plan_s {
   bool hx = false;
   int *xe = nullptr;           // [B][Ci] exponents of the forward spectra
   signed char *ye = nullptr;   // [B][Co][ceil(K / 4)] exponents of the contracted spectra
+  // half exchange in the backward as well (fp16 hx plans whose adjoint runs
+  // on the matrix-core contraction, which then multiplies fp16 operands
+  // directly; bf16 plans measured no faster with it): exponents of the
+  // spectra of dL/dy and of the adjoint-contracted spectra
+  bool hx_b = false;
+  int *ge = nullptr;           // [B][Co]
+  signed char *gxe = nullptr;  // [B][Ci][ceil(K / 4)]
   // backward: the adjoint contraction (Co -> Ci channels), the weight
   // gradient, plane transforms over the other channel count (forward of g
   // over Co channels, inverse over Ci)
@@ -381,6 +388,8 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
   p.cmx_a = contract_mx_supported((int)dtype, c_in, p.K) && contract_mx_workgroups(batch, c_in, p.K) >= 256 &&
             batch >= 16;
   p.adj_w = !p.cmx_a && contract_adj_supported((int)dtype, c_out, p.bb_a);
+  // (the weight gradient reads the half-exchanged spectra 4 modes at a time)
+  p.hx_b = p.hx && p.cmx_a && dtype == FNO_F16 && p.K % 4 == 0;
   p.ppw_fg = plane_ppw(true, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_i);
   p.ppw_ib = plane_ppw(false, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_f);
   p.lds_fg = p.mx ? p.lds_fwd : plane_fwd_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP, p.ppw_fg);
@@ -496,6 +505,8 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   const size_t o_bar = off; off += al(sizeof(FusedBarrier));
   const size_t o_xe = off; off += al(p->hx ? (size_t)p->B * p->Ci * sizeof(int) : 0);
   const size_t o_ye = off; off += al(p->hx ? (size_t)p->B * p->Co * ((p->K + 3) / 4) : 0);
+  const size_t o_ge = off; off += al(p->hx_b ? (size_t)p->B * p->Co * sizeof(int) : 0);
+  const size_t o_gxe = off; off += al(p->hx_b ? (size_t)p->B * p->Ci * ((p->K + 3) / 4) : 0);
   std::vector<uint16_t> tfh, tfl, tbh, tbl, efh, efl, eih, eil;
   if (p->mx) {
     const bool sp = p->dtype == FNO_F32;
@@ -535,6 +546,8 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   p->bar = (FusedBarrier *)(base + o_bar);
   p->xe = p->hx ? (int *)(base + o_xe) : nullptr;
   p->ye = p->hx ? (signed char *)(base + o_ye) : nullptr;
+  p->ge = p->hx_b ? (int *)(base + o_ge) : nullptr;
+  p->gxe = p->hx_b ? (signed char *)(base + o_gxe) : nullptr;
   uint4 *tab_ptr[8] = {};
   for (int t = 0; t < 8; ++t) tab_ptr[t] = tabs[t]->empty() ? nullptr : (uint4 *)(base + o_tab[t]);
   p->tf = tab_ptr[0];
@@ -682,6 +695,8 @@ static PlaneMxFwdArgs mx_fwd_args(fno_plan_t p, const Bufs &b, const void *x, in
   m.x2 = m.x;
   m.out2 = m.out;
   m.nsplit = m.nplanes;
+  m.out16_2 = m.out16;
+  m.oexp2 = m.oexp;
   return m;
 }
 
@@ -718,8 +733,10 @@ static hipError_t fwd_plane_launch(fno_plan_t p, const Bufs &b, const void *x, i
 }
 
 // 2D matrix-core planes of x (Ci channels) and gy (Co channels) in one
-// launch: spectra of x to xh, of gy to yh
-static hipError_t fwd_planes_both(fno_plan_t p, const Bufs &b, const void *x, const void *gy, hipStream_t s) {
+// launch: spectra of x to xh, of gy to yh (half: fp16 pairs with exponents
+// in xe and ge)
+static hipError_t fwd_planes_both(fno_plan_t p, const Bufs &b, const void *x, const void *gy, hipStream_t s,
+                                  bool half = false) {
   PlaneMxFwdArgs m;
   m.x = x;
   m.out = b.xh;
@@ -727,8 +744,10 @@ static hipError_t fwd_planes_both(fno_plan_t p, const Bufs &b, const void *x, co
   m.out2 = b.yh;
   m.nsplit = p->B * p->Ci;
   m.nplanes = p->B * (p->Ci + p->Co);
-  m.out16 = nullptr;
-  m.oexp = nullptr;
+  m.out16 = half ? reinterpret_cast<uint32_t *>(b.xh) : nullptr;
+  m.oexp = half ? b.xe : nullptr;
+  m.out16_2 = half ? reinterpret_cast<uint32_t *>(b.yh) : nullptr;
+  m.oexp2 = half ? p->ge : nullptr;
   m.tw_h = p->tw_h;
   m.tf = p->tf;
   m.tf_lo = p->tf_lo;
@@ -1014,20 +1033,30 @@ static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const v
   auto step = [&](hipError_t r) {
     if (e == hipSuccess) e = r == hipSuccess ? hipGetLastError() : r;
   };
+  // half exchange: spectra of x with exponents xe, of dL/dy with ge, the
+  // adjoint-contracted spectra with gxe (bg: the buffers seen with those)
+  const bool hb = p->hx_b;
+  Bufs bg = b;
+  bg.xe = p->ge;
+  bg.ye = p->gxe;
   if (gw && p->mx && !d3 && p->mx_grid_fb > 0) {
-    step(fwd_planes_both(p, b, x, gy, s));  // both plane sets, one launch
+    step(fwd_planes_both(p, b, x, gy, s, hb));  // both plane sets, one launch
   } else {
     if (gw) {
-      step(fwd_plane_launch(p, b, x, p->Ci, b.xh, s));
+      step(fwd_plane_launch(p, b, x, p->Ci, b.xh, s, hb));
       if (d3 && e == hipSuccess) step(fwd_axis_launch(p, b, p->Ci, b.xh, s));
     }
-    if (e == hipSuccess) step(fwd_plane_launch(p, b, gy, p->Co, b.yh, s));
+    if (e == hipSuccess) step(fwd_plane_launch(p, bg, gy, p->Co, b.yh, s, hb));
     if (d3 && e == hipSuccess) step(fwd_axis_launch(p, b, p->Co, b.yh, s));
   }
   if (gw && e == hipSuccess) {
     GradWArgs a;
     a.xs = p->xh;
     a.gs = p->yh;
+    a.xs16 = hb ? reinterpret_cast<const uint32_t *>(p->xh) : nullptr;
+    a.gs16 = hb ? reinterpret_cast<const uint32_t *>(p->yh) : nullptr;
+    a.xexp = hb ? p->xe : nullptr;
+    a.gexp = hb ? p->ge : nullptr;
     a.dw = gw;
     a.B = p->B;
     a.Ci = p->Ci;
@@ -1043,10 +1072,10 @@ static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const v
         step(launch_contract_adj(contract_args(p, b, p->yh, w, p->xh, true, false), p->bb_a, p->split_a, s));
     } else {
       if (e == hipSuccess) step(launch_conj_transpose(w, p->wh, p->K, p->Ci, p->Co, p->dtype, s));
-      if (e == hipSuccess) step(contract_launch(p, b, p->yh, p->wh, p->xh, true, s));
+      if (e == hipSuccess) step(contract_launch(p, bg, p->yh, p->wh, p->xh, true, s, hb));
     }
     if (d3 && e == hipSuccess) step(inv_axis_launch(p, b, p->xh, p->Ci, s));
-    if (e == hipSuccess) step(inv_plane_launch(p, b, p->xh, p->Ci, gx, s));
+    if (e == hipSuccess) step(inv_plane_launch(p, bg, p->xh, p->Ci, gx, s, hb));
   }
   return map_err(e);
 }

@@ -481,10 +481,20 @@ __device__ __forceinline__ void fwd_col(int g, int se, int pe, const FwdShape &s
   }
   if (r == (1 << s.lgr) - 1) {
     const size_t plane = (size_t)s.bid + (size_t)(g >> s.lgr) * s.nblk;
-    if (!TW && a.out16) {
+    uint32_t *o16 = a.out16;
+    int *oe = a.oexp;
+    size_t lp = plane;  // index within its plane set
+    if constexpr (TW) {
+      if (plane >= (size_t)a.nsplit) {
+        o16 = a.out16_2;
+        oe = a.oexp2;
+        lp = plane - a.nsplit;
+      }
+    }
+    if (o16) {
       const int sx = pe > -1000 ? max(-120, min(120, 14 - pe)) : 0;
       const float f = a.scale * pow2f(sx);
-      uint32_t *op = a.out16 + plane * (2 * s.m1 * s.m2);
+      uint32_t *op = o16 + lp * (2 * s.m1 * s.m2);
 #pragma unroll
       for (int nn = 0; nn < 2; ++nn) {
         const int ky = nn * 16 + (lane & 15);
@@ -495,7 +505,7 @@ __device__ __forceinline__ void fwd_col(int g, int se, int pe, const FwdShape &s
           X[nn][t] = make_float2(0.f, 0.f);
         }
       }
-      if (threadIdx.x == 0) a.oexp[plane] = sx;
+      if (threadIdx.x == 0) oe[lp] = sx;
       return;
     }
     float2 *op = a.out + plane * (2 * s.m1 * s.m2);
