@@ -24,7 +24,9 @@ of the sustained rate. Prints one JSON line:
   sample of the headline workload (whole batch elements), scaled to layers/s;
 * metric_configs: the same three objects (layer rate, roofline,
   cpu_baseline) for every workload the metric is quoted on: 128x128 fp32 and
-  fp16, 256x256 fp16 and bf16, 64^3 fp32;
+  fp16, 256x256 fp16 and bf16, 64^3 fp32. The headline times exactly K
+  layers; every other workload at least 200 (its `steps`), since 20 layers
+  of the 128x128 layer last ~0.5 ms, too short to read stably;
 * per_layer_us / hot_single_set_layers_per_s: the distribution of single
   layers inside the rotating back-to-back loop, and the same loop on one
   buffer set (which the Infinity Cache may serve; never the headline);
@@ -455,6 +457,10 @@ def measure(cfg, dtype, steps, warmup, settle_ms=SETTLE_MS, per_kernel=True, sha
         lay.close()
 
 
+# layers (or backward passes) timed per workload other than the headline
+EXTRA_STEPS = 200
+
+
 def measured_traffic(kernel, cfg_name, dtype):
     """HBM bytes per launch of `kernel` on this workload from the committed
     rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by
@@ -631,7 +637,11 @@ def main():
         for name, dt in METRIC_CONFIGS + [("c0", "f32")]:
             if (name, dt) in results:
                 continue
-            r = measure(wl.CONFIGS[name], dt, args.steps, args.warmup, settle, shapes=shapes)
+            # the other workloads time at least EXTRA_STEPS layers: a 20-layer
+            # loop of the 128x128 layer is ~0.5 ms, too short to read stably
+            r = measure(wl.CONFIGS[name], dt, max(args.steps, EXTRA_STEPS), max(args.warmup, EXTRA_STEPS // 10),
+                        settle, shapes=shapes)
+            r["steps"] = max(args.steps, EXTRA_STEPS)
             results[(name, dt)] = r
             print("[bench] " + _summary(r), file=sys.stderr, flush=True)
     cpu = {}
@@ -654,7 +664,8 @@ def main():
     if not args.no_backward:
         bwd = []
         for name, dt in (("c1", "f32"), ("c2", "f16"), ("c3", "f32")):
-            r = measure_backward(wl.CONFIGS[name], dt, max(20, args.steps // 2), max(5, args.warmup // 2), settle)
+            r = measure_backward(wl.CONFIGS[name], dt, max(EXTRA_STEPS, args.steps // 2), max(5, args.warmup // 2),
+                                 settle)
             bwd.append(r)
             print(f"[bench] backward {name} {dt}: {r['backward_per_s']:.1f} /s, {r['gbps']:.0f} GB/s",
                   file=sys.stderr, flush=True)

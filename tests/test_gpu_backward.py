@@ -74,6 +74,10 @@ SMALL = [
     ("mx-3d", _cfg("r", 3, 1, 3, 2, (8, 64, 128), (3, 12, 20), "uniform"), "f16"),
     ("cmx-rag-f16", _cfg("r", 2, 33, 20, 36, (128, 128), (30, 31), "uniform"), "f16"),
     ("cmx-rag-bf16", _cfg("r", 2, 40, 36, 12, (128, 128), (31, 30), "uniform"), "bf16"),
+    # fp16 forward on the half exchange but K = 2 m1 m2 not a multiple of 4:
+    # the backward keeps complex fp32 spectra (the other fp16 matrix-core
+    # cases above and the full-size 256x256 one run it on the half exchange)
+    ("hx-odd-k-f16", _cfg("r", 2, 33, 36, 20, (128, 128), (31, 31), "uniform"), "f16"),
     # the adjoint contraction (64 output channels) on four-mode workgroups,
     # the forward one (24 output channels) below the matrix-core size
     ("cmx-mb4-adjoint-f16", _cfg("r", 2, 20, 64, 24, (128, 128), (24, 24), "uniform"), "f16"),
