@@ -495,6 +495,46 @@ def copy_bandwidth(nbytes, steps=20, warmup=3):
     return {"bytes_copied": nbytes, "ms": ms, "gbps": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
+def cache_probe(cfg, dtype, n=100):
+    """Where the exchanged spectra are read from. Each launch of the layer
+    is timed alone (events around it) when it runs right after its producer,
+    against runs with a read-only sweep of 1 GiB (a sum, no dirty lines)
+    in between, which evicts the 256 MB Infinity Cache:
+      as_layer:        forward, contraction, inverse
+      weights_evicted: sweep, forward, contraction, inverse
+      spectra_evicted: forward, sweep, contraction, sweep, inverse
+    Medians over n iterations, in us."""
+    import torch
+    lay = Layer(cfg, dtype)
+    try:
+        big = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        acc = torch.zeros(1, device="cuda:0")
+        s = lay.stream
+        out = {}
+        for mode in ("as_layer", "weights_evicted", "spectra_evicted"):
+            t = {k: [] for k in lay.names}
+            for it in range(n + 10):
+                if mode == "weights_evicted":
+                    acc.add_(big.sum())
+                ev = []
+                for idx in range(len(lay.names)):
+                    if mode == "spectra_evicted" and idx > 0:
+                        acc.add_(big.sum())
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(s)
+                    lay.launch(idx, 0)
+                    e1.record(s)
+                    ev.append((e0, e1))
+                torch.cuda.synchronize()
+                if it >= 10:
+                    for idx, (e0, e1) in enumerate(ev):
+                        t[lay.names[idx]].append(e0.elapsed_time(e1) * 1000.0)
+            out[mode] = {k: float(np.median(v)) for k, v in t.items()}
+        return out
+    finally:
+        lay.close()
+
+
 def cpu_baseline(cfg, dtype, budget_s=8.0):
     """The float64 oracle, as it stands, on this host's cores. Batch elements
     of the layer are independent, so it runs on one batch element of the
@@ -587,6 +627,9 @@ def main():
                     help="only time the backward pass of --config/--dtype (profiling runs)")
     ap.add_argument("--separate-only", action="store_true",
                     help="time only the three-launch shape (profiling runs: no cooperative launch)")
+    ap.add_argument("--cache-probe", action="store_true",
+                    help="only time each launch of --config/--dtype right after its producer and with the "
+                         "Infinity Cache evicted in between (where the exchanged spectra are read from)")
     ap.add_argument("--copy-only", type=int, default=0, metavar="BYTES",
                     help="only time a device-to-device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -608,6 +651,9 @@ def main():
     settle = args.settle_ms
     if args.model_only:
         print(json.dumps({"model": measure_model(args.steps, args.warmup, settle)}))
+        return
+    if args.cache_probe:
+        print(json.dumps({"cache_probe": cache_probe(cfg, dtype)}))
         return
     if args.backward_only:
         print(json.dumps({"backward": [measure_backward(cfg, dtype, args.steps, args.warmup, settle)]}))
