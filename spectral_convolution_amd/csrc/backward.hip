@@ -120,55 +120,6 @@ __device__ __forceinline__ void gw_fetch(const float2 *src, int nc, int K, int B
   }
 }
 
-// Half exchange: the spectra as fp16 (re, im) pairs, 4 modes per 16-byte
-// unit, plane (b, c) scaled by 2^exp[b][c]; decoded to fp32 on staging.
-template <int MB, int CT>
-struct GwShape16 {
-  static constexpr int N = kGwB * CT * MB / 4;        // 16-byte units of a stage and operand
-  static constexpr int U = (N + kGwT - 1) / kGwT;     // per thread (the last pass may be partial)
-  static constexpr int QR = MB / 4;                   // mode quads per row
-};
-
-template <int MB, int CT>
-__device__ __forceinline__ void gw_fetch16(const uint32_t *src, const int *ex, int nc, int K, int B, int st, int k0,
-                                           int c0, int tid, gw_u32x4 (&p)[GwShape16<MB, CT>::U],
-                                           int (&e)[GwShape16<MB, CT>::U]) {
-  using G = GwShape16<MB, CT>;
-#pragma unroll
-  for (int v = 0; v < G::U; ++v) {
-    const int u = v * kGwT + tid;
-    const int row = u / G::QR, qr = u % G::QR;
-    const int b = st * kGwB + row / CT, c = c0 + row % CT, mode = k0 + 4 * qr;
-    const bool ok = u < G::N && b < B && c < nc && mode < K;
-    const size_t r = ok ? (size_t)b * nc + c : 0;
-    const gw_u32x4 t = *reinterpret_cast<const gw_u32x4 *>(src + (ok ? r * K + mode : 0));
-    p[v] = ok ? t : gw_u32x4{0u, 0u, 0u, 0u};
-    e[v] = ex[r];
-  }
-}
-
-template <int MB, int CT>
-__device__ __forceinline__ void gw_put16(float2 *stage, int tid, const gw_u32x4 (&p)[GwShape16<MB, CT>::U],
-                                         const int (&e)[GwShape16<MB, CT>::U]) {
-  using G = GwShape<MB, CT>;
-  using H = GwShape16<MB, CT>;
-#pragma unroll
-  for (int v = 0; v < H::U; ++v) {
-    const int u = v * kGwT + tid;
-    if (u >= H::N) continue;
-    const int row = u / H::QR, qr = u % H::QR;
-    const int b = row / CT, c = row % CT;
-    const float sc = pow2f(-e[v]);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      // each half converted on its own
-      const float re = (float)__builtin_bit_cast(_Float16, (uint16_t)(p[v][t] & 0xffffu)) * sc;
-      const float im = (float)__builtin_bit_cast(_Float16, (uint16_t)(p[v][t] >> 16)) * sc;
-      stage[(4 * qr + t) * G::S + b * G::P + c] = make_float2(re, im);
-    }
-  }
-}
-
 template <int MB, int CT>
 __device__ __forceinline__ void gw_put(float2 *stage, int tid, const gw_u32x4 (&p)[GwShape<MB, CT>::U]) {
   using G = GwShape<MB, CT>;
@@ -182,19 +133,23 @@ __device__ __forceinline__ void gw_put(float2 *stage, int tid, const gw_u32x4 (&
   }
 }
 
-template <int DT, int MB, int CT, bool HX>
+template <int DT, int MB, int CT>
 __global__ __launch_bounds__(kGwT) __attribute__((amdgpu_waves_per_eu(2))) void fno_grad_w(GradWArgs a) {
   using G = GwShape<MB, CT>;
   constexpr int MW = G::MW, NT = G::NT;
   __shared__ float2 xs[MB * G::S], gs[MB * G::S];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int K = a.K, Ci = a.Ci, Co = a.Co, B = a.B;
-  // workgroups of one mode block are gridDim.x apart: with gridDim.x a
-  // multiple of 8 they share an XCD (and its L2), where the second read of
-  // each spectra row hits
-  const int k0 = blockIdx.x * MB;
-  const int nto = (Co + CT - 1) / CT;
-  const int i0 = (blockIdx.y / nto) * CT, o0 = (blockIdx.y % nto) * CT;
+  // workgroup h runs on XCD h % 8; with the count a multiple of 8, XCD x
+  // takes the x-th eighth of the blocks in order (tiles of a mode block
+  // fastest), so the mode blocks that share a 128-byte spectra line and the
+  // tiles that re-read it go through one L2
+  const int nto = (Co + CT - 1) / CT, nti = (Ci + CT - 1) / CT;
+  const int ng = gridDim.x, h = blockIdx.x;
+  const int L = (ng & 7) == 0 ? (h & 7) * (ng >> 3) + (h >> 3) : h;
+  const int tile = L % (nti * nto);
+  const int k0 = (L / (nti * nto)) * MB;
+  const int i0 = (tile / nto) * CT, o0 = (tile % nto) * CT;
   const int nst = (B + kGwB - 1) / kGwB;
 
   v4f accr[MW][NT][NT], acci[MW][NT][NT];
@@ -208,27 +163,15 @@ __global__ __launch_bounds__(kGwT) __attribute__((amdgpu_waves_per_eu(2))) void 
         acci[m][ti][to] = v4f{0.f, 0.f, 0.f, 0.f};
       }
 
-  constexpr int NU = HX ? GwShape16<MB, CT>::U : G::U;
-  gw_u32x4 px[NU], pg[NU];
-  int ex[HX ? NU : 1], eg[HX ? NU : 1];
+  gw_u32x4 px[G::U], pg[G::U];
   auto fetch = [&](int st) {
-    if constexpr (HX) {
-      gw_fetch16<MB, CT>(a.xs16, a.xexp, Ci, K, B, st, k0, i0, tid, px, ex);
-      gw_fetch16<MB, CT>(a.gs16, a.gexp, Co, K, B, st, k0, o0, tid, pg, eg);
-    } else {
-      gw_fetch<MB, CT>(a.xs, Ci, K, B, st, k0, i0, tid, px);
-      gw_fetch<MB, CT>(a.gs, Co, K, B, st, k0, o0, tid, pg);
-    }
+    gw_fetch<MB, CT>(a.xs, Ci, K, B, st, k0, i0, tid, px);
+    gw_fetch<MB, CT>(a.gs, Co, K, B, st, k0, o0, tid, pg);
   };
   fetch(0);
   for (int st = 0; st < nst; ++st) {
-    if constexpr (HX) {
-      gw_put16<MB, CT>(xs, tid, px, ex);
-      gw_put16<MB, CT>(gs, tid, pg, eg);
-    } else {
-      gw_put<MB, CT>(xs, tid, px);
-      gw_put<MB, CT>(gs, tid, pg);
-    }
+    gw_put<MB, CT>(xs, tid, px);
+    gw_put<MB, CT>(gs, tid, pg);
     if (st + 1 < nst) fetch(st + 1);
     __syncthreads();
     // fragment of lane l: batch row l / 16, channel 16 t + l % 16
@@ -279,36 +222,261 @@ __global__ __launch_bounds__(kGwT) __attribute__((amdgpu_waves_per_eu(2))) void 
   }
 }
 
+// ------------------------------------------ dw on fp16 matrix cores
+//
+// For the half exchange (fp16 plans): the same per-mode product with the
+// batch as the reduction, on v_mfma_f32_16x16x32_f16. In real form, per mode,
+// M = i and K = (b, re/im); two products share the A operand
+//   A[i][(b,0)] = Re X,  A[i][(b,1)] = Im X,
+//   B0[(b,0)][o] = Re G, B0[(b,1)][o] = Im G   giving Re sum_b conj(X) G,
+//   B1[(b,0)][o] = Im G, B1[(b,1)][o] = -Re G  giving Im sum_b conj(X) G;
+// a B1 fragment is the B0 fragment with the halves of every pair swapped and
+// the new high half negated, so each lane ends with (re, im) of its outputs.
+// The exchanged spectra are fp16 pairs scaled per plane by 2^e; every input
+// channel row i is brought to the smallest exponent over the batch, EX_i (its
+// largest plane keeps its scale, the others are multiplied by 2^-d, d >= 0:
+// one correctly rounded fp16 product, the same value as the decode to fp32
+// and back), and likewise every output channel row o to EG_o, so one product
+// sums the whole batch in one scale, undone per (i, o) at the end. A
+// workgroup (4 waves) owns 8 modes x 32 input x 32 output channels and
+// streams the batch in stages of 16 rows (one 32-deep K block): 16-byte loads
+// of 4 modes' pairs one stage ahead, staged into LDS as fragment rows of 48
+// halves (32 + 16 pad: a fragment read is conflict-free with the row pitch
+// 2 mod 4 16-byte units); wave w multiplies modes 2 w and 2 w + 1.
+constexpr int kGhM = 8;        // modes per workgroup
+constexpr int kGhC = 32;       // input and output channels per workgroup
+constexpr int kGhB = 16;       // batch rows per stage
+constexpr int kGhP = 48;       // halves per staged fragment row
+constexpr int kGhS = 32 * kGhP + 8;   // halves per staged mode (rows + pad)
+constexpr int kGhU = kGhB * kGhC * kGhM / 4 / kGwT;  // 16-byte units per thread and operand (4)
+
+typedef _Float16 gh_f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 gh_f16x2 __attribute__((ext_vector_type(2)));
+
+// Units of a thread (lane l, wave w): mode quad q = l % 2, batch row
+// bl = (l / 2) % 16 of the stage and channels cb + 8 v, v < 4, with
+// cb = 4 (w / 2) + w % 2 + 2 (l / 32). A 4-byte LDS store serves 32 lanes per
+// pass over 32 banks; for lanes 0..31 (and 32..63) the words of one store are
+// the 16 batch rows on consecutive banks and, for the other mode quad, 4
+// staged modes on (3088 words, 16 banks mod 32).
+struct GhLane {
+  int q, bl, cb;
+};
+
+__device__ __forceinline__ GhLane gh_lane(int tid) {
+  const int lane = tid & 63, wv = tid >> 6;
+  return GhLane{lane & 1, (lane >> 1) & 15, 4 * (wv >> 1) + (wv & 1) + 2 * (lane >> 5)};
+}
+
+// one stage of one operand (nc channels, tile origin c0)
+__device__ __forceinline__ void gh_fetch(const uint32_t *src, const int *ex, int nc, int K, int B, int st, int k0,
+                                         int c0, const GhLane &g, gw_u32x4 (&p)[kGhU], int (&e)[kGhU]) {
+  const int b = st * kGhB + g.bl, mode = k0 + 4 * g.q;
+  const uint32_t *sb = src + (size_t)st * kGhB * nc * K;  // first plane row of the stage
+  const int *eb = ex + (size_t)st * kGhB * nc;
+  const int row = g.bl * nc + c0 + g.cb;                   // plane row within the stage, v = 0
+#pragma unroll
+  for (int v = 0; v < kGhU; ++v) {
+    const bool ok = b < B && c0 + g.cb + 8 * v < nc && mode < K;
+    const gw_u32x4 t = *reinterpret_cast<const gw_u32x4 *>(sb + (ok ? (row + 8 * v) * K + mode : 0));
+    p[v] = ok ? t : gw_u32x4{0u, 0u, 0u, 0u};
+    e[v] = eb[ok ? row + 8 * v : 0];
+  }
+}
+
+// bring one stage to the common exponents em[v] of the thread's channels and
+// store it as fragment rows st_[mode][c][2 b + re/im]
+__device__ __forceinline__ void gh_put(uint16_t *st_, const GhLane &g, const int (&em)[kGhU],
+                                       const gw_u32x4 (&p)[kGhU], const int (&e)[kGhU]) {
+  uint32_t *w = reinterpret_cast<uint32_t *>(st_ + 4 * g.q * kGhS + g.cb * kGhP) + g.bl;
+#pragma unroll
+  for (int v = 0; v < kGhU; ++v) {
+    const int d = max(0, e[v] - em[v]);  // invalid units hold zeros
+    // 2^-d in fp16: normal for d <= 14, subnormal up to d = 24
+    const uint32_t sbits = d <= 14 ? (15u - d) << 10 : (d <= 24 ? 1u << (24 - d) : 0u);
+    const gh_f16x2 s = __builtin_bit_cast(gh_f16x2, sbits | (sbits << 16));
+    // the words as scalars: a bit cast of a vector element read element 0
+    const uint32_t pw[4] = {p[v].x, p[v].y, p[v].z, p[v].w};
+    uint32_t r[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) r[t] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(gh_f16x2, pw[t]) * s);
+    if (d > 24) {
+      // beyond one fp16 factor: through fp32
+      const float f = pow2f(-d);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const gh_f16x2 h = __builtin_bit_cast(gh_f16x2, pw[t]);
+        const gh_f16x2 o = {(_Float16)((float)h.x * f), (_Float16)((float)h.y * f)};
+        r[t] = __builtin_bit_cast(uint32_t, o);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) w[t * (kGhS / 2) + v * 8 * (kGhP / 2)] = r[t];
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kGwT) __attribute__((amdgpu_waves_per_eu(3))) void fno_grad_w_hx(GradWArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kGhM * kGhS], gs[kGhM * kGhS];
+  __shared__ int exm[kGhC], egm[kGhC];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int K = a.K, Ci = a.Ci, Co = a.Co, B = a.B;
+  // workgroup h runs on XCD h % 8; with the count a multiple of 8, XCD x
+  // takes the x-th eighth of the blocks in order (tiles of a mode block
+  // fastest), so the four mode blocks that share a 128-byte spectra line and
+  // the tiles that re-read it all go through one L2
+  const int nto = (Co + kGhC - 1) / kGhC, nti = (Ci + kGhC - 1) / kGhC;
+  const int ng = gridDim.x, h = blockIdx.x;
+  const int L = (ng & 7) == 0 ? (h & 7) * (ng >> 3) + (h >> 3) : h;
+  const int tile = L % (nti * nto);
+  const int k0 = (L / (nti * nto)) * kGhM;
+  const int i0 = (tile / nto) * kGhC, o0 = (tile % nto) * kGhC;
+  const int nst = (B + kGhB - 1) / kGhB;
+  const GhLane g = gh_lane(tid);
+
+  gw_u32x4 px[kGhU], pg[kGhU];
+  int ex[kGhU], eg[kGhU];
+  gh_fetch(a.xs16, a.xexp, Ci, K, B, 0, k0, i0, g, px, ex);
+  gh_fetch(a.gs16, a.gexp, Co, K, B, 0, k0, o0, g, pg, eg);
+  // common exponent of every channel row over the batch: four threads per
+  // row, rows 0..31 the input channels, 32..63 the output channels
+  {
+    const int row = tid >> 2, part = tid & 3;
+    const bool isx = row < kGhC;
+    const int c = (isx ? i0 : o0) + (row & (kGhC - 1)), nc = isx ? Ci : Co;
+    const int *exs = isx ? a.xexp : a.gexp;
+    int m = 1 << 20;
+    if (c < nc) {
+#pragma unroll 8
+      for (int b = part; b < B; b += 4) m = min(m, exs[(size_t)b * nc + c]);
+    }
+    m = min(m, __shfl_xor(m, 1, 64));
+    m = min(m, __shfl_xor(m, 2, 64));
+    if (part == 0) (isx ? exm : egm)[row & (kGhC - 1)] = m < (1 << 20) ? m : 0;
+  }
+  __syncthreads();
+  int emx[kGhU], emg[kGhU];
+#pragma unroll
+  for (int v = 0; v < kGhU; ++v) {
+    emx[v] = exm[g.cb + 8 * v];
+    emg[v] = egm[g.cb + 8 * v];
+  }
+
+  v4f acc[2][2][2][2];  // [mode of the wave][i tile][o tile][re, im]
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int ot = 0; ot < 2; ++ot) acc[m][mt][ot][0] = acc[m][mt][ot][1] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // fragment of lane l: row 16 t + l % 16, halves 8 (l / 16) .. + 7
+  const int fr = (lane & 15) * kGhP + 8 * (lane >> 4);
+  for (int st = 0; st < nst; ++st) {
+    gh_put(xs, g, emx, px, ex);
+    gh_put(gs, g, emg, pg, eg);
+    if (st + 1 < nst) {
+      gh_fetch(a.xs16, a.xexp, Ci, K, B, st + 1, k0, i0, g, px, ex);
+      gh_fetch(a.gs16, a.gexp, Co, K, B, st + 1, k0, o0, g, pg, eg);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const int m = 2 * wv + mm;
+      gw_u32x4 af[2], b0[2], b1[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        af[t] = *reinterpret_cast<const gw_u32x4 *>(xs + m * kGhS + 16 * t * kGhP + fr);
+        b0[t] = *reinterpret_cast<const gw_u32x4 *>(gs + m * kGhS + 16 * t * kGhP + fr);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b1[t][j] = __builtin_amdgcn_alignbit(b0[t][j], b0[t][j], 16) ^ 0x80000000u;
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int ot = 0; ot < 2; ++ot) {
+          const gh_f16x8 av = __builtin_bit_cast(gh_f16x8, af[mt]);
+          acc[mm][mt][ot][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(gh_f16x8, b0[ot]),
+                                                                      acc[mm][mt][ot][0], 0, 0, 0);
+          acc[mm][mt][ot][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(gh_f16x8, b1[ot]),
+                                                                      acc[mm][mt][ot][1], 0, 0, 0);
+        }
+    }
+    __syncthreads();
+  }
+
+  // accumulator register j of lane l: i = 16 mt + 4 (l / 16) + j,
+  // o = 16 ot + l % 16; 16 lanes store 16 consecutive outputs
+  float fx[2][4], fg[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    fg[t] = pow2f(-egm[16 * t + (lane & 15)]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fx[t][j] = pow2f(-exm[16 * t + 4 * (lane >> 4) + j]);
+  }
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm) {
+    const int mode = k0 + 2 * wv + mm;
+    const float sc = a.scale * ((mode % a.mlast) == 0 ? 1.0f : 2.0f);
+#pragma unroll
+    for (int ot = 0; ot < 2; ++ot) {
+      const int o = o0 + 16 * ot + (lane & 15);
+      const float fo = sc * fg[ot];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = i0 + 16 * mt + 4 * (lane >> 4) + j;
+          if (mode < K && i < Ci && o < Co) {
+            const float f = fo * fx[mt][j];
+            store_pair<DT>(a.dw, 2 * (((size_t)mode * Ci + i) * Co + o), acc[mm][mt][ot][0][j] * f,
+                           acc[mm][mt][ot][1][j] * f);
+          }
+        }
+    }
+  }
+}
+
 // tile shape: the large one when it gives at least 256 workgroups
 static bool gradw_small_tiles(const GradWArgs &a) {
   const long big = (long)((a.K + 15) / 16) * ((a.Ci + 31) / 32) * ((a.Co + 31) / 32);
   return big < 256;
 }
 
-// hx: the spectra arrive as the half exchange (fp16 / bf16 plans only)
 template <int MB, int CT>
-static const void *gradw_kernel_t(int dtype, bool hx) {
+static const void *gradw_kernel_t(int dtype) {
   switch (dtype) {
-    case DT_F32: return hx ? nullptr : (const void *)fno_grad_w<DT_F32, MB, CT, false>;
-    case DT_F16: return hx ? (const void *)fno_grad_w<DT_F16, MB, CT, true> : (const void *)fno_grad_w<DT_F16, MB, CT, false>;
-    case DT_BF16:
-      return hx ? (const void *)fno_grad_w<DT_BF16, MB, CT, true> : (const void *)fno_grad_w<DT_BF16, MB, CT, false>;
+    case DT_F32: return (const void *)fno_grad_w<DT_F32, MB, CT>;
+    case DT_F16: return (const void *)fno_grad_w<DT_F16, MB, CT>;
+    case DT_BF16: return (const void *)fno_grad_w<DT_BF16, MB, CT>;
   }
   return nullptr;
 }
 
 bool gradw_supported(int K) { return (K & 1) == 0; }
 
+// the half-exchange weight gradient: fp16, 16-byte mode quads, and the
+// per-stage element offsets (16 batch rows of a spectra operand) in int
+bool gradw_hx_supported(int dtype, int K, int Ci, int Co) {
+  return dtype == DT_F16 && K % 4 == 0 && (long)kGhB * (Ci > Co ? Ci : Co) * K < 0x7fffffffL;
+}
+
 hipError_t launch_grad_w(const GradWArgs &a, int dtype, hipStream_t s) {
   FNO_BOUNDS(check_grad_w(a, dtype);)
+  if (a.xs16) {
+    // half exchange (fp16 plans): the fp16 matrix-core kernel
+    const long n = (long)((a.K + kGhM - 1) / kGhM) * ((a.Ci + kGhC - 1) / kGhC) * ((a.Co + kGhC - 1) / kGhC);
+    if (!gradw_hx_supported(dtype, a.K, a.Ci, a.Co) || n > 0x7fffffffL) return hipErrorInvalidValue;
+    void *args[] = {(void *)&a};
+    return hipLaunchKernel((const void *)fno_grad_w_hx<DT_F16>, dim3((unsigned)n), dim3(kGwT), args, 0, s);
+  }
   const bool small = gradw_small_tiles(a);
   const int MB = small ? 8 : 16, CT = small ? 16 : 32;
-  const bool hx = a.xs16 != nullptr;
-  const void *k = small ? gradw_kernel_t<8, 16>(dtype, hx) : gradw_kernel_t<16, 32>(dtype, hx);
-  if (!k || !gradw_supported(a.K) || (hx && (a.K & 3))) return hipErrorInvalidValue;
-  const long gy = (long)((a.Ci + CT - 1) / CT) * ((a.Co + CT - 1) / CT);
-  if (gy > 65535) return hipErrorInvalidValue;
-  dim3 grid((a.K + MB - 1) / MB, (unsigned)gy);
+  const void *k = small ? gradw_kernel_t<8, 16>(dtype) : gradw_kernel_t<16, 32>(dtype);
+  if (!k || !gradw_supported(a.K)) return hipErrorInvalidValue;
+  const long n = (long)((a.K + MB - 1) / MB) * ((a.Ci + CT - 1) / CT) * ((a.Co + CT - 1) / CT);
+  if (n > 0x7fffffffL) return hipErrorInvalidValue;
+  dim3 grid((unsigned)n);
   void *args[] = {(void *)&a};
   return hipLaunchKernel(k, grid, dim3(kGwT), args, 0, s);
 }

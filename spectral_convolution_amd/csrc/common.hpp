@@ -175,8 +175,8 @@ struct ContractArgs {
 struct GradWArgs {
   const float2 *xs;  // [B][Ci][K]
   const float2 *gs;  // [B][Co][K]
-  // half exchange (both or neither; xs / gs unused then): fp16 (re, im)
-  // pairs in the same layouts, plane (b, c) scaled by 2^exp[b][c]
+  // half exchange (fp16 plans; both or neither, xs / gs unused then): fp16
+  // (re, im) pairs in the same layouts, plane (b, c) scaled by 2^exp[b][c]
   const uint32_t *xs16, *gs16;
   const int *xexp, *gexp;
   void *dw;          // [K][Ci][Co][2] storage dtype
@@ -285,6 +285,7 @@ hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s);
 hipError_t launch_weights_repack(const WeightsArgs &a, int dtype, hipStream_t s);
 hipError_t launch_conj_transpose(const void *w, void *wh, int K, int Ci, int Co, int dtype, hipStream_t s);
 bool gradw_supported(int K);
+bool gradw_hx_supported(int dtype, int K, int Ci, int Co);
 hipError_t launch_grad_w(const GradWArgs &a, int dtype, hipStream_t s);
 
 hipError_t launch_channel_mix(const void *x, const void *A, const void *bias, const void *add, void *y, int B,

@@ -389,7 +389,7 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
             batch >= 16;
   p.adj_w = !p.cmx_a && contract_adj_supported((int)dtype, c_out, p.bb_a);
   // (the weight gradient reads the half-exchanged spectra 4 modes at a time)
-  p.hx_b = p.hx && p.cmx_a && dtype == FNO_F16 && p.K % 4 == 0;
+  p.hx_b = p.hx && p.cmx_a && gradw_hx_supported(DT_F16, p.K, c_in, c_out) && dtype == FNO_F16;
   p.ppw_fg = plane_ppw(true, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_i);
   p.ppw_ib = plane_ppw(false, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_f);
   p.lds_fg = p.mx ? p.lds_fwd : plane_fwd_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP, p.ppw_fg);
@@ -1021,7 +1021,7 @@ static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const v
              (gx && overlap(gw, nw, gx, nx))))
     return FNO_ERR_INVALID_ARG;
   // launch-shape limits of the two backward-only kernels
-  if (gw && (!gradw_supported(p->K) || (long)((p->Ci + 31) / 32) * ((p->Co + 31) / 32) > 65535))
+  if (gw && (!gradw_supported(p->K) || (long)((p->K + 7) / 8) * ((p->Ci + 31) / 32) * ((p->Co + 31) / 32) > 0x7fffffffL))
     return FNO_ERR_UNSUPPORTED;
   if (gx && (long)p->K * ((p->Ci + 31) / 32) * ((p->Co + 31) / 32) > 0x7fffffffL) return FNO_ERR_UNSUPPORTED;
   DeviceGuard g(p->device);
