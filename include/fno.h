@@ -32,10 +32,11 @@
  *
  * Ownership. The caller owns x, w and y and keeps them alive until the work
  * queued on `stream` has finished. The plan owns its twiddle tables and its
- * spectra workspace and, for fp16 / bf16 plans and fp32 plans with an odd
- * c_out, a buffer for the conjugate-transposed weights of the backward pass
- * (fp32 plans with an even c_out read w directly in the backward's adjoint
- * contraction); all allocated by fno_plan_create, freed by fno_plan_destroy.
+ * spectra workspace and, where the backward's adjoint contraction cannot
+ * read w directly, a buffer for the conjugate-transposed weights: fp32 plans
+ * with an odd c_out, and fp16 / bf16 plans whose adjoint contraction runs
+ * off the matrix cores or whose c_out is not a multiple of 4; all allocated
+ * by fno_plan_create, freed by fno_plan_destroy.
  * Execution calls allocate nothing.
  *
  * Execution calls are asynchronous on `stream` (a hipStream_t; NULL is the
@@ -138,8 +139,8 @@ fno_status_t fno_spectral_conv3d(fno_plan_t plan, const void *x, const void *w,
  * aligned; outputs must not overlap any other argument. INVALID_ARG when
  * both outputs are NULL or an input an output needs is NULL, or on a plan of
  * the other ndim; UNSUPPORTED when ceil(c_in/32) * ceil(c_out/32) exceeds
- * 65535 (grad_w) or that product times the retained modes exceeds 2^31 - 1
- * (grad_x). Uses the plan's workspace (one call in flight per plan,
+ * 65535 (grad_w) or that product times ceil(K/8) (grad_w) or times K
+ * (grad_x) exceeds 2^31 - 1, K the retained modes. Uses the plan's workspace (one call in flight per plan,
  * forward or backward); asynchronous on `stream`; allocates nothing. */
 fno_status_t fno_spectral_conv2d_backward(fno_plan_t plan, const void *x,
                                           const void *w, const void *grad_y,

@@ -140,16 +140,13 @@ __global__ __launch_bounds__(kGwT) __attribute__((amdgpu_waves_per_eu(2))) void 
   __shared__ float2 xs[MB * G::S], gs[MB * G::S];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int K = a.K, Ci = a.Ci, Co = a.Co, B = a.B;
-  // workgroup h runs on XCD h % 8; with the count a multiple of 8, XCD x
-  // takes the x-th eighth of the blocks in order (tiles of a mode block
-  // fastest), so the mode blocks that share a 128-byte spectra line and the
-  // tiles that re-read it go through one L2
-  const int nto = (Co + CT - 1) / CT, nti = (Ci + CT - 1) / CT;
-  const int ng = gridDim.x, h = blockIdx.x;
-  const int L = (ng & 7) == 0 ? (h & 7) * (ng >> 3) + (h >> 3) : h;
-  const int tile = L % (nti * nto);
-  const int k0 = (L / (nti * nto)) * MB;
-  const int i0 = (tile / nto) * CT, o0 = (tile % nto) * CT;
+  // workgroups of one mode block are gridDim.x apart: with gridDim.x a
+  // multiple of 8 they share an XCD (and its L2), where the second read of
+  // each spectra row hits (measured 4 % faster than also keeping the mode
+  // blocks of one 128-byte line on one XCD)
+  const int k0 = blockIdx.x * MB;
+  const int nto = (Co + CT - 1) / CT;
+  const int i0 = (blockIdx.y / nto) * CT, o0 = (blockIdx.y % nto) * CT;
   const int nst = (B + kGwB - 1) / kGwB;
 
   v4f accr[MW][NT][NT], acci[MW][NT][NT];
@@ -474,9 +471,9 @@ hipError_t launch_grad_w(const GradWArgs &a, int dtype, hipStream_t s) {
   const int MB = small ? 8 : 16, CT = small ? 16 : 32;
   const void *k = small ? gradw_kernel_t<8, 16>(dtype) : gradw_kernel_t<16, 32>(dtype);
   if (!k || !gradw_supported(a.K)) return hipErrorInvalidValue;
-  const long n = (long)((a.K + MB - 1) / MB) * ((a.Ci + CT - 1) / CT) * ((a.Co + CT - 1) / CT);
-  if (n > 0x7fffffffL) return hipErrorInvalidValue;
-  dim3 grid((unsigned)n);
+  const long gy = (long)((a.Ci + CT - 1) / CT) * ((a.Co + CT - 1) / CT);
+  if (gy > 65535) return hipErrorInvalidValue;
+  dim3 grid((a.K + MB - 1) / MB, (unsigned)gy);
   void *args[] = {(void *)&a};
   return hipLaunchKernel(k, grid, dim3(kGwT), args, 0, s);
 }

@@ -280,7 +280,10 @@ bool contract_mx_supported(int dtype, int Co, int K);
 long contract_mx_workgroups(int B, int Co, int K);
 size_t contract_mx_lds_bytes(int dtype, int B);
 hipError_t contract_mx_prepare(int dtype, int B);
-hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s);
+// wt: w holds the layer's W[K][Co][Ci] and the product's weight is its
+// conjugate transpose (the backward's adjoint contraction); needs Ci % 4 == 0
+hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s, bool wt = false);
+bool contract_mx_wt_supported(int Ci);
 
 hipError_t launch_weights_repack(const WeightsArgs &a, int dtype, hipStream_t s);
 hipError_t launch_conj_transpose(const void *w, void *wh, int K, int Ci, int Co, int dtype, hipStream_t s);

@@ -29,6 +29,12 @@
 // there. The results leave through LDS as rows of MB modes of Yh[b][o][k].
 // Four-mode workgroups (half the LDS and registers, so more of them fit on a
 // CU) are used when eight-mode ones would leave resident slots empty.
+//
+// Adjoint from W (WT): the backward's Xh[k] = Yh[k] W[k]^H reads the layer's
+// W[k][i][o] directly. With the product's contracted index c = o and output
+// n = i, a stage row (mode, n) of 16 c is 64 contiguous bytes of W, which
+// go to LDS as they are: 16-byte stores straight into the fragment rows; the
+// conjugation is folded into the fragment forming.
 
 #include "common.hpp"
 
@@ -110,6 +116,17 @@ __device__ __forceinline__ void wunit(int u, int &m, int &i, int &c) {
   m = u >> 7;
 }
 
+// WT: weight unit u of a stage: mode m, output row n, contracted channels
+// 4 q .. 4 q + 3 of the stage. Four lanes read 64 bytes of one W row; the
+// 8 lanes of one 16-byte store pass cover rows n and n + 8 (wrow 2 apart:
+// 48 words, 16 banks mod 32), so their stores hit 32 distinct banks.
+__device__ __forceinline__ void wunit_t(int u, int &m, int &n, int &q) {
+  const int x = (u >> 2) & 31;
+  q = u & 3;
+  n = 8 * (x & 1) + ((x >> 1) & 7) + 16 * (x >> 4);
+  m = u >> 7;
+}
+
 // one spectra unit in flight: two modes of one (b, i) row; complex fp32
 // (re, im, re, im) bits, or (HX) two fp16 pairs and the row's exponent
 template <bool HX>
@@ -122,7 +139,7 @@ struct XReg<true> {
   int e;
 };
 
-template <int DT, int MT, int MB, bool HX>
+template <int DT, int MT, int MB, bool HX, bool WT>
 __device__ __forceinline__ void cmx_fetch(const ContractArgs &a, int st, int k0, int b0, int o0, int tid,
                                           XReg<HX> (&px)[CmxShape<DT, MT, MB, HX>::XU],
                                           u32x4 (&pw)[CmxShape<DT, MT, MB, HX>::WU]) {
@@ -147,20 +164,31 @@ __device__ __forceinline__ void cmx_fetch(const ContractArgs &a, int st, int k0,
   }
 #pragma unroll
   for (int v = 0; v < S::WU; ++v) {
-    int m, il, c;
-    wunit(v * kCT + tid, m, il, c);
-    const int mode = k0 + m, i = st * kIC + il, o = o0 + 4 * c;
-    const bool ok = mode < K && i < Ci && o < Co;
-    const u32x4 t = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.w) +
-                                                     (ok ? (((size_t)mode * Ci + i) * Co + o) * 2 : 0));
-    pw[v] = ok ? t : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (WT) {
+      // w[mode][n][c] (Ci % 4 == 0: a 16-byte group is whole or absent)
+      int m, nl, q;
+      wunit_t(v * kCT + tid, m, nl, q);
+      const int mode = k0 + m, n = o0 + nl, c = st * kIC + 4 * q;
+      const bool ok = mode < K && n < Co && c < Ci;
+      const u32x4 t = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.w) +
+                                                       (ok ? (((size_t)mode * Co + n) * Ci + c) * 2 : 0));
+      pw[v] = ok ? t : u32x4{0u, 0u, 0u, 0u};
+    } else {
+      int m, il, c;
+      wunit(v * kCT + tid, m, il, c);
+      const int mode = k0 + m, i = st * kIC + il, o = o0 + 4 * c;
+      const bool ok = mode < K && i < Ci && o < Co;
+      const u32x4 t = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.w) +
+                                                       (ok ? (((size_t)mode * Ci + i) * Co + o) * 2 : 0));
+      pw[v] = ok ? t : u32x4{0u, 0u, 0u, 0u};
+    }
   }
 }
 
 // split and transpose one stage into fragment rows:
 //   xs[mode][part][b][2 i + re/im], ws[mode][part][o][2 i + re/im]
 // sb: the batch rows' common exponents (DIRECT)
-template <int DT, int MT, int MB, bool HX>
+template <int DT, int MT, int MB, bool HX, bool WT>
 __device__ __forceinline__ void cmx_put(uint16_t *xs, uint16_t *ws, int tid,
                                         const XReg<HX> (&px)[CmxShape<DT, MT, MB, HX>::XU],
                                         const u32x4 (&pw)[CmxShape<DT, MT, MB, HX>::WU], const int *sb) {
@@ -202,6 +230,32 @@ __device__ __forceinline__ void cmx_put(uint16_t *xs, uint16_t *ws, int tid,
       reinterpret_cast<uint32_t *>(xs + (m * 2 + 1) * S::XB + xrow<MT>(m, b) * kSP)[i] = lo;
     }
   }
+  if constexpr (WT) {
+#pragma unroll
+    for (int v = 0; v < S::WU; ++v) {
+      int m, nl, q;
+      wunit_t(v * kCT + tid, m, nl, q);
+      uint16_t *dst = ws + ((m * S::HL) * kOT + wrow(nl)) * kSP + 8 * q;
+      if constexpr (S::HL == 2) {
+        // fp16 weights in bf16 hi + lo parts, each half converted on its own
+        u32x4 hi, lo;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float re = (float)__builtin_bit_cast(_Float16, (uint16_t)(pw[v][t] & 0xffffu));
+          const float im = (float)__builtin_bit_cast(_Float16, (uint16_t)(pw[v][t] >> 16));
+          uint32_t h, l;
+          split_pair(re, im, h, l);
+          hi[t] = h;
+          lo[t] = l;
+        }
+        *reinterpret_cast<u32x4 *>(dst) = hi;
+        *reinterpret_cast<u32x4 *>(dst + kOT * kSP) = lo;
+      } else {
+        *reinterpret_cast<u32x4 *>(dst) = pw[v];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int v = 0; v < S::WU; ++v) {
     int m, i, c;
@@ -229,11 +283,18 @@ __device__ __forceinline__ void cmx_put(uint16_t *xs, uint16_t *ws, int tid,
 
 // B fragment of output column n = 16 nt + l % 16 = (o, part) from raw
 // (Re W, Im W) pairs of four consecutive input channels: part 0 takes
-// (Re, -Im), part 1 takes (Im, Re)
+// (Re, -Im), part 1 takes (Im, Re). WT (the weight is conj(W)): part 0 takes
+// (Re, Im) as it is, part 1 (-Im, Re).
+template <bool WT>
 __device__ __forceinline__ u32x4 w_form(u32x4 raw, bool part1) {
   u32x4 o;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) o[j] = part1 ? __builtin_amdgcn_alignbit(raw[j], raw[j], 16) : raw[j] ^ 0x80000000u;
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (WT)
+      o[j] = part1 ? __builtin_amdgcn_alignbit(raw[j], raw[j], 16) ^ 0x00008000u : raw[j];
+    else
+      o[j] = part1 ? __builtin_amdgcn_alignbit(raw[j], raw[j], 16) : raw[j] ^ 0x80000000u;
+  }
   return o;
 }
 
@@ -243,7 +304,7 @@ __device__ __forceinline__ u32x4 w_form(u32x4 raw, bool part1) {
 template <int DT, int MB, bool HX>
 constexpr int cmx_waves() { return MB == 8 ? 2 : DT == DT_F16 && !HX ? 3 : 4; }
 
-template <int DT, int MT, int MB, bool HX>
+template <int DT, int MT, int MB, bool HX, bool WT>
 __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<DT, MB, HX>()))) void fno_contract_mx(
     ContractArgs a) {
   using S = CmxShape<DT, MT, MB, HX>;
@@ -272,7 +333,7 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<D
   // minimum below.
   XReg<HX> px[S::XU];
   u32x4 pw[S::WU];
-  cmx_fetch<DT, MT, MB, HX>(a, 0, k0, b0, o0, tid, px, pw);
+  cmx_fetch<DT, MT, MB, HX, WT>(a, 0, k0, b0, o0, tid, px, pw);
 
   // DIRECT: each batch row's common exponent, the smallest over its planes
   // (the largest plane then fits fp16 and every other is scaled down); the
@@ -312,8 +373,8 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<D
       for (int nt = 0; nt < 4; ++nt) acc[mm][mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
   for (int st = 0; st < nst; ++st) {
-    cmx_put<DT, MT, MB, HX>(xs, ws, tid, px, pw, sbl);
-    if (st + 1 < nst) cmx_fetch<DT, MT, MB, HX>(a, st + 1, k0, b0, o0, tid, px, pw);
+    cmx_put<DT, MT, MB, HX, WT>(xs, ws, tid, px, pw, sbl);
+    if (st + 1 < nst) cmx_fetch<DT, MT, MB, HX, WT>(a, st + 1, k0, b0, o0, tid, px, pw);
     __syncthreads();
 #pragma unroll
     for (int mm = 0; mm < S::MW; ++mm) {
@@ -338,7 +399,7 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<D
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int p = 0; p < S::HL; ++p) bf[t][p] = w_form(bf[t][p], part1);
+          for (int p = 0; p < S::HL; ++p) bf[t][p] = w_form<WT>(bf[t][p], part1);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -450,17 +511,23 @@ long contract_mx_workgroups(int B, int Co, int K) {
 // layer (B = 32, 64 channels, 32 x 32 modes: 512) slower.
 static int cmx_modes(int B, int Co, int K) { return contract_mx_workgroups(B, Co, K) < 512 ? 4 : 8; }
 
-template <int DT, bool HX>
+template <int DT, bool HX, bool WT>
 static const void *contract_mx_kernel_dt(int B, int mb) {
   const bool one = B <= 16;
-  if (mb == 4) return one ? (const void *)fno_contract_mx<DT, 1, 4, HX> : (const void *)fno_contract_mx<DT, 2, 4, HX>;
-  return one ? (const void *)fno_contract_mx<DT, 1, 8, HX> : (const void *)fno_contract_mx<DT, 2, 8, HX>;
+  if (mb == 4)
+    return one ? (const void *)fno_contract_mx<DT, 1, 4, HX, WT> : (const void *)fno_contract_mx<DT, 2, 4, HX, WT>;
+  return one ? (const void *)fno_contract_mx<DT, 1, 8, HX, WT> : (const void *)fno_contract_mx<DT, 2, 8, HX, WT>;
 }
 
-static const void *contract_mx_kernel(int dtype, int B, int mb, bool hx) {
-  if (dtype == DT_F16) return hx ? contract_mx_kernel_dt<DT_F16, true>(B, mb) : contract_mx_kernel_dt<DT_F16, false>(B, mb);
-  if (dtype == DT_BF16)
-    return hx ? contract_mx_kernel_dt<DT_BF16, true>(B, mb) : contract_mx_kernel_dt<DT_BF16, false>(B, mb);
+template <int DT>
+static const void *contract_mx_kernel_d(int B, int mb, bool hx, bool wt) {
+  if (hx) return wt ? contract_mx_kernel_dt<DT, true, true>(B, mb) : contract_mx_kernel_dt<DT, true, false>(B, mb);
+  return wt ? contract_mx_kernel_dt<DT, false, true>(B, mb) : contract_mx_kernel_dt<DT, false, false>(B, mb);
+}
+
+static const void *contract_mx_kernel(int dtype, int B, int mb, bool hx, bool wt) {
+  if (dtype == DT_F16) return contract_mx_kernel_d<DT_F16>(B, mb, hx, wt);
+  if (dtype == DT_BF16) return contract_mx_kernel_d<DT_BF16>(B, mb, hx, wt);
   return nullptr;
 }
 
@@ -481,20 +548,23 @@ size_t contract_mx_lds_bytes(int dtype, int B) {
 
 hipError_t contract_mx_prepare(int dtype, int B) {
   for (int mb : {4, 8})
-    for (bool hx : {false, true}) {
-      const void *k = contract_mx_kernel(dtype, B, mb, hx);
-      if (!k) return hipErrorInvalidValue;
-      const hipError_t e = raise_lds_cap(k, contract_mx_lds_bytes(dtype, B, mb, hx));
-      if (e != hipSuccess) return e;
-    }
+    for (bool hx : {false, true})
+      for (bool wt : {false, true}) {
+        const void *k = contract_mx_kernel(dtype, B, mb, hx, wt);
+        if (!k) return hipErrorInvalidValue;
+        const hipError_t e = raise_lds_cap(k, contract_mx_lds_bytes(dtype, B, mb, hx));
+        if (e != hipSuccess) return e;
+      }
   return hipSuccess;
 }
 
-hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s) {
+bool contract_mx_wt_supported(int Ci) { return (Ci & 3) == 0; }
+
+hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s, bool wt) {
   FNO_BOUNDS(check_contract(a, dtype, true);)
   const int mb = cmx_modes(a.B, a.Co, a.K);
-  const void *k = contract_mx_kernel(dtype, a.B, mb, a.xh16 != nullptr);
-  if (!k) return hipErrorInvalidValue;
+  const void *k = contract_mx_kernel(dtype, a.B, mb, a.xh16 != nullptr, wt);
+  if (!k || (wt && !contract_mx_wt_supported(a.Ci))) return hipErrorInvalidValue;
   const int BT = a.B <= 16 ? 16 : 32;
   const long nkb = (long)((a.K + mb - 1) / mb) * ((a.B + BT - 1) / BT), no = (a.Co + kOT - 1) / kOT;
   const long n = (nkb + 7) / 8 * 8 * no;

@@ -12,8 +12,9 @@
 //
 // The backward pass (gradients of x and w from g = dL/dy) reuses the same
 // kernels: dx is the layer applied to g with every mode's weight replaced by
-// its conjugate transpose (fno_conj_transpose, then forward planes of g,
-// the contraction from Co to Ci channels, inverse planes); dw is a per-mode
+// its conjugate transpose (forward planes of g, the contraction from Co to Ci
+// channels reading W transposed, or W^H from fno_conj_transpose where it
+// cannot, inverse planes); dw is a per-mode
 // reduction over the batch of conj(forward(x)) * forward(g) (fno_grad_w).
 
 #include <hip/hip_runtime.h>
@@ -254,6 +255,7 @@ struct fno_plan_s {
   // fp32 plans: the adjoint contraction reads W in its forward layout (no
   // conjugate-transposed copy, no W^H buffer)
   bool adj_w = false;
+  bool adj_mx = false;  // the matrix-core adjoint contraction reads W itself (no W^H)
   int ppw_fg = 1, ppw_ib = 1;
   size_t lds_fg = 0, lds_ib = 0;
   int mx_grid_fg = 0, mx_grid_ib = 0;
@@ -388,6 +390,7 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
   p.cmx_a = contract_mx_supported((int)dtype, c_in, p.K) && contract_mx_workgroups(batch, c_in, p.K) >= 256 &&
             batch >= 16;
   p.adj_w = !p.cmx_a && contract_adj_supported((int)dtype, c_out, p.bb_a);
+  p.adj_mx = p.cmx_a && contract_mx_wt_supported(c_out);
   // (the weight gradient reads the half-exchanged spectra 4 modes at a time)
   p.hx_b = p.hx && p.cmx_a && gradw_hx_supported(DT_F16, p.K, c_in, c_out) && dtype == FNO_F16;
   p.ppw_fg = plane_ppw(true, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_i);
@@ -501,7 +504,8 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   const size_t o_xh = off; off += al(n_xh * sizeof(float2));
   const size_t o_yh = off; off += al(n_yh * sizeof(float2));
   const size_t o_t = off; off += al(n_t * sizeof(float2));
-  const size_t o_wh = off; off += al(p->adj_w ? 0 : (size_t)p->K * p->Ci * p->Co * 2 * (p->dtype == FNO_F32 ? 4 : 2));
+  const bool need_wh = !p->adj_w && !p->adj_mx;
+  const size_t o_wh = off; off += al(need_wh ? (size_t)p->K * p->Ci * p->Co * 2 * (p->dtype == FNO_F32 ? 4 : 2) : 0);
   const size_t o_bar = off; off += al(sizeof(FusedBarrier));
   const size_t o_xe = off; off += al(p->hx ? (size_t)p->B * p->Ci * sizeof(int) : 0);
   const size_t o_ye = off; off += al(p->hx ? (size_t)p->B * p->Co * ((p->K + 3) / 4) : 0);
@@ -542,7 +546,7 @@ fno_status_t fno_plan_create(fno_plan_t *out, int ndim, int batch, int c_in, int
   p->xh = (float2 *)(base + o_xh);
   p->yh = (float2 *)(base + o_yh);
   p->tbuf = n_t ? (float2 *)(base + o_t) : nullptr;
-  p->wh = p->adj_w ? nullptr : base + o_wh;
+  p->wh = need_wh ? base + o_wh : nullptr;
   p->bar = (FusedBarrier *)(base + o_bar);
   p->xe = p->hx ? (int *)(base + o_xe) : nullptr;
   p->ye = p->hx ? (signed char *)(base + o_ye) : nullptr;
@@ -797,12 +801,14 @@ static ContractArgs contract_args(fno_plan_t p, const Bufs &b, const float2 *in,
   return a;
 }
 
-// contraction: forward (Ci -> Co with w) or adjoint (Co -> Ci with W^H)
+// contraction: forward (Ci -> Co with w) or adjoint (Co -> Ci with W^H;
+// wt: w is the layer's W, read transposed by the matrix-core kernel)
 static hipError_t contract_launch(fno_plan_t p, const Bufs &b, const float2 *in, const void *w, float2 *out,
-                                  bool adjoint, hipStream_t s, bool half = false) {
+                                  bool adjoint, hipStream_t s, bool half = false, bool wt = false) {
   const ContractArgs a = contract_args(p, b, in, w, out, adjoint, half);
   if (adjoint)
-    return p->cmx_a ? launch_contract_mx(a, p->dtype, s) : launch_contract(a, p->bb_a, p->split_a, p->dtype, s);
+    return p->cmx_a ? launch_contract_mx(a, p->dtype, s, wt)
+                    : launch_contract(a, p->bb_a, p->split_a, p->dtype, s);
   return p->cmx ? launch_contract_mx(a, p->dtype, s) : launch_contract(a, p->bb, p->split, p->dtype, s);
 }
 
@@ -1021,7 +1027,8 @@ static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const v
              (gx && overlap(gw, nw, gx, nx))))
     return FNO_ERR_INVALID_ARG;
   // launch-shape limits of the two backward-only kernels
-  if (gw && (!gradw_supported(p->K) || (long)((p->K + 7) / 8) * ((p->Ci + 31) / 32) * ((p->Co + 31) / 32) > 0x7fffffffL))
+  if (gw && (!gradw_supported(p->K) || (long)((p->Ci + 31) / 32) * ((p->Co + 31) / 32) > 65535 ||
+             (long)((p->K + 7) / 8) * ((p->Ci + 31) / 32) * ((p->Co + 31) / 32) > 0x7fffffffL))
     return FNO_ERR_UNSUPPORTED;
   if (gx && (long)p->K * ((p->Ci + 31) / 32) * ((p->Co + 31) / 32) > 0x7fffffffL) return FNO_ERR_UNSUPPORTED;
   DeviceGuard g(p->device);
@@ -1070,6 +1077,8 @@ static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const v
     if (p->adj_w) {
       if (e == hipSuccess)
         step(launch_contract_adj(contract_args(p, b, p->yh, w, p->xh, true, false), p->bb_a, p->split_a, s));
+    } else if (p->adj_mx) {
+      if (e == hipSuccess) step(contract_launch(p, bg, p->yh, w, p->xh, true, s, hb, true));
     } else {
       if (e == hipSuccess) step(launch_conj_transpose(w, p->wh, p->K, p->Ci, p->Co, p->dtype, s));
       if (e == hipSuccess) step(contract_launch(p, bg, p->yh, p->wh, p->xh, true, s, hb));

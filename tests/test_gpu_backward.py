@@ -81,6 +81,10 @@ SMALL = [
     # the adjoint contraction (64 output channels) on four-mode workgroups,
     # the forward one (24 output channels) below the matrix-core size
     ("cmx-mb4-adjoint-f16", _cfg("r", 2, 20, 64, 24, (128, 128), (24, 24), "uniform"), "f16"),
+    # the matrix-core adjoint reads W transposed in 16-byte groups of 4
+    # output channels (every matrix-core case above); c_out = 22 keeps the
+    # conjugate-transposed copy of W
+    ("cmx-wh-f16", _cfg("r", 2, 33, 36, 22, (128, 128), (31, 30), "uniform"), "f16"),
     # weight-gradient tiles: wide batch split over waves, channel tails
     ("gw-split", _cfg("r", 2, 64, 6, 10, (64, 64), (4, 6), "uniform"), "f32"),
     ("gw-ib4", _cfg("r", 2, 4, 48, 40, (64, 64), (20, 28), "uniform"), "f32"),
