@@ -74,8 +74,10 @@ typedef struct fno_plan_s *fno_plan_t;
  *             cores: fp16 products of the spectra (brought to one
  *             power-of-two scale per batch row) and fp16 weights as stored,
  *             or bf16 hi + lo products for bf16 weights (exact); the
- *             backward of such fp16 layers exchanges its spectra the same
- *             way (K a multiple of 4). Other layers and passes exchange
+ *             backward of such layers exchanges its spectra the same way
+ *             (K a multiple of 4) and forms grad_w from fp16 products of the
+ *             spectra, each channel row brought to one power-of-two scale
+ *             over the batch. Other layers and passes exchange
  *             complex fp32 spectra and contract them with
  *             bf16 hi + lo matrix-core products (batch >= 16) or fp32
  *             matrix-core products.

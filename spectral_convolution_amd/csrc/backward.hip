@@ -221,7 +221,8 @@ __global__ __launch_bounds__(kGwT) __attribute__((amdgpu_waves_per_eu(2))) void 
 
 // ------------------------------------------ dw on fp16 matrix cores
 //
-// For the half exchange (fp16 plans): the same per-mode product with the
+// For the half exchange (fp16 / bf16 plans; the exchanged spectra are fp16
+// pairs either way, the gradient is rounded to the plan's dtype): the same per-mode product with the
 // batch as the reduction, on v_mfma_f32_16x16x32_f16. In real form, per mode,
 // M = i and K = (b, re/im); two products share the A operand
 //   A[i][(b,0)] = Re X,  A[i][(b,1)] = Im X,
@@ -452,20 +453,21 @@ static const void *gradw_kernel_t(int dtype) {
 
 bool gradw_supported(int K) { return (K & 1) == 0; }
 
-// the half-exchange weight gradient: fp16, 16-byte mode quads, and the
+// the half-exchange weight gradient: fp16 / bf16 plans, 16-byte mode quads, and the
 // per-stage element offsets (16 batch rows of a spectra operand) in int
 bool gradw_hx_supported(int dtype, int K, int Ci, int Co) {
-  return dtype == DT_F16 && K % 4 == 0 && (long)kGhB * (Ci > Co ? Ci : Co) * K < 0x7fffffffL;
+  return (dtype == DT_F16 || dtype == DT_BF16) && K % 4 == 0 && (long)kGhB * (Ci > Co ? Ci : Co) * K < 0x7fffffffL;
 }
 
 hipError_t launch_grad_w(const GradWArgs &a, int dtype, hipStream_t s) {
   FNO_BOUNDS(check_grad_w(a, dtype);)
   if (a.xs16) {
-    // half exchange (fp16 plans): the fp16 matrix-core kernel
+    // half exchange: the fp16 matrix-core kernel
     const long n = (long)((a.K + kGhM - 1) / kGhM) * ((a.Ci + kGhC - 1) / kGhC) * ((a.Co + kGhC - 1) / kGhC);
     if (!gradw_hx_supported(dtype, a.K, a.Ci, a.Co) || n > 0x7fffffffL) return hipErrorInvalidValue;
     void *args[] = {(void *)&a};
-    return hipLaunchKernel((const void *)fno_grad_w_hx<DT_F16>, dim3((unsigned)n), dim3(kGwT), args, 0, s);
+    const void *k = dtype == DT_F16 ? (const void *)fno_grad_w_hx<DT_F16> : (const void *)fno_grad_w_hx<DT_BF16>;
+    return hipLaunchKernel(k, dim3((unsigned)n), dim3(kGwT), args, 0, s);
   }
   const bool small = gradw_small_tiles(a);
   const int MB = small ? 8 : 16, CT = small ? 16 : 32;

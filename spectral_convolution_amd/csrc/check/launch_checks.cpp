@@ -221,8 +221,8 @@ void check_grad_w(const GradWArgs &a, int dtype) {
     c.span("gs16", a.gs16, (size_t)a.B * a.Co * K * 4);
     c.span("xexp", a.xexp, (size_t)a.B * a.Ci * 4);
     c.span("gexp", a.gexp, (size_t)a.B * a.Co * 4);
-    c.need("half exchange: both operands, fp16 plan, K % 4 == 0 (16-byte mode quads)",
-           a.gs16 && a.xexp && a.gexp && dtype == DT_F16 && a.K % 4 == 0);
+    c.need("half exchange: both operands, fp16 / bf16 plan, K % 4 == 0 (16-byte mode quads)",
+           a.gs16 && a.xexp && a.gexp && dtype != DT_F32 && a.K % 4 == 0);
   } else {
     c.span("xs", a.xs, (size_t)a.B * a.Ci * K * 8);
     c.span("gs", a.gs, (size_t)a.B * a.Co * K * 8);

@@ -175,7 +175,7 @@ struct ContractArgs {
 struct GradWArgs {
   const float2 *xs;  // [B][Ci][K]
   const float2 *gs;  // [B][Co][K]
-  // half exchange (fp16 plans; both or neither, xs / gs unused then): fp16
+  // half exchange (fp16 / bf16 plans; both or neither, xs / gs unused then): fp16
   // (re, im) pairs in the same layouts, plane (b, c) scaled by 2^exp[b][c]
   const uint32_t *xs16, *gs16;
   const int *xexp, *gexp;

@@ -392,7 +392,7 @@ static fno_status_t validate(fno_plan_s &p, int ndim, int batch, int c_in, int c
   p.adj_w = !p.cmx_a && contract_adj_supported((int)dtype, c_out, p.bb_a);
   p.adj_mx = p.cmx_a && contract_mx_wt_supported(c_out);
   // (the weight gradient reads the half-exchanged spectra 4 modes at a time)
-  p.hx_b = p.hx && p.cmx_a && gradw_hx_supported(DT_F16, p.K, c_in, c_out) && dtype == FNO_F16;
+  p.hx_b = p.hx && p.cmx_a && gradw_hx_supported((int)dtype, p.K, c_in, c_out);
   p.ppw_fg = plane_ppw(true, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_i);
   p.ppw_ib = plane_ppw(false, p.pH, p.pW, p.pm1, p.pm2, p.pMP, np_f);
   p.lds_fg = p.mx ? p.lds_fwd : plane_fwd_lds_bytes(p.pH, p.pW, p.pm1, p.pm2, p.pMP, p.ppw_fg);
