@@ -156,6 +156,47 @@ fno_status_t fno_spectral_conv3d_backward(fno_plan_t plan, const void *x,
                                           void *grad_x, void *grad_w,
                                           void *stream);
 
+/* Saved spectra for the backward pass (TurboFNO write-up, section 4.3: the
+ * layer as an autograd Function, whose forward keeps what its backward
+ * needs). grad_w needs the retained spectra of x, not x itself: a forward
+ * that leaves them in a caller-owned buffer spares the backward the
+ * transforms of x (a full read of x) and lets a training step keep
+ * B * c_in * K complex modes instead of x.
+ *
+ * fno_plan_saved_bytes: bytes of that buffer, in *bytes: the spectra of x in
+ * the exchange format of the plan's backward (complex fp32, or fp16 pairs
+ * and one int exponent per (b, i) plane), each part 256-byte aligned.
+ * UNSUPPORTED (and *bytes untouched) for plans whose forward and backward
+ * exchange those spectra in different formats: 2D fp16 / bf16 layers on the
+ * half exchange whose backward keeps complex fp32 (K not a multiple of 4, or
+ * an adjoint contraction off the matrix cores). INVALID_ARG on a NULL
+ * argument. */
+fno_status_t fno_plan_saved_bytes(fno_plan_t plan, size_t *bytes);
+
+/* The layer (2D or 3D by the plan) computing y as fno_spectral_conv2d / 3d
+ * do, with the plan's stand-alone kernels, that also leaves the spectra of
+ * x in `saved` (device, 256-byte aligned, fno_plan_saved_bytes long, owned
+ * by the caller and not overlapping x, w or y). The contents are valid for
+ * fno_spectral_conv_backward_saved on this plan while x is unchanged.
+ * INVALID_ARG, UNSUPPORTED as fno_plan_saved_bytes and the forward;
+ * asynchronous on `stream`; allocates nothing. */
+fno_status_t fno_spectral_conv_forward_save(fno_plan_t plan, const void *x,
+                                            const void *w, void *y,
+                                            void *saved, void *stream);
+
+/* The backward (2D or 3D by the plan) with the spectra of x read from
+ * `saved`, as written by fno_spectral_conv_forward_save on this plan,
+ * instead of transformed from x; otherwise as fno_spectral_conv2d_backward
+ * (same results). saved may be NULL when grad_w is NULL; outputs must not
+ * overlap it. INVALID_ARG also when saved is not 256-byte aligned or the
+ * plan has no saved format (fno_plan_saved_bytes UNSUPPORTED). */
+fno_status_t fno_spectral_conv_backward_saved(fno_plan_t plan,
+                                              const void *saved,
+                                              const void *w,
+                                              const void *grad_y,
+                                              void *grad_x, void *grad_w,
+                                              void *stream);
+
 /* Weight layouts of a PyTorch FNO module, for fno_weights_pack / _unpack.
  *
  * FNO_WEIGHTS_SPLIT: the TurboFNO write-up's form (section 2.2: a weight of

@@ -18,6 +18,8 @@ __all__ = [
     "fno_weights_pack", "fno_weights_unpack", "SpectralConvFunction", "spectral_conv",
     "fno_channel_mix", "fno_projection", "fno_model2d_create", "fno_model2d_forward",
     "fno_model2d_destroy", "Model2d", "fno_model2d_set_graph", "fno_block2d", "fno_block2d_prepare",
+    "fno_plan_saved_bytes", "fno_saved_empty", "fno_spectral_conv_forward_save",
+    "fno_spectral_conv_backward_saved",
 ]
 
 
@@ -178,6 +180,60 @@ def fno_spectral_conv3d_backward(plan, x, w, grad_y, grad_x, grad_w, stream=None
           "fno_spectral_conv3d_backward")
 
 
+def fno_plan_saved_bytes(plan):
+    """Bytes of the saved-spectra buffer of fno_spectral_conv_forward_save,
+    or None when the plan has no saved format (see include/fno.h)."""
+    n = ctypes.c_size_t()
+    st = lib().fno_plan_saved_bytes(plan.handle, ctypes.byref(n))
+    if st == 2:  # FNO_ERR_UNSUPPORTED
+        return None
+    check(st, "fno_plan_saved_bytes")
+    return n.value
+
+
+def fno_saved_empty(plan):
+    """A device buffer (uint8 tensor) for the plan's saved spectra, or None."""
+    import torch
+    n = fno_plan_saved_bytes(plan)
+    if n is None:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=f"cuda:{plan.device}")
+
+
+def _check_saved(plan, saved):
+    import torch
+    if saved is None or isinstance(saved, int):
+        return
+    if not isinstance(saved, torch.Tensor):
+        raise TypeError("saved must be a torch tensor, a device pointer or None")
+    n = fno_plan_saved_bytes(plan)
+    if n is None:
+        raise ValueError("the plan has no saved-spectra format")
+    if saved.numel() * saved.element_size() < n:
+        raise ValueError(f"saved holds {saved.numel() * saved.element_size()} bytes, the plan needs {n}")
+    if saved.data_ptr() % 256:
+        raise ValueError("saved must be 256-byte aligned")
+
+
+def fno_spectral_conv_forward_save(plan, x, w, y, saved, stream=None):
+    """The layer (2D or 3D by the plan) that also leaves the spectra of x in
+    `saved` for fno_spectral_conv_backward_saved."""
+    _check_tensors(plan, x, w, y)
+    _check_saved(plan, saved)
+    check(lib().fno_spectral_conv_forward_save(plan.handle, _ptr(x), _ptr(w), _ptr(y), _ptr(saved),
+                                               _stream(stream, plan.device)), "fno_spectral_conv_forward_save")
+
+
+def fno_spectral_conv_backward_saved(plan, saved, w, grad_y, grad_x, grad_w, stream=None):
+    """Gradients with the spectra of x read from `saved` (see include/fno.h);
+    grad_x or grad_w may be None, saved may be None when grad_w is."""
+    _check_backward(plan, None, w, grad_y, grad_x, grad_w)
+    _check_saved(plan, saved)
+    check(lib().fno_spectral_conv_backward_saved(plan.handle, _ptr(saved), _ptr(w), _ptr(grad_y),
+                                                 _ptr(grad_x), _ptr(grad_w), _stream(stream, plan.device)),
+          "fno_spectral_conv_backward_saved")
+
+
 _LAYOUTS = {"split": 0, "corners": 1}
 
 
@@ -240,9 +296,17 @@ def _autograd_function():
             w = torch.empty(plan.w_shape(), dtype=x.dtype, device=x.device)
             fno_weights_pack(plan, "split", weight_real, weight_imag, w)
             y = torch.empty(plan.y_shape(), dtype=x.dtype, device=x.device)
-            (fno_spectral_conv2d if plan.ndim == 2 else fno_spectral_conv3d)(plan, x, w, y)
             ctx.plan = plan
-            ctx.save_for_backward(x, w)
+            saved = fno_saved_empty(plan)
+            if saved is not None:
+                # keep the retained spectra of x (what grad_w needs), not x
+                fno_spectral_conv_forward_save(plan, x, w, y, saved)
+                ctx.save_for_backward(saved, w)
+                ctx.kept = "spectra"
+            else:
+                (fno_spectral_conv2d if plan.ndim == 2 else fno_spectral_conv3d)(plan, x, w, y)
+                ctx.save_for_backward(x, w)
+                ctx.kept = "x"
             return y
 
         @staticmethod
@@ -250,15 +314,20 @@ def _autograd_function():
         def backward(ctx, grad_y):
             # first derivatives only: a second backward raises instead of
             # silently returning no higher-order terms
-            x, w = ctx.saved_tensors
+            kept, w = ctx.saved_tensors
             plan = ctx.plan
             need_x, need_re, need_im = ctx.needs_input_grad[:3]
-            gx = torch.empty_like(x) if need_x else None
+            gx = torch.empty(plan.x_shape(), dtype=w.dtype, device=w.device) if need_x else None
             gw = torch.empty_like(w) if (need_re or need_im) else None
             if gx is None and gw is None:
                 return None, None, None, None
-            f = fno_spectral_conv2d_backward if plan.ndim == 2 else fno_spectral_conv3d_backward
-            f(plan, x if gw is not None else None, w if gx is not None else None, grad_y.contiguous(), gx, gw)
+            if ctx.kept == "spectra":
+                fno_spectral_conv_backward_saved(plan, kept if gw is not None else None,
+                                                 w if gx is not None else None, grad_y.contiguous(), gx, gw)
+            else:
+                f = fno_spectral_conv2d_backward if plan.ndim == 2 else fno_spectral_conv3d_backward
+                f(plan, kept if gw is not None else None, w if gx is not None else None, grad_y.contiguous(),
+                  gx, gw)
             g_re = g_im = None
             if gw is not None:
                 g_re = torch.empty(plan.split_shape(), dtype=w.dtype, device=w.device)

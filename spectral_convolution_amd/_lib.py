@@ -26,6 +26,9 @@ SIGNATURES = {
     "fno_block2d_prepare": (_c_int, [_c_void_p]),
     "fno_spectral_conv2d_backward": (_c_int, [_c_void_p] * 7),
     "fno_spectral_conv3d_backward": (_c_int, [_c_void_p] * 7),
+    "fno_plan_saved_bytes": (_c_int, [_c_void_p, ctypes.POINTER(_c_size_t)]),
+    "fno_spectral_conv_forward_save": (_c_int, [_c_void_p] * 6),
+    "fno_spectral_conv_backward_saved": (_c_int, [_c_void_p] * 7),
     "fno_weights_pack": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "fno_weights_unpack": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "fno_plan_destroy": (_c_int, [_c_void_p]),

@@ -1006,16 +1006,32 @@ static size_t carve(fno_plan_t p, unsigned char *base, Bufs *b) {
   return total;
 }
 
+// Saved spectra of x (a forward that keeps them for the backward): the
+// retained spectra in the exchange format the backward's weight gradient
+// reads, then (half exchange) the per-plane exponents. Only where the forward
+// leaves them in that same format: the half exchange in both passes, or
+// complex fp32 in both.
+static bool saved_ok(fno_plan_t p) { return p->hx == p->hx_b; }
+
+static size_t saved_spectra_bytes(fno_plan_t p) {
+  return (((size_t)p->B * p->Ci * p->K * (p->hx ? 4 : sizeof(float2))) + 255) & ~(size_t)255;
+}
+
+static size_t saved_bytes(fno_plan_t p) {
+  return saved_spectra_bytes(p) + (p->hx ? (((size_t)p->B * p->Ci * sizeof(int)) + 255) & ~(size_t)255 : 0);
+}
+
 // Gradients: every launch is stream-ordered on `stream`; the spectra
-// workspace holds forward(x) and forward(g), then the adjoint-contracted
-// spectra; wh holds W^H (plans whose adjoint contraction reads W directly
-// have none).
+// workspace holds forward(x) (or, with `saved`, the caller keeps them) and
+// forward(g), then the adjoint-contracted spectra; wh holds W^H (plans whose
+// adjoint contraction reads W directly have none).
 static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const void *w, const void *gy, void *gx,
-                                  void *gw, void *stream) {
+                                  void *gw, void *stream, const void *saved = nullptr) {
   if (!p || p->ndim != ndim) return FNO_ERR_INVALID_ARG;
   if (!gy || (!gx && !gw)) return FNO_ERR_INVALID_ARG;
-  if ((gw && !x) || (gx && !w)) return FNO_ERR_INVALID_ARG;
+  if ((gw && !x && !saved) || (gx && !w)) return FNO_ERR_INVALID_ARG;
   if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)gy | (uintptr_t)gx | (uintptr_t)gw) & 15) return FNO_ERR_INVALID_ARG;
+  if (((uintptr_t)saved & 255) || (saved && !saved_ok(p))) return FNO_ERR_INVALID_ARG;
   size_t pts = 1;
   for (int d = 0; d < p->ndim; ++d) pts *= (size_t)p->grid[d];
   const size_t es = elem_bytes(p->dtype);
@@ -1023,9 +1039,13 @@ static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const v
   const size_t nw = (size_t)p->K * p->Ci * p->Co * 2 * es;
   if (gx && (overlap(gx, nx, gy, ny) || (x && overlap(gx, nx, x, nx)) || overlap(gx, nx, w, nw)))
     return FNO_ERR_INVALID_ARG;
-  if (gw && (overlap(gw, nw, gy, ny) || overlap(gw, nw, x, nx) || (w && overlap(gw, nw, w, nw)) ||
+  if (gw && (overlap(gw, nw, gy, ny) || (x && overlap(gw, nw, x, nx)) || (w && overlap(gw, nw, w, nw)) ||
              (gx && overlap(gw, nw, gx, nx))))
     return FNO_ERR_INVALID_ARG;
+  if (saved) {
+    const size_t ns = saved_bytes(p);
+    if ((gx && overlap(gx, nx, saved, ns)) || (gw && overlap(gw, nw, saved, ns))) return FNO_ERR_INVALID_ARG;
+  }
   // launch-shape limits of the two backward-only kernels
   if (gw && (!gradw_supported(p->K) || (long)((p->Ci + 31) / 32) * ((p->Co + 31) / 32) > 65535 ||
              (long)((p->K + 7) / 8) * ((p->Ci + 31) / 32) * ((p->Co + 31) / 32) > 0x7fffffffL))
@@ -1046,10 +1066,14 @@ static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const v
   Bufs bg = b;
   bg.xe = p->ge;
   bg.ye = p->gxe;
-  if (gw && p->mx && !d3 && p->mx_grid_fb > 0) {
+  // the spectra of x: transformed here into the workspace, or the caller's
+  const bool fx = gw && !saved;
+  const float2 *xs = saved ? (const float2 *)saved : p->xh;
+  const int *xse = saved ? (const int *)((const unsigned char *)saved + saved_spectra_bytes(p)) : p->xe;
+  if (fx && p->mx && !d3 && p->mx_grid_fb > 0) {
     step(fwd_planes_both(p, b, x, gy, s, hb));  // both plane sets, one launch
   } else {
-    if (gw) {
+    if (fx) {
       step(fwd_plane_launch(p, b, x, p->Ci, b.xh, s, hb));
       if (d3 && e == hipSuccess) step(fwd_axis_launch(p, b, p->Ci, b.xh, s));
     }
@@ -1058,11 +1082,11 @@ static fno_status_t exec_backward(fno_plan_t p, int ndim, const void *x, const v
   }
   if (gw && e == hipSuccess) {
     GradWArgs a;
-    a.xs = p->xh;
+    a.xs = xs;
     a.gs = p->yh;
-    a.xs16 = hb ? reinterpret_cast<const uint32_t *>(p->xh) : nullptr;
+    a.xs16 = hb ? reinterpret_cast<const uint32_t *>(xs) : nullptr;
     a.gs16 = hb ? reinterpret_cast<const uint32_t *>(p->yh) : nullptr;
-    a.xexp = hb ? p->xe : nullptr;
+    a.xexp = hb ? xse : nullptr;
     a.gexp = hb ? p->ge : nullptr;
     a.dw = gw;
     a.B = p->B;
@@ -1147,6 +1171,48 @@ fno_status_t fno_spectral_conv2d_backward(fno_plan_t plan, const void *x, const 
 fno_status_t fno_spectral_conv3d_backward(fno_plan_t plan, const void *x, const void *w, const void *grad_y,
                                           void *grad_x, void *grad_w, void *stream) {
   return exec_backward(plan, 3, x, w, grad_y, grad_x, grad_w, stream);
+}
+
+fno_status_t fno_plan_saved_bytes(fno_plan_t plan, size_t *bytes) {
+  if (!plan || !bytes) return FNO_ERR_INVALID_ARG;
+  if (!saved_ok(plan)) return FNO_ERR_UNSUPPORTED;
+  *bytes = saved_bytes(plan);
+  return FNO_OK;
+}
+
+fno_status_t fno_spectral_conv_forward_save(fno_plan_t plan, const void *x, const void *w, void *y, void *saved,
+                                            void *stream) {
+  if (!plan || !saved || ((uintptr_t)saved & 255)) return FNO_ERR_INVALID_ARG;
+  if (!saved_ok(plan)) return FNO_ERR_UNSUPPORTED;
+  fno_status_t st = check_exec(plan, plan->ndim, x, w, y);
+  if (st != FNO_OK) return st;
+  size_t pts = 1;
+  for (int d = 0; d < plan->ndim; ++d) pts *= (size_t)plan->grid[d];
+  const size_t es = elem_bytes(plan->dtype), ns = saved_bytes(plan);
+  if (overlap(saved, ns, x, (size_t)plan->B * plan->Ci * pts * es) ||
+      overlap(saved, ns, y, (size_t)plan->B * plan->Co * pts * es) ||
+      overlap(saved, ns, w, (size_t)plan->K * plan->Ci * plan->Co * 2 * es))
+    return FNO_ERR_INVALID_ARG;
+  DeviceGuard g(plan->device);
+  if (g.err != hipSuccess) return FNO_ERR_DEVICE;
+  // the stand-alone kernels with the spectra of x (and their exponents) in
+  // the caller's buffer: the contraction reads them from there
+  Bufs b = plan_bufs(plan);
+  b.xh = (float2 *)saved;
+  if (plan->hx) b.xe = (int *)((unsigned char *)saved + saved_spectra_bytes(plan));
+  const hipStream_t s = (hipStream_t)stream;
+  for (int kind : plan->sep_launches) {
+    hipError_t e = run_one(plan, b, kind, x, w, y, s);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return map_err(e);
+  }
+  return FNO_OK;
+}
+
+fno_status_t fno_spectral_conv_backward_saved(fno_plan_t plan, const void *saved, const void *w,
+                                              const void *grad_y, void *grad_x, void *grad_w, void *stream) {
+  if (!plan || (grad_w && !saved)) return FNO_ERR_INVALID_ARG;
+  return exec_backward(plan, plan->ndim, nullptr, w, grad_y, grad_x, grad_w, stream, grad_w ? saved : nullptr);
 }
 
 fno_status_t fno_spectral_conv_noalloc(fno_plan_t plan, const void *x, const void *w, void *y, void *stream) {

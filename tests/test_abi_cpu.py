@@ -89,6 +89,10 @@ def test_null_arguments(L):
     assert L.fno_spectral_conv3d(None, p, p, p, None) == INVALID
     assert L.fno_spectral_conv2d_backward(None, p, p, p, p, p, None) == INVALID
     assert L.fno_spectral_conv3d_backward(None, p, p, p, p, p, None) == INVALID
+    assert L.fno_spectral_conv_forward_save(None, p, p, p, p, None) == INVALID
+    assert L.fno_spectral_conv_backward_saved(None, p, p, p, p, p, None) == INVALID
+    sz0 = ctypes.c_size_t()
+    assert L.fno_plan_saved_bytes(None, ctypes.byref(sz0)) == INVALID
     assert L.fno_weights_pack(None, 0, p, p, p, None) == INVALID
     assert L.fno_weights_unpack(None, 1, p, p, None, None) == INVALID
     n = ctypes.c_int()

@@ -33,6 +33,8 @@ def test_minimal_bytes(name, dtype, expect):
 def test_backward_minimal_bytes():
     # 128^2 fp32: x, dL/dy, grad_x (3 x 32 MiB) + w, grad_w (2 x 4 MiB)
     assert bench.backward_minimal_bytes(wl.CONFIGS["c1"], "f32") == 3 * 33_554_432 + 2 * 4_194_304
+    # from the saved spectra: those instead of x, the rest unchanged
+    assert bench.backward_saved_minimal_bytes(wl.CONFIGS["c1"], "f32", 1000) == 1000 + 2 * 33_554_432 + 2 * 4_194_304
 
 
 def test_per_launch_bytes_2d():

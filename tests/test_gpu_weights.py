@@ -143,11 +143,16 @@ def test_corner_layout_meaning(ndim):
     assert err <= 1e-5
 
 
+# the Function keeps the saved spectra of x where the plan has a saved
+# format (every case but the last), else x: the fp16 layer on the half
+# exchange with K = 2*31*31 has none
 AG = [(_cfg(2, 3, 4, 5, (64, 64), (8, 12)), "f32"), (_cfg(2, 2, 6, 4, (128, 64), (16, 9)), "f16"),
-      (_cfg(3, 2, 3, 2, (16, 16, 8), (4, 3, 2)), "f32")]
+      (_cfg(3, 2, 3, 2, (16, 16, 8), (4, 3, 2)), "f32"),
+      (_cfg(2, 33, 20, 36, (128, 128), (30, 31)), "f16"), (_cfg(2, 40, 36, 12, (128, 128), (31, 30)), "bf16"),
+      (_cfg(2, 33, 36, 20, (128, 128), (31, 31)), "f16")]
 
 
-@pytest.mark.parametrize("case", AG, ids=[f"{c.ndim}d-{d}" for c, d in AG])
+@pytest.mark.parametrize("case", AG, ids=[f"{c.ndim}d-{d}-b{c.batch}-k{c.n_modes}" for c, d in AG])
 def test_autograd_function(case):
     cfg, dtype = case
     print(f"[autograd] {cfg.ndim}d {dtype} grid={cfg.grid}", flush=True)
