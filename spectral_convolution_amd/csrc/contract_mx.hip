@@ -45,7 +45,13 @@ namespace fno {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 
-constexpr int kCT = 256;  // threads per workgroup (4 waves, MB / 4 modes each)
+// Threads per workgroup: one wave per mode, 8 waves for eight-mode
+// workgroups and 4 for four-mode ones (measured against 4 waves of two modes
+// each at 256^2: 26.2 -> 25.1 us fp16 on the half exchange, 25.1 -> 22.4 us
+// its adjoint, 24.7 -> 22.9 us bf16: twice the waves per CU to hide the
+// stage latencies, half the registers per lane)
+template <int MB>
+constexpr int cmx_threads() { return MB * 64; }
 constexpr int kIC = 16;   // input channels per stage (one 32-deep block of K)
 constexpr int kOT = 32;   // output channels per workgroup (four 16-column tiles of N)
 constexpr int kSP = 48;   // halves per staged fragment row (32 + 16 pad: 6 units, conflict-free fragment reads)
@@ -80,15 +86,16 @@ __device__ __forceinline__ void split_pair(float re, float im, uint32_t &hi, uin
 template <int DT, int MT, int MB, bool HX>
 struct CmxShape {
   static constexpr bool DIRECT = HX && DT == DT_F16;
-  static constexpr int MW = MB / 4;                         // modes per wave
+  static constexpr int NT = cmx_threads<MB>();              // threads per workgroup
+  static constexpr int MW = 1;                              // modes per wave
   static constexpr int UX = MB / 2;                         // units (two modes) per spectra / result row
   static constexpr int YO = 2 * MB + 4;                     // floats per output-channel row of the result stage (+ 4 pad)
   static constexpr int YB = kOT * YO + 4;                   // floats per batch row of the result stage
   static constexpr int BT = 16 * MT;                        // batch rows per workgroup
   static constexpr int XP = DIRECT ? 1 : 2;                 // spectra parts
   static constexpr int HL = DT == DT_F16 && !DIRECT ? 2 : 1;  // weight parts
-  static constexpr int XU = MB * BT * kIC * 8 / (16 * kCT);   // spectra units (two modes) per thread and stage
-  static constexpr int WU = MB * kIC * kOT * 4 / (16 * kCT);  // 16-byte weight units per thread and stage
+  static constexpr int XU = MB * BT * kIC * 8 / (16 * NT);   // spectra units (two modes) per thread and stage
+  static constexpr int WU = MB * kIC * kOT * 4 / (16 * NT);  // 16-byte weight units per thread and stage
   static constexpr int XB = BT * kSP;                        // halves of one (mode, part) block
   static constexpr int XS = MB * XP * XB;                   // halves of the spectra stage
   static constexpr int WS = MB * HL * kOT * kSP;           // halves of the weight stage
@@ -147,7 +154,7 @@ __device__ __forceinline__ void cmx_fetch(const ContractArgs &a, int st, int k0,
   const int K = a.K, Ci = a.Ci, Co = a.Co, B = a.B;
 #pragma unroll
   for (int v = 0; v < S::XU; ++v) {
-    const int u = v * kCT + tid;
+    const int u = v * S::NT + tid;
     const int row = u / S::UX, c = u % S::UX;  // row = (b, i), i fastest; c: modes 2c, 2c + 1
     const int b = b0 + row / kIC, i = st * kIC + row % kIC, mode = k0 + 2 * c;
     const bool ok = b < B && i < Ci && mode < K;
@@ -167,7 +174,7 @@ __device__ __forceinline__ void cmx_fetch(const ContractArgs &a, int st, int k0,
     if constexpr (WT) {
       // w[mode][n][c] (Ci % 4 == 0: a 16-byte group is whole or absent)
       int m, nl, q;
-      wunit_t(v * kCT + tid, m, nl, q);
+      wunit_t(v * S::NT + tid, m, nl, q);
       const int mode = k0 + m, n = o0 + nl, c = st * kIC + 4 * q;
       const bool ok = mode < K && n < Co && c < Ci;
       const u32x4 t = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.w) +
@@ -175,7 +182,7 @@ __device__ __forceinline__ void cmx_fetch(const ContractArgs &a, int st, int k0,
       pw[v] = ok ? t : u32x4{0u, 0u, 0u, 0u};
     } else {
       int m, il, c;
-      wunit(v * kCT + tid, m, il, c);
+      wunit(v * S::NT + tid, m, il, c);
       const int mode = k0 + m, i = st * kIC + il, o = o0 + 4 * c;
       const bool ok = mode < K && i < Ci && o < Co;
       const u32x4 t = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.w) +
@@ -195,7 +202,7 @@ __device__ __forceinline__ void cmx_put(uint16_t *xs, uint16_t *ws, int tid,
   using S = CmxShape<DT, MT, MB, HX>;
 #pragma unroll
   for (int v = 0; v < S::XU; ++v) {
-    const int u = v * kCT + tid;
+    const int u = v * S::NT + tid;
     const int row = u / S::UX, c = u % S::UX;
     const int b = row / kIC, i = row % kIC;
     if constexpr (S::DIRECT) {
@@ -234,7 +241,7 @@ __device__ __forceinline__ void cmx_put(uint16_t *xs, uint16_t *ws, int tid,
 #pragma unroll
     for (int v = 0; v < S::WU; ++v) {
       int m, nl, q;
-      wunit_t(v * kCT + tid, m, nl, q);
+      wunit_t(v * S::NT + tid, m, nl, q);
       uint16_t *dst = ws + ((m * S::HL) * kOT + wrow(nl)) * kSP + 8 * q;
       if constexpr (S::HL == 2) {
         // fp16 weights in bf16 hi + lo parts, each half converted on its own
@@ -259,7 +266,7 @@ __device__ __forceinline__ void cmx_put(uint16_t *xs, uint16_t *ws, int tid,
 #pragma unroll
   for (int v = 0; v < S::WU; ++v) {
     int m, i, c;
-    wunit(v * kCT + tid, m, i, c);
+    wunit(v * S::NT + tid, m, i, c);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int o = wrow(4 * c + t);
@@ -298,14 +305,15 @@ __device__ __forceinline__ u32x4 w_form(u32x4 raw, bool part1) {
   return o;
 }
 
-// Waves per SIMD the register allocation targets: two for eight-mode
-// workgroups (the LDS allows two per CU with split operands), three (fp16
-// weights, split in two parts) or four for four-mode ones.
+// Waves per SIMD the register allocation targets: four for eight-mode
+// workgroups (two 8-wave workgroups per CU; the fp16-weight split form then
+// spills 15 registers and still runs faster than with 4-wave workgroups),
+// three (fp16 weights, split in two parts) or four for four-mode ones.
 template <int DT, int MB, bool HX>
-constexpr int cmx_waves() { return MB == 8 ? 2 : DT == DT_F16 && !HX ? 3 : 4; }
+constexpr int cmx_waves() { return MB == 8 ? 4 : DT == DT_F16 && !HX ? 3 : 4; }
 
 template <int DT, int MT, int MB, bool HX, bool WT>
-__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<DT, MB, HX>()))) void fno_contract_mx(
+__global__ __launch_bounds__(cmx_threads<MB>()) __attribute__((amdgpu_waves_per_eu(cmx_waves<DT, MB, HX>()))) void fno_contract_mx(
     ContractArgs a) {
   using S = CmxShape<DT, MT, MB, HX>;
   extern __shared__ uint16_t sm[];
@@ -341,8 +349,8 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<D
   // are in flight together
   int *sbl = reinterpret_cast<int *>(sm + S::LH);
   if constexpr (S::DIRECT) {
-    int *part = reinterpret_cast<int *>(sm);  // [kCT / BT][BT] partial minima
-    constexpr int G = kCT / S::BT;
+    int *part = reinterpret_cast<int *>(sm);  // [NT / BT][BT] partial minima
+    constexpr int G = S::NT / S::BT;
     const int bl = tid % S::BT, grp = tid / S::BT, b = b0 + bl;
     const int *xe = a.xexp + (size_t)min(b, B - 1) * a.Ci;
     int e = 1 << 20;
@@ -441,11 +449,11 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<D
       // groups of four modes of one (b, o) row: largest magnitude ->
       // exponent, fp16 pairs scaled by it (a group cut by K keeps two modes)
       constexpr int GR = MB / 4;                    // groups per row
-      constexpr int YG = 16 * kOT * GR / kCT;       // groups per thread
+      constexpr int YG = 16 * kOT * GR / S::NT;     // groups per thread
       const int KQ = (K + 3) >> 2;
 #pragma unroll
       for (int v = 0; v < YG; ++v) {
-        const int u = v * kCT + tid;
+        const int u = v * S::NT + tid;
         const int row = u / GR, c = u % GR;
         const int bl = row / kOT, ol = row % kOT;
         const int b = b0 + mt * 16 + bl, o = o0 + ol, mode = k0 + 4 * c;
@@ -476,10 +484,10 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(cmx_waves<D
         }
       }
     } else {
-      constexpr int YU = 16 * kOT * MB * 8 / 16 / kCT;  // 16-byte result units per thread
+      constexpr int YU = 16 * kOT * MB * 8 / 16 / S::NT;  // 16-byte result units per thread
 #pragma unroll
       for (int v = 0; v < YU; ++v) {
-        const int u = v * kCT + tid;
+        const int u = v * S::NT + tid;
         const int row = u / S::UX, c = u % S::UX;  // row = (b, o); c: modes 2c, 2c + 1
         const int bl = row / kOT, ol = row % kOT;
         const int b = b0 + mt * 16 + bl, o = o0 + ol, mode = k0 + 2 * c;
@@ -536,7 +544,7 @@ static size_t contract_mx_lds_bytes(int dtype, int B, int mb, bool hx) {
   const int BT = B <= 16 ? 16 : 32, XP = direct ? 1 : 2, HL = dtype == DT_F16 && !direct ? 2 : 1;
   const size_t stage = ((size_t)mb * XP * BT * kSP + (size_t)mb * HL * kOT * kSP) * 2;
   const size_t out = (size_t)16 * (kOT * (2 * mb + 4) + 4) * 4;
-  return std::max(std::max(stage, out), (size_t)kCT * 4) + (direct ? BT * 4 : 0);
+  return std::max(std::max(stage, out), (size_t)mb * 64 * 4) + (direct ? BT * 4 : 0);
 }
 
 size_t contract_mx_lds_bytes(int dtype, int B) {
@@ -571,7 +579,7 @@ hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s, b
   if (n > 0x7fffffffL) return hipErrorInvalidValue;
   dim3 grid((unsigned)n);
   void *args[] = {(void *)&a};
-  return hipLaunchKernel(k, grid, dim3(kCT), args, contract_mx_lds_bytes(dtype, a.B, mb, a.xh16 != nullptr), s);
+  return hipLaunchKernel(k, grid, dim3(mb * 64), args, contract_mx_lds_bytes(dtype, a.B, mb, a.xh16 != nullptr), s);
 }
 
 }  // namespace fno
