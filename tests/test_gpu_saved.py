@@ -170,3 +170,21 @@ def test_saved_argument_errors():
         torch.cuda.synchronize()
     finally:
         fno.fno_plan_destroy(plan)
+
+
+def test_saved_forward_ignores_single_launch_shape():
+    """A plan set to the single cooperative launch still saves through the
+    stand-alone kernels: y and the gradients as from the default shape."""
+    cfg = _cfg(2, 3, 32, 32, (128, 128), (16, 16))
+    plan = fno.fno_plan_create(2, cfg.batch, cfg.c_in, cfg.c_out, cfg.grid, cfg.modes, "f32", 0)
+    try:
+        inp, gout, x, w, g = _tensors(plan, cfg, "f32")
+        y0, gx0, gw0 = _saved_pass(plan, x, w, g)
+        try:
+            fno.fno_plan_set_launch_shape(plan, "fused")
+        except fno.FnoError:
+            pytest.skip("no single-launch shape for this plan on this device")
+        y1, gx1, gw1 = _saved_pass(plan, x, w, g)
+    finally:
+        fno.fno_plan_destroy(plan)
+    assert np.array_equal(y0, y1) and np.array_equal(gx0, gx1) and np.array_equal(gw0, gw1)
