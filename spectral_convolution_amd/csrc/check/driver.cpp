@@ -1,7 +1,8 @@
 // driver.cpp - the bounds-check build's driver: every public entry point on a
 // spread of shapes (matrix-core and VALU planes, 2D and 3D, the three dtypes,
 // ragged modes and channels, both launch shapes, the half exchange, the
-// backward pass, weight repacking, the allocation-free entry, the FNO block
+// backward pass (from x and from saved spectra), weight repacking, the
+// allocation-free entry, the FNO block
 // and the full FNO2d network). Each launch is checked by its launcher's
 // bounds hook against the recording runtime's allocations; the program exits
 // non-zero if any span or assumption was broken. Host code only.
@@ -67,6 +68,16 @@ void run_layer(int ndim, int B, int Ci, int Co, std::vector<int> grid, std::vect
   EXPECT(bwd(p, x.p, w.p, gy.p, gx.p, gw.p, nullptr) == FNO_OK);
   EXPECT(bwd(p, x.p, w.p, gy.p, gx.p, nullptr, nullptr) == FNO_OK);
   EXPECT(bwd(p, x.p, w.p, gy.p, nullptr, gw.p, nullptr) == FNO_OK);
+  // the saved-spectra pair, where the plan has a saved format
+  size_t sb = 0;
+  const fno_status_t ss = fno_plan_saved_bytes(p, &sb);
+  EXPECT(ss == FNO_OK || ss == FNO_ERR_UNSUPPORTED);
+  if (ss == FNO_OK) {
+    Buf sv(sb);
+    EXPECT(fno_spectral_conv_forward_save(p, x.p, w.p, y.p, sv.p, nullptr) == FNO_OK);
+    EXPECT(fno_spectral_conv_backward_saved(p, sv.p, w.p, gy.p, gx.p, gw.p, nullptr) == FNO_OK);
+    EXPECT(fno_spectral_conv_backward_saved(p, sv.p, nullptr, gy.p, nullptr, gw.p, nullptr) == FNO_OK);
+  }
   const fno_status_t na = fno_spectral_conv_noalloc(p, x.p, w.p, y.p, nullptr);
   EXPECT(na == FNO_OK || na == FNO_ERR_UNSUPPORTED);
   int nl = 0;
