@@ -1,5 +1,5 @@
-// backward.hip - the two kernels of the layer's backward pass that the
-// forward path does not already provide.
+// backward.hip - the kernels of the layer's backward pass that the forward
+// path does not already provide.
 //
 // For a loss with gradient g = dL/dy, every step of the layer is linear, so
 // its gradients are the adjoints of the steps in reverse order (the TurboFNO
@@ -16,7 +16,9 @@
 // and gamma_k the c2r weight of the mode's last-axis index (1 for index 0,
 // whose imaginary part never reaches y, 2 otherwise).
 //
-// fno_conj_transpose forms W^H; fno_grad_w is the per-mode batch reduction.
+// fno_conj_transpose forms W^H (only where the adjoint contraction cannot
+// read W itself); fno_grad_w is the per-mode batch reduction on complex fp32
+// spectra, fno_grad_w_hx the same on the half exchange (fp16 matrix cores).
 
 #include "common.hpp"
 
