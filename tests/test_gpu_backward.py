@@ -113,6 +113,29 @@ def test_backward_parity_small(case):
     assert ex <= TOL[dtype] and ew <= TOL[dtype], f"{name}: grad_x {ex:.3e} grad_w {ew:.3e}"
 
 
+@pytest.mark.parametrize("dtype,shift", [("f16", 20), ("bf16", 30)])
+def test_backward_half_exchange_wide_batch_range(dtype, shift):
+    """Batch elements 1.. of x scaled down by 2^-shift: their spectra planes sit
+    2^shift below element 0's, so the weight gradient's per-row rescale takes
+    its fp16 product by a subnormal power of two (shift 20) or its fp32 path
+    (shift 30, bf16 storage, which holds such inputs). Their contributions
+    to grad_w are that much smaller; the result must stay finite and match
+    the oracle, dominated by element 0."""
+    cfg = _cfg("r", 2, 33, 20, 36, (128, 128), (30, 31), "uniform", seed=7)
+    inp = wl.layer_inputs(cfg, dtype)
+    x64 = inp["x64"].copy()
+    x64[1:] *= 2.0 ** -shift
+    xs = wl.generate.round_to_storage(x64, dtype)
+    inp = dict(inp, x=xs, x64=wl.generate.storage_to_float64(xs, dtype))
+    gout = wl.layer_grad_output(cfg, dtype)
+    gx, gw = _backward_gpu(cfg, dtype, inp, gout)
+    rx, rw = _oracle(cfg, inp["x64"], inp["w64"], gout["g64"])
+    assert np.all(np.isfinite(gw.real)) and np.all(np.isfinite(gw.imag))
+    ex, ew = rel_l2(gx, rx), rel_l2(gw, rw)
+    print(f"[bwd-range] {dtype} shift={shift} grad_x rel_l2={ex:.3e} grad_w rel_l2={ew:.3e}", flush=True)
+    assert ex <= TOL[dtype] and ew <= TOL[dtype]
+
+
 FULL = [("c1", "f32", (0, 15)), ("c1", "f16", (3,)), ("c2", "f16", (0, 31)), ("c2", "bf16", (17,)),
         ("c3", "f32", (0, 3))]
 
