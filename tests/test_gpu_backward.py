@@ -78,6 +78,9 @@ SMALL = [
     # the backward keeps complex fp32 spectra (the other fp16 matrix-core
     # cases above and the full-size 256x256 one run it on the half exchange)
     ("hx-odd-k-f16", _cfg("r", 2, 33, 36, 20, (128, 128), (31, 31), "uniform"), "f16"),
+    ("hx-odd-k-bf16", _cfg("r", 2, 33, 36, 20, (128, 128), (31, 31), "uniform"), "bf16"),
+    # 16-row batch tiles in the adjoint contraction (W read transposed)
+    ("cmx-b16-f16", _cfg("r", 2, 16, 64, 24, (128, 128), (30, 30), "uniform"), "f16"),
     # the adjoint contraction (64 output channels) on four-mode workgroups,
     # the forward one (24 output channels) below the matrix-core size
     ("cmx-mb4-adjoint-f16", _cfg("r", 2, 20, 64, 24, (128, 128), (24, 24), "uniform"), "f16"),
