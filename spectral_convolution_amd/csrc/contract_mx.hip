@@ -21,7 +21,7 @@
 // largest, a normal fp16. An fp16 value splits into bf16 hi + lo exactly, so
 // the products stay exact; only the roundings to fp16 are added.
 //
-// A workgroup owns MB = 8 (or 4) consecutive modes x 16 or 32 batch rows x
+// A workgroup owns MB = 16, 8 or 4 consecutive modes x 16 or 32 batch rows x
 // 32 output channels and streams the input channels in stages of 16: the
 // spectra rows [b][i][MB modes] (8 MB contiguous bytes) and weight rows [mode][i][32 o]
 // (128 bytes) are loaded with 16-byte accesses one stage ahead into
@@ -45,11 +45,11 @@ namespace fno {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 
-// Threads per workgroup: one wave per mode, 8 waves for eight-mode
-// workgroups and 4 for four-mode ones (measured against 4 waves of two modes
-// each at 256^2: 26.2 -> 25.1 us fp16 on the half exchange, 25.1 -> 22.4 us
-// its adjoint, 24.7 -> 22.9 us bf16: twice the waves per CU to hide the
-// stage latencies, half the registers per lane)
+// Threads per workgroup: one wave per mode (16, 8 or 4 waves; eight-mode
+// workgroups measured against 4 waves of two modes each at 256^2: 26.2 ->
+// 25.1 us fp16 on the half exchange, 25.1 -> 22.4 us its adjoint, 24.7 ->
+// 22.9 us bf16: twice the waves per CU to hide the stage latencies, half the
+// registers per lane)
 template <int MB>
 constexpr int cmx_threads() { return MB * 64; }
 constexpr int kIC = 16;   // input channels per stage (one 32-deep block of K)
@@ -305,12 +305,12 @@ __device__ __forceinline__ u32x4 w_form(u32x4 raw, bool part1) {
   return o;
 }
 
-// Waves per SIMD the register allocation targets: four for eight-mode
-// workgroups (two 8-wave workgroups per CU; the fp16-weight split form then
+// Waves per SIMD the register allocation targets: four for eight- and
+// sixteen-mode workgroups (16 waves per CU; the fp16-weight split form then
 // spills 15 registers and still runs faster than with 4-wave workgroups),
 // three (fp16 weights, split in two parts) or four for four-mode ones.
 template <int DT, int MB, bool HX>
-constexpr int cmx_waves() { return MB == 8 ? 4 : DT == DT_F16 && !HX ? 3 : 4; }
+constexpr int cmx_waves() { return MB >= 8 ? 4 : DT == DT_F16 && !HX ? 3 : 4; }
 
 template <int DT, int MT, int MB, bool HX, bool WT>
 __global__ __launch_bounds__(cmx_threads<MB>()) __attribute__((amdgpu_waves_per_eu(cmx_waves<DT, MB, HX>()))) void fno_contract_mx(
@@ -512,18 +512,33 @@ long contract_mx_workgroups(int B, int Co, int K) {
   return (long)((K + 7) / 8) * ((B + BT - 1) / BT) * ((Co + kOT - 1) / kOT);
 }
 
-// Modes per workgroup: 8 unless that leaves resident slots empty (two
-// eight-mode workgroups fit on each of the 256 CUs); then 4, which doubles
-// the workgroups. Measured: the FNO2d layer (B = 20, 64 -> 64 channels,
-// modes 24 x 24: 288 eight-mode workgroups) runs faster with 4, the 256^2
-// layer (B = 32, 64 channels, 32 x 32 modes: 512) slower.
-static int cmx_modes(int B, int Co, int K) { return contract_mx_workgroups(B, Co, K) < 512 ? 4 : 8; }
+static size_t contract_mx_lds_bytes(int dtype, int B, int mb, bool hx);
+
+constexpr size_t kLdsMax = 160 * 1024;  // LDS of a CU, the most one workgroup may take
+
+// Modes per workgroup. 16 (one 16-wave workgroup per CU) where that still
+// gives every CU a workgroup and its LDS fits: at 256^2 (B = 32, 64
+// channels, 32 x 32 modes) 25.0 -> 23.9 us fp16 and 22.9 -> 20.0 us bf16 on
+// the half exchange against 8 modes; not for the fp16 adjoint, which
+// measured 22.4 -> 22.9 us. Else 8 unless that leaves resident slots empty
+// (two eight-mode workgroups fit on each CU); then 4, which doubles the
+// workgroups. Measured: the FNO2d layer (B = 20, 64 -> 64 channels, modes
+// 24 x 24: 288 eight-mode workgroups) runs faster with 4 (16.1 against 17.4
+// us with 8), the 256^2 layer with 8 faster than with 4 (25.0 against 31.1).
+static int cmx_modes(int dtype, int B, int Co, int K, bool hx, bool wt) {
+  const long BT = B <= 16 ? 16 : 32;
+  const long wg16 = (long)((K + 15) / 16) * ((B + BT - 1) / BT) * ((Co + kOT - 1) / kOT);
+  if (!(wt && dtype == DT_F16) && wg16 >= 256 && contract_mx_lds_bytes(dtype, B, 16, hx) <= kLdsMax) return 16;
+  return contract_mx_workgroups(B, Co, K) < 512 ? 4 : 8;
+}
 
 template <int DT, bool HX, bool WT>
 static const void *contract_mx_kernel_dt(int B, int mb) {
   const bool one = B <= 16;
   if (mb == 4)
     return one ? (const void *)fno_contract_mx<DT, 1, 4, HX, WT> : (const void *)fno_contract_mx<DT, 2, 4, HX, WT>;
+  if (mb == 16)
+    return one ? (const void *)fno_contract_mx<DT, 1, 16, HX, WT> : (const void *)fno_contract_mx<DT, 2, 16, HX, WT>;
   return one ? (const void *)fno_contract_mx<DT, 1, 8, HX, WT> : (const void *)fno_contract_mx<DT, 2, 8, HX, WT>;
 }
 
@@ -549,18 +564,23 @@ static size_t contract_mx_lds_bytes(int dtype, int B, int mb, bool hx) {
 
 size_t contract_mx_lds_bytes(int dtype, int B) {
   size_t m = 0;
-  for (int mb : {4, 8})
-    for (bool hx : {false, true}) m = std::max(m, contract_mx_lds_bytes(dtype, B, mb, hx));
+  for (int mb : {4, 8, 16})
+    for (bool hx : {false, true}) {
+      const size_t l = contract_mx_lds_bytes(dtype, B, mb, hx);
+      if (l <= kLdsMax) m = std::max(m, l);
+    }
   return m;
 }
 
 hipError_t contract_mx_prepare(int dtype, int B) {
-  for (int mb : {4, 8})
+  for (int mb : {4, 8, 16})
     for (bool hx : {false, true})
       for (bool wt : {false, true}) {
+        const size_t lds = contract_mx_lds_bytes(dtype, B, mb, hx);
+        if (mb == 16 && lds > kLdsMax) continue;  // never chosen
         const void *k = contract_mx_kernel(dtype, B, mb, hx, wt);
         if (!k) return hipErrorInvalidValue;
-        const hipError_t e = raise_lds_cap(k, contract_mx_lds_bytes(dtype, B, mb, hx));
+        const hipError_t e = raise_lds_cap(k, lds);
         if (e != hipSuccess) return e;
       }
   return hipSuccess;
@@ -570,7 +590,7 @@ bool contract_mx_wt_supported(int Ci) { return (Ci & 3) == 0; }
 
 hipError_t launch_contract_mx(const ContractArgs &a, int dtype, hipStream_t s, bool wt) {
   FNO_BOUNDS(check_contract(a, dtype, true);)
-  const int mb = cmx_modes(a.B, a.Co, a.K);
+  const int mb = cmx_modes(dtype, a.B, a.Co, a.K, a.xh16 != nullptr, wt);
   const void *k = contract_mx_kernel(dtype, a.B, mb, a.xh16 != nullptr, wt);
   if (!k || (wt && !contract_mx_wt_supported(a.Ci))) return hipErrorInvalidValue;
   const int BT = a.B <= 16 ? 16 : 32;
